@@ -1,0 +1,377 @@
+"""CPU oracle for chunkwise-parallel causal linear attention.
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call this module.  It shares
+no code with the HIP path (``chunked_causal_linear_amd``) and imports nothing
+from it.
+
+Everything here is the plain definition of what the method computes, written
+from two pages:
+
+* "attention と線形の間" (sharin-2a1.pages.dev/parts/chunked.html), below
+  called *the chunking page*: section ① (the two association orders and the
+  d x d state), section ② (the chunked algorithm and its two causal ends) and
+  section ③ (the operation counts).
+* "Linear Attention / Performerの理論と実装" (disassemble-channel.com/
+  linear-attention/), below called *the linear-attention page*: the kernel
+  re-formulation with feature maps and normaliser, the RNN view (state S_t,
+  normaliser z_t), the elu+1 and FAVOR+ feature maps, and the recurrent and
+  materialised-prefix causal forms.
+
+Precision.  Floating-point inputs arrive as float64 arrays holding bf16 values
+(exact), and every form computes in float64 with no intermediate rounding.
+Integer inputs arrive as int64 arrays; the matrix forms then compute in float64,
+which is exact because every intermediate is an integer below 2**53 in
+magnitude (``_check_int_exact`` asserts the bound), and the results are returned
+as int64.  ``brute_force`` uses Python integers / Fractions and pins the rest.
+
+Shapes.  All forms take one head: q, k as [L, d_k] (after the feature map),
+v as [L, d_v].  ``over_heads`` maps a form over a leading head axis.
+
+Parity status.  Every function below is pinned by tests under
+``tests/test_oracle_*.py`` (closed forms, brute force, exhaustive tiny cases,
+cross-form identities, the chunking page's printed tables).  ``phi_favor`` is
+pinned by its closed form at hand-computed points and by the large-m
+convergence of phi(q).phi(k) to exp(q.k); the W it consumes is an input.
+"""
+from __future__ import annotations
+
+from fractions import Fraction
+from typing import Callable, Optional, Tuple
+
+import numpy as np
+
+_EXACT_LIMIT = 2 ** 53
+
+
+# ---------------------------------------------------------------------------
+# Feature maps (linear-attention page: ELU feature map, FAVOR+ positive random
+# features).  The map is applied to queries and keys only, never to values.
+# ---------------------------------------------------------------------------
+def phi_identity(x: np.ndarray) -> np.ndarray:
+    """No feature map: the chunking page works directly on q and k."""
+    return x
+
+
+def phi_elu1(x: np.ndarray) -> np.ndarray:
+    """elu(x) + 1 with ELU's alpha = 1: x + 1 where x >= 0, exp(x) where x < 0."""
+    x = np.asarray(x, dtype=np.float64)
+    return np.where(x >= 0, x + 1.0, np.exp(np.minimum(x, 0.0)))
+
+
+def phi_favor(x: np.ndarray, W: np.ndarray) -> np.ndarray:
+    """FAVOR+ positive random features.
+
+    phi(x)_l = exp(w_l . x - |x|^2 / 2) / sqrt(m) for the m rows w_l of W
+    (linear-attention page, FAVOR+ section: positive random features and their
+    implementation).  x: [..., d], W: [m, d] -> [..., m].
+    """
+    x = np.asarray(x, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    m = W.shape[0]
+    proj = x @ W.T
+    half_sq = 0.5 * np.sum(x * x, axis=-1, keepdims=True)
+    return np.exp(proj - half_sq) / np.sqrt(m)
+
+
+def apply_phi(x: np.ndarray, fmap: str, W: Optional[np.ndarray] = None,
+              in_scale: float = 1.0) -> np.ndarray:
+    """phi(in_scale * x) for fmap in {"identity", "elu1", "favor"}."""
+    if in_scale != 1.0:
+        x = np.asarray(x, dtype=np.float64) * in_scale
+    if fmap == "identity":
+        return phi_identity(x)
+    if fmap == "elu1":
+        return phi_elu1(x)
+    if fmap == "favor":
+        if W is None:
+            raise ValueError("favor needs W")
+        return phi_favor(x, W)
+    raise ValueError(fmap)
+
+
+# ---------------------------------------------------------------------------
+# helpers
+# ---------------------------------------------------------------------------
+def _is_int(*arrays) -> bool:
+    return all(np.issubdtype(np.asarray(a).dtype, np.integer) for a in arrays)
+
+
+def _check_int_exact(q, k, v) -> None:
+    """Integer inputs: the float64 matrix forms are exact below 2**53.
+
+    Any entry of any intermediate is bounded by L * d_k * max|q| * max|k| * max|v|
+    (scores times values, or queries times the summed state).
+    """
+    L, dk = q.shape
+    bound = (L * dk * max(1, int(np.abs(q).max(initial=0))) * max(1, int(np.abs(k).max(initial=0)))
+             * max(1, int(np.abs(v).max(initial=0))))
+    if bound >= _EXACT_LIMIT:
+        raise OverflowError("integer case too large for exact float64 evaluation")
+
+
+def _prep(q, k, v):
+    integer = _is_int(q, k, v)
+    if integer:
+        _check_int_exact(np.asarray(q), np.asarray(k), np.asarray(v))
+    return (np.asarray(q, dtype=np.float64), np.asarray(k, dtype=np.float64),
+            np.asarray(v, dtype=np.float64), integer)
+
+
+def _finish(x: np.ndarray, integer: bool) -> np.ndarray:
+    if integer:
+        r = np.rint(x)
+        assert np.array_equal(r, x), "non-integer intermediate on the integer path"
+        return r.astype(np.int64)
+    return x
+
+
+def tril(scores: np.ndarray) -> np.ndarray:
+    """Causal mask: zero position (i, j) for j > i, keep the diagonal.
+
+    The chunking page's tril keeps j <= i (a token sees itself); the RNN view of
+    the linear-attention page adds token t to the state before reading it.
+    """
+    n_rows, n_cols = scores.shape[-2], scores.shape[-1]
+    keep = np.arange(n_cols)[None, :] <= np.arange(n_rows)[:, None]
+    return np.where(keep, scores, 0.0)
+
+
+def _divide(num: np.ndarray, den: np.ndarray) -> np.ndarray:
+    """Row-wise division of the numerator by the denominator, no epsilon."""
+    with np.errstate(divide="ignore", invalid="ignore"):
+        return num / den[..., None]
+
+
+# ---------------------------------------------------------------------------
+# O1: causal scores-first  (chunking page, section ②: CausalScoresFirst;
+# linear-attention page: normalised output as a ratio of kernel sums)
+# ---------------------------------------------------------------------------
+def causal_scores_first(q, k, v, normalize: bool = False) -> np.ndarray:
+    """A = tril(q k^T) (L x L); numerator A v; normalised: divide by the row sums of A."""
+    q, k, v, integer = _prep(q, k, v)
+    A = tril(q @ k.T)
+    num = A @ v
+    if not normalize:
+        return _finish(num, integer)
+    return _divide(num, A.sum(axis=1))
+
+
+# ---------------------------------------------------------------------------
+# O2: causal state-first, token by token (chunking page, section ②:
+# CausalStateFirst; linear-attention page: RNN view, S_t and z_t recurrences)
+# ---------------------------------------------------------------------------
+def causal_state_first(q, k, v, normalize: bool = False, S0=None, z0=None):
+    """S_t = S_{t-1} + k_t^T v_t, z_t = z_{t-1} + k_t; read y_t = q_t S_t [/ q_t . z_t].
+
+    The state is updated with token t before token t reads it.  Returns
+    (out [L, d_v], S_L [d_k, d_v], z_L [d_k]).  S0/z0 continue from a given state
+    (zero when omitted, as on both pages).
+    """
+    q, k, v, integer = _prep(q, k, v)
+    L, dk = q.shape
+    dv = v.shape[1]
+    S = np.zeros((dk, dv)) if S0 is None else np.array(S0, dtype=np.float64)
+    z = np.zeros(dk) if z0 is None else np.array(z0, dtype=np.float64)
+    out = np.zeros((L, dv))
+    for t in range(L):
+        S = S + np.outer(k[t], v[t])
+        z = z + k[t]
+        num = q[t] @ S
+        out[t] = num / (q[t] @ z) if normalize else num
+    if normalize:
+        return out, S, z
+    return _finish(out, integer), _finish(S, integer), _finish(z, integer)
+
+
+def recurrent_step(S, z, q_t, k_t, v_t, normalize: bool = True):
+    """One decode step on one state: S += k^T v, z += k, then o = q S [/ q . z].
+
+    The same update-then-read order as causal_state_first.  Returns (o, S', z').
+    """
+    S = np.asarray(S, dtype=np.float64) + np.outer(k_t, v_t)
+    z = np.asarray(z, dtype=np.float64) + k_t
+    num = q_t @ S
+    o = num / (q_t @ z) if normalize else num
+    return o, S, z
+
+
+# ---------------------------------------------------------------------------
+# O2': the materialised-prefix causal form (linear-attention page: the
+# "parallel" causal implementation that stores every prefix state)
+# ---------------------------------------------------------------------------
+def causal_materialized_prefix(q, k, v, normalize: bool = False) -> np.ndarray:
+    """Store all L prefix states S_1..S_L (L x d_k x d_v) first, then read each."""
+    q, k, v, integer = _prep(q, k, v)
+    S_pref = np.cumsum(k[:, :, None] * v[:, None, :], axis=0)
+    z_pref = np.cumsum(k, axis=0)
+    num = np.einsum("ta,tab->tb", q, S_pref)
+    if not normalize:
+        return _finish(num, integer)
+    return _divide(num, np.einsum("ta,ta->t", q, z_pref))
+
+
+# ---------------------------------------------------------------------------
+# O3: chunked (chunking page, section ②: Chunked), with the normaliser of the
+# linear-attention page carried alongside the state.
+# ---------------------------------------------------------------------------
+def chunked(q, k, v, C: int, normalize: bool = False):
+    """Chunkwise form with chunk size C (C <= 0 is treated as 1).
+
+    State starts at zero.  For each chunk [s, e) (the last may be shorter):
+        inter = q_c state            (and q_c . z for the denominator)
+        intra = tril(q_c k_c^T) v_c  (and the row sums of tril(q_c k_c^T))
+        out_c = inter + intra        (normalised: numerator / denominator)
+        state += k_c^T v_c ; z += sum of k_c rows
+    Returns (out, S_L, z_L).
+    """
+    if C <= 0:
+        C = 1
+    q, k, v, integer = _prep(q, k, v)
+    L, dk = q.shape
+    dv = v.shape[1]
+    out = np.zeros((L, dv))
+    S = np.zeros((dk, dv))
+    z = np.zeros(dk)
+    for s in range(0, L, C):
+        e = min(s + C, L)
+        qc, kc, vc = q[s:e], k[s:e], v[s:e]
+        sc = tril(qc @ kc.T)
+        num = qc @ S + sc @ vc
+        if normalize:
+            den = qc @ z + sc.sum(axis=1)
+            out[s:e] = _divide(num, den)
+        else:
+            out[s:e] = num
+        S = S + kc.T @ vc
+        z = z + kc.sum(axis=0)
+    if normalize:
+        return out, S, z
+    return _finish(out, integer), _finish(S, integer), _finish(z, integer)
+
+
+# ---------------------------------------------------------------------------
+# Phase definitions used by the three-kernel pipeline: per-chunk states and
+# their exclusive prefix (chunking page, section ②: the state carried across
+# chunks is the sum of k_c^T v_c over the chunks already processed).
+# ---------------------------------------------------------------------------
+def chunk_states(k, v, C: int):
+    """Per-chunk local states S_n = k_c^T v_c and z_n = sum of k_c rows, n = 0..N-1."""
+    if C <= 0:
+        C = 1
+    integer = _is_int(k, v)
+    kf = np.asarray(k, dtype=np.float64)
+    vf = np.asarray(v, dtype=np.float64)
+    L, dk = kf.shape
+    N = (L + C - 1) // C
+    S = np.zeros((N, dk, vf.shape[1]))
+    z = np.zeros((N, dk))
+    for n in range(N):
+        s, e = n * C, min((n + 1) * C, L)
+        S[n] = kf[s:e].T @ vf[s:e]
+        z[n] = kf[s:e].sum(axis=0)
+    return _finish(S, integer), _finish(z, integer)
+
+
+def exclusive_scan(S_n: np.ndarray):
+    """P_0 = 0, P_n = P_{n-1} + S_{n-1}; also the total sum (the final state)."""
+    integer = _is_int(S_n)
+    Sf = np.asarray(S_n, dtype=np.float64)
+    P = np.zeros_like(Sf)
+    run = np.zeros(Sf.shape[1:])
+    for n in range(Sf.shape[0]):
+        P[n] = run
+        run = run + Sf[n]
+    return _finish(P, integer), _finish(run, integer)
+
+
+# ---------------------------------------------------------------------------
+# O4: non-causal, both association orders (chunking page, section ①:
+# ScoresFirst, StateFirst, State; linear-attention page: matrix form with the
+# diag^{-1} normaliser and its linear_attention description)
+# ---------------------------------------------------------------------------
+def noncausal_scores_first(q, k, v, normalize: bool = False) -> np.ndarray:
+    q, k, v, integer = _prep(q, k, v)
+    A = q @ k.T
+    if not normalize:
+        return _finish(A @ v, integer)
+    return _divide(A @ v, A.sum(axis=1))
+
+
+def noncausal_state_first(q, k, v, normalize: bool = False) -> np.ndarray:
+    q, k, v, integer = _prep(q, k, v)
+    S = k.T @ v
+    if not normalize:
+        return _finish(q @ S, integer)
+    return _divide(q @ S, q @ k.sum(axis=0))
+
+
+def final_state(k, v):
+    """S = sum_t k_t^T v_t (d_k x d_v, independent of L) and z = sum_t k_t."""
+    integer = _is_int(k, v)
+    kf = np.asarray(k, dtype=np.float64)
+    vf = np.asarray(v, dtype=np.float64)
+    return _finish(kf.T @ vf, integer), _finish(kf.sum(axis=0), integer)
+
+
+# ---------------------------------------------------------------------------
+# O7: brute force on tiny inputs, in exact arithmetic
+# ---------------------------------------------------------------------------
+def brute_force(q, k, v, causal: bool = True, normalize: bool = False):
+    """o_{i,c} = sum_{j<=i} sum_a q_{i,a} k_{j,a} v_{j,c}  [/ sum_{j<=i} sum_a q_{i,a} k_{j,a}].
+
+    Nested Python loops over exact integers (or Fractions of the exact binary
+    values of float inputs).  Returns a list of lists of Fractions.
+    """
+    def exact(x):
+        if isinstance(x, (int, np.integer)):
+            return Fraction(int(x))
+        return Fraction(float(x))
+
+    L, dk = len(q), len(q[0])
+    dv = len(v[0])
+    out = []
+    for i in range(L):
+        last = i if causal else L - 1
+        row = []
+        den = Fraction(0)
+        for j in range(last + 1):
+            for a in range(dk):
+                den += exact(q[i][a]) * exact(k[j][a])
+        for c in range(dv):
+            acc = Fraction(0)
+            for j in range(last + 1):
+                s = Fraction(0)
+                for a in range(dk):
+                    s += exact(q[i][a]) * exact(k[j][a])
+                acc += s * exact(v[j][c])
+            row.append(acc / den if normalize else acc)
+        out.append(row)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# mapping over heads
+# ---------------------------------------------------------------------------
+def over_heads(form: Callable, q, k, v, *args, **kwargs):
+    """Apply a single-head form to [H, L, d] arrays; stacks each returned array."""
+    results = [form(q[h], k[h], v[h], *args, **kwargs) for h in range(q.shape[0])]
+    if isinstance(results[0], tuple):
+        return tuple(np.stack([r[i] for r in results]) for i in range(len(results[0])))
+    return np.stack(results)
+
+
+def forward(q_raw, k_raw, v, C: int, causal: bool = True, normalize: bool = False,
+            fmap: str = "identity", W=None, in_scale: float = 1.0):
+    """What the forward entry point returns for one head: (out, S_L, z_L).
+
+    phi is applied to q and k, then the chunked form (causal) or the
+    state-first form (non-causal, C ignored) gives the output.
+    """
+    qp = apply_phi(q_raw, fmap, W, in_scale) if (fmap != "identity" or in_scale != 1.0) else q_raw
+    kp = apply_phi(k_raw, fmap, W, in_scale) if (fmap != "identity" or in_scale != 1.0) else k_raw
+    if causal:
+        return chunked(qp, kp, v, C, normalize)
+    out = noncausal_state_first(qp, kp, v, normalize)
+    S, z = final_state(kp, v)
+    return out, S, z

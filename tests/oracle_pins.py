@@ -1,0 +1,287 @@
+"""Checks that pin the CPU oracle to what the pages and the mathematics fix.
+
+Each ``check_*`` takes the oracle module and raises AssertionError on a
+violation.  ``tests/test_oracle_pins.py`` runs them on the real oracle;
+``tests/test_oracle_mutants.py`` plants plausible mistakes in a copy of the
+oracle and requires that at least one check fails for every mistake.
+
+Pages: the chunking page is "attention と線形の間"
+(sharin-2a1.pages.dev/parts/chunked.html); the linear-attention page is
+"Linear Attention / Performerの理論と実装" (disassemble-channel.com/linear-attention/).
+"""
+from __future__ import annotations
+
+import itertools
+import math
+from fractions import Fraction
+
+import numpy as np
+
+from workloads import bf16_bits_to_f64, f32_to_bf16_bits
+
+
+def _ints(rng, shape, lo=-3, hi=3):
+    return rng.integers(lo, hi + 1, size=shape).astype(np.int64)
+
+
+def _bf16(rng, shape, scale=1.0):
+    return bf16_bits_to_f64(f32_to_bf16_bits(rng.standard_normal(shape).astype(np.float32) * scale))
+
+
+def _frac_matrix(m):
+    return np.array([[float(x) for x in row] for row in m])
+
+
+# ---------------------------------------------------------------------------
+# P-a / P-c: the forms agree exactly on integers, for every chunk size
+# ---------------------------------------------------------------------------
+def check_exhaustive_tiny(o, L: int = 2, vals=(-1, 0, 1)) -> None:
+    """All q, k, v in {-1,0,1}^(L x 1): scores-first, state-first, the materialised
+    prefix form, chunked for every C in 0..L+1 and brute force agree exactly
+    (chunking page, section ②: both ends and every chunk size give one answer)."""
+    for flat in itertools.product(vals, repeat=3 * L):
+        a = np.array(flat, dtype=np.int64).reshape(3, L, 1)
+        q, k, v = a[0], a[1], a[2]
+        ref = o.causal_scores_first(q, k, v)
+        bf = np.array([[int(x) for x in row] for row in o.brute_force(q, k, v)], dtype=np.int64)
+        assert np.array_equal(ref, bf), (flat, ref, bf)
+        rec, S, z = o.causal_state_first(q, k, v)
+        assert np.array_equal(rec, ref), flat
+        assert np.array_equal(o.causal_materialized_prefix(q, k, v), ref), flat
+        for C in range(0, L + 2):
+            ch, Sc, zc = o.chunked(q, k, v, C)
+            assert np.array_equal(ch, ref), (flat, C)
+            assert np.array_equal(Sc, S) and np.array_equal(zc, z), (flat, C)
+
+
+def check_random_int_all_chunks(o, seed: int = 0) -> None:
+    """Random integers, d_k != d_v, every C from 0 to L+3 including non-divisors."""
+    rng = np.random.default_rng([seed, 11])
+    L, dk, dv = 23, 5, 3
+    q, k, v = _ints(rng, (L, dk)), _ints(rng, (L, dk)), _ints(rng, (L, dv))
+    ref = o.causal_scores_first(q, k, v)
+    bf = np.array([[int(x) for x in row] for row in o.brute_force(q, k, v)], dtype=np.int64)
+    assert np.array_equal(ref, bf)
+    rec, S, z = o.causal_state_first(q, k, v)
+    assert np.array_equal(rec, ref)
+    # final state: S = sum_t k_t^T v_t (d_k x d_v), z = sum_t k_t
+    S_def = sum(np.outer(k[t], v[t]) for t in range(L))
+    assert S.shape == (dk, dv) and np.array_equal(S, S_def)
+    assert np.array_equal(z, k.sum(axis=0))
+    Sf, zf = o.final_state(k, v)
+    assert np.array_equal(Sf, S_def) and np.array_equal(zf, z)
+    for C in range(0, L + 4):
+        ch, Sc, zc = o.chunked(q, k, v, C)
+        assert np.array_equal(ch, ref), C
+        assert np.array_equal(Sc, S_def) and np.array_equal(zc, z), C
+
+
+def check_chunk_phases(o, seed: int = 1) -> None:
+    """Per-chunk states are k_c^T v_c of each chunk; the exclusive prefix P_n sums
+    the chunks before n; the total is the final state; out_c = q_c P_n + tril(q_c k_c^T) v_c."""
+    rng = np.random.default_rng([seed, 12])
+    L, dk, dv = 29, 4, 6
+    q, k, v = _ints(rng, (L, dk)), _ints(rng, (L, dk)), _ints(rng, (L, dv))
+    for C in (1, 4, 7, 29, 40):
+        Sn, zn = o.chunk_states(k, v, C)
+        N = (L + C - 1) // C
+        assert Sn.shape == (N, dk, dv) and zn.shape == (N, dk)
+        for n in range(N):
+            rows = range(n * C, min((n + 1) * C, L))
+            assert np.array_equal(Sn[n], sum(np.outer(k[t], v[t]) for t in rows))
+            assert np.array_equal(zn[n], sum(k[t] for t in rows))
+        P, total = o.exclusive_scan(Sn)
+        assert np.array_equal(P[0], np.zeros((dk, dv)))
+        for n in range(1, N):
+            assert np.array_equal(P[n], Sn[:n].sum(axis=0))
+        assert np.array_equal(total, o.final_state(k, v)[0])
+        ref = o.causal_scores_first(q, k, v)
+        for n in range(N):
+            s, e = n * C, min((n + 1) * C, L)
+            blk = q[s:e] @ P[n] + o.tril(q[s:e] @ k[s:e].T) @ v[s:e]
+            assert np.array_equal(blk, ref[s:e]), (C, n)
+
+
+def check_brute_force_float(o, seed: int = 2) -> None:
+    """bf16-valued floats: the float64 forms match exact rational arithmetic to
+    float64 rounding, normalised and not."""
+    rng = np.random.default_rng([seed, 13])
+    L, dk, dv = 9, 3, 2
+    q, k, v = _bf16(rng, (L, dk)), _bf16(rng, (L, dk)), _bf16(rng, (L, dv))
+    qp, kp = o.phi_elu1(q), o.phi_elu1(k)
+    for normalize in (False, True):
+        exact = _frac_matrix(o.brute_force(qp, kp, v, causal=True, normalize=normalize))
+        forms = [o.causal_scores_first(qp, kp, v, normalize),
+                 o.causal_state_first(qp, kp, v, normalize)[0],
+                 o.causal_materialized_prefix(qp, kp, v, normalize)]
+        forms += [o.chunked(qp, kp, v, C, normalize)[0] for C in (1, 2, 4, 9)]
+        for f in forms:
+            assert np.allclose(f, exact, rtol=1e-12, atol=1e-12), (normalize, f, exact)
+        exact_nc = _frac_matrix(o.brute_force(qp, kp, v, causal=False, normalize=normalize))
+        assert np.allclose(o.noncausal_state_first(qp, kp, v, normalize), exact_nc, rtol=1e-12, atol=1e-12)
+        assert np.allclose(o.noncausal_scores_first(qp, kp, v, normalize), exact_nc, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# P-b: the two association orders (chunking page, section ①)
+# ---------------------------------------------------------------------------
+def check_association_orders(o, seed: int = 3) -> None:
+    rng = np.random.default_rng([seed, 14])
+    for L, dk, dv in ((4, 2, 2), (17, 6, 3), (40, 8, 8)):
+        q, k, v = _ints(rng, (L, dk)), _ints(rng, (L, dk)), _ints(rng, (L, dv))
+        a = o.noncausal_scores_first(q, k, v)
+        b = o.noncausal_state_first(q, k, v)
+        assert np.array_equal(a, b)
+        direct = np.array([[sum(int(q[i] @ k[j]) * int(v[j, c]) for j in range(L)) for c in range(dv)]
+                           for i in range(L)])
+        assert np.array_equal(a, direct)
+
+
+# ---------------------------------------------------------------------------
+# P-g, P-h, P-i, P-j: structural invariants
+# ---------------------------------------------------------------------------
+def check_last_row(o, seed: int = 4) -> None:
+    """The last causal row sees every token, so it equals the last non-causal row
+    (the page's printed pair shares its last row, [18 20])."""
+    rng = np.random.default_rng([seed, 15])
+    q, k, v = _ints(rng, (12, 3)), _ints(rng, (12, 3)), _ints(rng, (12, 4))
+    assert np.array_equal(o.causal_scores_first(q, k, v)[-1], o.noncausal_state_first(q, k, v)[-1])
+    qf, kf, vf = (_bf16(rng, (12, 3)), _bf16(rng, (12, 3)), _bf16(rng, (12, 4)))
+    qf, kf = o.phi_elu1(qf), o.phi_elu1(kf)
+    a = o.chunked(qf, kf, vf, 5, True)[0][-1]
+    b = o.noncausal_state_first(qf, kf, vf, True)[-1]
+    assert np.allclose(a, b, rtol=1e-12, atol=1e-14)
+
+
+def check_causality(o, seed: int = 5) -> None:
+    """Changing token t's q, k or v changes no output row before t."""
+    rng = np.random.default_rng([seed, 16])
+    L, dk, dv = 15, 3, 3
+    q, k, v = _ints(rng, (L, dk)), _ints(rng, (L, dk)), _ints(rng, (L, dv))
+    base = o.chunked(q, k, v, 4)[0]
+    for t in (0, 3, 4, 9, 14):
+        for which in range(3):
+            arrs = [q.copy(), k.copy(), v.copy()]
+            arrs[which][t] += 5
+            pert = o.chunked(*arrs, 4)[0]
+            assert np.array_equal(pert[:t], base[:t]), (t, which)
+    # and the diagonal is included: changing v_t changes row t when q_t . k_t != 0
+    q2, k2, v2 = q.copy(), k.copy(), v.copy()
+    q2[6] = k2[6] = np.array([1, 0, 0])
+    v3 = v2.copy()
+    v3[6] += 1
+    assert not np.array_equal(o.chunked(q2, k2, v2, 4)[0][6], o.chunked(q2, k2, v3, 4)[0][6])
+
+
+def check_linearity_and_normalised_cases(o, seed: int = 6) -> None:
+    """Unnormalised output is linear in v (exactly, on integers).  Normalised
+    output with positive features: o_0 = v_0, and each o_i lies coordinate-wise
+    within [min_{j<=i} v_j, max_{j<=i} v_j] (a convex combination of past values)."""
+    rng = np.random.default_rng([seed, 17])
+    L, dk, dv = 14, 3, 4
+    q, k = _ints(rng, (L, dk)), _ints(rng, (L, dk))
+    v1, v2 = _ints(rng, (L, dv)), _ints(rng, (L, dv))
+    for C in (1, 3, 14):
+        f = lambda vv: o.chunked(q, k, vv, C)[0]
+        assert np.array_equal(f(v1 + 2 * v2), f(v1) + 2 * f(v2))
+    qf, kf, vf = o.phi_elu1(_bf16(rng, (L, dk))), o.phi_elu1(_bf16(rng, (L, dk))), _bf16(rng, (L, dv))
+    for C in (1, 5, 14):
+        out = o.chunked(qf, kf, vf, C, True)[0]
+        assert np.allclose(out[0], vf[0], rtol=1e-14, atol=0)
+        for i in range(L):
+            lo, hi = vf[: i + 1].min(axis=0), vf[: i + 1].max(axis=0)
+            assert np.all(out[i] >= lo - 1e-12) and np.all(out[i] <= hi + 1e-12)
+
+
+def check_query_scale_invariance(o, seed: int = 7) -> None:
+    """Normalised output does not change when each phi(q_i) is multiplied by a
+    positive factor (so FAVOR+'s exp(-|q|^2/2)/sqrt(m) factor cancels)."""
+    rng = np.random.default_rng([seed, 18])
+    L, dk, dv = 11, 4, 3
+    qf, kf, vf = o.phi_elu1(_bf16(rng, (L, dk))), o.phi_elu1(_bf16(rng, (L, dk))), _bf16(rng, (L, dv))
+    s = np.exp(rng.standard_normal((L, 1)))
+    for C in (1, 4, 11):
+        a = o.chunked(qf, kf, vf, C, True)[0]
+        b = o.chunked(qf * s, kf, vf, C, True)[0]
+        assert np.allclose(a, b, rtol=1e-12, atol=1e-14)
+        # the unnormalised output does scale
+        a0 = o.chunked(qf, kf, vf, C, False)[0]
+        b0 = o.chunked(qf * s, kf, vf, C, False)[0]
+        assert np.allclose(b0, a0 * s, rtol=1e-12, atol=1e-14)
+
+
+def check_recurrent_vs_prefix_page_inputs(o) -> None:
+    """The linear-attention page checks its recurrent form against its
+    materialised-prefix form on inputs from numpy's legacy generator, seed 42,
+    n = 32, d_k = d_v = 16, scaled by 0.5, with elu+1 features and the
+    normaliser, and reports agreement to floating-point error."""
+    rs = np.random.RandomState(42)
+    Q = rs.randn(32, 16) * 0.5
+    K = rs.randn(32, 16) * 0.5
+    V = rs.randn(32, 16) * 0.5
+    qp, kp = o.phi_elu1(Q), o.phi_elu1(K)
+    rec = o.causal_state_first(qp, kp, V, True)[0]
+    par = o.causal_materialized_prefix(qp, kp, V, True)
+    assert np.max(np.abs(rec - par)) < 1e-12
+    quad = o.causal_scores_first(qp, kp, V, True)
+    assert np.max(np.abs(rec - quad)) < 1e-12
+
+
+def check_resume(o, seed: int = 8) -> None:
+    """Forward over the first L1 tokens, then token-by-token steps from its final
+    state, equals the forward over all L tokens (exact on integers)."""
+    rng = np.random.default_rng([seed, 19])
+    L, L1, dk, dv = 20, 13, 3, 5
+    q, k, v = _ints(rng, (L, dk)), _ints(rng, (L, dk)), _ints(rng, (L, dv))
+    full = o.chunked(q, k, v, 4)[0]
+    _, S, z = o.chunked(q[:L1], k[:L1], v[:L1], 4)
+    tail, _, _ = o.causal_state_first(q[L1:], k[L1:], v[L1:], False, S0=S, z0=z)
+    assert np.array_equal(tail, full[L1:])
+    # normalised decode steps on floats
+    qf, kf, vf = o.phi_elu1(_bf16(rng, (L, dk))), o.phi_elu1(_bf16(rng, (L, dk))), _bf16(rng, (L, dv))
+    fullf = o.chunked(qf, kf, vf, 6, True)[0]
+    _, S, z = o.chunked(qf[:L1], kf[:L1], vf[:L1], 6, True)
+    for t in range(L1, L):
+        ot, S, z = o.recurrent_step(S, z, qf[t], kf[t], vf[t], True)
+        assert np.allclose(ot, fullf[t], rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# P-l: feature maps against closed forms
+# ---------------------------------------------------------------------------
+def check_elu1(o) -> None:
+    x = np.array([-3.0, -1.0, -0.5, 0.0, 0.25, 1.0, 2.0])
+    want = np.array([math.exp(-3.0), math.exp(-1.0), math.exp(-0.5), 1.0, 1.25, 2.0, 3.0])
+    assert np.allclose(o.phi_elu1(x), want, rtol=1e-15, atol=0)
+    big = np.linspace(-20, 20, 4001)
+    assert np.all(o.phi_elu1(big) > 0)
+
+
+def check_favor_closed_form(o) -> None:
+    """phi(x)_l = exp(w_l.x - |x|^2/2)/sqrt(m), checked at hand-computed points."""
+    d, m = 3, 4
+    W = np.array([[1.0, 0, 0], [0, 1.0, 0], [0, 0, 1.0], [1.0, -1.0, 2.0]])
+    x0 = np.zeros(d)
+    assert np.allclose(o.phi_favor(x0, W), np.full(m, 0.5), rtol=1e-15)
+    x = np.array([1.0, 2.0, -1.0])  # |x|^2 / 2 = 3
+    want = np.array([math.exp(1 - 3), math.exp(2 - 3), math.exp(-1 - 3), math.exp((1 - 2 - 2) - 3)]) / 2.0
+    assert np.allclose(o.phi_favor(x, W), want, rtol=1e-15)
+    xs = np.stack([x0, x])
+    assert np.allclose(o.phi_favor(xs, W)[1], want, rtol=1e-15)
+
+
+def check_favor_convergence(o) -> None:
+    """phi(q).phi(k) is an unbiased estimate of exp(q.k) for Gaussian rows; with
+    many rows it converges (the page's moment-generating-function argument)."""
+    from workloads import orthogonal_random_features
+    q = np.array([0.3, -0.2, 0.1, 0.4])
+    k = np.array([-0.1, 0.5, 0.2, 0.3])
+    target = math.exp(float(q @ k))
+    rng = np.random.default_rng([9, 20])
+    W = rng.standard_normal((400000, 4))
+    est = float(o.phi_favor(q, W) @ o.phi_favor(k, W))
+    assert abs(est / target - 1) < 0.01, (est, target)
+    _, Wo = orthogonal_random_features(65536, 4, [9, 21])
+    est_o = float(o.phi_favor(q, Wo) @ o.phi_favor(k, Wo))
+    assert abs(est_o / target - 1) < 0.02, (est_o, target)
+    assert np.all(o.phi_favor(rng.standard_normal((10, 4)), W[:64]) > 0)

@@ -1,0 +1,63 @@
+"""The CPU oracle against what the pages and the mathematics fix (no GPU)."""
+import pytest
+
+import oracle
+from tests import oracle_pins as pins
+
+
+@pytest.mark.parametrize("L", [1, 2, 3])
+def test_exhaustive_tiny(L):
+    pins.check_exhaustive_tiny(oracle, L=L)
+
+
+def test_random_int_all_chunks():
+    for seed in range(3):
+        pins.check_random_int_all_chunks(oracle, seed)
+
+
+def test_chunk_phases():
+    pins.check_chunk_phases(oracle)
+
+
+def test_brute_force_float():
+    pins.check_brute_force_float(oracle)
+
+
+def test_association_orders():
+    pins.check_association_orders(oracle)
+
+
+def test_last_row():
+    pins.check_last_row(oracle)
+
+
+def test_causality():
+    pins.check_causality(oracle)
+
+
+def test_linearity_and_normalised_cases():
+    pins.check_linearity_and_normalised_cases(oracle)
+
+
+def test_query_scale_invariance():
+    pins.check_query_scale_invariance(oracle)
+
+
+def test_recurrent_vs_prefix_page_inputs():
+    pins.check_recurrent_vs_prefix_page_inputs(oracle)
+
+
+def test_resume():
+    pins.check_resume(oracle)
+
+
+def test_elu1():
+    pins.check_elu1(oracle)
+
+
+def test_favor_closed_form():
+    pins.check_favor_closed_form(oracle)
+
+
+def test_favor_convergence():
+    pins.check_favor_convergence(oracle)
