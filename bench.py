@@ -1,0 +1,273 @@
+#!/usr/bin/env python3
+"""Benchmark: chunked causal linear-attention forward on one MI355X.
+
+A step is one call of la_chunked_forward on one batch of synthetic input of
+the headline workload: B=8, H=16, L=8192, d_k=d_v=128, bf16, identity feature
+map, no normaliser, causal, chunk size C (default 64).  Inputs are resident in
+HBM before the timed region; W untimed warmup steps, then exactly K timed
+steps bracketed by device synchronisation, timed with HIP events on the
+stream the kernels run on.
+
+Prints one JSON line with the metric, the roofline of the dominant kernel and
+the CPU oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--chunk C] [--extra]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "chunked causal linear-attn forward tokens/sec and % MFMA peak, L=8192 d=128"
+PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_I8_TOPS = 5000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_chunked_fwd_bf16_identity-L8192-d128.json")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def lib_hash() -> str:
+    """Hash of the kernel sources the library is built from (ties measured
+    counters to the code they were taken on)."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "chunked_causal_linear_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def dev_bf16(bits):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def time_steps(fn, steps: int, warmup: int):
+    """Average ms per call over exactly `steps` calls (HIP events on the current stream)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def per_launch_ms(fn, steps: int):
+    """Per-call durations (ms) with an event pair around each call."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def cpu_baseline(w, C: int, budget_s: float = 10.0):
+    """The CPU oracle's chunked form, as it stands, on whole heads of the
+    workload at full L, head after head until about `budget_s` seconds of CPU
+    work; tokens/s extrapolated linearly over the heads."""
+    import oracle
+    import workloads as wl
+    cores = len(os.sched_getaffinity(0))
+    elapsed, heads = 0.0, 0
+    while elapsed < budget_s and heads < w.BH:
+        q, k, v = wl.head_inputs(w, heads)  # input generation is not timed
+        t1 = time.perf_counter()
+        oracle.chunked(q.exact, k.exact, v.exact, C, w.normalize)
+        elapsed += time.perf_counter() - t1
+        heads += 1
+    per_head = elapsed / heads
+    tokens_per_s = w.L / (w.H * per_head)  # B*L tokens take B*H head passes
+    return {"value": tokens_per_s, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"oracle.chunked (numpy float64, C={C}) on {heads} of {w.BH} heads at full L={w.L} "
+                      f"({elapsed:.1f} s); {per_head:.3f} s per head, extrapolated over all heads",
+            "cpu": platform.processor() or platform.machine()}
+
+
+def run_headline(args):
+    import numpy as np
+    import torch
+
+    import chunked_causal_linear_amd as la
+    import workloads as wl
+    from chunked_causal_linear_amd.accounting import Work
+
+    w = wl.WORKLOADS[3]
+    C = args.chunk
+    log(f"generating workload {w.name} (B={w.B} H={w.H} L={w.L} d={w.d_in})")
+    q, k, v, _ = wl.workload_inputs(w, want_exact=False)
+    qd, kd, vd = dev_bf16(q.bits), dev_bf16(k.bits), dev_bf16(v.bits)
+    del q, k, v
+    fwd = la.Forward(qd, kd, vd, C, causal=True, normalize=False, fmap="identity", group=args.group)
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup}, timing {args.steps} steps, C={C}, workspace {fwd.ws_bytes} B")
+    ms = time_steps(fwd.run, args.steps, args.warmup)
+    per = per_launch_ms(fwd.run, min(args.steps, 20))
+    work = Work(w.BH, w.L, w.d_in, w.d_k, w.d_v, C)
+    tokens = w.B * w.L
+    flops = work.page_flops()
+    useful = 2 * work.causal_useful_macs()
+    alg_bytes = work.fused_bytes()
+    sec = ms * 1e-3
+    # single-launch plan: the forward is one kernel, so its event time is the kernel's
+    kern_ms = float(np.mean(per))
+    achieved_gbs = alg_bytes / (kern_ms * 1e-3) / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        tr = json.load(open(TRAFFIC_FILE))
+        if tr.get("lib_hash") == lib_hash() and tr.get("chunk") == C:
+            traffic = tr.get("bytes_per_launch")
+    res = {
+        "metric": METRIC,
+        "value": tokens / sec,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: B={w.B} H={w.H} L={w.L} d_k=d_v={w.d_in} bf16, identity map, "
+                               f"no normaliser, causal, C={C}",
+                   "B": w.B, "H": w.H, "L": w.L, "d": w.d_in, "C": C, "parallelism": "single-gpu"},
+        "tflops_page_count": flops / sec / 1e12,
+        "mfma_frac_page_count": flops / sec / 1e12 / PEAK_BF16_TFLOPS,
+        "tflops_causal_useful": useful / sec / 1e12,
+        "head_tokens_per_s": w.BH * w.L / sec,
+        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved_gbs / PEAK_HBM_GBS, "traffic": traffic,
+                     "kernel": "chunked_fwd_bf16", "alg_bytes_per_launch": alg_bytes,
+                     "avg_launch_ms": kern_ms},
+    }
+    return res, fwd
+
+
+def run_extras(args, out):
+    """Other workloads and chunk sizes, each timed separately (not the headline)."""
+    import torch
+
+    import chunked_causal_linear_amd as la
+    import workloads as wl
+    from chunked_causal_linear_amd.accounting import Work, decode_bytes
+
+    extras = {}
+    w3 = wl.WORKLOADS[3]
+    q, k, v, _ = wl.workload_inputs(w3, want_exact=False)
+    qd, kd, vd = dev_bf16(q.bits), dev_bf16(k.bits), dev_bf16(v.bits)
+    del q, k, v
+    for C in (32, 64, 128):
+        for g in (0, 32):
+            f = la.Forward(qd, kd, vd, C, group=g)
+            ms = time_steps(f.run, 10, 3)
+            wk = Work(w3.BH, w3.L, w3.d_in, w3.d_k, w3.d_v, C)
+            extras[f"w3_C{C}_group{g}"] = {"ms": ms, "tokens_per_s": w3.B * w3.L / (ms * 1e-3),
+                                           "hbm_frac": wk.fused_bytes() / (ms * 1e-3) / 8e12,
+                                           "tflops": wk.page_flops() / (ms * 1e-3) / 1e12}
+            del f
+    # int8 at the headline shape
+    qi, ki, vi = wl.random_case(33, w3.BH, w3.L, 128, 128, "i8")
+    tq, tk, tv = (torch.from_numpy(x.bits).cuda() for x in (qi, ki, vi))
+    del qi, ki, vi
+    f = la.Forward(tq, tk, tv, 64)
+    ms = time_steps(f.run, 10, 3)
+    wk = Work(w3.BH, w3.L, 128, 128, 128, 64, in_bytes=1, out_bytes=4)
+    extras["w3_int8_C64"] = {"ms": ms, "tokens_per_s": w3.B * w3.L / (ms * 1e-3),
+                             "tops": wk.page_flops() / (ms * 1e-3) / 1e12,
+                             "hbm_frac": wk.fused_bytes() / (ms * 1e-3) / 8e12}
+    del f, tq, tk, tv, qd, kd, vd
+    torch.cuda.empty_cache()
+    for wid in (2, 4, 5):
+        w = wl.WORKLOADS[wid]
+        q, k, v, W = wl.workload_inputs(w, want_exact=False)
+        qd, kd, vd = dev_bf16(q.bits), dev_bf16(k.bits), dev_bf16(v.bits)
+        Wd = dev_bf16(W[0]) if W is not None else None
+        C = w.chunks[0]
+        f = la.Forward(qd, kd, vd, C, normalize=w.normalize, fmap=w.fmap, W=Wd, return_state=w.return_state)
+        ms = time_steps(f.run, 10, 3)
+        wk = Work(w.BH, w.L, w.d_in, w.d_k, w.d_v, C, w.normalize, w.fmap)
+        extras[f"w{wid}"] = {"workload": w.name, "ms": ms, "tokens_per_s": w.B * w.L / (ms * 1e-3),
+                             "hbm_frac_fused_bytes": wk.fused_bytes(w.return_state) / (ms * 1e-3) / 8e12,
+                             "tflops": wk.page_flops() / (ms * 1e-3) / 1e12}
+        if wid == 5:
+            n = wl.DECODE_STREAMS * w.H
+            idx = torch.tensor([(s % w.B) * w.H + h for s in range(wl.DECODE_STREAMS) for h in range(w.H)],
+                               device="cuda")
+            S = f.S_final[idx].contiguous()
+            z = f.z_final[idx].contiguous()
+            pq, pk, pv = wl.decode_pool(w, n, pool=wl.DECODE_POOL)
+            dq, dk_, dv_ = dev_bf16(pq.bits), dev_bf16(pk.bits), dev_bf16(pv.bits)
+            o = torch.empty(n, w.d_v, dtype=torch.float32, device="cuda")
+            steps = args.decode_steps
+            state = {"t": 0}
+
+            def step():
+                t = state["t"] % wl.DECODE_POOL
+                la.recurrent_step(dq[t], dk_[t], dv_[t], S, z, fmap="favor", W=Wd, normalize=True, out=o)
+                state["t"] += 1
+            ms_d = time_steps(step, steps, 8)
+            db = decode_bytes(n, w.d_in, w.d_k, w.d_v, True, m_proj=w.m)
+            extras["w5_decode"] = {"states": n, "steps": steps, "ms_per_step": ms_d,
+                                   "tokens_per_s": wl.DECODE_STREAMS / (ms_d * 1e-3),
+                                   "effective_GBs": db / (ms_d * 1e-3) / 1e9,
+                                   "note": "state set 201 MB fits the 256 MB Infinity Cache; effective bandwidth"}
+        del f, qd, kd, vd
+        torch.cuda.empty_cache()
+    out["extras"] = extras
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--chunk", type=int, default=64)
+    ap.add_argument("--group", type=int, default=0)
+    ap.add_argument("--extra", action="store_true", help="also time the other workloads and chunk sizes")
+    ap.add_argument("--decode-steps", type=int, default=4096)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); this build has no multi-GPU path",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    res, fwd = run_headline(args)
+    del fwd
+    torch.cuda.empty_cache()
+    if args.extra:
+        run_extras(args, res)
+    if not args.no_cpu_baseline:
+        import workloads as wl
+        log("timing the CPU oracle on a bounded sample")
+        res["cpu_baseline"] = cpu_baseline(wl.WORKLOADS[3], args.chunk)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

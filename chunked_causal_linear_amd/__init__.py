@@ -1,0 +1,14 @@
+"""chunked_causal_linear_amd - chunkwise-parallel causal linear attention on MI355X.
+
+The compute path is ``liblinattn.so`` (hand-written HIP for gfx950) behind the
+C ABI in ``include/la.h``; ``binding`` marshals torch tensors into it.  The
+library is loaded on first use; calling any entry point without it raises
+``LibraryNotBuilt``.
+"""
+from .binding import (  # noqa: F401
+    EXPORTS, FMAPS, LAError, LibraryNotBuilt, Forward, chunk_states, chunked_forward, feature_map,
+    forward_workspace_bytes, lib, recurrent_step, state_scan,
+)
+
+__all__ = ["chunked_forward", "Forward", "chunk_states", "state_scan", "feature_map", "recurrent_step",
+           "forward_workspace_bytes", "lib", "LAError", "LibraryNotBuilt", "EXPORTS", "FMAPS"]

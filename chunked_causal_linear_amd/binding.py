@@ -1,0 +1,242 @@
+"""Thin Python binding of liblinattn's C ABI (``include/la.h``).
+
+Argument marshalling only: every wrapper checks the torch tensors it is handed
+(device, dtype, shape, contiguity), passes their device pointers and the
+current HIP stream to the library, and raises on a non-OK status.  All the
+arithmetic runs in the library's HIP kernels; there is no fallback.  The
+library is loaded on first use and a missing or unloadable library raises
+``LibraryNotBuilt``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "liblinattn.so")
+
+# la_status
+LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_HIP, LA_ERR_WORKSPACE = range(5)
+# la_dtype
+LA_BF16, LA_F32, LA_I8, LA_I32 = range(4)
+# la_fmap
+FMAPS = {"identity": 0, "elu1": 1, "favor": 2}
+
+EXPORTS = (
+    "la_feature_map", "la_chunk_states", "la_state_scan", "la_chunked_forward",
+    "la_chunked_forward_workspace", "la_recurrent_step", "la_status_string", "la_last_error",
+    "la_version",
+)
+
+
+class LibraryNotBuilt(RuntimeError):
+    pass
+
+
+class LAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"liblinattn status {status}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def _declare(lib: ctypes.CDLL) -> None:
+    i64, f32, vp, i32, sz = ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.la_feature_map.argtypes = [i32, vp, i32, i64, i64, vp, i64, f32, vp, i32, vp]
+    lib.la_chunk_states.argtypes = [vp, vp, i32, i64, i64, i64, i64, i64, vp, vp, vp]
+    lib.la_state_scan.argtypes = [vp, vp, i32, i64, i64, i64, i64, vp, vp, vp]
+    lib.la_chunked_forward.argtypes = [vp, vp, vp, i32, i64, i64, i64, i64, i64, i32, i32, i32, vp, i64, f32,
+                                       vp, i32, vp, vp, i64, vp, sz, vp]
+    lib.la_chunked_forward_workspace.argtypes = [i32, i64, i64, i64, i64, i64, i32, i32, i32, i64, f32, i64]
+    lib.la_chunked_forward_workspace.restype = sz
+    lib.la_recurrent_step.argtypes = [vp, vp, vp, i32, i64, i64, i64, i32, vp, i64, f32, i32, vp, vp, vp, i32, vp]
+    for name in ("la_feature_map", "la_chunk_states", "la_state_scan", "la_chunked_forward", "la_recurrent_step"):
+        getattr(lib, name).restype = i32
+    lib.la_status_string.argtypes = [i32]
+    lib.la_status_string.restype = ctypes.c_char_p
+    lib.la_last_error.argtypes = []
+    lib.la_last_error.restype = ctypes.c_char_p
+    lib.la_version.argtypes = []
+    lib.la_version.restype = i32
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (loads it on first call)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise LibraryNotBuilt(f"{LIB_PATH} is missing: build it with "
+                                  "`python -m chunked_causal_linear_amd.build`")
+        try:
+            handle = ctypes.CDLL(LIB_PATH)
+        except OSError as e:
+            raise LibraryNotBuilt(f"cannot load {LIB_PATH}: {e}") from e
+        _declare(handle)
+        _lib = handle
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != LA_OK:
+        msg = lib().la_last_error().decode("utf-8", "replace")
+        raise LAError(status, msg or lib().la_status_string(status).decode())
+
+
+# ---------------------------------------------------------------------------
+# torch helpers (device memory and streams only)
+# ---------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr() -> int:
+    torch = _torch()
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    m = {torch.bfloat16: LA_BF16, torch.float32: LA_F32, torch.int8: LA_I8, torch.int32: LA_I32}
+    if t.dtype not in m:
+        raise TypeError(f"unsupported tensor dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def _dev(t, name: str):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _fmap_code(fmap: str) -> int:
+    if fmap not in FMAPS:
+        raise ValueError(f"fmap must be one of {sorted(FMAPS)}")
+    return FMAPS[fmap]
+
+
+# ---------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------
+def feature_map(x, fmap: str, W=None, in_scale: float = 1.0, out_dtype=None):
+    """phi(in_scale * x) row by row; x [..., d_in] bf16 -> [..., d_k]."""
+    torch = _torch()
+    d_in = x.shape[-1]
+    rows = x.numel() // d_in
+    m = W.shape[0] if (fmap == "favor" and W is not None) else 0
+    d_k = m if fmap == "favor" else d_in
+    y = torch.empty(*x.shape[:-1], d_k, dtype=out_dtype or torch.bfloat16, device=x.device)
+    _check(lib().la_feature_map(_fmap_code(fmap), _dev(x, "x"), _dtype_code(x), rows, d_in,
+                                _dev(W, "W"), m, float(in_scale), _dev(y, "y"), _dtype_code(y), _stream_ptr()))
+    return y
+
+
+def chunk_states(k, v, C: int, want_z: bool = False):
+    """Phase 1: per-chunk states S [BH, N, d_k, d_v] (and z [BH, N, d_k])."""
+    torch = _torch()
+    BH, L, d_k = k.shape
+    d_v = v.shape[-1]
+    Cs = 1 if C <= 0 else min(C, L)
+    N = (L + Cs - 1) // Cs
+    st = torch.int32 if k.dtype == torch.int8 else torch.float32
+    S = torch.empty(BH, N, d_k, d_v, dtype=st, device=k.device)
+    z = torch.empty(BH, N, d_k, dtype=st, device=k.device) if want_z else None
+    _check(lib().la_chunk_states(_dev(k, "k"), _dev(v, "v"), _dtype_code(k), BH, L, d_k, d_v, C,
+                                 _dev(S, "S"), _dev(z, "z"), _stream_ptr()))
+    return S, z
+
+
+def state_scan(S, z=None, want_final: bool = True):
+    """Phase 2, in place: S (and z) become exclusive prefixes; returns (S_final, z_final)."""
+    torch = _torch()
+    BH, N, d_k, d_v = S.shape
+    Sf = torch.empty(BH, d_k, d_v, dtype=S.dtype, device=S.device) if want_final else None
+    zf = torch.empty(BH, d_k, dtype=S.dtype, device=S.device) if (want_final and z is not None) else None
+    _check(lib().la_state_scan(_dev(S, "S"), _dev(z, "z"), _dtype_code(S), BH, N, d_k, d_v,
+                               _dev(Sf, "S_final"), _dev(zf, "z_final"), _stream_ptr()))
+    return Sf, zf
+
+
+def forward_workspace_bytes(in_dtype_code: int, BH: int, L: int, d_in: int, d_v: int, C: int, causal: bool,
+                            normalize: bool, fmap: str, m: int = 0, in_scale: float = 1.0, group: int = 0) -> int:
+    return int(lib().la_chunked_forward_workspace(in_dtype_code, BH, L, d_in, d_v, C, int(causal), int(normalize),
+                                                  _fmap_code(fmap), m, float(in_scale), group))
+
+
+class Forward:
+    """A planned forward call with its output, final-state and workspace buffers.
+
+    Allocate once (``__init__``), then ``run()`` enqueues only the library's
+    kernels on the current stream - the form the benchmark times.
+    """
+
+    def __init__(self, q, k, v, C: int, causal: bool = True, normalize: bool = False, fmap: str = "identity",
+                 W=None, in_scale: float = 1.0, out_dtype=None, return_state: bool = False, group: int = 0):
+        torch = _torch()
+        self.q, self.k, self.v, self.W = q, k, v, W
+        BH, L, d_in = q.shape
+        d_v = v.shape[-1]
+        self.m = W.shape[0] if (fmap == "favor" and W is not None) else 0
+        d_k = self.m if fmap == "favor" else d_in
+        self.shape = (BH, L, d_in, d_v, d_k)
+        self.C, self.causal, self.normalize, self.fmap = C, causal, normalize, fmap
+        self.in_scale, self.group = float(in_scale), group
+        i8 = q.dtype == torch.int8
+        if out_dtype is None:
+            out_dtype = torch.int32 if i8 else torch.bfloat16
+        self.o = torch.empty(BH, L, d_v, dtype=out_dtype, device=q.device)
+        st = torch.int32 if i8 else torch.float32
+        self.S_final = torch.empty(BH, d_k, d_v, dtype=st, device=q.device) if return_state else None
+        self.z_final = (torch.empty(BH, d_k, dtype=torch.float32, device=q.device)
+                        if (return_state and normalize) else None)
+        ws = forward_workspace_bytes(_dtype_code(q), BH, L, d_in, d_v, C, causal, normalize, fmap, self.m,
+                                     self.in_scale, group)
+        self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=q.device)
+        self.ws_bytes = ws
+        for name, t in (("q", q), ("k", k), ("v", v), ("W", W)):
+            _dev(t, name)
+
+    def run(self):
+        BH, L, d_in, d_v, _ = self.shape
+        _check(lib().la_chunked_forward(
+            self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), _dtype_code(self.q), BH, L, d_in, d_v,
+            self.C, int(self.causal), int(self.normalize), _fmap_code(self.fmap),
+            self.W.data_ptr() if self.W is not None else None, self.m, self.in_scale,
+            self.o.data_ptr(), _dtype_code(self.o),
+            self.S_final.data_ptr() if self.S_final is not None else None,
+            self.z_final.data_ptr() if self.z_final is not None else None,
+            self.group, self.workspace.data_ptr(), self.ws_bytes, _stream_ptr()))
+        return self.o
+
+
+def chunked_forward(q, k, v, C: int, causal: bool = True, normalize: bool = False, fmap: str = "identity",
+                    W=None, in_scale: float = 1.0, out_dtype=None, return_state: bool = False,
+                    group: int = 0) -> Tuple:
+    """O (and, with return_state, the final S and z) of the chunked forward."""
+    f = Forward(q, k, v, C, causal, normalize, fmap, W, in_scale, out_dtype, return_state, group)
+    o = f.run()
+    if return_state:
+        return o, f.S_final, f.z_final
+    return o
+
+
+def recurrent_step(q, k, v, S, z=None, fmap: str = "identity", W=None, in_scale: float = 1.0,
+                   normalize: bool = True, out=None):
+    """One decode step over n states; S [n, d_k, d_v] and z [n, d_k] (fp32) update in place."""
+    torch = _torch()
+    n, d_in = q.shape
+    d_v = v.shape[-1]
+    m = W.shape[0] if (fmap == "favor" and W is not None) else 0
+    if out is None:
+        out = torch.empty(n, d_v, dtype=torch.float32, device=q.device)
+    _check(lib().la_recurrent_step(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dtype_code(q), n, d_in, d_v,
+                                   _fmap_code(fmap), _dev(W, "W"), m, float(in_scale), int(normalize),
+                                   _dev(S, "S"), _dev(z, "z"), _dev(out, "o"), _dtype_code(out), _stream_ptr()))
+    return out

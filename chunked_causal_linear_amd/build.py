@@ -1,0 +1,102 @@
+"""Build liblinattn.so (HIP, gfx950) in-tree.
+
+Compiles every ``csrc/*.hip`` translation unit with hipcc in parallel into
+``_build/`` and links ``chunked_causal_linear_amd/liblinattn.so``.  The build
+runs on a machine without a GPU (hipcc cross-compiles for gfx950).
+
+    python -m chunked_causal_linear_amd.build            # rebuild everything
+    python -m chunked_causal_linear_amd.build --changed  # only stale objects
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+import time
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "liblinattn.so")
+ROOT = os.path.dirname(PKG)
+INCLUDE = os.path.join(ROOT, "include")
+
+ARCH = "gfx950"
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+# -packed-fp32-ops: keep the compiler from emitting packed fp32 vector ops.
+CFLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-I" + INCLUDE, "-I" + CSRC,
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def _sources():
+    return sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
+
+
+def _headers_mtime() -> float:
+    hs = [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hpp")]
+    hs.append(os.path.join(INCLUDE, "la.h"))
+    return max(os.path.getmtime(h) for h in hs)
+
+
+def _compile(src: str) -> tuple:
+    obj = os.path.join(BUILD, src[:-4] + ".o")
+    cmd = [HIPCC] + CFLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    t0 = time.time()
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    # hipcc's host pass does not know the packed-fp32 feature; that warning is harmless
+    err = "\n".join(l for l in (r.stderr or "").splitlines() if "packed-fp32-ops" not in l)
+    return src, r.returncode, err, time.time() - t0
+
+
+def build(changed_only: bool = False, jobs: int = None, verbose: bool = True) -> str:
+    if shutil.which(HIPCC) is None and not os.path.exists(HIPCC):
+        raise RuntimeError(f"hipcc not found at {HIPCC}")
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = _sources()
+    todo = []
+    hdr_t = _headers_mtime()
+    for s in srcs:
+        obj = os.path.join(BUILD, s[:-4] + ".o")
+        if changed_only and os.path.exists(obj):
+            ot = os.path.getmtime(obj)
+            if ot >= os.path.getmtime(os.path.join(CSRC, s)) and ot >= hdr_t:
+                continue
+        todo.append(s)
+    jobs = jobs or min(len(todo) or 1, max(1, (os.cpu_count() or 4)))
+    failed = []
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        for src, rc, err, dt in ex.map(_compile, todo):
+            if verbose:
+                print(f"[build] {src}: {'ok' if rc == 0 else 'FAILED'} ({dt:.1f}s)", flush=True)
+            if rc != 0:
+                failed.append((src, err))
+            elif err.strip() and verbose:
+                print(err, flush=True)
+    if failed:
+        msg = "\n".join(f"--- {s}\n{e}" for s, e in failed)
+        raise RuntimeError("HIP build failed:\n" + msg)
+    objs = [os.path.join(BUILD, s[:-4] + ".o") for s in srcs]
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n" + r.stderr)
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"[build] linked {LIB}", flush=True)
+    return LIB
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--changed", action="store_true", help="recompile only stale objects")
+    ap.add_argument("-j", type=int, default=None)
+    a = ap.parse_args(argv)
+    build(changed_only=a.changed, jobs=a.j)
+
+
+if __name__ == "__main__":
+    sys.exit(main())

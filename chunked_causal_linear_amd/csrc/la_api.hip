@@ -1,0 +1,500 @@
+// liblinattn C ABI: argument checks, planning (tile sizes, groups, workspace)
+// and launches.  Every entry point validates everything before it enqueues
+// anything, never allocates, never synchronises, and never throws.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/la.h"
+#include "la_chunked_bf16.hpp"
+#include "la_kernels.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+la_status fail(la_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+la_status hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return LA_OK;
+    return fail(LA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool pow2_in(int64_t x, int64_t lo, int64_t hi) {
+    if (x < lo || x > hi) return false;
+    return (x & (x - 1)) == 0;
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// ---------------------------------------------------------------------------
+// tile choices
+// ---------------------------------------------------------------------------
+int kernel_dk_bf16(int64_t dk) { return dk <= 32 ? 32 : (int)dk; }
+int kernel_dk_i8(int64_t dk) { return dk <= 64 ? 64 : (int)dk; }
+int kernel_dvt(int64_t dv) { return dv >= 64 ? 64 : (int)dv; }
+
+// largest row tile compiled for (DK, DVT); the hi/lo split of phi(K) (elu+1
+// in the kernel) needs one more K^T tile of LDS
+int max_tile_bf16(int DK, int DVT, bool split) {
+    if (DK <= 64) return 128;
+    if (DK == 128) return (DVT == 16 || split) ? 64 : 128;
+    return DVT == 16 ? 32 : 64;  // DK == 256
+}
+
+int tile_bf16(int64_t C, int DK, int DVT, bool split) {
+    int T = C <= 32 ? 32 : (C <= 64 ? 64 : 128);
+    const int tmax = max_tile_bf16(DK, DVT, split);
+    return T < tmax ? T : tmax;
+}
+
+int tile_i8(int64_t C, int DK, int DVT) {
+    const bool has128 = (DK == 64) || (DK == 128 && DVT == 64);
+    return (C > 64 && has128) ? 128 : 64;
+}
+
+// ---------------------------------------------------------------------------
+// forward plan
+// ---------------------------------------------------------------------------
+struct Plan {
+    bool i8;
+    int64_t BH, L, C, dk, dv, d_in;
+    int64_t n_chunks, G, n_groups;
+    int DK, DVT, T, n_dvt;
+    bool premap;  // phi computed by a separate pass into the workspace
+    bool causal, normalize;
+    size_t ws_phi;     // bytes of one mapped q or k copy
+    size_t ws_states;  // bytes of the group states
+    size_t ws_z;
+    size_t ws_total;
+};
+
+la_status check_dtypes_forward(la_dtype in_dt, la_dtype out_dt, int normalize, la_fmap f, float in_scale) {
+    if (in_dt == LA_BF16) {
+        if (out_dt != LA_BF16 && out_dt != LA_F32)
+            return fail(LA_ERR_UNSUPPORTED, "bf16 inputs need an LA_BF16 or LA_F32 output");
+        return LA_OK;
+    }
+    if (in_dt == LA_I8) {
+        if (normalize) return fail(LA_ERR_UNSUPPORTED, "the int8 path has no normaliser");
+        if (in_scale != 1.0f) return fail(LA_ERR_UNSUPPORTED, "the int8 path has no input scale");
+        if (f != LA_FMAP_IDENTITY) return fail(LA_ERR_UNSUPPORTED, "the int8 path has no feature map");
+        if (out_dt != LA_I32) return fail(LA_ERR_UNSUPPORTED, "int8 inputs need an LA_I32 output");
+        return LA_OK;
+    }
+    return fail(LA_ERR_UNSUPPORTED, "input type must be LA_BF16 or LA_I8");
+}
+
+la_status make_plan(Plan& P, la_dtype in_dt, int64_t BH, int64_t L, int64_t d_in, int64_t d_v, int64_t C,
+                    int causal, int normalize, la_fmap f, int64_t m, float in_scale, int64_t group) {
+    if (BH < 1 || L < 1 || d_in < 1 || d_v < 1) return fail(LA_ERR_INVALID_ARG, "sizes must be positive");
+    if (f != LA_FMAP_IDENTITY && f != LA_FMAP_ELU1 && f != LA_FMAP_FAVOR)
+        return fail(LA_ERR_INVALID_ARG, "unknown feature map %d", (int)f);
+    if (!(in_scale == in_scale)) return fail(LA_ERR_INVALID_ARG, "in_scale is NaN");
+    P.i8 = in_dt == LA_I8;
+    P.BH = BH;
+    P.L = L;
+    P.d_in = d_in;
+    P.dv = d_v;
+    P.causal = causal != 0;
+    P.normalize = normalize != 0;
+    P.dk = f == LA_FMAP_FAVOR ? m : d_in;
+    if (f == LA_FMAP_FAVOR) {
+        if (!pow2_in(m, 16, 256)) return fail(LA_ERR_UNSUPPORTED, "FAVOR+ feature count m must be 16..256, a power of two");
+        if (!pow2_in(d_in, 16, 128)) return fail(LA_ERR_UNSUPPORTED, "FAVOR+ input width must be 16..128, a power of two");
+    }
+    if (!pow2_in(P.dk, 16, 256)) return fail(LA_ERR_UNSUPPORTED, "feature width d_k=%lld unsupported (16..256, power of two)", (long long)P.dk);
+    if (!pow2_in(d_v, 16, 256)) return fail(LA_ERR_UNSUPPORTED, "value width d_v=%lld unsupported (16..256, power of two)", (long long)d_v);
+    if (BH * L > ((int64_t)1 << 40)) return fail(LA_ERR_UNSUPPORTED, "problem too large");
+
+    int64_t Ce = C <= 0 ? 1 : C;
+    if (Ce > L) Ce = L;  // one chunk
+    // FAVOR+ maps q and k in a separate pass; elu+1 is applied while loading;
+    // the identity map with a scale s runs unscaled and scales the results
+    // (outputs by s^2 unless normalised, the final state by s), which is exact.
+    P.premap = f == LA_FMAP_FAVOR;
+    P.DVT = kernel_dvt(d_v);
+    P.n_dvt = (int)(d_v / P.DVT);
+    if (P.i8) {
+        P.DK = kernel_dk_i8(P.dk);
+    } else {
+        P.DK = kernel_dk_bf16(P.dk);
+    }
+
+    if (!P.causal) {
+        // total state from one chunk of L rows, then every tile reads it
+        P.T = 64;
+        if (!P.i8 && P.T > max_tile_bf16(P.DK, P.DVT, false)) P.T = max_tile_bf16(P.DK, P.DVT, false);
+        P.C = P.T;
+        P.n_chunks = cdiv(L, P.C);
+        P.G = 1;
+        P.n_groups = P.n_chunks;
+    } else {
+        P.C = Ce;
+        P.T = P.i8 ? tile_i8(Ce, P.DK, P.DVT) : tile_bf16(Ce, P.DK, P.DVT, f == LA_FMAP_ELU1);
+        P.n_chunks = cdiv(L, Ce);
+        if (group > 0) {
+            P.G = group < P.n_chunks ? group : P.n_chunks;
+        } else {
+            // enough workgroups to cover the 256 compute units, otherwise one
+            // sequential walk per (head, column tile)
+            const int64_t base = BH * P.n_dvt;
+            int64_t want = base >= 256 ? 1 : cdiv(256, base);
+            if (want > P.n_chunks) want = P.n_chunks;
+            P.G = cdiv(P.n_chunks, want);
+        }
+        P.n_groups = cdiv(P.n_chunks, P.G);
+    }
+    const int64_t grid = BH * P.n_groups * P.n_dvt;
+    if (grid > 0x7FFFFFFFLL) return fail(LA_ERR_UNSUPPORTED, "grid too large");
+
+    const size_t st_elem = 4;
+    P.ws_phi = P.premap ? align256((size_t)BH * L * P.dk * 2) : 0;
+    const int64_t n_state_slots = P.causal ? (P.n_groups > 1 ? P.n_groups : 0) : 1;
+    P.ws_states = align256((size_t)BH * n_state_slots * P.dk * d_v * st_elem);
+    P.ws_z = (P.normalize && n_state_slots) ? align256((size_t)BH * n_state_slots * P.dk * st_elem) : 0;
+    if (n_state_slots == 0) P.ws_states = 0;
+    // FAVOR+: phi(q), phi(k) and the bf16 residual of phi(k) (the state sums
+    // use hi + lo, so the bf16 rounding of phi does not accumulate over L)
+    P.ws_total = 3 * P.ws_phi + P.ws_states + P.ws_z;
+    return LA_OK;
+}
+
+bool xcd_ok(int64_t grid) { return grid >= 8 && grid % 8 == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* la_status_string(la_status s) {
+    switch (s) {
+        case LA_OK: return "ok";
+        case LA_ERR_INVALID_ARG: return "invalid argument";
+        case LA_ERR_UNSUPPORTED: return "unsupported";
+        case LA_ERR_HIP: return "HIP runtime error";
+        case LA_ERR_WORKSPACE: return "workspace missing or too small";
+    }
+    return "unknown status";
+}
+
+const char* la_last_error(void) { return g_last_error; }
+
+int la_version(void) { return 100; }
+
+// ---------------------------------------------------------------------------
+la_status la_feature_map(la_fmap f, const void* x, la_dtype xdt, int64_t rows, int64_t d_in, const void* W,
+                         int64_t m, float in_scale, void* y, la_dtype ydt, la_stream_t stream) {
+    g_last_error[0] = 0;
+    if (x == nullptr || y == nullptr) return fail(LA_ERR_INVALID_ARG, "x and y must not be NULL");
+    if (rows < 1 || d_in < 1) return fail(LA_ERR_INVALID_ARG, "rows and d_in must be positive");
+    if (xdt != LA_BF16) return fail(LA_ERR_UNSUPPORTED, "x must be LA_BF16");
+    if (ydt != LA_BF16 && ydt != LA_F32) return fail(LA_ERR_UNSUPPORTED, "y must be LA_BF16 or LA_F32");
+    if (!(in_scale == in_scale)) return fail(LA_ERR_INVALID_ARG, "in_scale is NaN");
+    la::FmapParams p{};
+    p.x = static_cast<const unsigned short*>(x);
+    p.y = y;
+    p.rows = rows;
+    p.d_in = (int)d_in;
+    p.in_scale = in_scale;
+    p.y_f32 = ydt == LA_F32;
+    if (f == LA_FMAP_FAVOR) {
+        if (W == nullptr) return fail(LA_ERR_INVALID_ARG, "FAVOR+ needs W");
+        if (!pow2_in(m, 16, 256)) return fail(LA_ERR_UNSUPPORTED, "m must be 16..256, a power of two");
+        if (!pow2_in(d_in, 16, 128)) return fail(LA_ERR_UNSUPPORTED, "d_in must be 16..128, a power of two");
+        p.W = static_cast<const unsigned short*>(W);
+        p.m = (int)m;
+        p.fmap = 2;
+    } else if (f == LA_FMAP_ELU1 || f == LA_FMAP_IDENTITY) {
+        if (d_in % 8 != 0) return fail(LA_ERR_UNSUPPORTED, "d_in must be a multiple of 8");
+        p.fmap = f == LA_FMAP_ELU1 ? 1 : 0;
+    } else {
+        return fail(LA_ERR_INVALID_ARG, "unknown feature map %d", (int)f);
+    }
+    return hip_status(la::run_feature_map(p, (hipStream_t)stream), "la_feature_map launch");
+}
+
+// ---------------------------------------------------------------------------
+static la_status chunk_states_impl(const void* k, const void* v, bool i8, int64_t BH, int64_t L, int64_t d_k,
+                                   int64_t d_v, int64_t Cs, int n_items, int n_out, void* S, void* z, int fmap,
+                                   float in_scale, hipStream_t s, const void* k_lo = nullptr) {
+    const int DVT = kernel_dvt(d_v);
+    const int n_dvt = (int)(d_v / DVT);
+    const int64_t grid = BH * (int64_t)n_items * n_dvt;
+    if (grid > 0x7FFFFFFFLL) return fail(LA_ERR_UNSUPPORTED, "grid too large");
+    if (grid == 0) return LA_OK;
+    if (i8) {
+        la::StatesParamsI8 p{};
+        p.k = static_cast<const signed char*>(k);
+        p.v = static_cast<const signed char*>(v);
+        p.S = static_cast<int*>(S);
+        p.z = static_cast<int*>(z);
+        p.L = L;
+        p.C = Cs;
+        p.n_items = n_items;
+        p.n_out = n_out;
+        p.n_dvt = n_dvt;
+        p.dk_g = (int)d_k;
+        p.dv = (int)d_v;
+        p.xcd_remap = xcd_ok(grid);
+        return hip_status(la::run_chunk_states_i8(p, kernel_dk_i8(d_k), DVT, grid, s), "chunk states launch");
+    }
+    la::StatesParams p{};
+    p.k = static_cast<const unsigned short*>(k);
+    p.v = static_cast<const unsigned short*>(v);
+    p.k_lo = static_cast<const unsigned short*>(k_lo);
+    p.S = static_cast<float*>(S);
+    p.z = static_cast<float*>(z);
+    p.L = L;
+    p.C = Cs;
+    p.n_items = n_items;
+    p.n_out = n_out;
+    p.n_dvt = n_dvt;
+    p.dk_g = (int)d_k;
+    p.dv = (int)d_v;
+    p.fmap = fmap;
+    p.in_scale = in_scale;
+    p.want_z = z != nullptr;
+    p.xcd_remap = xcd_ok(grid);
+    hipError_t e;
+    switch (kernel_dk_bf16(d_k)) {
+        case 32: e = la::states_bf16_dk32(p, DVT, grid, s); break;
+        case 64: e = la::states_bf16_dk64(p, DVT, grid, s); break;
+        case 128: e = la::states_bf16_dk128(p, DVT, grid, s); break;
+        default: e = la::states_bf16_dk256(p, DVT, grid, s); break;
+    }
+    return hip_status(e, "chunk states launch");
+}
+
+la_status la_chunk_states(const void* k, const void* v, la_dtype in_dt, int64_t BH, int64_t L, int64_t d_k,
+                          int64_t d_v, int64_t C, void* S, void* z, la_stream_t stream) {
+    g_last_error[0] = 0;
+    if (k == nullptr || v == nullptr || S == nullptr) return fail(LA_ERR_INVALID_ARG, "k, v and S must not be NULL");
+    if (BH < 1 || L < 1) return fail(LA_ERR_INVALID_ARG, "BH and L must be positive");
+    if (in_dt != LA_BF16 && in_dt != LA_I8) return fail(LA_ERR_UNSUPPORTED, "input type must be LA_BF16 or LA_I8");
+    if (!pow2_in(d_k, 16, 256) || !pow2_in(d_v, 16, 256))
+        return fail(LA_ERR_UNSUPPORTED, "d_k and d_v must be 16..256, powers of two");
+    const int64_t Cs = C <= 0 ? 1 : (C > L ? L : C);
+    const int64_t N = cdiv(L, Cs);
+    if (N > 0x7FFFFFFFLL) return fail(LA_ERR_UNSUPPORTED, "too many chunks");
+    return chunk_states_impl(k, v, in_dt == LA_I8, BH, L, d_k, d_v, Cs, (int)N, (int)N, S, z, la::FMAP_NONE, 1.0f,
+                             (hipStream_t)stream);
+}
+
+// ---------------------------------------------------------------------------
+la_status la_state_scan(void* S, void* z, la_dtype st_dt, int64_t BH, int64_t N, int64_t d_k, int64_t d_v,
+                        void* S_final, void* z_final, la_stream_t stream) {
+    g_last_error[0] = 0;
+    if (S == nullptr) return fail(LA_ERR_INVALID_ARG, "S must not be NULL");
+    if (BH < 1 || N < 1) return fail(LA_ERR_INVALID_ARG, "BH and N must be positive");
+    if (st_dt != LA_F32 && st_dt != LA_I32) return fail(LA_ERR_UNSUPPORTED, "state type must be LA_F32 or LA_I32");
+    if (!pow2_in(d_k, 16, 256) || !pow2_in(d_v, 16, 256))
+        return fail(LA_ERR_UNSUPPORTED, "d_k and d_v must be 16..256, powers of two");
+    if (z == nullptr && z_final != nullptr) return fail(LA_ERR_INVALID_ARG, "z_final needs z");
+    la::ScanParams p{};
+    p.S = S;
+    p.z = z;
+    p.S_final = S_final;
+    p.z_final = z_final;
+    p.N = N;
+    p.E = d_k * d_v;
+    p.Ez = d_k;
+    p.is_int = st_dt == LA_I32;
+    return hip_status(la::run_state_scan(p, BH, (hipStream_t)stream), "state scan launch");
+}
+
+// ---------------------------------------------------------------------------
+size_t la_chunked_forward_workspace(la_dtype in_dt, int64_t BH, int64_t L, int64_t d_in, int64_t d_v, int64_t C,
+                                    int causal, int normalize, la_fmap f, int64_t m, float in_scale,
+                                    int64_t group) {
+    Plan P{};
+    char saved[sizeof(g_last_error)];
+    memcpy(saved, g_last_error, sizeof(saved));
+    const la_status s = make_plan(P, in_dt, BH, L, d_in, d_v, C, causal, normalize, f, m, in_scale, group);
+    memcpy(g_last_error, saved, sizeof(saved));
+    if (s != LA_OK) return 0;
+    return P.ws_total;
+}
+
+la_status la_chunked_forward(const void* q, const void* k, const void* v, la_dtype in_dt, int64_t BH, int64_t L,
+                             int64_t d_in, int64_t d_v, int64_t C, int causal, int normalize, la_fmap f,
+                             const void* W, int64_t m, float in_scale, void* o, la_dtype out_dt, void* S_final,
+                             void* z_final, int64_t group, void* workspace, size_t ws_bytes,
+                             la_stream_t stream) {
+    g_last_error[0] = 0;
+    if (q == nullptr || k == nullptr || v == nullptr || o == nullptr)
+        return fail(LA_ERR_INVALID_ARG, "q, k, v and o must not be NULL");
+    la_status st = check_dtypes_forward(in_dt, out_dt, normalize, f, in_scale);
+    if (st != LA_OK) return st;
+    if (f == LA_FMAP_FAVOR && W == nullptr) return fail(LA_ERR_INVALID_ARG, "FAVOR+ needs W");
+    if (z_final != nullptr && !normalize) return fail(LA_ERR_INVALID_ARG, "z_final needs normalize");
+    Plan P{};
+    st = make_plan(P, in_dt, BH, L, d_in, d_v, C, causal, normalize, f, m, in_scale, group);
+    if (st != LA_OK) return st;
+    if (P.ws_total > 0 && (workspace == nullptr || ws_bytes < P.ws_total))
+        return fail(LA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", P.ws_total,
+                    workspace ? ws_bytes : (size_t)0);
+    hipStream_t s = (hipStream_t)stream;
+    char* ws = static_cast<char*>(workspace);
+    const void* qm = q;
+    const void* km = k;
+    const void* klo = nullptr;
+    int fmap_in_kernel = la::FMAP_NONE;
+    if (P.premap) {
+        void* qp = ws;
+        void* kp = ws + P.ws_phi;
+        void* kl = ws + 2 * P.ws_phi;
+        la_status a = la_feature_map(f, q, LA_BF16, BH * L, d_in, W, m, in_scale, qp, LA_BF16, stream);
+        if (a != LA_OK) return a;
+        la::FmapParams fp{};
+        fp.x = static_cast<const unsigned short*>(k);
+        fp.W = static_cast<const unsigned short*>(W);
+        fp.y = kp;
+        fp.y_lo = static_cast<unsigned short*>(kl);
+        fp.rows = BH * L;
+        fp.d_in = (int)d_in;
+        fp.m = (int)m;
+        fp.fmap = 2;
+        fp.in_scale = in_scale;
+        a = hip_status(la::run_feature_map(fp, s), "feature map launch");
+        if (a != LA_OK) return a;
+        qm = qp;
+        km = kp;
+        klo = kl;
+        ws += 3 * P.ws_phi;
+    } else if (f == LA_FMAP_ELU1) {
+        fmap_in_kernel = la::FMAP_ELU1;
+    }
+    void* states = P.ws_states ? ws : nullptr;
+    void* zst = P.ws_z ? ws + P.ws_states : nullptr;
+
+    // phase 1 + 2 at group granularity (or the total state for non-causal)
+    if (P.causal && P.n_groups > 1) {
+        st = chunk_states_impl(km, v, P.i8, BH, L, P.dk, d_v, P.G * P.C, (int)(P.n_groups - 1), (int)P.n_groups,
+                               states, zst, fmap_in_kernel, in_scale, s, klo);
+        if (st != LA_OK) return st;
+        la::ScanParams sp{};
+        sp.S = states;
+        sp.z = zst;
+        sp.N = P.n_groups;
+        sp.E = P.dk * d_v;
+        sp.Ez = P.dk;
+        sp.is_int = P.i8;
+        st = hip_status(la::run_state_scan(sp, BH, s), "state scan launch");
+        if (st != LA_OK) return st;
+    } else if (!P.causal) {
+        st = chunk_states_impl(km, v, P.i8, BH, L, P.dk, d_v, L, 1, 1, states, zst, fmap_in_kernel, in_scale, s, klo);
+        if (st != LA_OK) return st;
+    }
+
+    // phase 3
+    const int64_t grid = BH * P.n_groups * P.n_dvt;
+    if (P.i8) {
+        la::FwdParamsI8 p{};
+        p.q = static_cast<const signed char*>(qm);
+        p.k = static_cast<const signed char*>(km);
+        p.v = static_cast<const signed char*>(v);
+        p.o = static_cast<int*>(o);
+        p.P0 = static_cast<const int*>(states);
+        p.S_final = static_cast<int*>(S_final);
+        p.L = L;
+        p.C = (int)P.C;
+        p.G = (int)P.G;
+        p.n_groups = (int)P.n_groups;
+        p.n_dvt = P.n_dvt;
+        p.dk_g = (int)P.dk;
+        p.dv = (int)d_v;
+        p.xcd_remap = xcd_ok(grid);
+        p.noncausal = !P.causal;
+        return hip_status(la::run_chunked_fwd_i8(p, P.DK, P.DVT, P.T, grid, s), "chunked forward launch");
+    }
+    la::FwdParams p{};
+    p.q = static_cast<const unsigned short*>(qm);
+    p.k = static_cast<const unsigned short*>(km);
+    p.v = static_cast<const unsigned short*>(v);
+    p.k_lo = static_cast<const unsigned short*>(klo);
+    p.o = o;
+    p.P0 = static_cast<const float*>(states);
+    p.z0 = static_cast<const float*>(zst);
+    p.S_final = static_cast<float*>(S_final);
+    p.z_final = static_cast<float*>(z_final);
+    p.L = L;
+    p.C = (int)P.C;
+    p.G = (int)P.G;
+    p.n_groups = (int)P.n_groups;
+    p.n_dvt = P.n_dvt;
+    p.dk_g = (int)P.dk;
+    p.dv = (int)d_v;
+    p.fmap = fmap_in_kernel;
+    p.in_scale = in_scale;
+    p.normalize = P.normalize;
+    p.out_f32 = out_dt == LA_F32;
+    p.xcd_remap = xcd_ok(grid);
+    p.noncausal = !P.causal;
+    const bool scaled_identity = f == LA_FMAP_IDENTITY && in_scale != 1.0f;
+    p.out_scale = (scaled_identity && !P.normalize) ? in_scale * in_scale : 1.0f;
+    p.state_scale = scaled_identity ? in_scale : 1.0f;
+    hipError_t e;
+    switch (P.DK) {
+        case 32: e = la::fwd_bf16_dk32(p, P.DVT, P.T, grid, s); break;
+        case 64: e = la::fwd_bf16_dk64(p, P.DVT, P.T, grid, s); break;
+        case 128: e = la::fwd_bf16_dk128(p, P.DVT, P.T, grid, s); break;
+        default: e = la::fwd_bf16_dk256(p, P.DVT, P.T, grid, s); break;
+    }
+    return hip_status(e, "chunked forward launch");
+}
+
+// ---------------------------------------------------------------------------
+la_status la_recurrent_step(const void* q, const void* k, const void* v, la_dtype in_dt, int64_t n_states,
+                            int64_t d_in, int64_t d_v, la_fmap f, const void* W, int64_t m, float in_scale,
+                            int normalize, float* S, float* z, void* o, la_dtype out_dt, la_stream_t stream) {
+    g_last_error[0] = 0;
+    if (q == nullptr || k == nullptr || v == nullptr || S == nullptr || o == nullptr)
+        return fail(LA_ERR_INVALID_ARG, "q, k, v, S and o must not be NULL");
+    if (normalize && z == nullptr) return fail(LA_ERR_INVALID_ARG, "normalize needs z");
+    if (n_states < 1 || d_in < 1 || d_v < 1) return fail(LA_ERR_INVALID_ARG, "sizes must be positive");
+    if (in_dt != LA_BF16) return fail(LA_ERR_UNSUPPORTED, "decode inputs must be LA_BF16");
+    if (out_dt != LA_F32 && out_dt != LA_BF16) return fail(LA_ERR_UNSUPPORTED, "decode output must be LA_F32 or LA_BF16");
+    if (!(in_scale == in_scale)) return fail(LA_ERR_INVALID_ARG, "in_scale is NaN");
+    int64_t dk = d_in;
+    int fm = 0;
+    if (f == LA_FMAP_FAVOR) {
+        if (W == nullptr) return fail(LA_ERR_INVALID_ARG, "FAVOR+ needs W");
+        if (!pow2_in(m, 16, 256) || !pow2_in(d_in, 16, 128))
+            return fail(LA_ERR_UNSUPPORTED, "FAVOR+ needs m in 16..256 and d_in in 16..128 (powers of two)");
+        dk = m;
+        fm = 2;
+    } else if (f == LA_FMAP_ELU1) {
+        fm = 1;
+    } else if (f != LA_FMAP_IDENTITY) {
+        return fail(LA_ERR_INVALID_ARG, "unknown feature map %d", (int)f);
+    }
+    if (!pow2_in(dk, 16, 256) || !pow2_in(d_v, 16, 256))
+        return fail(LA_ERR_UNSUPPORTED, "d_k and d_v must be 16..256, powers of two");
+    la::DecodeParams p{};
+    p.q = static_cast<const unsigned short*>(q);
+    p.k = static_cast<const unsigned short*>(k);
+    p.v = static_cast<const unsigned short*>(v);
+    p.W = static_cast<const unsigned short*>(W);
+    p.S = S;
+    p.z = z;
+    p.o = o;
+    p.n = n_states;
+    p.d_in = (int)d_in;
+    p.dk = (int)dk;
+    p.dv = (int)d_v;
+    p.fmap = fm;
+    p.in_scale = in_scale;
+    p.normalize = normalize != 0;
+    p.out_f32 = out_dt == LA_F32;
+    return hip_status(la::run_recurrent_step(p, (hipStream_t)stream), "recurrent step launch");
+}
+
+}  // extern "C"

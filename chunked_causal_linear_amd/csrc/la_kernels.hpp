@@ -1,0 +1,141 @@
+// Kernel parameter blocks and launcher declarations (host and device side).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace la {
+
+enum { FMAP_NONE = 0, FMAP_ELU1 = 1 };
+
+// Fused phase 3 (with the carry over the chunks of a group).
+struct FwdParams {
+    const unsigned short* q;  // [BH, L, dk_g]
+    const unsigned short* k;  // [BH, L, dk_g]
+    const unsigned short* v;  // [BH, L, dv]
+    const unsigned short* k_lo;  // [BH, L, dk_g] bf16 residual of pre-mapped phi(k), or null
+    void* o;                  // [BH, L, dv] bf16 or f32
+    const float* P0;          // [BH, n_groups, dk_g, dv] exclusive prefix per group, or null
+    const float* z0;          // [BH, n_groups, dk_g]
+    float* S_final;           // [BH, dk_g, dv] or null
+    float* z_final;           // [BH, dk_g] or null
+    int64_t L;
+    int C;          // chunk size, >= 1
+    int G;          // chunks per group
+    int n_groups;
+    int n_dvt;      // column tiles per head
+    int dk_g;       // feature width in memory (<= the kernel's DK)
+    int dv;         // full value width
+    int fmap;       // FMAP_NONE or FMAP_ELU1 (applied to q and k on load)
+    float in_scale;
+    int normalize;
+    int out_f32;
+    int xcd_remap;
+    int noncausal;  // every row reads P0 (the total state); no intra part, no update
+    float out_scale;    // multiplies every output row (identity map with in_scale: s^2)
+    float state_scale;  // multiplies the returned final state and normaliser (s)
+};
+
+// Phase 1 (per-chunk states).
+struct StatesParams {
+    const unsigned short* k;
+    const unsigned short* v;
+    const unsigned short* k_lo;  // bf16 residual of pre-mapped phi(k), or null
+    float* S;      // [BH, n_out, dk_g, dv]
+    float* z;      // [BH, n_out, dk_g] or null
+    int64_t L;
+    int64_t C;     // rows per chunk
+    int n_items;   // chunks computed per head
+    int n_out;     // chunk stride of S / z per head
+    int n_dvt;
+    int dk_g;
+    int dv;
+    int fmap;
+    float in_scale;
+    int want_z;
+    int xcd_remap;
+};
+
+// int8 path: fused phase 3 and phase 1 with exact int32 arithmetic.
+struct FwdParamsI8 {
+    const signed char* q;
+    const signed char* k;
+    const signed char* v;
+    int* o;            // [BH, L, dv]
+    const int* P0;     // [BH, n_groups, dk_g, dv] or null
+    int* S_final;      // [BH, dk_g, dv] or null
+    int64_t L;
+    int C;
+    int G;
+    int n_groups;
+    int n_dvt;
+    int dk_g;
+    int dv;
+    int xcd_remap;
+    int noncausal;
+};
+
+struct StatesParamsI8 {
+    const signed char* k;
+    const signed char* v;
+    int* S;        // [BH, n_out, dk_g, dv]
+    int* z;        // [BH, n_out, dk_g] or null
+    int64_t L;
+    int64_t C;
+    int n_items;
+    int n_out;
+    int n_dvt;
+    int dk_g;
+    int dv;
+    int xcd_remap;
+};
+
+struct ScanParams {
+    void* S;         // [BH, N, E] (E = dk*dv), fp32 or int32
+    void* z;         // [BH, N, dk] or null
+    void* S_final;   // [BH, E] or null
+    void* z_final;   // [BH, dk] or null
+    int64_t N;
+    int64_t E;
+    int64_t Ez;
+    int is_int;
+};
+
+struct FmapParams {
+    const unsigned short* x;  // [rows, d_in]
+    const unsigned short* W;  // [m, d_in] or null
+    void* y;                  // [rows, d_out] bf16 or f32
+    unsigned short* y_lo;     // [rows, d_out] bf16 residual y - bf16(y) (FAVOR+, bf16 y), or null
+    int64_t rows;
+    int d_in;
+    int m;
+    int fmap;       // 0 identity (scaled), 1 elu1, 2 favor
+    float in_scale;
+    int y_f32;
+};
+
+struct DecodeParams {
+    const unsigned short* q;  // [n, d_in]
+    const unsigned short* k;
+    const unsigned short* v;  // [n, dv]
+    const unsigned short* W;  // [m, d_in] or null
+    float* S;                 // [n, dk, dv]
+    float* z;                 // [n, dk] or null
+    void* o;                  // [n, dv]
+    int64_t n;
+    int d_in;
+    int dk;
+    int dv;
+    int fmap;       // 0 identity, 1 elu1, 2 favor
+    float in_scale;
+    int normalize;
+    int out_f32;
+};
+
+hipError_t run_chunked_fwd_i8(const FwdParamsI8& p, int DK, int DVT, int T, int64_t grid, hipStream_t s);
+hipError_t run_chunk_states_i8(const StatesParamsI8& p, int DK, int DVT, int64_t grid, hipStream_t s);
+hipError_t run_state_scan(const ScanParams& p, int64_t BH, hipStream_t s);
+hipError_t run_feature_map(const FmapParams& p, hipStream_t s);
+hipError_t run_recurrent_step(const DecodeParams& p, hipStream_t s);
+
+}  // namespace la

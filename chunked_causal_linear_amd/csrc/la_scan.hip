@@ -1,0 +1,81 @@
+// Phase 2: exclusive prefix of the per-chunk states over chunks.
+//
+// P_0 = 0, P_n = P_{n-1} + S_{n-1}, done in place, plus the total (the state
+// after the last chunk) - page "attention と線形の間", section ②: chunk n reads
+// the state carried from every chunk before it, starting from zero.
+//
+// Elementwise-parallel over (head, state element); each thread walks the N
+// chunks of four consecutive elements in order (a deterministic sum).  The
+// loads of eight chunks are issued before their adds so that several reads are
+// in flight per thread: the kernel is a pure HBM stream (read and write every
+// per-chunk state once).
+#include "la_common.hpp"
+#include "la_kernels.hpp"
+
+namespace la {
+
+template <typename V4>
+__device__ __forceinline__ V4 add4(const V4& a, const V4& b) {
+    V4 r;
+    r.x = a.x + b.x;
+    r.y = a.y + b.y;
+    r.z = a.z + b.z;
+    r.w = a.w + b.w;
+    return r;
+}
+
+template <typename V4, typename E>
+__global__ __launch_bounds__(256) void state_scan_kernel(V4* __restrict__ S, V4* __restrict__ total, int64_t N,
+                                                          int64_t E4, int64_t BH) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= BH * E4) return;
+    const int64_t bh = idx / E4, e = idx % E4;
+    V4* base = S + bh * N * E4 + e;
+    V4 run;
+    run.x = run.y = run.z = run.w = E(0);
+    constexpr int U = 8;
+    int64_t n = 0;
+    for (; n + U <= N; n += U) {
+        V4 x[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) x[u] = base[(n + u) * E4];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            base[(n + u) * E4] = run;
+            run = add4(run, x[u]);
+        }
+    }
+    for (; n < N; ++n) {
+        const V4 x = base[n * E4];
+        base[n * E4] = run;
+        run = add4(run, x);
+    }
+    if (total != nullptr) total[bh * E4 + e] = run;
+}
+
+// Wrapping int32 adds (unsigned arithmetic) so overflow is defined.
+struct WrapInt4 {
+    unsigned x, y, z, w;
+};
+
+static hipError_t scan_one(void* S, void* total, int64_t N, int64_t E, int64_t BH, int is_int, hipStream_t s) {
+    const int64_t E4 = E / 4;
+    const int64_t threads = BH * E4;
+    const int64_t blocks = (threads + 255) / 256;
+    if (is_int)
+        hipLaunchKernelGGL((state_scan_kernel<WrapInt4, unsigned>), dim3((unsigned)blocks), dim3(256), 0, s,
+                           reinterpret_cast<WrapInt4*>(S), reinterpret_cast<WrapInt4*>(total), N, E4, BH);
+    else
+        hipLaunchKernelGGL((state_scan_kernel<float4, float>), dim3((unsigned)blocks), dim3(256), 0, s,
+                           reinterpret_cast<float4*>(S), reinterpret_cast<float4*>(total), N, E4, BH);
+    return hipGetLastError();
+}
+
+hipError_t run_state_scan(const ScanParams& p, int64_t BH, hipStream_t s) {
+    hipError_t e = scan_one(p.S, p.S_final, p.N, p.E, BH, p.is_int, s);
+    if (e != hipSuccess) return e;
+    if (p.z != nullptr) e = scan_one(p.z, p.z_final, p.N, p.Ez, BH, p.is_int, s);
+    return e;
+}
+
+}  // namespace la

@@ -1,0 +1,201 @@
+/*
+ * la.h - C ABI of liblinattn: chunkwise-parallel causal linear attention for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  For each of BH independent (batch, head) slices, with
+ * feature map phi applied to queries and keys (never to values):
+ *
+ *   causal:      o_i = phi(q_i)^T S_i [/ phi(q_i)^T z_i],
+ *                S_i = sum_{j<=i} phi(k_j) v_j^T,  z_i = sum_{j<=i} phi(k_j)
+ *   non-causal:  the same with every sum over all j
+ *
+ * The causal mask includes the diagonal (token i sees itself).  The causal
+ * result is produced chunkwise with chunk size C: inside a chunk the output is
+ * the lower-triangular (diagonal kept) product tril(Q_c K_c^T) V_c, across
+ * chunks it is Q_c P_c with P_c the state carried from the chunks before, and
+ * the state then grows by K_c^T V_c.  Every C gives the same value in exact
+ * arithmetic; C <= 0 is treated as 1, C >= L is a single chunk, and the last
+ * chunk may be shorter than C.
+ *
+ * Sources.  Page "attention と線形の間" (sharin-2a1.pages.dev/parts/
+ * chunked.html): section ① (the association orders and the d x d state),
+ * section ② (the chunked algorithm, its causal mask and its two ends).  Page
+ * "Linear Attention / Performerの理論と実装" (disassemble-channel.com/
+ * linear-attention/): the kernel re-formulation with the normaliser, the RNN
+ * view (S_t, z_t recurrences), the elu+1 and FAVOR+ feature maps.
+ *
+ * Layout.  Every tensor is dense and row-major.  q, k: [BH, L, d_in];
+ * v: [BH, L, d_v]; o: [BH, L, d_v]; states: [BH, (N,) d_k, d_v] with d_k the
+ * feature width (d_k = d_in, or m for FAVOR+); normalisers z: [BH, (N,) d_k].
+ * A [B, H, L, d] tensor is passed as BH = B * H slices.
+ *
+ * Precision.  LA_BF16 inputs: phi computed in fp32 and rounded to bf16,
+ * products on bf16 matrix cores with fp32 accumulation, states fp32, output
+ * bf16 (round to nearest even) or fp32.  LA_I8 inputs (identity map, no
+ * normaliser): int8 x int8 products accumulated exactly in int32; states and
+ * output int32; results are exact whenever they fit in int32 (two's-complement
+ * wrap otherwise).
+ *
+ * Ownership and synchronisation.  The caller owns every buffer; all pointers
+ * except those documented as host pointers are device pointers.  No entry
+ * point allocates device memory: scratch comes from the caller's workspace.
+ * Every call only enqueues work on the given stream (0 = the null stream) and
+ * returns without waiting for it; there is no host synchronisation inside.
+ *
+ * Errors.  Invalid arguments are detected before anything is enqueued and
+ * reported as LA_ERR_INVALID_ARG or LA_ERR_UNSUPPORTED; a launch failure
+ * reported by the HIP runtime gives LA_ERR_HIP.  la_last_error() returns a
+ * thread-local description of the most recent failure on the calling thread.
+ * Nothing is thrown across the ABI.
+ *
+ * Supported sizes.  d_k in {16, 32, 64, 128, 256}, d_v in {16, 32, 64, 128,
+ * 256}; FAVOR+: d_in in {16, 32, 64, 128} and m = d_k.  L >= 1, BH >= 1.
+ */
+#ifndef LIBLINATTN_LA_H
+#define LIBLINATTN_LA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* la_stream_t; /* a hipStream_t */
+
+typedef enum {
+    LA_OK = 0,
+    LA_ERR_INVALID_ARG = 1, /* a null required pointer, a non-positive size, mismatched sizes */
+    LA_ERR_UNSUPPORTED = 2, /* a valid request this library does not implement */
+    LA_ERR_HIP = 3,         /* the HIP runtime reported an error */
+    LA_ERR_WORKSPACE = 4    /* the workspace is missing or smaller than required */
+} la_status;
+
+typedef enum { LA_BF16 = 0, LA_F32 = 1, LA_I8 = 2, LA_I32 = 3 } la_dtype;
+
+typedef enum {
+    LA_FMAP_IDENTITY = 0, /* phi(x) = x                                      */
+    LA_FMAP_ELU1 = 1,     /* phi(x) = x + 1 for x >= 0, exp(x) for x < 0      */
+    LA_FMAP_FAVOR = 2     /* phi(x)_l = exp(w_l . x - |x|^2 / 2) / sqrt(m)    */
+} la_fmap;
+
+/*
+ * la_feature_map - y = phi(in_scale * x), row by row.
+ *
+ * Defined by the linear-attention page: its ELU feature map (elu with
+ * alpha = 1, plus one) and its FAVOR+ positive random features (projection by
+ * the m rows of W, minus half the squared norm, exponentiated, over sqrt(m)).
+ *
+ *   x    [rows, d_in] LA_BF16.
+ *   W    [m, d_in] LA_BF16, FAVOR+ only (NULL otherwise); m is ignored unless
+ *        f == LA_FMAP_FAVOR.
+ *   y    [rows, d_k] of type ydt (LA_BF16 or LA_F32), d_k = m for FAVOR+,
+ *        d_in otherwise.  y must not overlap x.
+ */
+la_status la_feature_map(la_fmap f, const void* x, la_dtype xdt, int64_t rows, int64_t d_in,
+                         const void* W, int64_t m, float in_scale, void* y, la_dtype ydt,
+                         la_stream_t stream);
+
+/*
+ * la_chunk_states - phase 1: local state of every chunk,
+ *   S_n = K_c^T V_c (d_k x d_v) and, when z != NULL, z_n = sum of the rows of K_c,
+ * for chunks [n*C, min((n+1)*C, L)), n = 0 .. N-1, N = ceil(L / C).
+ *
+ * Defined by the chunking page, section ②: the state each chunk adds before
+ * the next one reads it.  k is taken as already feature-mapped.
+ *
+ *   k    [BH, L, d_k], v [BH, L, d_v], both of type in_dt (LA_BF16 or LA_I8).
+ *   S    [BH, N, d_k, d_v]: LA_F32 for bf16 inputs, LA_I32 for int8 inputs.
+ *   z    [BH, N, d_k], same type as S, or NULL.
+ */
+la_status la_chunk_states(const void* k, const void* v, la_dtype in_dt, int64_t BH, int64_t L,
+                          int64_t d_k, int64_t d_v, int64_t C, void* S, void* z,
+                          la_stream_t stream);
+
+/*
+ * la_state_scan - phase 2: exclusive prefix over chunks, in place:
+ *   P_0 = 0, P_n = P_{n-1} + S_{n-1}   (same for z when z != NULL)
+ * and, when S_final / z_final are not NULL, the total sum_n S_n (the state
+ * after the whole sequence) / sum_n z_n.
+ *
+ * Defined by the chunking page, section ②: chunk n reads the state carried
+ * from every chunk before it; the state starts at zero.
+ *
+ *   S    [BH, N, d_k, d_v] of type st_dt (LA_F32 or LA_I32), overwritten by P.
+ *   z    [BH, N, d_k] of the same type, or NULL.
+ *   S_final [BH, d_k, d_v], z_final [BH, d_k]: optional outputs.
+ * Sums run in chunk order, so the result is deterministic; int32 sums wrap.
+ */
+la_status la_state_scan(void* S, void* z, la_dtype st_dt, int64_t BH, int64_t N, int64_t d_k,
+                        int64_t d_v, void* S_final, void* z_final, la_stream_t stream);
+
+/*
+ * la_chunked_forward - the whole forward: phi, then (causal) the chunked
+ * computation with chunk size C, or (non-causal) phi(Q) (phi(K)^T V).
+ * normalize != 0 divides each output row by phi(q_i)^T z_i (the numerator and
+ * the denominator each sum their intra- and inter-chunk parts first; no
+ * epsilon).
+ *
+ * Defined by the chunking page, section ② (Chunked and its two causal ends)
+ * and the linear-attention page (normalised output, RNN view).
+ *
+ *   q, k [BH, L, d_in], v [BH, L, d_v] of type in_dt (LA_BF16, or LA_I8 with
+ *        f == LA_FMAP_IDENTITY and normalize == 0).
+ *   W    [m, d_in] LA_BF16 for FAVOR+ (d_k = m), else NULL.
+ *   in_scale  multiplies q and k before phi (1.0f: none).
+ *   o    [BH, L, d_v] of type out_dt (LA_BF16 or LA_F32 for bf16 inputs,
+ *        LA_I32 for int8 inputs).
+ *   S_final [BH, d_k, d_v] (LA_F32, or LA_I32 for int8) and z_final [BH, d_k]
+ *        (LA_F32; only with normalize): optional final state.
+ *   group  consecutive chunks one workgroup carries the state through (0 =
+ *        chosen by the library).  Groups are joined through la_chunk_states +
+ *        la_state_scan at group granularity; group = 1 is the literal
+ *        three-phase form, group >= N the fully sequential form.  Every value
+ *        gives the same result in exact arithmetic.
+ *   workspace / ws_bytes  device scratch of at least
+ *        la_chunked_forward_workspace(...) bytes (may be NULL when that is 0).
+ */
+la_status la_chunked_forward(const void* q, const void* k, const void* v, la_dtype in_dt,
+                             int64_t BH, int64_t L, int64_t d_in, int64_t d_v, int64_t C,
+                             int causal, int normalize, la_fmap f, const void* W, int64_t m,
+                             float in_scale, void* o, la_dtype out_dt, void* S_final,
+                             void* z_final, int64_t group, void* workspace, size_t ws_bytes,
+                             la_stream_t stream);
+
+/* Bytes of workspace la_chunked_forward needs for these arguments (0 when it
+ * needs none, and also on an invalid combination, which la_chunked_forward
+ * then reports).  FAVOR+, or the identity map with in_scale != 1, stores the
+ * mapped q and k there; more than one group stores the group states there. */
+size_t la_chunked_forward_workspace(la_dtype in_dt, int64_t BH, int64_t L, int64_t d_in,
+                                    int64_t d_v, int64_t C, int causal, int normalize,
+                                    la_fmap f, int64_t m, float in_scale, int64_t group);
+
+/*
+ * la_recurrent_step - one decode step for n_states independent states:
+ *   S += phi(k) v^T;  z += phi(k);  o = phi(q)^T S [/ phi(q)^T z]
+ * (update first, then read, as in the RNN view of the linear-attention page
+ * and the token-by-token causal form of the chunking page).
+ *
+ *   q, k [n_states, d_in], v [n_states, d_v]: LA_BF16.
+ *   W    [m, d_in] LA_BF16 for FAVOR+ (d_k = m), else NULL.
+ *   S    [n_states, d_k, d_v] fp32, z [n_states, d_k] fp32: read and updated
+ *        in place (z may be NULL when normalize == 0).
+ *   o    [n_states, d_v] of type out_dt (LA_F32 or LA_BF16).
+ */
+la_status la_recurrent_step(const void* q, const void* k, const void* v, la_dtype in_dt,
+                            int64_t n_states, int64_t d_in, int64_t d_v, la_fmap f,
+                            const void* W, int64_t m, float in_scale, int normalize, float* S,
+                            float* z, void* o, la_dtype out_dt, la_stream_t stream);
+
+/* Static description of a status code. */
+const char* la_status_string(la_status s);
+/* Thread-local description of the last failure on this thread ("" if none). */
+const char* la_last_error(void);
+/* Library version, major * 10000 + minor * 100 + patch. */
+int la_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBLINATTN_LA_H */

@@ -1,0 +1,142 @@
+"""The C ABI library on the CPU: it loads, exports every symbol include/la.h
+declares, and rejects invalid arguments before launching anything (no GPU
+needed; no call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import chunked_causal_linear_amd as la
+from chunked_causal_linear_amd import binding as b
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "la.h")
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    src = open(HEADER, encoding="utf-8").read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(la_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_library_loads_and_exports_header_symbols():
+    lib = la.lib()
+    names = declared_functions()
+    assert "la_chunked_forward" in names and "la_recurrent_step" in names
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", b.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert set(names) <= exported
+    assert set(b.EXPORTS) == set(names)
+
+
+def test_version_and_status_strings():
+    lib = la.lib()
+    assert lib.la_version() >= 100
+    for code, text in ((0, b"ok"), (1, b"invalid argument"), (2, b"unsupported"), (3, b"HIP runtime error"),
+                       (4, b"workspace missing or too small")):
+        assert lib.la_status_string(code) == text
+    assert lib.la_status_string(99) == b"unknown status"
+
+
+def _fwd(**kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, in_dt=b.LA_BF16, BH=2, L=64, d_in=64, d_v=64, C=64, causal=1,
+                normalize=0, f=0, W=None, m=0, in_scale=1.0, o=FAKE, out_dt=b.LA_BF16, S_final=None,
+                z_final=None, group=0, ws=None, ws_bytes=0, stream=None)
+    args.update(kw)
+    lib = la.lib()
+    return lib.la_chunked_forward(*args.values())
+
+
+def test_forward_argument_errors():
+    lib = la.lib()
+    assert _fwd(q=None) == b.LA_ERR_INVALID_ARG
+    assert b"NULL" in lib.la_last_error()
+    assert _fwd(L=0) == b.LA_ERR_INVALID_ARG
+    assert _fwd(BH=-1) == b.LA_ERR_INVALID_ARG
+    assert _fwd(d_in=48) == b.LA_ERR_UNSUPPORTED
+    assert _fwd(d_v=512) == b.LA_ERR_UNSUPPORTED
+    assert _fwd(d_in=8) == b.LA_ERR_UNSUPPORTED
+    assert _fwd(in_dt=b.LA_I8, normalize=1, out_dt=b.LA_I32) == b.LA_ERR_UNSUPPORTED
+    assert _fwd(in_dt=b.LA_I8, f=1, out_dt=b.LA_I32) == b.LA_ERR_UNSUPPORTED
+    assert _fwd(in_dt=b.LA_I8, out_dt=b.LA_BF16) == b.LA_ERR_UNSUPPORTED
+    assert _fwd(in_dt=b.LA_I8, out_dt=b.LA_I32, in_scale=0.5) == b.LA_ERR_UNSUPPORTED
+    assert _fwd(out_dt=b.LA_I32) == b.LA_ERR_UNSUPPORTED
+    assert _fwd(in_dt=b.LA_F32) == b.LA_ERR_UNSUPPORTED
+    assert _fwd(f=2, W=None, m=256) == b.LA_ERR_INVALID_ARG  # FAVOR+ without W
+    assert _fwd(f=2, W=FAKE, m=100) == b.LA_ERR_UNSUPPORTED
+    assert _fwd(f=7) == b.LA_ERR_INVALID_ARG
+    assert _fwd(z_final=FAKE) == b.LA_ERR_INVALID_ARG  # z_final needs normalize
+    assert _fwd(in_scale=float("nan")) == b.LA_ERR_INVALID_ARG
+
+
+def test_workspace_sizes_and_errors():
+    lib = la.lib()
+    ws = lambda *a: lib.la_chunked_forward_workspace(*a)  # noqa: E731
+    # one group, identity map: no scratch
+    assert ws(b.LA_BF16, 128, 8192, 128, 128, 64, 1, 0, 0, 0, 1.0, 0) == 0
+    assert ws(b.LA_BF16, 128, 8192, 128, 128, 64, 1, 0, 0, 0, 0.5, 0) == 0  # scale folded into the results
+    # groups: BH * n_groups * (dk*dv + dk) floats (normalised), 256-byte aligned pieces
+    n = ws(b.LA_BF16, 2, 1024, 64, 64, 64, 1, 1, 1, 0, 1.0, 4)
+    groups = 1024 // 64 // 4
+    assert n == 2 * groups * 64 * 64 * 4 + 2 * groups * 64 * 4
+    # FAVOR+: three mapped copies (q, k and k's residual) of BH*L*m bf16
+    n = ws(b.LA_BF16, 24, 16384, 64, 64, 64, 1, 1, 2, 256, 1.0, 0)
+    per = 24 * 16384 * 256 * 2
+    assert n >= 3 * per
+    # non-causal: one total state per head
+    assert ws(b.LA_BF16, 3, 100, 64, 32, 64, 0, 0, 0, 0, 1.0, 0) == 3 * 64 * 32 * 4
+    # invalid combination
+    assert ws(b.LA_BF16, 0, 100, 64, 64, 64, 1, 0, 0, 0, 1.0, 0) == 0
+    # too small a workspace is rejected before any launch
+    assert _fwd(BH=2, L=1024, normalize=1, f=1, group=4, ws=None, ws_bytes=0) == b.LA_ERR_WORKSPACE
+    assert _fwd(BH=2, L=1024, normalize=1, f=1, group=4, ws=FAKE, ws_bytes=100) == b.LA_ERR_WORKSPACE
+
+
+def test_other_entry_point_errors():
+    lib = la.lib()
+    assert lib.la_feature_map(0, None, b.LA_BF16, 10, 64, None, 0, 1.0, FAKE, b.LA_BF16, None) == b.LA_ERR_INVALID_ARG
+    assert lib.la_feature_map(0, FAKE, b.LA_I8, 10, 64, None, 0, 1.0, FAKE, b.LA_BF16, None) == b.LA_ERR_UNSUPPORTED
+    assert lib.la_feature_map(2, FAKE, b.LA_BF16, 10, 64, None, 256, 1.0, FAKE, b.LA_BF16, None) == b.LA_ERR_INVALID_ARG
+    assert lib.la_feature_map(1, FAKE, b.LA_BF16, 0, 64, None, 0, 1.0, FAKE, b.LA_BF16, None) == b.LA_ERR_INVALID_ARG
+    assert lib.la_chunk_states(None, FAKE, b.LA_BF16, 1, 64, 64, 64, 16, FAKE, None, None) == b.LA_ERR_INVALID_ARG
+    assert lib.la_chunk_states(FAKE, FAKE, b.LA_BF16, 1, 64, 24, 64, 16, FAKE, None, None) == b.LA_ERR_UNSUPPORTED
+    assert lib.la_chunk_states(FAKE, FAKE, b.LA_F32, 1, 64, 64, 64, 16, FAKE, None, None) == b.LA_ERR_UNSUPPORTED
+    assert lib.la_state_scan(None, None, b.LA_F32, 1, 4, 64, 64, None, None, None) == b.LA_ERR_INVALID_ARG
+    assert lib.la_state_scan(FAKE, None, b.LA_BF16, 1, 4, 64, 64, None, None, None) == b.LA_ERR_UNSUPPORTED
+    assert lib.la_state_scan(FAKE, None, b.LA_F32, 1, 0, 64, 64, None, None, None) == b.LA_ERR_INVALID_ARG
+    assert lib.la_state_scan(FAKE, None, b.LA_F32, 1, 4, 64, 64, None, FAKE, None) == b.LA_ERR_INVALID_ARG
+    assert lib.la_recurrent_step(FAKE, FAKE, FAKE, b.LA_BF16, 4, 64, 64, 1, None, 0, 1.0, 1, FAKE, None, FAKE,
+                                 b.LA_F32, None) == b.LA_ERR_INVALID_ARG  # normalise without z
+    assert lib.la_recurrent_step(FAKE, FAKE, FAKE, b.LA_BF16, 4, 64, 64, 2, None, 256, 1.0, 1, FAKE, FAKE, FAKE,
+                                 b.LA_F32, None) == b.LA_ERR_INVALID_ARG  # FAVOR+ without W
+    assert lib.la_recurrent_step(FAKE, FAKE, FAKE, b.LA_I8, 4, 64, 64, 0, None, 0, 1.0, 0, FAKE, None, FAKE,
+                                 b.LA_F32, None) == b.LA_ERR_UNSUPPORTED
+    assert lib.la_recurrent_step(FAKE, FAKE, FAKE, b.LA_BF16, 4, 48, 64, 0, None, 0, 1.0, 0, FAKE, None, FAKE,
+                                 b.LA_F32, None) == b.LA_ERR_UNSUPPORTED
+
+
+def test_last_error_is_thread_local():
+    import threading
+    lib = la.lib()
+    _fwd(q=None)
+    seen = {}
+
+    def other():
+        seen["msg"] = lib.la_last_error()
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen["msg"] == b""
+    assert lib.la_last_error() != b""
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    monkeypatch.setattr(b, "_lib", None)
+    monkeypatch.setattr(b, "LIB_PATH", "/nonexistent/liblinattn.so")
+    with pytest.raises(b.LibraryNotBuilt):
+        b.lib()

@@ -1,0 +1,276 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+int8 inputs: bit-exact int32.  bf16 inputs: per element
+|gpu - oracle| <= 1e-2 * (1 + |oracle|), with the oracle in float64 on the
+same bf16 values.  Sizes here span several tiles and a ragged tail and finish
+in seconds on the oracle; the full workloads are in test_gpu_workloads.py.
+"""
+import numpy as np
+import pytest
+
+import chunked_causal_linear_amd as la
+import oracle
+import workloads as wl
+from tests.gpu_helpers import assert_close, assert_exact, dev_input, host, log, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(seed, BH, L, d_in, d_v, dtype, scale=None):
+    if scale is None:
+        scale = 1.0 / np.sqrt(d_in) if dtype == "bf16" else 1.0
+    return wl.random_case(seed, BH, L, d_in, d_v, dtype, scale)
+
+
+def _oracle_forward(q, k, v, C, causal=True, normalize=False, fmap="identity", W=None, in_scale=1.0):
+    outs, Ss, zs = [], [], []
+    for h in range(q.shape[0]):
+        o, S, z = oracle.forward(q[h], k[h], v[h], C, causal, normalize, fmap, W, in_scale)
+        outs.append(o)
+        Ss.append(S)
+        zs.append(z)
+    return np.stack(outs), np.stack(Ss), np.stack(zs)
+
+
+# ---------------------------------------------------------------------------
+# int8: bit-exact
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("C", [1, 16, 64, 256, 3, 100, 0, 1000])
+def test_int8_workload1_all_chunks(C):
+    w = wl.WORKLOADS[1]
+    q, k, v, _ = wl.workload_inputs(w)
+    log(f"int8 workload 1, C={C}")
+    o, S, _ = la.chunked_forward(dev_input(q), dev_input(k), dev_input(v), C, return_state=True)
+    ref_quad = oracle.causal_scores_first(q.exact[0], k.exact[0], v.exact[0])
+    ref_rec, ref_S, _ = oracle.causal_state_first(q.exact[0], k.exact[0], v.exact[0])
+    assert np.array_equal(ref_quad, ref_rec)
+    assert_exact(host(o)[0], ref_quad, f"o C={C}")
+    assert_exact(host(S)[0], ref_S, f"S C={C}")
+
+
+@pytest.mark.parametrize("C,group", [(1, 0), (7, 0), (64, 1), (64, 2), (100, 0), (200, 0), (33, 3), (128, 0)])
+def test_int8_ragged_multihead(C, group):
+    q, k, v = _case(1, 3, 200, 64, 32, "i8")
+    log(f"int8 BH=3 L=200 dk=64 dv=32 C={C} group={group}")
+    o, S, _ = la.chunked_forward(dev_input(q), dev_input(k), dev_input(v), C, return_state=True, group=group)
+    ref, refS, _ = _oracle_forward(q.exact, k.exact, v.exact, C)
+    assert_exact(host(o), ref, f"o C={C} g={group}")
+    assert_exact(host(S), refS, f"S C={C} g={group}")
+
+
+@pytest.mark.parametrize("dk,dv", [(16, 16), (128, 64), (256, 16), (32, 128)])
+def test_int8_widths(dk, dv):
+    q, k, v = _case(2, 2, 150, dk, dv, "i8")
+    log(f"int8 widths dk={dk} dv={dv}")
+    o, S, _ = la.chunked_forward(dev_input(q), dev_input(k), dev_input(v), 64, return_state=True)
+    ref, refS, _ = _oracle_forward(q.exact, k.exact, v.exact, 64)
+    assert_exact(host(o), ref, f"o {dk}x{dv}")
+    assert_exact(host(S), refS, f"S {dk}x{dv}")
+
+
+def test_int8_noncausal():
+    q, k, v = _case(3, 2, 130, 64, 64, "i8")
+    log("int8 non-causal")
+    o = la.chunked_forward(dev_input(q), dev_input(k), dev_input(v), 64, causal=False)
+    ref = np.stack([oracle.noncausal_scores_first(q.exact[h], k.exact[h], v.exact[h]) for h in range(2)])
+    assert_exact(host(o), ref, "noncausal")
+
+
+def test_int8_phases():
+    q, k, v = _case(4, 2, 190, 64, 32, "i8")
+    for C in (1, 16, 50, 64, 190):
+        log(f"int8 phases C={C}")
+        S, z = la.chunk_states(dev_input(k), dev_input(v), C, want_z=True)
+        refS = [oracle.chunk_states(k.exact[h], v.exact[h], C) for h in range(2)]
+        assert_exact(host(S), np.stack([r[0] for r in refS]), "chunk states")
+        assert_exact(host(z), np.stack([r[1] for r in refS]), "chunk z")
+        Sf, zf = la.state_scan(S, z)
+        refP = [oracle.exclusive_scan(r[0]) for r in refS]
+        refz = [oracle.exclusive_scan(r[1]) for r in refS]
+        assert_exact(host(S), np.stack([r[0] for r in refP]), "scan")
+        assert_exact(host(Sf), np.stack([r[1] for r in refP]), "scan total")
+        assert_exact(host(z), np.stack([r[0] for r in refz]), "scan z")
+        assert_exact(host(zf), np.stack([r[1] for r in refz]), "scan z total")
+
+
+# ---------------------------------------------------------------------------
+# bf16
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("C", [32, 64, 128, 1, 17, 100, 300, 0])
+def test_bf16_identity_chunks(C):
+    q, k, v = _case(10, 4, 300, 128, 128, "bf16")
+    log(f"bf16 identity d=128 L=300 C={C}")
+    o, S, _ = la.chunked_forward(dev_input(q), dev_input(k), dev_input(v), C, return_state=True)
+    ref, refS, _ = _oracle_forward(q.exact, k.exact, v.exact, C)
+    assert_close(host(o), ref, what=f"o C={C}")
+    assert_close(host(S), refS, what=f"S C={C}")
+
+
+@pytest.mark.parametrize("group", [1, 2, 3, 5, 100])
+def test_bf16_groups(group):
+    q, k, v = _case(11, 2, 640, 64, 64, "bf16")
+    log(f"bf16 groups={group}")
+    o, S, z = la.chunked_forward(dev_input(q), dev_input(k), dev_input(v), 64, normalize=True, fmap="elu1",
+                                 return_state=True, group=group)
+    ref, refS, refz = _oracle_forward(q.exact, k.exact, v.exact, 64, True, True, "elu1")
+    assert_close(host(o), ref, what="o")
+    assert_close(host(S), refS, what="S")
+    assert_close(host(z), refz, what="z")
+
+
+@pytest.mark.parametrize("dk,dv,C", [(16, 16, 16), (32, 128, 64), (64, 32, 40), (256, 64, 64), (256, 16, 32),
+                                     (128, 16, 64), (64, 256, 128), (128, 64, 128)])
+def test_bf16_widths(dk, dv, C):
+    q, k, v = _case(12, 2, 333, dk, dv, "bf16")
+    log(f"bf16 widths dk={dk} dv={dv} C={C}")
+    for norm, fmap in ((False, "identity"), (True, "elu1")):
+        o, S, z = la.chunked_forward(dev_input(q), dev_input(k), dev_input(v), C, normalize=norm, fmap=fmap,
+                                     return_state=True)
+        ref, refS, refz = _oracle_forward(q.exact, k.exact, v.exact, C, True, norm, fmap)
+        assert_close(host(o), ref, what=f"o norm={norm}")
+        assert_close(host(S), refS, what=f"S norm={norm}")
+        if norm:
+            assert_close(host(z), refz, what="z")
+
+
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+def test_bf16_elu1_normalized_out_dtypes(out):
+    torch = torch_cuda()
+    q, k, v = _case(13, 3, 257, 64, 64, "bf16")
+    log(f"bf16 elu1 norm out={out}")
+    od = torch.bfloat16 if out == "bf16" else torch.float32
+    o = la.chunked_forward(dev_input(q), dev_input(k), dev_input(v), 64, normalize=True, fmap="elu1", out_dtype=od)
+    ref, _, _ = _oracle_forward(q.exact, k.exact, v.exact, 64, True, True, "elu1")
+    worst = assert_close(host(o), ref, what=f"o {out}")
+    log(f"worst ratio {worst:.4f}")
+
+
+def test_bf16_in_scale():
+    # inputs 4x the workloads' N(0,1)/sqrt(d) scale, brought back by in_scale = 1/4
+    # (the tolerance band presumes O(1) scores, as on the workloads)
+    q, k, v = _case(14, 2, 200, 64, 64, "bf16", scale=4.0 / 8.0)
+    for fmap, norm in (("identity", False), ("identity", True), ("elu1", True)):
+        log(f"bf16 in_scale fmap={fmap} norm={norm}")
+        o, S, z = la.chunked_forward(dev_input(q), dev_input(k), dev_input(v), 64, normalize=norm, fmap=fmap,
+                                     in_scale=0.25, return_state=True)
+        ref, refS, refz = _oracle_forward(q.exact, k.exact, v.exact, 64, True, norm, fmap, None, 0.25)
+        assert_close(host(o), ref, what=f"in_scale {fmap} o")
+        assert_close(host(S), refS, what=f"in_scale {fmap} S")
+        if norm:
+            assert_close(host(z), refz, what=f"in_scale {fmap} z")
+
+
+def test_bf16_favor_small():
+    q, k, v = _case(15, 2, 300, 64, 64, "bf16", scale=1.0 / 8)
+    Wb, W = wl.orthogonal_random_features(256, 64, [15, 3])
+    log("bf16 favor m=256")
+    from tests.gpu_helpers import dev_bf16
+    o, S, z = la.chunked_forward(dev_input(q), dev_input(k), dev_input(v), 64, normalize=True, fmap="favor",
+                                 W=dev_bf16(Wb), return_state=True)
+    ref, refS, refz = _oracle_forward(q.exact, k.exact, v.exact, 64, True, True, "favor", W)
+    assert_close(host(o), ref, what="favor o")
+    assert_close(host(S), refS, what="favor S")
+    assert_close(host(z), refz, what="favor z")
+
+
+@pytest.mark.parametrize("norm,fmap", [(False, "identity"), (True, "elu1")])
+def test_bf16_noncausal(norm, fmap):
+    q, k, v = _case(16, 3, 210, 64, 64, "bf16")
+    log(f"bf16 non-causal norm={norm}")
+    o, S, z = la.chunked_forward(dev_input(q), dev_input(k), dev_input(v), 64, causal=False, normalize=norm,
+                                 fmap=fmap, return_state=True)
+    ref, refS, refz = _oracle_forward(q.exact, k.exact, v.exact, 64, False, norm, fmap)
+    assert_close(host(o), ref, what="noncausal o")
+    assert_close(host(S), refS, what="noncausal S")
+
+
+def test_bf16_phases():
+    q, k, v = _case(17, 2, 300, 128, 64, "bf16")
+    for C in (1, 32, 64, 100, 300):
+        log(f"bf16 phases C={C}")
+        S, z = la.chunk_states(dev_input(k), dev_input(v), C, want_z=True)
+        refS = [oracle.chunk_states(k.exact[h], v.exact[h], C) for h in range(2)]
+        assert_close(host(S), np.stack([r[0] for r in refS]), what="chunk states")
+        assert_close(host(z), np.stack([r[1] for r in refS]), what="chunk z")
+        Sf, zf = la.state_scan(S, z)
+        refP = [oracle.exclusive_scan(r[0]) for r in refS]
+        assert_close(host(S), np.stack([r[0] for r in refP]), what="scan")
+        assert_close(host(Sf), np.stack([r[1] for r in refP]), what="scan total")
+
+
+def test_feature_maps():
+    torch = torch_cuda()
+    q, _, _ = _case(18, 1, 500, 64, 64, "bf16", scale=1.0)
+    Wb, W = wl.orthogonal_random_features(128, 64, [18, 3])
+    from tests.gpu_helpers import dev_bf16
+    x = dev_input(q)
+    for fmap in ("identity", "elu1", "favor"):
+        log(f"feature map {fmap}")
+        y = la.feature_map(x, fmap, W=dev_bf16(Wb) if fmap == "favor" else None, in_scale=0.5,
+                           out_dtype=torch.float32)
+        ref = oracle.apply_phi(q.exact, fmap, W, 0.5)
+        # fp32 output: relative 1e-5 band, except exp's few-ulp error
+        assert_close(host(y), ref, tol=1e-4, what=fmap)
+        yb = la.feature_map(x, fmap, W=dev_bf16(Wb) if fmap == "favor" else None, in_scale=0.5)
+        assert_close(host(yb), ref, tol=8e-3, what=fmap + " bf16")
+
+
+def test_causality_bitwise():
+    """Changing tokens at and after t leaves every earlier output row bit-identical."""
+    q, k, v = _case(19, 2, 256, 64, 64, "bf16")
+    log("causality")
+    base = host(la.chunked_forward(dev_input(q), dev_input(k), dev_input(v), 64, normalize=True, fmap="elu1"))
+    for t in (0, 63, 64, 100, 255):
+        q2, k2, v2 = [x.bits.copy() for x in (q, k, v)]
+        for b in (q2, k2, v2):
+            b[:, t:] ^= np.uint16(0x0040)
+        from tests.gpu_helpers import dev_bf16
+        pert = host(la.chunked_forward(dev_bf16(q2), dev_bf16(k2), dev_bf16(v2), 64, normalize=True, fmap="elu1"))
+        assert np.array_equal(pert[:, :t], base[:, :t]), t
+
+
+def test_decode_steps_and_resume():
+    torch = torch_cuda()
+    q, k, v = _case(20, 4, 96, 64, 64, "bf16", scale=1.0 / 8)
+    Wb, W = wl.orthogonal_random_features(128, 64, [20, 3])
+    from tests.gpu_helpers import dev_bf16
+    for fmap in ("elu1", "favor", "identity"):
+        norm = fmap != "identity"
+        log(f"decode resume fmap={fmap}")
+        Wd = dev_bf16(Wb) if fmap == "favor" else None
+        L1 = 70
+        qd, kd, vd = dev_input(q), dev_input(k), dev_input(v)
+        o1, S, z = la.chunked_forward(qd[:, :L1].contiguous(), kd[:, :L1].contiguous(), vd[:, :L1].contiguous(),
+                                      32, normalize=norm, fmap=fmap, W=Wd, return_state=True)
+        if z is None:
+            z = torch.zeros(4, S.shape[1], dtype=torch.float32, device="cuda")
+        ref_full, _, _ = _oracle_forward(q.exact, k.exact, v.exact, 32, True, norm, fmap, W)
+        for t in range(L1, 96):
+            o = la.recurrent_step(qd[:, t].contiguous(), kd[:, t].contiguous(), vd[:, t].contiguous(), S, z,
+                                  fmap=fmap, W=Wd, normalize=norm)
+            assert_close(host(o), ref_full[:, t], what=f"decode t={t}")
+        # final state after the steps equals the oracle's
+        _, refS, refz = _oracle_forward(q.exact, k.exact, v.exact, 32, True, norm, fmap, W)
+        assert_close(host(S), refS, what="decode S")
+        if norm:
+            assert_close(host(z), refz, what="decode z")
+
+
+def test_decode_matches_oracle_step():
+    torch = torch_cuda()
+    rng = np.random.default_rng([21, 1])
+    n, dk, dv = 37, 64, 32
+    S0 = rng.standard_normal((n, dk, dv)) * 0.5
+    z0 = np.abs(rng.standard_normal((n, dk))) * 10 + 1
+    q, k, v = _case(21, 1, n, dk, dv, "bf16", scale=0.3)
+    S = torch.tensor(S0, dtype=torch.float32, device="cuda")
+    z = torch.tensor(z0, dtype=torch.float32, device="cuda")
+    log("decode single step")
+    o = la.recurrent_step(dev_input(q)[0], dev_input(k)[0], dev_input(v)[0], S, z, fmap="elu1", normalize=True)
+    S32, z32 = S0.astype(np.float32).astype(np.float64), z0.astype(np.float32).astype(np.float64)
+    for i in range(n):
+        qp, kp = oracle.phi_elu1(q.exact[0, i]), oracle.phi_elu1(k.exact[0, i])
+        ro, rS, rz = oracle.recurrent_step(S32[i], z32[i], qp, kp, v.exact[0, i], True)
+        assert_close(host(o)[i], ro, tol=1e-4, what="o")
+        assert_close(host(S)[i], rS, tol=1e-5, what="S")
+        assert_close(host(z)[i], rz, tol=1e-5, what="z")

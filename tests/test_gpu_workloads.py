@@ -1,0 +1,124 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times (automatic grouping), checked on sampled heads / states that
+the oracle recomputes in full."""
+import numpy as np
+import pytest
+
+import chunked_causal_linear_amd as la
+import oracle
+import workloads as wl
+from tests.gpu_helpers import assert_close, assert_exact, dev_bf16, dev_i8, host, log, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev_full(w, BH=None, L=None):
+    q, k, v, W = wl.workload_inputs(w, BH=BH, L=L, want_exact=False)
+    to = dev_bf16 if w.dtype == "bf16" else dev_i8
+    return to(q.bits), to(k.bits), to(v.bits), W
+
+
+def _oracle_head(w, bh, C, W=None, L=None):
+    q, k, v = wl.head_inputs(w, bh, L)
+    return oracle.forward(q.exact, k.exact, v.exact, C, True, w.normalize, w.fmap, W)
+
+
+def test_workload2_all_heads():
+    w = wl.WORKLOADS[2]
+    log("workload 2 (all 32 heads)")
+    q, k, v, _ = _dev_full(w)
+    o = host(la.chunked_forward(q, k, v, 64, normalize=True, fmap="elu1"))
+    for bh in range(w.BH):
+        ref, _, _ = _oracle_head(w, bh, 64)
+        assert_close(o[bh], ref, what=f"head {bh}")
+
+
+@pytest.mark.parametrize("C", [32, 64, 128])
+def test_workload3_sampled_heads(C):
+    w = wl.WORKLOADS[3]
+    log(f"workload 3 C={C}")
+    q, k, v, _ = _dev_full(w)
+    o, S, _ = la.chunked_forward(q, k, v, C, return_state=True)
+    o, S = host(o), host(S)
+    for bh in (0, 77, w.BH - 1):
+        ref, refS, _ = _oracle_head(w, bh, C)
+        worst = assert_close(o[bh], ref, what=f"o head {bh}")
+        assert_close(S[bh], refS, what=f"S head {bh}")
+        log(f"head {bh} worst ratio {worst:.3f}")
+
+
+def test_workload4_sampled_heads_and_state():
+    w = wl.WORKLOADS[4]
+    log("workload 4")
+    q, k, v, _ = _dev_full(w)
+    o, S, z = la.chunked_forward(q, k, v, 128, normalize=True, fmap="elu1", return_state=True)
+    o, S, z = host(o), host(S), host(z)
+    for bh in (0, w.BH - 1):
+        ref, refS, refz = _oracle_head(w, bh, 128)
+        worst = assert_close(o[bh], ref, what=f"o head {bh}")
+        assert_close(S[bh], refS, what=f"S head {bh}")
+        assert_close(z[bh], refz, what=f"z head {bh}")
+        log(f"head {bh} worst ratio {worst:.3f}")
+
+
+def _favor_W(w):
+    return wl.orthogonal_random_features(w.m, w.d_in, [w.wid, wl.TENSOR_W])
+
+
+def test_workload5_forward_and_decode():
+    torch = torch_cuda()
+    w = wl.WORKLOADS[5]
+    log("workload 5 forward")
+    q, k, v, (Wb, W) = _dev_full(w)
+    Wd = dev_bf16(Wb)
+    o, S, z = la.chunked_forward(q, k, v, 64, normalize=True, fmap="favor", W=Wd, return_state=True)
+    oh, Sh, zh = host(o), host(S), host(z)
+    states = {}
+    for bh in (0, 13, w.BH - 1):
+        ref, refS, refz = _oracle_head(w, bh, 64, W)
+        worst = assert_close(oh[bh], ref, what=f"o head {bh}")
+        assert_close(Sh[bh], refS, what=f"S head {bh}")
+        assert_close(zh[bh], refz, what=f"z head {bh}")
+        states[bh] = (refS, refz)
+        log(f"head {bh} worst ratio {worst:.3f}")
+
+    # decode: 256 streams x 12 heads; stream s starts from batch s % 2 of the forward
+    n = wl.DECODE_STREAMS * w.H
+    idx = torch.tensor([(s % w.B) * w.H + h for s in range(wl.DECODE_STREAMS) for h in range(w.H)], device="cuda")
+    Sd = S[idx].contiguous()
+    zd = z[idx].contiguous()
+    pq, pk, pv = wl.decode_pool(w, n, pool=4)
+    qd, kd, vd = dev_bf16(pq.bits), dev_bf16(pk.bits), dev_bf16(pv.bits)
+    samples = [0, 13, n - 1]  # state (s, h) continues forward head (s % 2) * 12 + h: 0, 13, 23
+    ref_state = {}
+    for st in samples:
+        s, h = divmod(st, w.H)
+        Sr, zr = states[(s % w.B) * w.H + h]
+        ref_state[st] = [Sr.copy(), zr.copy()]
+    steps = 4
+    for t in range(steps):
+        log(f"decode step {t}")
+        out = host(la.recurrent_step(qd[t], kd[t], vd[t], Sd, zd, fmap="favor", W=Wd, normalize=True))
+        for st in samples:
+            Sr, zr = ref_state[st]
+            qp = oracle.phi_favor(pq.exact[t, st], W)
+            kp = oracle.phi_favor(pk.exact[t, st], W)
+            ro, Sr, zr = oracle.recurrent_step(Sr, zr, qp, kp, pv.exact[t, st], True)
+            ref_state[st] = [Sr, zr]
+            assert_close(out[st], ro, what=f"decode state {st} step {t}")
+    Sh2 = host(Sd)
+    for st in samples:
+        assert_close(Sh2[st], ref_state[st][0], what=f"decode S {st}")
+
+
+def test_int8_headline_shape():
+    """int8 at L=8192, d=128 (4 heads): exact, |o| stays well inside int32."""
+    w = wl.WORKLOADS[3]
+    log("int8 headline shape")
+    q, k, v = wl.random_case(31, 4, 8192, 128, 128, "i8")
+    o, S, _ = la.chunked_forward(dev_i8(q.bits), dev_i8(k.bits), dev_i8(v.bits), 64, return_state=True)
+    o, S = host(o), host(S)
+    for bh in range(4):
+        ref, refS, _ = oracle.chunked(q.exact[bh], k.exact[bh], v.exact[bh], 64)
+        assert_exact(o[bh], ref, f"o head {bh}")
+        assert_exact(S[bh], refS, f"S head {bh}")
