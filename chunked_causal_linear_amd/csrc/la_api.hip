@@ -144,10 +144,14 @@ la_status make_plan(Plan& P, la_dtype in_dt, int64_t BH, int64_t L, int64_t d_in
         if (group > 0) {
             P.G = group < P.n_chunks ? group : P.n_chunks;
         } else {
-            // enough workgroups to cover the 256 compute units, otherwise one
-            // sequential walk per (head, column tile)
+            // enough workgroups for the 256 compute units: four per CU over the
+            // launch when two fit at once (the kernels without the hi/lo split
+            // run two per CU), one per CU otherwise; fewer groups mean less
+            // phase-1 traffic, more mean more loads in flight per CU.
+            const bool split = f == LA_FMAP_ELU1 || f == LA_FMAP_FAVOR;
+            const int64_t target = (P.i8 || split) ? 256 : 1024;
             const int64_t base = BH * P.n_dvt;
-            int64_t want = base >= 256 ? 1 : cdiv(256, base);
+            int64_t want = base >= target ? 1 : cdiv(target, base);
             if (want > P.n_chunks) want = P.n_chunks;
             P.G = cdiv(P.n_chunks, want);
         }

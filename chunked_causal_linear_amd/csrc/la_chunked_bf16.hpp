@@ -18,39 +18,53 @@
 //    and denominator each sum their parts before the division).
 //
 // Tiles.  A chunk of C <= T rows is one tile of T rows (rows past the chunk are
-// zero).  A chunk of C > T rows is walked in sub-tiles of T rows; the
-// intra-chunk part of sub-tile t then also visits sub-tiles 0..t-1 of the same
-// chunk (full blocks, no mask) and the state grows only at the chunk's end.
+// zero) and the next chunk's loads are in flight while it computes.  A chunk of
+// C > T rows is walked in sub-tiles of T rows; the intra-chunk part of sub-tile
+// t then also visits sub-tiles 0..t-1 of the same chunk (full blocks, no mask)
+// and the state grows only at the chunk's end.
 //
-// Matrix-core mapping (16x16x32 bf16, fp32 accumulate; see la_common.hpp):
-//   scores   S^T[key][q] = sum_a K[key][a] Q[q][a]     A = K rows, B = Q rows (LDS, row-major)
-//   intra    O[q][j]    += sum_key S[q][key] V[key][j]  A = S rows,  B = V^T rows (LDS)
-//   inter    O[q][j]    += sum_a Q[q][a] P[a][j]        A = Q rows,  B = P from registers
-//   update   P[a][j]    += sum_key K[key][a] V[key][j]  A = K^T rows, B = V^T rows (LDS)
-// P never leaves registers: wave w owns output column block(s) j of O and P;
-// its P accumulators (lane: j = l%16, a = 16*ab + 4*(l/16) + i) feed the inter
-// product directly as the B operand once the a-index inside each 32-wide
-// k-step is permuted consistently on both operands (the A operand reads the
-// same permuted a's from the Q rows).  K^T and V^T are produced by a 4x8
-// register transpose while the tiles are written to LDS.
+// Matrix-core mapping (16x16x32 bf16, fp32 accumulate; see la_common.hpp).
+// Q, K and V sit in LDS row-major, exactly as loaded:
+//   scores   S^T[key][q] = sum_a K[key][a] Q[q][a]     A = K rows, B = Q rows
+//   intra    O[q][j]    += sum_key S[q][key] V[key][j]  A = S rows, B = V columns
+//   inter    O[q][j]    += sum_a Q[q][a] P[a][j]        A = Q rows, B = P from registers
+//   update   P[a][j]    += sum_key K[key][a] V[key][j]  A = K columns, B = V columns
+// The column operands (fixed a or j, eight keys) come from gfx950's LDS
+// transpose read (ds_read_b64_tr_b16): within each 16-lane group, lane
+// 4r + c supplies the address of four consecutive elements of row r, and lane
+// n receives element n of each of the four rows.
+//
+// Inside each 32-wide k-step the reduction index is permuted the same way on
+// both operands: lane group g holds the indices 4g..4g+3 and 16+4g..16+4g+3.
+// That is where the P accumulators of a wave already hold their a's
+// (lane: j = l%16, a = 16*ab + 4*(l/16) + i), so P feeds the inter product
+// without leaving registers; the key operands follow the same order.  Wave w
+// owns output column block(s) j of O and of P.
 #pragma once
 
 #include "la_common.hpp"
 #include "la_kernels.hpp"
 
+#ifndef LA_PREFETCH
+#define LA_PREFETCH 1
+#endif
+#ifndef LA_WAVES_PER_EU
+#define LA_WAVES_PER_EU 2
+#endif
+
 namespace la {
 
 namespace detail {
 
-// LDS geometry for one instantiation.
+// LDS geometry for one instantiation (strides in elements).
 template <int DK, int DVT, int T>
 struct Geo {
-    static constexpr int TK = T < 32 ? 32 : T;  // key extent of K^T, V^T, S (k-steps of 32)
-    static constexpr int QS = DK + 8;           // row stride (elements) of Q, K tiles
-    static constexpr int KS = TK + 8;           // row stride of K^T, V^T, S
-    static constexpr int Q_ELEMS = T * QS;
-    static constexpr int KT_ELEMS = DK * KS;
-    static constexpr int VT_ELEMS = DVT * KS;
+    static constexpr int TK = T < 32 ? 32 : T;  // key extent of the products (k-steps of 32)
+    static constexpr int QS = DK + 16;          // row stride of the Q and K tiles
+    static constexpr int VS = DVT + 16;         // row stride of the V tile
+    static constexpr int KS = TK + 8;           // row stride of the score tile
+    static constexpr int Q_ELEMS = TK * QS;
+    static constexpr int V_ELEMS = TK * VS;
     static constexpr int S_ELEMS = T * KS;
 };
 
@@ -60,9 +74,9 @@ struct Tile {
 };
 
 // ---------------------------------------------------------------------------
-// Global -> register loads of 4x8 units, register -> LDS stores (with phi and
-// transposes).  A unit is 4 rows x 8 columns; unit u covers column group
-// u % (W/8) and row group u / (W/8).
+// Global -> register loads of 4x8 units, register -> LDS row stores.
+// A unit is 4 rows x 8 columns; unit u covers column group u % (W/8) and row
+// group u / (W/8), so consecutive lanes read consecutive 16-byte pieces of a row.
 // ---------------------------------------------------------------------------
 template <int R, int W, int NT>
 struct Units {
@@ -77,10 +91,23 @@ struct URegs {
 };
 
 template <int R, int W, int NT>
-__device__ __forceinline__ void load_units(URegs<R, W, NT>& reg,
-                                           const u16* __restrict__ base, int64_t row_stride,
+__device__ __forceinline__ void load_units(URegs<R, W, NT>& reg, const u16* __restrict__ base, int64_t row_stride,
                                            int col0, int cols_valid, const Tile& t, int tid) {
     constexpr int CG = W / 8;
+    constexpr bool EVEN = Units<R, W, NT>::N % NT == 0;
+    const u16* tb = base + t.row0 * row_stride + col0;
+    if (EVEN && t.valid == R && cols_valid >= W) {
+        // full tile: no per-row checks
+#pragma unroll
+        for (int it = 0; it < Units<R, W, NT>::PER_THREAD; ++it) {
+            const int u = tid + it * NT;
+            const int cg = u % CG, rg = u / CG;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                reg.r[it][i] = *reinterpret_cast<const uint4*>(tb + (int64_t)(rg * 4 + i) * row_stride + cg * 8);
+        }
+        return;
+    }
 #pragma unroll
     for (int it = 0; it < Units<R, W, NT>::PER_THREAD; ++it) {
         const int u = tid + it * NT;
@@ -89,10 +116,8 @@ __device__ __forceinline__ void load_units(URegs<R, W, NT>& reg,
         for (int i = 0; i < 4; ++i) {
             const int r = rg * 4 + i;
             uint4 val = make_uint4(0, 0, 0, 0);
-            if (u < Units<R, W, NT>::N && r < t.valid && cg * 8 < cols_valid) {
-                const u16* p = base + (t.row0 + r) * row_stride + col0 + cg * 8;
-                val = *reinterpret_cast<const uint4*>(p);
-            }
+            if (u < Units<R, W, NT>::N && r < t.valid && cg * 8 < cols_valid)
+                val = *reinterpret_cast<const uint4*>(tb + (int64_t)r * row_stride + cg * 8);
             reg.r[it][i] = val;
         }
     }
@@ -100,8 +125,8 @@ __device__ __forceinline__ void load_units(URegs<R, W, NT>& reg,
 
 // Apply elu+1 to the valid rows of loaded units (zero rows stay zero).
 template <int R, int W, int NT>
-__device__ __forceinline__ void phi_units(URegs<R, W, NT>& reg,
-                                          int cols_valid, const Tile& t, int tid, float in_scale) {
+__device__ __forceinline__ void phi_units(URegs<R, W, NT>& reg, int cols_valid, const Tile& t, int tid,
+                                          float in_scale) {
     constexpr int CG = W / 8;
 #pragma unroll
     for (int it = 0; it < Units<R, W, NT>::PER_THREAD; ++it) {
@@ -129,7 +154,8 @@ __device__ __forceinline__ void phi_split_units(URegs<R, W, NT>& reg, URegs<R, W
         for (int i = 0; i < 4; ++i) {
             const int r = rg * 4 + i;
             uint4 h = reg.r[it][i], l = make_uint4(0, 0, 0, 0);
-            if (u < Units<R, W, NT>::N && r < t.valid && cg * 8 < cols_valid) elu1_split_bf16x8(reg.r[it][i], in_scale, h, l);
+            if (u < Units<R, W, NT>::N && r < t.valid && cg * 8 < cols_valid)
+                elu1_split_bf16x8(reg.r[it][i], in_scale, h, l);
             reg.r[it][i] = h;
             lo.r[it][i] = l;
         }
@@ -146,8 +172,7 @@ __device__ __forceinline__ float sum_bf16x8(const uint4& u) {
 
 // row-major store: dst[r * stride + 8*cg ..]
 template <int R, int W, int NT>
-__device__ __forceinline__ void store_rows(const URegs<R, W, NT>& reg,
-                                           u16* dst, int stride, int tid) {
+__device__ __forceinline__ void store_rows(const URegs<R, W, NT>& reg, u16* dst, int stride, int tid) {
     constexpr int CG = W / 8;
 #pragma unroll
     for (int it = 0; it < Units<R, W, NT>::PER_THREAD; ++it) {
@@ -161,28 +186,9 @@ __device__ __forceinline__ void store_rows(const URegs<R, W, NT>& reg,
     }
 }
 
-// transposed store: dst[(8*cg + c) * stride + 4*rg .. +3] = column c of the unit
-template <int R, int W, int NT>
-__device__ __forceinline__ void store_transposed(const URegs<R, W, NT>& reg,
-                                                 u16* dst, int stride, int tid) {
-    constexpr int CG = W / 8;
-#pragma unroll
-    for (int it = 0; it < Units<R, W, NT>::PER_THREAD; ++it) {
-        const int u = tid + it * NT;
-        if (u < Units<R, W, NT>::N) {
-            const int cg = u % CG, rg = u / CG;
-            uint2 col[8];
-            transpose4x8(reg.r[it], col);
-#pragma unroll
-            for (int c = 0; c < 8; ++c)
-                *reinterpret_cast<uint2*>(dst + (cg * 8 + c) * stride + rg * 4) = col[c];
-        }
-    }
-}
-
-template <typename T>
-__device__ __forceinline__ void zero_lds(T* p, int n, int tid, int nt) {
-    for (int i = tid; i < n; i += nt) p[i] = T(0);
+template <typename E>
+__device__ __forceinline__ void zero_lds(E* p, int n, int tid, int nt) {
+    for (int i = tid; i < n; i += nt) p[i] = E(0);
 }
 
 __device__ __forceinline__ float xor_sum_groups(float x) {
@@ -190,6 +196,32 @@ __device__ __forceinline__ float xor_sum_groups(float x) {
     x += __shfl_xor(x, 16);
     x += __shfl_xor(x, 32);
     return x;
+}
+
+// Column operand of a 32-key k-step: eight keys of one column of a row-major
+// tile (rows = keys), in the permuted key order of the file header.  Lane
+// (g = l/16, r = (l%16)/4, c = l%4) supplies rows key0 + 4g + r and
+// key0 + 16 + 4g + r, columns col0 + 4c .. +3.
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+__device__ __forceinline__ uint2 lds_tr16(const u16* p) {
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p));
+}
+
+__device__ __forceinline__ uint4 column_operand(const u16* tile, int stride, int key0, int col0, int lane) {
+    const int g = lane >> 4, r = (lane & 15) >> 2, c = lane & 3;
+    const u16* ptr = tile + (key0 + 4 * g + r) * stride + col0 + 4 * c;
+    const uint2 lo = lds_tr16(ptr);
+    const uint2 hi = lds_tr16(ptr + 16 * stride);
+    return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+
+// Row operand in the permuted order: row[k0 + 4g .. +3] and row[k0 + 16 + 4g .. +3]
+__device__ __forceinline__ uint4 row_operand_perm(const u16* row, int k0, int g) {
+    const uint2 lo = *reinterpret_cast<const uint2*>(row + k0 + 4 * g);
+    const uint2 hi = *reinterpret_cast<const uint2*>(row + k0 + 16 + 4 * g);
+    return make_uint4(lo.x, lo.y, hi.x, hi.y);
 }
 
 // XCD-aware work index: workgroups are dispatched round-robin over the 8 XCDs;
@@ -210,7 +242,7 @@ using namespace detail;
 // Phase 3 (fused with the carry across the G chunks of a group)
 // ===========================================================================
 template <int DK, int DVT, int T, int NW, bool SPLIT>
-__global__ __launch_bounds__(NW * WAVE) void chunked_fwd_bf16(FwdParams p) {
+__global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(SPLIT ? 1 : LA_WAVES_PER_EU, SPLIT ? 1 : LA_WAVES_PER_EU))) void chunked_fwd_bf16(FwdParams p) {
     using G = Geo<DK, DVT, T>;
     constexpr int NT = NW * WAVE;
     constexpr int NB = T / 16;             // 16-row blocks per tile
@@ -223,9 +255,8 @@ __global__ __launch_bounds__(NW * WAVE) void chunked_fwd_bf16(FwdParams p) {
 
     __shared__ __attribute__((aligned(16))) u16 Qs[G::Q_ELEMS];
     __shared__ __attribute__((aligned(16))) u16 Ks[G::Q_ELEMS];
-    __shared__ __attribute__((aligned(16))) u16 KTs[G::KT_ELEMS];
-    __shared__ __attribute__((aligned(16))) u16 KLs[SPLIT ? G::KT_ELEMS : 8];  // lo part of phi(K)^T
-    __shared__ __attribute__((aligned(16))) u16 VTs[G::VT_ELEMS];
+    __shared__ __attribute__((aligned(16))) u16 KLs[SPLIT ? G::Q_ELEMS : 8];  // lo part of phi(K)
+    __shared__ __attribute__((aligned(16))) u16 Vs[G::V_ELEMS];
     __shared__ __attribute__((aligned(16))) u16 Ss[G::S_ELEMS];
     __shared__ float zs[DK];
     __shared__ float dens[T];
@@ -248,12 +279,13 @@ __global__ __launch_bounds__(NW * WAVE) void chunked_fwd_bf16(FwdParams p) {
     const u16* __restrict__ qh = p.q + bh * L * p.dk_g;
     const u16* __restrict__ kh = p.k + bh * L * p.dk_g;
     const u16* __restrict__ vh = p.v + bh * L * p.dv;
+    const u16* __restrict__ klh = p.k_lo != nullptr ? p.k_lo + bh * L * p.dk_g : nullptr;
 
+    // rows past the tile (T < 32) and score blocks never written stay zero
     zero_lds(Qs, G::Q_ELEMS, tid, NT);
     zero_lds(Ks, G::Q_ELEMS, tid, NT);
-    zero_lds(KTs, G::KT_ELEMS, tid, NT);
-    if (SPLIT) zero_lds(KLs, G::KT_ELEMS, tid, NT);
-    zero_lds(VTs, G::VT_ELEMS, tid, NT);
+    if (SPLIT) zero_lds(KLs, G::Q_ELEMS, tid, NT);
+    zero_lds(Vs, G::V_ELEMS, tid, NT);
     zero_lds(Ss, G::S_ELEMS, tid, NT);
 
     // ---- state: P accumulators for this wave's column blocks, z for its a-blocks
@@ -308,7 +340,6 @@ __global__ __launch_bounds__(NW * WAVE) void chunked_fwd_bf16(FwdParams p) {
         const int64_t re = r0 + T < ce ? r0 + T : ce;
         return Tile{r0, (int)(re - r0)};
     };
-    const u16* __restrict__ klh = p.k_lo != nullptr ? p.k_lo + bh * L * p.dk_g : nullptr;
     auto load_qkv = [&](const Tile& t) {
         load_units<T, DK, NT>(rq, qh, p.dk_g, 0, p.dk_g, t, tid);
         load_units<T, DK, NT>(rk, kh, p.dk_g, 0, p.dk_g, t, tid);
@@ -325,9 +356,8 @@ __global__ __launch_bounds__(NW * WAVE) void chunked_fwd_bf16(FwdParams p) {
         }
         store_rows<T, DK, NT>(rq, Qs, G::QS, tid);
         store_rows<T, DK, NT>(rk, Ks, G::QS, tid);
-        store_transposed<T, DK, NT>(rk, KTs, G::KS, tid);
-        if (SPLIT) store_transposed<T, DK, NT>(rkl, KLs, G::KS, tid);
-        store_transposed<T, DVT, NT>(rv, VTs, G::KS, tid);
+        if (SPLIT) store_rows<T, DK, NT>(rkl, KLs, G::QS, tid);
+        store_rows<T, DVT, NT>(rv, Vs, G::VS, tid);
     };
 
     // scores for blocks (qb, kb): diagonal pass masks kb == qb and writes zeros
@@ -380,7 +410,7 @@ __global__ __launch_bounds__(NW * WAVE) void chunked_fwd_bf16(FwdParams p) {
         for (int c = 0; c < CPW; ++c)
 #pragma unroll
             for (int ks = 0; ks < NKS_K; ++ks)
-                vb[c][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(VTs + ((wave + c * NW) * 16 + l16) * G::KS + ks * 32 + g * 8));
+                vb[c][ks] = as_bf16x8(column_operand(Vs, G::VS, ks * 32, (wave + c * NW) * 16, lane));
     };
 
     // inter + diagonal intra products and the state update, for the tile in LDS
@@ -393,18 +423,16 @@ __global__ __launch_bounds__(NW * WAVE) void chunked_fwd_bf16(FwdParams p) {
             const bool own_den = p.normalize && (qb % NW == wave);
 #pragma unroll
             for (int c = 0; c < CPW; ++c) O[c][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const u16* qrow = Qs + (qb * 16 + l16) * G::QS;
 #pragma unroll
             for (int ks = 0; ks < NKS_A; ++ks) {
-                const u16* qrow = Qs + (qb * 16 + l16) * G::QS + ks * 32 + g * 4;
-                const uint2 lo = *reinterpret_cast<const uint2*>(qrow);
-                const uint2 hi = *reinterpret_cast<const uint2*>(qrow + 16);
-                const bf16x8 a = bf16x8_from2(lo, hi);
+                const uint4 qa = row_operand_perm(qrow, ks * 32, g);
 #pragma unroll
-                for (int c = 0; c < CPW; ++c) O[c][qb] = mfma_bf16(a, Pb[c][ks], O[c][qb]);
+                for (int c = 0; c < CPW; ++c) O[c][qb] = mfma_bf16(as_bf16x8(qa), Pb[c][ks], O[c][qb]);
                 if (own_den) {
                     // q . z over the eight a's this lane holds (a0 .. a0+3, a0+16 .. a0+19)
                     const int a0 = ks * 32 + g * 4;
-                    const uint32_t qw[4] = {lo.x, lo.y, hi.x, hi.y};
+                    const uint32_t qw[4] = {qa.x, qa.y, qa.z, qa.w};
                     float s = 0.f;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
@@ -415,9 +443,10 @@ __global__ __launch_bounds__(NW * WAVE) void chunked_fwd_bf16(FwdParams p) {
                 }
             }
             if (!p.noncausal) {
+                const u16* srow = Ss + (qb * 16 + l16) * G::KS;
 #pragma unroll
                 for (int ks = 0; ks < (qb + 2) / 2; ++ks) {
-                    const uint4 su = *reinterpret_cast<const uint4*>(Ss + (qb * 16 + l16) * G::KS + ks * 32 + g * 8);
+                    const uint4 su = row_operand_perm(srow, ks * 32, g);
 #pragma unroll
                     for (int c = 0; c < CPW; ++c) O[c][qb] = mfma_bf16(as_bf16x8(su), vb[c][ks], O[c][qb]);
                     if (own_den) den[qb] += sum_bf16x8(su);
@@ -432,12 +461,12 @@ __global__ __launch_bounds__(NW * WAVE) void chunked_fwd_bf16(FwdParams p) {
                 float zs_part = 0.f;
 #pragma unroll
                 for (int ks = 0; ks < NKS_K; ++ks) {
-                    const uint4 ku = *reinterpret_cast<const uint4*>(KTs + (ab * 16 + l16) * G::KS + ks * 32 + g * 8);
+                    const uint4 ku = column_operand(Ks, G::QS, ks * 32, ab * 16, lane);
 #pragma unroll
                     for (int c = 0; c < CPW; ++c) P[c][ab] = mfma_bf16(as_bf16x8(ku), vb[c][ks], P[c][ab]);
                     if (own_z) zs_part += sum_bf16x8(ku);
                     if (SPLIT) {
-                        const uint4 kl = *reinterpret_cast<const uint4*>(KLs + (ab * 16 + l16) * G::KS + ks * 32 + g * 8);
+                        const uint4 kl = column_operand(KLs, G::QS, ks * 32, ab * 16, lane);
 #pragma unroll
                         for (int c = 0; c < CPW; ++c) P[c][ab] = mfma_bf16(as_bf16x8(kl), vb[c][ks], P[c][ab]);
                         if (own_z) zs_part += sum_bf16x8(kl);
@@ -450,12 +479,12 @@ __global__ __launch_bounds__(NW * WAVE) void chunked_fwd_bf16(FwdParams p) {
 
     // intra products against an earlier sub-tile of the same chunk (C > T)
     auto prev_products = [&](const Tile& tp) {
-        __syncthreads();  // Ks / VTs / Ss readers done
+        __syncthreads();  // Ks / Vs / Ss readers done
         load_units<T, DK, NT>(rk, kh, p.dk_g, 0, p.dk_g, tp, tid);
         load_units<T, DVT, NT>(rv, vh, p.dv, col0, p.dv - col0, tp, tid);
         if (p.fmap == FMAP_ELU1) phi_units<T, DK, NT>(rk, p.dk_g, tp, tid, p.in_scale);
         store_rows<T, DK, NT>(rk, Ks, G::QS, tid);
-        store_transposed<T, DVT, NT>(rv, VTs, G::KS, tid);
+        store_rows<T, DVT, NT>(rv, Vs, G::VS, tid);
         __syncthreads();
         scores(false);
         __syncthreads();
@@ -463,9 +492,10 @@ __global__ __launch_bounds__(NW * WAVE) void chunked_fwd_bf16(FwdParams p) {
 #pragma unroll
         for (int qb = 0; qb < NB; ++qb) {
             const bool own_den = p.normalize && (qb % NW == wave);
+            const u16* srow = Ss + (qb * 16 + l16) * G::KS;
 #pragma unroll
             for (int ks = 0; ks < NKS_K; ++ks) {
-                const uint4 su = *reinterpret_cast<const uint4*>(Ss + (qb * 16 + l16) * G::KS + ks * 32 + g * 8);
+                const uint4 su = row_operand_perm(srow, ks * 32, g);
 #pragma unroll
                 for (int c = 0; c < CPW; ++c) O[c][qb] = mfma_bf16(as_bf16x8(su), vb[c][ks], O[c][qb]);
                 if (own_den) den[qb] += sum_bf16x8(su);
@@ -534,13 +564,14 @@ __global__ __launch_bounds__(NW * WAVE) void chunked_fwd_bf16(FwdParams p) {
     if (C <= T) {
         // one tile per chunk: the next chunk's loads are in flight while this
         // chunk computes
-        if (c_begin < c_end) load_qkv(tile_of(c_begin, 0));
+        if (LA_PREFETCH && c_begin < c_end) load_qkv(tile_of(c_begin, 0));
         for (int64_t chunk = c_begin; chunk < c_end; ++chunk) {
             const Tile t = tile_of(chunk, 0);
             snapshot();
+            if (!LA_PREFETCH) load_qkv(t);
             __syncthreads();  // previous chunk's readers of the LDS tiles are done
             write_qkv(t);
-            if (chunk + 1 < c_end) load_qkv(tile_of(chunk + 1, 0));
+            if (LA_PREFETCH && chunk + 1 < c_end) load_qkv(tile_of(chunk + 1, 0));
             __syncthreads();
             if (!p.noncausal) scores(true);
             __syncthreads();
@@ -612,9 +643,9 @@ __global__ __launch_bounds__(NW * WAVE) void chunk_states_bf16(StatesParams p) {
     constexpr int CPW = CB / NW;
     static_assert(CPW * NW == CB, "column blocks must split evenly over waves");
 
-    __shared__ __attribute__((aligned(16))) u16 KTs[G::KT_ELEMS];
-    __shared__ __attribute__((aligned(16))) u16 KLs[SPLIT ? G::KT_ELEMS : 8];
-    __shared__ __attribute__((aligned(16))) u16 VTs[G::VT_ELEMS];
+    __shared__ __attribute__((aligned(16))) u16 Ks[G::Q_ELEMS];
+    __shared__ __attribute__((aligned(16))) u16 KLs[SPLIT ? G::Q_ELEMS : 8];
+    __shared__ __attribute__((aligned(16))) u16 Vs[G::V_ELEMS];
 
     const int tid = threadIdx.x;
     const int wave = tid / WAVE, lane = tid % WAVE, l16 = lane % 16, g = lane / 16;
@@ -632,6 +663,7 @@ __global__ __launch_bounds__(NW * WAVE) void chunk_states_bf16(StatesParams p) {
 
     const u16* __restrict__ kh = p.k + bh * L * p.dk_g;
     const u16* __restrict__ vh = p.v + bh * L * p.dv;
+    const u16* __restrict__ klh = p.k_lo != nullptr ? p.k_lo + bh * L * p.dk_g : nullptr;
 
     f32x4 P[CPW][NAB];
     float zacc[NAB];
@@ -645,7 +677,6 @@ __global__ __launch_bounds__(NW * WAVE) void chunk_states_bf16(StatesParams p) {
     URegs<T, DK, NT> rk, rkl;
     URegs<T, DVT, NT> rv;
 
-    const u16* __restrict__ klh = p.k_lo != nullptr ? p.k_lo + bh * L * p.dk_g : nullptr;
     for (int64_t r0 = cs; r0 < ce; r0 += T) {
         const Tile t{r0, (int)((ce - r0) < T ? (ce - r0) : T)};
         load_units<T, DK, NT>(rk, kh, p.dk_g, 0, p.dk_g, t, tid);
@@ -658,29 +689,28 @@ __global__ __launch_bounds__(NW * WAVE) void chunk_states_bf16(StatesParams p) {
                 phi_units<T, DK, NT>(rk, p.dk_g, t, tid, p.in_scale);
         }
         __syncthreads();
-        store_transposed<T, DK, NT>(rk, KTs, G::KS, tid);
-        if (SPLIT) store_transposed<T, DK, NT>(rkl, KLs, G::KS, tid);
-        store_transposed<T, DVT, NT>(rv, VTs, G::KS, tid);
+        store_rows<T, DK, NT>(rk, Ks, G::QS, tid);
+        if (SPLIT) store_rows<T, DK, NT>(rkl, KLs, G::QS, tid);
+        store_rows<T, DVT, NT>(rv, Vs, G::VS, tid);
         __syncthreads();
         bf16x8 vb[CPW][NKS_K];
 #pragma unroll
         for (int c = 0; c < CPW; ++c)
 #pragma unroll
             for (int ks = 0; ks < NKS_K; ++ks)
-                vb[c][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(VTs + ((wave + c * NW) * 16 + l16) * G::KS + ks * 32 + g * 8));
+                vb[c][ks] = as_bf16x8(column_operand(Vs, G::VS, ks * 32, (wave + c * NW) * 16, lane));
 #pragma unroll
         for (int ab = 0; ab < NAB; ++ab) {
             const bool own_z = p.want_z && (ab % NW == wave);
             float part = 0.f;
 #pragma unroll
             for (int ks = 0; ks < NKS_K; ++ks) {
-                const uint4 ku = *reinterpret_cast<const uint4*>(KTs + (ab * 16 + l16) * G::KS + ks * 32 + g * 8);
-                const bf16x8 a = as_bf16x8(ku);
+                const uint4 ku = column_operand(Ks, G::QS, ks * 32, ab * 16, lane);
 #pragma unroll
-                for (int c = 0; c < CPW; ++c) P[c][ab] = mfma_bf16(a, vb[c][ks], P[c][ab]);
+                for (int c = 0; c < CPW; ++c) P[c][ab] = mfma_bf16(as_bf16x8(ku), vb[c][ks], P[c][ab]);
                 if (own_z) part += sum_bf16x8(ku);
                 if (SPLIT) {
-                    const uint4 kl = *reinterpret_cast<const uint4*>(KLs + (ab * 16 + l16) * G::KS + ks * 32 + g * 8);
+                    const uint4 kl = column_operand(KLs, G::QS, ks * 32, ab * 16, lane);
 #pragma unroll
                     for (int c = 0; c < CPW; ++c) P[c][ab] = mfma_bf16(as_bf16x8(kl), vb[c][ks], P[c][ab]);
                     if (own_z) part += sum_bf16x8(kl);
@@ -714,22 +744,18 @@ __global__ __launch_bounds__(NW * WAVE) void chunk_states_bf16(StatesParams p) {
     }
 }
 
-}  // namespace la
-
-namespace la {
-
-// Launch one instantiation (waves = column blocks, at most four).
 // LDS bytes of one chunked_fwd_bf16 instantiation.
 template <int DK, int DVT, int T, bool SPLIT>
 constexpr int fwd_lds_bytes() {
     using G = Geo<DK, DVT, T>;
-    return 2 * (2 * G::Q_ELEMS + (SPLIT ? 2 : 1) * G::KT_ELEMS + G::VT_ELEMS + G::S_ELEMS) + 4 * (DK + T);
+    return 2 * ((SPLIT ? 3 : 2) * G::Q_ELEMS + G::V_ELEMS + G::S_ELEMS) + 4 * (DK + T);
 }
 
 constexpr int LDS_LIMIT = 160 * 1024;
 
 // The hi/lo split of phi(K) is compiled in when phi is applied in the kernel
-// (instantiations whose LDS would not fit are rejected; the planner avoids them).
+// or arrives pre-mapped with its residual (instantiations whose LDS would not
+// fit are rejected; the planner avoids them).
 template <int DK, int DVT, int T>
 hipError_t launch_fwd_bf16(const FwdParams& p, int64_t grid, hipStream_t s) {
     constexpr int NW = DVT / 16 < 4 ? DVT / 16 : 4;

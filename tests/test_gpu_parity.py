@@ -149,7 +149,11 @@ def test_bf16_in_scale():
     # inputs 4x the workloads' N(0,1)/sqrt(d) scale, brought back by in_scale = 1/4
     # (the tolerance band presumes O(1) scores, as on the workloads)
     q, k, v = _case(14, 2, 200, 64, 64, "bf16", scale=4.0 / 8.0)
-    for fmap, norm in (("identity", False), ("identity", True), ("elu1", True)):
+    # (identity with the normaliser is left out: with signed features the
+    # denominator can vanish and the quotient is ill-conditioned; elu+1 without
+    # it sums positive scores of size ~d into outputs of size ~L*d, far outside
+    # the O(1) scale the tolerance band is written for)
+    for fmap, norm in (("identity", False), ("elu1", True)):
         log(f"bf16 in_scale fmap={fmap} norm={norm}")
         o, S, z = la.chunked_forward(dev_input(q), dev_input(k), dev_input(v), 64, normalize=norm, fmap=fmap,
                                      in_scale=0.25, return_state=True)
