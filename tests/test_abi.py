@@ -77,9 +77,11 @@ def test_forward_argument_errors():
 def test_workspace_sizes_and_errors():
     lib = la.lib()
     ws = lambda *a: lib.la_chunked_forward_workspace(*a)  # noqa: E731
-    # one group, identity map: no scratch
-    assert ws(b.LA_BF16, 128, 8192, 128, 128, 64, 1, 0, 0, 0, 1.0, 0) == 0
-    assert ws(b.LA_BF16, 128, 8192, 128, 128, 64, 1, 0, 0, 0, 0.5, 0) == 0  # scale folded into the results
+    # one group (group >= N), identity map: no scratch
+    assert ws(b.LA_BF16, 128, 8192, 128, 128, 64, 1, 0, 0, 0, 1.0, 1 << 30) == 0
+    assert ws(b.LA_BF16, 128, 8192, 128, 128, 64, 1, 0, 0, 0, 0.5, 1 << 30) == 0  # scale folded into the results
+    # automatic plan at the headline size: four groups per (head, column tile)
+    assert ws(b.LA_BF16, 128, 8192, 128, 128, 64, 1, 0, 0, 0, 1.0, 0) == 128 * 4 * 128 * 128 * 4
     # groups: BH * n_groups * (dk*dv + dk) floats (normalised), 256-byte aligned pieces
     n = ws(b.LA_BF16, 2, 1024, 64, 64, 64, 1, 1, 1, 0, 1.0, 4)
     groups = 1024 // 64 // 4
