@@ -119,23 +119,42 @@ def run_headline(args):
     qd, kd, vd = dev_bf16(q.bits), dev_bf16(k.bits), dev_bf16(v.bits)
     del q, k, v
     fwd = la.Forward(qd, kd, vd, C, causal=True, normalize=False, fmap="identity", group=args.group)
+    G = la.forward_group(0, w.BH, w.L, w.d_in, w.d_v, C, True, False, "identity", 0, args.group)
+    n_chunks = (w.L + C - 1) // C
+    n_groups = (n_chunks + G - 1) // G
     torch.cuda.synchronize()
-    log(f"warmup {args.warmup}, timing {args.steps} steps, C={C}, workspace {fwd.ws_bytes} B")
+    log(f"warmup {args.warmup}, timing {args.steps} steps, C={C}, group={G} ({n_groups} groups), "
+        f"workspace {fwd.ws_bytes} B")
     ms = time_steps(fwd.run, args.steps, args.warmup)
-    per = per_launch_ms(fwd.run, min(args.steps, 20))
+
+    # the phases one by one (same kernels the forward launches)
+    S, _ = la.chunk_states(kd, vd, C * G)
+    la.state_scan(S, None, want_final=False)
+    o3 = torch.empty_like(fwd.o)
+    ph3 = lambda: la.chunk_output(qd, kd, vd, C, G, P_prefix=S, out=o3)  # noqa: E731
+    ph1 = lambda: la.chunk_states(kd, vd, C * G)  # noqa: E731
+    S2 = S.clone()
+    ph2 = lambda: la.state_scan(S2, None, want_final=False)  # noqa: E731
+    for fn in (ph3, ph1, ph2):
+        fn()
+    torch.cuda.synchronize()
+    k3 = float(np.mean(per_launch_ms(ph3, 20)))
+    k1 = float(np.mean(per_launch_ms(ph1, 10))) if n_groups > 1 else 0.0
+    k2 = float(np.mean(per_launch_ms(ph2, 10))) if n_groups > 1 else 0.0
+    assert torch.equal(o3, fwd.o), "phase 3 alone differs from the forward"
+
     work = Work(w.BH, w.L, w.d_in, w.d_k, w.d_v, C)
     tokens = w.B * w.L
     flops = work.page_flops()
     useful = 2 * work.causal_useful_macs()
-    alg_bytes = work.fused_bytes()
+    prefix_bytes = w.BH * (n_groups - 1) * w.d_k * w.d_v * 4
+    alg_bytes3 = work.fused_bytes() + prefix_bytes
     sec = ms * 1e-3
-    # single-launch plan: the forward is one kernel, so its event time is the kernel's
-    kern_ms = float(np.mean(per))
-    achieved_gbs = alg_bytes / (kern_ms * 1e-3) / 1e9
+    achieved_gbs = alg_bytes3 / (k3 * 1e-3) / 1e9
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         tr = json.load(open(TRAFFIC_FILE))
-        if tr.get("lib_hash") == lib_hash() and tr.get("chunk") == C:
+        if tr.get("lib_hash") == lib_hash() and tr.get("chunk") == C and tr.get("group") == G:
             traffic = tr.get("bytes_per_launch")
     res = {
         "metric": METRIC,
@@ -152,15 +171,18 @@ def run_headline(args):
         "data": "synthetic",
         "config": {"workload": f"{w.name}: B={w.B} H={w.H} L={w.L} d_k=d_v={w.d_in} bf16, identity map, "
                                f"no normaliser, causal, C={C}",
-                   "B": w.B, "H": w.H, "L": w.L, "d": w.d_in, "C": C, "parallelism": "single-gpu"},
+                   "B": w.B, "H": w.H, "L": w.L, "d": w.d_in, "C": C, "chunks_per_group": G,
+                   "parallelism": "single-gpu"},
         "tflops_page_count": flops / sec / 1e12,
         "mfma_frac_page_count": flops / sec / 1e12 / PEAK_BF16_TFLOPS,
         "tflops_causal_useful": useful / sec / 1e12,
         "head_tokens_per_s": w.BH * w.L / sec,
+        "phases_ms": {"chunk_states": k1, "state_scan": k2, "chunk_output": k3},
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved_gbs / PEAK_HBM_GBS, "traffic": traffic,
-                     "kernel": "chunked_fwd_bf16", "alg_bytes_per_launch": alg_bytes,
-                     "avg_launch_ms": kern_ms},
+                     "kernel": "chunked_fwd_bf16 (la_chunk_output)", "alg_bytes_per_launch": alg_bytes3,
+                     "avg_launch_ms": k3,
+                     "mfma_frac_of_kernel": flops / (k3 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
     }
     return res, fwd
 

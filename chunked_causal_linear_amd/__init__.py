@@ -6,9 +6,9 @@ library is loaded on first use; calling any entry point without it raises
 ``LibraryNotBuilt``.
 """
 from .binding import (  # noqa: F401
-    EXPORTS, FMAPS, LAError, LibraryNotBuilt, Forward, chunk_states, chunked_forward, feature_map,
-    forward_workspace_bytes, lib, recurrent_step, state_scan,
+    EXPORTS, FMAPS, LAError, LibraryNotBuilt, Forward, chunk_output, chunk_states, chunked_forward, feature_map,
+    forward_group, forward_workspace_bytes, lib, recurrent_step, state_scan,
 )
 
-__all__ = ["chunked_forward", "Forward", "chunk_states", "state_scan", "feature_map", "recurrent_step",
+__all__ = ["chunked_forward", "Forward", "chunk_states", "chunk_output", "state_scan", "feature_map", "recurrent_step",
            "forward_workspace_bytes", "lib", "LAError", "LibraryNotBuilt", "EXPORTS", "FMAPS"]

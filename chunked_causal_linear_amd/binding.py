@@ -24,8 +24,8 @@ LA_BF16, LA_F32, LA_I8, LA_I32 = range(4)
 FMAPS = {"identity": 0, "elu1": 1, "favor": 2}
 
 EXPORTS = (
-    "la_feature_map", "la_chunk_states", "la_state_scan", "la_chunked_forward",
-    "la_chunked_forward_workspace", "la_recurrent_step", "la_status_string", "la_last_error",
+    "la_feature_map", "la_chunk_states", "la_state_scan", "la_chunk_output", "la_chunked_forward",
+    "la_chunked_forward_workspace", "la_chunked_forward_group", "la_recurrent_step", "la_status_string", "la_last_error",
     "la_version",
 )
 
@@ -48,12 +48,16 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.la_feature_map.argtypes = [i32, vp, i32, i64, i64, vp, i64, f32, vp, i32, vp]
     lib.la_chunk_states.argtypes = [vp, vp, i32, i64, i64, i64, i64, i64, vp, vp, vp]
     lib.la_state_scan.argtypes = [vp, vp, i32, i64, i64, i64, i64, vp, vp, vp]
+    lib.la_chunk_output.argtypes = [vp, vp, vp, i32, i64, i64, i64, i64, i64, i64, vp, vp, i32, vp, i32, vp, vp, vp]
     lib.la_chunked_forward.argtypes = [vp, vp, vp, i32, i64, i64, i64, i64, i64, i32, i32, i32, vp, i64, f32,
                                        vp, i32, vp, vp, i64, vp, sz, vp]
     lib.la_chunked_forward_workspace.argtypes = [i32, i64, i64, i64, i64, i64, i32, i32, i32, i64, f32, i64]
     lib.la_chunked_forward_workspace.restype = sz
+    lib.la_chunked_forward_group.argtypes = [i32, i64, i64, i64, i64, i64, i32, i32, i32, i64, i64]
+    lib.la_chunked_forward_group.restype = i64
     lib.la_recurrent_step.argtypes = [vp, vp, vp, i32, i64, i64, i64, i32, vp, i64, f32, i32, vp, vp, vp, i32, vp]
-    for name in ("la_feature_map", "la_chunk_states", "la_state_scan", "la_chunked_forward", "la_recurrent_step"):
+    for name in ("la_feature_map", "la_chunk_states", "la_state_scan", "la_chunk_output", "la_chunked_forward",
+                 "la_recurrent_step"):
         getattr(lib, name).restype = i32
     lib.la_status_string.argtypes = [i32]
     lib.la_status_string.restype = ctypes.c_char_p
@@ -164,10 +168,38 @@ def state_scan(S, z=None, want_final: bool = True):
     return Sf, zf
 
 
+def chunk_output(q, k, v, C: int, group: int, P_prefix=None, z_prefix=None, normalize: bool = False,
+                 out_dtype=None, return_state: bool = False, out=None):
+    """Phase 3 alone from group prefix states (see la_chunk_output)."""
+    torch = _torch()
+    BH, L, d_k = q.shape
+    d_v = v.shape[-1]
+    i8 = q.dtype == torch.int8
+    if out is None:
+        out = torch.empty(BH, L, d_v, dtype=out_dtype or (torch.int32 if i8 else torch.bfloat16), device=q.device)
+    st = torch.int32 if i8 else torch.float32
+    Sf = torch.empty(BH, d_k, d_v, dtype=st, device=q.device) if return_state else None
+    zf = torch.empty(BH, d_k, dtype=torch.float32, device=q.device) if (return_state and normalize) else None
+    _check(lib().la_chunk_output(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dtype_code(q), BH, L, d_k, d_v, C,
+                                 group, _dev(P_prefix, "P_prefix"), _dev(z_prefix, "z_prefix"), int(normalize),
+                                 _dev(out, "o"), _dtype_code(out), _dev(Sf, "S_final"), _dev(zf, "z_final"),
+                                 _stream_ptr()))
+    if return_state:
+        return out, Sf, zf
+    return out
+
+
 def forward_workspace_bytes(in_dtype_code: int, BH: int, L: int, d_in: int, d_v: int, C: int, causal: bool,
                             normalize: bool, fmap: str, m: int = 0, in_scale: float = 1.0, group: int = 0) -> int:
     return int(lib().la_chunked_forward_workspace(in_dtype_code, BH, L, d_in, d_v, C, int(causal), int(normalize),
                                                   _fmap_code(fmap), m, float(in_scale), group))
+
+
+def forward_group(in_dtype_code: int, BH: int, L: int, d_in: int, d_v: int, C: int, causal: bool,
+                  normalize: bool, fmap: str, m: int = 0, group: int = 0) -> int:
+    """Chunks per group la_chunked_forward uses for these arguments."""
+    return int(lib().la_chunked_forward_group(in_dtype_code, BH, L, d_in, d_v, C, int(causal), int(normalize),
+                                              _fmap_code(fmap), m, group))
 
 
 class Forward:

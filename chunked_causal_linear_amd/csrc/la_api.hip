@@ -176,6 +176,69 @@ bool xcd_ok(int64_t grid) { return grid >= 8 && grid % 8 == 0; }
 
 }  // namespace
 
+// Phase 3 for a planned call: the fused output kernel over every (head,
+// group, column tile), starting each group from its prefix state.
+static la_status launch_phase3(const Plan& P, const void* qm, const void* km, const void* klo, const void* v,
+                               void* o, la_dtype out_dt, const void* states, const void* zst, void* S_final,
+                               void* z_final, int fmap_in_kernel, float in_scale, bool scaled_identity,
+                               hipStream_t s) {
+    const int64_t BH = P.BH, L = P.L, d_v = P.dv;
+    const int64_t grid = BH * P.n_groups * P.n_dvt;
+    if (P.i8) {
+        la::FwdParamsI8 p{};
+        p.q = static_cast<const signed char*>(qm);
+        p.k = static_cast<const signed char*>(km);
+        p.v = static_cast<const signed char*>(v);
+        p.o = static_cast<int*>(o);
+        p.P0 = static_cast<const int*>(states);
+        p.S_final = static_cast<int*>(S_final);
+        p.L = L;
+        p.C = (int)P.C;
+        p.G = (int)P.G;
+        p.n_groups = (int)P.n_groups;
+        p.n_dvt = P.n_dvt;
+        p.dk_g = (int)P.dk;
+        p.dv = (int)d_v;
+        p.xcd_remap = xcd_ok(grid);
+        p.noncausal = !P.causal;
+        return hip_status(la::run_chunked_fwd_i8(p, P.DK, P.DVT, P.T, grid, s), "chunked forward launch");
+    }
+    la::FwdParams p{};
+    p.q = static_cast<const unsigned short*>(qm);
+    p.k = static_cast<const unsigned short*>(km);
+    p.v = static_cast<const unsigned short*>(v);
+    p.k_lo = static_cast<const unsigned short*>(klo);
+    p.o = o;
+    p.P0 = static_cast<const float*>(states);
+    p.z0 = static_cast<const float*>(zst);
+    p.S_final = static_cast<float*>(S_final);
+    p.z_final = static_cast<float*>(z_final);
+    p.L = L;
+    p.C = (int)P.C;
+    p.G = (int)P.G;
+    p.n_groups = (int)P.n_groups;
+    p.n_dvt = P.n_dvt;
+    p.dk_g = (int)P.dk;
+    p.dv = (int)d_v;
+    p.fmap = fmap_in_kernel;
+    p.in_scale = in_scale;
+    p.normalize = P.normalize;
+    p.out_f32 = out_dt == LA_F32;
+    p.xcd_remap = xcd_ok(grid);
+    p.noncausal = !P.causal;
+    p.out_scale = (scaled_identity && !P.normalize) ? in_scale * in_scale : 1.0f;
+    p.state_scale = scaled_identity ? in_scale : 1.0f;
+    hipError_t e;
+    switch (P.DK) {
+        case 32: e = la::fwd_bf16_dk32(p, P.DVT, P.T, grid, s); break;
+        case 64: e = la::fwd_bf16_dk64(p, P.DVT, P.T, grid, s); break;
+        case 128: e = la::fwd_bf16_dk128(p, P.DVT, P.T, grid, s); break;
+        default: e = la::fwd_bf16_dk256(p, P.DVT, P.T, grid, s); break;
+    }
+    return hip_status(e, "chunked forward launch");
+}
+
+
 extern "C" {
 
 const char* la_status_string(la_status s) {
@@ -327,6 +390,16 @@ size_t la_chunked_forward_workspace(la_dtype in_dt, int64_t BH, int64_t L, int64
     return P.ws_total;
 }
 
+int64_t la_chunked_forward_group(la_dtype in_dt, int64_t BH, int64_t L, int64_t d_in, int64_t d_v, int64_t C,
+                                 int causal, int normalize, la_fmap f, int64_t m, int64_t group) {
+    Plan P{};
+    char saved[sizeof(g_last_error)];
+    memcpy(saved, g_last_error, sizeof(saved));
+    const la_status s = make_plan(P, in_dt, BH, L, d_in, d_v, C, causal, normalize, f, m, 1.0f, group);
+    memcpy(g_last_error, saved, sizeof(saved));
+    return s == LA_OK ? P.G : 0;
+}
+
 la_status la_chunked_forward(const void* q, const void* k, const void* v, la_dtype in_dt, int64_t BH, int64_t L,
                              int64_t d_in, int64_t d_v, int64_t C, int causal, int normalize, la_fmap f,
                              const void* W, int64_t m, float in_scale, void* o, la_dtype out_dt, void* S_final,
@@ -399,60 +472,29 @@ la_status la_chunked_forward(const void* q, const void* k, const void* v, la_dty
     }
 
     // phase 3
-    const int64_t grid = BH * P.n_groups * P.n_dvt;
-    if (P.i8) {
-        la::FwdParamsI8 p{};
-        p.q = static_cast<const signed char*>(qm);
-        p.k = static_cast<const signed char*>(km);
-        p.v = static_cast<const signed char*>(v);
-        p.o = static_cast<int*>(o);
-        p.P0 = static_cast<const int*>(states);
-        p.S_final = static_cast<int*>(S_final);
-        p.L = L;
-        p.C = (int)P.C;
-        p.G = (int)P.G;
-        p.n_groups = (int)P.n_groups;
-        p.n_dvt = P.n_dvt;
-        p.dk_g = (int)P.dk;
-        p.dv = (int)d_v;
-        p.xcd_remap = xcd_ok(grid);
-        p.noncausal = !P.causal;
-        return hip_status(la::run_chunked_fwd_i8(p, P.DK, P.DVT, P.T, grid, s), "chunked forward launch");
-    }
-    la::FwdParams p{};
-    p.q = static_cast<const unsigned short*>(qm);
-    p.k = static_cast<const unsigned short*>(km);
-    p.v = static_cast<const unsigned short*>(v);
-    p.k_lo = static_cast<const unsigned short*>(klo);
-    p.o = o;
-    p.P0 = static_cast<const float*>(states);
-    p.z0 = static_cast<const float*>(zst);
-    p.S_final = static_cast<float*>(S_final);
-    p.z_final = static_cast<float*>(z_final);
-    p.L = L;
-    p.C = (int)P.C;
-    p.G = (int)P.G;
-    p.n_groups = (int)P.n_groups;
-    p.n_dvt = P.n_dvt;
-    p.dk_g = (int)P.dk;
-    p.dv = (int)d_v;
-    p.fmap = fmap_in_kernel;
-    p.in_scale = in_scale;
-    p.normalize = P.normalize;
-    p.out_f32 = out_dt == LA_F32;
-    p.xcd_remap = xcd_ok(grid);
-    p.noncausal = !P.causal;
-    const bool scaled_identity = f == LA_FMAP_IDENTITY && in_scale != 1.0f;
-    p.out_scale = (scaled_identity && !P.normalize) ? in_scale * in_scale : 1.0f;
-    p.state_scale = scaled_identity ? in_scale : 1.0f;
-    hipError_t e;
-    switch (P.DK) {
-        case 32: e = la::fwd_bf16_dk32(p, P.DVT, P.T, grid, s); break;
-        case 64: e = la::fwd_bf16_dk64(p, P.DVT, P.T, grid, s); break;
-        case 128: e = la::fwd_bf16_dk128(p, P.DVT, P.T, grid, s); break;
-        default: e = la::fwd_bf16_dk256(p, P.DVT, P.T, grid, s); break;
-    }
-    return hip_status(e, "chunked forward launch");
+    return launch_phase3(P, qm, km, klo, v, o, out_dt, states, zst, S_final, z_final, fmap_in_kernel, in_scale,
+                         f == LA_FMAP_IDENTITY && in_scale != 1.0f, s);
+}
+
+// ---------------------------------------------------------------------------
+la_status la_chunk_output(const void* q, const void* k, const void* v, la_dtype in_dt, int64_t BH, int64_t L,
+                          int64_t d_k, int64_t d_v, int64_t C, int64_t group, const void* P_prefix,
+                          const void* z_prefix, int normalize, void* o, la_dtype out_dt, void* S_final,
+                          void* z_final, la_stream_t stream) {
+    g_last_error[0] = 0;
+    if (q == nullptr || k == nullptr || v == nullptr || o == nullptr)
+        return fail(LA_ERR_INVALID_ARG, "q, k, v and o must not be NULL");
+    la_status st = check_dtypes_forward(in_dt, out_dt, normalize, LA_FMAP_IDENTITY, 1.0f);
+    if (st != LA_OK) return st;
+    if (z_final != nullptr && !normalize) return fail(LA_ERR_INVALID_ARG, "z_final needs normalize");
+    if (group < 1) return fail(LA_ERR_INVALID_ARG, "group must be at least 1");
+    Plan P{};
+    st = make_plan(P, in_dt, BH, L, d_k, d_v, C, 1, normalize, LA_FMAP_IDENTITY, 0, 1.0f, group);
+    if (st != LA_OK) return st;
+    if (P.n_groups > 1 && (P_prefix == nullptr || (normalize && z_prefix == nullptr)))
+        return fail(LA_ERR_INVALID_ARG, "more than one group needs the prefix states (and normalisers)");
+    return launch_phase3(P, q, k, nullptr, v, o, out_dt, P_prefix, z_prefix, S_final, z_final, la::FMAP_NONE,
+                         1.0f, false, (hipStream_t)stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -413,23 +413,28 @@ __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(SPLIT
                 vb[c][ks] = as_bf16x8(column_operand(Vs, G::VS, ks * 32, (wave + c * NW) * 16, lane));
     };
 
-    // inter + diagonal intra products and the state update, for the tile in LDS
-    auto diag_products = [&]() {
-#pragma unroll
-        for (int qb = 0; qb < NB; ++qb) den[qb] = 0.f;
-        load_vb();
+    // inter + diagonal intra products and the state update, for the tile in LDS.
+    // With one tile per chunk (fresh == true) the inter product reads P before
+    // this chunk's update, so it packs P on the fly instead of the snapshot.
+    auto diag_products = [&](bool fresh) {
 #pragma unroll
         for (int qb = 0; qb < NB; ++qb) {
-            const bool own_den = p.normalize && (qb % NW == wave);
+            den[qb] = 0.f;
 #pragma unroll
             for (int c = 0; c < CPW; ++c) O[c][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const u16* qrow = Qs + (qb * 16 + l16) * G::QS;
+        }
+        // inter: O = Q P  (k-steps over a outermost: one packed P operand per step)
 #pragma unroll
-            for (int ks = 0; ks < NKS_A; ++ks) {
-                const uint4 qa = row_operand_perm(qrow, ks * 32, g);
+        for (int ks = 0; ks < NKS_A; ++ks) {
+            bf16x8 pb[CPW];
 #pragma unroll
-                for (int c = 0; c < CPW; ++c) O[c][qb] = mfma_bf16(as_bf16x8(qa), Pb[c][ks], O[c][qb]);
-                if (own_den) {
+            for (int c = 0; c < CPW; ++c) pb[c] = fresh ? pack_acc_bf16(P[c][2 * ks], P[c][2 * ks + 1]) : Pb[c][ks];
+#pragma unroll
+            for (int qb = 0; qb < NB; ++qb) {
+                const uint4 qa = row_operand_perm(Qs + (qb * 16 + l16) * G::QS, ks * 32, g);
+#pragma unroll
+                for (int c = 0; c < CPW; ++c) O[c][qb] = mfma_bf16(as_bf16x8(qa), pb[c], O[c][qb]);
+                if (p.normalize && (qb % NW == wave)) {
                     // q . z over the eight a's this lane holds (a0 .. a0+3, a0+16 .. a0+19)
                     const int a0 = ks * 32 + g * 4;
                     const uint32_t qw[4] = {qa.x, qa.y, qa.z, qa.w};
@@ -442,7 +447,13 @@ __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(SPLIT
                     den[qb] += s;
                 }
             }
-            if (!p.noncausal) {
+        }
+        load_vb();
+        // intra: O += tril(S) V
+        if (!p.noncausal) {
+#pragma unroll
+            for (int qb = 0; qb < NB; ++qb) {
+                const bool own_den = p.normalize && (qb % NW == wave);
                 const u16* srow = Ss + (qb * 16 + l16) * G::KS;
 #pragma unroll
                 for (int ks = 0; ks < (qb + 2) / 2; ++ks) {
@@ -514,43 +525,59 @@ __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(SPLIT
             for (int qb = 0; qb < NB; ++qb)
                 if (qb % NW == wave) {
                     const float d = xor_sum_groups(den[qb]);
-                    if (g == 0) dens[qb * 16 + l16] = d;
+                    if (g == 0) dens[qb * 16 + l16] = 1.0f / d;
                 }
         }
         __syncthreads();  // dens visible; every wave is done with Qs
-        const bool stage = STAGE && !p.out_f32;
+        if (STAGE && !p.out_f32) {
 #pragma unroll
-        for (int c = 0; c < CPW; ++c) {
-            const int jl = (wave + c * NW) * 16 + l16;
-            const int j = col0 + jl;
+            for (int c = 0; c < CPW; ++c) {
+                const int jl = (wave + c * NW) * 16 + l16;
+                if (p.normalize) {
 #pragma unroll
-            for (int qb = 0; qb < NB; ++qb)
+                    for (int qb = 0; qb < NB; ++qb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = qb * 16 + g * 4 + i;
-                    float val = O[c][qb][i];
-                    if (p.normalize) val = val / dens[r];
-                    val *= p.out_scale;
-                    if (stage) {
-                        Qs[r * OS + jl] = f2bf(val);
-                    } else if (r < t.valid && j < p.dv) {
-                        const int64_t off = (bh * L + t.row0 + r) * p.dv + j;
-                        if (p.out_f32)
-                            reinterpret_cast<float*>(p.o)[off] = val;
-                        else
-                            reinterpret_cast<u16*>(p.o)[off] = f2bf(val);
-                    }
+                        for (int i = 0; i < 4; ++i) {
+                            const int r = qb * 16 + g * 4 + i;
+                            Qs[r * OS + jl] = f2bf(O[c][qb][i] * dens[r] * p.out_scale);
+                        }
+                } else {
+#pragma unroll
+                    for (int qb = 0; qb < NB; ++qb)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            Qs[(qb * 16 + g * 4 + i) * OS + jl] = f2bf(O[c][qb][i] * p.out_scale);
                 }
-        }
-        if (stage) {
+            }
             __syncthreads();
             constexpr int SEGS = T * DVT / 8;
-            for (int sg = tid; sg < SEGS; sg += NT) {
+            u16* ob = reinterpret_cast<u16*>(p.o) + (bh * L + t.row0) * p.dv + col0;
+#pragma unroll
+            for (int it = 0; it < (SEGS + NT - 1) / NT; ++it) {
+                const int sg = tid + it * NT;
                 const int r = sg / (DVT / 8), c8 = sg % (DVT / 8);
-                if (r < t.valid) {
-                    const uint4 val = *reinterpret_cast<const uint4*>(Qs + r * OS + c8 * 8);
-                    *reinterpret_cast<uint4*>(reinterpret_cast<u16*>(p.o) + (bh * L + t.row0 + r) * p.dv + col0 + c8 * 8) = val;
-                }
+                if ((SEGS % NT == 0 || sg < SEGS) && r < t.valid)
+                    *reinterpret_cast<uint4*>(ob + (r * p.dv + c8 * 8)) =
+                        *reinterpret_cast<const uint4*>(Qs + r * OS + c8 * 8);
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < CPW; ++c) {
+                const int j = col0 + (wave + c * NW) * 16 + l16;
+#pragma unroll
+                for (int qb = 0; qb < NB; ++qb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = qb * 16 + g * 4 + i;
+                        const float val = O[c][qb][i] * (p.normalize ? dens[r] : 1.0f) * p.out_scale;
+                        if (r < t.valid && j < p.dv) {
+                            const int64_t off = (bh * L + t.row0 + r) * p.dv + j;
+                            if (p.out_f32)
+                                reinterpret_cast<float*>(p.o)[off] = val;
+                            else
+                                reinterpret_cast<u16*>(p.o)[off] = f2bf(val);
+                        }
+                    }
             }
         }
     };
@@ -567,7 +594,6 @@ __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(SPLIT
         if (LA_PREFETCH && c_begin < c_end) load_qkv(tile_of(c_begin, 0));
         for (int64_t chunk = c_begin; chunk < c_end; ++chunk) {
             const Tile t = tile_of(chunk, 0);
-            snapshot();
             if (!LA_PREFETCH) load_qkv(t);
             __syncthreads();  // previous chunk's readers of the LDS tiles are done
             write_qkv(t);
@@ -575,7 +601,7 @@ __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(SPLIT
             __syncthreads();
             if (!p.noncausal) scores(true);
             __syncthreads();
-            diag_products();
+            diag_products(true);
             finish_tile(t);  // its first barrier also ends every read of zs
             if (p.normalize) publish_z();
         }
@@ -593,7 +619,7 @@ __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(SPLIT
                 __syncthreads();
                 scores(true);
                 __syncthreads();
-                diag_products();
+                diag_products(false);
                 for (int prev = 0; prev < sub; ++prev) prev_products(tile_of(chunk, prev));
                 finish_tile(t);
                 if (sub + 1 < nsub) __syncthreads();  // staging reads done before the next tile's writes

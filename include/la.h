@@ -130,6 +130,31 @@ la_status la_state_scan(void* S, void* z, la_dtype st_dt, int64_t BH, int64_t N,
                         int64_t d_v, void* S_final, void* z_final, la_stream_t stream);
 
 /*
+ * la_chunk_output - phase 3 alone: the causal output of every chunk from the
+ * prefix states of its group.  For each group of `group` consecutive chunks of
+ * C rows, starting from P = P_prefix of that group (zero for the first group)
+ * and, with normalize, z = z_prefix:
+ *   O_c = Q_c P + tril(Q_c K_c^T) V_c   [ / (Q_c z + row sums of tril(Q_c K_c^T)) ]
+ *   P  += K_c^T V_c ;  z += column sums of K_c        (then the next chunk)
+ * The carried state of the chunked algorithm on the chunking page, section ②
+ * (intra-chunk scores masked with the diagonal kept, inter-chunk read from the
+ * carried state), with the linear-attention page's normaliser.
+ *
+ *   q, k [BH, L, d_k] (already feature-mapped), v [BH, L, d_v]: LA_BF16, or
+ *        LA_I8 without normalize.
+ *   group   chunks per group (>= 1); n_groups = ceil(ceil(L / C) / group).
+ *   P_prefix [BH, n_groups, d_k, d_v] (LA_F32; LA_I32 for int8) and z_prefix
+ *        [BH, n_groups, d_k] (LA_F32): the exclusive prefix at group
+ *        granularity, i.e. la_chunk_states with chunk size C * group followed
+ *        by la_state_scan.  May be NULL when n_groups == 1 (zero start).
+ *   o, S_final, z_final: as for la_chunked_forward.
+ */
+la_status la_chunk_output(const void* q, const void* k, const void* v, la_dtype in_dt, int64_t BH,
+                          int64_t L, int64_t d_k, int64_t d_v, int64_t C, int64_t group,
+                          const void* P_prefix, const void* z_prefix, int normalize, void* o,
+                          la_dtype out_dt, void* S_final, void* z_final, la_stream_t stream);
+
+/*
  * la_chunked_forward - the whole forward: phi, then (causal) the chunked
  * computation with chunk size C, or (non-causal) phi(Q) (phi(K)^T V).
  * normalize != 0 divides each output row by phi(q_i)^T z_i (the numerator and
@@ -148,10 +173,11 @@ la_status la_state_scan(void* S, void* z, la_dtype st_dt, int64_t BH, int64_t N,
  *   S_final [BH, d_k, d_v] (LA_F32, or LA_I32 for int8) and z_final [BH, d_k]
  *        (LA_F32; only with normalize): optional final state.
  *   group  consecutive chunks one workgroup carries the state through (0 =
- *        chosen by the library).  Groups are joined through la_chunk_states +
- *        la_state_scan at group granularity; group = 1 is the literal
- *        three-phase form, group >= N the fully sequential form.  Every value
- *        gives the same result in exact arithmetic.
+ *        chosen by the library).  The call runs la_chunk_states at group
+ *        granularity, la_state_scan over the groups and la_chunk_output;
+ *        group = 1 is the literal three-phase form (one state per chunk),
+ *        group >= N a single sequential walk per head.  Every value gives the
+ *        same result in exact arithmetic.
  *   workspace / ws_bytes  device scratch of at least
  *        la_chunked_forward_workspace(...) bytes (may be NULL when that is 0).
  */
@@ -169,6 +195,13 @@ la_status la_chunked_forward(const void* q, const void* k, const void* v, la_dty
 size_t la_chunked_forward_workspace(la_dtype in_dt, int64_t BH, int64_t L, int64_t d_in,
                                     int64_t d_v, int64_t C, int causal, int normalize,
                                     la_fmap f, int64_t m, float in_scale, int64_t group);
+
+/* Chunks per group that la_chunked_forward uses for these arguments (its
+ * group argument when positive, else the library's choice, capped at the
+ * number of chunks); 0 on an invalid combination. */
+int64_t la_chunked_forward_group(la_dtype in_dt, int64_t BH, int64_t L, int64_t d_in, int64_t d_v,
+                                 int64_t C, int causal, int normalize, la_fmap f, int64_t m,
+                                 int64_t group);
 
 /*
  * la_recurrent_step - one decode step for n_states independent states:

@@ -122,6 +122,20 @@ def test_other_entry_point_errors():
                                  b.LA_F32, None) == b.LA_ERR_UNSUPPORTED
 
 
+def test_chunk_output_argument_errors():
+    lib = la.lib()
+    co = lambda **kw: lib.la_chunk_output(*dict(dict(q=FAKE, k=FAKE, v=FAKE, dt=b.LA_BF16, BH=2, L=256, dk=64, dv=64,
+                                                     C=64, group=1, P=None, z=None, norm=0, o=FAKE,
+                                                     odt=b.LA_BF16, Sf=None, zf=None, s=None), **kw).values())  # noqa: E731
+    assert co(q=None) == b.LA_ERR_INVALID_ARG
+    assert co(group=0) == b.LA_ERR_INVALID_ARG
+    assert co(group=2, P=None) == b.LA_ERR_INVALID_ARG  # two groups need the prefixes
+    assert co(group=2, P=FAKE, norm=1, z=None) == b.LA_ERR_INVALID_ARG
+    assert co(dk=96) == b.LA_ERR_UNSUPPORTED
+    assert co(dt=b.LA_I8, norm=1, odt=b.LA_I32) == b.LA_ERR_UNSUPPORTED
+    assert co(zf=FAKE) == b.LA_ERR_INVALID_ARG
+
+
 def test_last_error_is_thread_local():
     import threading
     lib = la.lib()

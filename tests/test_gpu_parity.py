@@ -278,3 +278,44 @@ def test_decode_matches_oracle_step():
         assert_close(host(o)[i], ro, tol=1e-4, what="o")
         assert_close(host(S)[i], rS, tol=1e-5, what="S")
         assert_close(host(z)[i], rz, tol=1e-5, what="z")
+
+
+@pytest.mark.parametrize("dtype,C,group", [("bf16", 64, 1), ("bf16", 64, 3), ("bf16", 50, 2), ("i8", 64, 2),
+                                           ("i8", 16, 1)])
+def test_three_phase_composition(dtype, C, group):
+    """la_chunk_states at group granularity, la_state_scan, then la_chunk_output
+    reproduce la_chunked_forward bit for bit, and the oracle."""
+    torch = torch_cuda()
+    q, k, v = _case(40, 3, 290, 64, 64, dtype)
+    log(f"three phases {dtype} C={C} group={group}")
+    qd, kd, vd = dev_input(q), dev_input(k), dev_input(v)
+    S, _ = la.chunk_states(kd, vd, C * group)
+    la.state_scan(S, None, want_final=False)
+    o3, Sf3, _ = la.chunk_output(qd, kd, vd, C, group, P_prefix=S, return_state=True)
+    o, Sf, _ = la.chunked_forward(qd, kd, vd, C, return_state=True, group=group)
+    torch.cuda.synchronize()
+    assert torch.equal(o3, o) and torch.equal(Sf3, Sf)
+    ref, refS, _ = _oracle_forward(q.exact, k.exact, v.exact, C)
+    if dtype == "i8":
+        assert_exact(host(o3), ref, "o")
+        assert_exact(host(Sf3), refS, "S")
+    else:
+        assert_close(host(o3), ref, what="o")
+        assert_close(host(Sf3), refS, what="S")
+
+
+def test_three_phase_normalized():
+    torch = torch_cuda()
+    q, k, v = _case(41, 2, 333, 64, 32, "bf16")
+    log("three phases, elu+1 mapped first, normalised")
+    qm = la.feature_map(dev_input(q), "elu1")
+    km = la.feature_map(dev_input(k), "elu1")
+    S, z = la.chunk_states(km, dev_input(v), 64 * 2, want_z=True)
+    la.state_scan(S, z, want_final=False)
+    o, Sf, zf = la.chunk_output(qm, km, dev_input(v), 64, 2, P_prefix=S, z_prefix=z, normalize=True,
+                                return_state=True)
+    ref, refS, refz = _oracle_forward(q.exact, k.exact, v.exact, 64, True, True, "elu1")
+    assert_close(host(o), ref, what="o")
+    assert_close(host(zf), refz, what="z")
+    # phi(k) was rounded to bf16 before the state sums: a 2e-2 band for S here
+    assert_close(host(Sf), refS, tol=2e-2, what="S")
