@@ -31,7 +31,7 @@ METRIC = "chunked causal linear-attn forward tokens/sec and % MFMA peak, L=8192 
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_I8_TOPS = 5000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_chunked_fwd_bf16_identity-L8192-d128.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_chunked_fwd_bf16_identity-L8192-d128.txt")
 
 
 def log(msg):
@@ -47,6 +47,33 @@ def lib_hash() -> str:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """The `key: value` lines of the committed counter summary (or {})."""
+    out = {}
+    if not os.path.exists(TRAFFIC_FILE):
+        return out
+    with open(TRAFFIC_FILE) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                out[key.strip()] = val.strip()
+    return out
+
+
+def copy_calibration():
+    """A plain device copy of 512 MiB, twice: under rocprofv3 --pmc its
+    FETCH_SIZE / WRITE_SIZE readings calibrate those counters."""
+    import torch
+    a = torch.empty(256 * 1024 * 1024, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+    torch.cuda.empty_cache()
 
 
 def dev_bf16(bits):
@@ -152,10 +179,9 @@ def run_headline(args):
     sec = ms * 1e-3
     achieved_gbs = alg_bytes3 / (k3 * 1e-3) / 1e9
     traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        tr = json.load(open(TRAFFIC_FILE))
-        if tr.get("lib_hash") == lib_hash() and tr.get("chunk") == C and tr.get("group") == G:
-            traffic = tr.get("bytes_per_launch")
+    tr = read_traffic()
+    if tr.get("lib_hash") == lib_hash() and tr.get("chunk") == str(C) and tr.get("group") == str(G):
+        traffic = float(tr["bytes_per_launch"])
     res = {
         "metric": METRIC,
         "value": tokens / sec,
@@ -270,6 +296,8 @@ def main():
     ap.add_argument("--extra", action="store_true", help="also time the other workloads and chunk sizes")
     ap.add_argument("--decode-steps", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="end with a plain 512 MiB device copy (counter calibration under rocprofv3)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); this build has no multi-GPU path",
@@ -284,6 +312,8 @@ def main():
     torch.cuda.empty_cache()
     if args.extra:
         run_extras(args, res)
+    if args.copy_calibration:
+        copy_calibration()
     if not args.no_cpu_baseline:
         import workloads as wl
         log("timing the CPU oracle on a bounded sample")
