@@ -31,6 +31,12 @@ CFLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-I" + INCLUDE
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
+# Per-file flags.  The streaming kernel keeps its matrix-core accumulators in
+# ordinary VGPRs (it runs one wave per SIMD, so all 512 registers are there),
+# which saves the copies out of accumulation registers before every pack.
+FILE_FLAGS = {"la_pipe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _sources():
     return sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
 
@@ -43,7 +49,7 @@ def _headers_mtime() -> float:
 
 def _compile(src: str) -> tuple:
     obj = os.path.join(BUILD, src[:-4] + ".o")
-    cmd = [HIPCC] + CFLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + CFLAGS + FILE_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     t0 = time.time()
     r = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass does not know the packed-fp32 feature; that warning is harmless

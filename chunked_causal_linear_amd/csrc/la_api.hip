@@ -9,6 +9,17 @@
 #include "la_chunked_bf16.hpp"
 #include "la_kernels.hpp"
 
+#ifndef LA_PIPE_DVT
+#define LA_PIPE_DVT 64
+#endif
+#ifndef LA_PIPE_TARGET
+#define LA_PIPE_TARGET 256
+#endif
+
+namespace la {
+hipError_t fwd_pipe_bf16(const FwdParams& p, int DK, int DVT, int64_t grid, hipStream_t s);
+}
+
 namespace {
 
 thread_local char g_last_error[512] = "";
@@ -70,6 +81,7 @@ struct Plan {
     int64_t n_chunks, G, n_groups;
     int DK, DVT, T, n_dvt;
     bool premap;  // phi computed by a separate pass into the workspace
+    bool pipe;    // streaming phase-3 kernel (chunks of 64 rows, identity map, no normaliser)
     bool causal, normalize;
     size_t ws_phi;     // bytes of one mapped q or k copy
     size_t ws_states;  // bytes of the group states
@@ -129,6 +141,17 @@ la_status make_plan(Plan& P, la_dtype in_dt, int64_t BH, int64_t L, int64_t d_in
         P.DK = kernel_dk_bf16(P.dk);
     }
 
+    // The streaming kernel covers chunks of exactly 64 rows with the identity
+    // map, no normaliser and feature widths of 64 or 128; it holds three LDS
+    // stages and runs one workgroup per CU.
+    P.pipe = !P.i8 && P.causal && Ce == 64 && !P.normalize && f == LA_FMAP_IDENTITY &&
+             (P.dk == 64 || P.dk == 128) && d_v % 64 == 0;
+    if (P.pipe) {
+        P.DK = (int)P.dk;
+        P.DVT = (P.dk == 128 && d_v % LA_PIPE_DVT == 0) ? LA_PIPE_DVT : 64;
+        P.n_dvt = (int)(d_v / P.DVT);
+    }
+
     if (!P.causal) {
         // total state from one chunk of L rows, then every tile reads it
         P.T = 64;
@@ -149,7 +172,7 @@ la_status make_plan(Plan& P, la_dtype in_dt, int64_t BH, int64_t L, int64_t d_in
             // run two per CU), one per CU otherwise; fewer groups mean less
             // phase-1 traffic, more mean more loads in flight per CU.
             const bool split = f == LA_FMAP_ELU1 || f == LA_FMAP_FAVOR;
-            const int64_t target = (P.i8 || split) ? 256 : 1024;
+            const int64_t target = P.pipe ? LA_PIPE_TARGET : ((P.i8 || split) ? 256 : 1024);
             const int64_t base = BH * P.n_dvt;
             int64_t want = base >= target ? 1 : cdiv(target, base);
             if (want > P.n_chunks) want = P.n_chunks;
@@ -229,11 +252,23 @@ static la_status launch_phase3(const Plan& P, const void* qm, const void* km, co
     p.out_scale = (scaled_identity && !P.normalize) ? in_scale * in_scale : 1.0f;
     p.state_scale = scaled_identity ? in_scale : 1.0f;
     hipError_t e;
+    if (P.pipe && out_dt == LA_BF16)
+        return hip_status(la::fwd_pipe_bf16(p, P.DK, P.DVT, grid, s), "chunked forward launch");
+    int DVT = P.DVT, T = P.T;
+    int64_t grid_g = grid;
+    if (P.pipe) {
+        // fp32 outputs: the general kernel on the same groups
+        DVT = kernel_dvt(d_v);
+        T = tile_bf16(P.C, P.DK, DVT, false);
+        p.n_dvt = (int)(d_v / DVT);
+        grid_g = BH * P.n_groups * p.n_dvt;
+        p.xcd_remap = xcd_ok(grid_g);
+    }
     switch (P.DK) {
-        case 32: e = la::fwd_bf16_dk32(p, P.DVT, P.T, grid, s); break;
-        case 64: e = la::fwd_bf16_dk64(p, P.DVT, P.T, grid, s); break;
-        case 128: e = la::fwd_bf16_dk128(p, P.DVT, P.T, grid, s); break;
-        default: e = la::fwd_bf16_dk256(p, P.DVT, P.T, grid, s); break;
+        case 32: e = la::fwd_bf16_dk32(p, DVT, T, grid_g, s); break;
+        case 64: e = la::fwd_bf16_dk64(p, DVT, T, grid_g, s); break;
+        case 128: e = la::fwd_bf16_dk128(p, DVT, T, grid_g, s); break;
+        default: e = la::fwd_bf16_dk256(p, DVT, T, grid_g, s); break;
     }
     return hip_status(e, "chunked forward launch");
 }

@@ -106,6 +106,24 @@ def test_bf16_identity_chunks(C):
     assert_close(host(S), refS, what=f"S C={C}")
 
 
+@pytest.mark.parametrize("dk,dv,L,group,out", [(128, 128, 700, 0, "bf16"), (128, 128, 1024, 3, "f32"),
+                                               (64, 64, 700, 4, "bf16"), (128, 256, 193, 0, "bf16"),
+                                               (64, 128, 64, 0, "f32"), (128, 128, 2000, 1, "bf16"),
+                                               (128, 128, 130, 2, "bf16")])
+def test_bf16_chunk64_streaming(dk, dv, L, group, out):
+    """Chunks of 64 with the identity map (the streaming kernel's cases): runs of
+    many chunks per group, ragged tails, prefix states, both output types."""
+    torch = torch_cuda()
+    q, k, v = _case(15, 2, L, dk, dv, "bf16")
+    log(f"bf16 chunk64 dk={dk} dv={dv} L={L} group={group} out={out}")
+    od = torch.bfloat16 if out == "bf16" else torch.float32
+    o, S, _ = la.chunked_forward(dev_input(q), dev_input(k), dev_input(v), 64, return_state=True, group=group,
+                                 out_dtype=od)
+    ref, refS, _ = _oracle_forward(q.exact, k.exact, v.exact, 64)
+    assert_close(host(o), ref, what="o")
+    assert_close(host(S), refS, what="S")
+
+
 @pytest.mark.parametrize("group", [1, 2, 3, 5, 100])
 def test_bf16_groups(group):
     q, k, v = _case(11, 2, 640, 64, 64, "bf16")
