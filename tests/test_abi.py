@@ -80,8 +80,12 @@ def test_workspace_sizes_and_errors():
     # one group (group >= N), identity map: no scratch
     assert ws(b.LA_BF16, 128, 8192, 128, 128, 64, 1, 0, 0, 0, 1.0, 1 << 30) == 0
     assert ws(b.LA_BF16, 128, 8192, 128, 128, 64, 1, 0, 0, 0, 0.5, 1 << 30) == 0  # scale folded into the results
-    # automatic plan at the headline size: four groups per (head, column tile)
-    assert ws(b.LA_BF16, 128, 8192, 128, 128, 64, 1, 0, 0, 0, 1.0, 0) == 128 * 4 * 128 * 128 * 4
+    # automatic plan at the headline size, chunks of 64: the streaming kernel's
+    # 128 heads x 2 column tiles already fill the GPU, one group per head
+    assert ws(b.LA_BF16, 128, 8192, 128, 128, 64, 1, 0, 0, 0, 1.0, 0) == 0
+    assert lib.la_chunked_forward_group(b.LA_BF16, 128, 8192, 128, 128, 64, 1, 0, 0, 0, 0) == 8192 // 64
+    # chunks of 32 (general kernel): four groups per (head, column tile)
+    assert ws(b.LA_BF16, 128, 8192, 128, 128, 32, 1, 0, 0, 0, 1.0, 0) == 128 * 4 * 128 * 128 * 4
     # groups: BH * n_groups * (dk*dv + dk) floats (normalised), 256-byte aligned pieces
     n = ws(b.LA_BF16, 2, 1024, 64, 64, 64, 1, 1, 1, 0, 1.0, 4)
     groups = 1024 // 64 // 4
