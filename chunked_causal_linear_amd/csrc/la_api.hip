@@ -9,9 +9,6 @@
 #include "la_chunked_bf16.hpp"
 #include "la_kernels.hpp"
 
-#ifndef LA_PIPE_DVT
-#define LA_PIPE_DVT 64
-#endif
 #ifndef LA_PIPE_TARGET
 #define LA_PIPE_TARGET 256
 #endif
@@ -148,7 +145,7 @@ la_status make_plan(Plan& P, la_dtype in_dt, int64_t BH, int64_t L, int64_t d_in
              (P.dk == 64 || P.dk == 128) && d_v % 64 == 0;
     if (P.pipe) {
         P.DK = (int)P.dk;
-        P.DVT = (P.dk == 128 && d_v % LA_PIPE_DVT == 0) ? LA_PIPE_DVT : 64;
+        P.DVT = 64;
         P.n_dvt = (int)(d_v / P.DVT);
     }
 

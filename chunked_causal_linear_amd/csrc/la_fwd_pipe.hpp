@@ -43,7 +43,11 @@ namespace la {
 namespace pipe {
 
 constexpr int T = 64;   // rows per chunk (this kernel is for C == 64)
-constexpr int NW = 4;   // waves per workgroup
+#ifndef LA_PIPE_NW
+#define LA_PIPE_NW 2
+#endif
+constexpr int NW = LA_PIPE_NW;  // compute waves per workgroup
+constexpr int NCP = 2;          // copy waves per workgroup
 
 // Byte offset of element e of row r in a tile with NSEG 16-byte segments per
 // row: segment index XOR (row mod NSEG).  Row reads of 16 bytes over 16
@@ -129,23 +133,26 @@ __device__ __forceinline__ int work_index(int remap) {
 
 }  // namespace pipe
 
-// One workgroup: (head, group of chunks, tile of DVT value columns); four
-// compute waves and one copy wave.  Compute wave w owns value columns
-// [w*DVT/4, (w+1)*DVT/4) of O and of the state; it touches only LDS and the
-// matrix cores.  The copy wave issues every global access of the chunk loop:
-// the direct-to-LDS copies of Q, K, V and the output stores.  A wave that
-// issues global accesses stalls whenever the memory queue is full; keeping
-// those stalls on their own wave lets the copies stream continuously while the
-// compute waves work.
+// One workgroup: (head, group of chunks, tile of DVT value columns); NW
+// compute waves (two by default: each then owns 32 value columns, which halves
+// the LDS reads of Q and K per output column against four waves of 16) and
+// two copy waves.  Compute wave w owns value columns [w*DVT/NW, (w+1)*DVT/NW)
+// of O and of the state; it touches only LDS and the
+// matrix cores.  The copy waves issue every global access of the chunk loop,
+// half each: the direct-to-LDS copies of Q, K, V and the output stores.  A
+// wave stalls when it has 63 memory instructions in flight (the counter's
+// limit) or the memory queue is full; keeping those stalls on waves of their
+// own lets the copies stream continuously while the compute waves work, and
+// two copy waves keep two chunks of copies in flight under that limit.
 //
 // Per chunk j, after the barrier B(j) that makes chunk j's tiles visible:
 //   compute waves: products of chunk j from stage j % NSTAGE; the output rows
 //     go back into that stage's V tile, into the columns the same wave read V
 //     from (no other wave reads them);
-//   copy wave: reads the output of chunk j - 1 from stage (j - 1) % NSTAGE,
-//     refills that stage with chunk j + NSTAGE - 1, stores the output rows
-//     (full 16-byte segments of a row), then waits until chunk j + 1 has
-//     landed and meets the compute waves at B(j + 1).
+//   copy waves: read the output of chunk j - 1 from stage (j - 1) % NSTAGE,
+//     refill that stage with chunk j + NSTAGE - 1, stores the output rows
+//     (full 16-byte segments of a row), then wait until chunk j + 1 has
+//     landed and meet the compute waves at B(j + 1).
 //
 // Index orders inside 32-wide k-steps.  Keys: permuted (lane group g holds keys
 // 4g..4g+3 and 16+4g..16+4g+3), the order in which the score accumulators
@@ -156,8 +163,9 @@ __device__ __forceinline__ int work_index(int remap) {
 // at column 8c (+4 for the second half), so the update's accumulator rows come
 // out as a = 32ks + 8g + 4h + i (h = half) and a packed pair (h = 0, 1) is the
 // inter product's operand in natural order, again without leaving registers.
-template <int DK, int DVT, int NSTAGE>
-__global__ __launch_bounds__((pipe::NW + 1) * WAVE) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int DK, int DVT, int NSTAGE, bool SCALED>
+__global__ __launch_bounds__((pipe::NW + pipe::NCP) * WAVE)
+__attribute__((amdgpu_waves_per_eu((pipe::NW + pipe::NCP + 3) / 4, (pipe::NW + pipe::NCP + 3) / 4)))
 void chunked_fwd_pipe(FwdParams p) {
     using namespace pipe;
     constexpr int CPW = DVT / 16 / NW;     // 16-column blocks per compute wave
@@ -165,20 +173,22 @@ void chunked_fwd_pipe(FwdParams p) {
     constexpr int NKA = DK / 32;           // k-steps over the feature index
     constexpr int NKK = T / 32;            // k-steps over keys
     constexpr int QSEG = DK / 8, VSEG = DVT / 8;
-    constexpr int NCQ = T * QSEG / WAVE;   // copy instructions per chunk, Q (and K)
-    constexpr int NCV = T * VSEG / WAVE;   // copy instructions per chunk, V (and O stores)
+    constexpr int NCQ = T * QSEG / WAVE / NCP;  // copy instructions per chunk and copy wave, Q (and K)
+    constexpr int NCV = T * VSEG / WAVE / NCP;  // the same for V (and for the output stores)
     constexpr int NL = 2 * NCQ + NCV;
     constexpr int NTRI = NQB * (NQB + 1) / 2;
     constexpr int RPV = WAVE / VSEG;       // output rows per store instruction
     static_assert(CPW >= 1 && CPW * 16 * NW == DVT, "DVT must be 64 or 128");
     static_assert(NSTAGE == 3, "three LDS stages");
     static_assert(NL < 64, "vmcnt range");
+    static_assert(NCV >= 1, "tile too small for the copy split");
 
     __shared__ Stage<DK, DVT> st[NSTAGE];
 
     const int tid = threadIdx.x;
     const int wave = tid / WAVE, lane = tid % WAVE, l16 = lane % 16, g = lane / 16;
-    const bool copier = wave == NW;  // wave-uniform
+    const bool copier = wave >= NW;  // wave-uniform
+    const int cw = __builtin_amdgcn_readfirstlane(wave - NW);  // copy wave index (wave-uniform)
 
     const int w = work_index(p.xcd_remap);
     const int jt = w % p.n_dvt;
@@ -200,7 +210,7 @@ void chunked_fwd_pipe(FwdParams p) {
     auto zero_tail = [&](Stage<DK, DVT>& s, int valid) __attribute__((always_inline)) {
         const int n = (T - valid) * QSEG;
         uint4* kk = reinterpret_cast<uint4*>(s.k + valid * DK);
-        for (int i = tid; i < n; i += (NW + 1) * WAVE) kk[i] = make_uint4(0, 0, 0, 0);
+        for (int i = tid; i < n; i += (NW + NCP) * WAVE) kk[i] = make_uint4(0, 0, 0, 0);
     };
 
     if (copier) {
@@ -220,17 +230,19 @@ void chunked_fwd_pipe(FwdParams p) {
             const uint32_t lq = lds_addr(s.q), lk = lds_addr(s.k), lv = lds_addr(s.v);
 #pragma unroll
             for (int i = 0; i < NCQ; ++i) {
-                const int slot = i * WAVE + lane;
+                const int b = cw * NCQ + i;  // copy instruction within the tile
+                const int slot = b * WAVE + lane;
                 const int r = slot / QSEG, seg = (slot % QSEG) ^ (r & (QSEG - 1));
                 const uint32_t off = (uint32_t)(((r < last ? r : last) * DK + seg * 8) * 2);
-                dma16(qb_, off, lq + i * WAVE * 16);
-                dma16(kb_, off, lk + i * WAVE * 16);
+                dma16(qb_, off, lq + b * WAVE * 16);
+                dma16(kb_, off, lk + b * WAVE * 16);
             }
 #pragma unroll
             for (int i = 0; i < NCV; ++i) {
-                const int slot = i * WAVE + lane;
+                const int b = cw * NCV + i;
+                const int slot = b * WAVE + lane;
                 const int r = slot / VSEG, seg = (slot % VSEG) ^ (r & (VSEG - 1));
-                dma16(vb_, (uint32_t)(((r < last ? r : last) * dv + seg * 8) * 2), lv + i * WAVE * 16);
+                dma16(vb_, (uint32_t)(((r < last ? r : last) * dv + seg * 8) * 2), lv + b * WAVE * 16);
             }
         };
         // Output rows of chunk c sit in the V tile of stage `from`: instruction
@@ -242,7 +254,7 @@ void chunked_fwd_pipe(FwdParams p) {
             u32x4 ob[NCV];
 #pragma unroll
             for (int i = 0; i < NCV; ++i) {
-                const int r = i * RPV + lane / VSEG, seg = lane % VSEG;
+                const int r = (cw * NCV + i) * RPV + lane / VSEG, seg = lane % VSEG;
                 ob[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(from.v) +
                                                         tile_off<VSEG>(r, seg * 8));
             }
@@ -252,7 +264,7 @@ void chunked_fwd_pipe(FwdParams p) {
             u16* o = reinterpret_cast<u16*>(p.o) + (bh * L + c * T) * dv + col0;
 #pragma unroll
             for (int i = 0; i < NCV; ++i) {
-                const int r = i * RPV + lane / VSEG, seg = lane % VSEG;
+                const int r = (cw * NCV + i) * RPV + lane / VSEG, seg = lane % VSEG;
                 if (r < valid) *reinterpret_cast<u32x4*>(o + (int64_t)r * dv + seg * 8) = ob[i];
             }
         };
@@ -323,7 +335,6 @@ void chunked_fwd_pipe(FwdParams p) {
                         P[c][ks][h][i] = P0[(int64_t)(32 * ks + 8 * g + 4 * h + i) * dv + c * 16];
     }
     const float osc = p.out_scale;
-    const bool scaled = osc != 1.0f;
 
     // Operands of one 32-wide feature step: Q rows (B of the scores and of the
     // inter product) and K rows (A of the scores).
@@ -336,10 +347,31 @@ void chunked_fwd_pipe(FwdParams p) {
         }
     };
 
-    // The chunk's products; the output goes back into this wave's V columns.
+    // K column operands of one feature step for the state update: columns
+    // 32ks + 8c + 4h (lane c of each row quad), keys in the permuted order.
+    const int c4 = 4 * (lane & 3), c8 = 8 * (lane & 3);
+    auto load_kc = [&](const Stage<DK, DVT>& s, int ks, bf16x8 (&kc)[2][NKK]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) kc[h][kk] = col_op<QSEG>(s.k, kk * 32, ks * 32 + c8 + 4 * h, lane);
+    };
+
+    // The chunk's products, one 32-wide feature step at a time: scores, the
+    // inter product (which reads the state as it was before this chunk) and
+    // that step's rows of the state update, with the next step's operands
+    // loaded ahead.  Then the mask, the intra product and the output, which
+    // goes back into this wave's V columns.
     auto compute = [&](Stage<DK, DVT>& s) __attribute__((always_inline)) {
         bf16x8 qa0[NQB], ka0[NQB], qa1[NQB], ka1[NQB];
+        bf16x8 kc0[2][NKK], kc1[2][NKK];
+        bf16x8 vb[CPW][NKK];
         load_qk(s, 0, qa0, ka0);
+#pragma unroll
+        for (int c = 0; c < CPW; ++c)
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) vb[c][kk] = col_op<VSEG>(s.v, kk * 32, colw + c * 16 + c4, lane);
+        load_kc(s, 0, kc0);
         f32x4 S[NTRI];  // S^T blocks (kb <= qb), index qb(qb+1)/2 + kb
         f32x4 O[CPW][NQB];  // O^T blocks: lane holds O[q = 16qb + l16][j = colw + 16c + 4g + i]
 #pragma unroll
@@ -348,13 +380,15 @@ void chunked_fwd_pipe(FwdParams p) {
         for (int c = 0; c < CPW; ++c)
 #pragma unroll
             for (int qb = 0; qb < NQB; ++qb) O[c][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        // scores and inter, one 32-wide step of the feature index at a time,
-        // the next step's operands loaded ahead
 #pragma unroll
         for (int ks = 0; ks < NKA; ++ks) {
             bf16x8 (&qa)[NQB] = (ks & 1) ? qa1 : qa0;
             bf16x8 (&ka)[NQB] = (ks & 1) ? ka1 : ka0;
-            if (ks + 1 < NKA) load_qk(s, ks + 1, (ks & 1) ? qa0 : qa1, (ks & 1) ? ka0 : ka1);
+            bf16x8 (&kc)[2][NKK] = (ks & 1) ? kc1 : kc0;
+            if (ks + 1 < NKA) {
+                load_qk(s, ks + 1, (ks & 1) ? qa0 : qa1, (ks & 1) ? ka0 : ka1);
+                load_kc(s, ks + 1, (ks & 1) ? kc0 : kc1);
+            }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int qb = 0; qb < NQB; ++qb)
@@ -366,18 +400,12 @@ void chunked_fwd_pipe(FwdParams p) {
                 const bf16x8 pb = pack_acc_bf16(P[c][ks][0], P[c][ks][1]);
 #pragma unroll
                 for (int qb = 0; qb < NQB; ++qb) O[c][qb] = mfma_bf16(pb, qa[qb], O[c][qb]);
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int kk = 0; kk < NKK; ++kk) P[c][ks][h] = mfma_bf16(kc[h][kk], vb[c][kk], P[c][ks][h]);
             }
         }
-        // V columns of this wave (permuted key order) and the first K column operands
-        const int c4 = 4 * (lane & 3), c8 = 8 * (lane & 3);
-        bf16x8 vb[CPW][NKK], kc[2][NKK];
-#pragma unroll
-        for (int c = 0; c < CPW; ++c)
-#pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) vb[c][kk] = col_op<VSEG>(s.v, kk * 32, colw + c * 16 + c4, lane);
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) kc[0][kk] = col_op<QSEG>(s.k, kk * 32, c8, lane);
-        __builtin_amdgcn_sched_barrier(0);
         // causal mask on the diagonal blocks: keep key 16qb + 4g + i <= q = 16qb + l16
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb)
@@ -398,30 +426,13 @@ void chunked_fwd_pipe(FwdParams p) {
                 for (int c = 0; c < CPW; ++c) O[c][qb] = mfma_bf16(vb[c][kk], sb, O[c][qb]);
             }
         }
-        // state update: K columns 32ks + 8c + 4h (lane c of each row quad), one
-        // (ks, h) step ahead
-#pragma unroll
-        for (int t = 0; t < 2 * NKA; ++t) {
-            const int ks = t >> 1, h = t & 1;
-            if (t + 1 < 2 * NKA) {
-                const int ks1 = (t + 1) >> 1, h1 = (t + 1) & 1;
-#pragma unroll
-                for (int kk = 0; kk < NKK; ++kk)
-                    kc[(t + 1) & 1][kk] = col_op<QSEG>(s.k, kk * 32, ks1 * 32 + c8 + 4 * h1, lane);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int kk = 0; kk < NKK; ++kk)
-#pragma unroll
-                for (int c = 0; c < CPW; ++c) P[c][ks][h] = mfma_bf16(kc[t & 1][kk], vb[c][kk], P[c][ks][h]);
-        }
         // output rows into this wave's V columns (after its last V read, in order)
 #pragma unroll
         for (int c = 0; c < CPW; ++c)
 #pragma unroll
             for (int qb = 0; qb < NQB; ++qb) {
                 f32x4 o = O[c][qb];
-                if (scaled) o *= osc;
+                if (SCALED) o *= osc;
                 *reinterpret_cast<uint2*>(reinterpret_cast<char*>(s.v) +
                                           tile_off<VSEG>(qb * 16 + l16, colw + c * 16 + 4 * g)) =
                     make_uint2(pack2_bf16(o[0], o[1]), pack2_bf16(o[2], o[3]));
@@ -461,7 +472,11 @@ void chunked_fwd_pipe(FwdParams p) {
 
 template <int DK, int DVT>
 hipError_t launch_fwd_pipe(const FwdParams& p, int64_t grid, hipStream_t s) {
-    hipLaunchKernelGGL((chunked_fwd_pipe<DK, DVT, 3>), dim3((unsigned)grid), dim3((pipe::NW + 1) * WAVE), 0, s, p);
+    const dim3 block((pipe::NW + pipe::NCP) * WAVE);
+    if (p.out_scale != 1.0f)
+        hipLaunchKernelGGL((chunked_fwd_pipe<DK, DVT, 3, true>), dim3((unsigned)grid), block, 0, s, p);
+    else
+        hipLaunchKernelGGL((chunked_fwd_pipe<DK, DVT, 3, false>), dim3((unsigned)grid), block, 0, s, p);
     return hipGetLastError();
 }
 

@@ -5,7 +5,6 @@ namespace la {
 
 hipError_t fwd_pipe_bf16(const FwdParams& p, int DK, int DVT, int64_t grid, hipStream_t s) {
     switch (DK * 1000 + DVT) {
-        case 128128: return launch_fwd_pipe<128, 128>(p, grid, s);
         case 128064: return launch_fwd_pipe<128, 64>(p, grid, s);
         case 64064: return launch_fwd_pipe<64, 64>(p, grid, s);
     }
