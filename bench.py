@@ -175,6 +175,15 @@ def run_headline(args):
     k1 = float(np.mean(per_launch_ms(ph1, 10))) if n_groups > 1 else 0.0
     k2 = float(np.mean(per_launch_ms(ph2, 10))) if n_groups > 1 else 0.0
     assert torch.equal(o3, fwd.o), "phase 3 alone differs from the forward"
+    # a plain streaming kernel with the same traffic (three reads and one write
+    # of B*H*L*d bf16 each): the bandwidth this memory system gives that mix
+    scratch = torch.empty_like(qd)
+    ref = lambda: torch.addcmul(qd, kd, vd, out=scratch)  # noqa: E731
+    ref()
+    torch.cuda.synchronize()
+    ref_ms = float(np.median(per_launch_ms(ref, 20)))
+    ref_gbs = 4 * qd.numel() * 2 / (ref_ms * 1e-3) / 1e9
+    del scratch
 
     work = Work(w.BH, w.L, w.d_in, w.d_k, w.d_v, C)
     tokens = w.B * w.L
@@ -215,82 +224,167 @@ def run_headline(args):
                      "kernel": "chunked_fwd_pipe (la_chunk_output)" if C == 64 else "chunked_fwd_bf16 (la_chunk_output)",
                      "alg_bytes_per_launch": alg_bytes3,
                      "avg_launch_ms": k3,
-                     "mfma_frac_of_kernel": flops / (k3 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
+                     "mfma_frac_of_kernel": flops / (k3 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                     "stream_reference": {"kernel": "torch.addcmul over q, k, v into a scratch tensor "
+                                                    "(three reads and one write of the same sizes)",
+                                          "ms": ref_ms, "GB/s": ref_gbs, "frac": ref_gbs / PEAK_HBM_GBS}},
     }
     return res, fwd
 
 
+def _oracle_time(fn, budget_s: float = 3.0):
+    """Seconds per call of an oracle function, repeated until about budget_s."""
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        fn()
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= 50:
+            return el / n
+
+
 def run_extras(args, out):
-    """Other workloads and chunk sizes, each timed separately (not the headline)."""
+    """Every hot-path row measured on its own against its roofline, with the
+    CPU oracle timed beside it on a bounded sample (not the headline line)."""
+    import numpy as np
     import torch
 
     import chunked_causal_linear_amd as la
+    import oracle
     import workloads as wl
-    from chunked_causal_linear_amd.accounting import Work, decode_bytes
+    from chunked_causal_linear_amd.accounting import Work, decode_bytes, phase1_bytes, scan_bytes
 
-    extras = {}
+    rows = {}
+    hbm = lambda b, ms: {"GB/s": b / (ms * 1e-3) / 1e9, "frac_of_8TBs": b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}  # noqa
+
+    def med_ms(fn, n=10):
+        fn()
+        torch.cuda.synchronize()
+        return float(np.median(per_launch_ms(fn, n)))
+
+    # ---- a1: feature maps
+    w4, w5 = wl.WORKLOADS[4], wl.WORKLOADS[5]
+    x, _, _, _ = wl.workload_inputs(w4, want_exact=False)
+    xd = dev_bf16(x.bits)
+    x_sample = wl.bf16_bits_to_f64(x.bits[0, :4096])
+    n_el = xd.numel()
+    y = torch.empty_like(xd)
+    ms = med_ms(lambda: la.feature_map(xd, "elu1", out=y))
+    rows["a1_elu1"] = {"shape": f"[{w4.BH},{w4.L},{w4.d_in}] bf16 -> bf16", "ms": ms, **hbm(4 * n_el, ms),
+                       "bound": "hbm", "oracle_s_per_row": _oracle_time(
+                           lambda: oracle.phi_elu1(x_sample)) / 4096}
+    del xd, y, x
+    q5, _, _, W5 = wl.workload_inputs(w5, want_exact=False)
+    qd = dev_bf16(q5.bits)
+    Wd = dev_bf16(W5[0])
+    yf = torch.empty(w5.BH, w5.L, w5.m, dtype=torch.bfloat16, device="cuda")
+    ms = med_ms(lambda: la.feature_map(qd, "favor", W=Wd, out=yf))
+    fl = 2.0 * w5.BH * w5.L * w5.m * w5.d_in
+    byt = qd.numel() * 2 + yf.numel() * 2
+    Wx = W5[1]
+    q_sample = wl.bf16_bits_to_f64(q5.bits[0, :2048])
+    rows["a1_favor"] = {"shape": f"[{w5.BH},{w5.L},{w5.d_in}] x W[{w5.m},{w5.d_in}] -> bf16 [..,{w5.m}]", "ms": ms,
+                        **hbm(byt, ms), "TFLOP/s": fl / (ms * 1e-3) / 1e12,
+                        "mfma_frac": fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "bound": "hbm",
+                        "oracle_s_per_row": _oracle_time(lambda: oracle.phi_favor(q_sample, Wx)) / 2048}
+    del qd, yf, q5
+    torch.cuda.empty_cache()
+
+    # ---- a2, a3: per-chunk states and their scan at the headline shape, C = 64
     w3 = wl.WORKLOADS[3]
     q, k, v, _ = wl.workload_inputs(w3, want_exact=False)
-    qd, kd, vd = dev_bf16(q.bits), dev_bf16(k.bits), dev_bf16(v.bits)
+    kd, vd = dev_bf16(k.bits), dev_bf16(v.bits)
+    C = 64
+    N = w3.L // C
+    S, _ = la.chunk_states(kd, vd, C)
+    ms = med_ms(lambda: la.chunk_states(kd, vd, C, out=S))
+    kh = wl.bf16_bits_to_f64(k.bits[0])
+    vh = wl.bf16_bits_to_f64(v.bits[0])
+    rows["a2_chunk_states"] = {"shape": f"BH={w3.BH} L={w3.L} d={w3.d_in} C={C}", "ms": ms,
+                               **hbm(phase1_bytes(w3.BH, w3.L, w3.d_k, w3.d_v, C, False), ms), "bound": "hbm",
+                               "oracle_s_per_head": _oracle_time(lambda: oracle.chunk_states(kh, vh, C))}
+    S2 = S.clone()
+    ms = med_ms(lambda: la.state_scan(S2, None, want_final=False))
+    Sh = np.asarray(S[0].float().cpu(), dtype=np.float64)
+    rows["a3_state_scan"] = {"shape": f"BH={w3.BH} N={N} d={w3.d_k}x{w3.d_v} fp32", "ms": ms,
+                             **hbm(scan_bytes(w3.BH, N, w3.d_k, w3.d_v, False, False), ms), "bound": "hbm",
+                             "oracle_s_per_head": _oracle_time(lambda: oracle.exclusive_scan(Sh))}
+    del S, S2, Sh
+    torch.cuda.empty_cache()
+
+    # ---- a4: the forward at every workload and chunk size
+    qd = dev_bf16(q.bits)
     del q, k, v
+    fwd = {}
     for C in (32, 64, 128):
-        for g in (0, 32):
-            f = la.Forward(qd, kd, vd, C, group=g)
-            ms = time_steps(f.run, 10, 3)
-            wk = Work(w3.BH, w3.L, w3.d_in, w3.d_k, w3.d_v, C)
-            extras[f"w3_C{C}_group{g}"] = {"ms": ms, "tokens_per_s": w3.B * w3.L / (ms * 1e-3),
-                                           "hbm_frac": wk.fused_bytes() / (ms * 1e-3) / 8e12,
-                                           "tflops": wk.page_flops() / (ms * 1e-3) / 1e12}
-            del f
-    # int8 at the headline shape
+        f = la.Forward(qd, kd, vd, C)
+        ms = time_steps(f.run, 10, 3)
+        wk = Work(w3.BH, w3.L, w3.d_in, w3.d_k, w3.d_v, C)
+        fwd[f"w3_C{C}"] = {"ms": ms, "tokens_per_s": w3.B * w3.L / (ms * 1e-3), **hbm(wk.fused_bytes(), ms),
+                           "TFLOP/s_page": wk.page_flops() / (ms * 1e-3) / 1e12}
+        del f
     qi, ki, vi = wl.random_case(33, w3.BH, w3.L, 128, 128, "i8")
-    tq, tk, tv = (torch.from_numpy(x.bits).cuda() for x in (qi, ki, vi))
+    tq, tk, tv = (torch.from_numpy(t.bits).cuda() for t in (qi, ki, vi))
     del qi, ki, vi
     f = la.Forward(tq, tk, tv, 64)
     ms = time_steps(f.run, 10, 3)
     wk = Work(w3.BH, w3.L, 128, 128, 128, 64, in_bytes=1, out_bytes=4)
-    extras["w3_int8_C64"] = {"ms": ms, "tokens_per_s": w3.B * w3.L / (ms * 1e-3),
-                             "tops": wk.page_flops() / (ms * 1e-3) / 1e12,
-                             "hbm_frac": wk.fused_bytes() / (ms * 1e-3) / 8e12}
+    fwd["w3_int8_C64"] = {"ms": ms, "tokens_per_s": w3.B * w3.L / (ms * 1e-3), **hbm(wk.fused_bytes(), ms),
+                          "TOP/s_page": wk.page_flops() / (ms * 1e-3) / 1e12}
     del f, tq, tk, tv, qd, kd, vd
     torch.cuda.empty_cache()
+    decode = None
     for wid in (2, 4, 5):
         w = wl.WORKLOADS[wid]
         q, k, v, W = wl.workload_inputs(w, want_exact=False)
         qd, kd, vd = dev_bf16(q.bits), dev_bf16(k.bits), dev_bf16(v.bits)
+        del q, k, v
         Wd = dev_bf16(W[0]) if W is not None else None
         C = w.chunks[0]
         f = la.Forward(qd, kd, vd, C, normalize=w.normalize, fmap=w.fmap, W=Wd, return_state=w.return_state)
         ms = time_steps(f.run, 10, 3)
         wk = Work(w.BH, w.L, w.d_in, w.d_k, w.d_v, C, w.normalize, w.fmap)
-        extras[f"w{wid}"] = {"workload": w.name, "ms": ms, "tokens_per_s": w.B * w.L / (ms * 1e-3),
-                             "hbm_frac_fused_bytes": wk.fused_bytes(w.return_state) / (ms * 1e-3) / 8e12,
-                             "tflops": wk.page_flops() / (ms * 1e-3) / 1e12}
+        fwd[f"w{wid}"] = {"workload": w.name, "ms": ms, "tokens_per_s": w.B * w.L / (ms * 1e-3),
+                          **hbm(wk.fused_bytes(w.return_state), ms),
+                          "TFLOP/s_page": wk.page_flops() / (ms * 1e-3) / 1e12}
         if wid == 5:
+            # ---- a5: decode on 256 streams x 12 heads of 256 x 64 fp32 states
             n = wl.DECODE_STREAMS * w.H
-            idx = torch.tensor([(s % w.B) * w.H + h for s in range(wl.DECODE_STREAMS) for h in range(w.H)],
+            idx = torch.tensor([(s_ % w.B) * w.H + h for s_ in range(wl.DECODE_STREAMS) for h in range(w.H)],
                                device="cuda")
             S = f.S_final[idx].contiguous()
             z = f.z_final[idx].contiguous()
             pq, pk, pv = wl.decode_pool(w, n, pool=wl.DECODE_POOL)
             dq, dk_, dv_ = dev_bf16(pq.bits), dev_bf16(pk.bits), dev_bf16(pv.bits)
             o = torch.empty(n, w.d_v, dtype=torch.float32, device="cuda")
-            steps = args.decode_steps
             state = {"t": 0}
 
             def step():
                 t = state["t"] % wl.DECODE_POOL
                 la.recurrent_step(dq[t], dk_[t], dv_[t], S, z, fmap="favor", W=Wd, normalize=True, out=o)
                 state["t"] += 1
-            ms_d = time_steps(step, steps, 8)
+            ms_d = time_steps(step, args.decode_steps, 8)
             db = decode_bytes(n, w.d_in, w.d_k, w.d_v, True, m_proj=w.m)
-            extras["w5_decode"] = {"states": n, "steps": steps, "ms_per_step": ms_d,
-                                   "tokens_per_s": wl.DECODE_STREAMS / (ms_d * 1e-3),
-                                   "effective_GBs": db / (ms_d * 1e-3) / 1e9,
-                                   "note": "state set 201 MB fits the 256 MB Infinity Cache; effective bandwidth"}
+            Sh = np.asarray(S[:64].cpu(), dtype=np.float64)
+            zh = np.asarray(z[:64].cpu(), dtype=np.float64)
+            Wx = W[1]
+            qh = oracle.phi_favor(wl.bf16_bits_to_f64(pq.bits[0][:64]), Wx)
+            kh = oracle.phi_favor(wl.bf16_bits_to_f64(pk.bits[0][:64]), Wx)
+            vh = wl.bf16_bits_to_f64(pv.bits[0][:64])
+
+            def oracle_step():
+                for i in range(64):
+                    oracle.recurrent_step(Sh[i], zh[i], qh[i], kh[i], vh[i], True)
+            decode = {"states": n, "steps": args.decode_steps, "ms_per_step": ms_d,
+                      "tokens_per_s": wl.DECODE_STREAMS / (ms_d * 1e-3), **hbm(db, ms_d), "bound": "hbm",
+                      "note": "the 201 MB state set fits the 256 MB Infinity Cache: an effective rate",
+                      "oracle_s_per_state_step": _oracle_time(oracle_step) / 64}
         del f, qd, kd, vd
         torch.cuda.empty_cache()
-    out["extras"] = extras
+    rows["a4_forward"] = fwd
+    rows["a5_decode"] = decode
+    out["rows"] = rows
 
 
 def main():

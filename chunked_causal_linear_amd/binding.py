@@ -129,28 +129,33 @@ def _fmap_code(fmap: str) -> int:
 # ---------------------------------------------------------------------------
 # entry points
 # ---------------------------------------------------------------------------
-def feature_map(x, fmap: str, W=None, in_scale: float = 1.0, out_dtype=None):
-    """phi(in_scale * x) row by row; x [..., d_in] bf16 -> [..., d_k]."""
+def feature_map(x, fmap: str, W=None, in_scale: float = 1.0, out_dtype=None, out=None):
+    """phi(in_scale * x) row by row; x [..., d_in] bf16 -> [..., d_k] (into `out` if given)."""
     torch = _torch()
     d_in = x.shape[-1]
     rows = x.numel() // d_in
     m = W.shape[0] if (fmap == "favor" and W is not None) else 0
     d_k = m if fmap == "favor" else d_in
-    y = torch.empty(*x.shape[:-1], d_k, dtype=out_dtype or torch.bfloat16, device=x.device)
+    y = out if out is not None else torch.empty(*x.shape[:-1], d_k, dtype=out_dtype or torch.bfloat16,
+                                                device=x.device)
+    if tuple(y.shape) != tuple(x.shape[:-1]) + (d_k,):
+        raise ValueError(f"out has shape {tuple(y.shape)}, expected {tuple(x.shape[:-1]) + (d_k,)}")
     _check(lib().la_feature_map(_fmap_code(fmap), _dev(x, "x"), _dtype_code(x), rows, d_in,
                                 _dev(W, "W"), m, float(in_scale), _dev(y, "y"), _dtype_code(y), _stream_ptr()))
     return y
 
 
-def chunk_states(k, v, C: int, want_z: bool = False):
-    """Phase 1: per-chunk states S [BH, N, d_k, d_v] (and z [BH, N, d_k])."""
+def chunk_states(k, v, C: int, want_z: bool = False, out=None):
+    """Phase 1: per-chunk states S [BH, N, d_k, d_v] (and z [BH, N, d_k]); `out` = S to reuse."""
     torch = _torch()
     BH, L, d_k = k.shape
     d_v = v.shape[-1]
     Cs = 1 if C <= 0 else min(C, L)
     N = (L + Cs - 1) // Cs
     st = torch.int32 if k.dtype == torch.int8 else torch.float32
-    S = torch.empty(BH, N, d_k, d_v, dtype=st, device=k.device)
+    S = out if out is not None else torch.empty(BH, N, d_k, d_v, dtype=st, device=k.device)
+    if tuple(S.shape) != (BH, N, d_k, d_v) or S.dtype != st:
+        raise ValueError(f"out must be {(BH, N, d_k, d_v)} {st}")
     z = torch.empty(BH, N, d_k, dtype=st, device=k.device) if want_z else None
     _check(lib().la_chunk_states(_dev(k, "k"), _dev(v, "v"), _dtype_code(k), BH, L, d_k, d_v, C,
                                  _dev(S, "S"), _dev(z, "z"), _stream_ptr()))
