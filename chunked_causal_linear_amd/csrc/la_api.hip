@@ -14,7 +14,7 @@
 #endif
 
 namespace la {
-hipError_t fwd_pipe_bf16(const FwdParams& p, int DK, int DVT, int64_t grid, hipStream_t s);
+hipError_t fwd_pipe_bf16(const FwdParams& p, int DK, int DVT, int C, int64_t grid, hipStream_t s);
 }
 
 namespace {
@@ -78,7 +78,7 @@ struct Plan {
     int64_t n_chunks, G, n_groups;
     int DK, DVT, T, n_dvt;
     bool premap;  // phi computed by a separate pass into the workspace
-    bool pipe;    // streaming phase-3 kernel (chunks of 64 rows, identity map, no normaliser)
+    bool pipe;    // streaming phase-3 kernel (chunks of 32, 64 or 128 rows, identity map, no normaliser)
     bool causal, normalize;
     size_t ws_phi;     // bytes of one mapped q or k copy
     size_t ws_states;  // bytes of the group states
@@ -138,11 +138,11 @@ la_status make_plan(Plan& P, la_dtype in_dt, int64_t BH, int64_t L, int64_t d_in
         P.DK = kernel_dk_bf16(P.dk);
     }
 
-    // The streaming kernel covers chunks of exactly 64 rows with the identity
-    // map, no normaliser and feature widths of 64 or 128; it holds three LDS
-    // stages and runs one workgroup per CU.
-    P.pipe = !P.i8 && P.causal && Ce == 64 && !P.normalize && f == LA_FMAP_IDENTITY &&
-             (P.dk == 64 || P.dk == 128) && d_v % 64 == 0;
+    // The streaming kernel covers chunks of 32, 64 or 128 rows with the
+    // identity map, no normaliser and feature widths of 64 or 128; it fills
+    // the LDS and runs one workgroup per CU.
+    P.pipe = !P.i8 && P.causal && (Ce == 32 || Ce == 64 || Ce == 128) && !P.normalize &&
+             f == LA_FMAP_IDENTITY && (P.dk == 64 || P.dk == 128) && d_v % 64 == 0;
     if (P.pipe) {
         P.DK = (int)P.dk;
         P.DVT = 64;
@@ -175,7 +175,18 @@ la_status make_plan(Plan& P, la_dtype in_dt, int64_t BH, int64_t L, int64_t d_in
             if (want > P.n_chunks) want = P.n_chunks;
             P.G = cdiv(P.n_chunks, want);
         }
+        // chunks of 32 are walked in tiles of two: groups start on a tile
+        if (P.pipe && Ce == 32 && P.G < P.n_chunks && (P.G & 1)) {
+            if (group > 0)
+                P.pipe = false;  // an odd group the caller asked for: the general kernel
+            else
+                P.G += 1;
+        }
         P.n_groups = cdiv(P.n_chunks, P.G);
+    }
+    if (!P.pipe && !P.i8 && P.causal && P.DVT != kernel_dvt(d_v)) {
+        P.DVT = kernel_dvt(d_v);
+        P.n_dvt = (int)(d_v / P.DVT);
     }
     const int64_t grid = BH * P.n_groups * P.n_dvt;
     if (grid > 0x7FFFFFFFLL) return fail(LA_ERR_UNSUPPORTED, "grid too large");
@@ -250,7 +261,7 @@ static la_status launch_phase3(const Plan& P, const void* qm, const void* km, co
     p.state_scale = scaled_identity ? in_scale : 1.0f;
     hipError_t e;
     if (P.pipe && out_dt == LA_BF16)
-        return hip_status(la::fwd_pipe_bf16(p, P.DK, P.DVT, grid, s), "chunked forward launch");
+        return hip_status(la::fwd_pipe_bf16(p, P.DK, P.DVT, (int)P.C, grid, s), "chunked forward launch");
     int DVT = P.DVT, T = P.T;
     int64_t grid_g = grid;
     if (P.pipe) {

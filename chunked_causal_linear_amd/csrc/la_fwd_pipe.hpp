@@ -1,36 +1,56 @@
-// Chunked causal linear attention, fused phase 3, streaming variant for chunks
-// of 64 rows (gfx950).
+// Chunked causal linear attention, fused phase 3, streaming kernel (gfx950)
+// for chunks of 32, 64 or 128 rows, bf16 in and out, no normaliser.
 //
 // Same mathematics as chunked_fwd_bf16 (page "attention と線形の間",
 // section ②: O_c = Q_c P + tril(Q_c K_c^T) V_c with the diagonal kept, then
-// P += K_c^T V_c), organised for HBM streaming:
+// P += K_c^T V_c), organised for HBM streaming.
 //
-//  * Global -> LDS copies go through the direct-to-LDS load
-//    (global_load_lds_dwordx4): no register staging, no LDS store pass.  Three
-//    LDS stages per workgroup; the copy of chunk i+2 is issued right after the
-//    barrier that opens chunk i, so two chunks are in flight while one computes.
-//    One barrier per chunk.
-//  * Each wave computes every score block it needs itself (S^T = K Q^T on the
-//    matrix cores) and keeps the masked scores in registers: the accumulator
-//    layout of S^T is exactly the operand layout of the intra product in the
-//    permuted key order below, so scores never go through LDS.
-//  * Output blocks are produced transposed (O^T = P^T Q^T + V^T tril(S)^T), so
-//    a lane holds four consecutive output columns of one row and writes them
-//    as one 8-byte store; the store of chunk i is issued after the barrier of
-//    chunk i+1, before that chunk's copies, which keeps the memory counter
-//    arithmetic exact (stores never sit between a copy and its wait).
+// One workgroup: (head, group of chunks, tile of DVT = 64 value columns), four
+// waves, one per SIMD, in two pairs.  Pair h owns value columns [32h, 32h+32):
 //
-// LDS tiles are row-major with a per-row XOR swizzle of the 16-byte segment
-// index (the copy picks, per lane, which global segment lands in which LDS
-// slot).  The swizzle never touches bit 1 of the segment index, so the two
-// 8-byte halves of a permuted row operand stay 32 bytes apart.
+//  * compute wave h touches only LDS and the matrix cores: the scores of each
+//    chunk (S^T = K Q^T), the inter product Q P, the intra product tril(S) V and
+//    the state update P += K^T V for its 32 columns (P in fp32 accumulators).
+//    Its output rows go back into its own V columns of the LDS stage (no other
+//    wave reads them).
+//  * copy wave h issues half of every global access: direct-to-LDS copies
+//    (global_load_lds_dwordx4) of the coming tiles of Q, K and V, and the output
+//    stores (16-byte row segments read back from the stage).  A wave stalls when
+//    it has 63 memory instructions in flight or the memory queue is full; those
+//    stalls stay on the copy waves.
 //
-// Matrix-core mapping (16x16x32 bf16; permuted order inside every 32-wide
-// k-step: lane group g holds indices 4g..4g+3 and 16+4g..16+4g+3):
+// The sequence is walked in tiles of TT rows (64, or 128 for chunks of 128),
+// NSTAGE LDS stages of (Q, K, V) tiles (3, or 2 for 128-row tiles).  Per tile j,
+// after the barrier B(j) that makes tile j visible:
+//   compute waves: products of tile j from stage j % NSTAGE, output into the V
+//     tile of that stage;
+//   copy waves: read the output of tile j - 1 from stage (j - 1) % NSTAGE,
+//     refill that stage with tile j + NSTAGE - 1, store the output rows, wait
+//     until tile j + 1 has landed, B(j + 1).
+// The wait count is exact: the only memory instructions issued after tile
+// j + 1's copies and not needed yet are the copies of the tiles after it, and
+// loads complete in order (stores in between do not change that).
+//
+// LDS tiles are row-major with the 16-byte segment index XORed with the row
+// (the copy picks, per lane, which global segment lands in which LDS slot):
+// 16-byte row reads and transpose reads are conflict-free.
+//
+// Matrix-core mapping (16x16x32 bf16, fp32 accumulate):
 //   scores  S^T[key][q] += K[key][a]  Q[q][a]      A = K rows,    B = Q rows
 //   inter   O^T[j][q]   += P[a][j]    Q[q][a]      A = P (regs),  B = Q rows
 //   intra   O^T[j][q]   += V[key][j]  S^T[key][q]  A = V columns, B = S^T (regs)
 //   update  P[a][j]     += K[key][a]  V[key][j]    A = K columns, B = V columns
+// Keys are permuted inside each 32-wide k-step (lane group g holds keys
+// 4g..4g+3 and 16+4g..16+4g+3): the order in which S^T comes out of the
+// matrix core, so masked scores feed the intra product from registers; V and K
+// column operands are transpose reads (ds_read_b64_tr_b16) with that row order.
+// Features a are in natural order (lane group g holds 8g..8g+7, one 16-byte
+// read per row operand); the update reads K's columns with lane c of each row
+// quad pointing at column 8c (+4 for the second half), so its accumulator rows
+// come out as a = 32ks + 8g + 4h + i and a packed pair (h = 0, 1) is the inter
+// product's operand in natural order.  Outputs come out transposed
+// (O^T = P^T Q^T + V^T tril(S)^T): a lane holds four consecutive columns of one
+// row.
 #pragma once
 
 #include <type_traits>
@@ -42,27 +62,18 @@ namespace la {
 
 namespace pipe {
 
-constexpr int T = 64;   // rows per chunk (this kernel is for C == 64)
-#ifndef LA_PIPE_NW
-#define LA_PIPE_NW 2
-#endif
-constexpr int NW = LA_PIPE_NW;  // compute waves per workgroup
-constexpr int NCP = 2;          // copy waves per workgroup
-
 // Byte offset of element e of row r in a tile with NSEG 16-byte segments per
-// row: segment index XOR (row mod NSEG).  Row reads of 16 bytes over 16
-// consecutive rows and the transpose reads over 16 rows both spread over all
-// banks with this swizzle.
+// row: segment index XOR (row mod NSEG).
 template <int NSEG>
 __device__ __forceinline__ int tile_off(int r, int e) {
     return r * NSEG * 16 + ((((e >> 3) ^ r) & (NSEG - 1)) << 4) + ((e & 7) << 1);
 }
 
-template <int DK, int DVT>
+template <int DK, int DVT, int TT>
 struct alignas(16) Stage {
-    u16 q[T * DK];
-    u16 k[T * DK];
-    u16 v[T * DVT];
+    u16 q[TT * DK];
+    u16 k[TT * DK];
+    u16 v[TT * DVT];
 };
 
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
@@ -131,64 +142,38 @@ __device__ __forceinline__ int work_index(int remap) {
     return (b & 7) * per + (b >> 3);
 }
 
+template <int I>
+using ic = std::integral_constant<int, I>;
+
 }  // namespace pipe
 
-// One workgroup: (head, group of chunks, tile of DVT value columns); NW
-// compute waves (two by default: each then owns 32 value columns, which halves
-// the LDS reads of Q and K per output column against four waves of 16) and
-// two copy waves.  Compute wave w owns value columns [w*DVT/NW, (w+1)*DVT/NW)
-// of O and of the state; it touches only LDS and the
-// matrix cores.  The copy waves issue every global access of the chunk loop,
-// half each: the direct-to-LDS copies of Q, K, V and the output stores.  A
-// wave stalls when it has 63 memory instructions in flight (the counter's
-// limit) or the memory queue is full; keeping those stalls on waves of their
-// own lets the copies stream continuously while the compute waves work, and
-// two copy waves keep two chunks of copies in flight under that limit.
-//
-// Per chunk j, after the barrier B(j) that makes chunk j's tiles visible:
-//   compute waves: products of chunk j from stage j % NSTAGE; the output rows
-//     go back into that stage's V tile, into the columns the same wave read V
-//     from (no other wave reads them);
-//   copy waves: read the output of chunk j - 1 from stage (j - 1) % NSTAGE,
-//     refill that stage with chunk j + NSTAGE - 1, stores the output rows
-//     (full 16-byte segments of a row), then wait until chunk j + 1 has
-//     landed and meet the compute waves at B(j + 1).
-//
-// Index orders inside 32-wide k-steps.  Keys: permuted (lane group g holds keys
-// 4g..4g+3 and 16+4g..16+4g+3), the order in which the score accumulators
-// S^T[key][q] come out of the matrix core (C rows 4g + i of 16-key blocks), so
-// the masked scores feed the intra product straight from registers.  Features
-// a: natural (lane group g holds 8g..8g+7) for the 16-byte row reads of Q and
-// K; the state update reads K's columns with lane c of each row quad pointing
-// at column 8c (+4 for the second half), so the update's accumulator rows come
-// out as a = 32ks + 8g + 4h + i (h = half) and a packed pair (h = 0, 1) is the
-// inter product's operand in natural order, again without leaving registers.
-template <int DK, int DVT, int NSTAGE, bool SCALED>
-__global__ __launch_bounds__((pipe::NW + pipe::NCP) * WAVE)
-__attribute__((amdgpu_waves_per_eu((pipe::NW + pipe::NCP + 3) / 4, (pipe::NW + pipe::NCP + 3) / 4)))
+template <int DK, int DVT, int CH, bool SCALED>
+__global__ __launch_bounds__(4 * WAVE) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void chunked_fwd_pipe(FwdParams p) {
     using namespace pipe;
-    constexpr int CPW = DVT / 16 / NW;     // 16-column blocks per compute wave
-    constexpr int NQB = T / 16;            // 16-row blocks per chunk
-    constexpr int NKA = DK / 32;           // k-steps over the feature index
-    constexpr int NKK = T / 32;            // k-steps over keys
+    constexpr int TT = CH > 64 ? CH : 64;          // rows per tile
+    constexpr int NSTAGE = TT == 128 ? 2 : 3;      // LDS stages
+    constexpr int CPW = DVT / 32;                  // 16-column blocks per pair
+    constexpr int NKA = DK / 32;                   // k-steps over the feature index
     constexpr int QSEG = DK / 8, VSEG = DVT / 8;
-    constexpr int NCQ = T * QSEG / WAVE / NCP;  // copy instructions per chunk and copy wave, Q (and K)
-    constexpr int NCV = T * VSEG / WAVE / NCP;  // the same for V (and for the output stores)
+    constexpr int NCQ = TT * QSEG / WAVE / 2;      // copy instructions per tile and copy wave, Q (and K)
+    constexpr int NCV = TT * VSEG / WAVE / 2;      // the same for V (and for the output stores)
     constexpr int NL = 2 * NCQ + NCV;
-    constexpr int NTRI = NQB * (NQB + 1) / 2;
-    constexpr int RPV = WAVE / VSEG;       // output rows per store instruction
-    static_assert(CPW >= 1 && CPW * 16 * NW == DVT, "DVT must be 64 or 128");
-    static_assert(NSTAGE == 3, "three LDS stages");
+    constexpr int RPV = WAVE / VSEG;               // output rows per store instruction
+    static_assert(DVT == 64, "tile of 64 value columns");
+    static_assert(CH == 32 || CH == 64 || CH == 128, "chunks of 32, 64 or 128 rows");
+    static_assert(DK == 64 || DK == 128, "feature width 64 or 128");
     static_assert(NL < 64, "vmcnt range");
-    static_assert(NCV >= 1, "tile too small for the copy split");
+    static_assert(NSTAGE * (int)sizeof(Stage<DK, DVT, TT>) <= 160 * 1024, "LDS");
+    typedef Stage<DK, DVT, TT> StageT;
 
-    __shared__ Stage<DK, DVT> st[NSTAGE];
+    __shared__ StageT st[NSTAGE];
 
     const int tid = threadIdx.x;
     const int wave = tid / WAVE, lane = tid % WAVE, l16 = lane % 16, g = lane / 16;
-    const bool copier = wave >= NW;  // wave-uniform
-    const int cw = __builtin_amdgcn_readfirstlane(wave - NW);  // copy wave index (wave-uniform)
+    const bool copier = wave >= 2;                               // wave-uniform
+    const int h = __builtin_amdgcn_readfirstlane(wave & 1);      // pair (wave-uniform)
+    const int colw = h * CPW * 16;                               // first column of the pair
 
     const int w = work_index(p.xcd_remap);
     const int jt = w % p.n_dvt;
@@ -198,31 +183,37 @@ void chunked_fwd_pipe(FwdParams p) {
 
     const int64_t L = p.L;
     const int dv = p.dv;
-    const int64_t n_chunks = (L + T - 1) / T;
+    // This group's chunks and the tiles that hold them (for chunks of 32 the
+    // plan keeps an even number of chunks per group, so groups start on a tile).
+    const int64_t n_chunks = (L + CH - 1) / CH;
     const int64_t c_begin = (int64_t)grp * p.G;
     const int64_t c_end = c_begin + p.G < n_chunks ? c_begin + p.G : n_chunks;
+    const int64_t r_end = c_end * CH < L ? c_end * CH : L;
+    const int64_t t_begin = c_begin * CH / TT;
+    const int64_t t_end = (r_end + TT - 1) / TT;
+    const int64_t n_tiles = (L + TT - 1) / TT;
 
-    // rows of chunk c that exist
-    auto valid_rows = [&](int64_t c) -> int { return (int)(L - c * T < T ? L - c * T : T); };
+    // rows of tile t that exist
+    auto valid_rows = [&](int64_t t) -> int { return (int)(L - t * TT < TT ? L - t * TT : TT); };
 
     // rows past the end of the sequence: zero their K rows (scores and state
     // contributions vanish; their Q rows produce outputs that are not stored)
-    auto zero_tail = [&](Stage<DK, DVT>& s, int valid) __attribute__((always_inline)) {
-        const int n = (T - valid) * QSEG;
+    auto zero_tail = [&](StageT& s, int valid) __attribute__((always_inline)) {
+        const int n = (TT - valid) * QSEG;
         uint4* kk = reinterpret_cast<uint4*>(s.k + valid * DK);
-        for (int i = tid; i < n; i += (NW + NCP) * WAVE) kk[i] = make_uint4(0, 0, 0, 0);
+        for (int i = tid; i < n; i += 4 * WAVE) kk[i] = make_uint4(0, 0, 0, 0);
     };
 
     if (copier) {
-        // ================= copy wave =================
+        // ================= copy wave h =================
         const u16* qh = p.q + bh * L * DK;
         const u16* kh = p.k + bh * L * DK;
         const u16* vh = p.v + bh * L * dv + col0;
         // Lane l of copy instruction b lands in LDS slot 64b + l = (row,
         // physical segment) = (slot / NSEG, slot % NSEG), which holds the
         // global segment (physical ^ row) of that row.
-        auto issue = [&](int64_t chunk, Stage<DK, DVT>& s) __attribute__((always_inline)) {
-            const int64_t r0 = chunk * T;
+        auto issue = [&](int64_t t, StageT& s) __attribute__((always_inline)) {
+            const int64_t r0 = t * TT;
             const int last = (int)(L - 1 - r0);  // rows past it are clamped to it
             const u16* qb_ = qh + r0 * DK;
             const u16* kb_ = kh + r0 * DK;
@@ -230,7 +221,7 @@ void chunked_fwd_pipe(FwdParams p) {
             const uint32_t lq = lds_addr(s.q), lk = lds_addr(s.k), lv = lds_addr(s.v);
 #pragma unroll
             for (int i = 0; i < NCQ; ++i) {
-                const int b = cw * NCQ + i;  // copy instruction within the tile
+                const int b = h * NCQ + i;  // copy instruction within the tile
                 const int slot = b * WAVE + lane;
                 const int r = slot / QSEG, seg = (slot % QSEG) ^ (r & (QSEG - 1));
                 const uint32_t off = (uint32_t)(((r < last ? r : last) * DK + seg * 8) * 2);
@@ -239,84 +230,84 @@ void chunked_fwd_pipe(FwdParams p) {
             }
 #pragma unroll
             for (int i = 0; i < NCV; ++i) {
-                const int b = cw * NCV + i;
+                const int b = h * NCV + i;
                 const int slot = b * WAVE + lane;
                 const int r = slot / VSEG, seg = (slot % VSEG) ^ (r & (VSEG - 1));
                 dma16(vb_, (uint32_t)(((r < last ? r : last) * dv + seg * 8) * 2), lv + b * WAVE * 16);
             }
         };
-        // Output rows of chunk c sit in the V tile of stage `from`: instruction
-        // i, lane l covers row i * RPV + l / VSEG, segment l % VSEG.  Read them,
-        // refill the stage with chunk `refill` (if any), store them.
-        auto drain_refill = [&](const Stage<DK, DVT>& from, int64_t c, int64_t refill, Stage<DK, DVT>& to)
+        // Output rows of tile t sit in the V tile of stage `from`: instruction
+        // i, lane l covers row (h * NCV + i) * RPV + l / VSEG, segment l % VSEG.
+        // Read them, refill the stage with tile `refill` (if any), store them.
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        auto drain_refill = [&](const StageT& from, int64_t t, int64_t refill, StageT& to)
             __attribute__((always_inline)) {
-            typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
             u32x4 ob[NCV];
 #pragma unroll
             for (int i = 0; i < NCV; ++i) {
-                const int r = (cw * NCV + i) * RPV + lane / VSEG, seg = lane % VSEG;
+                const int r = (h * NCV + i) * RPV + lane / VSEG, seg = lane % VSEG;
                 ob[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(from.v) +
                                                         tile_off<VSEG>(r, seg * 8));
             }
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): reads done before the refill
             if (refill >= 0) issue(refill, to);
-            const int valid = valid_rows(c);
-            u16* o = reinterpret_cast<u16*>(p.o) + (bh * L + c * T) * dv + col0;
+            const int valid = valid_rows(t);
+            u16* o = reinterpret_cast<u16*>(p.o) + (bh * L + t * TT) * dv + col0;
 #pragma unroll
             for (int i = 0; i < NCV; ++i) {
-                const int r = (cw * NCV + i) * RPV + lane / VSEG, seg = lane % VSEG;
+                const int r = (h * NCV + i) * RPV + lane / VSEG, seg = lane % VSEG;
                 if (r < valid) *reinterpret_cast<u32x4*>(o + (int64_t)r * dv + seg * 8) = ob[i];
             }
         };
 
 #pragma unroll
         for (int s0 = 0; s0 < NSTAGE - 1; ++s0)
-            if (c_begin + s0 < c_end) issue(c_begin + s0, st[s0]);
-        // wait for the first chunk: the copies issued after it are those of the second
-        if (c_begin + 1 < c_end)
+            if (t_begin + s0 < t_end) issue(t_begin + s0, st[s0]);
+        // wait for the first tile: the copies issued after it are those of the tiles after it
+        if (NSTAGE == 3 && t_begin + 1 < t_end)
             wait_vm<NL>();
         else
             wait_vm<0>();
 
-        auto step = [&](auto sidx, int64_t chunk) __attribute__((always_inline)) {
+        auto step = [&](auto sidx, int64_t t) __attribute__((always_inline)) {
             constexpr int SI = decltype(sidx)::value;
-            constexpr int SP = (SI + NSTAGE - 1) % NSTAGE;  // stage of chunk - 1
-            __syncthreads();  // B(chunk)
-            if (valid_rows(chunk) < T) {
-                zero_tail(st[SI], valid_rows(chunk));
+            constexpr int SP = (SI + NSTAGE - 1) % NSTAGE;  // stage of tile t - 1
+            __syncthreads();  // B(t)
+            if (valid_rows(t) < TT) {
+                zero_tail(st[SI], valid_rows(t));
                 __syncthreads();
             }
-            const int64_t refill = chunk + NSTAGE - 1 < c_end ? chunk + NSTAGE - 1 : -1;
-            if (chunk > c_begin)
-                drain_refill(st[SP], chunk - 1, refill, st[SP]);
+            const int64_t refill = t + NSTAGE - 1 < t_end ? t + NSTAGE - 1 : -1;
+            if (t > t_begin)
+                drain_refill(st[SP], t - 1, refill, st[SP]);
             else if (refill >= 0)
                 issue(refill, st[SP]);
-            // chunk + 1 must have landed before B(chunk + 1); the loads issued after
-            // it are those of chunk + 2 (if any); loads complete in order
-            if (chunk + 2 < c_end)
+            // tile t + 1 must have landed before B(t + 1); the loads issued after
+            // it are those of tile t + 2 (three stages, if any); loads complete in order
+            if (NSTAGE == 3 && t + 2 < t_end)
                 wait_vm<NL>();
             else
                 wait_vm<0>();
         };
-        for (int64_t chunk = c_begin; chunk < c_end; chunk += NSTAGE) {
-            step(std::integral_constant<int, 0>{}, chunk);
-            if (chunk + 1 < c_end) step(std::integral_constant<int, 1>{}, chunk + 1);
-            if (chunk + 2 < c_end) step(std::integral_constant<int, 2>{}, chunk + 2);
+        for (int64_t t = t_begin; t < t_end; t += NSTAGE) {
+            step(ic<0>{}, t);
+            if (t + 1 < t_end) step(ic<1>{}, t + 1);
+            if constexpr (NSTAGE == 3)
+                if (t + 2 < t_end) step(ic<NSTAGE - 1>{}, t + 2);
         }
-        __syncthreads();  // the last chunk's output is in its stage
-        const int sl = (int)((c_end - 1 - c_begin) % NSTAGE);
+        __syncthreads();  // the last tile's output is in its stage
+        const int sl = (int)((t_end - 1 - t_begin) % NSTAGE);
         if (sl == 0)
-            drain_refill(st[0], c_end - 1, -1, st[0]);
+            drain_refill(st[0], t_end - 1, -1, st[0]);
         else if (sl == 1)
-            drain_refill(st[1], c_end - 1, -1, st[1]);
+            drain_refill(st[1], t_end - 1, -1, st[1]);
         else
-            drain_refill(st[2], c_end - 1, -1, st[2]);
+            drain_refill(st[NSTAGE - 1], t_end - 1, -1, st[NSTAGE - 1]);
         return;
     }
 
-    // ================= compute waves =================
-    // ---- state P: P[c][ks][h] lane (l16, g) element i = P[a = 32ks + 8g + 4h + i][j = colw + 16c + l16]
-    const int colw = wave * CPW * 16;
+    // ================= compute wave h =================
+    // state P: P[c][ks][hf] lane (l16, g) element i = P[a = 32ks + 8g + 4hf + i][j = colw + 16c + l16]
     f32x4 P[CPW][NKA][2];
 #pragma unroll
     for (int c = 0; c < CPW; ++c)
@@ -329,133 +320,272 @@ void chunked_fwd_pipe(FwdParams p) {
 #pragma unroll
             for (int ks = 0; ks < NKA; ++ks)
 #pragma unroll
-                for (int h = 0; h < 2; ++h)
+                for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        P[c][ks][h][i] = P0[(int64_t)(32 * ks + 8 * g + 4 * h + i) * dv + c * 16];
+                        P[c][ks][hf][i] = P0[(int64_t)(32 * ks + 8 * g + 4 * hf + i) * dv + c * 16];
     }
     const float osc = p.out_scale;
-
-    // Operands of one 32-wide feature step: Q rows (B of the scores and of the
-    // inter product) and K rows (A of the scores).
-    auto load_qk = [&](const Stage<DK, DVT>& s, int ks, bf16x8 (&qa)[NQB], bf16x8 (&ka)[NQB])
-        __attribute__((always_inline)) {
-#pragma unroll
-        for (int b = 0; b < NQB; ++b) {
-            qa[b] = row_op<QSEG>(s.q, b * 16 + l16, ks * 32, g);
-            ka[b] = row_op<QSEG>(s.k, b * 16 + l16, ks * 32, g);
-        }
-    };
-
-    // K column operands of one feature step for the state update: columns
-    // 32ks + 8c + 4h (lane c of each row quad), keys in the permuted order.
     const int c4 = 4 * (lane & 3), c8 = 8 * (lane & 3);
-    auto load_kc = [&](const Stage<DK, DVT>& s, int ks, bf16x8 (&kc)[2][NKK]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) kc[h][kk] = col_op<QSEG>(s.k, kk * 32, ks * 32 + c8 + 4 * h, lane);
-    };
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
-    // The chunk's products, one 32-wide feature step at a time: scores, the
-    // inter product (which reads the state as it was before this chunk) and
-    // that step's rows of the state update, with the next step's operands
-    // loaded ahead.  Then the mask, the intra product and the output, which
-    // goes back into this wave's V columns.
-    auto compute = [&](Stage<DK, DVT>& s) __attribute__((always_inline)) {
-        bf16x8 qa0[NQB], ka0[NQB], qa1[NQB], ka1[NQB];
-        bf16x8 kc0[2][NKK], kc1[2][NKK];
-        bf16x8 vb[CPW][NKK];
-        load_qk(s, 0, qa0, ka0);
+    // Scores of the lower-triangle window of query blocks Q0 + qb and key blocks
+    // K0 + kb, kb <= qb < 4 (10 blocks, index qb(qb+1)/2 + kb; with HALVES only
+    // the blocks inside each 32-row half), masked on the diagonal, and the
+    // inter product with the packed state for the query blocks in INTER (a bit
+    // mask); feature steps one at a time, the next step's operands loaded ahead.
+    auto tri_window = [&](const StageT& s, auto q0c, auto k0c, auto halvesc, auto interc, f32x4 (&S)[10],
+                          f32x4 (&O)[CPW][4], const bf16x8 (&pst)[CPW][NKA]) __attribute__((always_inline)) {
+        constexpr int Q0 = decltype(q0c)::value, K0 = decltype(k0c)::value;
+        constexpr bool HALVES = decltype(halvesc)::value != 0;
+        constexpr int INTER = decltype(interc)::value;
+        bf16x8 qa[2][4], ka[2][4];
+        auto load = [&](int ks, bf16x8 (&q_)[4], bf16x8 (&k_)[4]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int c = 0; c < CPW; ++c)
+            for (int b = 0; b < 4; ++b) {
+                q_[b] = row_op<QSEG>(s.q, (Q0 + b) * 16 + l16, ks * 32, g);
+                k_[b] = row_op<QSEG>(s.k, (K0 + b) * 16 + l16, ks * 32, g);
+            }
+        };
 #pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) vb[c][kk] = col_op<VSEG>(s.v, kk * 32, colw + c * 16 + c4, lane);
-        load_kc(s, 0, kc0);
-        f32x4 S[NTRI];  // S^T blocks (kb <= qb), index qb(qb+1)/2 + kb
-        f32x4 O[CPW][NQB];  // O^T blocks: lane holds O[q = 16qb + l16][j = colw + 16c + 4g + i]
-#pragma unroll
-        for (int t = 0; t < NTRI; ++t) S[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int c = 0; c < CPW; ++c)
-#pragma unroll
-            for (int qb = 0; qb < NQB; ++qb) O[c][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < 10; ++i) S[i] = zero4;
+        load(0, qa[0], ka[0]);
 #pragma unroll
         for (int ks = 0; ks < NKA; ++ks) {
-            bf16x8 (&qa)[NQB] = (ks & 1) ? qa1 : qa0;
-            bf16x8 (&ka)[NQB] = (ks & 1) ? ka1 : ka0;
-            bf16x8 (&kc)[2][NKK] = (ks & 1) ? kc1 : kc0;
-            if (ks + 1 < NKA) {
-                load_qk(s, ks + 1, (ks & 1) ? qa0 : qa1, (ks & 1) ? ka0 : ka1);
-                load_kc(s, ks + 1, (ks & 1) ? kc0 : kc1);
-            }
+            if (ks + 1 < NKA) load(ks + 1, qa[(ks + 1) & 1], ka[(ks + 1) & 1]);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int qb = 0; qb < NQB; ++qb)
+            for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
                 for (int kb = 0; kb <= qb; ++kb)
-                    S[qb * (qb + 1) / 2 + kb] = mfma_bf16(ka[kb], qa[qb], S[qb * (qb + 1) / 2 + kb]);
+                    if (!HALVES || (qb >> 1) == (kb >> 1))
+                        S[qb * (qb + 1) / 2 + kb] =
+                            mfma_bf16(ka[ks & 1][kb], qa[ks & 1][qb], S[qb * (qb + 1) / 2 + kb]);
 #pragma unroll
-            for (int c = 0; c < CPW; ++c) {
-                const bf16x8 pb = pack_acc_bf16(P[c][ks][0], P[c][ks][1]);
+            for (int c = 0; c < CPW; ++c)
 #pragma unroll
-                for (int qb = 0; qb < NQB; ++qb) O[c][qb] = mfma_bf16(pb, qa[qb], O[c][qb]);
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-#pragma unroll
-                    for (int kk = 0; kk < NKK; ++kk) P[c][ks][h] = mfma_bf16(kc[h][kk], vb[c][kk], P[c][ks][h]);
-            }
+                for (int qb = 0; qb < 4; ++qb)
+                    if ((INTER >> qb) & 1) O[c][qb] = mfma_bf16(pst[c][ks], qa[ks & 1][qb], O[c][qb]);
         }
-        // causal mask on the diagonal blocks: keep key 16qb + 4g + i <= q = 16qb + l16
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb)
+        for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 if (4 * g + i > l16) S[qb * (qb + 1) / 2 + qb][i] = 0.f;
-        // intra: key steps kk <= qb / 2 (blocks past the diagonal are zero)
-        const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) {
-#pragma unroll
-            for (int kk = 0; kk <= qb / 2; ++kk) {
-                const int kb0 = 2 * kk, kb1 = 2 * kk + 1;
-                const f32x4 s0 = S[qb * (qb + 1) / 2 + kb0];
-                const f32x4 s1 = kb1 <= qb ? S[qb * (qb + 1) / 2 + kb1] : zero4;
-                const bf16x8 sb = pack_acc_bf16(s0, s1);
-#pragma unroll
-                for (int c = 0; c < CPW; ++c) O[c][qb] = mfma_bf16(vb[c][kk], sb, O[c][qb]);
-            }
-        }
-        // output rows into this wave's V columns (after its last V read, in order)
+    };
+
+    // intra product of a window: query blocks qb < 4 of O against the key steps
+    // kk <= qb / 2 of its own 64 keys (V key rows 32 * (KK0 + kk))
+    auto tri_intra = [&](const StageT& s, auto kk0c, const f32x4 (&S)[10], f32x4 (&O)[CPW][4])
+        __attribute__((always_inline)) {
+        constexpr int KK0 = decltype(kk0c)::value;
+        bf16x8 vb[CPW][2];
 #pragma unroll
         for (int c = 0; c < CPW; ++c)
 #pragma unroll
-            for (int qb = 0; qb < NQB; ++qb) {
+            for (int kk = 0; kk < 2; ++kk) vb[c][kk] = col_op<VSEG>(s.v, (KK0 + kk) * 32, colw + c * 16 + c4, lane);
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+            for (int kk = 0; kk <= qb / 2; ++kk) {
+                const f32x4 s1 = 2 * kk + 1 <= qb ? S[qb * (qb + 1) / 2 + 2 * kk + 1] : zero4;
+                const bf16x8 sb = pack_acc_bf16(S[qb * (qb + 1) / 2 + 2 * kk], s1);
+#pragma unroll
+                for (int c = 0; c < CPW; ++c) O[c][qb] = mfma_bf16(vb[c][kk], sb, O[c][qb]);
+            }
+    };
+
+    // state update with the key steps KK0 .. KK0 + NK - 1 of the tile, K column
+    // operands one (ks, hf) step ahead
+    auto update = [&](const StageT& s, auto kk0c, auto nkc) __attribute__((always_inline)) {
+        constexpr int KK0 = decltype(kk0c)::value, NK = decltype(nkc)::value;
+        bf16x8 vb[CPW][NK];
+#pragma unroll
+        for (int c = 0; c < CPW; ++c)
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk) vb[c][kk] = col_op<VSEG>(s.v, (KK0 + kk) * 32, colw + c * 16 + c4, lane);
+        bf16x8 kc[2][NK];
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) kc[0][kk] = col_op<QSEG>(s.k, (KK0 + kk) * 32, c8, lane);
+#pragma unroll
+        for (int t = 0; t < 2 * NKA; ++t) {
+            const int ks = t >> 1, hf = t & 1;
+            if (t + 1 < 2 * NKA) {
+                const int ks1 = (t + 1) >> 1, hf1 = (t + 1) & 1;
+#pragma unroll
+                for (int kk = 0; kk < NK; ++kk)
+                    kc[(t + 1) & 1][kk] = col_op<QSEG>(s.k, (KK0 + kk) * 32, ks1 * 32 + c8 + 4 * hf1, lane);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk)
+#pragma unroll
+                for (int c = 0; c < CPW; ++c) P[c][ks][hf] = mfma_bf16(kc[t & 1][kk], vb[c][kk], P[c][ks][hf]);
+        }
+    };
+
+    auto pack_state = [&](bf16x8 (&pst)[CPW][NKA]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int c = 0; c < CPW; ++c)
+#pragma unroll
+            for (int ks = 0; ks < NKA; ++ks) pst[c][ks] = pack_acc_bf16(P[c][ks][0], P[c][ks][1]);
+    };
+
+    // inter product of query blocks Q0 + b, b in [B0, B0 + 2), reading Q again
+    auto inter2 = [&](const StageT& s, auto q0c, auto b0c, f32x4 (&O)[CPW][4], const bf16x8 (&pst)[CPW][NKA])
+        __attribute__((always_inline)) {
+        constexpr int Q0 = decltype(q0c)::value, B0 = decltype(b0c)::value;
+        bf16x8 qa[NKA][2];
+#pragma unroll
+        for (int ks = 0; ks < NKA; ++ks)
+#pragma unroll
+            for (int b = 0; b < 2; ++b) qa[ks][b] = row_op<QSEG>(s.q, (Q0 + B0 + b) * 16 + l16, ks * 32, g);
+#pragma unroll
+        for (int ks = 0; ks < NKA; ++ks)
+#pragma unroll
+            for (int c = 0; c < CPW; ++c)
+#pragma unroll
+                for (int b = 0; b < 2; ++b) O[c][B0 + b] = mfma_bf16(pst[c][ks], qa[ks][b], O[c][B0 + b]);
+    };
+
+    // output rows of query blocks Q0 + qb into this wave's V columns (after its
+    // last V read of the tile, in program order)
+    auto write_out = [&](StageT& s, auto q0c, f32x4 (&O)[CPW][4]) __attribute__((always_inline)) {
+        constexpr int Q0 = decltype(q0c)::value;
+#pragma unroll
+        for (int c = 0; c < CPW; ++c)
+#pragma unroll
+            for (int qb = 0; qb < 4; ++qb) {
                 f32x4 o = O[c][qb];
                 if (SCALED) o *= osc;
                 *reinterpret_cast<uint2*>(reinterpret_cast<char*>(s.v) +
-                                          tile_off<VSEG>(qb * 16 + l16, colw + c * 16 + 4 * g)) =
+                                          tile_off<VSEG>((Q0 + qb) * 16 + l16, colw + c * 16 + 4 * g)) =
                     make_uint2(pack2_bf16(o[0], o[1]), pack2_bf16(o[2], o[3]));
             }
     };
 
-    auto step = [&](auto sidx, int64_t chunk) __attribute__((always_inline)) {
+    auto zero_o = [&](f32x4 (&O)[CPW][4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int c = 0; c < CPW; ++c)
+#pragma unroll
+            for (int qb = 0; qb < 4; ++qb) O[c][qb] = zero4;
+    };
+
+    // ---- one tile's products
+    auto compute = [&](StageT& s) __attribute__((always_inline)) {
+        bf16x8 pst[CPW][NKA];
+        pack_state(pst);
+        if constexpr (CH == 64) {
+            f32x4 S[10], O[CPW][4];
+            zero_o(O);
+            tri_window(s, ic<0>{}, ic<0>{}, ic<0>{}, ic<15>{}, S, O, pst);
+            tri_intra(s, ic<0>{}, S, O);
+            update(s, ic<0>{}, ic<2>{});
+            write_out(s, ic<0>{}, O);
+        } else if constexpr (CH == 32) {
+            // two chunks per tile: rows 0..31 (A) and 32..63 (B).  Scores only
+            // inside each chunk; A's inter product reads the state before A,
+            // B's the state after A's update.
+            f32x4 S[10], O[CPW][4];
+            zero_o(O);
+            tri_window(s, ic<0>{}, ic<0>{}, ic<1>{}, ic<3>{}, S, O, pst);
+            update(s, ic<0>{}, ic<1>{});  // A's keys (key step 0)
+            pack_state(pst);
+            inter2(s, ic<0>{}, ic<2>{}, O, pst);
+            update(s, ic<1>{}, ic<1>{});  // B's keys (key step 1)
+            bf16x8 vb[CPW][2];
+#pragma unroll
+            for (int c = 0; c < CPW; ++c)
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) vb[c][kk] = col_op<VSEG>(s.v, kk * 32, colw + c * 16 + c4, lane);
+            // intra inside each chunk: query block 0 (key block 0), 1 (key blocks
+            // 0, 1), 2 (key block 2), 3 (key blocks 2, 3); diagonals masked
+            const bf16x8 s0 = pack_acc_bf16(S[0], zero4);
+            const bf16x8 s1 = pack_acc_bf16(S[1], S[2]);
+            const bf16x8 s2 = pack_acc_bf16(S[5], zero4);
+            const bf16x8 s3 = pack_acc_bf16(S[8], S[9]);
+#pragma unroll
+            for (int c = 0; c < CPW; ++c) {
+                O[c][0] = mfma_bf16(vb[c][0], s0, O[c][0]);
+                O[c][1] = mfma_bf16(vb[c][0], s1, O[c][1]);
+                O[c][2] = mfma_bf16(vb[c][1], s2, O[c][2]);
+                O[c][3] = mfma_bf16(vb[c][1], s3, O[c][3]);
+            }
+            write_out(s, ic<0>{}, O);
+        } else {
+            // one chunk of 128 rows per tile: query rows 0..63 against their own
+            // keys; query rows 64..127 against their own keys and the full block
+            // of keys 0..63; then the update with all 128 keys.
+            f32x4 Oa[CPW][4], Ob[CPW][4];
+            zero_o(Oa);
+            zero_o(Ob);
+            {
+                f32x4 S[10];
+                tri_window(s, ic<0>{}, ic<0>{}, ic<0>{}, ic<15>{}, S, Oa, pst);
+                tri_intra(s, ic<0>{}, S, Oa);
+            }
+            {
+                f32x4 S[10];
+                tri_window(s, ic<4>{}, ic<4>{}, ic<0>{}, ic<15>{}, S, Ob, pst);
+                tri_intra(s, ic<2>{}, S, Ob);
+            }
+            // cross block, one key step (two 16-key blocks) at a time
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                f32x4 X[4][2];
+#pragma unroll
+                for (int qb = 0; qb < 4; ++qb) X[qb][0] = X[qb][1] = zero4;
+                bf16x8 qa[2][4], ka[2][2];
+                auto load = [&](int ks, bf16x8 (&q_)[4], bf16x8 (&k_)[2]) __attribute__((always_inline)) {
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) q_[b] = row_op<QSEG>(s.q, (4 + b) * 16 + l16, ks * 32, g);
+#pragma unroll
+                    for (int b = 0; b < 2; ++b) k_[b] = row_op<QSEG>(s.k, (2 * kk + b) * 16 + l16, ks * 32, g);
+                };
+                load(0, qa[0], ka[0]);
+#pragma unroll
+                for (int ks = 0; ks < NKA; ++ks) {
+                    if (ks + 1 < NKA) load(ks + 1, qa[(ks + 1) & 1], ka[(ks + 1) & 1]);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+                        for (int b = 0; b < 2; ++b) X[qb][b] = mfma_bf16(ka[ks & 1][b], qa[ks & 1][qb], X[qb][b]);
+                }
+                bf16x8 vb[CPW];
+#pragma unroll
+                for (int c = 0; c < CPW; ++c) vb[c] = col_op<VSEG>(s.v, kk * 32, colw + c * 16 + c4, lane);
+#pragma unroll
+                for (int qb = 0; qb < 4; ++qb) {
+                    const bf16x8 xb = pack_acc_bf16(X[qb][0], X[qb][1]);
+#pragma unroll
+                    for (int c = 0; c < CPW; ++c) Ob[c][qb] = mfma_bf16(vb[c], xb, Ob[c][qb]);
+                }
+            }
+            update(s, ic<0>{}, ic<4>{});
+            write_out(s, ic<0>{}, Oa);
+            write_out(s, ic<4>{}, Ob);
+        }
+    };
+
+    auto step = [&](auto sidx, int64_t t) __attribute__((always_inline)) {
         constexpr int SI = decltype(sidx)::value;
-        __syncthreads();  // B(chunk)
-        if (valid_rows(chunk) < T) {
-            zero_tail(st[SI], valid_rows(chunk));
+        __syncthreads();  // B(t)
+        if (valid_rows(t) < TT) {
+            zero_tail(st[SI], valid_rows(t));
             __syncthreads();
         }
         compute(st[SI]);
     };
-    for (int64_t chunk = c_begin; chunk < c_end; chunk += NSTAGE) {
-        step(std::integral_constant<int, 0>{}, chunk);
-        if (chunk + 1 < c_end) step(std::integral_constant<int, 1>{}, chunk + 1);
-        if (chunk + 2 < c_end) step(std::integral_constant<int, 2>{}, chunk + 2);
+    for (int64_t t = t_begin; t < t_end; t += NSTAGE) {
+        step(ic<0>{}, t);
+        if (t + 1 < t_end) step(ic<1>{}, t + 1);
+        if constexpr (NSTAGE == 3)
+            if (t + 2 < t_end) step(ic<NSTAGE - 1>{}, t + 2);
     }
-    __syncthreads();  // matches the copy wave's final barrier
+    __syncthreads();  // matches the copy waves' final barrier
 
-    if (c_end == n_chunks && p.S_final != nullptr) {
+    if (t_end == n_tiles && p.S_final != nullptr) {
         float* Sf = p.S_final + (bh * DK) * (int64_t)dv + col0 + colw + l16;
         const float ss = p.state_scale;
 #pragma unroll
@@ -463,20 +593,20 @@ void chunked_fwd_pipe(FwdParams p) {
 #pragma unroll
             for (int ks = 0; ks < NKA; ++ks)
 #pragma unroll
-                for (int h = 0; h < 2; ++h)
+                for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        Sf[(int64_t)(32 * ks + 8 * g + 4 * h + i) * dv + c * 16] = P[c][ks][h][i] * ss;
+                        Sf[(int64_t)(32 * ks + 8 * g + 4 * hf + i) * dv + c * 16] = P[c][ks][hf][i] * ss;
     }
 }
 
-template <int DK, int DVT>
+template <int DK, int DVT, int CH>
 hipError_t launch_fwd_pipe(const FwdParams& p, int64_t grid, hipStream_t s) {
-    const dim3 block((pipe::NW + pipe::NCP) * WAVE);
+    const dim3 block(4 * WAVE);
     if (p.out_scale != 1.0f)
-        hipLaunchKernelGGL((chunked_fwd_pipe<DK, DVT, 3, true>), dim3((unsigned)grid), block, 0, s, p);
+        hipLaunchKernelGGL((chunked_fwd_pipe<DK, DVT, CH, true>), dim3((unsigned)grid), block, 0, s, p);
     else
-        hipLaunchKernelGGL((chunked_fwd_pipe<DK, DVT, 3, false>), dim3((unsigned)grid), block, 0, s, p);
+        hipLaunchKernelGGL((chunked_fwd_pipe<DK, DVT, CH, false>), dim3((unsigned)grid), block, 0, s, p);
     return hipGetLastError();
 }
 

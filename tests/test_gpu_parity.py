@@ -124,6 +124,20 @@ def test_bf16_chunk64_streaming(dk, dv, L, group, out):
     assert_close(host(S), refS, what="S")
 
 
+@pytest.mark.parametrize("C,dk,dv,L,group", [(32, 128, 128, 700, 0), (32, 64, 64, 1000, 4), (32, 128, 64, 700, 3),
+                                              (32, 64, 128, 75, 0), (128, 128, 128, 1000, 0),
+                                              (128, 64, 128, 1300, 2), (128, 128, 64, 200, 0), (128, 64, 64, 128, 0)])
+def test_bf16_chunk32_128_streaming(C, dk, dv, L, group):
+    """Chunks of 32 (two per 64-row tile; an odd group falls back to the general
+    kernel) and of 128 (one per 128-row tile): ragged tails, groups, widths."""
+    q, k, v = _case(16, 2, L, dk, dv, "bf16")
+    log(f"bf16 C={C} dk={dk} dv={dv} L={L} group={group}")
+    o, S, _ = la.chunked_forward(dev_input(q), dev_input(k), dev_input(v), C, return_state=True, group=group)
+    ref, refS, _ = _oracle_forward(q.exact, k.exact, v.exact, C)
+    assert_close(host(o), ref, what="o")
+    assert_close(host(S), refS, what="S")
+
+
 @pytest.mark.parametrize("group", [1, 2, 3, 5, 100])
 def test_bf16_groups(group):
     q, k, v = _case(11, 2, 640, 64, 64, "bf16")
