@@ -84,8 +84,13 @@ def test_workspace_sizes_and_errors():
     # 128 heads x 2 column tiles already fill the GPU, one group per head
     assert ws(b.LA_BF16, 128, 8192, 128, 128, 64, 1, 0, 0, 0, 1.0, 0) == 0
     assert lib.la_chunked_forward_group(b.LA_BF16, 128, 8192, 128, 128, 64, 1, 0, 0, 0, 0) == 8192 // 64
-    # chunks of 32 (general kernel): four groups per (head, column tile)
-    assert ws(b.LA_BF16, 128, 8192, 128, 128, 32, 1, 0, 0, 0, 1.0, 0) == 128 * 4 * 128 * 128 * 4
+    # chunks of 32 and 128 stream the same way: one group per head
+    assert ws(b.LA_BF16, 128, 8192, 128, 128, 32, 1, 0, 0, 0, 1.0, 0) == 0
+    assert ws(b.LA_BF16, 128, 8192, 128, 128, 128, 1, 0, 0, 0, 1.0, 0) == 0
+    # chunks of 48 (general kernel): four groups per (head, column tile)
+    assert ws(b.LA_BF16, 128, 8192, 128, 128, 48, 1, 0, 0, 0, 1.0, 0) == 128 * 4 * 128 * 128 * 4
+    # chunks of 32 keep an even number per group on the streaming kernel
+    assert lib.la_chunked_forward_group(b.LA_BF16, 2, 8192, 128, 128, 32, 1, 0, 0, 0, 0) % 2 == 0
     # groups: BH * n_groups * (dk*dv + dk) floats (normalised), 256-byte aligned pieces
     n = ws(b.LA_BF16, 2, 1024, 64, 64, 64, 1, 1, 1, 0, 1.0, 4)
     groups = 1024 // 64 // 4
