@@ -97,6 +97,16 @@ def time_steps(fn, steps: int, warmup: int):
     return start.elapsed_time(end) / steps
 
 
+def row_time(fn, steps: int = 20, spin_s: float = 0.15):
+    """time_steps after running fn untimed for spin_s seconds (clock ramp)."""
+    import torch
+    t_end = time.perf_counter() + spin_s
+    while time.perf_counter() < t_end:
+        fn()
+        torch.cuda.synchronize()
+    return time_steps(fn, steps, 2)
+
+
 def per_launch_ms(fn, steps: int):
     """Per-call durations (ms) with an event pair around each call."""
     import torch
@@ -319,7 +329,7 @@ def run_extras(args, out):
     fwd = {}
     for C in (32, 64, 128):
         f = la.Forward(qd, kd, vd, C)
-        ms = time_steps(f.run, 10, 3)
+        ms = row_time(f.run)
         wk = Work(w3.BH, w3.L, w3.d_in, w3.d_k, w3.d_v, C)
         fwd[f"w3_C{C}"] = {"ms": ms, "tokens_per_s": w3.B * w3.L / (ms * 1e-3), **hbm(wk.fused_bytes(), ms),
                            "TFLOP/s_page": wk.page_flops() / (ms * 1e-3) / 1e12}
@@ -328,7 +338,7 @@ def run_extras(args, out):
     tq, tk, tv = (torch.from_numpy(t.bits).cuda() for t in (qi, ki, vi))
     del qi, ki, vi
     f = la.Forward(tq, tk, tv, 64)
-    ms = time_steps(f.run, 10, 3)
+    ms = row_time(f.run)
     wk = Work(w3.BH, w3.L, 128, 128, 128, 64, in_bytes=1, out_bytes=4)
     fwd["w3_int8_C64"] = {"ms": ms, "tokens_per_s": w3.B * w3.L / (ms * 1e-3), **hbm(wk.fused_bytes(), ms),
                           "TOP/s_page": wk.page_flops() / (ms * 1e-3) / 1e12}
@@ -343,7 +353,7 @@ def run_extras(args, out):
         Wd = dev_bf16(W[0]) if W is not None else None
         C = w.chunks[0]
         f = la.Forward(qd, kd, vd, C, normalize=w.normalize, fmap=w.fmap, W=Wd, return_state=w.return_state)
-        ms = time_steps(f.run, 10, 3)
+        ms = row_time(f.run)
         wk = Work(w.BH, w.L, w.d_in, w.d_k, w.d_v, C, w.normalize, w.fmap)
         fwd[f"w{wid}"] = {"workload": w.name, "ms": ms, "tokens_per_s": w.B * w.L / (ms * 1e-3),
                           **hbm(wk.fused_bytes(w.return_state), ms),

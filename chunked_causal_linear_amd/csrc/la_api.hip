@@ -78,7 +78,7 @@ struct Plan {
     int64_t n_chunks, G, n_groups;
     int DK, DVT, T, n_dvt;
     bool premap;  // phi computed by a separate pass into the workspace
-    bool pipe;    // streaming phase-3 kernel (chunks of 32, 64 or 128 rows, identity map, no normaliser)
+    bool pipe;    // streaming phase-3 kernel (chunks of 32, 64 or 128 rows; identity map, or elu+1 pre-mapped)
     bool causal, normalize;
     size_t ws_phi;     // bytes of one mapped q or k copy
     size_t ws_states;  // bytes of the group states
@@ -126,10 +126,10 @@ la_status make_plan(Plan& P, la_dtype in_dt, int64_t BH, int64_t L, int64_t d_in
 
     int64_t Ce = C <= 0 ? 1 : C;
     if (Ce > L) Ce = L;  // one chunk
-    // FAVOR+ maps q and k in a separate pass; elu+1 is applied while loading;
-    // the identity map with a scale s runs unscaled and scales the results
-    // (outputs by s^2 unless normalised, the final state by s), which is exact.
-    P.premap = f == LA_FMAP_FAVOR;
+    // FAVOR+ maps q and k in a separate pass; elu+1 too where the streaming
+    // kernel runs, else it is applied while loading; the identity map with a
+    // scale s runs unscaled and scales the results (outputs by s^2 unless
+    // normalised, the final state by s), which is exact.
     P.DVT = kernel_dvt(d_v);
     P.n_dvt = (int)(d_v / P.DVT);
     if (P.i8) {
@@ -138,11 +138,14 @@ la_status make_plan(Plan& P, la_dtype in_dt, int64_t BH, int64_t L, int64_t d_in
         P.DK = kernel_dk_bf16(P.dk);
     }
 
-    // The streaming kernel covers chunks of 32, 64 or 128 rows with the
-    // identity map, no normaliser and feature widths of 64 or 128; it fills
-    // the LDS and runs one workgroup per CU.
-    P.pipe = !P.i8 && P.causal && (Ce == 32 || Ce == 64 || Ce == 128) && !P.normalize &&
-             f == LA_FMAP_IDENTITY && (P.dk == 64 || P.dk == 128) && d_v % 64 == 0;
+    // The streaming kernel covers chunks of 32, 64 or 128 rows, with or
+    // without the normaliser: the identity map at feature widths 64 and 128,
+    // elu+1 at width 64 (mapped beforehand, with the bf16 residual of phi(k),
+    // whose tile fits the LDS next to three stages at that width only).  It
+    // fills the LDS and runs one workgroup per CU.
+    P.pipe = !P.i8 && P.causal && (Ce == 32 || Ce == 64 || Ce == 128) && d_v % 64 == 0 &&
+             ((f == LA_FMAP_IDENTITY && (P.dk == 64 || P.dk == 128)) || (f == LA_FMAP_ELU1 && P.dk == 64));
+    P.premap = f == LA_FMAP_FAVOR || (P.pipe && f == LA_FMAP_ELU1);
     if (P.pipe) {
         P.DK = (int)P.dk;
         P.DVT = 64;
@@ -197,8 +200,8 @@ la_status make_plan(Plan& P, la_dtype in_dt, int64_t BH, int64_t L, int64_t d_in
     P.ws_states = align256((size_t)BH * n_state_slots * P.dk * d_v * st_elem);
     P.ws_z = (P.normalize && n_state_slots) ? align256((size_t)BH * n_state_slots * P.dk * st_elem) : 0;
     if (n_state_slots == 0) P.ws_states = 0;
-    // FAVOR+: phi(q), phi(k) and the bf16 residual of phi(k) (the state sums
-    // use hi + lo, so the bf16 rounding of phi does not accumulate over L)
+    // pre-mapped: phi(q), phi(k) and the bf16 residual of phi(k) (the state
+    // sums use hi + lo, so the bf16 rounding of phi does not accumulate over L)
     P.ws_total = 3 * P.ws_phi + P.ws_states + P.ws_z;
     return LA_OK;
 }
@@ -267,7 +270,7 @@ static la_status launch_phase3(const Plan& P, const void* qm, const void* km, co
     if (P.pipe) {
         // fp32 outputs: the general kernel on the same groups
         DVT = kernel_dvt(d_v);
-        T = tile_bf16(P.C, P.DK, DVT, false);
+        T = tile_bf16(P.C, P.DK, DVT, klo != nullptr);
         p.n_dvt = (int)(d_v / DVT);
         grid_g = BH * P.n_groups * p.n_dvt;
         p.xcd_remap = xcd_ok(grid_g);
@@ -480,8 +483,8 @@ la_status la_chunked_forward(const void* q, const void* k, const void* v, la_dty
         fp.y_lo = static_cast<unsigned short*>(kl);
         fp.rows = BH * L;
         fp.d_in = (int)d_in;
-        fp.m = (int)m;
-        fp.fmap = 2;
+        fp.m = f == LA_FMAP_FAVOR ? (int)m : (int)d_in;
+        fp.fmap = f == LA_FMAP_FAVOR ? 2 : 1;
         fp.in_scale = in_scale;
         a = hip_status(la::run_feature_map(fp, s), "feature map launch");
         if (a != LA_OK) return a;

@@ -2,7 +2,8 @@
 // Performerの理論と実装": the ELU feature map and FAVOR+ positive random
 // features).
 //
-//  * identity and elu+1 are elementwise (8 bf16 per thread, fp32 math).
+//  * identity and elu+1 are elementwise (8 bf16 per thread, fp32 math); with a
+//    bf16 output they can also write the bf16 residual y - bf16(y).
 //  * FAVOR+ is a small GEMM x W^T (k = d_in) on bf16 matrix cores with an
 //    fp32 epilogue exp(proj - |x|^2 / 2) / sqrt(m).  W stays in LDS for the
 //    life of the workgroup, which walks row tiles of 64.
@@ -32,8 +33,19 @@ __global__ __launch_bounds__(256) void fmap_elementwise(FmapParams p) {
             y[0] = make_float4(f[0], f[1], f[2], f[3]);
             y[1] = make_float4(f[4], f[5], f[6], f[7]);
         } else {
-            reinterpret_cast<uint4*>(p.y)[u] = make_uint4(pack2_bf16(f[0], f[1]), pack2_bf16(f[2], f[3]),
-                                                          pack2_bf16(f[4], f[5]), pack2_bf16(f[6], f[7]));
+            uint32_t hb[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) hb[j] = pack2_bf16(f[2 * j], f[2 * j + 1]);
+            reinterpret_cast<uint4*>(p.y)[u] = make_uint4(hb[0], hb[1], hb[2], hb[3]);
+            if (p.y_lo != nullptr) {
+                // residual y - bf16(y), so that hi + lo carries y to about 2^-17
+                uint32_t lb[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    lb[j] = pack2_bf16(f[2 * j] - __uint_as_float(hb[j] << 16),
+                                       f[2 * j + 1] - __uint_as_float(hb[j] & 0xFFFF0000u));
+                reinterpret_cast<uint4*>(p.y_lo)[u] = make_uint4(lb[0], lb[1], lb[2], lb[3]);
+            }
         }
     }
 }

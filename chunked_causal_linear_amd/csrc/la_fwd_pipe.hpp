@@ -1,5 +1,6 @@
 // Chunked causal linear attention, fused phase 3, streaming kernel (gfx950)
-// for chunks of 32, 64 or 128 rows, bf16 in and out, no normaliser.
+// for chunks of 32, 64 or 128 rows, bf16 in and out, with or without the
+// normaliser, with or without the bf16 residual of pre-mapped phi(k).
 //
 // Same mathematics as chunked_fwd_bf16 (page "attention と線形の間",
 // section ②: O_c = Q_c P + tril(Q_c K_c^T) V_c with the diagonal kept, then
@@ -51,6 +52,15 @@
 // product's operand in natural order.  Outputs come out transposed
 // (O^T = P^T Q^T + V^T tril(S)^T): a lane holds four consecutive columns of one
 // row.
+//
+// Normaliser (page "Linear Attention / Performerの理論と実装", RNN view: the
+// denominator phi(q) . sum phi(k) next to the numerator): one more 16-column
+// block whose V operand is all ones.  Its state block is z in every column
+// (z += K^T 1), its inter product is Q z and its intra product the row sums of
+// the masked scores, so every lane ends up holding the denominator of its row
+// next to the four numerators it divides.  With the residual of pre-mapped
+// phi(k) (SPLIT), the state and z updates add K_lo^T V and K_lo^T 1, which keeps
+// long state sums free of the bf16 rounding of phi(k); scores use bf16 phi(k).
 #pragma once
 
 #include <type_traits>
@@ -69,11 +79,18 @@ __device__ __forceinline__ int tile_off(int r, int e) {
     return r * NSEG * 16 + ((((e >> 3) ^ r) & (NSEG - 1)) << 4) + ((e & 7) << 1);
 }
 
-template <int DK, int DVT, int TT>
+template <int DK, int DVT, int TT, bool SPLIT>
 struct alignas(16) Stage {
     u16 q[TT * DK];
     u16 k[TT * DK];
     u16 v[TT * DVT];
+};
+template <int DK, int DVT, int TT>
+struct alignas(16) Stage<DK, DVT, TT, true> {
+    u16 q[TT * DK];
+    u16 k[TT * DK];
+    u16 v[TT * DVT];
+    u16 klo[TT * DK];  // residual of pre-mapped phi(k)
 };
 
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
@@ -147,25 +164,26 @@ using ic = std::integral_constant<int, I>;
 
 }  // namespace pipe
 
-template <int DK, int DVT, int CH, bool SCALED>
+template <int DK, int DVT, int CH, bool SCALED, bool NORM, bool SPLIT>
 __global__ __launch_bounds__(4 * WAVE) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void chunked_fwd_pipe(FwdParams p) {
     using namespace pipe;
     constexpr int TT = CH > 64 ? CH : 64;          // rows per tile
     constexpr int NSTAGE = TT == 128 ? 2 : 3;      // LDS stages
     constexpr int CPW = DVT / 32;                  // 16-column blocks per pair
+    constexpr int NCB = CPW + (NORM ? 1 : 0);      // + the denominator block
     constexpr int NKA = DK / 32;                   // k-steps over the feature index
     constexpr int QSEG = DK / 8, VSEG = DVT / 8;
     constexpr int NCQ = TT * QSEG / WAVE / 2;      // copy instructions per tile and copy wave, Q (and K)
     constexpr int NCV = TT * VSEG / WAVE / 2;      // the same for V (and for the output stores)
-    constexpr int NL = 2 * NCQ + NCV;
+    constexpr int NL = (SPLIT ? 3 : 2) * NCQ + NCV;
     constexpr int RPV = WAVE / VSEG;               // output rows per store instruction
     static_assert(DVT == 64, "tile of 64 value columns");
     static_assert(CH == 32 || CH == 64 || CH == 128, "chunks of 32, 64 or 128 rows");
     static_assert(DK == 64 || DK == 128, "feature width 64 or 128");
     static_assert(NL < 64, "vmcnt range");
-    static_assert(NSTAGE * (int)sizeof(Stage<DK, DVT, TT>) <= 160 * 1024, "LDS");
-    typedef Stage<DK, DVT, TT> StageT;
+    static_assert(NSTAGE * (int)sizeof(Stage<DK, DVT, TT, SPLIT>) <= 160 * 1024, "LDS");
+    typedef Stage<DK, DVT, TT, SPLIT> StageT;
 
     __shared__ StageT st[NSTAGE];
 
@@ -202,6 +220,10 @@ void chunked_fwd_pipe(FwdParams p) {
         const int n = (TT - valid) * QSEG;
         uint4* kk = reinterpret_cast<uint4*>(s.k + valid * DK);
         for (int i = tid; i < n; i += 4 * WAVE) kk[i] = make_uint4(0, 0, 0, 0);
+        if constexpr (SPLIT) {
+            uint4* kl = reinterpret_cast<uint4*>(s.klo + valid * DK);
+            for (int i = tid; i < n; i += 4 * WAVE) kl[i] = make_uint4(0, 0, 0, 0);
+        }
     };
 
     if (copier) {
@@ -209,6 +231,7 @@ void chunked_fwd_pipe(FwdParams p) {
         const u16* qh = p.q + bh * L * DK;
         const u16* kh = p.k + bh * L * DK;
         const u16* vh = p.v + bh * L * dv + col0;
+        const u16* klh = SPLIT ? p.k_lo + bh * L * DK : nullptr;
         // Lane l of copy instruction b lands in LDS slot 64b + l = (row,
         // physical segment) = (slot / NSEG, slot % NSEG), which holds the
         // global segment (physical ^ row) of that row.
@@ -218,6 +241,7 @@ void chunked_fwd_pipe(FwdParams p) {
             const u16* qb_ = qh + r0 * DK;
             const u16* kb_ = kh + r0 * DK;
             const u16* vb_ = vh + r0 * dv;
+            const u16* klb_ = SPLIT ? klh + r0 * DK : nullptr;
             const uint32_t lq = lds_addr(s.q), lk = lds_addr(s.k), lv = lds_addr(s.v);
 #pragma unroll
             for (int i = 0; i < NCQ; ++i) {
@@ -227,6 +251,7 @@ void chunked_fwd_pipe(FwdParams p) {
                 const uint32_t off = (uint32_t)(((r < last ? r : last) * DK + seg * 8) * 2);
                 dma16(qb_, off, lq + b * WAVE * 16);
                 dma16(kb_, off, lk + b * WAVE * 16);
+                if constexpr (SPLIT) dma16(klb_, off, lds_addr(s.klo) + b * WAVE * 16);
             }
 #pragma unroll
             for (int i = 0; i < NCV; ++i) {
@@ -307,10 +332,11 @@ void chunked_fwd_pipe(FwdParams p) {
     }
 
     // ================= compute wave h =================
-    // state P: P[c][ks][hf] lane (l16, g) element i = P[a = 32ks + 8g + 4hf + i][j = colw + 16c + l16]
-    f32x4 P[CPW][NKA][2];
+    // state P: P[c][ks][hf] lane (l16, g) element i = P[a = 32ks + 8g + 4hf + i][j = colw + 16c + l16];
+    // with the normaliser, block c = CPW holds z[a] in every column
+    f32x4 P[NCB][NKA][2];
 #pragma unroll
-    for (int c = 0; c < CPW; ++c)
+    for (int c = 0; c < NCB; ++c)
 #pragma unroll
         for (int ks = 0; ks < NKA; ++ks) P[c][ks][0] = P[c][ks][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (p.P0 != nullptr && grp > 0) {
@@ -324,7 +350,18 @@ void chunked_fwd_pipe(FwdParams p) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         P[c][ks][hf][i] = P0[(int64_t)(32 * ks + 8 * g + 4 * hf + i) * dv + c * 16];
+        if constexpr (NORM) {
+            const float* z0 = p.z0 + (bh * p.n_groups + grp) * DK;
+#pragma unroll
+            for (int ks = 0; ks < NKA; ++ks)
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) P[CPW][ks][hf][i] = z0[32 * ks + 8 * g + 4 * hf + i];
+        }
     }
+    // V operand of the denominator block: all ones (bf16 1.0)
+    const bf16x8 ones = as_bf16x8(make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
     const float osc = p.out_scale;
     const int c4 = 4 * (lane & 3), c8 = 8 * (lane & 3);
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
@@ -335,7 +372,7 @@ void chunked_fwd_pipe(FwdParams p) {
     // inter product with the packed state for the query blocks in INTER (a bit
     // mask); feature steps one at a time, the next step's operands loaded ahead.
     auto tri_window = [&](const StageT& s, auto q0c, auto k0c, auto halvesc, auto interc, f32x4 (&S)[10],
-                          f32x4 (&O)[CPW][4], const bf16x8 (&pst)[CPW][NKA]) __attribute__((always_inline)) {
+                          f32x4 (&O)[NCB][4], const bf16x8 (&pst)[NCB][NKA]) __attribute__((always_inline)) {
         constexpr int Q0 = decltype(q0c)::value, K0 = decltype(k0c)::value;
         constexpr bool HALVES = decltype(halvesc)::value != 0;
         constexpr int INTER = decltype(interc)::value;
@@ -362,7 +399,7 @@ void chunked_fwd_pipe(FwdParams p) {
                         S[qb * (qb + 1) / 2 + kb] =
                             mfma_bf16(ka[ks & 1][kb], qa[ks & 1][qb], S[qb * (qb + 1) / 2 + kb]);
 #pragma unroll
-            for (int c = 0; c < CPW; ++c)
+            for (int c = 0; c < NCB; ++c)
 #pragma unroll
                 for (int qb = 0; qb < 4; ++qb)
                     if ((INTER >> qb) & 1) O[c][qb] = mfma_bf16(pst[c][ks], qa[ks & 1][qb], O[c][qb]);
@@ -376,14 +413,15 @@ void chunked_fwd_pipe(FwdParams p) {
 
     // intra product of a window: query blocks qb < 4 of O against the key steps
     // kk <= qb / 2 of its own 64 keys (V key rows 32 * (KK0 + kk))
-    auto tri_intra = [&](const StageT& s, auto kk0c, const f32x4 (&S)[10], f32x4 (&O)[CPW][4])
+    auto tri_intra = [&](const StageT& s, auto kk0c, const f32x4 (&S)[10], f32x4 (&O)[NCB][4])
         __attribute__((always_inline)) {
         constexpr int KK0 = decltype(kk0c)::value;
-        bf16x8 vb[CPW][2];
+        bf16x8 vb[NCB][2];
 #pragma unroll
-        for (int c = 0; c < CPW; ++c)
+        for (int c = 0; c < NCB; ++c)
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) vb[c][kk] = col_op<VSEG>(s.v, (KK0 + kk) * 32, colw + c * 16 + c4, lane);
+            for (int kk = 0; kk < 2; ++kk)
+                vb[c][kk] = c < CPW ? col_op<VSEG>(s.v, (KK0 + kk) * 32, colw + c * 16 + c4, lane) : ones;
 #pragma unroll
         for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
@@ -391,7 +429,7 @@ void chunked_fwd_pipe(FwdParams p) {
                 const f32x4 s1 = 2 * kk + 1 <= qb ? S[qb * (qb + 1) / 2 + 2 * kk + 1] : zero4;
                 const bf16x8 sb = pack_acc_bf16(S[qb * (qb + 1) / 2 + 2 * kk], s1);
 #pragma unroll
-                for (int c = 0; c < CPW; ++c) O[c][qb] = mfma_bf16(vb[c][kk], sb, O[c][qb]);
+                for (int c = 0; c < NCB; ++c) O[c][qb] = mfma_bf16(vb[c][kk], sb, O[c][qb]);
             }
     };
 
@@ -399,40 +437,46 @@ void chunked_fwd_pipe(FwdParams p) {
     // operands one (ks, hf) step ahead
     auto update = [&](const StageT& s, auto kk0c, auto nkc) __attribute__((always_inline)) {
         constexpr int KK0 = decltype(kk0c)::value, NK = decltype(nkc)::value;
-        bf16x8 vb[CPW][NK];
+        constexpr int NSRC = SPLIT ? 2 : 1;  // phi(k), and its residual
+        bf16x8 vb[NCB][NK];
 #pragma unroll
-        for (int c = 0; c < CPW; ++c)
+        for (int c = 0; c < NCB; ++c)
 #pragma unroll
-            for (int kk = 0; kk < NK; ++kk) vb[c][kk] = col_op<VSEG>(s.v, (KK0 + kk) * 32, colw + c * 16 + c4, lane);
-        bf16x8 kc[2][NK];
+            for (int kk = 0; kk < NK; ++kk)
+                vb[c][kk] = c < CPW ? col_op<VSEG>(s.v, (KK0 + kk) * 32, colw + c * 16 + c4, lane) : ones;
+        bf16x8 kc[2][NSRC][NK];
+        auto load_kc = [&](int ks, int hf, bf16x8 (&k_)[NSRC][NK]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int kk = 0; kk < NK; ++kk) kc[0][kk] = col_op<QSEG>(s.k, (KK0 + kk) * 32, c8, lane);
+            for (int kk = 0; kk < NK; ++kk) {
+                k_[0][kk] = col_op<QSEG>(s.k, (KK0 + kk) * 32, ks * 32 + c8 + 4 * hf, lane);
+                if constexpr (SPLIT) k_[NSRC - 1][kk] = col_op<QSEG>(s.klo, (KK0 + kk) * 32, ks * 32 + c8 + 4 * hf, lane);
+            }
+        };
+        load_kc(0, 0, kc[0]);
 #pragma unroll
         for (int t = 0; t < 2 * NKA; ++t) {
             const int ks = t >> 1, hf = t & 1;
-            if (t + 1 < 2 * NKA) {
-                const int ks1 = (t + 1) >> 1, hf1 = (t + 1) & 1;
-#pragma unroll
-                for (int kk = 0; kk < NK; ++kk)
-                    kc[(t + 1) & 1][kk] = col_op<QSEG>(s.k, (KK0 + kk) * 32, ks1 * 32 + c8 + 4 * hf1, lane);
-            }
+            if (t + 1 < 2 * NKA) load_kc((t + 1) >> 1, (t + 1) & 1, kc[(t + 1) & 1]);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int kk = 0; kk < NK; ++kk)
+            for (int src = 0; src < NSRC; ++src)
 #pragma unroll
-                for (int c = 0; c < CPW; ++c) P[c][ks][hf] = mfma_bf16(kc[t & 1][kk], vb[c][kk], P[c][ks][hf]);
+                for (int kk = 0; kk < NK; ++kk)
+#pragma unroll
+                    for (int c = 0; c < NCB; ++c)
+                        P[c][ks][hf] = mfma_bf16(kc[t & 1][src][kk], vb[c][kk], P[c][ks][hf]);
         }
     };
 
-    auto pack_state = [&](bf16x8 (&pst)[CPW][NKA]) __attribute__((always_inline)) {
+    auto pack_state = [&](bf16x8 (&pst)[NCB][NKA]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int c = 0; c < CPW; ++c)
+        for (int c = 0; c < NCB; ++c)
 #pragma unroll
             for (int ks = 0; ks < NKA; ++ks) pst[c][ks] = pack_acc_bf16(P[c][ks][0], P[c][ks][1]);
     };
 
     // inter product of query blocks Q0 + b, b in [B0, B0 + 2), reading Q again
-    auto inter2 = [&](const StageT& s, auto q0c, auto b0c, f32x4 (&O)[CPW][4], const bf16x8 (&pst)[CPW][NKA])
+    auto inter2 = [&](const StageT& s, auto q0c, auto b0c, f32x4 (&O)[NCB][4], const bf16x8 (&pst)[NCB][NKA])
         __attribute__((always_inline)) {
         constexpr int Q0 = decltype(q0c)::value, B0 = decltype(b0c)::value;
         bf16x8 qa[NKA][2];
@@ -443,20 +487,25 @@ void chunked_fwd_pipe(FwdParams p) {
 #pragma unroll
         for (int ks = 0; ks < NKA; ++ks)
 #pragma unroll
-            for (int c = 0; c < CPW; ++c)
+            for (int c = 0; c < NCB; ++c)
 #pragma unroll
                 for (int b = 0; b < 2; ++b) O[c][B0 + b] = mfma_bf16(pst[c][ks], qa[ks][b], O[c][B0 + b]);
     };
 
     // output rows of query blocks Q0 + qb into this wave's V columns (after its
     // last V read of the tile, in program order)
-    auto write_out = [&](StageT& s, auto q0c, f32x4 (&O)[CPW][4]) __attribute__((always_inline)) {
+    auto write_out = [&](StageT& s, auto q0c, f32x4 (&O)[NCB][4]) __attribute__((always_inline)) {
         constexpr int Q0 = decltype(q0c)::value;
 #pragma unroll
         for (int c = 0; c < CPW; ++c)
 #pragma unroll
             for (int qb = 0; qb < 4; ++qb) {
                 f32x4 o = O[c][qb];
+                if constexpr (NORM) {
+                    // the denominator block holds the row's denominator in every column
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) o[i] = o[i] / O[CPW][qb][i];
+                }
                 if (SCALED) o *= osc;
                 *reinterpret_cast<uint2*>(reinterpret_cast<char*>(s.v) +
                                           tile_off<VSEG>((Q0 + qb) * 16 + l16, colw + c * 16 + 4 * g)) =
@@ -464,19 +513,19 @@ void chunked_fwd_pipe(FwdParams p) {
             }
     };
 
-    auto zero_o = [&](f32x4 (&O)[CPW][4]) __attribute__((always_inline)) {
+    auto zero_o = [&](f32x4 (&O)[NCB][4]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int c = 0; c < CPW; ++c)
+        for (int c = 0; c < NCB; ++c)
 #pragma unroll
             for (int qb = 0; qb < 4; ++qb) O[c][qb] = zero4;
     };
 
     // ---- one tile's products
     auto compute = [&](StageT& s) __attribute__((always_inline)) {
-        bf16x8 pst[CPW][NKA];
+        bf16x8 pst[NCB][NKA];
         pack_state(pst);
         if constexpr (CH == 64) {
-            f32x4 S[10], O[CPW][4];
+            f32x4 S[10], O[NCB][4];
             zero_o(O);
             tri_window(s, ic<0>{}, ic<0>{}, ic<0>{}, ic<15>{}, S, O, pst);
             tri_intra(s, ic<0>{}, S, O);
@@ -486,18 +535,19 @@ void chunked_fwd_pipe(FwdParams p) {
             // two chunks per tile: rows 0..31 (A) and 32..63 (B).  Scores only
             // inside each chunk; A's inter product reads the state before A,
             // B's the state after A's update.
-            f32x4 S[10], O[CPW][4];
+            f32x4 S[10], O[NCB][4];
             zero_o(O);
             tri_window(s, ic<0>{}, ic<0>{}, ic<1>{}, ic<3>{}, S, O, pst);
             update(s, ic<0>{}, ic<1>{});  // A's keys (key step 0)
             pack_state(pst);
             inter2(s, ic<0>{}, ic<2>{}, O, pst);
             update(s, ic<1>{}, ic<1>{});  // B's keys (key step 1)
-            bf16x8 vb[CPW][2];
+            bf16x8 vb[NCB][2];
 #pragma unroll
-            for (int c = 0; c < CPW; ++c)
+            for (int c = 0; c < NCB; ++c)
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk) vb[c][kk] = col_op<VSEG>(s.v, kk * 32, colw + c * 16 + c4, lane);
+                for (int kk = 0; kk < 2; ++kk)
+                    vb[c][kk] = c < CPW ? col_op<VSEG>(s.v, kk * 32, colw + c * 16 + c4, lane) : ones;
             // intra inside each chunk: query block 0 (key block 0), 1 (key blocks
             // 0, 1), 2 (key block 2), 3 (key blocks 2, 3); diagonals masked
             const bf16x8 s0 = pack_acc_bf16(S[0], zero4);
@@ -505,7 +555,7 @@ void chunked_fwd_pipe(FwdParams p) {
             const bf16x8 s2 = pack_acc_bf16(S[5], zero4);
             const bf16x8 s3 = pack_acc_bf16(S[8], S[9]);
 #pragma unroll
-            for (int c = 0; c < CPW; ++c) {
+            for (int c = 0; c < NCB; ++c) {
                 O[c][0] = mfma_bf16(vb[c][0], s0, O[c][0]);
                 O[c][1] = mfma_bf16(vb[c][0], s1, O[c][1]);
                 O[c][2] = mfma_bf16(vb[c][1], s2, O[c][2]);
@@ -516,7 +566,7 @@ void chunked_fwd_pipe(FwdParams p) {
             // one chunk of 128 rows per tile: query rows 0..63 against their own
             // keys; query rows 64..127 against their own keys and the full block
             // of keys 0..63; then the update with all 128 keys.
-            f32x4 Oa[CPW][4], Ob[CPW][4];
+            f32x4 Oa[NCB][4], Ob[NCB][4];
             zero_o(Oa);
             zero_o(Ob);
             {
@@ -552,14 +602,14 @@ void chunked_fwd_pipe(FwdParams p) {
 #pragma unroll
                         for (int b = 0; b < 2; ++b) X[qb][b] = mfma_bf16(ka[ks & 1][b], qa[ks & 1][qb], X[qb][b]);
                 }
-                bf16x8 vb[CPW];
+                bf16x8 vb[NCB];
 #pragma unroll
-                for (int c = 0; c < CPW; ++c) vb[c] = col_op<VSEG>(s.v, kk * 32, colw + c * 16 + c4, lane);
+                for (int c = 0; c < NCB; ++c) vb[c] = c < CPW ? col_op<VSEG>(s.v, kk * 32, colw + c * 16 + c4, lane) : ones;
 #pragma unroll
                 for (int qb = 0; qb < 4; ++qb) {
                     const bf16x8 xb = pack_acc_bf16(X[qb][0], X[qb][1]);
 #pragma unroll
-                    for (int c = 0; c < CPW; ++c) Ob[c][qb] = mfma_bf16(vb[c], xb, Ob[c][qb]);
+                    for (int c = 0; c < NCB; ++c) Ob[c][qb] = mfma_bf16(vb[c], xb, Ob[c][qb]);
                 }
             }
             update(s, ic<0>{}, ic<4>{});
@@ -598,15 +648,34 @@ void chunked_fwd_pipe(FwdParams p) {
                     for (int i = 0; i < 4; ++i)
                         Sf[(int64_t)(32 * ks + 8 * g + 4 * hf + i) * dv + c * 16] = P[c][ks][hf][i] * ss;
     }
+    if constexpr (NORM) {
+        if (t_end == n_tiles && p.z_final != nullptr && jt == 0 && h == 0 && l16 == 0) {
+            float* zf = p.z_final + bh * DK;
+            const float ss = p.state_scale;
+#pragma unroll
+            for (int ks = 0; ks < NKA; ++ks)
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) zf[32 * ks + 8 * g + 4 * hf + i] = P[CPW][ks][hf][i] * ss;
+        }
+    }
 }
 
-template <int DK, int DVT, int CH>
+// Output scaling exists for the scaled identity map without the normaliser
+// only (normalised outputs are scale-free; pre-mapped inputs carry the scale).
+template <int DK, int DVT, int CH, bool NORM, bool SPLIT>
 hipError_t launch_fwd_pipe(const FwdParams& p, int64_t grid, hipStream_t s) {
     const dim3 block(4 * WAVE);
-    if (p.out_scale != 1.0f)
-        hipLaunchKernelGGL((chunked_fwd_pipe<DK, DVT, CH, true>), dim3((unsigned)grid), block, 0, s, p);
-    else
-        hipLaunchKernelGGL((chunked_fwd_pipe<DK, DVT, CH, false>), dim3((unsigned)grid), block, 0, s, p);
+    if (p.out_scale != 1.0f) {
+        if constexpr (NORM || SPLIT) {
+            return hipErrorInvalidValue;
+        } else {
+            hipLaunchKernelGGL((chunked_fwd_pipe<DK, DVT, CH, true, false, false>), dim3((unsigned)grid), block, 0, s, p);
+        }
+    } else {
+        hipLaunchKernelGGL((chunked_fwd_pipe<DK, DVT, CH, false, NORM, SPLIT>), dim3((unsigned)grid), block, 0, s, p);
+    }
     return hipGetLastError();
 }
 

@@ -3,15 +3,35 @@
 
 namespace la {
 
+namespace {
+
+// normaliser from p.normalize; the residual of pre-mapped phi(k) from p.k_lo
+// (feature width 64 only: three LDS stages with the residual tile fit there)
+template <int DK, int C>
+hipError_t by_flags(const FwdParams& p, int64_t grid, hipStream_t s) {
+    const bool norm = p.normalize != 0;
+    if (p.k_lo != nullptr) {
+        if constexpr (DK == 64)
+            return norm ? launch_fwd_pipe<64, 64, C, true, true>(p, grid, s)
+                        : launch_fwd_pipe<64, 64, C, false, true>(p, grid, s);
+        else
+            return hipErrorInvalidValue;
+    }
+    return norm ? launch_fwd_pipe<DK, 64, C, true, false>(p, grid, s)
+                : launch_fwd_pipe<DK, 64, C, false, false>(p, grid, s);
+}
+
+}  // namespace
+
 hipError_t fwd_pipe_bf16(const FwdParams& p, int DK, int DVT, int C, int64_t grid, hipStream_t s) {
-    if (DVT != 64) return hipErrorInvalidValue;
+    if (DVT != 64 || p.noncausal || p.fmap != FMAP_NONE || p.out_f32) return hipErrorInvalidValue;
     switch (DK * 1000 + C) {
-        case 128032: return launch_fwd_pipe<128, 64, 32>(p, grid, s);
-        case 128064: return launch_fwd_pipe<128, 64, 64>(p, grid, s);
-        case 128128: return launch_fwd_pipe<128, 64, 128>(p, grid, s);
-        case 64032: return launch_fwd_pipe<64, 64, 32>(p, grid, s);
-        case 64064: return launch_fwd_pipe<64, 64, 64>(p, grid, s);
-        case 64128: return launch_fwd_pipe<64, 64, 128>(p, grid, s);
+        case 128032: return by_flags<128, 32>(p, grid, s);
+        case 128064: return by_flags<128, 64>(p, grid, s);
+        case 128128: return by_flags<128, 128>(p, grid, s);
+        case 64032: return by_flags<64, 32>(p, grid, s);
+        case 64064: return by_flags<64, 64>(p, grid, s);
+        case 64128: return by_flags<64, 128>(p, grid, s);
     }
     return hipErrorInvalidValue;
 }

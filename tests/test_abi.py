@@ -92,9 +92,16 @@ def test_workspace_sizes_and_errors():
     # chunks of 32 keep an even number per group on the streaming kernel
     assert lib.la_chunked_forward_group(b.LA_BF16, 2, 8192, 128, 128, 32, 1, 0, 0, 0, 0) % 2 == 0
     # groups: BH * n_groups * (dk*dv + dk) floats (normalised), 256-byte aligned pieces
-    n = ws(b.LA_BF16, 2, 1024, 64, 64, 64, 1, 1, 1, 0, 1.0, 4)
+    n = ws(b.LA_BF16, 2, 1024, 64, 64, 64, 1, 1, 0, 0, 1.0, 4)
     groups = 1024 // 64 // 4
     assert n == 2 * groups * 64 * 64 * 4 + 2 * groups * 64 * 4
+    # elu+1 at d_k = 64 on the streaming kernel: mapped beforehand, three
+    # copies (phi(q), phi(k), phi(k)'s residual) of BH*L*d_k bf16 in front
+    n = ws(b.LA_BF16, 2, 1024, 64, 64, 64, 1, 1, 1, 0, 1.0, 4)
+    assert n == 3 * 2 * 1024 * 64 * 2 + 2 * groups * 64 * 64 * 4 + 2 * groups * 64 * 4
+    # elu+1 at d_k = 128 (general kernel, map applied while loading): no copies
+    n = ws(b.LA_BF16, 2, 1024, 128, 64, 64, 1, 1, 1, 0, 1.0, 4)
+    assert n == 2 * groups * 128 * 64 * 4 + 2 * groups * 128 * 4
     # FAVOR+: three mapped copies (q, k and k's residual) of BH*L*m bf16
     n = ws(b.LA_BF16, 24, 16384, 64, 64, 64, 1, 1, 2, 256, 1.0, 0)
     per = 24 * 16384 * 256 * 2

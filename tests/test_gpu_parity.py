@@ -138,6 +138,34 @@ def test_bf16_chunk32_128_streaming(C, dk, dv, L, group):
     assert_close(host(S), refS, what="S")
 
 
+def _positive(t):
+    """The same tensor with every sign cleared (bf16 |x| is exact)."""
+    return wl.Tensor(bits=t.bits & np.uint16(0x7FFF), exact=np.abs(t.exact), dtype=t.dtype)
+
+
+@pytest.mark.parametrize("C,dk,dv,L,group,fmap,scale", [
+    (64, 64, 64, 700, 0, "elu1", 1.0), (64, 64, 128, 1000, 3, "elu1", 1.0), (32, 64, 64, 530, 2, "elu1", 1.0),
+    (32, 64, 128, 75, 0, "elu1", 1.0), (128, 64, 64, 1300, 0, "elu1", 1.0), (128, 64, 128, 900, 3, "elu1", 1.0),
+    (64, 128, 128, 700, 2, "identity", 1.0), (128, 128, 64, 600, 0, "identity", 1.0),
+    (32, 128, 64, 300, 0, "identity", 1.0), (64, 64, 64, 64, 0, "identity", 0.5),
+    (128, 64, 128, 257, 2, "identity", 1.0)])
+def test_bf16_streaming_normalized(C, dk, dv, L, group, fmap, scale):
+    """Normalised forwards on the streaming kernel: elu+1 at d_k = 64 (mapped
+    beforehand, with phi(k)'s residual in the state sums) and the identity map
+    on non-negative features (the denominator stays away from zero), at chunks
+    of 32, 64 and 128, with groups, ragged tails and a folded input scale."""
+    q, k, v = _case(17, 2, L, dk, dv, "bf16")
+    if fmap == "identity":
+        q, k = _positive(q), _positive(k)
+    log(f"bf16 streaming norm C={C} dk={dk} dv={dv} L={L} group={group} fmap={fmap} in_scale={scale}")
+    o, S, z = la.chunked_forward(dev_input(q), dev_input(k), dev_input(v), C, normalize=True, fmap=fmap,
+                                 in_scale=scale, return_state=True, group=group)
+    ref, refS, refz = _oracle_forward(q.exact, k.exact, v.exact, C, True, True, fmap, None, scale)
+    assert_close(host(o), ref, what="o")
+    assert_close(host(S), refS, what="S")
+    assert_close(host(z), refz, what="z")
+
+
 @pytest.mark.parametrize("group", [1, 2, 3, 5, 100])
 def test_bf16_groups(group):
     q, k, v = _case(11, 2, 640, 64, 64, "bf16")
@@ -336,10 +364,11 @@ def test_three_phase_composition(dtype, C, group):
         assert_close(host(Sf3), refS, what="S")
 
 
-def test_three_phase_normalized():
+@pytest.mark.parametrize("dv", [32, 64])
+def test_three_phase_normalized(dv):
     torch = torch_cuda()
-    q, k, v = _case(41, 2, 333, 64, 32, "bf16")
-    log("three phases, elu+1 mapped first, normalised")
+    q, k, v = _case(41, 2, 333, 64, dv, "bf16")
+    log(f"three phases, elu+1 mapped first, normalised, dv={dv}")
     qm = la.feature_map(dev_input(q), "elu1")
     km = la.feature_map(dev_input(k), "elu1")
     S, z = la.chunk_states(km, dev_input(v), 64 * 2, want_z=True)
