@@ -80,6 +80,7 @@ struct Plan {
     bool premap;  // phi computed by a separate pass into the workspace
     bool pipe;    // streaming phase-3 kernel (chunks of 32, 64 or 128 rows; identity map, or elu+1 pre-mapped)
     bool causal, normalize;
+    int64_t sub;       // phase-1 states per group (finer grain than the groups when they are few and long)
     size_t ws_phi;     // bytes of one mapped q or k copy
     size_t ws_states;  // bytes of the group states
     size_t ws_z;
@@ -194,9 +195,21 @@ la_status make_plan(Plan& P, la_dtype in_dt, int64_t BH, int64_t L, int64_t d_in
     const int64_t grid = BH * P.n_groups * P.n_dvt;
     if (grid > 0x7FFFFFFFLL) return fail(LA_ERR_UNSUPPORTED, "grid too large");
 
+    // Phase 1 sums each group's rows; a few long groups would leave most CUs
+    // idle, so each group's sum is split into `sub` pieces of >= 1024 rows
+    // until about 1024 workgroups run; the scan then walks the pieces and
+    // group g starts from the prefix at piece g * sub.
+    P.sub = 1;
+    if (P.causal && P.n_groups > 1) {
+        const int64_t n_dvt1 = d_v / kernel_dvt(d_v);
+        while (P.G % (2 * P.sub) == 0 && P.G * P.C / (2 * P.sub) >= 1024 &&
+               BH * (P.n_groups - 1) * P.sub * n_dvt1 < 1024)
+            P.sub *= 2;
+    }
+
     const size_t st_elem = 4;
     P.ws_phi = P.premap ? align256((size_t)BH * L * P.dk * 2) : 0;
-    const int64_t n_state_slots = P.causal ? (P.n_groups > 1 ? P.n_groups : 0) : 1;
+    const int64_t n_state_slots = P.causal ? (P.n_groups > 1 ? P.n_groups * P.sub : 0) : 1;
     P.ws_states = align256((size_t)BH * n_state_slots * P.dk * d_v * st_elem);
     P.ws_z = (P.normalize && n_state_slots) ? align256((size_t)BH * n_state_slots * P.dk * st_elem) : 0;
     if (n_state_slots == 0) P.ws_states = 0;
@@ -235,6 +248,7 @@ static la_status launch_phase3(const Plan& P, const void* qm, const void* km, co
         p.dv = (int)d_v;
         p.xcd_remap = xcd_ok(grid);
         p.noncausal = !P.causal;
+        p.p0_sub = (int)P.sub;
         return hip_status(la::run_chunked_fwd_i8(p, P.DK, P.DVT, P.T, grid, s), "chunked forward launch");
     }
     la::FwdParams p{};
@@ -262,6 +276,7 @@ static la_status launch_phase3(const Plan& P, const void* qm, const void* km, co
     p.noncausal = !P.causal;
     p.out_scale = (scaled_identity && !P.normalize) ? in_scale * in_scale : 1.0f;
     p.state_scale = scaled_identity ? in_scale : 1.0f;
+    p.p0_sub = (int)P.sub;
     hipError_t e;
     if (P.pipe && out_dt == LA_BF16)
         return hip_status(la::fwd_pipe_bf16(p, P.DK, P.DVT, (int)P.C, grid, s), "chunked forward launch");
@@ -500,13 +515,14 @@ la_status la_chunked_forward(const void* q, const void* k, const void* v, la_dty
 
     // phase 1 + 2 at group granularity (or the total state for non-causal)
     if (P.causal && P.n_groups > 1) {
-        st = chunk_states_impl(km, v, P.i8, BH, L, P.dk, d_v, P.G * P.C, (int)(P.n_groups - 1), (int)P.n_groups,
-                               states, zst, fmap_in_kernel, in_scale, s, klo);
+        const int64_t n_slots = P.n_groups * P.sub;
+        st = chunk_states_impl(km, v, P.i8, BH, L, P.dk, d_v, P.G * P.C / P.sub, (int)(n_slots - P.sub),
+                               (int)n_slots, states, zst, fmap_in_kernel, in_scale, s, klo);
         if (st != LA_OK) return st;
         la::ScanParams sp{};
         sp.S = states;
         sp.z = zst;
-        sp.N = P.n_groups;
+        sp.N = P.n_groups * P.sub;
         sp.E = P.dk * d_v;
         sp.Ez = P.dk;
         sp.is_int = P.i8;
@@ -539,6 +555,7 @@ la_status la_chunk_output(const void* q, const void* k, const void* v, la_dtype 
     if (st != LA_OK) return st;
     if (P.n_groups > 1 && (P_prefix == nullptr || (normalize && z_prefix == nullptr)))
         return fail(LA_ERR_INVALID_ARG, "more than one group needs the prefix states (and normalisers)");
+    P.sub = 1;  // the caller's prefixes: one per group
     return launch_phase3(P, q, k, nullptr, v, o, out_dt, P_prefix, z_prefix, S_final, z_final, la::FMAP_NONE,
                          1.0f, false, (hipStream_t)stream);
 }

@@ -300,8 +300,9 @@ __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(SPLIT
 
     // prefix state of this group: phase 2's exclusive scan at group granularity
     // (causal, groups after the first) or the total state (non-causal)
-    const int p0_groups = p.noncausal ? 1 : p.n_groups;
-    const int p0_index = p.noncausal ? 0 : grp;
+    const int p0_sub = p.p0_sub > 1 ? p.p0_sub : 1;
+    const int p0_groups = p.noncausal ? 1 : p.n_groups * p0_sub;
+    const int p0_index = p.noncausal ? 0 : grp * p0_sub;
     if (p.P0 != nullptr && (grp > 0 || p.noncausal)) {
         const float* P0 = p.P0 + ((bh * p0_groups + p0_index) * p.dk_g) * (int64_t)p.dv;
 #pragma unroll

@@ -206,8 +206,9 @@ __global__ __launch_bounds__(NW * WAVE) void chunked_fwd_i8(FwdParamsI8 p) {
     for (int c = 0; c < CPW; ++c)
 #pragma unroll
         for (int ab = 0; ab < NAB; ++ab) P[c][ab] = i32x4{0, 0, 0, 0};
-    const int p0_groups = p.noncausal ? 1 : p.n_groups;
-    const int p0_index = p.noncausal ? 0 : grp;
+    const int p0_sub = p.p0_sub > 1 ? p.p0_sub : 1;
+    const int p0_groups = p.noncausal ? 1 : p.n_groups * p0_sub;
+    const int p0_index = p.noncausal ? 0 : grp * p0_sub;
     if (p.P0 != nullptr && (grp > 0 || p.noncausal)) {
         const int* P0 = p.P0 + ((bh * p0_groups + p0_index) * p.dk_g) * (int64_t)p.dv;
 #pragma unroll

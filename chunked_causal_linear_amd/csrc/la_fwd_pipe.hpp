@@ -340,7 +340,8 @@ void chunked_fwd_pipe(FwdParams p) {
 #pragma unroll
         for (int ks = 0; ks < NKA; ++ks) P[c][ks][0] = P[c][ks][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (p.P0 != nullptr && grp > 0) {
-        const float* P0 = p.P0 + ((bh * p.n_groups + grp) * DK) * (int64_t)dv + col0 + colw + l16;
+        const int64_t slot = (bh * p.n_groups + grp) * (int64_t)(p.p0_sub > 1 ? p.p0_sub : 1);
+        const float* P0 = p.P0 + (slot * DK) * (int64_t)dv + col0 + colw + l16;
 #pragma unroll
         for (int c = 0; c < CPW; ++c)
 #pragma unroll
@@ -351,7 +352,7 @@ void chunked_fwd_pipe(FwdParams p) {
                     for (int i = 0; i < 4; ++i)
                         P[c][ks][hf][i] = P0[(int64_t)(32 * ks + 8 * g + 4 * hf + i) * dv + c * 16];
         if constexpr (NORM) {
-            const float* z0 = p.z0 + (bh * p.n_groups + grp) * DK;
+            const float* z0 = p.z0 + slot * DK;
 #pragma unroll
             for (int ks = 0; ks < NKA; ++ks)
 #pragma unroll

@@ -15,8 +15,8 @@ struct FwdParams {
     const unsigned short* v;  // [BH, L, dv]
     const unsigned short* k_lo;  // [BH, L, dk_g] bf16 residual of pre-mapped phi(k), or null
     void* o;                  // [BH, L, dv] bf16 or f32
-    const float* P0;          // [BH, n_groups, dk_g, dv] exclusive prefix per group, or null
-    const float* z0;          // [BH, n_groups, dk_g]
+    const float* P0;          // [BH, n_groups * p0_sub, dk_g, dv] exclusive prefixes, or null
+    const float* z0;          // [BH, n_groups * p0_sub, dk_g]
     float* S_final;           // [BH, dk_g, dv] or null
     float* z_final;           // [BH, dk_g] or null
     int64_t L;
@@ -34,6 +34,7 @@ struct FwdParams {
     int noncausal;  // every row reads P0 (the total state); no intra part, no update
     float out_scale;    // multiplies every output row (identity map with in_scale: s^2)
     float state_scale;  // multiplies the returned final state and normaliser (s)
+    int p0_sub;         // prefix slots per group (group g starts at slot g * p0_sub); 0 means 1
 };
 
 // Phase 1 (per-chunk states).
@@ -62,7 +63,7 @@ struct FwdParamsI8 {
     const signed char* k;
     const signed char* v;
     int* o;            // [BH, L, dv]
-    const int* P0;     // [BH, n_groups, dk_g, dv] or null
+    const int* P0;     // [BH, n_groups * p0_sub, dk_g, dv] or null
     int* S_final;      // [BH, dk_g, dv] or null
     int64_t L;
     int C;
@@ -73,6 +74,7 @@ struct FwdParamsI8 {
     int dv;
     int xcd_remap;
     int noncausal;
+    int p0_sub;        // prefix slots per group; 0 means 1
 };
 
 struct StatesParamsI8 {

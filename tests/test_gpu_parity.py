@@ -166,6 +166,28 @@ def test_bf16_streaming_normalized(C, dk, dv, L, group, fmap, scale):
     assert_close(host(z), refz, what="z")
 
 
+@pytest.mark.parametrize("dtype,C,dk,dv,L,group,norm,fmap", [
+    ("bf16", 64, 64, 64, 8192, 64, True, "elu1"), ("bf16", 128, 64, 64, 6000, 16, True, "elu1"),
+    ("bf16", 64, 128, 128, 8192, 32, False, "identity"), ("bf16", 100, 64, 64, 5000, 24, False, "identity"),
+    ("bf16", 32, 64, 128, 4500, 64, True, "elu1"), ("i8", 64, 64, 64, 4096, 32, False, "identity")])
+def test_long_groups_in_pieces(dtype, C, dk, dv, L, group, norm, fmap):
+    """Few long groups: phase 1 sums each group in pieces of >= 1024 rows, the
+    scan walks the pieces and every group starts from its piece's prefix."""
+    q, k, v = _case(18, 2, L, dk, dv, dtype)
+    log(f"{dtype} long groups C={C} dk={dk} dv={dv} L={L} group={group} norm={norm} fmap={fmap}")
+    o, S, z = la.chunked_forward(dev_input(q), dev_input(k), dev_input(v), C, normalize=norm, fmap=fmap,
+                                 return_state=True, group=group)
+    ref, refS, refz = _oracle_forward(q.exact, k.exact, v.exact, C, True, norm, fmap)
+    if dtype == "i8":
+        assert_exact(host(o), ref, "o")
+        assert_exact(host(S), refS, "S")
+        return
+    assert_close(host(o), ref, what="o")
+    assert_close(host(S), refS, what="S")
+    if norm:
+        assert_close(host(z), refz, what="z")
+
+
 @pytest.mark.parametrize("group", [1, 2, 3, 5, 100])
 def test_bf16_groups(group):
     q, k, v = _case(11, 2, 640, 64, 64, "bf16")
