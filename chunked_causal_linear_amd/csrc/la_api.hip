@@ -78,7 +78,7 @@ struct Plan {
     int64_t n_chunks, G, n_groups;
     int DK, DVT, T, n_dvt;
     bool premap;  // phi computed by a separate pass into the workspace
-    bool pipe;    // streaming phase-3 kernel (chunks of 32, 64 or 128 rows; identity map, or elu+1 pre-mapped)
+    bool pipe;    // streaming phase-3 kernel (chunks of 32, 64 or 128 rows)
     bool causal, normalize;
     int64_t sub;       // phase-1 states per group (finer grain than the groups when they are few and long)
     size_t ws_phi;     // bytes of one mapped q or k copy
@@ -127,10 +127,10 @@ la_status make_plan(Plan& P, la_dtype in_dt, int64_t BH, int64_t L, int64_t d_in
 
     int64_t Ce = C <= 0 ? 1 : C;
     if (Ce > L) Ce = L;  // one chunk
-    // FAVOR+ maps q and k in a separate pass; elu+1 too where the streaming
-    // kernel runs, else it is applied while loading; the identity map with a
-    // scale s runs unscaled and scales the results (outputs by s^2 unless
-    // normalised, the final state by s), which is exact.
+    // FAVOR+ maps q and k in a separate pass; elu+1 is applied in the kernels
+    // (on load, or to the landed tiles); the identity map with a scale s runs
+    // unscaled and scales the results (outputs by s^2 unless normalised, the
+    // final state by s), which is exact.
     P.DVT = kernel_dvt(d_v);
     P.n_dvt = (int)(d_v / P.DVT);
     if (P.i8) {
@@ -140,13 +140,13 @@ la_status make_plan(Plan& P, la_dtype in_dt, int64_t BH, int64_t L, int64_t d_in
     }
 
     // The streaming kernel covers chunks of 32, 64 or 128 rows, with or
-    // without the normaliser: the identity map at feature widths 64 and 128,
-    // elu+1 at width 64 (mapped beforehand, with the bf16 residual of phi(k),
-    // whose tile fits the LDS next to three stages at that width only).  It
-    // fills the LDS and runs one workgroup per CU.
+    // without the normaliser: the identity map at feature widths 64 and 128;
+    // elu+1 and FAVOR+ at width 64, where the tile of phi(k)'s bf16 residual
+    // fits the LDS next to three stages (elu+1 mapped in the kernel, FAVOR+
+    // beforehand).  It fills the LDS and runs one workgroup per CU.
     P.pipe = !P.i8 && P.causal && (Ce == 32 || Ce == 64 || Ce == 128) && d_v % 64 == 0 &&
-             ((f == LA_FMAP_IDENTITY && (P.dk == 64 || P.dk == 128)) || (f == LA_FMAP_ELU1 && P.dk == 64));
-    P.premap = f == LA_FMAP_FAVOR || (P.pipe && f == LA_FMAP_ELU1);
+             ((f == LA_FMAP_IDENTITY && (P.dk == 64 || P.dk == 128)) || (f != LA_FMAP_IDENTITY && P.dk == 64));
+    P.premap = f == LA_FMAP_FAVOR;
     if (P.pipe) {
         P.DK = (int)P.dk;
         P.DVT = 64;

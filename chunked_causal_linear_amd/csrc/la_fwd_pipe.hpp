@@ -58,9 +58,15 @@
 // block whose V operand is all ones.  Its state block is z in every column
 // (z += K^T 1), its inter product is Q z and its intra product the row sums of
 // the masked scores, so every lane ends up holding the denominator of its row
-// next to the four numerators it divides.  With the residual of pre-mapped
-// phi(k) (SPLIT), the state and z updates add K_lo^T V and K_lo^T 1, which keeps
-// long state sums free of the bf16 rounding of phi(k); scores use bf16 phi(k).
+// next to the four numerators it divides.  With a residual tile K_lo of phi(k)
+// (phi(k) - bf16(phi(k))), the state and z updates add K_lo^T V and K_lo^T 1,
+// which keeps long state sums free of the bf16 rounding of phi(k); scores use
+// bf16 phi(k).  The residual is either copied in with the tile (phi mapped
+// beforehand) or made here: with elu+1 (same page, the ELU feature map) each
+// copy wave maps its own 16-byte slots of a tile once they have landed, Q in
+// place, K in place as bf16(phi) plus the residual tile, so the mapped values
+// never go through memory.  The copies are issued Q, K, V, so the mapping of Q
+// and K overlaps the arrival of the rest of the tile.
 #pragma once
 
 #include <type_traits>
@@ -164,7 +170,11 @@ using ic = std::integral_constant<int, I>;
 
 }  // namespace pipe
 
-template <int DK, int DVT, int CH, bool SCALED, bool NORM, bool SPLIT>
+// Residual tile of phi(k): none, copied from memory (pre-mapped phi), or
+// computed here (elu+1 applied to the landed Q and K tiles).
+enum { KLO_NONE = 0, KLO_LOAD = 1, KLO_ELU = 2 };
+
+template <int DK, int DVT, int CH, bool SCALED, bool NORM, int KLO>
 __global__ __launch_bounds__(4 * WAVE) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void chunked_fwd_pipe(FwdParams p) {
     using namespace pipe;
@@ -176,7 +186,9 @@ void chunked_fwd_pipe(FwdParams p) {
     constexpr int QSEG = DK / 8, VSEG = DVT / 8;
     constexpr int NCQ = TT * QSEG / WAVE / 2;      // copy instructions per tile and copy wave, Q (and K)
     constexpr int NCV = TT * VSEG / WAVE / 2;      // the same for V (and for the output stores)
-    constexpr int NL = (SPLIT ? 3 : 2) * NCQ + NCV;
+    constexpr bool SPLIT = KLO != KLO_NONE;          // residual tile present
+    constexpr bool PHI = KLO == KLO_ELU;             // copy waves apply elu+1
+    constexpr int NL = (KLO == KLO_LOAD ? 3 : 2) * NCQ + NCV;  // copy instructions per tile and wave
     constexpr int RPV = WAVE / VSEG;               // output rows per store instruction
     static_assert(DVT == 64, "tile of 64 value columns");
     static_assert(CH == 32 || CH == 64 || CH == 128, "chunks of 32, 64 or 128 rows");
@@ -228,10 +240,11 @@ void chunked_fwd_pipe(FwdParams p) {
 
     if (copier) {
         // ================= copy wave h =================
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
         const u16* qh = p.q + bh * L * DK;
         const u16* kh = p.k + bh * L * DK;
         const u16* vh = p.v + bh * L * dv + col0;
-        const u16* klh = SPLIT ? p.k_lo + bh * L * DK : nullptr;
+        const u16* klh = KLO == KLO_LOAD ? p.k_lo + bh * L * DK : nullptr;
         // Lane l of copy instruction b lands in LDS slot 64b + l = (row,
         // physical segment) = (slot / NSEG, slot % NSEG), which holds the
         // global segment (physical ^ row) of that row.
@@ -241,17 +254,23 @@ void chunked_fwd_pipe(FwdParams p) {
             const u16* qb_ = qh + r0 * DK;
             const u16* kb_ = kh + r0 * DK;
             const u16* vb_ = vh + r0 * dv;
-            const u16* klb_ = SPLIT ? klh + r0 * DK : nullptr;
+            const u16* klb_ = KLO == KLO_LOAD ? klh + r0 * DK : nullptr;
             const uint32_t lq = lds_addr(s.q), lk = lds_addr(s.k), lv = lds_addr(s.v);
-#pragma unroll
-            for (int i = 0; i < NCQ; ++i) {
+            // Q, then K (then K's residual), then V: with elu+1 applied here the
+            // Q and K tiles are mapped while the rest is still arriving
+            auto qk_off = [&](int i) __attribute__((always_inline)) {
                 const int b = h * NCQ + i;  // copy instruction within the tile
                 const int slot = b * WAVE + lane;
                 const int r = slot / QSEG, seg = (slot % QSEG) ^ (r & (QSEG - 1));
-                const uint32_t off = (uint32_t)(((r < last ? r : last) * DK + seg * 8) * 2);
-                dma16(qb_, off, lq + b * WAVE * 16);
-                dma16(kb_, off, lk + b * WAVE * 16);
-                if constexpr (SPLIT) dma16(klb_, off, lds_addr(s.klo) + b * WAVE * 16);
+                return (uint32_t)(((r < last ? r : last) * DK + seg * 8) * 2);
+            };
+#pragma unroll
+            for (int i = 0; i < NCQ; ++i) dma16(qb_, qk_off(i), lq + (h * NCQ + i) * WAVE * 16);
+#pragma unroll
+            for (int i = 0; i < NCQ; ++i) dma16(kb_, qk_off(i), lk + (h * NCQ + i) * WAVE * 16);
+            if constexpr (KLO == KLO_LOAD) {
+#pragma unroll
+                for (int i = 0; i < NCQ; ++i) dma16(klb_, qk_off(i), lds_addr(s.klo) + (h * NCQ + i) * WAVE * 16);
             }
 #pragma unroll
             for (int i = 0; i < NCV; ++i) {
@@ -264,7 +283,6 @@ void chunked_fwd_pipe(FwdParams p) {
         // Output rows of tile t sit in the V tile of stage `from`: instruction
         // i, lane l covers row (h * NCV + i) * RPV + l / VSEG, segment l % VSEG.
         // Read them, refill the stage with tile `refill` (if any), store them.
-        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
         auto drain_refill = [&](const StageT& from, int64_t t, int64_t refill, StageT& to)
             __attribute__((always_inline)) {
             u32x4 ob[NCV];
@@ -285,14 +303,59 @@ void chunked_fwd_pipe(FwdParams p) {
             }
         };
 
+        // elu+1 of this wave's own slots of a landed tile (the copies it made):
+        // Q in place; K in place as bf16(phi) with phi - bf16(phi) in the
+        // residual tile
+        auto phi_q = [&](StageT& s) __attribute__((always_inline)) {
+            u32x4 x[NCQ];
+#pragma unroll
+            for (int i = 0; i < NCQ; ++i)
+                x[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(s.q) + ((h * NCQ + i) * WAVE + lane) * 16);
+#pragma unroll
+            for (int i = 0; i < NCQ; ++i) {
+                const uint4 y = elu1_bf16x8(make_uint4(x[i].x, x[i].y, x[i].z, x[i].w), p.in_scale);
+                *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(s.q) + ((h * NCQ + i) * WAVE + lane) * 16) =
+                    u32x4{y.x, y.y, y.z, y.w};
+            }
+        };
+        auto phi_k = [&](StageT& s) __attribute__((always_inline)) {
+            if constexpr (SPLIT) {
+                u32x4 x[NCQ];
+#pragma unroll
+                for (int i = 0; i < NCQ; ++i)
+                    x[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(s.k) +
+                                                           ((h * NCQ + i) * WAVE + lane) * 16);
+#pragma unroll
+                for (int i = 0; i < NCQ; ++i) {
+                    uint4 hi, lo;
+                    elu1_split_bf16x8(make_uint4(x[i].x, x[i].y, x[i].z, x[i].w), p.in_scale, hi, lo);
+                    const int o = ((h * NCQ + i) * WAVE + lane) * 16;
+                    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(s.k) + o) = u32x4{hi.x, hi.y, hi.z, hi.w};
+                    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(s.klo) + o) = u32x4{lo.x, lo.y, lo.z, lo.w};
+                }
+            }
+        };
+        // wait until this wave's copies of a tile have landed (X = copies issued
+        // after them: the next tile's), mapping Q and K as soon as they are in
+        auto land = [&](auto xc, StageT& s) __attribute__((always_inline)) {
+            constexpr int X = decltype(xc)::value;
+            if constexpr (PHI) {
+                wait_vm<X + NCQ + NCV>();
+                phi_q(s);
+                wait_vm<X + NCV>();
+                phi_k(s);
+            }
+            wait_vm<X>();
+        };
+
 #pragma unroll
         for (int s0 = 0; s0 < NSTAGE - 1; ++s0)
             if (t_begin + s0 < t_end) issue(t_begin + s0, st[s0]);
-        // wait for the first tile: the copies issued after it are those of the tiles after it
+        // the first tile: the copies issued after it are those of the tile after it
         if (NSTAGE == 3 && t_begin + 1 < t_end)
-            wait_vm<NL>();
+            land(ic<NL>{}, st[0]);
         else
-            wait_vm<0>();
+            land(ic<0>{}, st[0]);
 
         auto step = [&](auto sidx, int64_t t) __attribute__((always_inline)) {
             constexpr int SI = decltype(sidx)::value;
@@ -309,10 +372,13 @@ void chunked_fwd_pipe(FwdParams p) {
                 issue(refill, st[SP]);
             // tile t + 1 must have landed before B(t + 1); the loads issued after
             // it are those of tile t + 2 (three stages, if any); loads complete in order
-            if (NSTAGE == 3 && t + 2 < t_end)
-                wait_vm<NL>();
-            else
+            constexpr int SN = (SI + 1) % NSTAGE;  // stage of tile t + 1
+            if (t + 1 >= t_end)
                 wait_vm<0>();
+            else if (NSTAGE == 3 && t + 2 < t_end)
+                land(ic<NL>{}, st[SN]);
+            else
+                land(ic<0>{}, st[SN]);
         };
         for (int64_t t = t_begin; t < t_end; t += NSTAGE) {
             step(ic<0>{}, t);
@@ -665,17 +731,17 @@ void chunked_fwd_pipe(FwdParams p) {
 
 // Output scaling exists for the scaled identity map without the normaliser
 // only (normalised outputs are scale-free; pre-mapped inputs carry the scale).
-template <int DK, int DVT, int CH, bool NORM, bool SPLIT>
+template <int DK, int DVT, int CH, bool NORM, int KLO>
 hipError_t launch_fwd_pipe(const FwdParams& p, int64_t grid, hipStream_t s) {
     const dim3 block(4 * WAVE);
     if (p.out_scale != 1.0f) {
-        if constexpr (NORM || SPLIT) {
+        if constexpr (NORM || KLO != KLO_NONE) {
             return hipErrorInvalidValue;
         } else {
-            hipLaunchKernelGGL((chunked_fwd_pipe<DK, DVT, CH, true, false, false>), dim3((unsigned)grid), block, 0, s, p);
+            hipLaunchKernelGGL((chunked_fwd_pipe<DK, DVT, CH, true, false, KLO_NONE>), dim3((unsigned)grid), block, 0, s, p);
         }
     } else {
-        hipLaunchKernelGGL((chunked_fwd_pipe<DK, DVT, CH, false, NORM, SPLIT>), dim3((unsigned)grid), block, 0, s, p);
+        hipLaunchKernelGGL((chunked_fwd_pipe<DK, DVT, CH, false, NORM, KLO>), dim3((unsigned)grid), block, 0, s, p);
     }
     return hipGetLastError();
 }

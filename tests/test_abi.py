@@ -95,15 +95,17 @@ def test_workspace_sizes_and_errors():
     n = ws(b.LA_BF16, 2, 1024, 64, 64, 64, 1, 1, 0, 0, 1.0, 4)
     groups = 1024 // 64 // 4
     assert n == 2 * groups * 64 * 64 * 4 + 2 * groups * 64 * 4
-    # elu+1 at d_k = 64 on the streaming kernel: mapped beforehand, three
-    # copies (phi(q), phi(k), phi(k)'s residual) of BH*L*d_k bf16 in front
+    # elu+1 (mapped inside the kernels): no mapped copies
     n = ws(b.LA_BF16, 2, 1024, 64, 64, 64, 1, 1, 1, 0, 1.0, 4)
+    assert n == 2 * groups * 64 * 64 * 4 + 2 * groups * 64 * 4
+    # FAVOR+ with m = 64 (streaming kernel): three mapped copies in front
+    n = ws(b.LA_BF16, 2, 1024, 64, 64, 64, 1, 1, 2, 64, 1.0, 4)
     assert n == 3 * 2 * 1024 * 64 * 2 + 2 * groups * 64 * 64 * 4 + 2 * groups * 64 * 4
     # few long groups: phase 1 in pieces of 1024 rows, eight per group here
     # (32 heads x 7 groups x 8 pieces), every piece a state slot
     n = ws(b.LA_BF16, 32, 65536, 64, 64, 128, 1, 1, 1, 0, 1.0, 0)
     assert lib.la_chunked_forward_group(b.LA_BF16, 32, 65536, 64, 64, 128, 1, 1, 1, 0, 0) == 64
-    assert n == 3 * 32 * 65536 * 64 * 2 + 32 * 8 * 8 * 64 * 64 * 4 + 32 * 8 * 8 * 64 * 4
+    assert n == 32 * 8 * 8 * 64 * 64 * 4 + 32 * 8 * 8 * 64 * 4
     # elu+1 at d_k = 128 (general kernel, map applied while loading): no copies
     n = ws(b.LA_BF16, 2, 1024, 128, 64, 64, 1, 1, 1, 0, 1.0, 4)
     assert n == 2 * groups * 128 * 64 * 4 + 2 * groups * 128 * 4

@@ -259,6 +259,22 @@ def test_bf16_favor_small():
     assert_close(host(z), refz, what="favor z")
 
 
+@pytest.mark.parametrize("C,L,group", [(64, 700, 0), (32, 530, 3), (128, 900, 2)])
+def test_bf16_favor_m64_streaming(C, L, group):
+    """FAVOR+ with 64 features: mapped beforehand (phi(q), phi(k) and phi(k)'s
+    residual), then the streaming kernel with the residual tile copied in."""
+    q, k, v = _case(19, 2, L, 64, 64, "bf16", scale=1.0 / 8)
+    Wb, W = wl.orthogonal_random_features(64, 64, [19, 3])
+    log(f"bf16 favor m=64 C={C} L={L} group={group}")
+    from tests.gpu_helpers import dev_bf16
+    o, S, z = la.chunked_forward(dev_input(q), dev_input(k), dev_input(v), C, normalize=True, fmap="favor",
+                                 W=dev_bf16(Wb), return_state=True, group=group)
+    ref, refS, refz = _oracle_forward(q.exact, k.exact, v.exact, C, True, True, "favor", W)
+    assert_close(host(o), ref, what="favor o")
+    assert_close(host(S), refS, what="favor S")
+    assert_close(host(z), refz, what="favor z")
+
+
 @pytest.mark.parametrize("norm,fmap", [(False, "identity"), (True, "elu1")])
 def test_bf16_noncausal(norm, fmap):
     q, k, v = _case(16, 3, 210, 64, 64, "bf16")
