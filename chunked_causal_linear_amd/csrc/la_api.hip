@@ -81,6 +81,7 @@ struct Plan {
     bool pipe;    // streaming phase-3 kernel (chunks of 32, 64 or 128 rows)
     bool causal, normalize;
     int64_t sub;       // phase-1 states per group (finer grain than the groups when they are few and long)
+    bool final_from_scan;  // a returned final state / normaliser is the scan's total, not phase 3's
     size_t ws_phi;     // bytes of one mapped q or k copy
     size_t ws_states;  // bytes of the group states
     size_t ws_z;
@@ -139,13 +140,15 @@ la_status make_plan(Plan& P, la_dtype in_dt, int64_t BH, int64_t L, int64_t d_in
         P.DK = kernel_dk_bf16(P.dk);
     }
 
-    // The streaming kernel covers chunks of 32, 64 or 128 rows, with or
-    // without the normaliser: the identity map at feature widths 64 and 128;
-    // elu+1 and FAVOR+ at width 64, where the tile of phi(k)'s bf16 residual
-    // fits the LDS next to three stages (elu+1 mapped in the kernel, FAVOR+
-    // beforehand).  It fills the LDS and runs one workgroup per CU.
+    // The streaming kernel covers chunks of 32, 64 or 128 rows at feature
+    // widths 64 and 128, with or without the normaliser, for every map (elu+1
+    // applied in the kernel, FAVOR+ beforehand).  It fills the LDS and runs one
+    // workgroup per CU.  With a map it sums bf16(phi(k)) into its state; a
+    // returned final state then comes from phase 1 (which adds phi(k)'s
+    // residual) and the scan's total.
     P.pipe = !P.i8 && P.causal && (Ce == 32 || Ce == 64 || Ce == 128) && d_v % 64 == 0 &&
-             ((f == LA_FMAP_IDENTITY && (P.dk == 64 || P.dk == 128)) || (f != LA_FMAP_IDENTITY && P.dk == 64));
+             (P.dk == 64 || P.dk == 128);
+    P.final_from_scan = P.pipe && f != LA_FMAP_IDENTITY;
     P.premap = f == LA_FMAP_FAVOR;
     if (P.pipe) {
         P.DK = (int)P.dk;
@@ -200,16 +203,18 @@ la_status make_plan(Plan& P, la_dtype in_dt, int64_t BH, int64_t L, int64_t d_in
     // until about 1024 workgroups run; the scan then walks the pieces and
     // group g starts from the prefix at piece g * sub.
     P.sub = 1;
-    if (P.causal && P.n_groups > 1) {
+    const int64_t n_summed = P.final_from_scan ? P.n_groups : P.n_groups - 1;  // groups phase 1 may sum
+    if (P.causal && n_summed > 0) {
         const int64_t n_dvt1 = d_v / kernel_dvt(d_v);
         while (P.G % (2 * P.sub) == 0 && P.G * P.C / (2 * P.sub) >= 1024 &&
-               BH * (P.n_groups - 1) * P.sub * n_dvt1 < 1024)
+               BH * n_summed * P.sub * n_dvt1 < 1024)
             P.sub *= 2;
     }
 
     const size_t st_elem = 4;
     P.ws_phi = P.premap ? align256((size_t)BH * L * P.dk * 2) : 0;
-    const int64_t n_state_slots = P.causal ? (P.n_groups > 1 ? P.n_groups * P.sub : 0) : 1;
+    const int64_t n_state_slots =
+        P.causal ? ((P.n_groups > 1 || P.final_from_scan) ? P.n_groups * P.sub : 0) : 1;
     P.ws_states = align256((size_t)BH * n_state_slots * P.dk * d_v * st_elem);
     P.ws_z = (P.normalize && n_state_slots) ? align256((size_t)BH * n_state_slots * P.dk * st_elem) : 0;
     if (n_state_slots == 0) P.ws_states = 0;
@@ -277,9 +282,15 @@ static la_status launch_phase3(const Plan& P, const void* qm, const void* km, co
     p.out_scale = (scaled_identity && !P.normalize) ? in_scale * in_scale : 1.0f;
     p.state_scale = scaled_identity ? in_scale : 1.0f;
     p.p0_sub = (int)P.sub;
+    if (P.final_from_scan) {
+        p.S_final = nullptr;
+        p.z_final = nullptr;
+    }
     hipError_t e;
-    if (P.pipe && out_dt == LA_BF16)
+    if (P.pipe && out_dt == LA_BF16) {
+        p.k_lo = nullptr;  // its state sums bf16(phi(k)) only
         return hip_status(la::fwd_pipe_bf16(p, P.DK, P.DVT, (int)P.C, grid, s), "chunked forward launch");
+    }
     int DVT = P.DVT, T = P.T;
     int64_t grid_g = grid;
     if (P.pipe) {
@@ -513,16 +524,23 @@ la_status la_chunked_forward(const void* q, const void* k, const void* v, la_dty
     void* states = P.ws_states ? ws : nullptr;
     void* zst = P.ws_z ? ws + P.ws_states : nullptr;
 
-    // phase 1 + 2 at group granularity (or the total state for non-causal)
-    if (P.causal && P.n_groups > 1) {
+    // phase 1 + 2 at group granularity (or the total state for non-causal);
+    // with the final state from the scan, phase 1 also sums the last group
+    const bool want_final = P.final_from_scan && (S_final != nullptr || z_final != nullptr);
+    if (P.causal && (P.n_groups > 1 || want_final)) {
         const int64_t n_slots = P.n_groups * P.sub;
-        st = chunk_states_impl(km, v, P.i8, BH, L, P.dk, d_v, P.G * P.C / P.sub, (int)(n_slots - P.sub),
-                               (int)n_slots, states, zst, fmap_in_kernel, in_scale, s, klo);
+        const int64_t n_items = want_final ? n_slots : n_slots - P.sub;
+        st = chunk_states_impl(km, v, P.i8, BH, L, P.dk, d_v, P.G * P.C / P.sub, (int)n_items, (int)n_slots,
+                               states, zst, fmap_in_kernel, in_scale, s, klo);
         if (st != LA_OK) return st;
         la::ScanParams sp{};
         sp.S = states;
         sp.z = zst;
-        sp.N = P.n_groups * P.sub;
+        sp.N = n_slots;
+        if (want_final) {
+            sp.S_final = S_final;
+            sp.z_final = z_final;
+        }
         sp.E = P.dk * d_v;
         sp.Ez = P.dk;
         sp.is_int = P.i8;

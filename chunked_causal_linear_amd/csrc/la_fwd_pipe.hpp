@@ -58,15 +58,16 @@
 // block whose V operand is all ones.  Its state block is z in every column
 // (z += K^T 1), its inter product is Q z and its intra product the row sums of
 // the masked scores, so every lane ends up holding the denominator of its row
-// next to the four numerators it divides.  With a residual tile K_lo of phi(k)
-// (phi(k) - bf16(phi(k))), the state and z updates add K_lo^T V and K_lo^T 1,
-// which keeps long state sums free of the bf16 rounding of phi(k); scores use
-// bf16 phi(k).  The residual is either copied in with the tile (phi mapped
-// beforehand) or made here: with elu+1 (same page, the ELU feature map) each
-// copy wave maps its own 16-byte slots of a tile once they have landed, Q in
-// place, K in place as bf16(phi) plus the residual tile, so the mapped values
+// next to the four numerators it divides.
+//
+// elu+1 (same page, the ELU feature map; PHI): each copy wave maps its own
+// 16-byte slots of a tile in place once they have landed, so the mapped values
 // never go through memory.  The copies are issued Q, K, V, so the mapping of Q
-// and K overlaps the arrival of the rest of the tile.
+// and K overlaps the arrival of the rest of the tile.  The state here sums
+// bf16(phi(k)): the products read it rounded to bf16 anyway, so that rounding
+// stays below the operand rounding of the inter product; a returned final
+// state or normaliser, where it would not, is summed elsewhere with phi(k)'s
+// residual (phase 1 and the scan), and the kernel then writes none.
 #pragma once
 
 #include <type_traits>
@@ -85,18 +86,11 @@ __device__ __forceinline__ int tile_off(int r, int e) {
     return r * NSEG * 16 + ((((e >> 3) ^ r) & (NSEG - 1)) << 4) + ((e & 7) << 1);
 }
 
-template <int DK, int DVT, int TT, bool SPLIT>
+template <int DK, int DVT, int TT>
 struct alignas(16) Stage {
     u16 q[TT * DK];
     u16 k[TT * DK];
     u16 v[TT * DVT];
-};
-template <int DK, int DVT, int TT>
-struct alignas(16) Stage<DK, DVT, TT, true> {
-    u16 q[TT * DK];
-    u16 k[TT * DK];
-    u16 v[TT * DVT];
-    u16 klo[TT * DK];  // residual of pre-mapped phi(k)
 };
 
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
@@ -170,32 +164,26 @@ using ic = std::integral_constant<int, I>;
 
 }  // namespace pipe
 
-// Residual tile of phi(k): none, copied from memory (pre-mapped phi), or
-// computed here (elu+1 applied to the landed Q and K tiles).
-enum { KLO_NONE = 0, KLO_LOAD = 1, KLO_ELU = 2 };
-
-template <int DK, int DVT, int CH, bool SCALED, bool NORM, int KLO>
+template <int DK, int DVT, int CH, bool SCALED, bool NORM, bool PHI>
 __global__ __launch_bounds__(4 * WAVE) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void chunked_fwd_pipe(FwdParams p) {
     using namespace pipe;
     constexpr int TT = CH > 64 ? CH : 64;          // rows per tile
-    constexpr int NSTAGE = TT == 128 ? 2 : 3;      // LDS stages
+    constexpr int NSTAGE = 3 * sizeof(Stage<DK, DVT, TT>) <= 160 * 1024 ? 3 : 2;  // LDS stages
     constexpr int CPW = DVT / 32;                  // 16-column blocks per pair
     constexpr int NCB = CPW + (NORM ? 1 : 0);      // + the denominator block
     constexpr int NKA = DK / 32;                   // k-steps over the feature index
     constexpr int QSEG = DK / 8, VSEG = DVT / 8;
     constexpr int NCQ = TT * QSEG / WAVE / 2;      // copy instructions per tile and copy wave, Q (and K)
     constexpr int NCV = TT * VSEG / WAVE / 2;      // the same for V (and for the output stores)
-    constexpr bool SPLIT = KLO != KLO_NONE;          // residual tile present
-    constexpr bool PHI = KLO == KLO_ELU;             // copy waves apply elu+1
-    constexpr int NL = (KLO == KLO_LOAD ? 3 : 2) * NCQ + NCV;  // copy instructions per tile and wave
+    constexpr int NL = 2 * NCQ + NCV;              // copy instructions per tile and copy wave
     constexpr int RPV = WAVE / VSEG;               // output rows per store instruction
     static_assert(DVT == 64, "tile of 64 value columns");
     static_assert(CH == 32 || CH == 64 || CH == 128, "chunks of 32, 64 or 128 rows");
     static_assert(DK == 64 || DK == 128, "feature width 64 or 128");
     static_assert(NL < 64, "vmcnt range");
-    static_assert(NSTAGE * (int)sizeof(Stage<DK, DVT, TT, SPLIT>) <= 160 * 1024, "LDS");
-    typedef Stage<DK, DVT, TT, SPLIT> StageT;
+    static_assert(NSTAGE * (int)sizeof(Stage<DK, DVT, TT>) <= 160 * 1024, "LDS");
+    typedef Stage<DK, DVT, TT> StageT;
 
     __shared__ StageT st[NSTAGE];
 
@@ -232,10 +220,6 @@ void chunked_fwd_pipe(FwdParams p) {
         const int n = (TT - valid) * QSEG;
         uint4* kk = reinterpret_cast<uint4*>(s.k + valid * DK);
         for (int i = tid; i < n; i += 4 * WAVE) kk[i] = make_uint4(0, 0, 0, 0);
-        if constexpr (SPLIT) {
-            uint4* kl = reinterpret_cast<uint4*>(s.klo + valid * DK);
-            for (int i = tid; i < n; i += 4 * WAVE) kl[i] = make_uint4(0, 0, 0, 0);
-        }
     };
 
     if (copier) {
@@ -244,7 +228,6 @@ void chunked_fwd_pipe(FwdParams p) {
         const u16* qh = p.q + bh * L * DK;
         const u16* kh = p.k + bh * L * DK;
         const u16* vh = p.v + bh * L * dv + col0;
-        const u16* klh = KLO == KLO_LOAD ? p.k_lo + bh * L * DK : nullptr;
         // Lane l of copy instruction b lands in LDS slot 64b + l = (row,
         // physical segment) = (slot / NSEG, slot % NSEG), which holds the
         // global segment (physical ^ row) of that row.
@@ -254,10 +237,9 @@ void chunked_fwd_pipe(FwdParams p) {
             const u16* qb_ = qh + r0 * DK;
             const u16* kb_ = kh + r0 * DK;
             const u16* vb_ = vh + r0 * dv;
-            const u16* klb_ = KLO == KLO_LOAD ? klh + r0 * DK : nullptr;
             const uint32_t lq = lds_addr(s.q), lk = lds_addr(s.k), lv = lds_addr(s.v);
-            // Q, then K (then K's residual), then V: with elu+1 applied here the
-            // Q and K tiles are mapped while the rest is still arriving
+            // Q, then K, then V: with elu+1 applied here the Q and K tiles are
+            // mapped while the rest is still arriving
             auto qk_off = [&](int i) __attribute__((always_inline)) {
                 const int b = h * NCQ + i;  // copy instruction within the tile
                 const int slot = b * WAVE + lane;
@@ -268,10 +250,6 @@ void chunked_fwd_pipe(FwdParams p) {
             for (int i = 0; i < NCQ; ++i) dma16(qb_, qk_off(i), lq + (h * NCQ + i) * WAVE * 16);
 #pragma unroll
             for (int i = 0; i < NCQ; ++i) dma16(kb_, qk_off(i), lk + (h * NCQ + i) * WAVE * 16);
-            if constexpr (KLO == KLO_LOAD) {
-#pragma unroll
-                for (int i = 0; i < NCQ; ++i) dma16(klb_, qk_off(i), lds_addr(s.klo) + (h * NCQ + i) * WAVE * 16);
-            }
 #pragma unroll
             for (int i = 0; i < NCV; ++i) {
                 const int b = h * NCV + i;
@@ -303,97 +281,78 @@ void chunked_fwd_pipe(FwdParams p) {
             }
         };
 
-        // elu+1 of this wave's own slots of a landed tile (the copies it made):
-        // Q in place; K in place as bf16(phi) with phi - bf16(phi) in the
-        // residual tile
-        auto phi_q = [&](StageT& s) __attribute__((always_inline)) {
+        // elu+1 of this wave's own slots of a landed Q or K tile, in place
+        auto phi_tile = [&](u16* tile) __attribute__((always_inline)) {
             u32x4 x[NCQ];
 #pragma unroll
             for (int i = 0; i < NCQ; ++i)
-                x[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(s.q) + ((h * NCQ + i) * WAVE + lane) * 16);
+                x[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(tile) +
+                                                       ((h * NCQ + i) * WAVE + lane) * 16);
 #pragma unroll
             for (int i = 0; i < NCQ; ++i) {
                 const uint4 y = elu1_bf16x8(make_uint4(x[i].x, x[i].y, x[i].z, x[i].w), p.in_scale);
-                *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(s.q) + ((h * NCQ + i) * WAVE + lane) * 16) =
+                *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(tile) + ((h * NCQ + i) * WAVE + lane) * 16) =
                     u32x4{y.x, y.y, y.z, y.w};
-            }
-        };
-        auto phi_k = [&](StageT& s) __attribute__((always_inline)) {
-            if constexpr (SPLIT) {
-                u32x4 x[NCQ];
-#pragma unroll
-                for (int i = 0; i < NCQ; ++i)
-                    x[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(s.k) +
-                                                           ((h * NCQ + i) * WAVE + lane) * 16);
-#pragma unroll
-                for (int i = 0; i < NCQ; ++i) {
-                    uint4 hi, lo;
-                    elu1_split_bf16x8(make_uint4(x[i].x, x[i].y, x[i].z, x[i].w), p.in_scale, hi, lo);
-                    const int o = ((h * NCQ + i) * WAVE + lane) * 16;
-                    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(s.k) + o) = u32x4{hi.x, hi.y, hi.z, hi.w};
-                    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(s.klo) + o) = u32x4{lo.x, lo.y, lo.z, lo.w};
-                }
             }
         };
         // wait until this wave's copies of a tile have landed (X = copies issued
         // after them: the next tile's), mapping Q and K as soon as they are in
-        auto land = [&](auto xc, StageT& s) __attribute__((always_inline)) {
-            constexpr int X = decltype(xc)::value;
+        // `more`: the next tile's copies were issued after this tile's (three
+        // stages, not at the end); the wait counts are immediates, so each is
+        // picked by a branch rather than by duplicating the mapping code
+        auto land = [&](bool more, StageT& s) __attribute__((always_inline)) {
+            if constexpr (NSTAGE == 2) more = false;
             if constexpr (PHI) {
-                wait_vm<X + NCQ + NCV>();
-                phi_q(s);
-                wait_vm<X + NCV>();
-                phi_k(s);
+                if (more)
+                    wait_vm<(NSTAGE == 3 ? NL : 0) + NCQ + NCV>();
+                else
+                    wait_vm<NCQ + NCV>();
+                phi_tile(s.q);
+                if (more)
+                    wait_vm<(NSTAGE == 3 ? NL : 0) + NCV>();
+                else
+                    wait_vm<NCV>();
+                phi_tile(s.k);
             }
-            wait_vm<X>();
+            if (more)
+                wait_vm<NSTAGE == 3 ? NL : 0>();
+            else
+                wait_vm<0>();
         };
 
 #pragma unroll
         for (int s0 = 0; s0 < NSTAGE - 1; ++s0)
             if (t_begin + s0 < t_end) issue(t_begin + s0, st[s0]);
         // the first tile: the copies issued after it are those of the tile after it
-        if (NSTAGE == 3 && t_begin + 1 < t_end)
-            land(ic<NL>{}, st[0]);
-        else
-            land(ic<0>{}, st[0]);
+        land(t_begin + 1 < t_end, st[0]);
 
-        auto step = [&](auto sidx, int64_t t) __attribute__((always_inline)) {
-            constexpr int SI = decltype(sidx)::value;
-            constexpr int SP = (SI + NSTAGE - 1) % NSTAGE;  // stage of tile t - 1
+        // The copy side walks the stages with a run-time index (its accesses
+        // take computed addresses anyway), so its code appears once.
+        int si = 0;  // stage of tile t
+        for (int64_t t = t_begin; t < t_end; ++t) {
+            const int sp = si == 0 ? NSTAGE - 1 : si - 1;  // stage of tile t - 1
+            const int sn = si == NSTAGE - 1 ? 0 : si + 1;  // stage of tile t + 1
             __syncthreads();  // B(t)
             if (valid_rows(t) < TT) {
-                zero_tail(st[SI], valid_rows(t));
+                zero_tail(st[si], valid_rows(t));
                 __syncthreads();
             }
             const int64_t refill = t + NSTAGE - 1 < t_end ? t + NSTAGE - 1 : -1;
             if (t > t_begin)
-                drain_refill(st[SP], t - 1, refill, st[SP]);
+                drain_refill(st[sp], t - 1, refill, st[sp]);
             else if (refill >= 0)
-                issue(refill, st[SP]);
+                issue(refill, st[sp]);
             // tile t + 1 must have landed before B(t + 1); the loads issued after
             // it are those of tile t + 2 (three stages, if any); loads complete in order
-            constexpr int SN = (SI + 1) % NSTAGE;  // stage of tile t + 1
-            if (t + 1 >= t_end)
-                wait_vm<0>();
-            else if (NSTAGE == 3 && t + 2 < t_end)
-                land(ic<NL>{}, st[SN]);
+            if (t + 1 < t_end)
+                land(t + 2 < t_end, st[sn]);
             else
-                land(ic<0>{}, st[SN]);
-        };
-        for (int64_t t = t_begin; t < t_end; t += NSTAGE) {
-            step(ic<0>{}, t);
-            if (t + 1 < t_end) step(ic<1>{}, t + 1);
-            if constexpr (NSTAGE == 3)
-                if (t + 2 < t_end) step(ic<NSTAGE - 1>{}, t + 2);
+                wait_vm<0>();
+            si = sn;
         }
         __syncthreads();  // the last tile's output is in its stage
-        const int sl = (int)((t_end - 1 - t_begin) % NSTAGE);
-        if (sl == 0)
-            drain_refill(st[0], t_end - 1, -1, st[0]);
-        else if (sl == 1)
-            drain_refill(st[1], t_end - 1, -1, st[1]);
-        else
-            drain_refill(st[NSTAGE - 1], t_end - 1, -1, st[NSTAGE - 1]);
+        const int sl = si == 0 ? NSTAGE - 1 : si - 1;
+        drain_refill(st[sl], t_end - 1, -1, st[sl]);
         return;
     }
 
@@ -504,20 +463,16 @@ void chunked_fwd_pipe(FwdParams p) {
     // operands one (ks, hf) step ahead
     auto update = [&](const StageT& s, auto kk0c, auto nkc) __attribute__((always_inline)) {
         constexpr int KK0 = decltype(kk0c)::value, NK = decltype(nkc)::value;
-        constexpr int NSRC = SPLIT ? 2 : 1;  // phi(k), and its residual
         bf16x8 vb[NCB][NK];
 #pragma unroll
         for (int c = 0; c < NCB; ++c)
 #pragma unroll
             for (int kk = 0; kk < NK; ++kk)
                 vb[c][kk] = c < CPW ? col_op<VSEG>(s.v, (KK0 + kk) * 32, colw + c * 16 + c4, lane) : ones;
-        bf16x8 kc[2][NSRC][NK];
-        auto load_kc = [&](int ks, int hf, bf16x8 (&k_)[NSRC][NK]) __attribute__((always_inline)) {
+        bf16x8 kc[2][NK];
+        auto load_kc = [&](int ks, int hf, bf16x8 (&k_)[NK]) __attribute__((always_inline)) {
 #pragma unroll
-            for (int kk = 0; kk < NK; ++kk) {
-                k_[0][kk] = col_op<QSEG>(s.k, (KK0 + kk) * 32, ks * 32 + c8 + 4 * hf, lane);
-                if constexpr (SPLIT) k_[NSRC - 1][kk] = col_op<QSEG>(s.klo, (KK0 + kk) * 32, ks * 32 + c8 + 4 * hf, lane);
-            }
+            for (int kk = 0; kk < NK; ++kk) k_[kk] = col_op<QSEG>(s.k, (KK0 + kk) * 32, ks * 32 + c8 + 4 * hf, lane);
         };
         load_kc(0, 0, kc[0]);
 #pragma unroll
@@ -526,12 +481,9 @@ void chunked_fwd_pipe(FwdParams p) {
             if (t + 1 < 2 * NKA) load_kc((t + 1) >> 1, (t + 1) & 1, kc[(t + 1) & 1]);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int src = 0; src < NSRC; ++src)
+            for (int kk = 0; kk < NK; ++kk)
 #pragma unroll
-                for (int kk = 0; kk < NK; ++kk)
-#pragma unroll
-                    for (int c = 0; c < NCB; ++c)
-                        P[c][ks][hf] = mfma_bf16(kc[t & 1][src][kk], vb[c][kk], P[c][ks][hf]);
+                for (int c = 0; c < NCB; ++c) P[c][ks][hf] = mfma_bf16(kc[t & 1][kk], vb[c][kk], P[c][ks][hf]);
         }
     };
 
@@ -563,16 +515,17 @@ void chunked_fwd_pipe(FwdParams p) {
     // last V read of the tile, in program order)
     auto write_out = [&](StageT& s, auto q0c, f32x4 (&O)[NCB][4]) __attribute__((always_inline)) {
         constexpr int Q0 = decltype(q0c)::value;
+        // the denominator block holds the row's denominator in every column:
+        // one reciprocal (v_rcp_f32, about 1 ulp) per row and lane
+        float rden[4];
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb) rden[qb] = NORM ? __builtin_amdgcn_rcpf(O[NCB - 1][qb][0]) : 1.0f;
 #pragma unroll
         for (int c = 0; c < CPW; ++c)
 #pragma unroll
             for (int qb = 0; qb < 4; ++qb) {
                 f32x4 o = O[c][qb];
-                if constexpr (NORM) {
-                    // the denominator block holds the row's denominator in every column
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) o[i] = o[i] / O[CPW][qb][i];
-                }
+                if constexpr (NORM) o *= rden[qb];
                 if (SCALED) o *= osc;
                 *reinterpret_cast<uint2*>(reinterpret_cast<char*>(s.v) +
                                           tile_off<VSEG>((Q0 + qb) * 16 + l16, colw + c * 16 + 4 * g)) =
@@ -731,17 +684,17 @@ void chunked_fwd_pipe(FwdParams p) {
 
 // Output scaling exists for the scaled identity map without the normaliser
 // only (normalised outputs are scale-free; pre-mapped inputs carry the scale).
-template <int DK, int DVT, int CH, bool NORM, int KLO>
+template <int DK, int DVT, int CH, bool NORM, bool PHI>
 hipError_t launch_fwd_pipe(const FwdParams& p, int64_t grid, hipStream_t s) {
     const dim3 block(4 * WAVE);
     if (p.out_scale != 1.0f) {
-        if constexpr (NORM || KLO != KLO_NONE) {
+        if constexpr (NORM || PHI) {
             return hipErrorInvalidValue;
         } else {
-            hipLaunchKernelGGL((chunked_fwd_pipe<DK, DVT, CH, true, false, KLO_NONE>), dim3((unsigned)grid), block, 0, s, p);
+            hipLaunchKernelGGL((chunked_fwd_pipe<DK, DVT, CH, true, false, false>), dim3((unsigned)grid), block, 0, s, p);
         }
     } else {
-        hipLaunchKernelGGL((chunked_fwd_pipe<DK, DVT, CH, false, NORM, KLO>), dim3((unsigned)grid), block, 0, s, p);
+        hipLaunchKernelGGL((chunked_fwd_pipe<DK, DVT, CH, false, NORM, PHI>), dim3((unsigned)grid), block, 0, s, p);
     }
     return hipGetLastError();
 }

@@ -5,32 +5,22 @@ namespace la {
 
 namespace {
 
-// normaliser from p.normalize; the residual tile of phi(k) from p.k_lo (phi
-// mapped beforehand) or p.fmap (elu+1 applied here); feature width 64 only
-// for the residual: three LDS stages with its tile fit there.
+// normaliser from p.normalize; elu+1 applied in the kernel from p.fmap
 template <int DK, int C>
 hipError_t by_flags(const FwdParams& p, int64_t grid, hipStream_t s) {
     const bool norm = p.normalize != 0;
-    if (p.k_lo != nullptr || p.fmap == FMAP_ELU1) {
-        if constexpr (DK == 64) {
-            if (p.fmap == FMAP_ELU1)
-                return norm ? launch_fwd_pipe<64, 64, C, true, KLO_ELU>(p, grid, s)
-                            : launch_fwd_pipe<64, 64, C, false, KLO_ELU>(p, grid, s);
-            return norm ? launch_fwd_pipe<64, 64, C, true, KLO_LOAD>(p, grid, s)
-                        : launch_fwd_pipe<64, 64, C, false, KLO_LOAD>(p, grid, s);
-        } else {
-            return hipErrorInvalidValue;
-        }
-    }
-    return norm ? launch_fwd_pipe<DK, 64, C, true, KLO_NONE>(p, grid, s)
-                : launch_fwd_pipe<DK, 64, C, false, KLO_NONE>(p, grid, s);
+    if (p.fmap == FMAP_ELU1)
+        return norm ? launch_fwd_pipe<DK, 64, C, true, true>(p, grid, s)
+                    : launch_fwd_pipe<DK, 64, C, false, true>(p, grid, s);
+    return norm ? launch_fwd_pipe<DK, 64, C, true, false>(p, grid, s)
+                : launch_fwd_pipe<DK, 64, C, false, false>(p, grid, s);
 }
 
 }  // namespace
 
 hipError_t fwd_pipe_bf16(const FwdParams& p, int DK, int DVT, int C, int64_t grid, hipStream_t s) {
-    if (DVT != 64 || p.noncausal || p.out_f32) return hipErrorInvalidValue;
-    if (p.fmap != FMAP_NONE && (p.fmap != FMAP_ELU1 || p.k_lo != nullptr)) return hipErrorInvalidValue;
+    if (DVT != 64 || p.noncausal || p.out_f32 || p.k_lo != nullptr) return hipErrorInvalidValue;
+    if (p.fmap != FMAP_NONE && p.fmap != FMAP_ELU1) return hipErrorInvalidValue;
     switch (DK * 1000 + C) {
         case 128032: return by_flags<128, 32>(p, grid, s);
         case 128064: return by_flags<128, 64>(p, grid, s);

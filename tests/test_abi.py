@@ -101,12 +101,16 @@ def test_workspace_sizes_and_errors():
     # FAVOR+ with m = 64 (streaming kernel): three mapped copies in front
     n = ws(b.LA_BF16, 2, 1024, 64, 64, 64, 1, 1, 2, 64, 1.0, 4)
     assert n == 3 * 2 * 1024 * 64 * 2 + 2 * groups * 64 * 64 * 4 + 2 * groups * 64 * 4
-    # few long groups: phase 1 in pieces of 1024 rows, eight per group here
-    # (32 heads x 7 groups x 8 pieces), every piece a state slot
+    # few long groups: phase 1 in pieces of >= 1024 rows, four per group here
+    # (32 heads x 8 groups x 4 pieces: with a map phase 1 also sums the last
+    # group, whose total is the returned final state), every piece a state slot
     n = ws(b.LA_BF16, 32, 65536, 64, 64, 128, 1, 1, 1, 0, 1.0, 0)
     assert lib.la_chunked_forward_group(b.LA_BF16, 32, 65536, 64, 64, 128, 1, 1, 1, 0, 0) == 64
+    assert n == 32 * 8 * 4 * 64 * 64 * 4 + 32 * 8 * 4 * 64 * 4
+    # the identity map: the last group is never summed (seven groups x 8 pieces)
+    n = ws(b.LA_BF16, 32, 65536, 64, 64, 128, 1, 1, 0, 0, 1.0, 0)
     assert n == 32 * 8 * 8 * 64 * 64 * 4 + 32 * 8 * 8 * 64 * 4
-    # elu+1 at d_k = 128 (general kernel, map applied while loading): no copies
+    # elu+1 at d_k = 128: no copies either
     n = ws(b.LA_BF16, 2, 1024, 128, 64, 64, 1, 1, 1, 0, 1.0, 4)
     assert n == 2 * groups * 128 * 64 * 4 + 2 * groups * 128 * 4
     # FAVOR+: three mapped copies (q, k and k's residual) of BH*L*m bf16

@@ -148,12 +148,14 @@ def _positive(t):
     (32, 64, 128, 75, 0, "elu1", 1.0), (128, 64, 64, 1300, 0, "elu1", 1.0), (128, 64, 128, 900, 3, "elu1", 1.0),
     (64, 128, 128, 700, 2, "identity", 1.0), (128, 128, 64, 600, 0, "identity", 1.0),
     (32, 128, 64, 300, 0, "identity", 1.0), (64, 64, 64, 64, 0, "identity", 0.5),
-    (128, 64, 128, 257, 2, "identity", 1.0)])
+    (128, 64, 128, 257, 2, "identity", 1.0), (64, 128, 128, 700, 0, "elu1", 1.0),
+    (128, 128, 64, 500, 2, "elu1", 1.0), (32, 128, 64, 333, 0, "elu1", 0.5)])
 def test_bf16_streaming_normalized(C, dk, dv, L, group, fmap, scale):
-    """Normalised forwards on the streaming kernel: elu+1 at d_k = 64 (mapped
-    beforehand, with phi(k)'s residual in the state sums) and the identity map
-    on non-negative features (the denominator stays away from zero), at chunks
-    of 32, 64 and 128, with groups, ragged tails and a folded input scale."""
+    """Normalised forwards on the streaming kernel: elu+1 (mapped in the kernel;
+    the final state and normaliser from phase 1 with phi(k)'s residual and the
+    scan) and the identity map on non-negative features (the denominator stays
+    away from zero), at chunks of 32, 64 and 128, with groups, ragged tails and
+    an input scale."""
     q, k, v = _case(17, 2, L, dk, dv, "bf16")
     if fmap == "identity":
         q, k = _positive(q), _positive(k)
@@ -259,13 +261,13 @@ def test_bf16_favor_small():
     assert_close(host(z), refz, what="favor z")
 
 
-@pytest.mark.parametrize("C,L,group", [(64, 700, 0), (32, 530, 3), (128, 900, 2)])
-def test_bf16_favor_m64_streaming(C, L, group):
-    """FAVOR+ with 64 features: mapped beforehand (phi(q), phi(k) and phi(k)'s
-    residual), then the streaming kernel with the residual tile copied in."""
+@pytest.mark.parametrize("m,C,L,group", [(64, 64, 700, 0), (64, 32, 530, 3), (64, 128, 900, 2), (128, 64, 400, 2)])
+def test_bf16_favor_streaming(m, C, L, group):
+    """FAVOR+ with 64 or 128 features: mapped beforehand (phi(q), phi(k) and
+    phi(k)'s residual for phase 1), then the streaming kernel."""
     q, k, v = _case(19, 2, L, 64, 64, "bf16", scale=1.0 / 8)
-    Wb, W = wl.orthogonal_random_features(64, 64, [19, 3])
-    log(f"bf16 favor m=64 C={C} L={L} group={group}")
+    Wb, W = wl.orthogonal_random_features(m, 64, [19, 3])
+    log(f"bf16 favor m={m} C={C} L={L} group={group}")
     from tests.gpu_helpers import dev_bf16
     o, S, z = la.chunked_forward(dev_input(q), dev_input(k), dev_input(v), C, normalize=True, fmap="favor",
                                  W=dev_bf16(Wb), return_state=True, group=group)
