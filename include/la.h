@@ -174,10 +174,13 @@ la_status la_chunk_output(const void* q, const void* k, const void* v, la_dtype 
  *        (LA_F32; only with normalize): optional final state.
  *   group  consecutive chunks one workgroup carries the state through (0 =
  *        chosen by the library).  The call runs la_chunk_states at group
- *        granularity, la_state_scan over the groups and la_chunk_output;
- *        group = 1 is the literal three-phase form (one state per chunk),
- *        group >= N a single sequential walk per head.  Every value gives the
- *        same result in exact arithmetic.
+ *        granularity (few long groups: in up to eight pieces per group),
+ *        la_state_scan over those states and la_chunk_output; group = 1 is
+ *        the literal three-phase form (one state per chunk), group >= N a
+ *        single sequential walk per head.  Every value gives the same result
+ *        in exact arithmetic.  With a feature map, a requested final state
+ *        and normaliser are the scan's total over phase-1 states that keep
+ *        phi(k) to about 2^-17 (bf16 value plus bf16 residual).
  *   workspace / ws_bytes  device scratch of at least
  *        la_chunked_forward_workspace(...) bytes (may be NULL when that is 0).
  */
@@ -190,8 +193,9 @@ la_status la_chunked_forward(const void* q, const void* k, const void* v, la_dty
 
 /* Bytes of workspace la_chunked_forward needs for these arguments (0 when it
  * needs none, and also on an invalid combination, which la_chunked_forward
- * then reports).  FAVOR+, or the identity map with in_scale != 1, stores the
- * mapped q and k there; more than one group stores the group states there. */
+ * then reports).  FAVOR+ stores phi(q), phi(k) and phi(k)'s bf16 residual
+ * there; the phase-1 states (and normalisers) go there when there is more than
+ * one group, or when a mapped forward may return its final state. */
 size_t la_chunked_forward_workspace(la_dtype in_dt, int64_t BH, int64_t L, int64_t d_in,
                                     int64_t d_v, int64_t C, int causal, int normalize,
                                     la_fmap f, int64_t m, float in_scale, int64_t group);
