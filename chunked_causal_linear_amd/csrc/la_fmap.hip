@@ -6,7 +6,7 @@
 //    bf16 output they can also write the bf16 residual y - bf16(y).
 //  * FAVOR+ is a small GEMM x W^T (k = d_in) on bf16 matrix cores with an
 //    fp32 epilogue exp(proj - |x|^2 / 2) / sqrt(m).  W stays in LDS for the
-//    life of the workgroup, which walks row tiles of 64.
+//    life of the workgroup, whose waves walk slabs of 16 rows.
 #include "la_common.hpp"
 #include "la_kernels.hpp"
 
@@ -51,20 +51,29 @@ __global__ __launch_bounds__(256) void fmap_elementwise(FmapParams p) {
 }
 
 // FAVOR+: DINP = d_in padded to a multiple of 32 (columns past d_in are zero).
+// W (m x d_in) stays in LDS; every wave walks slabs of 16 rows on its own
+// (the next slab's rows are loaded while the current one is mapped): the
+// slab's x rows go straight into registers as matrix-core operands, the
+// product is taken as (W x^T) so that a lane ends with four consecutive
+// features of one row (16 nb + 4g + i, row l16), and |x|^2 of the row is summed
+// from the same operand registers.  bf16 results are staged per wave in LDS and
+// leave as 16-byte stores with consecutive lanes on consecutive addresses
+// (whole rows per instruction: a row's pieces spread over several instructions
+// wrote at two thirds of the rate).  No barrier after W is in.
 template <int DINP>
 __global__ __launch_bounds__(256) void fmap_favor(FmapParams p) {
-    constexpr int RT = 64;          // rows per tile
-    constexpr int XS = DINP + 8;    // LDS row stride (elements)
+    constexpr int XS = DINP + 8;    // LDS row stride of W (elements)
     constexpr int MMAX = 256;
     constexpr int NKS = DINP / 32;
+    constexpr int YS = MMAX + 8;    // staging row stride (elements)
     __shared__ __attribute__((aligned(16))) u16 Ws[MMAX * XS];
-    __shared__ __attribute__((aligned(16))) u16 Xs[RT * XS];
-    __shared__ float half_sq[RT];
+    __shared__ __attribute__((aligned(16))) u16 Ys[4][16 * YS];
 
     const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE, l16 = lane % 16, g = lane / 16;
     const int m = p.m, din = p.d_in;
     const float s = p.in_scale;
     const float inv_sqrt_m = 1.0f / sqrtf((float)m);
+    u16* ys = Ys[wave];
 
     // W -> LDS (zero-padded columns)
     for (int idx = tid; idx < m * (DINP / 8); idx += 256) {
@@ -73,66 +82,114 @@ __global__ __launch_bounds__(256) void fmap_favor(FmapParams p) {
         if (cg * 8 < din) val = *reinterpret_cast<const uint4*>(p.W + (int64_t)r * din + cg * 8);
         *reinterpret_cast<uint4*>(Ws + r * XS + cg * 8) = val;
     }
+    __syncthreads();
 
-    const int64_t n_tiles = (p.rows + RT - 1) / RT;
-    for (int64_t tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
-        const int64_t r0 = tile * RT;
-        __syncthreads();  // previous tile's readers done (and W written)
-        for (int idx = tid; idx < RT * (DINP / 8); idx += 256) {
-            const int r = idx / (DINP / 8), cg = idx % (DINP / 8);
-            uint4 val = make_uint4(0, 0, 0, 0);
-            if (r0 + r < p.rows && cg * 8 < din)
-                val = *reinterpret_cast<const uint4*>(p.x + (r0 + r) * din + cg * 8);
-            *reinterpret_cast<uint4*>(Xs + r * XS + cg * 8) = val;
+    const int64_t n_slabs = (p.rows + 15) / 16;
+    const int64_t stride = (int64_t)gridDim.x * 4;
+    // x[row][ks*32 + 8g .. +7] (zero past d_in or past the last row)
+    auto load_x = [&](int64_t slab, uint4 (&u)[NKS]) {
+        const int64_t row = slab * 16 + l16;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            u[ks] = make_uint4(0, 0, 0, 0);
+            if (row < p.rows && ks * 32 + g * 8 < din) u[ks] = *reinterpret_cast<const uint4*>(p.x + row * din + ks * 32 + g * 8);
         }
-        __syncthreads();
-        if (tid < RT) {
-            float acc = 0.f;
-            for (int c = 0; c < DINP; ++c) {
-                const float xv = bf2f(Xs[tid * XS + c]);
-                acc += xv * xv;
-            }
-            half_sq[tid] = 0.5f * s * s * acc;
+    };
+    // the staged 16 x m bf16 block of this slab to rows slab*16.. of dst
+    const int segs = m / 8;  // 16-byte pieces per row
+    auto store_staged = [&](int64_t slab, u16* dst) {
+        for (int e = lane; e < 16 * segs; e += WAVE) {
+            const int r = e / segs, sg = e % segs;
+            const int64_t row = slab * 16 + r;
+            const uint4 val = *reinterpret_cast<const uint4*>(ys + r * YS + sg * 8);
+            if (row < p.rows) *reinterpret_cast<uint4*>(dst + row * m + sg * 8) = val;
         }
-        __syncthreads();
-        // wave w: rows 16w .. 16w+15, all m features
-        bf16x8 a[NKS];
+    };
+
+    int64_t slab = (int64_t)blockIdx.x * 4 + wave;
+    uint4 xn[NKS];
+    if (slab < n_slabs) load_x(slab, xn);
+    for (; slab < n_slabs; slab += stride) {
+        uint4 xc[NKS];
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-            a[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(Xs + (wave * 16 + l16) * XS + ks * 32 + g * 8));
-        for (int nb = 0; nb < m / 16; ++nb) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int ks = 0; ks < NKS; ++ks) xc[ks] = xn[ks];
+        if (slab + stride < n_slabs) load_x(slab + stride, xn);
+        const int64_t row = slab * 16 + l16;
+        bf16x8 xb[NKS];
+        float sq = 0.f;
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                const bf16x8 b = as_bf16x8(*reinterpret_cast<const uint4*>(Ws + (nb * 16 + l16) * XS + ks * 32 + g * 8));
-                acc = mfma_bf16(a[ks], b, acc);
+        for (int ks = 0; ks < NKS; ++ks) {
+            const uint32_t w[4] = {xc[ks].x, xc[ks].y, xc[ks].z, xc[ks].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float a = __uint_as_float(w[j] << 16), b = __uint_as_float(w[j] & 0xFFFF0000u);
+                sq += a * a + b * b;
             }
-            // acc[i] = x[row 16w + 4g + i] . W[feature 16nb + l16]
-            const int feat = nb * 16 + l16;
+            xb[ks] = as_bf16x8(xc[ks]);
+        }
+        sq += __shfl_xor(sq, 16);
+        sq += __shfl_xor(sq, 32);
+        const float half_sq = 0.5f * s * s * sq;
+        // y for features 16 nb + 4g + i of row l16 (kept in registers: the
+        // residual pass reads them again)
+        constexpr int NBM = MMAX / 16;
+        float y[NBM][4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = wave * 16 + g * 4 + i;
-                if (r0 + r < p.rows) {
-                    const float y = __expf(s * acc[i] - half_sq[r]) * inv_sqrt_m;
-                    const int64_t off = (r0 + r) * m + feat;
-                    if (p.y_f32) {
-                        reinterpret_cast<float*>(p.y)[off] = y;
-                    } else {
-                        const u16 hb = f2bf(y);
-                        reinterpret_cast<u16*>(p.y)[off] = hb;
-                        if (p.y_lo != nullptr) p.y_lo[off] = f2bf(y - bf2f(hb));
-                    }
+        for (int nb = 0; nb < NBM; ++nb) {
+            if (nb < m / 16) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    const bf16x8 wb =
+                        as_bf16x8(*reinterpret_cast<const uint4*>(Ws + (nb * 16 + l16) * XS + ks * 32 + g * 8));
+                    acc = mfma_bf16(wb, xb[ks], acc);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) y[nb][i] = __expf(s * acc[i] - half_sq) * inv_sqrt_m;
+            }
+        }
+        if (p.y_f32) {
+#pragma unroll
+            for (int nb = 0; nb < NBM; ++nb)
+                if (nb < m / 16 && row < p.rows)
+                    *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.y) + row * m + nb * 16 + 4 * g) =
+                        make_float4(y[nb][0], y[nb][1], y[nb][2], y[nb][3]);
+            continue;
+        }
+        uint2 hb[NBM];
+#pragma unroll
+        for (int nb = 0; nb < NBM; ++nb) {
+            if (nb < m / 16) {
+                hb[nb] = make_uint2(pack2_bf16(y[nb][0], y[nb][1]), pack2_bf16(y[nb][2], y[nb][3]));
+                *reinterpret_cast<uint2*>(ys + l16 * YS + nb * 16 + 4 * g) = hb[nb];
+            }
+        }
+        store_staged(slab, reinterpret_cast<u16*>(p.y));
+        if (p.y_lo != nullptr) {
+            // residual y - bf16(y), so that hi + lo carries y to about 2^-17
+#pragma unroll
+            for (int nb = 0; nb < NBM; ++nb) {
+                if (nb < m / 16) {
+                    const uint2 h = hb[nb];
+                    *reinterpret_cast<uint2*>(ys + l16 * YS + nb * 16 + 4 * g) = make_uint2(
+                        pack2_bf16(y[nb][0] - __uint_as_float(h.x << 16), y[nb][1] - __uint_as_float(h.x & 0xFFFF0000u)),
+                        pack2_bf16(y[nb][2] - __uint_as_float(h.y << 16), y[nb][3] - __uint_as_float(h.y & 0xFFFF0000u)));
                 }
             }
+            store_staged(slab, p.y_lo);
         }
     }
 }
 
 hipError_t run_feature_map(const FmapParams& p, hipStream_t s) {
     if (p.fmap == 2) {
-        const int64_t n_tiles = (p.rows + 63) / 64;
-        const unsigned grid = (unsigned)(n_tiles < 2048 ? n_tiles : 2048);
+        // four 16-row slabs per workgroup and round; as many workgroups as fit
+        // the CUs at once (LDS: two per CU up to d_in = 64, one above), so W
+        // is loaded once per resident workgroup
         const int dinp = p.d_in <= 32 ? 32 : (p.d_in <= 64 ? 64 : 128);
+        const int64_t n_groups = (p.rows + 63) / 64;
+        const int64_t cap = dinp <= 64 ? 512 : 256;
+        const unsigned grid = (unsigned)(n_groups < cap ? n_groups : cap);
         switch (dinp) {
             case 32: hipLaunchKernelGGL(fmap_favor<32>, dim3(grid), dim3(256), 0, s, p); break;
             case 64: hipLaunchKernelGGL(fmap_favor<64>, dim3(grid), dim3(256), 0, s, p); break;
