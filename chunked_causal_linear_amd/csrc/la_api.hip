@@ -1,6 +1,7 @@
 // liblinattn C ABI: argument checks, planning (tile sizes, groups, workspace)
 // and launches.  Every entry point validates everything before it enqueues
 // anything, never allocates, never synchronises, and never throws.
+#include <algorithm>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -146,13 +147,16 @@ la_status make_plan(Plan& P, la_dtype in_dt, int64_t BH, int64_t L, int64_t d_in
     // workgroup per CU.  With a map it sums bf16(phi(k)) into its state; a
     // returned final state then comes from phase 1 (which adds phi(k)'s
     // residual) and the scan's total.
-    P.pipe = !P.i8 && P.causal && (Ce == 32 || Ce == 64 || Ce == 128) && d_v % 64 == 0 &&
-             (P.dk == 64 || P.dk == 128);
+    // At width 256 (FAVOR+ with 256 features) it takes 32 value columns per
+    // workgroup and chunks of 32 or 64 (two 68 KB stages).
+    P.pipe = !P.i8 && P.causal &&
+             (((Ce == 32 || Ce == 64 || Ce == 128) && d_v % 64 == 0 && (P.dk == 64 || P.dk == 128)) ||
+              ((Ce == 32 || Ce == 64) && d_v % 32 == 0 && P.dk == 256));
     P.final_from_scan = P.pipe && f != LA_FMAP_IDENTITY;
     P.premap = f == LA_FMAP_FAVOR;
     if (P.pipe) {
         P.DK = (int)P.dk;
-        P.DVT = 64;
+        P.DVT = P.dk == 256 ? 32 : 64;
         P.n_dvt = (int)(d_v / P.DVT);
     }
 
@@ -199,14 +203,17 @@ la_status make_plan(Plan& P, la_dtype in_dt, int64_t BH, int64_t L, int64_t d_in
     if (grid > 0x7FFFFFFFLL) return fail(LA_ERR_UNSUPPORTED, "grid too large");
 
     // Phase 1 sums each group's rows; a few long groups would leave most CUs
-    // idle, so each group's sum is split into `sub` pieces of >= 1024 rows
-    // until about 1024 workgroups run; the scan then walks the pieces and
-    // group g starts from the prefix at piece g * sub.
+    // idle, so each group's rows are split into `sub` equal pieces (of >= 512
+    // rows, each reading >= 8x the state it writes) until about 1024
+    // workgroups run; the scan then walks the pieces and group g starts from
+    // the prefix at piece g * sub.
     P.sub = 1;
     const int64_t n_summed = P.final_from_scan ? P.n_groups : P.n_groups - 1;  // groups phase 1 may sum
     if (P.causal && n_summed > 0) {
         const int64_t n_dvt1 = d_v / kernel_dvt(d_v);
-        while (P.G % (2 * P.sub) == 0 && P.G * P.C / (2 * P.sub) >= 1024 &&
+        // a piece reads at least eight times the state it writes
+        const int64_t min_rows = std::max<int64_t>(512, cdiv(16 * P.dk * d_v, P.dk + d_v));
+        while ((P.G * P.C) % (2 * P.sub) == 0 && P.G * P.C / (2 * P.sub) >= min_rows &&
                BH * n_summed * P.sub * n_dvt1 < 1024)
             P.sub *= 2;
     }

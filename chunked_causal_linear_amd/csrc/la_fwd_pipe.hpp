@@ -6,8 +6,10 @@
 // section ②: O_c = Q_c P + tril(Q_c K_c^T) V_c with the diagonal kept, then
 // P += K_c^T V_c), organised for HBM streaming.
 //
-// One workgroup: (head, group of chunks, tile of DVT = 64 value columns), four
-// waves, one per SIMD, in two pairs.  Pair h owns value columns [32h, 32h+32):
+// One workgroup: (head, group of chunks, tile of DVT = 64 value columns; 32 at
+// feature width 256, where the state of 64 columns would not fit the
+// registers), four waves, one per SIMD, in two pairs.  Pair h owns value
+// columns [h DVT/2, (h+1) DVT/2):
 //
 //  * compute wave h touches only LDS and the matrix cores: the scores of each
 //    chunk (S^T = K Q^T), the inter product Q P, the intra product tril(S) V and
@@ -178,9 +180,9 @@ void chunked_fwd_pipe(FwdParams p) {
     constexpr int NCV = TT * VSEG / WAVE / 2;      // the same for V (and for the output stores)
     constexpr int NL = 2 * NCQ + NCV;              // copy instructions per tile and copy wave
     constexpr int RPV = WAVE / VSEG;               // output rows per store instruction
-    static_assert(DVT == 64, "tile of 64 value columns");
+    static_assert(DVT == 64 || (DVT == 32 && DK == 256), "tile of 64 value columns (32 at feature width 256)");
     static_assert(CH == 32 || CH == 64 || CH == 128, "chunks of 32, 64 or 128 rows");
-    static_assert(DK == 64 || DK == 128, "feature width 64 or 128");
+    static_assert(DK == 64 || DK == 128 || DK == 256, "feature width 64, 128 or 256");
     static_assert(NL < 64, "vmcnt range");
     static_assert(NSTAGE * (int)sizeof(Stage<DK, DVT, TT>) <= 160 * 1024, "LDS");
     typedef Stage<DK, DVT, TT> StageT;

@@ -87,8 +87,9 @@ def test_workspace_sizes_and_errors():
     # chunks of 32 and 128 stream the same way: one group per head
     assert ws(b.LA_BF16, 128, 8192, 128, 128, 32, 1, 0, 0, 0, 1.0, 0) == 0
     assert ws(b.LA_BF16, 128, 8192, 128, 128, 128, 1, 0, 0, 0, 1.0, 0) == 0
-    # chunks of 48 (general kernel): four groups per (head, column tile)
-    assert ws(b.LA_BF16, 128, 8192, 128, 128, 48, 1, 0, 0, 0, 1.0, 0) == 128 * 4 * 128 * 128 * 4
+    # chunks of 48 (general kernel): four groups of 43 chunks per (head, column
+    # tile); phase 1 sums the first three in two pieces of 1032 rows each
+    assert ws(b.LA_BF16, 128, 8192, 128, 128, 48, 1, 0, 0, 0, 1.0, 0) == 128 * 4 * 2 * 128 * 128 * 4
     # chunks of 32 keep an even number per group on the streaming kernel
     assert lib.la_chunked_forward_group(b.LA_BF16, 2, 8192, 128, 128, 32, 1, 0, 0, 0, 0) % 2 == 0
     # groups: BH * n_groups * (dk*dv + dk) floats (normalised), 256-byte aligned pieces
@@ -101,7 +102,7 @@ def test_workspace_sizes_and_errors():
     # FAVOR+ with m = 64 (streaming kernel): three mapped copies in front
     n = ws(b.LA_BF16, 2, 1024, 64, 64, 64, 1, 1, 2, 64, 1.0, 4)
     assert n == 3 * 2 * 1024 * 64 * 2 + 2 * groups * 64 * 64 * 4 + 2 * groups * 64 * 4
-    # few long groups: phase 1 in pieces of >= 1024 rows, four per group here
+    # few long groups: phase 1 in pieces of >= 512 rows, four per group here
     # (32 heads x 8 groups x 4 pieces: with a map phase 1 also sums the last
     # group, whose total is the returned final state), every piece a state slot
     n = ws(b.LA_BF16, 32, 65536, 64, 64, 128, 1, 1, 1, 0, 1.0, 0)

@@ -109,7 +109,8 @@ def test_bf16_identity_chunks(C):
 @pytest.mark.parametrize("dk,dv,L,group,out", [(128, 128, 700, 0, "bf16"), (128, 128, 1024, 3, "f32"),
                                                (64, 64, 700, 4, "bf16"), (128, 256, 193, 0, "bf16"),
                                                (64, 128, 64, 0, "f32"), (128, 128, 2000, 1, "bf16"),
-                                               (128, 128, 130, 2, "bf16")])
+                                               (128, 128, 130, 2, "bf16"), (256, 64, 300, 0, "bf16"),
+                                               (256, 128, 500, 3, "bf16")])
 def test_bf16_chunk64_streaming(dk, dv, L, group, out):
     """Chunks of 64 with the identity map (the streaming kernel's cases): runs of
     many chunks per group, ragged tails, prefix states, both output types."""
@@ -149,7 +150,8 @@ def _positive(t):
     (64, 128, 128, 700, 2, "identity", 1.0), (128, 128, 64, 600, 0, "identity", 1.0),
     (32, 128, 64, 300, 0, "identity", 1.0), (64, 64, 64, 64, 0, "identity", 0.5),
     (128, 64, 128, 257, 2, "identity", 1.0), (64, 128, 128, 700, 0, "elu1", 1.0),
-    (128, 128, 64, 500, 2, "elu1", 1.0), (32, 128, 64, 333, 0, "elu1", 0.5)])
+    (128, 128, 64, 500, 2, "elu1", 1.0), (32, 128, 64, 333, 0, "elu1", 0.5),
+    (64, 256, 64, 400, 2, "elu1", 1.0), (32, 256, 32, 200, 0, "identity", 1.0)])
 def test_bf16_streaming_normalized(C, dk, dv, L, group, fmap, scale):
     """Normalised forwards on the streaming kernel: elu+1 (mapped in the kernel;
     the final state and normaliser from phase 1 with phi(k)'s residual and the
@@ -173,7 +175,7 @@ def test_bf16_streaming_normalized(C, dk, dv, L, group, fmap, scale):
     ("bf16", 64, 128, 128, 8192, 32, False, "identity"), ("bf16", 100, 64, 64, 5000, 24, False, "identity"),
     ("bf16", 32, 64, 128, 4500, 64, True, "elu1"), ("i8", 64, 64, 64, 4096, 32, False, "identity")])
 def test_long_groups_in_pieces(dtype, C, dk, dv, L, group, norm, fmap):
-    """Few long groups: phase 1 sums each group in pieces of >= 1024 rows, the
+    """Few long groups: phase 1 sums each group in pieces of >= 512 rows, the
     scan walks the pieces and every group starts from its piece's prefix."""
     q, k, v = _case(18, 2, L, dk, dv, dtype)
     log(f"{dtype} long groups C={C} dk={dk} dv={dv} L={L} group={group} norm={norm} fmap={fmap}")
@@ -261,10 +263,12 @@ def test_bf16_favor_small():
     assert_close(host(z), refz, what="favor z")
 
 
-@pytest.mark.parametrize("m,C,L,group", [(64, 64, 700, 0), (64, 32, 530, 3), (64, 128, 900, 2), (128, 64, 400, 2)])
+@pytest.mark.parametrize("m,C,L,group", [(64, 64, 700, 0), (64, 32, 530, 3), (64, 128, 900, 2), (128, 64, 400, 2),
+                                         (256, 64, 600, 2), (256, 32, 300, 0)])
 def test_bf16_favor_streaming(m, C, L, group):
-    """FAVOR+ with 64 or 128 features: mapped beforehand (phi(q), phi(k) and
-    phi(k)'s residual for phase 1), then the streaming kernel."""
+    """FAVOR+ with 64, 128 or 256 features: mapped beforehand (phi(q), phi(k)
+    and phi(k)'s residual for phase 1), then the streaming kernel (32 value
+    columns per workgroup at 256 features)."""
     q, k, v = _case(19, 2, L, 64, 64, "bf16", scale=1.0 / 8)
     Wb, W = wl.orthogonal_random_features(m, 64, [19, 3])
     log(f"bf16 favor m={m} C={C} L={L} group={group}")
