@@ -15,8 +15,9 @@ from two pages:
 * "Linear Attention / Performerの理論と実装" (disassemble-channel.com/
   linear-attention/), below called *the linear-attention page*: the kernel
   re-formulation with feature maps and normaliser, the RNN view (state S_t,
-  normaliser z_t), the elu+1 and FAVOR+ feature maps, and the recurrent and
-  materialised-prefix causal forms.
+  normaliser z_t, and the decayed recurrence it gives for Retention), the
+  elu+1 and FAVOR+ feature maps, and the recurrent and materialised-prefix
+  causal forms.
 
 Precision.  Floating-point inputs arrive as float64 arrays holding bf16 values
 (exact), and every form computes in float64 with no intermediate rounding.
@@ -351,6 +352,165 @@ def brute_force(q, k, v, causal: bool = True, normalize: bool = False):
 
 
 # ---------------------------------------------------------------------------
+# Retention decay (linear-attention page, RNN view, where forgetting is
+# introduced: S_t = gamma S_{t-1} + phi(k_t) v_t^T with 0 < gamma < 1).  The page
+# gives the state recurrence only; the normaliser is read as decaying the same
+# way, z_t = gamma z_{t-1} + phi(k_t), and the read stays y_t = phi(q_t) S_t
+# [/ phi(q_t) . z_t] after the update.  gamma = 1 is plain linear attention.
+# All of these compute in float64 (the decay weights are not integers).
+# ---------------------------------------------------------------------------
+def _f64(*arrays):
+    return tuple(np.asarray(a, dtype=np.float64) for a in arrays)
+
+
+def decay_weights(n_rows: int, n_cols: int, gamma: float) -> np.ndarray:
+    """D[i, j] = gamma^(i - j) where j <= i, else 0: the weight with which key j
+    reaches the read of query i (unrolling the recurrence i - j times)."""
+    e = np.arange(n_rows)[:, None] - np.arange(n_cols)[None, :]
+    return np.where(e >= 0, float(gamma) ** np.maximum(e, 0), 0.0)
+
+
+def decay_state_first(q, k, v, gamma: float, normalize: bool = False, S0=None, z0=None):
+    """The recurrence itself, token by token: S_t = gamma S_{t-1} + k_t^T v_t,
+    z_t = gamma z_{t-1} + k_t, then y_t = q_t S_t [/ q_t . z_t].  Returns
+    (out, S_L, z_L); S0/z0 continue from a given state (zero when omitted)."""
+    q, k, v = _f64(q, k, v)
+    L, dk = q.shape
+    dv = v.shape[1]
+    S = np.zeros((dk, dv)) if S0 is None else np.array(S0, dtype=np.float64)
+    z = np.zeros(dk) if z0 is None else np.array(z0, dtype=np.float64)
+    out = np.zeros((L, dv))
+    for t in range(L):
+        S = gamma * S + np.outer(k[t], v[t])
+        z = gamma * z + k[t]
+        num = q[t] @ S
+        out[t] = num / (q[t] @ z) if normalize else num
+    return out, S, z
+
+
+def decay_step(S, z, q_t, k_t, v_t, gamma: float, normalize: bool = True):
+    """One decode step of the decayed recurrence: S = gamma S + k^T v, z = gamma z
+    + k, then o = q S [/ q . z].  Returns (o, S', z')."""
+    S = gamma * np.asarray(S, dtype=np.float64) + np.outer(k_t, v_t)
+    z = gamma * np.asarray(z, dtype=np.float64) + k_t
+    num = q_t @ S
+    o = num / (q_t @ z) if normalize else num
+    return o, S, z
+
+
+def decay_scores_first(q, k, v, gamma: float, normalize: bool = False) -> np.ndarray:
+    """Unrolled recurrence as one L x L matrix: A = (q k^T) * D with D from
+    decay_weights; numerator A v; normalised: divide by the row sums of A."""
+    q, k, v = _f64(q, k, v)
+    A = (q @ k.T) * decay_weights(q.shape[0], k.shape[0], gamma)
+    num = A @ v
+    if not normalize:
+        return num
+    return _divide(num, A.sum(axis=1))
+
+
+def decay_chunked(q, k, v, C: int, gamma: float, normalize: bool = False):
+    """Chunkwise form of the decayed recurrence (C <= 0 is treated as 1).
+
+    Unrolling the recurrence inside a chunk [s, e) of n rows, with P the state
+    after row s - 1:  S_{s+i} = gamma^(i+1) P + sum_{j<=i} gamma^(i-j) k_{s+j}^T v_{s+j}.
+    So, for local rows i, j of the chunk:
+        inter  = gamma^(i+1) q_i P           (denominator: gamma^(i+1) q_i . z)
+        intra  = ((q_c k_c^T) * D) v_c       (denominator: row sums of (q_c k_c^T) * D)
+        P     <- gamma^n P + k_c^T diag(gamma^(n-1-j)) v_c
+        z     <- gamma^n z + sum_j gamma^(n-1-j) k_j
+    Returns (out, S_L, z_L)."""
+    if C <= 0:
+        C = 1
+    q, k, v = _f64(q, k, v)
+    L, dk = q.shape
+    dv = v.shape[1]
+    out = np.zeros((L, dv))
+    S = np.zeros((dk, dv))
+    z = np.zeros(dk)
+    for s in range(0, L, C):
+        e = min(s + C, L)
+        n = e - s
+        qc, kc, vc = q[s:e], k[s:e], v[s:e]
+        rows = np.arange(n)
+        g_in = float(gamma) ** (rows + 1)
+        g_out = float(gamma) ** (n - 1 - rows)
+        sc = (qc @ kc.T) * decay_weights(n, n, gamma)
+        num = g_in[:, None] * (qc @ S) + sc @ vc
+        if normalize:
+            den = g_in * (qc @ z) + sc.sum(axis=1)
+            out[s:e] = _divide(num, den)
+        else:
+            out[s:e] = num
+        S = float(gamma) ** n * S + kc.T @ (g_out[:, None] * vc)
+        z = float(gamma) ** n * z + (g_out[:, None] * kc).sum(axis=0)
+    return out, S, z
+
+
+def decay_chunk_states(k, v, C: int, gamma: float):
+    """Per-chunk states as they stand at each chunk's end: S_n = sum over the
+    chunk's rows j of gamma^(e-1-j) k_j^T v_j, z_n likewise; with the row count
+    of each chunk.  Returns (S [N, dk, dv], z [N, dk], lengths [N])."""
+    if C <= 0:
+        C = 1
+    kf, vf = _f64(k, v)
+    L, dk = kf.shape
+    N = (L + C - 1) // C
+    S = np.zeros((N, dk, vf.shape[1]))
+    z = np.zeros((N, dk))
+    lengths = np.zeros(N, dtype=np.int64)
+    for n in range(N):
+        s, e = n * C, min((n + 1) * C, L)
+        w = float(gamma) ** (e - 1 - np.arange(s, e))
+        S[n] = kf[s:e].T @ (w[:, None] * vf[s:e])
+        z[n] = (w[:, None] * kf[s:e]).sum(axis=0)
+        lengths[n] = e - s
+    return S, z, lengths
+
+
+def decay_exclusive_scan(S_n: np.ndarray, lengths, gamma: float):
+    """P_0 = 0, P_n = gamma^(len_{n-1}) P_{n-1} + S_{n-1}: the state after the rows
+    before chunk n; also the total after the last chunk (the final state)."""
+    Sf = np.asarray(S_n, dtype=np.float64)
+    P = np.zeros_like(Sf)
+    run = np.zeros(Sf.shape[1:])
+    for n in range(Sf.shape[0]):
+        P[n] = run
+        run = float(gamma) ** int(lengths[n]) * run + Sf[n]
+    return P, run
+
+
+def brute_force_decay(q, k, v, gamma, normalize: bool = False):
+    """o_{i,c} = sum_{j<=i} gamma^(i-j) sum_a q_{i,a} k_{j,a} v_{j,c}  [/ the same
+    without v], in exact Fractions (gamma given as a Fraction or an exact float)."""
+    def exact(x):
+        if isinstance(x, (int, np.integer)):
+            return Fraction(int(x))
+        return Fraction(float(x))
+
+    g = gamma if isinstance(gamma, Fraction) else Fraction(float(gamma))
+    L, dk = len(q), len(q[0])
+    dv = len(v[0])
+    out = []
+    for i in range(L):
+        row = []
+        den = Fraction(0)
+        for j in range(i + 1):
+            for a in range(dk):
+                den += g ** (i - j) * exact(q[i][a]) * exact(k[j][a])
+        for c in range(dv):
+            acc = Fraction(0)
+            for j in range(i + 1):
+                s = Fraction(0)
+                for a in range(dk):
+                    s += exact(q[i][a]) * exact(k[j][a])
+                acc += g ** (i - j) * s * exact(v[j][c])
+            row.append(acc / den if normalize else acc)
+        out.append(row)
+    return out
+
+
+# ---------------------------------------------------------------------------
 # mapping over heads
 # ---------------------------------------------------------------------------
 def over_heads(form: Callable, q, k, v, *args, **kwargs):
@@ -362,14 +522,19 @@ def over_heads(form: Callable, q, k, v, *args, **kwargs):
 
 
 def forward(q_raw, k_raw, v, C: int, causal: bool = True, normalize: bool = False,
-            fmap: str = "identity", W=None, in_scale: float = 1.0):
+            fmap: str = "identity", W=None, in_scale: float = 1.0, gamma: float = 1.0):
     """What the forward entry point returns for one head: (out, S_L, z_L).
 
-    phi is applied to q and k, then the chunked form (causal) or the
-    state-first form (non-causal, C ignored) gives the output.
+    phi is applied to q and k, then the chunked form (causal; with the decayed
+    recurrence when gamma != 1) or the state-first form (non-causal, C
+    ignored) gives the output.
     """
     qp = apply_phi(q_raw, fmap, W, in_scale) if (fmap != "identity" or in_scale != 1.0) else q_raw
     kp = apply_phi(k_raw, fmap, W, in_scale) if (fmap != "identity" or in_scale != 1.0) else k_raw
+    if gamma != 1.0:
+        if not causal:
+            raise ValueError("the decayed recurrence is causal")
+        return decay_chunked(qp, kp, v, C, gamma, normalize)
     if causal:
         return chunked(qp, kp, v, C, normalize)
     out = noncausal_state_first(qp, kp, v, normalize)

@@ -285,3 +285,145 @@ def check_favor_convergence(o) -> None:
     est_o = float(o.phi_favor(q, Wo) @ o.phi_favor(k, Wo))
     assert abs(est_o / target - 1) < 0.02, (est_o, target)
     assert np.all(o.phi_favor(rng.standard_normal((10, 4)), W[:64]) > 0)
+
+
+# ---------------------------------------------------------------------------
+# Retention decay (linear-attention page, RNN view: S_t = gamma S_{t-1} +
+# phi(k_t) v_t^T).  The recurrence is the definition; every other form is
+# pinned to it, to exact brute force and to closed forms.  gamma = 1/2 and 3/4
+# keep every weight a short binary fraction, so on small integers the float64
+# forms are exact and must agree bit for bit.
+# ---------------------------------------------------------------------------
+def check_decay_reduces_to_plain(o, seed: int = 30) -> None:
+    """gamma = 1 gives back plain linear attention in every form (exact on ints)."""
+    rng = np.random.default_rng([seed, 31])
+    L, dk, dv = 17, 3, 4
+    q, k, v = _ints(rng, (L, dk)), _ints(rng, (L, dk)), _ints(rng, (L, dv))
+    ref, S, z = o.causal_state_first(q, k, v)
+    out, Sd, zd = o.decay_state_first(q, k, v, 1.0)
+    assert np.array_equal(out, ref) and np.array_equal(Sd, S) and np.array_equal(zd, z)
+    assert np.array_equal(o.decay_scores_first(q, k, v, 1.0), ref)
+    for C in (1, 3, 5, 17, 20):
+        out, Sd, zd = o.decay_chunked(q, k, v, C, 1.0)
+        assert np.array_equal(out, ref) and np.array_equal(Sd, S) and np.array_equal(zd, z), C
+        Sn, zn, lens = o.decay_chunk_states(k, v, C, 1.0)
+        Sp, zp = o.chunk_states(k, v, C)
+        assert np.array_equal(Sn, Sp) and np.array_equal(zn, zp), C
+        P, tot = o.decay_exclusive_scan(Sn, lens, 1.0)
+        Pp, totp = o.exclusive_scan(Sp)
+        assert np.array_equal(P, Pp) and np.array_equal(tot, totp), C
+
+
+def check_decay_forms_exact(o, seed: int = 32) -> None:
+    """Dyadic gamma on small integers: the recurrence, the unrolled matrix form,
+    the chunked form at every C (0..L+1, non-divisors included) and exact
+    brute force agree exactly, normalised or not; the final states agree too."""
+    rng = np.random.default_rng([seed, 33])
+    L, dk, dv = 11, 2, 3
+    for gamma in (Fraction(1, 2), Fraction(3, 4)):
+        g = float(gamma)
+        q, k, v = _ints(rng, (L, dk)), _ints(rng, (L, dk)), _ints(rng, (L, dv))
+        ref, S, z = o.decay_state_first(q, k, v, g)
+        bf = _frac_matrix(o.brute_force_decay(q, k, v, gamma))
+        assert np.array_equal(ref, bf), gamma
+        assert np.array_equal(o.decay_scores_first(q, k, v, g), ref), gamma
+        for C in range(0, L + 2):
+            out, Sc, zc = o.decay_chunked(q, k, v, C, g)
+            assert np.array_equal(out, ref), (gamma, C)
+            assert np.array_equal(Sc, S) and np.array_equal(zc, z), (gamma, C)
+        # normalised, positive keys and queries (denominators away from zero)
+        qp, kp = np.abs(q) + 1, np.abs(k) + 1
+        refn = o.decay_state_first(qp, kp, v, g, True)[0]
+        bfn = _frac_matrix(o.brute_force_decay(qp, kp, v, gamma, True))
+        assert np.allclose(refn, bfn, rtol=1e-14, atol=0), gamma
+        assert np.allclose(o.decay_scores_first(qp, kp, v, g, True), refn, rtol=1e-14, atol=0)
+        for C in (1, 4, 7, L):
+            assert np.allclose(o.decay_chunked(qp, kp, v, C, g, True)[0], refn, rtol=1e-14, atol=0), (gamma, C)
+
+
+def check_decay_closed_forms(o) -> None:
+    """d = 1, q = k = v = 1: y_t = sum_{j<=t} gamma^(t-j) = (1 - gamma^(t+1)) / (1 - gamma)
+    (a geometric series), the final state is the same sum at t = L-1, the
+    normalised output is 1; and y_t changes by gamma^t (q_t . k_0) delta when
+    v_0 does (older tokens fade by one factor per step)."""
+    L, gamma = 40, 0.9
+    ones = np.ones((L, 1))
+    t = np.arange(L)
+    geo = (1 - gamma ** (t + 1)) / (1 - gamma)
+    for C in (1, 7, 16, L):
+        out, S, z = o.decay_chunked(ones, ones, ones, C, gamma)
+        assert np.allclose(out[:, 0], geo, rtol=1e-13, atol=0), C
+        assert np.allclose(S[0, 0], geo[-1], rtol=1e-13) and np.allclose(z[0], geo[-1], rtol=1e-13), C
+        outn = o.decay_chunked(ones, ones, ones, C, gamma, True)[0]
+        assert np.allclose(outn, 1.0, rtol=1e-14), C
+    rng = np.random.default_rng([34, 35])
+    q, k, v = _ints(rng, (12, 3)), _ints(rng, (12, 3)), _ints(rng, (12, 2))
+    v2 = v.copy()
+    v2[0, 1] += 4
+    d = o.decay_chunked(q, k, v2, 5, 0.5)[0] - o.decay_chunked(q, k, v, 5, 0.5)[0]
+    want = np.array([0.5 ** i * float(q[i] @ k[0]) * 4 for i in range(12)])
+    assert np.array_equal(d[:, 1], want) and np.array_equal(d[:, 0], np.zeros(12))
+
+
+def check_decay_phases(o, seed: int = 36) -> None:
+    """Per-chunk states at each chunk's end, their decayed exclusive prefix, and
+    the chunk output from the prefix reproduce the recurrence (exact, dyadic
+    gamma on integers); the scan's total is the final state."""
+    rng = np.random.default_rng([seed, 37])
+    L, dk, dv = 23, 3, 2
+    q, k, v = _ints(rng, (L, dk)), _ints(rng, (L, dk)), _ints(rng, (L, dv))
+    g = 0.5
+    ref, S, z = o.decay_state_first(q, k, v, g)
+    for C in (1, 4, 6, 23, 30):
+        Sn, zn, lens = o.decay_chunk_states(k, v, C, g)
+        N = (L + C - 1) // C
+        assert list(lens) == [min((n + 1) * C, L) - n * C for n in range(N)]
+        for n in range(N):
+            s, e = n * C, min((n + 1) * C, L)
+            want = sum(g ** (e - 1 - j) * np.outer(k[j], v[j]) for j in range(s, e))
+            assert np.array_equal(Sn[n], want), (C, n)
+        P, tot = o.decay_exclusive_scan(Sn, lens, g)
+        Pz, totz = o.decay_exclusive_scan(zn, lens, g)
+        assert np.array_equal(tot, S) and np.array_equal(totz, z), C
+        for n in range(N):
+            s, e = n * C, min((n + 1) * C, L)
+            rows = np.arange(e - s)
+            blk = (g ** (rows + 1))[:, None] * (q[s:e] @ P[n]) + \
+                ((q[s:e] @ k[s:e].T) * o.decay_weights(e - s, e - s, g)) @ v[s:e]
+            assert np.array_equal(blk, ref[s:e]), (C, n)
+            # the prefix is the recurrence's state after row s - 1
+            Ps = o.decay_state_first(q[:s], k[:s], v[:s], g)[1] if s > 0 else np.zeros((dk, dv))
+            assert np.array_equal(P[n], Ps) and np.array_equal(Pz[n], o.decay_state_first(q[:s], k[:s], v[:s], g)[2] if s > 0 else np.zeros(dk))
+
+
+def check_decay_resume(o, seed: int = 38) -> None:
+    """The decayed forward over L1 tokens, then decode steps from its final
+    state, equals the forward over all L tokens (normalised, elu+1 features)."""
+    rng = np.random.default_rng([seed, 39])
+    L, L1, dk, dv = 21, 12, 3, 4
+    for gamma in (0.5, 0.93):
+        qf, kf, vf = o.phi_elu1(_bf16(rng, (L, dk))), o.phi_elu1(_bf16(rng, (L, dk))), _bf16(rng, (L, dv))
+        full = o.decay_chunked(qf, kf, vf, 5, gamma, True)[0]
+        _, S, z = o.decay_chunked(qf[:L1], kf[:L1], vf[:L1], 5, gamma, True)
+        for t in range(L1, L):
+            ot, S, z = o.decay_step(S, z, qf[t], kf[t], vf[t], gamma, True)
+            assert np.allclose(ot, full[t], rtol=1e-12, atol=1e-14), (gamma, t)
+        fullu = o.decay_chunked(qf, kf, vf, 4, gamma)[0]
+        _, S, z = o.decay_chunked(qf[:L1], kf[:L1], vf[:L1], 4, gamma)
+        for t in range(L1, L):
+            ot, S, z = o.decay_step(S, z, qf[t], kf[t], vf[t], gamma, False)
+            assert np.allclose(ot, fullu[t], rtol=1e-12, atol=1e-14), (gamma, t)
+
+
+def check_decay_forward(o, seed: int = 40) -> None:
+    """The forward entry point's reference with a decay: phi applied first, then
+    the decayed recurrence (out, final state, final normaliser)."""
+    rng = np.random.default_rng([seed, 41])
+    L, dk, dv = 19, 4, 3
+    q, k, v = _bf16(rng, (L, dk)), _bf16(rng, (L, dk)), _bf16(rng, (L, dv))
+    for fmap, norm in (("identity", False), ("elu1", True)):
+        out, S, z = o.forward(q, k, v, 5, True, norm, fmap, None, 1.0, 0.75)
+        qp, kp = (q, k) if fmap == "identity" else (o.phi_elu1(q), o.phi_elu1(k))
+        ref, Sr, zr = o.decay_state_first(qp, kp, v, 0.75, norm)
+        assert np.allclose(out, ref, rtol=1e-12, atol=1e-14) and np.allclose(S, Sr, rtol=1e-12, atol=1e-14)
+        assert np.allclose(z, zr, rtol=1e-12, atol=1e-14)

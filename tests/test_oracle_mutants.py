@@ -53,6 +53,32 @@ MUTANTS = {
     "noncausal_scores_transposed": ("    A = q @ k.T\n", "    A = (q @ k.T).T\n"),
     "final_state_no_z": ("_finish(kf.sum(axis=0), integer)", "_finish(kf.sum(axis=0) * 0, integer)"),
     "brute_force_exclusive": ("last = i if causal else L - 1", "last = i - 1 if causal else L - 1"),
+    # the decayed recurrence
+    "decay_weights_transposed": ("e = np.arange(n_rows)[:, None] - np.arange(n_cols)[None, :]",
+                                 "e = np.arange(n_cols)[None, :] - np.arange(n_rows)[:, None]"),
+    "decay_weights_off_by_one": ("float(gamma) ** np.maximum(e, 0), 0.0)", "float(gamma) ** np.maximum(e + 1, 0), 0.0)"),
+    "decay_recurrence_decays_input": ("        S = gamma * S + np.outer(k[t], v[t])\n",
+                                      "        S = gamma * (S + np.outer(k[t], v[t]))\n"),
+    "decay_recurrence_z_not_decayed": ("        z = gamma * z + k[t]\n", "        z = z + k[t]\n"),
+    "decay_step_no_decay": ("S = gamma * np.asarray(S, dtype=np.float64) + np.outer(k_t, v_t)",
+                            "S = np.asarray(S, dtype=np.float64) + np.outer(k_t, v_t)"),
+    "decay_step_z_not_decayed": ("z = gamma * np.asarray(z, dtype=np.float64) + k_t",
+                                 "z = np.asarray(z, dtype=np.float64) + k_t"),
+    "decay_chunked_inter_exponent": ("g_in = float(gamma) ** (rows + 1)", "g_in = float(gamma) ** rows"),
+    "decay_chunked_out_weight": ("g_out = float(gamma) ** (n - 1 - rows)", "g_out = float(gamma) ** (n - rows)"),
+    "decay_chunked_carry_full_chunk": ("S = float(gamma) ** n * S + kc.T @ (g_out[:, None] * vc)",
+                                       "S = float(gamma) ** C * S + kc.T @ (g_out[:, None] * vc)"),
+    "decay_chunked_z_carry": ("z = float(gamma) ** n * z + (g_out[:, None] * kc).sum(axis=0)",
+                              "z = z + (g_out[:, None] * kc).sum(axis=0)"),
+    "decay_chunked_den_no_decay": ("den = g_in * (qc @ z) + sc.sum(axis=1)", "den = (qc @ z) + sc.sum(axis=1)"),
+    "decay_chunk_states_weight": ("w = float(gamma) ** (e - 1 - np.arange(s, e))", "w = float(gamma) ** (e - np.arange(s, e))"),
+    "decay_scan_length_index": ("run = float(gamma) ** int(lengths[n]) * run + Sf[n]",
+                                "run = float(gamma) ** int(lengths[n - 1]) * run + Sf[n]"),
+    "decay_scan_inclusive": ("        P[n] = run\n        run = float(gamma)",
+                             "        P[n] = float(gamma) ** int(lengths[n]) * run + Sf[n]\n        run = float(gamma)"),
+    "brute_force_decay_exponent": ("acc += g ** (i - j) * s * exact(v[j][c])", "acc += g ** (i - j + 1) * s * exact(v[j][c])"),
+    "forward_ignores_gamma": ("        return decay_chunked(qp, kp, v, C, gamma, normalize)",
+                              "        return chunked(qp, kp, v, C, normalize)"),
 }
 
 CHECKS = [getattr(pins, n) for n in dir(pins) if n.startswith("check_")]

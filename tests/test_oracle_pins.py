@@ -61,3 +61,27 @@ def test_favor_closed_form():
 
 def test_favor_convergence():
     pins.check_favor_convergence(oracle)
+
+
+def test_decay_reduces_to_plain():
+    pins.check_decay_reduces_to_plain(oracle)
+
+
+def test_decay_forms_exact():
+    pins.check_decay_forms_exact(oracle)
+
+
+def test_decay_closed_forms():
+    pins.check_decay_closed_forms(oracle)
+
+
+def test_decay_phases():
+    pins.check_decay_phases(oracle)
+
+
+def test_decay_resume():
+    pins.check_decay_resume(oracle)
+
+
+def test_decay_forward():
+    pins.check_decay_forward(oracle)
