@@ -26,7 +26,8 @@ FMAPS = {"identity": 0, "elu1": 1, "favor": 2}
 EXPORTS = (
     "la_feature_map", "la_chunk_states", "la_state_scan", "la_chunk_output", "la_chunked_forward",
     "la_chunked_forward_workspace", "la_chunked_forward_group", "la_recurrent_step", "la_status_string", "la_last_error",
-    "la_version",
+    "la_version", "la_chunk_states_decay", "la_state_scan_decay", "la_chunk_output_decay", "la_chunked_forward_decay",
+    "la_recurrent_step_decay",
 )
 
 
@@ -56,8 +57,18 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.la_chunked_forward_group.argtypes = [i32, i64, i64, i64, i64, i64, i32, i32, i32, i64, i64]
     lib.la_chunked_forward_group.restype = i64
     lib.la_recurrent_step.argtypes = [vp, vp, vp, i32, i64, i64, i64, i32, vp, i64, f32, i32, vp, vp, vp, i32, vp]
+    # the decayed recurrence: the same arguments with gamma
+    lib.la_chunk_states_decay.argtypes = [vp, vp, i32, i64, i64, i64, i64, i64, f32, vp, vp, vp]
+    lib.la_state_scan_decay.argtypes = [vp, vp, i32, i64, i64, i64, i64, i64, i64, f32, vp, vp, vp]
+    lib.la_chunk_output_decay.argtypes = [vp, vp, vp, i32, i64, i64, i64, i64, i64, i64, vp, vp, i32, f32, vp, i32,
+                                          vp, vp, vp]
+    lib.la_chunked_forward_decay.argtypes = [vp, vp, vp, i32, i64, i64, i64, i64, i64, i32, i32, vp, i64, f32, f32,
+                                             vp, i32, vp, vp, i64, vp, sz, vp]
+    lib.la_recurrent_step_decay.argtypes = [vp, vp, vp, i32, i64, i64, i64, i32, vp, i64, f32, i32, f32, vp, vp, vp,
+                                            i32, vp]
     for name in ("la_feature_map", "la_chunk_states", "la_state_scan", "la_chunk_output", "la_chunked_forward",
-                 "la_recurrent_step"):
+                 "la_recurrent_step", "la_chunk_states_decay", "la_state_scan_decay", "la_chunk_output_decay",
+                 "la_chunked_forward_decay", "la_recurrent_step_decay"):
         getattr(lib, name).restype = i32
     lib.la_status_string.argtypes = [i32]
     lib.la_status_string.restype = ctypes.c_char_p
@@ -145,8 +156,9 @@ def feature_map(x, fmap: str, W=None, in_scale: float = 1.0, out_dtype=None, out
     return y
 
 
-def chunk_states(k, v, C: int, want_z: bool = False, out=None):
-    """Phase 1: per-chunk states S [BH, N, d_k, d_v] (and z [BH, N, d_k]); `out` = S to reuse."""
+def chunk_states(k, v, C: int, want_z: bool = False, out=None, gamma: float = 1.0):
+    """Phase 1: per-chunk states S [BH, N, d_k, d_v] (and z [BH, N, d_k]); `out` = S to reuse.
+    gamma != 1: the decayed recurrence's states at each chunk's end."""
     torch = _torch()
     BH, L, d_k = k.shape
     d_v = v.shape[-1]
@@ -157,25 +169,34 @@ def chunk_states(k, v, C: int, want_z: bool = False, out=None):
     if tuple(S.shape) != (BH, N, d_k, d_v) or S.dtype != st:
         raise ValueError(f"out must be {(BH, N, d_k, d_v)} {st}")
     z = torch.empty(BH, N, d_k, dtype=st, device=k.device) if want_z else None
-    _check(lib().la_chunk_states(_dev(k, "k"), _dev(v, "v"), _dtype_code(k), BH, L, d_k, d_v, C,
-                                 _dev(S, "S"), _dev(z, "z"), _stream_ptr()))
+    if gamma != 1.0:
+        _check(lib().la_chunk_states_decay(_dev(k, "k"), _dev(v, "v"), _dtype_code(k), BH, L, d_k, d_v, C,
+                                           float(gamma), _dev(S, "S"), _dev(z, "z"), _stream_ptr()))
+    else:
+        _check(lib().la_chunk_states(_dev(k, "k"), _dev(v, "v"), _dtype_code(k), BH, L, d_k, d_v, C,
+                                     _dev(S, "S"), _dev(z, "z"), _stream_ptr()))
     return S, z
 
 
-def state_scan(S, z=None, want_final: bool = True):
-    """Phase 2, in place: S (and z) become exclusive prefixes; returns (S_final, z_final)."""
+def state_scan(S, z=None, want_final: bool = True, gamma: float = 1.0, L: int = 0, C: int = 0):
+    """Phase 2, in place: S (and z) become exclusive prefixes; returns (S_final, z_final).
+    gamma != 1: the decayed prefix over chunks of C rows of an L-row sequence."""
     torch = _torch()
     BH, N, d_k, d_v = S.shape
     Sf = torch.empty(BH, d_k, d_v, dtype=S.dtype, device=S.device) if want_final else None
     zf = torch.empty(BH, d_k, dtype=S.dtype, device=S.device) if (want_final and z is not None) else None
-    _check(lib().la_state_scan(_dev(S, "S"), _dev(z, "z"), _dtype_code(S), BH, N, d_k, d_v,
-                               _dev(Sf, "S_final"), _dev(zf, "z_final"), _stream_ptr()))
+    if gamma != 1.0:
+        _check(lib().la_state_scan_decay(_dev(S, "S"), _dev(z, "z"), _dtype_code(S), BH, N, d_k, d_v, L, C,
+                                         float(gamma), _dev(Sf, "S_final"), _dev(zf, "z_final"), _stream_ptr()))
+    else:
+        _check(lib().la_state_scan(_dev(S, "S"), _dev(z, "z"), _dtype_code(S), BH, N, d_k, d_v,
+                                   _dev(Sf, "S_final"), _dev(zf, "z_final"), _stream_ptr()))
     return Sf, zf
 
 
 def chunk_output(q, k, v, C: int, group: int, P_prefix=None, z_prefix=None, normalize: bool = False,
-                 out_dtype=None, return_state: bool = False, out=None):
-    """Phase 3 alone from group prefix states (see la_chunk_output)."""
+                 out_dtype=None, return_state: bool = False, out=None, gamma: float = 1.0):
+    """Phase 3 alone from group prefix states (see la_chunk_output; gamma != 1: la_chunk_output_decay)."""
     torch = _torch()
     BH, L, d_k = q.shape
     d_v = v.shape[-1]
@@ -185,10 +206,16 @@ def chunk_output(q, k, v, C: int, group: int, P_prefix=None, z_prefix=None, norm
     st = torch.int32 if i8 else torch.float32
     Sf = torch.empty(BH, d_k, d_v, dtype=st, device=q.device) if return_state else None
     zf = torch.empty(BH, d_k, dtype=torch.float32, device=q.device) if (return_state and normalize) else None
-    _check(lib().la_chunk_output(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dtype_code(q), BH, L, d_k, d_v, C,
-                                 group, _dev(P_prefix, "P_prefix"), _dev(z_prefix, "z_prefix"), int(normalize),
-                                 _dev(out, "o"), _dtype_code(out), _dev(Sf, "S_final"), _dev(zf, "z_final"),
-                                 _stream_ptr()))
+    if gamma != 1.0:
+        _check(lib().la_chunk_output_decay(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dtype_code(q), BH, L, d_k,
+                                           d_v, C, group, _dev(P_prefix, "P_prefix"), _dev(z_prefix, "z_prefix"),
+                                           int(normalize), float(gamma), _dev(out, "o"), _dtype_code(out),
+                                           _dev(Sf, "S_final"), _dev(zf, "z_final"), _stream_ptr()))
+    else:
+        _check(lib().la_chunk_output(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dtype_code(q), BH, L, d_k, d_v, C,
+                                     group, _dev(P_prefix, "P_prefix"), _dev(z_prefix, "z_prefix"), int(normalize),
+                                     _dev(out, "o"), _dtype_code(out), _dev(Sf, "S_final"), _dev(zf, "z_final"),
+                                     _stream_ptr()))
     if return_state:
         return out, Sf, zf
     return out
@@ -215,8 +242,10 @@ class Forward:
     """
 
     def __init__(self, q, k, v, C: int, causal: bool = True, normalize: bool = False, fmap: str = "identity",
-                 W=None, in_scale: float = 1.0, out_dtype=None, return_state: bool = False, group: int = 0):
+                 W=None, in_scale: float = 1.0, out_dtype=None, return_state: bool = False, group: int = 0,
+                 gamma: float = 1.0):
         torch = _torch()
+        self.gamma = float(gamma)
         self.q, self.k, self.v, self.W = q, k, v, W
         BH, L, d_in = q.shape
         d_v = v.shape[-1]
@@ -242,6 +271,18 @@ class Forward:
 
     def run(self):
         BH, L, d_in, d_v, _ = self.shape
+        if self.gamma != 1.0:
+            if not self.causal:
+                raise ValueError("the decayed recurrence is causal")
+            _check(lib().la_chunked_forward_decay(
+                self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), _dtype_code(self.q), BH, L, d_in, d_v,
+                self.C, int(self.normalize), _fmap_code(self.fmap),
+                self.W.data_ptr() if self.W is not None else None, self.m, self.in_scale, self.gamma,
+                self.o.data_ptr(), _dtype_code(self.o),
+                self.S_final.data_ptr() if self.S_final is not None else None,
+                self.z_final.data_ptr() if self.z_final is not None else None,
+                self.group, self.workspace.data_ptr(), self.ws_bytes, _stream_ptr()))
+            return self.o
         _check(lib().la_chunked_forward(
             self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), _dtype_code(self.q), BH, L, d_in, d_v,
             self.C, int(self.causal), int(self.normalize), _fmap_code(self.fmap),
@@ -255,9 +296,10 @@ class Forward:
 
 def chunked_forward(q, k, v, C: int, causal: bool = True, normalize: bool = False, fmap: str = "identity",
                     W=None, in_scale: float = 1.0, out_dtype=None, return_state: bool = False,
-                    group: int = 0) -> Tuple:
-    """O (and, with return_state, the final S and z) of the chunked forward."""
-    f = Forward(q, k, v, C, causal, normalize, fmap, W, in_scale, out_dtype, return_state, group)
+                    group: int = 0, gamma: float = 1.0) -> Tuple:
+    """O (and, with return_state, the final S and z) of the chunked forward (gamma != 1: the decayed
+    recurrence, la_chunked_forward_decay)."""
+    f = Forward(q, k, v, C, causal, normalize, fmap, W, in_scale, out_dtype, return_state, group, gamma)
     o = f.run()
     if return_state:
         return o, f.S_final, f.z_final
@@ -265,15 +307,22 @@ def chunked_forward(q, k, v, C: int, causal: bool = True, normalize: bool = Fals
 
 
 def recurrent_step(q, k, v, S, z=None, fmap: str = "identity", W=None, in_scale: float = 1.0,
-                   normalize: bool = True, out=None):
-    """One decode step over n states; S [n, d_k, d_v] and z [n, d_k] (fp32) update in place."""
+                   normalize: bool = True, out=None, gamma: float = 1.0):
+    """One decode step over n states; S [n, d_k, d_v] and z [n, d_k] (fp32) update in place
+    (gamma != 1: S = gamma S + phi(k) v^T, la_recurrent_step_decay)."""
     torch = _torch()
     n, d_in = q.shape
     d_v = v.shape[-1]
     m = W.shape[0] if (fmap == "favor" and W is not None) else 0
     if out is None:
         out = torch.empty(n, d_v, dtype=torch.float32, device=q.device)
-    _check(lib().la_recurrent_step(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dtype_code(q), n, d_in, d_v,
-                                   _fmap_code(fmap), _dev(W, "W"), m, float(in_scale), int(normalize),
-                                   _dev(S, "S"), _dev(z, "z"), _dev(out, "o"), _dtype_code(out), _stream_ptr()))
+    if gamma != 1.0:
+        _check(lib().la_recurrent_step_decay(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dtype_code(q), n, d_in,
+                                             d_v, _fmap_code(fmap), _dev(W, "W"), m, float(in_scale),
+                                             int(normalize), float(gamma), _dev(S, "S"), _dev(z, "z"),
+                                             _dev(out, "o"), _dtype_code(out), _stream_ptr()))
+    else:
+        _check(lib().la_recurrent_step(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dtype_code(q), n, d_in, d_v,
+                                       _fmap_code(fmap), _dev(W, "W"), m, float(in_scale), int(normalize),
+                                       _dev(S, "S"), _dev(z, "z"), _dev(out, "o"), _dtype_code(out), _stream_ptr()))
     return out

@@ -33,7 +33,9 @@ CFLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-I" + INCLUDE
 
 # Per-file flags.  The streaming kernel keeps its matrix-core accumulators in
 # ordinary VGPRs (it runs one wave per SIMD, so all 512 registers are there),
-# which saves the copies out of accumulation registers before every pack.
+# which saves the copies out of accumulation registers before every pack.  Its
+# decayed variants are built without it (that form fails to compile at the
+# register pressure of the largest of them).
 FILE_FLAGS = {"la_pipe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 

@@ -2,6 +2,7 @@
 // and launches.  Every entry point validates everything before it enqueues
 // anything, never allocates, never synchronises, and never throws.
 #include <algorithm>
+#include <cmath>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -243,7 +244,7 @@ bool xcd_ok(int64_t grid) { return grid >= 8 && grid % 8 == 0; }
 static la_status launch_phase3(const Plan& P, const void* qm, const void* km, const void* klo, const void* v,
                                void* o, la_dtype out_dt, const void* states, const void* zst, void* S_final,
                                void* z_final, int fmap_in_kernel, float in_scale, bool scaled_identity,
-                               hipStream_t s) {
+                               hipStream_t s, float lg = 0.0f) {
     const int64_t BH = P.BH, L = P.L, d_v = P.dv;
     const int64_t grid = BH * P.n_groups * P.n_dvt;
     if (P.i8) {
@@ -292,6 +293,9 @@ static la_status launch_phase3(const Plan& P, const void* qm, const void* km, co
     p.out_scale = (scaled_identity && !P.normalize) ? in_scale * in_scale : 1.0f;
     p.state_scale = scaled_identity ? in_scale : 1.0f;
     p.p0_sub = (int)P.sub;
+    p.log2_gamma = lg;
+    if (lg != 0.0f && !(P.pipe && out_dt == LA_BF16))
+        return fail(LA_ERR_UNSUPPORTED, "the decayed recurrence needs the streaming kernel and bf16 output");
     if (P.final_from_scan) {
         p.S_final = nullptr;
         p.z_final = nullptr;
@@ -373,7 +377,7 @@ la_status la_feature_map(la_fmap f, const void* x, la_dtype xdt, int64_t rows, i
 // ---------------------------------------------------------------------------
 static la_status chunk_states_impl(const void* k, const void* v, bool i8, int64_t BH, int64_t L, int64_t d_k,
                                    int64_t d_v, int64_t Cs, int n_items, int n_out, void* S, void* z, int fmap,
-                                   float in_scale, hipStream_t s, const void* k_lo = nullptr) {
+                                   float in_scale, hipStream_t s, const void* k_lo = nullptr, float lg = 0.0f) {
     const int DVT = kernel_dvt(d_v);
     const int n_dvt = (int)(d_v / DVT);
     const int64_t grid = BH * (int64_t)n_items * n_dvt;
@@ -412,6 +416,7 @@ static la_status chunk_states_impl(const void* k, const void* v, bool i8, int64_
     p.in_scale = in_scale;
     p.want_z = z != nullptr;
     p.xcd_remap = xcd_ok(grid);
+    p.log2_gamma = lg;
     hipError_t e;
     switch (kernel_dk_bf16(d_k)) {
         case 32: e = la::states_bf16_dk32(p, DVT, grid, s); break;
@@ -422,9 +427,16 @@ static la_status chunk_states_impl(const void* k, const void* v, bool i8, int64_
     return hip_status(e, "chunk states launch");
 }
 
-la_status la_chunk_states(const void* k, const void* v, la_dtype in_dt, int64_t BH, int64_t L, int64_t d_k,
-                          int64_t d_v, int64_t C, void* S, void* z, la_stream_t stream) {
-    g_last_error[0] = 0;
+static la_status check_gamma(float gamma) {
+    if (!(gamma > 0.0f && gamma <= 1.0f)) return fail(LA_ERR_INVALID_ARG, "gamma must lie in (0, 1], got %g", (double)gamma);
+    return LA_OK;
+}
+
+static float log2_of(float gamma) { return gamma == 1.0f ? 0.0f : (float)std::log2((double)gamma); }
+
+static la_status chunk_states_entry(const void* k, const void* v, la_dtype in_dt, int64_t BH, int64_t L,
+                                    int64_t d_k, int64_t d_v, int64_t C, void* S, void* z, float gamma,
+                                    la_stream_t stream) {
     if (k == nullptr || v == nullptr || S == nullptr) return fail(LA_ERR_INVALID_ARG, "k, v and S must not be NULL");
     if (BH < 1 || L < 1) return fail(LA_ERR_INVALID_ARG, "BH and L must be positive");
     if (in_dt != LA_BF16 && in_dt != LA_I8) return fail(LA_ERR_UNSUPPORTED, "input type must be LA_BF16 or LA_I8");
@@ -433,14 +445,29 @@ la_status la_chunk_states(const void* k, const void* v, la_dtype in_dt, int64_t 
     const int64_t Cs = C <= 0 ? 1 : (C > L ? L : C);
     const int64_t N = cdiv(L, Cs);
     if (N > 0x7FFFFFFFLL) return fail(LA_ERR_UNSUPPORTED, "too many chunks");
+    if (gamma != 1.0f && in_dt != LA_BF16) return fail(LA_ERR_UNSUPPORTED, "the decayed recurrence needs LA_BF16 inputs");
     return chunk_states_impl(k, v, in_dt == LA_I8, BH, L, d_k, d_v, Cs, (int)N, (int)N, S, z, la::FMAP_NONE, 1.0f,
-                             (hipStream_t)stream);
+                             (hipStream_t)stream, nullptr, log2_of(gamma));
+}
+
+la_status la_chunk_states(const void* k, const void* v, la_dtype in_dt, int64_t BH, int64_t L, int64_t d_k,
+                          int64_t d_v, int64_t C, void* S, void* z, la_stream_t stream) {
+    g_last_error[0] = 0;
+    return chunk_states_entry(k, v, in_dt, BH, L, d_k, d_v, C, S, z, 1.0f, stream);
+}
+
+la_status la_chunk_states_decay(const void* k, const void* v, la_dtype in_dt, int64_t BH, int64_t L, int64_t d_k,
+                                int64_t d_v, int64_t C, float gamma, void* S, void* z, la_stream_t stream) {
+    g_last_error[0] = 0;
+    const la_status st = check_gamma(gamma);
+    if (st != LA_OK) return st;
+    return chunk_states_entry(k, v, in_dt, BH, L, d_k, d_v, C, S, z, gamma, stream);
 }
 
 // ---------------------------------------------------------------------------
-la_status la_state_scan(void* S, void* z, la_dtype st_dt, int64_t BH, int64_t N, int64_t d_k, int64_t d_v,
-                        void* S_final, void* z_final, la_stream_t stream) {
-    g_last_error[0] = 0;
+static la_status state_scan_entry(void* S, void* z, la_dtype st_dt, int64_t BH, int64_t N, int64_t d_k,
+                                  int64_t d_v, int64_t L, int64_t C, float gamma, void* S_final, void* z_final,
+                                  la_stream_t stream) {
     if (S == nullptr) return fail(LA_ERR_INVALID_ARG, "S must not be NULL");
     if (BH < 1 || N < 1) return fail(LA_ERR_INVALID_ARG, "BH and N must be positive");
     if (st_dt != LA_F32 && st_dt != LA_I32) return fail(LA_ERR_UNSUPPORTED, "state type must be LA_F32 or LA_I32");
@@ -456,7 +483,30 @@ la_status la_state_scan(void* S, void* z, la_dtype st_dt, int64_t BH, int64_t N,
     p.E = d_k * d_v;
     p.Ez = d_k;
     p.is_int = st_dt == LA_I32;
+    if (gamma != 1.0f) {
+        if (st_dt != LA_F32) return fail(LA_ERR_UNSUPPORTED, "the decayed prefix needs LA_F32 states");
+        if (L < 1) return fail(LA_ERR_INVALID_ARG, "L must be positive");
+        const int64_t Cs = C <= 0 ? 1 : (C > L ? L : C);
+        if (cdiv(L, Cs) != N) return fail(LA_ERR_INVALID_ARG, "N must be ceil(L / C)");
+        p.log2_gamma = log2_of(gamma);
+        p.L = L;
+        p.Cs = Cs;
+    }
     return hip_status(la::run_state_scan(p, BH, (hipStream_t)stream), "state scan launch");
+}
+
+la_status la_state_scan(void* S, void* z, la_dtype st_dt, int64_t BH, int64_t N, int64_t d_k, int64_t d_v,
+                        void* S_final, void* z_final, la_stream_t stream) {
+    g_last_error[0] = 0;
+    return state_scan_entry(S, z, st_dt, BH, N, d_k, d_v, 0, 0, 1.0f, S_final, z_final, stream);
+}
+
+la_status la_state_scan_decay(void* S, void* z, la_dtype st_dt, int64_t BH, int64_t N, int64_t d_k, int64_t d_v,
+                              int64_t L, int64_t C, float gamma, void* S_final, void* z_final, la_stream_t stream) {
+    g_last_error[0] = 0;
+    const la_status st = check_gamma(gamma);
+    if (st != LA_OK) return st;
+    return state_scan_entry(S, z, st_dt, BH, N, d_k, d_v, L, C, gamma, S_final, z_final, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -482,12 +532,11 @@ int64_t la_chunked_forward_group(la_dtype in_dt, int64_t BH, int64_t L, int64_t 
     return s == LA_OK ? P.G : 0;
 }
 
-la_status la_chunked_forward(const void* q, const void* k, const void* v, la_dtype in_dt, int64_t BH, int64_t L,
-                             int64_t d_in, int64_t d_v, int64_t C, int causal, int normalize, la_fmap f,
-                             const void* W, int64_t m, float in_scale, void* o, la_dtype out_dt, void* S_final,
-                             void* z_final, int64_t group, void* workspace, size_t ws_bytes,
-                             la_stream_t stream) {
-    g_last_error[0] = 0;
+static la_status forward_entry(const void* q, const void* k, const void* v, la_dtype in_dt, int64_t BH, int64_t L,
+                               int64_t d_in, int64_t d_v, int64_t C, int causal, int normalize, la_fmap f,
+                               const void* W, int64_t m, float in_scale, float gamma, void* o, la_dtype out_dt,
+                               void* S_final, void* z_final, int64_t group, void* workspace, size_t ws_bytes,
+                               la_stream_t stream) {
     if (q == nullptr || k == nullptr || v == nullptr || o == nullptr)
         return fail(LA_ERR_INVALID_ARG, "q, k, v and o must not be NULL");
     la_status st = check_dtypes_forward(in_dt, out_dt, normalize, f, in_scale);
@@ -497,6 +546,11 @@ la_status la_chunked_forward(const void* q, const void* k, const void* v, la_dty
     Plan P{};
     st = make_plan(P, in_dt, BH, L, d_in, d_v, C, causal, normalize, f, m, in_scale, group);
     if (st != LA_OK) return st;
+    const float lg = log2_of(gamma);
+    if (lg != 0.0f && !(causal && P.pipe && out_dt == LA_BF16))
+        return fail(LA_ERR_UNSUPPORTED,
+                    "the decayed recurrence runs on the streaming kernel: causal, bf16 in and out, C in {32, 64, 128} "
+                    "with d_k in {64, 128} and d_v a multiple of 64, or C in {32, 64} with d_k = 256");
     if (P.ws_total > 0 && (workspace == nullptr || ws_bytes < P.ws_total))
         return fail(LA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", P.ws_total,
                     workspace ? ws_bytes : (size_t)0);
@@ -540,13 +594,17 @@ la_status la_chunked_forward(const void* q, const void* k, const void* v, la_dty
     if (P.causal && (P.n_groups > 1 || want_final)) {
         const int64_t n_slots = P.n_groups * P.sub;
         const int64_t n_items = want_final ? n_slots : n_slots - P.sub;
-        st = chunk_states_impl(km, v, P.i8, BH, L, P.dk, d_v, P.G * P.C / P.sub, (int)n_items, (int)n_slots,
-                               states, zst, fmap_in_kernel, in_scale, s, klo);
+        const int64_t Cs = P.G * P.C / P.sub;
+        st = chunk_states_impl(km, v, P.i8, BH, L, P.dk, d_v, Cs, (int)n_items, (int)n_slots, states, zst,
+                               fmap_in_kernel, in_scale, s, klo, lg);
         if (st != LA_OK) return st;
         la::ScanParams sp{};
         sp.S = states;
         sp.z = zst;
         sp.N = n_slots;
+        sp.log2_gamma = lg;
+        sp.L = L;
+        sp.Cs = Cs;
         if (want_final) {
             sp.S_final = S_final;
             sp.z_final = z_final;
@@ -563,15 +621,36 @@ la_status la_chunked_forward(const void* q, const void* k, const void* v, la_dty
 
     // phase 3
     return launch_phase3(P, qm, km, klo, v, o, out_dt, states, zst, S_final, z_final, fmap_in_kernel, in_scale,
-                         f == LA_FMAP_IDENTITY && in_scale != 1.0f, s);
+                         f == LA_FMAP_IDENTITY && in_scale != 1.0f, s, lg);
+}
+
+la_status la_chunked_forward(const void* q, const void* k, const void* v, la_dtype in_dt, int64_t BH, int64_t L,
+                             int64_t d_in, int64_t d_v, int64_t C, int causal, int normalize, la_fmap f,
+                             const void* W, int64_t m, float in_scale, void* o, la_dtype out_dt, void* S_final,
+                             void* z_final, int64_t group, void* workspace, size_t ws_bytes,
+                             la_stream_t stream) {
+    g_last_error[0] = 0;
+    return forward_entry(q, k, v, in_dt, BH, L, d_in, d_v, C, causal, normalize, f, W, m, in_scale, 1.0f, o, out_dt,
+                         S_final, z_final, group, workspace, ws_bytes, stream);
+}
+
+la_status la_chunked_forward_decay(const void* q, const void* k, const void* v, la_dtype in_dt, int64_t BH,
+                                   int64_t L, int64_t d_in, int64_t d_v, int64_t C, int normalize, la_fmap f,
+                                   const void* W, int64_t m, float in_scale, float gamma, void* o, la_dtype out_dt,
+                                   void* S_final, void* z_final, int64_t group, void* workspace, size_t ws_bytes,
+                                   la_stream_t stream) {
+    g_last_error[0] = 0;
+    const la_status st = check_gamma(gamma);
+    if (st != LA_OK) return st;
+    return forward_entry(q, k, v, in_dt, BH, L, d_in, d_v, C, 1, normalize, f, W, m, in_scale, gamma, o, out_dt,
+                         S_final, z_final, group, workspace, ws_bytes, stream);
 }
 
 // ---------------------------------------------------------------------------
-la_status la_chunk_output(const void* q, const void* k, const void* v, la_dtype in_dt, int64_t BH, int64_t L,
-                          int64_t d_k, int64_t d_v, int64_t C, int64_t group, const void* P_prefix,
-                          const void* z_prefix, int normalize, void* o, la_dtype out_dt, void* S_final,
-                          void* z_final, la_stream_t stream) {
-    g_last_error[0] = 0;
+static la_status chunk_output_entry(const void* q, const void* k, const void* v, la_dtype in_dt, int64_t BH,
+                                    int64_t L, int64_t d_k, int64_t d_v, int64_t C, int64_t group,
+                                    const void* P_prefix, const void* z_prefix, int normalize, float gamma, void* o,
+                                    la_dtype out_dt, void* S_final, void* z_final, la_stream_t stream) {
     if (q == nullptr || k == nullptr || v == nullptr || o == nullptr)
         return fail(LA_ERR_INVALID_ARG, "q, k, v and o must not be NULL");
     la_status st = check_dtypes_forward(in_dt, out_dt, normalize, LA_FMAP_IDENTITY, 1.0f);
@@ -584,15 +663,40 @@ la_status la_chunk_output(const void* q, const void* k, const void* v, la_dtype 
     if (P.n_groups > 1 && (P_prefix == nullptr || (normalize && z_prefix == nullptr)))
         return fail(LA_ERR_INVALID_ARG, "more than one group needs the prefix states (and normalisers)");
     P.sub = 1;  // the caller's prefixes: one per group
+    const float lg = log2_of(gamma);
+    if (lg != 0.0f && !(P.pipe && out_dt == LA_BF16))
+        return fail(LA_ERR_UNSUPPORTED,
+                    "the decayed recurrence runs on the streaming kernel: bf16 in and out, C in {32, 64, 128} with d_k "
+                    "in {64, 128} and d_v a multiple of 64, or C in {32, 64} with d_k = 256");
     return launch_phase3(P, q, k, nullptr, v, o, out_dt, P_prefix, z_prefix, S_final, z_final, la::FMAP_NONE,
-                         1.0f, false, (hipStream_t)stream);
+                         1.0f, false, (hipStream_t)stream, lg);
+}
+
+la_status la_chunk_output(const void* q, const void* k, const void* v, la_dtype in_dt, int64_t BH, int64_t L,
+                          int64_t d_k, int64_t d_v, int64_t C, int64_t group, const void* P_prefix,
+                          const void* z_prefix, int normalize, void* o, la_dtype out_dt, void* S_final,
+                          void* z_final, la_stream_t stream) {
+    g_last_error[0] = 0;
+    return chunk_output_entry(q, k, v, in_dt, BH, L, d_k, d_v, C, group, P_prefix, z_prefix, normalize, 1.0f, o,
+                              out_dt, S_final, z_final, stream);
+}
+
+la_status la_chunk_output_decay(const void* q, const void* k, const void* v, la_dtype in_dt, int64_t BH,
+                                int64_t L, int64_t d_k, int64_t d_v, int64_t C, int64_t group, const void* P_prefix,
+                                const void* z_prefix, int normalize, float gamma, void* o, la_dtype out_dt,
+                                void* S_final, void* z_final, la_stream_t stream) {
+    g_last_error[0] = 0;
+    const la_status st = check_gamma(gamma);
+    if (st != LA_OK) return st;
+    return chunk_output_entry(q, k, v, in_dt, BH, L, d_k, d_v, C, group, P_prefix, z_prefix, normalize, gamma, o,
+                              out_dt, S_final, z_final, stream);
 }
 
 // ---------------------------------------------------------------------------
-la_status la_recurrent_step(const void* q, const void* k, const void* v, la_dtype in_dt, int64_t n_states,
+static la_status step_entry(const void* q, const void* k, const void* v, la_dtype in_dt, int64_t n_states,
                             int64_t d_in, int64_t d_v, la_fmap f, const void* W, int64_t m, float in_scale,
-                            int normalize, float* S, float* z, void* o, la_dtype out_dt, la_stream_t stream) {
-    g_last_error[0] = 0;
+                            int normalize, float gamma, float* S, float* z, void* o, la_dtype out_dt,
+                            la_stream_t stream) {
     if (q == nullptr || k == nullptr || v == nullptr || S == nullptr || o == nullptr)
         return fail(LA_ERR_INVALID_ARG, "q, k, v, S and o must not be NULL");
     if (normalize && z == nullptr) return fail(LA_ERR_INVALID_ARG, "normalize needs z");
@@ -631,7 +735,27 @@ la_status la_recurrent_step(const void* q, const void* k, const void* v, la_dtyp
     p.in_scale = in_scale;
     p.normalize = normalize != 0;
     p.out_f32 = out_dt == LA_F32;
+    p.gamma = gamma;
     return hip_status(la::run_recurrent_step(p, (hipStream_t)stream), "recurrent step launch");
+}
+
+la_status la_recurrent_step(const void* q, const void* k, const void* v, la_dtype in_dt, int64_t n_states,
+                            int64_t d_in, int64_t d_v, la_fmap f, const void* W, int64_t m, float in_scale,
+                            int normalize, float* S, float* z, void* o, la_dtype out_dt, la_stream_t stream) {
+    g_last_error[0] = 0;
+    return step_entry(q, k, v, in_dt, n_states, d_in, d_v, f, W, m, in_scale, normalize, 1.0f, S, z, o, out_dt,
+                      stream);
+}
+
+la_status la_recurrent_step_decay(const void* q, const void* k, const void* v, la_dtype in_dt, int64_t n_states,
+                                  int64_t d_in, int64_t d_v, la_fmap f, const void* W, int64_t m, float in_scale,
+                                  int normalize, float gamma, float* S, float* z, void* o, la_dtype out_dt,
+                                  la_stream_t stream) {
+    g_last_error[0] = 0;
+    const la_status st = check_gamma(gamma);
+    if (st != LA_OK) return st;
+    return step_entry(q, k, v, in_dt, n_states, d_in, d_v, f, W, m, in_scale, normalize, gamma, S, z, o, out_dt,
+                      stream);
 }
 
 }  // extern "C"

@@ -162,6 +162,48 @@ __device__ __forceinline__ void phi_split_units(URegs<R, W, NT>& reg, URegs<R, W
     }
 }
 
+// Decayed recurrence: row r of a chunk ending at row e enters the chunk's
+// state weighted gamma^(e-1-r).  The weight goes onto K (so the normaliser's
+// column sums carry it too), computed in fp32 and rounded back to bf16; with
+// the hi/lo split, w (hi + lo) is split again into a new hi/lo pair.
+template <int R, int W, int NT, bool SPLIT>
+__device__ __forceinline__ void decay_units(URegs<R, W, NT>& reg, URegs<R, W, NT>& lo, const Tile& t, int tid,
+                                            int64_t e, float lg) {
+    constexpr int CG = W / 8;
+#pragma unroll
+    for (int it = 0; it < Units<R, W, NT>::PER_THREAD; ++it) {
+        const int u = tid + it * NT;
+        const int rg = u / CG;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = rg * 4 + i;
+            const float w = (u < Units<R, W, NT>::N && r < t.valid)
+                                ? __builtin_amdgcn_exp2f((float)(e - 1 - (t.row0 + r)) * lg)
+                                : 0.f;
+            const uint4 h = reg.r[it][i];
+            const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
+            uint32_t nh[4], nl[4];
+            if constexpr (SPLIT) {
+                const uint4 l = lo.r[it][i];
+                const uint32_t lw[4] = {l.x, l.y, l.z, l.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float a = w * (__uint_as_float(hw[j] << 16) + __uint_as_float(lw[j] << 16));
+                    const float b = w * (__uint_as_float(hw[j] & 0xFFFF0000u) + __uint_as_float(lw[j] & 0xFFFF0000u));
+                    nh[j] = pack2_bf16(a, b);
+                    nl[j] = pack2_bf16(a - __uint_as_float(nh[j] << 16), b - __uint_as_float(nh[j] & 0xFFFF0000u));
+                }
+                lo.r[it][i] = make_uint4(nl[0], nl[1], nl[2], nl[3]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    nh[j] = pack2_bf16(w * __uint_as_float(hw[j] << 16), w * __uint_as_float(hw[j] & 0xFFFF0000u));
+            }
+            reg.r[it][i] = make_uint4(nh[0], nh[1], nh[2], nh[3]);
+        }
+    }
+}
+
 __device__ __forceinline__ float sum_bf16x8(const uint4& u) {
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
     float s = 0.f;
@@ -715,6 +757,7 @@ __global__ __launch_bounds__(NW * WAVE) void chunk_states_bf16(StatesParams p) {
             else
                 phi_units<T, DK, NT>(rk, p.dk_g, t, tid, p.in_scale);
         }
+        if (p.log2_gamma != 0.0f) decay_units<T, DK, NT, SPLIT>(rk, rkl, t, tid, ce, p.log2_gamma);
         __syncthreads();
         store_rows<T, DK, NT>(rk, Ks, G::QS, tid);
         if (SPLIT) store_rows<T, DK, NT>(rkl, KLs, G::QS, tid);

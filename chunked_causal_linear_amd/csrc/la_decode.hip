@@ -1,8 +1,9 @@
 // One recurrent decode step for many independent states:
-//     S += phi(k) v^T ;  z += phi(k) ;  o = phi(q)^T S [/ phi(q)^T z]
+//     S = gamma S + phi(k) v^T ;  z = gamma z + phi(k) ;  o = phi(q)^T S [/ phi(q)^T z]
 // (update, then read: the RNN view on the page "Linear Attention /
 // Performerの理論と実装" and the token-by-token form on the page "attention
-// と線形の間", section ②).
+// と線形の間", section ②; gamma < 1 is the decayed recurrence the first page
+// gives for Retention, gamma = 1 plain linear attention).
 //
 // The step is a read-modify-write stream over the fp32 states; a workgroup of
 // 256 threads walks NS states, keeping the FAVOR+ projection W in LDS for all
@@ -31,6 +32,7 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(DecodeParams p, int
     __shared__ u16 Ws[WMAX];  // FAVOR+ projection (m x d_in)
 
     const int tid = threadIdx.x;
+    const float gam = p.gamma;  // 1 without the decay
     const int j4 = tid % J4, ag = tid / J4;
     const int din = p.d_in;
     const float s = p.in_scale;
@@ -95,10 +97,10 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(DecodeParams p, int
             if (a < DK) {
                 const float kk = fk[a], qq = fq[a];
                 float4 x = cur[i];
-                x.x += kk * v4.x;
-                x.y += kk * v4.y;
-                x.z += kk * v4.z;
-                x.w += kk * v4.w;
+                x.x = fmaf(kk, v4.x, gam * x.x);
+                x.y = fmaf(kk, v4.y, gam * x.y);
+                x.z = fmaf(kk, v4.z, gam * x.z);
+                x.w = fmaf(kk, v4.w, gam * x.w);
                 S[a * J4 + j4] = x;
                 acc.x += qq * x.x;
                 acc.y += qq * x.y;
@@ -115,7 +117,7 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(DecodeParams p, int
         float dpart = 0.f;
         if (p.normalize && p.z != nullptr) {
             for (int a = tid; a < DK; a += NT) {
-                const float zn = p.z[st * DK + a] + fk[a];
+                const float zn = fmaf(gam, p.z[st * DK + a], fk[a]);
                 p.z[st * DK + a] = zn;
                 dpart += fq[a] * zn;
             }

@@ -140,6 +140,22 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t 
         : "memory");
 }
 
+// Eight bf16 values times per-element weights (fp32 math, rounded to nearest
+// even), and eight floats packed to bf16.
+__device__ __forceinline__ bf16x8 scale_bf16x8(const bf16x8& v, const float (&w)[8]) {
+    const uint4 u = __builtin_bit_cast(uint4, v);
+    const uint32_t x[4] = {u.x, u.y, u.z, u.w};
+    uint32_t y[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        y[j] = pack2_bf16(__uint_as_float(x[j] << 16) * w[2 * j], __uint_as_float(x[j] & 0xFFFF0000u) * w[2 * j + 1]);
+    return as_bf16x8(make_uint4(y[0], y[1], y[2], y[3]));
+}
+__device__ __forceinline__ bf16x8 pack_bf16x8(const float (&w)[8]) {
+    return as_bf16x8(make_uint4(pack2_bf16(w[0], w[1]), pack2_bf16(w[2], w[3]), pack2_bf16(w[4], w[5]),
+                                pack2_bf16(w[6], w[7])));
+}
+
 // LDS byte address of a pointer into a __shared__ object: the low 32 bits of
 // its generic address (the shared aperture sits in the high half).
 template <typename E>
@@ -166,7 +182,7 @@ using ic = std::integral_constant<int, I>;
 
 }  // namespace pipe
 
-template <int DK, int DVT, int CH, bool SCALED, bool NORM, bool PHI>
+template <int DK, int DVT, int CH, bool SCALED, bool NORM, bool PHI, bool DECAY>
 __global__ __launch_bounds__(4 * WAVE) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void chunked_fwd_pipe(FwdParams p) {
     using namespace pipe;
@@ -394,6 +410,43 @@ void chunked_fwd_pipe(FwdParams p) {
     const int c4 = 4 * (lane & 3), c8 = 8 * (lane & 3);
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
+    // Decay (the decayed recurrence S_t = gamma S_{t-1} + k_t^T v_t): powers of
+    // gamma as exp2(e log2 gamma) (v_exp_f32), 0 for negative e (masked).
+    //   fd[D][i] = gamma^(16 D + l16 - 4g - i): score of query 16 qb + l16 and key
+    //             16 kb + 4g + i of the same tile, D = qb - kb (the cross block
+    //             of 128-row chunks reaches D = 7);
+    //   fin[qb] = gamma^(16 qb + l16 + 1): the inter read of that query row at
+    //             the start of its chunk (fin64: 64 rows further on).
+    const float lg = p.log2_gamma;
+    auto gpow = [&](int e) __attribute__((always_inline)) {
+        return e < 0 ? 0.f : __builtin_amdgcn_exp2f((float)e * lg);
+    };
+    constexpr int ND = CH == 128 ? 8 : 4;
+    float fd[DECAY ? ND : 1][4], fin[4], fin64[4];
+    if constexpr (DECAY) {
+#pragma unroll
+        for (int d = 0; d < ND; ++d)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) fd[d][i] = gpow(16 * d + l16 - 4 * g - i);
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb) {
+            fin[qb] = gpow(16 * qb + l16 + 1);
+            fin64[qb] = gpow(64 + 16 * qb + l16 + 1);
+        }
+    }
+    // inter parts of query blocks [B0, B1) read the carried state from the start
+    // of their chunk: scale them before the intra parts are added
+    auto decay_inter = [&](f32x4 (&O)[NCB][4], const float (&f)[4], int b0, int b1, int shift)
+        __attribute__((always_inline)) {
+        if constexpr (DECAY) {
+#pragma unroll
+            for (int c = 0; c < NCB; ++c)
+#pragma unroll
+                for (int qb = 0; qb < 4; ++qb)
+                    if (qb >= b0 && qb < b1) O[c][qb] *= f[qb - shift];
+        }
+    };
+
     // Scores of the lower-triangle window of query blocks Q0 + qb and key blocks
     // K0 + kb, kb <= qb < 4 (10 blocks, index qb(qb+1)/2 + kb; with HALVES only
     // the blocks inside each 32-row half), masked on the diagonal, and the
@@ -432,11 +485,22 @@ void chunked_fwd_pipe(FwdParams p) {
                 for (int qb = 0; qb < 4; ++qb)
                     if ((INTER >> qb) & 1) O[c][qb] = mfma_bf16(pst[c][ks], qa[ks & 1][qb], O[c][qb]);
         }
+        if constexpr (DECAY) {
+            // every score times gamma^(query - key); 0 above the diagonal
 #pragma unroll
-        for (int qb = 0; qb < 4; ++qb)
+            for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (4 * g + i > l16) S[qb * (qb + 1) / 2 + qb][i] = 0.f;
+                for (int kb = 0; kb <= qb; ++kb)
+                    if (!HALVES || (qb >> 1) == (kb >> 1))
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) S[qb * (qb + 1) / 2 + kb][i] *= fd[qb - kb][i];
+        } else {
+#pragma unroll
+            for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (4 * g + i > l16) S[qb * (qb + 1) / 2 + qb][i] = 0.f;
+        }
     };
 
     // intra product of a window: query blocks qb < 4 of O against the key steps
@@ -463,7 +527,10 @@ void chunked_fwd_pipe(FwdParams p) {
 
     // state update with the key steps KK0 .. KK0 + NK - 1 of the tile, K column
     // operands one (ks, hf) step ahead
-    auto update = [&](const StageT& s, auto kk0c, auto nkc) __attribute__((always_inline)) {
+    // With the decay, the chunk (keys from row kbase, n_rows of them) enters as
+    // P <- gamma^n P + sum_j gamma^(n-1-j) k_j^T v_j: the state is scaled and
+    // each key's V operand (the ones of the denominator block too) weighted.
+    auto update = [&](const StageT& s, auto kk0c, auto nkc, int n_rows, int kbase) __attribute__((always_inline)) {
         constexpr int KK0 = decltype(kk0c)::value, NK = decltype(nkc)::value;
         bf16x8 vb[NCB][NK];
 #pragma unroll
@@ -471,6 +538,28 @@ void chunked_fwd_pipe(FwdParams p) {
 #pragma unroll
             for (int kk = 0; kk < NK; ++kk)
                 vb[c][kk] = c < CPW ? col_op<VSEG>(s.v, (KK0 + kk) * 32, colw + c * 16 + c4, lane) : ones;
+        if constexpr (DECAY) {
+            const float gn = __builtin_amdgcn_exp2f((float)n_rows * lg);
+#pragma unroll
+            for (int c = 0; c < NCB; ++c)
+#pragma unroll
+                for (int ks = 0; ks < NKA; ++ks) {
+                    P[c][ks][0] *= gn;
+                    P[c][ks][1] *= gn;
+                }
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk) {
+                // operand element j holds key 32 (KK0 + kk) + 4g + j (j < 4), + 16 (j >= 4)
+                float w[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int key = 32 * (KK0 + kk) + 4 * g + (j & 3) + 16 * (j >> 2) - kbase;
+                    w[j] = key < n_rows ? gpow(n_rows - 1 - key) : 0.f;
+                }
+#pragma unroll
+                for (int c = 0; c < NCB; ++c) vb[c][kk] = c < CPW ? scale_bf16x8(vb[c][kk], w) : pack_bf16x8(w);
+            }
+        }
         bf16x8 kc[2][NK];
         auto load_kc = [&](int ks, int hf, bf16x8 (&k_)[NK]) __attribute__((always_inline)) {
 #pragma unroll
@@ -543,15 +632,16 @@ void chunked_fwd_pipe(FwdParams p) {
     };
 
     // ---- one tile's products
-    auto compute = [&](StageT& s) __attribute__((always_inline)) {
+    auto compute = [&](StageT& s, int valid) __attribute__((always_inline)) {
         bf16x8 pst[NCB][NKA];
         pack_state(pst);
         if constexpr (CH == 64) {
             f32x4 S[10], O[NCB][4];
             zero_o(O);
             tri_window(s, ic<0>{}, ic<0>{}, ic<0>{}, ic<15>{}, S, O, pst);
+            decay_inter(O, fin, 0, 4, 0);
             tri_intra(s, ic<0>{}, S, O);
-            update(s, ic<0>{}, ic<2>{});
+            update(s, ic<0>{}, ic<2>{}, valid, 0);
             write_out(s, ic<0>{}, O);
         } else if constexpr (CH == 32) {
             // two chunks per tile: rows 0..31 (A) and 32..63 (B).  Scores only
@@ -560,10 +650,12 @@ void chunked_fwd_pipe(FwdParams p) {
             f32x4 S[10], O[NCB][4];
             zero_o(O);
             tri_window(s, ic<0>{}, ic<0>{}, ic<1>{}, ic<3>{}, S, O, pst);
-            update(s, ic<0>{}, ic<1>{});  // A's keys (key step 0)
+            decay_inter(O, fin, 0, 2, 0);
+            update(s, ic<0>{}, ic<1>{}, valid < 32 ? valid : 32, 0);  // A's keys (key step 0)
             pack_state(pst);
             inter2(s, ic<0>{}, ic<2>{}, O, pst);
-            update(s, ic<1>{}, ic<1>{});  // B's keys (key step 1)
+            decay_inter(O, fin, 2, 4, 2);
+            update(s, ic<1>{}, ic<1>{}, valid > 32 ? valid - 32 : 0, 32);  // B's keys (key step 1)
             bf16x8 vb[NCB][2];
 #pragma unroll
             for (int c = 0; c < NCB; ++c)
@@ -594,11 +686,13 @@ void chunked_fwd_pipe(FwdParams p) {
             {
                 f32x4 S[10];
                 tri_window(s, ic<0>{}, ic<0>{}, ic<0>{}, ic<15>{}, S, Oa, pst);
+                decay_inter(Oa, fin, 0, 4, 0);
                 tri_intra(s, ic<0>{}, S, Oa);
             }
             {
                 f32x4 S[10];
                 tri_window(s, ic<4>{}, ic<4>{}, ic<0>{}, ic<15>{}, S, Ob, pst);
+                decay_inter(Ob, fin64, 0, 4, 0);
                 tri_intra(s, ic<2>{}, S, Ob);
             }
             // cross block, one key step (two 16-key blocks) at a time
@@ -627,6 +721,15 @@ void chunked_fwd_pipe(FwdParams p) {
                 bf16x8 vb[NCB];
 #pragma unroll
                 for (int c = 0; c < NCB; ++c) vb[c] = c < CPW ? col_op<VSEG>(s.v, kk * 32, colw + c * 16 + c4, lane) : ones;
+                if constexpr (DECAY) {
+                    // query 64 + 16 qb + l16, key 32 kk + 16 b + 4g + i: D = 4 + qb - 2 kk - b
+#pragma unroll
+                    for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+                        for (int b = 0; b < 2; ++b)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) X[qb][b][i] *= fd[4 + qb - 2 * kk - b][i];
+                }
 #pragma unroll
                 for (int qb = 0; qb < 4; ++qb) {
                     const bf16x8 xb = pack_acc_bf16(X[qb][0], X[qb][1]);
@@ -634,7 +737,7 @@ void chunked_fwd_pipe(FwdParams p) {
                     for (int c = 0; c < NCB; ++c) Ob[c][qb] = mfma_bf16(vb[c], xb, Ob[c][qb]);
                 }
             }
-            update(s, ic<0>{}, ic<4>{});
+            update(s, ic<0>{}, ic<4>{}, valid, 0);
             write_out(s, ic<0>{}, Oa);
             write_out(s, ic<4>{}, Ob);
         }
@@ -647,7 +750,7 @@ void chunked_fwd_pipe(FwdParams p) {
             zero_tail(st[SI], valid_rows(t));
             __syncthreads();
         }
-        compute(st[SI]);
+        compute(st[SI], valid_rows(t));
     };
     for (int64_t t = t_begin; t < t_end; t += NSTAGE) {
         step(ic<0>{}, t);
@@ -686,17 +789,19 @@ void chunked_fwd_pipe(FwdParams p) {
 
 // Output scaling exists for the scaled identity map without the normaliser
 // only (normalised outputs are scale-free; pre-mapped inputs carry the scale).
-template <int DK, int DVT, int CH, bool NORM, bool PHI>
+template <int DK, int DVT, int CH, bool NORM, bool PHI, bool DECAY>
 hipError_t launch_fwd_pipe(const FwdParams& p, int64_t grid, hipStream_t s) {
     const dim3 block(4 * WAVE);
     if (p.out_scale != 1.0f) {
         if constexpr (NORM || PHI) {
             return hipErrorInvalidValue;
         } else {
-            hipLaunchKernelGGL((chunked_fwd_pipe<DK, DVT, CH, true, false, false>), dim3((unsigned)grid), block, 0, s, p);
+            hipLaunchKernelGGL((chunked_fwd_pipe<DK, DVT, CH, true, false, false, DECAY>), dim3((unsigned)grid), block,
+                               0, s, p);
         }
     } else {
-        hipLaunchKernelGGL((chunked_fwd_pipe<DK, DVT, CH, false, NORM, PHI>), dim3((unsigned)grid), block, 0, s, p);
+        hipLaunchKernelGGL((chunked_fwd_pipe<DK, DVT, CH, false, NORM, PHI, DECAY>), dim3((unsigned)grid), block, 0, s,
+                           p);
     }
     return hipGetLastError();
 }

@@ -35,6 +35,7 @@ struct FwdParams {
     float out_scale;    // multiplies every output row (identity map with in_scale: s^2)
     float state_scale;  // multiplies the returned final state and normaliser (s)
     int p0_sub;         // prefix slots per group (group g starts at slot g * p0_sub); 0 means 1
+    float log2_gamma;   // decayed recurrence S_t = gamma S_{t-1} + k_t^T v_t: log2(gamma) (0: no decay)
 };
 
 // Phase 1 (per-chunk states).
@@ -55,6 +56,7 @@ struct StatesParams {
     float in_scale;
     int want_z;
     int xcd_remap;
+    float log2_gamma;  // decayed recurrence: row r of a chunk ending at e weighs gamma^(e-1-r) (0: no decay)
 };
 
 // int8 path: fused phase 3 and phase 1 with exact int32 arithmetic.
@@ -101,6 +103,9 @@ struct ScanParams {
     int64_t E;
     int64_t Ez;
     int is_int;
+    float log2_gamma;  // decayed prefix P_n = gamma^len(n-1) P_{n-1} + S_{n-1} (0: plain sum)
+    int64_t L;         // with the decay: rows of the sequence and rows per chunk, so that
+    int64_t Cs;        //   len(n) = clamp(L - n Cs, 0, Cs)
 };
 
 struct FmapParams {
@@ -132,6 +137,7 @@ struct DecodeParams {
     float in_scale;
     int normalize;
     int out_f32;
+    float gamma;    // decayed recurrence: S = gamma S + k^T v, z = gamma z + k (1: none)
 };
 
 hipError_t run_chunked_fwd_i8(const FwdParamsI8& p, int DK, int DVT, int T, int64_t grid, hipStream_t s);

@@ -1,40 +1,13 @@
 // Streaming fused phase 3 for chunks of 32, 64 or 128 rows (instantiations;
-// feature width 256 with chunks of 32 or 64).
-#include "la_fwd_pipe.hpp"
+// feature width 256 with chunks of 32 or 64).  The decayed recurrence is
+// instantiated in la_pipe_decay.hip.
+#include "la_pipe.hpp"
 
 namespace la {
 
-namespace {
-
-// normaliser from p.normalize; elu+1 applied in the kernel from p.fmap;
-// tiles of 64 value columns, 32 at feature width 256 (LDS and registers)
-template <int DK, int C>
-hipError_t by_flags(const FwdParams& p, int64_t grid, hipStream_t s) {
-    constexpr int DVT = DK == 256 ? 32 : 64;
-    const bool norm = p.normalize != 0;
-    if (p.fmap == FMAP_ELU1)
-        return norm ? launch_fwd_pipe<DK, DVT, C, true, true>(p, grid, s)
-                    : launch_fwd_pipe<DK, DVT, C, false, true>(p, grid, s);
-    return norm ? launch_fwd_pipe<DK, DVT, C, true, false>(p, grid, s)
-                : launch_fwd_pipe<DK, DVT, C, false, false>(p, grid, s);
-}
-
-}  // namespace
-
 hipError_t fwd_pipe_bf16(const FwdParams& p, int DK, int DVT, int C, int64_t grid, hipStream_t s) {
-    if (DVT != (DK == 256 ? 32 : 64) || p.noncausal || p.out_f32 || p.k_lo != nullptr) return hipErrorInvalidValue;
-    if (p.fmap != FMAP_NONE && p.fmap != FMAP_ELU1) return hipErrorInvalidValue;
-    switch (DK * 1000 + C) {
-        case 128032: return by_flags<128, 32>(p, grid, s);
-        case 128064: return by_flags<128, 64>(p, grid, s);
-        case 128128: return by_flags<128, 128>(p, grid, s);
-        case 64032: return by_flags<64, 32>(p, grid, s);
-        case 64064: return by_flags<64, 64>(p, grid, s);
-        case 64128: return by_flags<64, 128>(p, grid, s);
-        case 256032: return by_flags<256, 32>(p, grid, s);
-        case 256064: return by_flags<256, 64>(p, grid, s);
-    }
-    return hipErrorInvalidValue;
+    if (p.log2_gamma != 0.0f) return fwd_pipe_decay_bf16(p, DK, DVT, C, grid, s);
+    return pipe_dispatch<false>(p, DK, DVT, C, grid, s);
 }
 
 }  // namespace la

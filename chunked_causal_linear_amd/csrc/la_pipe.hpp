@@ -1,0 +1,44 @@
+// Dispatch of the streaming phase-3 kernel over its compile-time cases.
+#pragma once
+
+#include "la_fwd_pipe.hpp"
+
+namespace la {
+
+hipError_t fwd_pipe_decay_bf16(const FwdParams& p, int DK, int DVT, int C, int64_t grid, hipStream_t s);
+
+namespace pipe {
+
+// normaliser from p.normalize; elu+1 applied in the kernel from p.fmap;
+// tiles of 64 value columns, 32 at feature width 256 (LDS and registers)
+template <int DK, int C, bool DECAY>
+hipError_t by_flags(const FwdParams& p, int64_t grid, hipStream_t s) {
+    constexpr int DVT = DK == 256 ? 32 : 64;
+    const bool norm = p.normalize != 0;
+    if (p.fmap == FMAP_ELU1)
+        return norm ? launch_fwd_pipe<DK, DVT, C, true, true, DECAY>(p, grid, s)
+                    : launch_fwd_pipe<DK, DVT, C, false, true, DECAY>(p, grid, s);
+    return norm ? launch_fwd_pipe<DK, DVT, C, true, false, DECAY>(p, grid, s)
+                : launch_fwd_pipe<DK, DVT, C, false, false, DECAY>(p, grid, s);
+}
+
+}  // namespace pipe
+
+template <bool DECAY>
+hipError_t pipe_dispatch(const FwdParams& p, int DK, int DVT, int C, int64_t grid, hipStream_t s) {
+    if (DVT != (DK == 256 ? 32 : 64) || p.noncausal || p.out_f32 || p.k_lo != nullptr) return hipErrorInvalidValue;
+    if (p.fmap != FMAP_NONE && p.fmap != FMAP_ELU1) return hipErrorInvalidValue;
+    switch (DK * 1000 + C) {
+        case 128032: return pipe::by_flags<128, 32, DECAY>(p, grid, s);
+        case 128064: return pipe::by_flags<128, 64, DECAY>(p, grid, s);
+        case 128128: return pipe::by_flags<128, 128, DECAY>(p, grid, s);
+        case 64032: return pipe::by_flags<64, 32, DECAY>(p, grid, s);
+        case 64064: return pipe::by_flags<64, 64, DECAY>(p, grid, s);
+        case 64128: return pipe::by_flags<64, 128, DECAY>(p, grid, s);
+        case 256032: return pipe::by_flags<256, 32, DECAY>(p, grid, s);
+        case 256064: return pipe::by_flags<256, 64, DECAY>(p, grid, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace la

@@ -53,16 +53,60 @@ __global__ __launch_bounds__(256) void state_scan_kernel(V4* __restrict__ S, V4*
     if (total != nullptr) total[bh * E4 + e] = run;
 }
 
+// The decayed prefix (page "Linear Attention / Performerの理論と実装", the
+// decayed recurrence): chunk n's state as it stands at the chunk's end enters
+// after the carried state has decayed over the chunk's rows,
+// P_n = gamma^len(n-1) P_{n-1} + S_{n-1}, len(n) = clamp(L - n Cs, 0, Cs).
+__global__ __launch_bounds__(256) void state_scan_decay_kernel(float4* __restrict__ S, float4* __restrict__ total,
+                                                               int64_t N, int64_t E4, int64_t BH, float lg,
+                                                               int64_t L, int64_t Cs) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= BH * E4) return;
+    const int64_t bh = idx / E4, e = idx % E4;
+    float4* base = S + bh * N * E4 + e;
+    float4 run = make_float4(0.f, 0.f, 0.f, 0.f);
+    auto decay_of = [&](int64_t n) {
+        int64_t len = L - n * Cs;
+        len = len < 0 ? 0 : (len > Cs ? Cs : len);
+        return __builtin_amdgcn_exp2f((float)len * lg);
+    };
+    constexpr int U = 8;
+    int64_t n = 0;
+    for (; n + U <= N; n += U) {
+        float4 x[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) x[u] = base[(n + u) * E4];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            base[(n + u) * E4] = run;
+            const float a = decay_of(n + u);
+            run = make_float4(fmaf(a, run.x, x[u].x), fmaf(a, run.y, x[u].y), fmaf(a, run.z, x[u].z),
+                              fmaf(a, run.w, x[u].w));
+        }
+    }
+    for (; n < N; ++n) {
+        const float4 x = base[n * E4];
+        base[n * E4] = run;
+        const float a = decay_of(n);
+        run = make_float4(fmaf(a, run.x, x.x), fmaf(a, run.y, x.y), fmaf(a, run.z, x.z), fmaf(a, run.w, x.w));
+    }
+    if (total != nullptr) total[bh * E4 + e] = run;
+}
+
 // Wrapping int32 adds (unsigned arithmetic) so overflow is defined.
 struct WrapInt4 {
     unsigned x, y, z, w;
 };
 
-static hipError_t scan_one(void* S, void* total, int64_t N, int64_t E, int64_t BH, int is_int, hipStream_t s) {
+static hipError_t scan_one(void* S, void* total, int64_t N, int64_t E, int64_t BH, int is_int, hipStream_t s,
+                           float lg, int64_t L, int64_t Cs) {
     const int64_t E4 = E / 4;
     const int64_t threads = BH * E4;
     const int64_t blocks = (threads + 255) / 256;
-    if (is_int)
+    if (lg != 0.0f && !is_int)
+        hipLaunchKernelGGL(state_scan_decay_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                           reinterpret_cast<float4*>(S), reinterpret_cast<float4*>(total), N, E4, BH, lg, L, Cs);
+    else if (is_int)
         hipLaunchKernelGGL((state_scan_kernel<WrapInt4, unsigned>), dim3((unsigned)blocks), dim3(256), 0, s,
                            reinterpret_cast<WrapInt4*>(S), reinterpret_cast<WrapInt4*>(total), N, E4, BH);
     else
@@ -72,9 +116,9 @@ static hipError_t scan_one(void* S, void* total, int64_t N, int64_t E, int64_t B
 }
 
 hipError_t run_state_scan(const ScanParams& p, int64_t BH, hipStream_t s) {
-    hipError_t e = scan_one(p.S, p.S_final, p.N, p.E, BH, p.is_int, s);
+    hipError_t e = scan_one(p.S, p.S_final, p.N, p.E, BH, p.is_int, s, p.log2_gamma, p.L, p.Cs);
     if (e != hipSuccess) return e;
-    if (p.z != nullptr) e = scan_one(p.z, p.z_final, p.N, p.Ez, BH, p.is_int, s);
+    if (p.z != nullptr) e = scan_one(p.z, p.z_final, p.N, p.Ez, BH, p.is_int, s, p.log2_gamma, p.L, p.Cs);
     return e;
 }
 

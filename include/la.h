@@ -224,6 +224,56 @@ la_status la_recurrent_step(const void* q, const void* k, const void* v, la_dtyp
                             const void* W, int64_t m, float in_scale, int normalize, float* S,
                             float* z, void* o, la_dtype out_dt, la_stream_t stream);
 
+/*
+ * The decayed recurrence (Retention): S_t = gamma S_{t-1} + phi(k_t) v_t^T and,
+ * as read here, z_t = gamma z_{t-1} + phi(k_t), with 0 < gamma <= 1 shared by
+ * every head; the output still reads y_t = phi(q_t)^T S_t [/ phi(q_t)^T z_t]
+ * after the update.  Defined by the linear-attention page, RNN view, where
+ * forgetting is introduced; gamma = 1 is plain linear attention.
+ *
+ * Each function below is its namesake with a gamma argument; a gamma outside
+ * (0, 1] (or NaN) is LA_ERR_INVALID_ARG.  Chunk n's state is the state its rows
+ * leave at the chunk's end: S_n = sum over its rows r (ending at row e) of
+ * gamma^(e-1-r) phi(k_r)^T v_r.  The forward and the chunk output run on the
+ * streaming kernel only: causal, LA_BF16 in and out, C in {32, 64, 128} with
+ * d_k in {64, 128} and d_v a multiple of 64, or C in {32, 64} with d_k = 256;
+ * any other combination is LA_ERR_UNSUPPORTED.  The forward needs the
+ * workspace la_chunked_forward_workspace gives for the same arguments.
+ */
+la_status la_chunked_forward_decay(const void* q, const void* k, const void* v, la_dtype in_dt,
+                                   int64_t BH, int64_t L, int64_t d_in, int64_t d_v, int64_t C,
+                                   int normalize, la_fmap f, const void* W, int64_t m,
+                                   float in_scale, float gamma, void* o, la_dtype out_dt,
+                                   void* S_final, void* z_final, int64_t group, void* workspace,
+                                   size_t ws_bytes, la_stream_t stream);
+
+/* Per-chunk states at each chunk's end (LA_BF16 inputs, LA_F32 states). */
+la_status la_chunk_states_decay(const void* k, const void* v, la_dtype in_dt, int64_t BH,
+                                int64_t L, int64_t d_k, int64_t d_v, int64_t C, float gamma,
+                                void* S, void* z, la_stream_t stream);
+
+/* The decayed exclusive prefix, in place: P_0 = 0, P_n = gamma^len(n-1) P_{n-1}
+ * + S_{n-1}, with len(n) the row count of chunk n of L rows in chunks of C
+ * (N must be ceil(L / C)); the total is the final state.  LA_F32 states. */
+la_status la_state_scan_decay(void* S, void* z, la_dtype st_dt, int64_t BH, int64_t N,
+                              int64_t d_k, int64_t d_v, int64_t L, int64_t C, float gamma,
+                              void* S_final, void* z_final, la_stream_t stream);
+
+/* Phase 3 from decayed group prefixes (la_chunk_states_decay with chunk size
+ * C * group, then la_state_scan_decay with the same L and chunk size). */
+la_status la_chunk_output_decay(const void* q, const void* k, const void* v, la_dtype in_dt,
+                                int64_t BH, int64_t L, int64_t d_k, int64_t d_v, int64_t C,
+                                int64_t group, const void* P_prefix, const void* z_prefix,
+                                int normalize, float gamma, void* o, la_dtype out_dt,
+                                void* S_final, void* z_final, la_stream_t stream);
+
+/* One decode step: S = gamma S + phi(k) v^T, z = gamma z + phi(k), then the read. */
+la_status la_recurrent_step_decay(const void* q, const void* k, const void* v, la_dtype in_dt,
+                                  int64_t n_states, int64_t d_in, int64_t d_v, la_fmap f,
+                                  const void* W, int64_t m, float in_scale, int normalize,
+                                  float gamma, float* S, float* z, void* o, la_dtype out_dt,
+                                  la_stream_t stream);
+
 /* Static description of a status code. */
 const char* la_status_string(la_status s);
 /* Thread-local description of the last failure on this thread ("" if none). */

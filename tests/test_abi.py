@@ -184,3 +184,39 @@ def test_missing_library_fails_loudly(monkeypatch):
     monkeypatch.setattr(b, "LIB_PATH", "/nonexistent/liblinattn.so")
     with pytest.raises(b.LibraryNotBuilt):
         b.lib()
+
+
+def test_decay_entry_point_errors():
+    """The decayed recurrence's entry points: gamma outside (0, 1] or NaN, cases
+    off the streaming kernel and wrong phase arguments are rejected up front."""
+    lib = la.lib()
+
+    def fwd(gamma=0.9, **kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, in_dt=b.LA_BF16, BH=2, L=64, d_in=64, d_v=64, C=64, normalize=0, f=0,
+                 W=None, m=0, in_scale=1.0, o=FAKE, out_dt=b.LA_BF16, S_final=None, z_final=None, group=0,
+                 ws=None, ws_bytes=0, stream=None)
+        a.update(kw)
+        return lib.la_chunked_forward_decay(a["q"], a["k"], a["v"], a["in_dt"], a["BH"], a["L"], a["d_in"], a["d_v"],
+                                            a["C"], a["normalize"], a["f"], a["W"], a["m"], a["in_scale"], gamma,
+                                            a["o"], a["out_dt"], a["S_final"], a["z_final"], a["group"], a["ws"],
+                                            a["ws_bytes"], a["stream"])
+    for g in (0.0, -0.5, 1.5, float("nan"), float("inf")):
+        assert fwd(gamma=g) == b.LA_ERR_INVALID_ARG, g
+    assert fwd(C=48) == b.LA_ERR_UNSUPPORTED            # not a streaming chunk size
+    assert fwd(d_in=32) == b.LA_ERR_UNSUPPORTED         # feature width off the streaming kernel
+    assert fwd(d_v=32) == b.LA_ERR_UNSUPPORTED          # value width off the streaming kernel
+    assert fwd(out_dt=b.LA_F32) == b.LA_ERR_UNSUPPORTED  # fp32 output runs on the general kernel
+    assert fwd(in_dt=b.LA_I8, out_dt=b.LA_I32) == b.LA_ERR_UNSUPPORTED
+    assert b"streaming" in lib.la_last_error()
+    assert lib.la_chunk_states_decay(FAKE, FAKE, b.LA_BF16, 1, 64, 64, 64, 16, 2.0, FAKE, None, None) == \
+        b.LA_ERR_INVALID_ARG
+    assert lib.la_chunk_states_decay(FAKE, FAKE, b.LA_I8, 1, 64, 64, 64, 16, 0.5, FAKE, None, None) == \
+        b.LA_ERR_UNSUPPORTED
+    assert lib.la_state_scan_decay(FAKE, None, b.LA_F32, 1, 5, 64, 64, 64, 16, 0.5, None, None, None) == \
+        b.LA_ERR_INVALID_ARG  # N != ceil(L / C)
+    assert lib.la_state_scan_decay(FAKE, None, b.LA_I32, 1, 4, 64, 64, 64, 16, 0.5, None, None, None) == \
+        b.LA_ERR_UNSUPPORTED
+    assert lib.la_chunk_output_decay(FAKE, FAKE, FAKE, b.LA_BF16, 1, 40, 64, 64, 48, 1, None, None, 0, 0.5, FAKE,
+                                     b.LA_BF16, None, None, None) == b.LA_ERR_UNSUPPORTED
+    assert lib.la_recurrent_step_decay(FAKE, FAKE, FAKE, b.LA_BF16, 4, 64, 64, 0, None, 0, 1.0, 0, 0.0, FAKE, None,
+                                       FAKE, b.LA_F32, None) == b.LA_ERR_INVALID_ARG
