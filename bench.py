@@ -351,6 +351,7 @@ def run_extras(args, out):
 
     # ---- a4: the forward at every workload and chunk size
     qd = dev_bf16(q.bits)
+    qh3, kh3, vh3 = (wl.bf16_bits_to_f64(t.bits[0][:1024]) for t in (q, k, v))  # oracle sample (one head)
     del q, k, v
     fwd = {}
     for C in (32, 64, 128):
@@ -360,6 +361,17 @@ def run_extras(args, out):
         fwd[f"w3_C{C}"] = {"ms": ms, "tokens_per_s": w3.B * w3.L / (ms * 1e-3), **hbm(wk.fused_bytes(), ms),
                            "TFLOP/s_page": wk.page_flops() / (ms * 1e-3) / 1e12}
         del f
+    # the decayed recurrence (next row: Retention), headline shape, C = 64
+    decay = {}
+    f = la.Forward(qd, kd, vd, 64, gamma=0.99)
+    ms = row_time(f.run)
+    wk = Work(w3.BH, w3.L, w3.d_in, w3.d_k, w3.d_v, 64)
+    decay["w3_C64_gamma0.99"] = {"ms": ms, "tokens_per_s": w3.B * w3.L / (ms * 1e-3), **hbm(wk.fused_bytes(), ms),
+                                 "vs_no_decay": fwd["w3_C64"]["ms"] / ms,
+                                 "oracle_s_per_head": _oracle_time(
+                                     lambda: oracle.decay_chunked(qh3, kh3, vh3, 64, 0.99)) * w3.L / 1024,
+                                 "oracle_sample": "oracle.decay_chunked on 1024 rows of one head, scaled to L"}
+    del f
     qi, ki, vi = wl.random_case(33, w3.BH, w3.L, 128, 128, "i8")
     tq, tk, tv = (torch.from_numpy(t.bits).cuda() for t in (qi, ki, vi))
     del qi, ki, vi
@@ -384,6 +396,13 @@ def run_extras(args, out):
         fwd[f"w{wid}"] = {"workload": w.name, "ms": ms, "tokens_per_s": w.B * w.L / (ms * 1e-3),
                           **hbm(wk.fused_bytes(w.return_state), ms),
                           "TFLOP/s_page": wk.page_flops() / (ms * 1e-3) / 1e12}
+        if wid == 4:
+            del f
+            f = la.Forward(qd, kd, vd, C, normalize=w.normalize, fmap=w.fmap, W=Wd, return_state=w.return_state,
+                           gamma=0.999)
+            ms_d = row_time(f.run)
+            decay["w4_gamma0.999"] = {"workload": w.name, "ms": ms_d, "tokens_per_s": w.B * w.L / (ms_d * 1e-3),
+                                      **hbm(wk.fused_bytes(w.return_state), ms_d), "vs_no_decay": ms / ms_d}
         if wid == 5:
             # ---- a5: decode on 256 streams x 12 heads of 256 x 64 fp32 states
             n = wl.DECODE_STREAMS * w.H
@@ -419,6 +438,7 @@ def run_extras(args, out):
         del f, qd, kd, vd
         torch.cuda.empty_cache()
     rows["a4_forward"] = fwd
+    rows["next_decay"] = decay
     rows["a5_decode"] = decode
     out["rows"] = rows
 

@@ -547,14 +547,21 @@ void chunked_fwd_pipe(FwdParams p) {
                     P[c][ks][0] *= gn;
                     P[c][ks][1] *= gn;
                 }
+            const float gam = __builtin_amdgcn_exp2f(lg);
 #pragma unroll
             for (int kk = 0; kk < NK; ++kk) {
-                // operand element j holds key 32 (KK0 + kk) + 4g + j (j < 4), + 16 (j >= 4)
+                // operand element j holds key 32 (KK0 + kk) + 4g + j (j < 4), + 16 (j >= 4);
+                // one power per run of four keys, the earlier keys by multiplying by gamma
                 float w[8];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int key = 32 * (KK0 + kk) + 4 * g + (j & 3) + 16 * (j >> 2) - kbase;
-                    w[j] = key < n_rows ? gpow(n_rows - 1 - key) : 0.f;
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int key3 = 32 * (KK0 + kk) + 16 * hh + 4 * g + 3 - kbase;
+                    float wk = __builtin_amdgcn_exp2f((float)(n_rows - 1 - key3) * lg);
+#pragma unroll
+                    for (int j = 3; j >= 0; --j) {
+                        w[4 * hh + j] = key3 - 3 + j < n_rows ? wk : 0.f;
+                        wk *= gam;
+                    }
                 }
 #pragma unroll
                 for (int c = 0; c < NCB; ++c) vb[c][kk] = c < CPW ? scale_bf16x8(vb[c][kk], w) : pack_bf16x8(w);
