@@ -439,6 +439,25 @@ def run_extras(args, out):
         torch.cuda.empty_cache()
     rows["a4_forward"] = fwd
     rows["next_decay"] = decay
+    # ---- next: FAVOR+ against exact softmax (the linear-attention page's error study)
+    qf, kf, vf = wl.favor_study_inputs()
+    dd = qf.exact.shape[2]
+    ref = oracle.softmax_attention(qf.exact[0], kf.exact[0], vf.exact[0], False)
+    study = {}
+    for m in (16, 32, 64, 128, 256):
+        errs = []
+        for t in range(4):
+            Wb, _ = wl.orthogonal_random_features(m, dd, [70, m, t])
+            fo = la.chunked_forward(dev_bf16(qf.bits), dev_bf16(kf.bits), dev_bf16(vf.bits), 64, causal=False,
+                                    normalize=True, fmap="favor", W=dev_bf16(Wb), in_scale=dd ** -0.25)
+            errs.append(float(np.mean((fo.float().cpu().numpy()[0].astype(np.float64) - ref) ** 2)))
+        study[str(m)] = float(np.mean(errs))
+    ms_ = [int(m) for m in study]
+    rows["next_favor_vs_softmax"] = {
+        "inputs": "one head, n=128, d=64, N(0,1)*0.4 (the page's study shape), bf16; non-causal, normalised",
+        "mse_by_m": study, "trials": 4,
+        "loglog_slope": float(np.polyfit(np.log(ms_), np.log([study[str(m)] for m in ms_]), 1)[0]),
+        "oracle_softmax_s": _oracle_time(lambda: oracle.softmax_attention(qf.exact[0], kf.exact[0], vf.exact[0]))}
     rows["a5_decode"] = decode
     out["rows"] = rows
 

@@ -511,6 +511,44 @@ def brute_force_decay(q, k, v, gamma, normalize: bool = False):
 
 
 # ---------------------------------------------------------------------------
+# Exact softmax attention, the reference FAVOR+ approximates (linear-attention
+# page: standard attention softmax(Q K^T / sqrt(d_k)) V, and the FAVOR+ kernel
+# phi(q).phi(k) whose expectation is exp(q.k), so that phi applied to inputs
+# pre-scaled by d_k^(-1/4) estimates the softmax numerator and denominator).
+# ---------------------------------------------------------------------------
+def softmax_attention(q, k, v, causal: bool = False, scale: Optional[float] = None) -> np.ndarray:
+    """softmax(q k^T * scale) v row by row (scale 1/sqrt(d_k) when omitted); causal
+    rows see keys j <= i.  The row maximum is subtracted before exp (the ratio is
+    unchanged)."""
+    q, k, v = _f64(q, k, v)
+    if scale is None:
+        scale = 1.0 / np.sqrt(q.shape[1])
+    s = (q @ k.T) * scale
+    if causal:
+        keep = np.arange(k.shape[0])[None, :] <= np.arange(q.shape[0])[:, None]
+        s = np.where(keep, s, -np.inf)
+    w = np.exp(s - s.max(axis=1, keepdims=True))
+    w = w / w.sum(axis=1, keepdims=True)
+    return w @ v
+
+
+def softmax_attention_loops(q, k, v, causal: bool = False, scale: Optional[float] = None):
+    """The same by the definition term by term (Python floats, math.exp, no max
+    subtraction): o_i = sum_j e^(s_ij) v_j / sum_j e^(s_ij).  Tiny inputs only."""
+    import math
+    L, dk = len(q), len(q[0])
+    if scale is None:
+        scale = 1.0 / math.sqrt(dk)
+    out = []
+    for i in range(L):
+        last = i if causal else len(k) - 1
+        e = [math.exp(sum(float(q[i][a]) * float(k[j][a]) for a in range(dk)) * scale) for j in range(last + 1)]
+        den = sum(e)
+        out.append([sum(e[j] * float(v[j][c]) for j in range(last + 1)) / den for c in range(len(v[0]))])
+    return out
+
+
+# ---------------------------------------------------------------------------
 # mapping over heads
 # ---------------------------------------------------------------------------
 def over_heads(form: Callable, q, k, v, *args, **kwargs):

@@ -427,3 +427,35 @@ def check_decay_forward(o, seed: int = 40) -> None:
         ref, Sr, zr = o.decay_state_first(qp, kp, v, 0.75, norm)
         assert np.allclose(out, ref, rtol=1e-12, atol=1e-14) and np.allclose(S, Sr, rtol=1e-12, atol=1e-14)
         assert np.allclose(z, zr, rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# Exact softmax attention (the reference of the FAVOR+ error study)
+# ---------------------------------------------------------------------------
+def check_softmax_reference(o, seed: int = 42) -> None:
+    """softmax_attention against the term-by-term definition; its weights are a
+    convex combination (outputs inside the values' range per column), the first
+    causal row is v_0, a constant added to every score of a row changes nothing,
+    and FAVOR+ with many orthogonal features (inputs pre-scaled by d^(-1/4)) comes
+    close to it (the kernel estimate the linear-attention page derives)."""
+    rng = np.random.default_rng([seed, 43])
+    L, d = 9, 4
+    q, k, v = rng.standard_normal((L, d)) * 0.5, rng.standard_normal((L, d)) * 0.5, rng.standard_normal((L, 3))
+    for causal in (False, True):
+        got = o.softmax_attention(q, k, v, causal)
+        ref = np.array(o.softmax_attention_loops(q, k, v, causal))
+        assert np.allclose(got, ref, rtol=1e-13, atol=1e-15), causal
+    assert np.allclose(o.softmax_attention(q, k, v, True)[0], v[0], rtol=1e-15)
+    out = o.softmax_attention(q, k, v)
+    assert np.all(out <= v.max(axis=0) + 1e-15) and np.all(out >= v.min(axis=0) - 1e-15)
+    # scores shifted by a constant: scale the queries' inner products by adding c * k-independent term
+    q2 = np.concatenate([q, np.full((L, 1), 3.0)], axis=1)
+    k2 = np.concatenate([k, np.ones((L, 1))], axis=1)
+    assert np.allclose(o.softmax_attention(q2, k2, v, scale=1 / np.sqrt(d)), o.softmax_attention(q, k, v),
+                       rtol=1e-12, atol=1e-14)
+    from workloads import orthogonal_random_features
+    _, W = orthogonal_random_features(65536, d, [seed, 44])
+    s4 = d ** -0.25
+    qp, kp = o.phi_favor(q * s4, W), o.phi_favor(k * s4, W)
+    fav = (qp @ (kp.T @ v)) / (qp @ kp.sum(axis=0))[:, None]
+    assert np.allclose(fav, out, rtol=0, atol=2e-2), np.abs(fav - out).max()

@@ -1,0 +1,53 @@
+"""FAVOR+ against exact softmax attention (the linear-attention page's error
+study): the GPU's FAVOR+ forward (features of inputs pre-scaled by d^(-1/4), so
+phi(q).phi(k) estimates exp(q.k / sqrt(d))) approaches softmax(q k^T / sqrt(d)) v
+as the number of random features m grows.
+
+Pinned here: the mean squared error falls as m grows (16 -> 64 -> 256), on a
+log-log slope between -1.6 and -0.4 (the estimator's variance falls like 1/m;
+the page reads its own plot as 1/sqrt(m)), for the non-causal form and the
+causal chunked form; the GPU's error matches the oracle's FAVOR+ error on the
+same W to a few percent.  Averaged over independent W draws.
+"""
+import numpy as np
+import pytest
+
+import chunked_causal_linear_amd as la
+import oracle
+import workloads as wl
+from tests.gpu_helpers import dev_bf16, dev_input, host, log
+
+pytestmark = pytest.mark.gpu
+
+MS = (16, 64, 256)
+TRIALS = 6
+
+
+def _study(causal: bool):
+    q, k, v = wl.favor_study_inputs()
+    n, d = q.exact.shape[1], q.exact.shape[2]
+    ref = oracle.softmax_attention(q.exact[0], k.exact[0], v.exact[0], causal)
+    s4 = d ** -0.25
+    gpu_mse, orc_mse = {}, {}
+    for m in MS:
+        g, o_ = [], []
+        for t in range(TRIALS):
+            Wb, W = wl.orthogonal_random_features(m, d, [70, m, t])
+            out = la.chunked_forward(dev_input(q), dev_input(k), dev_input(v), 64, causal=causal, normalize=True,
+                                     fmap="favor", W=dev_bf16(Wb), in_scale=s4)
+            g.append(float(np.mean((host(out)[0] - ref) ** 2)))
+            fo = oracle.forward(q.exact[0], k.exact[0], v.exact[0], 64, causal, True, "favor", W, s4)[0]
+            o_.append(float(np.mean((fo - ref) ** 2)))
+        gpu_mse[m], orc_mse[m] = float(np.mean(g)), float(np.mean(o_))
+    return gpu_mse, orc_mse
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_favor_error_falls_with_m(causal):
+    gpu, orc = _study(causal)
+    log(f"favor vs softmax causal={causal}: gpu {gpu} oracle {orc}")
+    assert gpu[16] > gpu[64] > gpu[256], gpu
+    slope = np.polyfit(np.log(MS), np.log([gpu[m] for m in MS]), 1)[0]
+    assert -1.6 < slope < -0.4, slope
+    for m in MS:
+        assert abs(gpu[m] / orc[m] - 1) < 0.05, (m, gpu[m], orc[m])

@@ -77,6 +77,10 @@ MUTANTS = {
     "decay_scan_inclusive": ("        P[n] = run\n        run = float(gamma)",
                              "        P[n] = float(gamma) ** int(lengths[n]) * run + Sf[n]\n        run = float(gamma)"),
     "brute_force_decay_exponent": ("acc += g ** (i - j) * s * exact(v[j][c])", "acc += g ** (i - j + 1) * s * exact(v[j][c])"),
+    "softmax_no_normalisation": ("    w = w / w.sum(axis=1, keepdims=True)\n", "\n"),
+    "softmax_no_scale": ("    s = (q @ k.T) * scale\n", "    s = q @ k.T\n"),
+    "softmax_causal_exclusive": ("keep = np.arange(k.shape[0])[None, :] <= np.arange(q.shape[0])[:, None]\n        s = np.where",
+                                 "keep = np.arange(k.shape[0])[None, :] < np.arange(q.shape[0])[:, None]\n        s = np.where"),
     "forward_ignores_gamma": ("        return decay_chunked(qp, kp, v, C, gamma, normalize)",
                               "        return chunked(qp, kp, v, C, normalize)"),
 }

@@ -85,3 +85,7 @@ def test_decay_resume():
 
 def test_decay_forward():
     pins.check_decay_forward(oracle)
+
+
+def test_softmax_reference():
+    pins.check_softmax_reference(oracle)

@@ -209,6 +209,19 @@ def decode_pool(w: Workload, n_states: int, pool: int = DECODE_POOL):
     return q, k, v
 
 
+def favor_study_inputs(seed: int = 123, n: int = 128, d: int = 64, scale: float = 0.4):
+    """Inputs of the FAVOR+-vs-softmax error study, shaped like the
+    linear-attention page's experiment (one head, n = 128, d = 64, entries
+    N(0, 1) * 0.4 from numpy's legacy generator seeded 123, drawn Q, K, V in
+    that order), rounded to bf16: q, k, v as [1, n, d] Tensors."""
+    rs = np.random.RandomState(seed)
+    out = []
+    for _ in range(3):
+        bits = f32_to_bf16_bits((rs.randn(n, d) * scale).astype(np.float32))[None]
+        out.append(Tensor(bits, bf16_bits_to_f64(bits), "bf16"))
+    return tuple(out)
+
+
 def random_case(seed: int, BH: int, L: int, d_in: int, d_v: int, dtype: str,
                 scale: float = 1.0):
     """Free-form seeded case for tests: q, k, v of shape [BH, L, d]."""
