@@ -12,6 +12,8 @@ from two pages:
   called *the chunking page*: section ① (the two association orders and the
   d x d state), section ② (the chunked algorithm and its two causal ends) and
   section ③ (the operation counts).
+* the slide deck "Log-Linear Attention" (docswell): the Fenwick-tree token
+  partition, the hierarchical mask, its recurrence and chunkwise computation.
 * "Linear Attention / Performerの理論と実装" (disassemble-channel.com/
   linear-attention/), below called *the linear-attention page*: the kernel
   re-formulation with feature maps and normaliser, the RNN view (state S_t,
@@ -506,6 +508,125 @@ def brute_force_decay(q, k, v, gamma, normalize: bool = False):
                     s += exact(q[i][a]) * exact(k[j][a])
                 acc += g ** (i - j) * s * exact(v[j][c])
             row.append(acc / den if normalize else acc)
+        out.append(row)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Log-linear attention (the slide deck "Log-Linear Attention": Fenwick-tree
+# token partition, the hierarchical mask M, the Fenwick tree recurrence, and
+# the chunkwise computation).  Query t sees key s <= t at level
+#     level(t, s) = 0 if s == t, else floor(log2(t XOR s)) + 1,
+# i.e. level l >= 1 holds the 2^(l-1) keys just below t's prefix with bits
+# below l-1 cleared, present when bit l-1 of t is set (t = 7: {7}, {6}, {4, 5},
+# {0..3}).  With per-token, per-level weights lam[t, l]:
+#     y_t = sum_{s <= t} lam[t, level(t, s)] (q_t . k_s) v_s
+# (M[t, s] = lam[t, level(t, s)]); lam = 1 everywhere is linear attention.
+# The weights are inputs; no normaliser (the slides give none).
+# ---------------------------------------------------------------------------
+def loglinear_levels(L: int) -> int:
+    """Levels a sequence of L tokens uses: 0 .. ceil(log2(L))."""
+    return 1 + max(0, int(L - 1).bit_length())
+
+
+def loglinear_level(t: int, s: int) -> int:
+    """Fenwick level of key s <= t for query t."""
+    return 0 if s == t else int(t ^ s).bit_length()
+
+
+def loglinear_scores_first(q, k, v, lam) -> np.ndarray:
+    """(q k^T * M) v with M[t, s] = lam[t, level(t, s)] for s <= t, 0 above."""
+    q, k, v = _f64(q, k, v)
+    lam = np.asarray(lam, dtype=np.float64)
+    L = q.shape[0]
+    M = np.zeros((L, L))
+    for t in range(L):
+        for s_ in range(t + 1):
+            M[t, s_] = lam[t, loglinear_level(t, s_)]
+    return ((q @ k.T) * M) @ v
+
+
+def loglinear_recurrent(q, k, v, lam) -> np.ndarray:
+    """The Fenwick tree recurrence over level states S^l (sum of k_s^T v_s over
+    level l's bucket): at token t, with b = the position of t's lowest set bit,
+    the buckets of levels 0..b at t-1 merge into level b+1, levels 1..b empty,
+    level 0 takes k_t^T v_t, higher levels stay; then y_t = sum_l lam[t, l] q_t S^l
+    (t = 0: only level 0)."""
+    q, k, v = _f64(q, k, v)
+    lam = np.asarray(lam, dtype=np.float64)
+    L, dk = q.shape
+    dv = v.shape[1]
+    n_lev = lam.shape[1]
+    S = np.zeros((n_lev, dk, dv))
+    out = np.zeros((L, dv))
+    for t in range(L):
+        if t > 0:
+            b = (t & -t).bit_length() - 1
+            merged = S[:b + 1].sum(axis=0)
+            S[1:b + 1] = 0.0
+            S[b + 1] = merged
+        S[0] = np.outer(k[t], v[t])
+        out[t] = sum(lam[t, l] * (q[t] @ S[l]) for l in range(n_lev))
+    return out
+
+
+def loglinear_chunked(q, k, v, lam, C: int) -> np.ndarray:
+    """Chunkwise log-linear attention with chunks of C = 2^c rows (C <= 0 is 1).
+
+    Inside a chunk (levels 0..c) the masked scores act directly.  Across chunks,
+    a key in chunk c' < chunk n sits at level c + floor(log2(n XOR c')) + 1, so
+    the earlier chunks group into buckets of 2^(m-1) whole chunks, one per set
+    bit m-1 of n: chunks [h - 2^(m-1), h) with h = n with its bits below m-1
+    cleared.  Each bucket enters through its summed state:
+        out_n = (q_n k_n^T * M_n) v_n + sum_m diag(lam[., c + m]) q_n S_bucket(n, m).
+    """
+    if C <= 0:
+        C = 1
+    if C & (C - 1):
+        raise ValueError("chunks of a power of two")
+    q, k, v = _f64(q, k, v)
+    lam = np.asarray(lam, dtype=np.float64)
+    L = q.shape[0]
+    cb = C.bit_length() - 1
+    N = (L + C - 1) // C
+    states = [k[n * C:(n + 1) * C].T @ v[n * C:(n + 1) * C] for n in range(N)]
+    out = np.zeros((L, v.shape[1]))
+    for n in range(N):
+        s, e = n * C, min((n + 1) * C, L)
+        rows = np.arange(s, e)
+        M = np.zeros((e - s, e - s))
+        for i, t in enumerate(rows):
+            for j in range(i + 1):
+                M[i, j] = lam[t, loglinear_level(int(t), int(rows[j]))]
+        acc = ((q[s:e] @ k[s:e].T) * M) @ v[s:e]
+        m = 1
+        while (1 << (m - 1)) <= n:
+            if (n >> (m - 1)) & 1:
+                h = (n >> (m - 1)) << (m - 1)
+                Sb = sum(states[c_] for c_ in range(h - (1 << (m - 1)), h))
+                acc = acc + lam[s:e, cb + m][:, None] * (q[s:e] @ Sb)
+            m += 1
+        out[s:e] = acc
+    return out
+
+
+def brute_force_loglinear(q, k, v, lam):
+    """y_{t,c} = sum_{s<=t} lam[t][level(t, s)] sum_a q_{t,a} k_{s,a} v_{s,c}, exact Fractions."""
+    def exact(x):
+        if isinstance(x, (int, np.integer)):
+            return Fraction(int(x))
+        return Fraction(float(x))
+
+    L, dk = len(q), len(q[0])
+    out = []
+    for t in range(L):
+        row = []
+        for c in range(len(v[0])):
+            acc = Fraction(0)
+            for s_ in range(t + 1):
+                dot = sum((exact(q[t][a]) * exact(k[s_][a]) for a in range(dk)), Fraction(0))
+                acc += exact(lam[t][loglinear_level(t, s_)]) * dot * exact(v[s_][c])
+            row.append(acc)
         out.append(row)
     return out
 

@@ -459,3 +459,76 @@ def check_softmax_reference(o, seed: int = 42) -> None:
     qp, kp = o.phi_favor(q * s4, W), o.phi_favor(k * s4, W)
     fav = (qp @ (kp.T @ v)) / (qp @ kp.sum(axis=0))[:, None]
     assert np.allclose(fav, out, rtol=0, atol=2e-2), np.abs(fav - out).max()
+
+
+# ---------------------------------------------------------------------------
+# Log-linear attention (the slide deck "Log-Linear Attention")
+# ---------------------------------------------------------------------------
+def check_loglinear_buckets(o) -> None:
+    """The slides' example, t = 7: level 0 {7}, level 1 {6}, level 2 {4, 5},
+    level 3 {0..3}; in general level l >= 1 holds 2^(l-1) keys, is present
+    exactly when bit l-1 of t is set, and the levels partition 0..t."""
+    got = {}
+    for s_ in range(8):
+        got.setdefault(o.loglinear_level(7, s_), []).append(s_)
+    assert got == {0: [7], 1: [6], 2: [4, 5], 3: [0, 1, 2, 3]}, got
+    for t in range(200):
+        lev = {}
+        for s_ in range(t + 1):
+            lev.setdefault(o.loglinear_level(t, s_), []).append(s_)
+        assert lev[0] == [t]
+        for l, members in lev.items():
+            if l == 0:
+                continue
+            assert (t >> (l - 1)) & 1, (t, l)
+            h = (t >> (l - 1)) << (l - 1)
+            assert members == list(range(h - (1 << (l - 1)), h)), (t, l, members)
+        assert sum(len(m) for m in lev.values()) == t + 1
+    assert o.loglinear_levels(1) == 1 and o.loglinear_levels(2) == 2 and o.loglinear_levels(8) == 4
+    assert o.loglinear_levels(9) == 5
+
+
+def check_loglinear_forms(o, seed: int = 60) -> None:
+    """Integer inputs and integer weights: the masked form, the Fenwick tree
+    recurrence, the chunked form at every power-of-two chunk size (1 up to past
+    L) and exact brute force agree exactly; all weights 1 give linear attention;
+    a weight vector that keeps one level gives that level's bucket sum."""
+    rng = np.random.default_rng([seed, 61])
+    L, dk, dv = 29, 3, 2
+    q, k, v = _ints(rng, (L, dk)), _ints(rng, (L, dk)), _ints(rng, (L, dv))
+    nl = o.loglinear_levels(L)
+    lam = _ints(rng, (L, nl), -2, 3)
+    ref = o.loglinear_scores_first(q, k, v, lam)
+    assert np.array_equal(o.loglinear_recurrent(q, k, v, lam), ref)
+    for C in (0, 1, 2, 4, 8, 16, 32, 64):
+        assert np.array_equal(o.loglinear_chunked(q, k, v, lam, C), ref), C
+    bf = _frac_matrix(o.brute_force_loglinear(q[:9], k[:9], v[:9], lam[:9]))
+    assert np.array_equal(bf, o.loglinear_scores_first(q[:9], k[:9], v[:9], lam[:9]))
+    ones = np.ones((L, nl))
+    lin = o.causal_scores_first(q, k, v)
+    for form in (o.loglinear_scores_first(q, k, v, ones), o.loglinear_recurrent(q, k, v, ones),
+                 o.loglinear_chunked(q, k, v, ones, 8)):
+        assert np.array_equal(form, lin)
+    for l in range(nl):
+        sel = np.zeros((L, nl))
+        sel[:, l] = 1
+        out = o.loglinear_chunked(q, k, v, sel, 4)
+        for t in range(L):
+            members = [s_ for s_ in range(t + 1) if o.loglinear_level(t, s_) == l]
+            want = sum((float(q[t] @ k[s_]) * v[s_] for s_ in members), np.zeros(dv))
+            assert np.array_equal(out[t], want), (l, t)
+
+
+def check_loglinear_causality(o, seed: int = 62) -> None:
+    """Changing token t's key or value leaves every earlier output unchanged."""
+    rng = np.random.default_rng([seed, 63])
+    L, d = 20, 3
+    q, k, v = _ints(rng, (L, d)), _ints(rng, (L, d)), _ints(rng, (L, d))
+    lam = _ints(rng, (L, o.loglinear_levels(L)), 1, 3)
+    base = o.loglinear_chunked(q, k, v, lam, 4)
+    for t in (0, 5, 13):
+        k2, v2 = k.copy(), v.copy()
+        k2[t] += 1
+        v2[t] -= 2
+        out = o.loglinear_chunked(q, k2, v2, lam, 4)
+        assert np.array_equal(out[:t], base[:t]) and not np.array_equal(out[t:], base[t:]), t

@@ -81,6 +81,17 @@ MUTANTS = {
     "softmax_no_scale": ("    s = (q @ k.T) * scale\n", "    s = q @ k.T\n"),
     "softmax_causal_exclusive": ("keep = np.arange(k.shape[0])[None, :] <= np.arange(q.shape[0])[:, None]\n        s = np.where",
                                  "keep = np.arange(k.shape[0])[None, :] < np.arange(q.shape[0])[:, None]\n        s = np.where"),
+    "loglinear_level_off_by_one": ("return 0 if s == t else int(t ^ s).bit_length()",
+                                   "return 0 if s == t else int(t ^ s).bit_length() - 1"),
+    "loglinear_merge_skips_level0": ("            merged = S[:b + 1].sum(axis=0)\n",
+                                     "            merged = S[1:b + 1].sum(axis=0)\n"),
+    "loglinear_merge_one_level_low": ("            S[b + 1] = merged\n", "            S[b] = merged\n"),
+    "loglinear_bucket_shifted": ("Sb = sum(states[c_] for c_ in range(h - (1 << (m - 1)), h))",
+                                 "Sb = sum(states[c_] for c_ in range(h - (1 << (m - 1)), h + 1) if c_ < n)"),
+    "loglinear_chunk_level_index": ("acc = acc + lam[s:e, cb + m][:, None] * (q[s:e] @ Sb)",
+                                    "acc = acc + lam[s:e, cb + m - 1][:, None] * (q[s:e] @ Sb)"),
+    "loglinear_masked_wrong_level": ("            M[t, s_] = lam[t, loglinear_level(t, s_)]",
+                                     "            M[t, s_] = lam[s_, loglinear_level(t, s_)]"),
     "forward_ignores_gamma": ("        return decay_chunked(qp, kp, v, C, gamma, normalize)",
                               "        return chunked(qp, kp, v, C, normalize)"),
 }

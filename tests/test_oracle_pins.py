@@ -89,3 +89,15 @@ def test_decay_forward():
 
 def test_softmax_reference():
     pins.check_softmax_reference(oracle)
+
+
+def test_loglinear_buckets():
+    pins.check_loglinear_buckets(oracle)
+
+
+def test_loglinear_forms():
+    pins.check_loglinear_forms(oracle)
+
+
+def test_loglinear_causality():
+    pins.check_loglinear_causality(oracle)
