@@ -27,7 +27,7 @@ EXPORTS = (
     "la_feature_map", "la_chunk_states", "la_state_scan", "la_chunk_output", "la_chunked_forward",
     "la_chunked_forward_workspace", "la_chunked_forward_group", "la_recurrent_step", "la_status_string", "la_last_error",
     "la_version", "la_chunk_states_decay", "la_state_scan_decay", "la_chunk_output_decay", "la_chunked_forward_decay",
-    "la_recurrent_step_decay",
+    "la_recurrent_step_decay", "la_loglinear_forward", "la_loglinear_forward_workspace", "la_loglinear_levels",
 )
 
 
@@ -66,7 +66,13 @@ def _declare(lib: ctypes.CDLL) -> None:
                                              vp, i32, vp, vp, i64, vp, sz, vp]
     lib.la_recurrent_step_decay.argtypes = [vp, vp, vp, i32, i64, i64, i64, i32, vp, i64, f32, i32, f32, vp, vp, vp,
                                             i32, vp]
-    for name in ("la_feature_map", "la_chunk_states", "la_state_scan", "la_chunk_output", "la_chunked_forward",
+    lib.la_loglinear_forward.argtypes = [vp, vp, vp, i32, i64, i64, i64, i64, i64, vp, i64, vp, i32, vp, sz, vp]
+    lib.la_loglinear_forward_workspace.argtypes = [i32, i64, i64, i64, i64, i64]
+    lib.la_loglinear_forward_workspace.restype = sz
+    lib.la_loglinear_levels.argtypes = [i64]
+    lib.la_loglinear_levels.restype = i64
+    for name in ("la_loglinear_forward", "la_feature_map", "la_chunk_states", "la_state_scan", "la_chunk_output",
+                 "la_chunked_forward",
                  "la_recurrent_step", "la_chunk_states_decay", "la_state_scan_decay", "la_chunk_output_decay",
                  "la_chunked_forward_decay", "la_recurrent_step_decay"):
         getattr(lib, name).restype = i32
@@ -304,6 +310,43 @@ def chunked_forward(q, k, v, C: int, causal: bool = True, normalize: bool = Fals
     if return_state:
         return o, f.S_final, f.z_final
     return o
+
+
+def loglinear_levels(L: int) -> int:
+    """Levels la_loglinear_forward uses for L tokens (1 + bit length of L - 1)."""
+    return int(lib().la_loglinear_levels(L))
+
+
+class LogLinearForward:
+    """A planned log-linear forward (chunks of 64) with its output and workspace."""
+
+    def __init__(self, q, k, v, lam, C: int = 64):
+        torch = _torch()
+        BH, L, d_k = q.shape
+        d_v = v.shape[-1]
+        self.q, self.k, self.v, self.lam, self.C = q, k, v, lam, C
+        self.shape = (BH, L, d_k, d_v)
+        if lam.dtype != torch.float32 or tuple(lam.shape) != (BH, L, loglinear_levels(L)):
+            raise ValueError(f"lam must be float32 {(BH, L, loglinear_levels(L))}")
+        self.o = torch.empty(BH, L, d_v, dtype=torch.bfloat16, device=q.device)
+        ws = int(lib().la_loglinear_forward_workspace(_dtype_code(q), BH, L, d_k, d_v, C))
+        self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=q.device)
+        self.ws_bytes = ws
+        for name, t in (("q", q), ("k", k), ("v", v), ("lam", lam)):
+            _dev(t, name)
+
+    def run(self):
+        BH, L, d_k, d_v = self.shape
+        _check(lib().la_loglinear_forward(self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(),
+                                          _dtype_code(self.q), BH, L, d_k, d_v, self.C, self.lam.data_ptr(),
+                                          self.lam.shape[-1], self.o.data_ptr(), _dtype_code(self.o),
+                                          self.workspace.data_ptr(), self.ws_bytes, _stream_ptr()))
+        return self.o
+
+
+def loglinear_forward(q, k, v, lam, C: int = 64):
+    """Log-linear attention output (see la_loglinear_forward); lam [BH, L, levels] float32."""
+    return LogLinearForward(q, k, v, lam, C).run()
 
 
 def recurrent_step(q, k, v, S, z=None, fmap: str = "identity", W=None, in_scale: float = 1.0,

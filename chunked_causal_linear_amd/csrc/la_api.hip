@@ -693,6 +693,98 @@ la_status la_chunk_output_decay(const void* q, const void* k, const void* v, la_
 }
 
 // ---------------------------------------------------------------------------
+// Log-linear attention (chunks of 64): per-chunk states, their bucket
+// pyramid, then the output kernel.
+static int64_t loglinear_levels_of(int64_t L) {
+    int64_t b = 0;
+    for (int64_t x = L - 1; x > 0; x >>= 1) ++b;
+    return 1 + b;
+}
+
+static int64_t loglinear_pyramid_nodes(int64_t N) {
+    int64_t total = 0;
+    for (int64_t nodes = N; nodes >= 2;) {
+        nodes /= 2;
+        total += nodes;
+    }
+    return total;
+}
+
+static la_status loglinear_check(la_dtype in_dt, int64_t BH, int64_t L, int64_t d_k, int64_t d_v, int64_t C,
+                                 size_t* ws_S, size_t* ws_T) {
+    if (BH < 1 || L < 1) return fail(LA_ERR_INVALID_ARG, "BH and L must be positive");
+    if (in_dt != LA_BF16) return fail(LA_ERR_UNSUPPORTED, "log-linear attention takes LA_BF16 inputs");
+    if (C != 64) return fail(LA_ERR_UNSUPPORTED, "log-linear attention runs on chunks of 64 rows");
+    if (d_k != 64 && d_k != 128) return fail(LA_ERR_UNSUPPORTED, "log-linear attention needs d_k of 64 or 128");
+    if (!pow2_in(d_v, 64, 256)) return fail(LA_ERR_UNSUPPORTED, "log-linear attention needs d_v of 64, 128 or 256");
+    if (loglinear_levels_of(L) > 40) return fail(LA_ERR_UNSUPPORTED, "sequence too long");
+    const int64_t N = cdiv(L, C);
+    if (BH * N * (d_v / 64) > 0x7FFFFFFFLL) return fail(LA_ERR_UNSUPPORTED, "grid too large");
+    *ws_S = N > 1 ? align256((size_t)(BH * N * d_k * d_v * 4)) : 0;
+    *ws_T = align256((size_t)(BH * loglinear_pyramid_nodes(N) * d_k * d_v * 4));
+    return LA_OK;
+}
+
+int64_t la_loglinear_levels(int64_t L) { return L < 1 ? 0 : loglinear_levels_of(L); }
+
+size_t la_loglinear_forward_workspace(la_dtype in_dt, int64_t BH, int64_t L, int64_t d_k, int64_t d_v, int64_t C) {
+    char saved[sizeof(g_last_error)];
+    memcpy(saved, g_last_error, sizeof(saved));
+    size_t a = 0, b = 0;
+    const la_status st = loglinear_check(in_dt, BH, L, d_k, d_v, C, &a, &b);
+    memcpy(g_last_error, saved, sizeof(saved));
+    return st == LA_OK ? a + b : 0;
+}
+
+la_status la_loglinear_forward(const void* q, const void* k, const void* v, la_dtype in_dt, int64_t BH, int64_t L,
+                               int64_t d_k, int64_t d_v, int64_t C, const float* lam, int64_t n_levels, void* o,
+                               la_dtype out_dt, void* workspace, size_t ws_bytes, la_stream_t stream) {
+    g_last_error[0] = 0;
+    if (q == nullptr || k == nullptr || v == nullptr || lam == nullptr || o == nullptr)
+        return fail(LA_ERR_INVALID_ARG, "q, k, v, lam and o must not be NULL");
+    size_t ws_S = 0, ws_T = 0;
+    la_status st = loglinear_check(in_dt, BH, L, d_k, d_v, C, &ws_S, &ws_T);
+    if (st != LA_OK) return st;
+    if (out_dt != LA_BF16) return fail(LA_ERR_UNSUPPORTED, "log-linear attention writes LA_BF16 outputs");
+    if (n_levels != loglinear_levels_of(L))
+        return fail(LA_ERR_INVALID_ARG, "lam must hold %lld levels per token for L = %lld, got %lld",
+                    (long long)loglinear_levels_of(L), (long long)L, (long long)n_levels);
+    if (ws_S + ws_T > 0 && (workspace == nullptr || ws_bytes < ws_S + ws_T))
+        return fail(LA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", ws_S + ws_T,
+                    workspace ? ws_bytes : (size_t)0);
+    hipStream_t s = (hipStream_t)stream;
+    const int64_t N = cdiv(L, C);
+    char* ws = static_cast<char*>(workspace);
+    float* S = N > 1 ? reinterpret_cast<float*>(ws) : nullptr;
+    float* T = ws_T > 0 ? reinterpret_cast<float*>(ws + ws_S) : nullptr;
+    if (N > 1) {
+        st = chunk_states_impl(k, v, false, BH, L, d_k, d_v, C, (int)N, (int)N, S, nullptr, la::FMAP_NONE, 1.0f, s);
+        if (st != LA_OK) return st;
+        st = hip_status(la::run_loglinear_pyramid(S, T, BH, (int)N, (int)loglinear_pyramid_nodes(N), d_k * d_v, s),
+                        "log-linear pyramid launch");
+        if (st != LA_OK) return st;
+    }
+    la::LogLinParams p{};
+    p.q = static_cast<const unsigned short*>(q);
+    p.k = static_cast<const unsigned short*>(k);
+    p.v = static_cast<const unsigned short*>(v);
+    p.lam = lam;
+    p.S = S;
+    p.T = T;
+    p.o = static_cast<unsigned short*>(o);
+    p.L = L;
+    p.N = (int)N;
+    p.n_pyr = (int)loglinear_pyramid_nodes(N);
+    p.n_lev = (int)n_levels;
+    p.n_dvt = (int)(d_v / 64);
+    p.dk = (int)d_k;
+    p.dv = (int)d_v;
+    const int64_t grid = BH * N * p.n_dvt;
+    p.xcd_remap = xcd_ok(grid);
+    return hip_status(la::run_loglinear_fwd(p, grid, s), "log-linear forward launch");
+}
+
+// ---------------------------------------------------------------------------
 static la_status step_entry(const void* q, const void* k, const void* v, la_dtype in_dt, int64_t n_states,
                             int64_t d_in, int64_t d_v, la_fmap f, const void* W, int64_t m, float in_scale,
                             int normalize, float gamma, float* S, float* z, void* o, la_dtype out_dt,

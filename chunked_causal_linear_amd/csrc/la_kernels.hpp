@@ -140,6 +140,29 @@ struct DecodeParams {
     float gamma;    // decayed recurrence: S = gamma S + k^T v, z = gamma z + k (1: none)
 };
 
+// Log-linear attention: bucket pyramid and the output kernel.
+struct LogLinParams {
+    const unsigned short* q;  // [BH, L, dk]
+    const unsigned short* k;  // [BH, L, dk]
+    const unsigned short* v;  // [BH, L, dv]
+    const float* lam;         // [BH, L, n_lev] level weights
+    const float* S;           // [BH, N, dk, dv] per-chunk states (level-1 buckets)
+    const float* T;           // [BH, n_pyr, dk, dv] whole-chunk buckets of levels 2.. (or null)
+    unsigned short* o;        // [BH, L, dv]
+    int64_t L;
+    int N;          // chunks
+    int n_pyr;      // pyramid nodes per head
+    int n_lev;      // levels (1 + bit length of L - 1)
+    int n_dvt;
+    int dk;
+    int dv;
+    int xcd_remap;
+};
+
+hipError_t run_loglinear_pyramid(const float* S, float* T, int64_t BH, int N, int n_pyr, int64_t E,
+                                 hipStream_t s);
+hipError_t run_loglinear_fwd(const LogLinParams& p, int64_t grid, hipStream_t s);
+
 hipError_t run_chunked_fwd_i8(const FwdParamsI8& p, int DK, int DVT, int T, int64_t grid, hipStream_t s);
 hipError_t run_chunk_states_i8(const StatesParamsI8& p, int DK, int DVT, int64_t grid, hipStream_t s);
 hipError_t run_state_scan(const ScanParams& p, int64_t BH, hipStream_t s);

@@ -1,0 +1,231 @@
+// Log-linear attention on chunks of 64 rows (slide deck "Log-Linear
+// Attention": the Fenwick-tree partition of the past, the hierarchical mask M
+// and the chunkwise computation - inside a chunk directly, across chunks
+// through bucket states, one per Fenwick level).
+//
+// Query t sees key s <= t at level 0 (s = t) or floor(log2(t XOR s)) + 1, with
+// per-token weights lam[t, level].  For a chunk n of C = 2^c rows, keys in an
+// earlier chunk n' sit at level c + floor(log2(n XOR n')) + 1, so the earlier
+// chunks form buckets of 2^(m-1) whole chunks, one for each set bit m-1 of n:
+// chunks [h - 2^(m-1), h), h = n with its bits below m-1 cleared.
+//
+//   * run_loglinear_pyramid: the bucket states.  Level 1 buckets are single
+//     chunks (the per-chunk states of phase 1); level m >= 2 node j sums level
+//     m-1 nodes 2j and 2j+1 (a pyramid of N/2 + N/4 + ... states; each thread
+//     owns four consecutive state elements through every level).
+//   * loglinear_fwd: one workgroup per (head, chunk, 64 value columns), four
+//     waves of 16 query rows.  Intra part: S^T = K Q^T on the matrix cores, each
+//     score times lam[query, level] (0 above the diagonal), then V^T S^T;
+//     inter part: for every set bit of n, the bucket state goes through LDS as
+//     bf16 (P^T, rows = value columns), O_m^T = P^T Q^T, and O += lam[t, c + m]
+//     O_m.  Outputs come out transposed (a lane holds four consecutive columns
+//     of one row) and are stored as 8-byte pieces.
+#include "la_common.hpp"
+#include "la_kernels.hpp"
+
+namespace la {
+
+namespace {
+
+constexpr int LL_C = 64;          // rows per chunk
+constexpr int LL_CB = 6;          // log2 of it
+constexpr int LL_DVT = 64;        // value columns per workgroup
+constexpr int LL_NLMAX = 40;      // levels held in LDS (bit length of L - 1 plus one)
+
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+
+__device__ __forceinline__ uint2 tr_read_ll(const char* p) {
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)p));
+}
+
+// 16-byte row operand: row r, elements k0 + 8g .. k0 + 8g + 7 of a row-major
+// tile with a row stride of `stride` elements.
+__device__ __forceinline__ bf16x8 row_operand(const u16* t, int stride, int r, int k0, int g) {
+    return as_bf16x8(*reinterpret_cast<const uint4*>(t + r * stride + k0 + 8 * g));
+}
+
+// Column operand over keys key0 .. key0 + 31 in the order the S^T accumulators
+// come out in (lane group g: keys 4g..4g+3 and 16+4g..16+4g+3), column base + n
+// for lane n of the group (transpose reads of four rows at a time).
+__device__ __forceinline__ bf16x8 col_operand(const u16* t, int stride, int key0, int base, int lane) {
+    const int g = lane >> 4, rr = (lane & 15) >> 2, c4 = 4 * (lane & 3);
+    const char* p = reinterpret_cast<const char*>(t);
+    const uint2 lo = tr_read_ll(p + ((key0 + 4 * g + rr) * stride + base + c4) * 2);
+    const uint2 hi = tr_read_ll(p + ((key0 + 16 + 4 * g + rr) * stride + base + c4) * 2);
+    return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
+__device__ __forceinline__ int bit_length(unsigned x) { return x == 0 ? 0 : 32 - __builtin_clz(x); }
+
+__global__ __launch_bounds__(256) void loglinear_pyramid_kernel(const float4* __restrict__ S, float4* __restrict__ T,
+                                                                int64_t BH, int N, int n_pyr, int64_t E4) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= BH * E4) return;
+    const int64_t bh = idx / E4, e = idx % E4;
+    const float4* src = S + bh * N * E4 + e;  // level 1: the chunk states
+    int64_t src_stride = E4;
+    float4* out = T + bh * (int64_t)n_pyr * E4 + e;
+    int nodes = N;
+    while (nodes >= 2) {
+        const int next = nodes / 2;
+        for (int j = 0; j < next; ++j) {
+            const float4 a = src[(2 * j) * src_stride], b = src[(2 * j + 1) * src_stride];
+            out[j * E4] = make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+        }
+        src = out;
+        src_stride = E4;
+        out += next * E4;
+        nodes = next;
+    }
+}
+
+template <int DK>
+__global__ __launch_bounds__(256) void loglinear_fwd(LogLinParams p) {
+    constexpr int QS = DK + 8, VS = LL_DVT + 8;  // padded row strides (elements)
+    constexpr int NKA = DK / 32;
+    __shared__ __attribute__((aligned(16))) u16 Qs[LL_C * QS];
+    __shared__ __attribute__((aligned(16))) u16 Ks[LL_C * QS];
+    __shared__ __attribute__((aligned(16))) u16 Vs[LL_C * VS];
+    __shared__ __attribute__((aligned(16))) u16 Ps[LL_DVT * QS];  // bucket state, transposed: Ps[j][a]
+    __shared__ float lam_s[LL_C * LL_NLMAX];
+
+    const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE, l16 = lane % 16, g = lane / 16;
+    int w = blockIdx.x;
+    if (p.xcd_remap) w = (w & 7) * (gridDim.x >> 3) + (w >> 3);
+    const int jt = w % p.n_dvt;
+    const int n = (w / p.n_dvt) % p.N;
+    const int64_t bh = w / (p.n_dvt * p.N);
+    const int col0 = jt * LL_DVT;
+    const int64_t r0 = (int64_t)n * LL_C;
+    const int valid = (int)(p.L - r0 < LL_C ? p.L - r0 : LL_C);
+    const int dv = p.dv;
+
+    // chunk tiles into LDS (rows past the end are zero)
+    for (int i = tid; i < LL_C * (DK / 8); i += 256) {
+        const int r = i / (DK / 8), cg = i % (DK / 8);
+        uint4 qv = make_uint4(0, 0, 0, 0), kv = qv;
+        if (r < valid) {
+            qv = *reinterpret_cast<const uint4*>(p.q + (bh * p.L + r0 + r) * DK + cg * 8);
+            kv = *reinterpret_cast<const uint4*>(p.k + (bh * p.L + r0 + r) * DK + cg * 8);
+        }
+        *reinterpret_cast<uint4*>(Qs + r * QS + cg * 8) = qv;
+        *reinterpret_cast<uint4*>(Ks + r * QS + cg * 8) = kv;
+    }
+    for (int i = tid; i < LL_C * (LL_DVT / 8); i += 256) {
+        const int r = i / (LL_DVT / 8), cg = i % (LL_DVT / 8);
+        uint4 vv = make_uint4(0, 0, 0, 0);
+        if (r < valid) vv = *reinterpret_cast<const uint4*>(p.v + (bh * p.L + r0 + r) * dv + col0 + cg * 8);
+        *reinterpret_cast<uint4*>(Vs + r * VS + cg * 8) = vv;
+    }
+    for (int i = tid; i < LL_C * LL_NLMAX; i += 256) {
+        const int r = i / LL_NLMAX, l = i % LL_NLMAX;
+        lam_s[i] = (r < valid && l < p.n_lev) ? p.lam[(bh * p.L + r0 + r) * p.n_lev + l] : 0.f;
+    }
+    __syncthreads();
+
+    const int qr = wave * 16 + l16;  // this lane's query row in the chunk
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    f32x4 O[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) O[c] = zero4;
+
+    // ---- intra: scores of query block `wave` against key blocks kb <= wave
+    {
+        f32x4 St[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) St[kb] = zero4;
+#pragma unroll
+        for (int ks = 0; ks < NKA; ++ks) {
+            const bf16x8 qa = row_operand(Qs, QS, qr, ks * 32, g);
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+                if (kb <= wave) St[kb] = mfma_bf16(row_operand(Ks, QS, kb * 16 + l16, ks * 32, g), qa, St[kb]);
+        }
+        // St[kb][i] = score of key 16 kb + 4g + i and query qr: weight by its level
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int key = kb * 16 + 4 * g + i;
+                const int lev = key == qr ? 0 : bit_length((unsigned)(key ^ qr));
+                St[kb][i] = (kb <= wave && key <= qr) ? St[kb][i] * lam_s[qr * LL_NLMAX + lev] : 0.f;
+            }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            if (2 * kk > wave) break;
+            const bf16x8 sb = pack_acc_bf16(St[2 * kk], St[2 * kk + 1]);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) O[c] = mfma_bf16(col_operand(Vs, VS, kk * 32, c * 16, lane), sb, O[c]);
+        }
+    }
+
+    // ---- inter: one bucket state per set bit of n
+    const int64_t E = (int64_t)DK * dv;
+    int pyr_base = 0;  // first node of level m in the pyramid (levels >= 2)
+    int level_nodes = p.N / 2;
+    for (int m = 1; (1 << (m - 1)) <= n; ++m) {
+        if (m >= 3) {
+            pyr_base += level_nodes;
+            level_nodes /= 2;
+        }
+        if (!((n >> (m - 1)) & 1)) continue;
+        const int node = (n >> (m - 1)) - 1;
+        const float* P = m == 1 ? p.S + (bh * p.N + node) * E : p.T + (bh * p.n_pyr + pyr_base + node) * E;
+        __syncthreads();  // Ps free
+        for (int i = tid; i < DK * (LL_DVT / 4); i += 256) {
+            const int a = i / (LL_DVT / 4), j4 = (i % (LL_DVT / 4)) * 4;
+            const float4 x = *reinterpret_cast<const float4*>(P + (int64_t)a * dv + col0 + j4);
+            const uint32_t ab = pack2_bf16(x.x, x.y), cd = pack2_bf16(x.z, x.w);
+            Ps[(j4 + 0) * QS + a] = (u16)(ab & 0xFFFFu);
+            Ps[(j4 + 1) * QS + a] = (u16)(ab >> 16);
+            Ps[(j4 + 2) * QS + a] = (u16)(cd & 0xFFFFu);
+            Ps[(j4 + 3) * QS + a] = (u16)(cd >> 16);
+        }
+        __syncthreads();
+        f32x4 Om[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) Om[c] = zero4;
+#pragma unroll
+        for (int ks = 0; ks < NKA; ++ks) {
+            const bf16x8 qb = row_operand(Qs, QS, qr, ks * 32, g);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) Om[c] = mfma_bf16(row_operand(Ps, QS, c * 16 + l16, ks * 32, g), qb, Om[c]);
+        }
+        const float lw = lam_s[qr * LL_NLMAX + LL_CB + m];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) O[c] += lw * Om[c];
+    }
+
+    // ---- output: lane holds columns 16c + 4g .. +3 of row qr
+    if (qr < valid) {
+        u16* o = p.o + (bh * p.L + r0 + qr) * dv + col0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            *reinterpret_cast<uint2*>(o + c * 16 + 4 * g) =
+                make_uint2(pack2_bf16(O[c][0], O[c][1]), pack2_bf16(O[c][2], O[c][3]));
+    }
+}
+
+}  // namespace
+
+hipError_t run_loglinear_pyramid(const float* S, float* T, int64_t BH, int N, int n_pyr, int64_t E, hipStream_t s) {
+    if (N < 2 || T == nullptr) return hipSuccess;
+    const int64_t E4 = E / 4;
+    const int64_t blocks = (BH * E4 + 255) / 256;
+    hipLaunchKernelGGL(loglinear_pyramid_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                       reinterpret_cast<const float4*>(S), reinterpret_cast<float4*>(T), BH, N, n_pyr, E4);
+    return hipGetLastError();
+}
+
+hipError_t run_loglinear_fwd(const LogLinParams& p, int64_t grid, hipStream_t s) {
+    if (p.n_lev > LL_NLMAX || p.dv % LL_DVT != 0) return hipErrorInvalidValue;
+    switch (p.dk) {
+        case 64: hipLaunchKernelGGL(loglinear_fwd<64>, dim3((unsigned)grid), dim3(256), 0, s, p); break;
+        case 128: hipLaunchKernelGGL(loglinear_fwd<128>, dim3((unsigned)grid), dim3(256), 0, s, p); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace la

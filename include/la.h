@@ -274,6 +274,34 @@ la_status la_recurrent_step_decay(const void* q, const void* k, const void* v, l
                                   float gamma, float* S, float* z, void* o, la_dtype out_dt,
                                   la_stream_t stream);
 
+/*
+ * Log-linear attention (slide deck "Log-Linear Attention": the Fenwick-tree
+ * partition of the past, the hierarchical mask and its chunkwise
+ * computation).  Query t sees key s <= t at level 0 when s == t, else
+ * floor(log2(t XOR s)) + 1 (level l >= 1 holds the 2^(l-1) keys just below t
+ * with its bits under l-1 cleared); with per-token level weights lam:
+ *     o_t = sum_{s <= t} lam[t, level(t, s)] (q_t . k_s) v_s
+ * (lam = 1 everywhere is causal linear attention; no normaliser, no map).
+ *
+ *   q, k [BH, L, d_k], v [BH, L, d_v]: LA_BF16; d_k in {64, 128}, d_v in
+ *        {64, 128, 256}; C must be 64 (chunks of 64 rows).
+ *   lam  [BH, L, n_levels] float32 (device), n_levels = la_loglinear_levels(L).
+ *   o    [BH, L, d_v] LA_BF16.
+ *   workspace  la_loglinear_forward_workspace(...) bytes (per-chunk states and
+ *        their bucket sums; 0 for a single chunk).
+ * Errors: LA_ERR_INVALID_ARG (NULL pointer, non-positive size, wrong
+ * n_levels), LA_ERR_UNSUPPORTED (other types, widths or chunk sizes),
+ * LA_ERR_WORKSPACE; nothing is launched on an error.
+ */
+la_status la_loglinear_forward(const void* q, const void* k, const void* v, la_dtype in_dt,
+                               int64_t BH, int64_t L, int64_t d_k, int64_t d_v, int64_t C,
+                               const float* lam, int64_t n_levels, void* o, la_dtype out_dt,
+                               void* workspace, size_t ws_bytes, la_stream_t stream);
+size_t la_loglinear_forward_workspace(la_dtype in_dt, int64_t BH, int64_t L, int64_t d_k,
+                                      int64_t d_v, int64_t C);
+/* Levels a sequence of L tokens uses: 1 + the bit length of L - 1 (0 for L < 1). */
+int64_t la_loglinear_levels(int64_t L);
+
 /* Static description of a status code. */
 const char* la_status_string(la_status s);
 /* Thread-local description of the last failure on this thread ("" if none). */

@@ -220,3 +220,30 @@ def test_decay_entry_point_errors():
                                      b.LA_BF16, None, None, None) == b.LA_ERR_UNSUPPORTED
     assert lib.la_recurrent_step_decay(FAKE, FAKE, FAKE, b.LA_BF16, 4, 64, 64, 0, None, 0, 1.0, 0, 0.0, FAKE, None,
                                        FAKE, b.LA_F32, None) == b.LA_ERR_INVALID_ARG
+
+
+def test_loglinear_entry_point_errors():
+    """Log-linear attention: level count, workspace size and argument checks."""
+    lib = la.lib()
+    assert [lib.la_loglinear_levels(L) for L in (0, 1, 2, 3, 8, 9, 8192)] == [0, 1, 2, 3, 4, 5, 14]
+    # 128 heads x 8192 rows, d = 128: 128 chunk states + 64 + 32 + ... + 1 = 127 bucket sums per head
+    ws = lib.la_loglinear_forward_workspace(b.LA_BF16, 128, 8192, 128, 128, 64)
+    assert ws == 128 * 128 * 128 * 128 * 4 + 128 * 127 * 128 * 128 * 4
+    assert lib.la_loglinear_forward_workspace(b.LA_BF16, 2, 64, 64, 64, 64) == 0  # one chunk
+    assert lib.la_loglinear_forward_workspace(b.LA_BF16, 2, 1000, 64, 64, 32) == 0  # unsupported chunk size
+
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, in_dt=b.LA_BF16, BH=2, L=1000, d_k=64, d_v=64, C=64, lam=FAKE,
+                 n_lev=lib.la_loglinear_levels(1000), o=FAKE, out_dt=b.LA_BF16, ws=None, ws_bytes=0)
+        a.update(kw)
+        return lib.la_loglinear_forward(a["q"], a["k"], a["v"], a["in_dt"], a["BH"], a["L"], a["d_k"], a["d_v"],
+                                        a["C"], a["lam"], a["n_lev"], a["o"], a["out_dt"], a["ws"], a["ws_bytes"],
+                                        None)
+    assert call(lam=None) == b.LA_ERR_INVALID_ARG
+    assert call(n_lev=5) == b.LA_ERR_INVALID_ARG
+    assert call(C=32) == b.LA_ERR_UNSUPPORTED
+    assert call(d_k=32) == b.LA_ERR_UNSUPPORTED
+    assert call(d_v=32) == b.LA_ERR_UNSUPPORTED
+    assert call(in_dt=b.LA_I8) == b.LA_ERR_UNSUPPORTED
+    assert call(out_dt=b.LA_F32) == b.LA_ERR_UNSUPPORTED
+    assert call() == b.LA_ERR_WORKSPACE

@@ -222,6 +222,13 @@ def favor_study_inputs(seed: int = 123, n: int = 128, d: int = 64, scale: float 
     return tuple(out)
 
 
+def loglinear_weights(seed: int, BH: int, L: int, n_levels: int, lo: float = 0.25, hi: float = 1.25) -> np.ndarray:
+    """Per-token level weights for log-linear attention, float32 [BH, L, n_levels],
+    uniform on [lo, hi) from a seeded generator."""
+    rng = np.random.default_rng([seed, 99])
+    return rng.uniform(lo, hi, size=(BH, L, n_levels)).astype(np.float32)
+
+
 def random_case(seed: int, BH: int, L: int, d_in: int, d_v: int, dtype: str,
                 scale: float = 1.0):
     """Free-form seeded case for tests: q, k, v of shape [BH, L, d]."""
