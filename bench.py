@@ -439,6 +439,33 @@ def run_extras(args, out):
         torch.cuda.empty_cache()
     rows["a4_forward"] = fwd
     rows["next_decay"] = decay
+    # ---- next: log-linear attention at the headline shape (chunks of 64, random level weights)
+    qd = dev_bf16(wl.full_tensor(3, wl.TENSOR_Q, w3.BH, w3.L, w3.d_in, "bf16", 1.0 / np.sqrt(w3.d_in), False).bits)
+    kd = dev_bf16(wl.full_tensor(3, wl.TENSOR_K, w3.BH, w3.L, w3.d_in, "bf16", 1.0 / np.sqrt(w3.d_in), False).bits)
+    vd = dev_bf16(wl.full_tensor(3, wl.TENSOR_V, w3.BH, w3.L, w3.d_v, "bf16", 1.0 / np.sqrt(w3.d_in), False).bits)
+    nl = la.loglinear_levels(w3.L)
+    lamd = torch.from_numpy(wl.loglinear_weights(3, w3.BH, w3.L, nl)).cuda()
+    f = la.LogLinearForward(qd, kd, vd, lamd)
+    ms = row_time(f.run)
+    N = w3.L // 64
+    pops = sum(bin(n).count("1") for n in range(N))
+    state = w3.d_k * w3.d_v * 4
+    wk3 = Work(w3.BH, w3.L, w3.d_in, w3.d_k, w3.d_v, 64)
+    ll_bytes = (wk3.fused_bytes() + w3.BH * w3.L * nl * 4           # q, k, v, o and the level weights
+                + w3.BH * N * state * 2                              # phase 1 reads k, v (in fused) and writes N states
+                + w3.BH * (N - 1) * state * 2                        # the pyramid reads and writes ~N states
+                + w3.BH * pops * state)                              # each chunk reads one bucket per set bit
+    lq, lk, lv = (wl.head_tensor(3, t, 0, 1024, w3.d_in, "bf16", 1.0 / np.sqrt(w3.d_in)).exact for t in
+                  (wl.TENSOR_Q, wl.TENSOR_K, wl.TENSOR_V))
+    lam_h = wl.loglinear_weights(3, 1, 1024, oracle.loglinear_levels(1024))[0].astype(np.float64)
+    rows["next_loglinear"] = {
+        "shape": f"BH={w3.BH} L={w3.L} d={w3.d_in} C=64, {nl} levels", "ms": ms,
+        "tokens_per_s": w3.B * w3.L / (ms * 1e-3), "vs_linear_forward": fwd["w3_C64"]["ms"] / ms,
+        **hbm(ll_bytes, ms), "bytes": ll_bytes,
+        "oracle_s_per_head": _oracle_time(lambda: oracle.loglinear_chunked(lq, lk, lv, lam_h, 64)) * w3.L / 1024,
+        "oracle_sample": "oracle.loglinear_chunked on 1024 rows of one head, scaled to L"}
+    del f, qd, kd, vd, lamd
+    torch.cuda.empty_cache()
     # ---- next: FAVOR+ against exact softmax (the linear-attention page's error study)
     qf, kf, vf = wl.favor_study_inputs()
     dd = qf.exact.shape[2]
