@@ -23,16 +23,17 @@
 //    stalls stay on the copy waves.
 //
 // The sequence is walked in tiles of TT rows (64, or 128 for chunks of 128),
-// NSTAGE LDS stages of (Q, K, V) tiles (3, or 2 for 128-row tiles).  Per tile j,
-// after the barrier B(j) that makes tile j visible:
+// NSTAGE LDS stages of (Q, K, V) tiles (as many as fit 160 KB, at most four).
+// Per tile j, after the barrier B(j) that makes tile j visible:
 //   compute waves: products of tile j from stage j % NSTAGE, output into the V
 //     tile of that stage;
 //   copy waves: read the output of tile j - 1 from stage (j - 1) % NSTAGE,
-//     refill that stage with tile j + NSTAGE - 1, store the output rows, wait
-//     until tile j + 1 has landed, B(j + 1).
-// The wait count is exact: the only memory instructions issued after tile
-// j + 1's copies and not needed yet are the copies of the tiles after it, and
-// loads complete in order (stores in between do not change that).
+//     refill that stage with tile j + NSTAGE - 1, wait until tile j + 1 has
+//     landed, store the output rows of tile j - 1, B(j + 1).
+// The wait counts only the copies of the tiles issued after tile j + 1: loads
+// complete in order, so once no more than those are outstanding, tile j + 1 is
+// in, whatever the order in which the stores in between complete.  The stores
+// go out after the wait so that it does not hold on them.
 //
 // LDS tiles are row-major with the 16-byte segment index XORed with the row
 // (the copy picks, per lane, which global segment lands in which LDS slot):
@@ -187,7 +188,8 @@ __global__ __launch_bounds__(4 * WAVE) __attribute__((amdgpu_waves_per_eu(1, 1))
 void chunked_fwd_pipe(FwdParams p) {
     using namespace pipe;
     constexpr int TT = CH > 64 ? CH : 64;          // rows per tile
-    constexpr int NSTAGE = 3 * sizeof(Stage<DK, DVT, TT>) <= 160 * 1024 ? 3 : 2;  // LDS stages
+    constexpr int NFIT = (int)(160 * 1024 / sizeof(Stage<DK, DVT, TT>));
+    constexpr int NSTAGE = NFIT < 4 ? NFIT : 4;    // LDS stages
     constexpr int CPW = DVT / 32;                  // 16-column blocks per pair
     constexpr int NCB = CPW + (NORM ? 1 : 0);      // + the denominator block
     constexpr int NKA = DK / 32;                   // k-steps over the feature index
@@ -199,7 +201,8 @@ void chunked_fwd_pipe(FwdParams p) {
     static_assert(DVT == 64 || (DVT == 32 && DK == 256), "tile of 64 value columns (32 at feature width 256)");
     static_assert(CH == 32 || CH == 64 || CH == 128, "chunks of 32, 64 or 128 rows");
     static_assert(DK == 64 || DK == 128 || DK == 256, "feature width 64, 128 or 256");
-    static_assert(NL < 64, "vmcnt range");
+    static_assert(NSTAGE >= 2, "two stages at least");
+    static_assert((NSTAGE - 2) * NL + NCQ + NCV < 64, "vmcnt range");
     static_assert(NSTAGE * (int)sizeof(Stage<DK, DVT, TT>) <= 160 * 1024, "LDS");
     typedef Stage<DK, DVT, TT> StageT;
 
@@ -276,20 +279,20 @@ void chunked_fwd_pipe(FwdParams p) {
                 dma16(vb_, (uint32_t)(((r < last ? r : last) * dv + seg * 8) * 2), lv + b * WAVE * 16);
             }
         };
-        // Output rows of tile t sit in the V tile of stage `from`: instruction
-        // i, lane l covers row (h * NCV + i) * RPV + l / VSEG, segment l % VSEG.
-        // Read them, refill the stage with tile `refill` (if any), store them.
-        auto drain_refill = [&](const StageT& from, int64_t t, int64_t refill, StageT& to)
-            __attribute__((always_inline)) {
-            u32x4 ob[NCV];
+        // Output rows of a tile sit in the V tile of its stage: instruction i,
+        // lane l covers row (h * NCV + i) * RPV + l / VSEG, segment l % VSEG.
+        // read_out takes them into registers (and waits for the reads, so the
+        // stage can be refilled); store_out writes them to rows of tile t.
+        auto read_out = [&](const StageT& from, u32x4 (&ob)[NCV]) __attribute__((always_inline)) {
 #pragma unroll
             for (int i = 0; i < NCV; ++i) {
                 const int r = (h * NCV + i) * RPV + lane / VSEG, seg = lane % VSEG;
                 ob[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(from.v) +
                                                         tile_off<VSEG>(r, seg * 8));
             }
-            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): reads done before the refill
-            if (refill >= 0) issue(refill, to);
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        };
+        auto store_out = [&](int64_t t, const u32x4 (&ob)[NCV]) __attribute__((always_inline)) {
             const int valid = valid_rows(t);
             u16* o = reinterpret_cast<u16*>(p.o) + (bh * L + t * TT) * dv + col0;
 #pragma unroll
@@ -313,36 +316,43 @@ void chunked_fwd_pipe(FwdParams p) {
                     u32x4{y.x, y.y, y.z, y.w};
             }
         };
-        // wait until this wave's copies of a tile have landed (X = copies issued
-        // after them: the next tile's), mapping Q and K as soon as they are in
-        // `more`: the next tile's copies were issued after this tile's (three
-        // stages, not at the end); the wait counts are immediates, so each is
-        // picked by a branch rather than by duplicating the mapping code
-        auto land = [&](bool more, StageT& s) __attribute__((always_inline)) {
-            if constexpr (NSTAGE == 2) more = false;
+        // wait until this wave's copies of a tile have landed, given that the
+        // copies of `after` more tiles were issued after them, mapping Q and K
+        // as soon as they are in.  The wait counts are immediates, so each is
+        // picked by a branch rather than by duplicating the mapping code.
+        auto wait_loads = [&](int after, auto extra) __attribute__((always_inline)) {
+            constexpr int X = decltype(extra)::value;
+            if constexpr (NSTAGE >= 4)
+                if (after >= 2) {
+                    wait_vm<2 * NL + X>();
+                    return;
+                }
+            if constexpr (NSTAGE >= 3)
+                if (after >= 1) {
+                    wait_vm<NL + X>();
+                    return;
+                }
+            wait_vm<X>();
+        };
+        auto land = [&](int after, StageT& s) __attribute__((always_inline)) {
             if constexpr (PHI) {
-                if (more)
-                    wait_vm<(NSTAGE == 3 ? NL : 0) + NCQ + NCV>();
-                else
-                    wait_vm<NCQ + NCV>();
+                wait_loads(after, ic<NCQ + NCV>{});
                 phi_tile(s.q);
-                if (more)
-                    wait_vm<(NSTAGE == 3 ? NL : 0) + NCV>();
-                else
-                    wait_vm<NCV>();
+                wait_loads(after, ic<NCV>{});
                 phi_tile(s.k);
             }
-            if (more)
-                wait_vm<NSTAGE == 3 ? NL : 0>();
-            else
-                wait_vm<0>();
+            wait_loads(after, ic<0>{});
+        };
+        // tiles issued after tile t while t is the oldest in flight
+        auto after_of = [&](int64_t t) -> int {
+            const int64_t newest = t + NSTAGE - 2 < t_end - 1 ? t + NSTAGE - 2 : t_end - 1;
+            return (int)(newest - t);
         };
 
 #pragma unroll
         for (int s0 = 0; s0 < NSTAGE - 1; ++s0)
             if (t_begin + s0 < t_end) issue(t_begin + s0, st[s0]);
-        // the first tile: the copies issued after it are those of the tile after it
-        land(t_begin + 1 < t_end, st[0]);
+        land(after_of(t_begin), st[0]);
 
         // The copy side walks the stages with a run-time index (its accesses
         // take computed addresses anyway), so its code appears once.
@@ -355,22 +365,26 @@ void chunked_fwd_pipe(FwdParams p) {
                 zero_tail(st[si], valid_rows(t));
                 __syncthreads();
             }
-            const int64_t refill = t + NSTAGE - 1 < t_end ? t + NSTAGE - 1 : -1;
-            if (t > t_begin)
-                drain_refill(st[sp], t - 1, refill, st[sp]);
-            else if (refill >= 0)
-                issue(refill, st[sp]);
-            // tile t + 1 must have landed before B(t + 1); the loads issued after
-            // it are those of tile t + 2 (three stages, if any); loads complete in order
+            // the output of tile t - 1 leaves stage sp, which takes tile
+            // t + NSTAGE - 1; the stores go out after the wait for tile t + 1,
+            // so that the wait does not hold on them
+            u32x4 ob[NCV];
+            if (t > t_begin) read_out(st[sp], ob);
+            if (t + NSTAGE - 1 < t_end) issue(t + NSTAGE - 1, st[sp]);
+            // tile t + 1 must have landed before B(t + 1); the newest tile
+            // issued is now t + NSTAGE - 1 (or the last one)
             if (t + 1 < t_end)
-                land(t + 2 < t_end, st[sn]);
-            else
-                wait_vm<0>();
+                land(after_of(t + 1), st[sn]);
+            if (t > t_begin) store_out(t - 1, ob);
             si = sn;
         }
         __syncthreads();  // the last tile's output is in its stage
-        const int sl = si == 0 ? NSTAGE - 1 : si - 1;
-        drain_refill(st[sl], t_end - 1, -1, st[sl]);
+        {
+            const int sl = si == 0 ? NSTAGE - 1 : si - 1;
+            u32x4 ob[NCV];
+            read_out(st[sl], ob);
+            store_out(t_end - 1, ob);
+        }
         return;
     }
 
@@ -762,8 +776,10 @@ void chunked_fwd_pipe(FwdParams p) {
     for (int64_t t = t_begin; t < t_end; t += NSTAGE) {
         step(ic<0>{}, t);
         if (t + 1 < t_end) step(ic<1>{}, t + 1);
-        if constexpr (NSTAGE == 3)
-            if (t + 2 < t_end) step(ic<NSTAGE - 1>{}, t + 2);
+        if constexpr (NSTAGE >= 3)
+            if (t + 2 < t_end) step(ic<2>{}, t + 2);
+        if constexpr (NSTAGE >= 4)
+            if (t + 3 < t_end) step(ic<3>{}, t + 3);
     }
     __syncthreads();  // matches the copy waves' final barrier
 
