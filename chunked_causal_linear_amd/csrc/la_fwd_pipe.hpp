@@ -63,10 +63,13 @@
 // the masked scores, so every lane ends up holding the denominator of its row
 // next to the four numerators it divides.
 //
-// elu+1 (same page, the ELU feature map; PHI): each copy wave maps its own
-// 16-byte slots of a tile in place once they have landed, so the mapped values
-// never go through memory.  The copies are issued Q, K, V, so the mapping of Q
-// and K overlaps the arrival of the rest of the tile.  The state here sums
+// elu+1 (same page, the ELU feature map; PHI): all four waves map the Q and K
+// of a landed tile in place, in LDS, so the mapped values never go through
+// memory.  Each copy wave maps its share as soon as the tile has landed (before
+// B(j)); each compute wave maps its share after B(j), and a second barrier
+// B'(j) separates that from the products.  K rows past the end of the sequence
+// are set to zero by the mapping instead of by a separate pass.  The state
+// here sums
 // bf16(phi(k)): the products read it rounded to bf16 anyway, so that rounding
 // stays below the operand rounding of the inter product; a returned final
 // state or normaliser, where it would not, is summed elsewhere with phi(k)'s
@@ -243,6 +246,51 @@ void chunked_fwd_pipe(FwdParams p) {
         for (int i = tid; i < n; i += 4 * WAVE) kk[i] = make_uint4(0, 0, 0, 0);
     };
 
+    // elu+1 of a landed tile's Q and K in place.  The tiles are 2 NP blocks of
+    // 64 16-byte pieces (Q's NP, then K's); the compute waves take NPC blocks
+    // each, the copy waves NPK, and lane l of a block maps its piece l.  The
+    // compute waves take half with 64-row tiles and a quarter with 128-row
+    // tiles, whose products leave them less time (the shares that measured
+    // fastest).
+    constexpr int NP = 2 * NCQ;
+    constexpr int NPC = TT > 64 ? NP / 4 : NP / 2, NPK = NP - NPC;
+    auto phi_blocks = [&](StageT& s, int valid, auto first_, auto count) __attribute__((always_inline)) {
+        constexpr int FIRST = decltype(first_)::value, N = decltype(count)::value;
+        // four pieces in flight at a time (bounded registers)
+#pragma unroll
+        for (int i0 = 0; i0 < N; i0 += 4) {
+            uint4 x[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int blk = FIRST + i0 + i, slot = (blk % NP) * WAVE + lane;
+                if (i0 + i < N) x[i] = *reinterpret_cast<const uint4*>((blk < NP ? s.q : s.k) + slot * 8);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int blk = FIRST + i0 + i, slot = (blk % NP) * WAVE + lane;
+                if (i0 + i < N) {
+                    const bool live = blk < NP || slot / QSEG < valid;  // K rows past the end become zero
+                    *reinterpret_cast<uint4*>((blk < NP ? s.q : s.k) + slot * 8) =
+                        live ? elu1_bf16x8(x[i], p.in_scale) : make_uint4(0, 0, 0, 0);
+                }
+            }
+        }
+    };
+    // this wave's share of the mapping of a landed tile
+    auto phi_share = [&](StageT& s, int valid) __attribute__((always_inline)) {
+        if (copier) {
+            if (h == 0)
+                phi_blocks(s, valid, ic<2 * NPC>{}, ic<NPK>{});
+            else
+                phi_blocks(s, valid, ic<2 * NPC + NPK>{}, ic<NPK>{});
+        } else {
+            if (h == 0)
+                phi_blocks(s, valid, ic<0>{}, ic<NPC>{});
+            else
+                phi_blocks(s, valid, ic<NPC>{}, ic<NPC>{});
+        }
+    };
+
     if (copier) {
         // ================= copy wave h =================
         typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -259,8 +307,6 @@ void chunked_fwd_pipe(FwdParams p) {
             const u16* kb_ = kh + r0 * DK;
             const u16* vb_ = vh + r0 * dv;
             const uint32_t lq = lds_addr(s.q), lk = lds_addr(s.k), lv = lds_addr(s.v);
-            // Q, then K, then V: with elu+1 applied here the Q and K tiles are
-            // mapped while the rest is still arriving
             auto qk_off = [&](int i) __attribute__((always_inline)) {
                 const int b = h * NCQ + i;  // copy instruction within the tile
                 const int slot = b * WAVE + lane;
@@ -302,46 +348,21 @@ void chunked_fwd_pipe(FwdParams p) {
             }
         };
 
-        // elu+1 of this wave's own slots of a landed Q or K tile, in place
-        auto phi_tile = [&](u16* tile) __attribute__((always_inline)) {
-            u32x4 x[NCQ];
-#pragma unroll
-            for (int i = 0; i < NCQ; ++i)
-                x[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(tile) +
-                                                       ((h * NCQ + i) * WAVE + lane) * 16);
-#pragma unroll
-            for (int i = 0; i < NCQ; ++i) {
-                const uint4 y = elu1_bf16x8(make_uint4(x[i].x, x[i].y, x[i].z, x[i].w), p.in_scale);
-                *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(tile) + ((h * NCQ + i) * WAVE + lane) * 16) =
-                    u32x4{y.x, y.y, y.z, y.w};
-            }
-        };
         // wait until this wave's copies of a tile have landed, given that the
-        // copies of `after` more tiles were issued after them, mapping Q and K
-        // as soon as they are in.  The wait counts are immediates, so each is
-        // picked by a branch rather than by duplicating the mapping code.
-        auto wait_loads = [&](int after, auto extra) __attribute__((always_inline)) {
-            constexpr int X = decltype(extra)::value;
+        // copies of `after` more tiles were issued after them (the wait counts
+        // are immediates, so each is picked by a branch)
+        auto land = [&](int after) __attribute__((always_inline)) {
             if constexpr (NSTAGE >= 4)
                 if (after >= 2) {
-                    wait_vm<2 * NL + X>();
+                    wait_vm<2 * NL>();
                     return;
                 }
             if constexpr (NSTAGE >= 3)
                 if (after >= 1) {
-                    wait_vm<NL + X>();
+                    wait_vm<NL>();
                     return;
                 }
-            wait_vm<X>();
-        };
-        auto land = [&](int after, StageT& s) __attribute__((always_inline)) {
-            if constexpr (PHI) {
-                wait_loads(after, ic<NCQ + NCV>{});
-                phi_tile(s.q);
-                wait_loads(after, ic<NCV>{});
-                phi_tile(s.k);
-            }
-            wait_loads(after, ic<0>{});
+            wait_vm<0>();
         };
         // tiles issued after tile t while t is the oldest in flight
         auto after_of = [&](int64_t t) -> int {
@@ -352,7 +373,8 @@ void chunked_fwd_pipe(FwdParams p) {
 #pragma unroll
         for (int s0 = 0; s0 < NSTAGE - 1; ++s0)
             if (t_begin + s0 < t_end) issue(t_begin + s0, st[s0]);
-        land(after_of(t_begin), st[0]);
+        land(after_of(t_begin));
+        if constexpr (PHI) phi_share(st[0], valid_rows(t_begin));
 
         // The copy side walks the stages with a run-time index (its accesses
         // take computed addresses anyway), so its code appears once.
@@ -361,7 +383,7 @@ void chunked_fwd_pipe(FwdParams p) {
             const int sp = si == 0 ? NSTAGE - 1 : si - 1;  // stage of tile t - 1
             const int sn = si == NSTAGE - 1 ? 0 : si + 1;  // stage of tile t + 1
             __syncthreads();  // B(t)
-            if (valid_rows(t) < TT) {
+            if (!PHI && valid_rows(t) < TT) {
                 zero_tail(st[si], valid_rows(t));
                 __syncthreads();
             }
@@ -371,10 +393,14 @@ void chunked_fwd_pipe(FwdParams p) {
             u32x4 ob[NCV];
             if (t > t_begin) read_out(st[sp], ob);
             if (t + NSTAGE - 1 < t_end) issue(t + NSTAGE - 1, st[sp]);
-            // tile t + 1 must have landed before B(t + 1); the newest tile
-            // issued is now t + NSTAGE - 1 (or the last one)
-            if (t + 1 < t_end)
-                land(after_of(t + 1), st[sn]);
+            if constexpr (PHI) __syncthreads();  // B'(t): the compute waves have mapped their share of tile t
+            // tile t + 1 must have landed (and this wave's share of it been
+            // mapped) before B(t + 1); the newest tile issued is now
+            // t + NSTAGE - 1 (or the last one)
+            if (t + 1 < t_end) {
+                land(after_of(t + 1));
+                if constexpr (PHI) phi_share(st[sn], valid_rows(t + 1));
+            }
             if (t > t_begin) store_out(t - 1, ob);
             si = sn;
         }
@@ -767,7 +793,10 @@ void chunked_fwd_pipe(FwdParams p) {
     auto step = [&](auto sidx, int64_t t) __attribute__((always_inline)) {
         constexpr int SI = decltype(sidx)::value;
         __syncthreads();  // B(t)
-        if (valid_rows(t) < TT) {
+        if constexpr (PHI) {
+            phi_share(st[SI], valid_rows(t));
+            __syncthreads();  // B'(t)
+        } else if (valid_rows(t) < TT) {
             zero_tail(st[SI], valid_rows(t));
             __syncthreads();
         }
