@@ -399,6 +399,11 @@ static la_status chunk_states_impl(const void* k, const void* v, bool i8, int64_
         p.xcd_remap = xcd_ok(grid);
         return hip_status(la::run_chunk_states_i8(p, kernel_dk_i8(d_k), DVT, grid, s), "chunk states launch");
     }
+    // long runs of whole 64-row tiles at feature width 64, 128 or 256: the
+    // streaming kernel (its own value tiling)
+    const int dvt_pipe = 64;
+    bool stream_ok = (d_k == 64 || d_k == 128 || d_k == 256) && d_v % dvt_pipe == 0 && Cs % 64 == 0 &&
+                           Cs >= 256 && lg == 0.0f && (fmap == 0 || fmap == 1);
     la::StatesParams p{};
     p.k = static_cast<const unsigned short*>(k);
     p.v = static_cast<const unsigned short*>(v);
@@ -417,6 +422,19 @@ static la_status chunk_states_impl(const void* k, const void* v, bool i8, int64_
     p.want_z = z != nullptr;
     p.xcd_remap = xcd_ok(grid);
     p.log2_gamma = lg;
+    // elu+1 mapped here: the streaming kernel (one workgroup per CU) only when
+    // its workgroups fit the CUs in one round; with more, the register-staged
+    // kernel at several workgroups per CU hides the mapping better (measured)
+    const bool elu_in_kernel = k_lo == nullptr && fmap == 1;
+    if (stream_ok && elu_in_kernel && BH * (int64_t)n_items * (d_v / dvt_pipe) > 256) stream_ok = false;
+    if (stream_ok) {
+        p.n_dvt = (int)(d_v / dvt_pipe);
+        const int64_t sgrid = BH * (int64_t)n_items * p.n_dvt;
+        if (sgrid > 0x7FFFFFFFLL) return fail(LA_ERR_UNSUPPORTED, "grid too large");
+        p.xcd_remap = xcd_ok(sgrid);
+        const int kind = k_lo != nullptr ? 2 : (fmap == 1 ? 1 : 0);
+        return hip_status(la::states_pipe_bf16(p, (int)d_k, kind, sgrid, s), "chunk states launch");
+    }
     hipError_t e;
     switch (kernel_dk_bf16(d_k)) {
         case 32: e = la::states_bf16_dk32(p, DVT, grid, s); break;

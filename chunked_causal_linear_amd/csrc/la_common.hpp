@@ -85,31 +85,48 @@ __device__ __forceinline__ void transpose4x8(const uint4 r[4], uint2 out[8]) {
 // elu(x) + 1 with alpha = 1
 __device__ __forceinline__ float elu1(float x) { return x >= 0.f ? x + 1.f : __expf(x); }
 
-// Apply phi (elu+1 of in_scale * x) to 8 bf16 values in place.
-__device__ __forceinline__ uint4 elu1_bf16x8(const uint4& u, float in_scale) {
-    uint32_t w[4] = {u.x, u.y, u.z, u.w};
+// elu+1 of in_scale * x for the eight bf16 values of u, in fp32: for
+// s = |in_scale| and t = x s log2(e), elu+1(s x) is s x + 1 when t > 0 and
+// exp2(t) = exp(s x) otherwise (1 at 0); a negative in_scale flips the sign
+// of x first.  One multiply feeds both the test and the exponential.
+struct Elu1Scale {
+    float s, sl;
+    uint32_t flip;  // sign bits of both halves of a bf16 pair, or 0
+};
+__device__ __forceinline__ Elu1Scale elu1_scale(float in_scale) {
+    const float s = fabsf(in_scale);
+    return Elu1Scale{s, s * 1.4426950408889634f, in_scale < 0.f ? 0x80008000u : 0u};
+}
+__device__ __forceinline__ void elu1_f32x8(const uint4& u, const Elu1Scale& e, float (&f)[8]) {
+    const uint32_t w[4] = {u.x ^ e.flip, u.y ^ e.flip, u.z ^ e.flip, u.w ^ e.flip};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const float lo = elu1(in_scale * __uint_as_float(w[j] << 16));
-        const float hi = elu1(in_scale * __uint_as_float(w[j] & 0xFFFF0000u));
-        w[j] = pack2_bf16(lo, hi);
+        const float a = __uint_as_float(w[j] << 16), b = __uint_as_float(w[j] & 0xFFFF0000u);
+        const float ta = a * e.sl, tb = b * e.sl;
+        f[2 * j] = ta > 0.f ? fmaf(a, e.s, 1.f) : __builtin_amdgcn_exp2f(ta);
+        f[2 * j + 1] = tb > 0.f ? fmaf(b, e.s, 1.f) : __builtin_amdgcn_exp2f(tb);
     }
-    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// Apply phi (elu+1 of in_scale * x) to 8 bf16 values in place.
+__device__ __forceinline__ uint4 elu1_bf16x8(const uint4& u, float in_scale) {
+    float f[8];
+    elu1_f32x8(u, elu1_scale(in_scale), f);
+    return make_uint4(pack2_bf16(f[0], f[1]), pack2_bf16(f[2], f[3]), pack2_bf16(f[4], f[5]),
+                      pack2_bf16(f[6], f[7]));
 }
 
 // elu+1 of in_scale * x for 8 bf16 values, as a bf16 pair (hi, lo) with
 // hi = bf16(phi) and lo = bf16(phi - hi): hi + lo carries phi to about 2^-17
 // relative, which keeps long state sums free of the bf16 rounding of phi.
 __device__ __forceinline__ void elu1_split_bf16x8(const uint4& u, float in_scale, uint4& hi, uint4& lo) {
-    uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    float f[8];
+    elu1_f32x8(u, elu1_scale(in_scale), f);
     uint32_t h[4], l[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const float a = elu1(in_scale * __uint_as_float(w[j] << 16));
-        const float b = elu1(in_scale * __uint_as_float(w[j] & 0xFFFF0000u));
-        h[j] = pack2_bf16(a, b);
-        const float ah = __uint_as_float(h[j] << 16), bh = __uint_as_float(h[j] & 0xFFFF0000u);
-        l[j] = pack2_bf16(a - ah, b - bh);
+        h[j] = pack2_bf16(f[2 * j], f[2 * j + 1]);
+        l[j] = pack2_bf16(f[2 * j] - __uint_as_float(h[j] << 16), f[2 * j + 1] - __uint_as_float(h[j] & 0xFFFF0000u));
     }
     hi = make_uint4(h[0], h[1], h[2], h[3]);
     lo = make_uint4(l[0], l[1], l[2], l[3]);

@@ -246,31 +246,36 @@ void chunked_fwd_pipe(FwdParams p) {
         for (int i = tid; i < n; i += 4 * WAVE) kk[i] = make_uint4(0, 0, 0, 0);
     };
 
-    // elu+1 of a landed tile's Q and K in place.  The tiles are 2 NP blocks of
-    // 64 16-byte pieces (Q's NP, then K's); the compute waves take NPC blocks
-    // each, the copy waves NPK, and lane l of a block maps its piece l.  The
-    // compute waves take half with 64-row tiles and a quarter with 128-row
-    // tiles, whose products leave them less time (the shares that measured
-    // fastest).
+    // elu+1 of a landed tile's Q and K in place.  Each tile is NP = 2 NCQ
+    // blocks of 64 16-byte pieces, and lane l of a block maps its piece l.
+    // Copy wave h copies (and waits for) Q blocks h NCQ .. h NCQ + NCQ - 1 and
+    // the same K blocks: the list of pair h, Q's then K's, j = 0 .. NP - 1.
+    // Copy wave h maps the first NPK of that list as soon as its copies have
+    // landed (only its own copies: the other copy wave's may still be in
+    // flight), compute wave h the other NPC after B(j).  The compute waves take
+    // half with 64-row tiles and a quarter with 128-row tiles, whose products
+    // leave them less time (the shares that measured fastest).
     constexpr int NP = 2 * NCQ;
     constexpr int NPC = TT > 64 ? NP / 4 : NP / 2, NPK = NP - NPC;
-    auto phi_blocks = [&](StageT& s, int valid, auto first_, auto count) __attribute__((always_inline)) {
-        constexpr int FIRST = decltype(first_)::value, N = decltype(count)::value;
+    auto phi_blocks = [&](StageT& s, int valid, auto j0_, auto count) __attribute__((always_inline)) {
+        constexpr int J0 = decltype(j0_)::value, N = decltype(count)::value;
         // four pieces in flight at a time (bounded registers)
 #pragma unroll
         for (int i0 = 0; i0 < N; i0 += 4) {
             uint4 x[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int blk = FIRST + i0 + i, slot = (blk % NP) * WAVE + lane;
-                if (i0 + i < N) x[i] = *reinterpret_cast<const uint4*>((blk < NP ? s.q : s.k) + slot * 8);
+                const int j = J0 + i0 + i;
+                const int slot = (h * NCQ + (j < NCQ ? j : j - NCQ)) * WAVE + lane;
+                if (i0 + i < N) x[i] = *reinterpret_cast<const uint4*>((j < NCQ ? s.q : s.k) + slot * 8);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int blk = FIRST + i0 + i, slot = (blk % NP) * WAVE + lane;
+                const int j = J0 + i0 + i;
+                const int slot = (h * NCQ + (j < NCQ ? j : j - NCQ)) * WAVE + lane;
                 if (i0 + i < N) {
-                    const bool live = blk < NP || slot / QSEG < valid;  // K rows past the end become zero
-                    *reinterpret_cast<uint4*>((blk < NP ? s.q : s.k) + slot * 8) =
+                    const bool live = j < NCQ || slot / QSEG < valid;  // K rows past the end become zero
+                    *reinterpret_cast<uint4*>((j < NCQ ? s.q : s.k) + slot * 8) =
                         live ? elu1_bf16x8(x[i], p.in_scale) : make_uint4(0, 0, 0, 0);
                 }
             }
@@ -278,17 +283,10 @@ void chunked_fwd_pipe(FwdParams p) {
     };
     // this wave's share of the mapping of a landed tile
     auto phi_share = [&](StageT& s, int valid) __attribute__((always_inline)) {
-        if (copier) {
-            if (h == 0)
-                phi_blocks(s, valid, ic<2 * NPC>{}, ic<NPK>{});
-            else
-                phi_blocks(s, valid, ic<2 * NPC + NPK>{}, ic<NPK>{});
-        } else {
-            if (h == 0)
-                phi_blocks(s, valid, ic<0>{}, ic<NPC>{});
-            else
-                phi_blocks(s, valid, ic<NPC>{}, ic<NPC>{});
-        }
+        if (copier)
+            phi_blocks(s, valid, ic<0>{}, ic<NPK>{});
+        else
+            phi_blocks(s, valid, ic<NPK>{}, ic<NPC>{});
     };
 
     if (copier) {

@@ -165,6 +165,10 @@ hipError_t run_loglinear_fwd(const LogLinParams& p, int64_t grid, hipStream_t s)
 
 hipError_t run_chunked_fwd_i8(const FwdParamsI8& p, int DK, int DVT, int T, int64_t grid, hipStream_t s);
 hipError_t run_chunk_states_i8(const StatesParamsI8& p, int DK, int DVT, int64_t grid, hipStream_t s);
+// Streaming phase 1 (la_states_pipe.hip): d_k = DK in {64, 128, 256}, value
+// tiles of 64 columns, runs of C rows with C a multiple of 64;
+// kind 0 plain K, 1 elu+1 applied here (split hi/lo), 2 pre-mapped with residual.
+hipError_t states_pipe_bf16(const StatesParams& p, int DK, int kind, int64_t grid, hipStream_t s);
 hipError_t run_state_scan(const ScanParams& p, int64_t BH, hipStream_t s);
 hipError_t run_feature_map(const FmapParams& p, hipStream_t s);
 hipError_t run_recurrent_step(const DecodeParams& p, hipStream_t s);

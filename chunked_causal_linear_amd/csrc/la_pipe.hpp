@@ -6,6 +6,14 @@
 namespace la {
 
 hipError_t fwd_pipe_decay_bf16(const FwdParams& p, int DK, int DVT, int C, int64_t grid, hipStream_t s);
+// the cases with the most live registers (la_pipe_wide.hip)
+hipError_t fwd_pipe_wide_bf16(const FwdParams& p, int DK, int C, bool decay, int64_t grid, hipStream_t s);
+
+// the cases every instantiation file accepts
+inline bool pipe_args_ok(const FwdParams& p, int DK, int DVT) {
+    if (DVT != (DK == 256 ? 32 : 64) || p.noncausal || p.out_f32 || p.k_lo != nullptr) return false;
+    return p.fmap == FMAP_NONE || p.fmap == FMAP_ELU1;
+}
 
 namespace pipe {
 
@@ -23,22 +31,5 @@ hipError_t by_flags(const FwdParams& p, int64_t grid, hipStream_t s) {
 }
 
 }  // namespace pipe
-
-template <bool DECAY>
-hipError_t pipe_dispatch(const FwdParams& p, int DK, int DVT, int C, int64_t grid, hipStream_t s) {
-    if (DVT != (DK == 256 ? 32 : 64) || p.noncausal || p.out_f32 || p.k_lo != nullptr) return hipErrorInvalidValue;
-    if (p.fmap != FMAP_NONE && p.fmap != FMAP_ELU1) return hipErrorInvalidValue;
-    switch (DK * 1000 + C) {
-        case 128032: return pipe::by_flags<128, 32, DECAY>(p, grid, s);
-        case 128064: return pipe::by_flags<128, 64, DECAY>(p, grid, s);
-        case 128128: return pipe::by_flags<128, 128, DECAY>(p, grid, s);
-        case 64032: return pipe::by_flags<64, 32, DECAY>(p, grid, s);
-        case 64064: return pipe::by_flags<64, 64, DECAY>(p, grid, s);
-        case 64128: return pipe::by_flags<64, 128, DECAY>(p, grid, s);
-        case 256032: return pipe::by_flags<256, 32, DECAY>(p, grid, s);
-        case 256064: return pipe::by_flags<256, 64, DECAY>(p, grid, s);
-    }
-    return hipErrorInvalidValue;
-}
 
 }  // namespace la

@@ -1,15 +1,12 @@
 // Streaming fused phase 3 with the decayed recurrence (instantiations), the
 // cases whose registers leave room for matrix-core accumulators in VGPRs; the
-// others are in la_pipe_decay_wide.hip.
+// others are in la_pipe_wide.hip.
 #include "la_pipe.hpp"
 
 namespace la {
 
-hipError_t fwd_pipe_decay_wide_bf16(const FwdParams& p, int DK, int C, int64_t grid, hipStream_t s);
-
 hipError_t fwd_pipe_decay_bf16(const FwdParams& p, int DK, int DVT, int C, int64_t grid, hipStream_t s) {
-    if (DVT != (DK == 256 ? 32 : 64) || p.noncausal || p.out_f32 || p.k_lo != nullptr) return hipErrorInvalidValue;
-    if (p.fmap != FMAP_NONE && p.fmap != FMAP_ELU1) return hipErrorInvalidValue;
+    if (!pipe_args_ok(p, DK, DVT)) return hipErrorInvalidValue;
     switch (DK * 1000 + C) {
         case 128032: return pipe::by_flags<128, 32, true>(p, grid, s);
         case 128064: return pipe::by_flags<128, 64, true>(p, grid, s);
@@ -18,7 +15,7 @@ hipError_t fwd_pipe_decay_bf16(const FwdParams& p, int DK, int DVT, int C, int64
         case 64128: return pipe::by_flags<64, 128, true>(p, grid, s);
         case 128128:
         case 256032:
-        case 256064: return fwd_pipe_decay_wide_bf16(p, DK, C, grid, s);
+        case 256064: return fwd_pipe_wide_bf16(p, DK, C, true, grid, s);
     }
     return hipErrorInvalidValue;
 }

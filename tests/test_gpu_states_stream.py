@@ -1,0 +1,78 @@
+"""GPU parity of the streaming phase 1 (runs of whole 64-row tiles at feature
+width 64, 128 or 256) against the CPU oracle.
+
+Standalone ``la_chunk_states`` at run lengths of 256 rows and more takes the
+streaming kernel with plain K; grouped forwards whose groups are summed in
+pieces of that size take it with elu+1 applied in the kernel (split into a
+bf16 pair) and with pre-mapped FAVOR+ features and their residual.  Every case
+has a ragged last tile, one a last run of a single row.  Tolerance as
+everywhere on the bf16 path: |gpu - oracle| <= 1e-2 (1 + |oracle|).
+"""
+import numpy as np
+import pytest
+
+import chunked_causal_linear_amd as la
+import oracle
+import workloads as wl
+from tests.gpu_helpers import assert_close, dev_bf16, dev_input, host, log
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(seed, BH, L, d_in, d_v, scale=None):
+    return wl.random_case(seed, BH, L, d_in, d_v, "bf16", 1.0 / np.sqrt(d_in) if scale is None else scale)
+
+
+@pytest.mark.parametrize("dk,dv,L,C,want_z", [
+    (64, 64, 1000, 256, True), (128, 128, 1300, 320, True), (256, 64, 900, 512, True),
+    (64, 128, 2000, 1024, False), (128, 64, 257, 256, True), (256, 32, 700, 256, False),
+    (128, 64, 200, 256, True)])
+def test_stream_states_plain(dk, dv, L, C, want_z):
+    """Per-run states and column sums of plain K over runs of C rows."""
+    q, k, v = _case(60, 2, L, dk, dv)
+    log(f"stream states dk={dk} dv={dv} L={L} C={C} want_z={want_z}")
+    S, z = la.chunk_states(dev_input(k), dev_input(v), C, want_z=want_z)
+    ref = [oracle.chunk_states(k.exact[h], v.exact[h], C) for h in range(2)]
+    assert_close(host(S), np.stack([r[0] for r in ref]), what="states")
+    if want_z:
+        assert_close(host(z), np.stack([r[1] for r in ref]), what="column sums")
+
+
+def _oracle_forward(q, k, v, C, fmap, W=None):
+    outs, Ss, zs = [], [], []
+    for h in range(q.shape[0]):
+        o, S, z = oracle.forward(q[h], k[h], v[h], C, True, True, fmap, W, 1.0)
+        outs.append(o)
+        Ss.append(S)
+        zs.append(z)
+    return np.stack(outs), np.stack(Ss), np.stack(zs)
+
+
+@pytest.mark.parametrize("dk,C,L,group", [(64, 64, 1500, 5), (128, 64, 1111, 4), (256, 64, 1000, 4),
+                                          (256, 32, 900, 8)])
+def test_stream_states_elu1_forward(dk, C, L, group):
+    """Normalised elu+1 forwards in groups of 256 rows or more: phase 1 maps
+    phi(k) in the kernel and sums it with its residual."""
+    q, k, v = _case(61, 2, L, dk, 64)
+    log(f"stream states elu1 forward dk={dk} C={C} L={L} group={group}")
+    o, S, z = la.chunked_forward(dev_input(q), dev_input(k), dev_input(v), C, normalize=True, fmap="elu1",
+                                 return_state=True, group=group)
+    ref, refS, refz = _oracle_forward(q.exact, k.exact, v.exact, C, "elu1")
+    assert_close(host(o), ref, what="o")
+    assert_close(host(S), refS, what="S")
+    assert_close(host(z), refz, what="z")
+
+
+@pytest.mark.parametrize("m,C,L,group", [(128, 64, 1200, 4), (256, 64, 1000, 5), (64, 128, 1400, 2)])
+def test_stream_states_favor_forward(m, C, L, group):
+    """FAVOR+ forwards in groups of 256 rows or more: phase 1 reads the
+    pre-mapped phi(k) and its residual."""
+    q, k, v = _case(62, 2, L, 64, 64, scale=1.0 / 8)
+    Wb, W = wl.orthogonal_random_features(m, 64, [62, 1])
+    log(f"stream states favor forward m={m} C={C} L={L} group={group}")
+    o, S, z = la.chunked_forward(dev_input(q), dev_input(k), dev_input(v), C, normalize=True, fmap="favor",
+                                 W=dev_bf16(Wb), return_state=True, group=group)
+    ref, refS, refz = _oracle_forward(q.exact, k.exact, v.exact, C, "favor", W)
+    assert_close(host(o), ref, what="favor o")
+    assert_close(host(S), refS, what="favor S")
+    assert_close(host(z), refz, what="favor z")
