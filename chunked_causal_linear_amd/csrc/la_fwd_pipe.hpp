@@ -254,9 +254,11 @@ void chunked_fwd_pipe(FwdParams p) {
     // landed (only its own copies: the other copy wave's may still be in
     // flight), compute wave h the other NPC after B(j).  The compute waves take
     // half with 64-row tiles and a quarter with 128-row tiles, whose products
-    // leave them less time (the shares that measured fastest).
+    // leave them less time, and an eighth with the decay, whose products leave
+    // them the least (the shares that measured fastest).
     constexpr int NP = 2 * NCQ;
-    constexpr int NPC = TT > 64 ? NP / 4 : NP / 2, NPK = NP - NPC;
+    constexpr int NPC = DECAY ? NP / 8 : (TT > 64 ? NP / 4 : NP / 2), NPK = NP - NPC;
+    constexpr bool MAP2 = PHI && NPC > 0;  // the compute waves map too
     auto phi_blocks = [&](StageT& s, int valid, auto j0_, auto count) __attribute__((always_inline)) {
         constexpr int J0 = decltype(j0_)::value, N = decltype(count)::value;
         // four pieces in flight at a time (bounded registers)
@@ -391,7 +393,7 @@ void chunked_fwd_pipe(FwdParams p) {
             u32x4 ob[NCV];
             if (t > t_begin) read_out(st[sp], ob);
             if (t + NSTAGE - 1 < t_end) issue(t + NSTAGE - 1, st[sp]);
-            if constexpr (PHI) __syncthreads();  // B'(t): the compute waves have mapped their share of tile t
+            if constexpr (MAP2) __syncthreads();  // B'(t): the compute waves have mapped their share of tile t
             // tile t + 1 must have landed (and this wave's share of it been
             // mapped) before B(t + 1); the newest tile issued is now
             // t + NSTAGE - 1 (or the last one)
@@ -791,10 +793,10 @@ void chunked_fwd_pipe(FwdParams p) {
     auto step = [&](auto sidx, int64_t t) __attribute__((always_inline)) {
         constexpr int SI = decltype(sidx)::value;
         __syncthreads();  // B(t)
-        if constexpr (PHI) {
+        if constexpr (MAP2) {
             phi_share(st[SI], valid_rows(t));
             __syncthreads();  // B'(t)
-        } else if (valid_rows(t) < TT) {
+        } else if (!PHI && valid_rows(t) < TT) {
             zero_tail(st[SI], valid_rows(t));
             __syncthreads();
         }
