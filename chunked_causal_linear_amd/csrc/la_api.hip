@@ -107,7 +107,8 @@ la_status check_dtypes_forward(la_dtype in_dt, la_dtype out_dt, int normalize, l
 }
 
 la_status make_plan(Plan& P, la_dtype in_dt, int64_t BH, int64_t L, int64_t d_in, int64_t d_v, int64_t C,
-                    int causal, int normalize, la_fmap f, int64_t m, float in_scale, int64_t group) {
+                    int causal, int normalize, la_fmap f, int64_t m, float in_scale, int64_t group,
+                    bool decay) {
     if (BH < 1 || L < 1 || d_in < 1 || d_v < 1) return fail(LA_ERR_INVALID_ARG, "sizes must be positive");
     if (f != LA_FMAP_IDENTITY && f != LA_FMAP_ELU1 && f != LA_FMAP_FAVOR)
         return fail(LA_ERR_INVALID_ARG, "unknown feature map %d", (int)f);
@@ -208,18 +209,28 @@ la_status make_plan(Plan& P, la_dtype in_dt, int64_t BH, int64_t L, int64_t d_in
 
     // Phase 1 sums each group's rows; a few long groups would leave most CUs
     // idle, so each group's rows are split into `sub` equal pieces (of >= 512
-    // rows, each reading >= 8x the state it writes) until about 1024
-    // workgroups run; the scan then walks the pieces and group g starts from
-    // the prefix at piece g * sub.
+    // rows, each reading >= 8x the state it writes); the scan then walks the
+    // pieces and group g starts from the prefix at piece g * sub.  The
+    // register-staged phase-1 kernel runs several workgroups per CU: pieces
+    // double while fewer than 1024 run.  The streaming one (bf16 at feature
+    // width 64, 128 or 256, value columns a multiple of 64, pieces of whole
+    // 64-row tiles, no decay) holds a CU alone: pieces double while the
+    // workgroups still fit the CUs in one round.
     P.sub = 1;
     const int64_t n_summed = P.final_from_scan ? P.n_groups : P.n_groups - 1;  // groups phase 1 may sum
     if (P.causal && n_summed > 0) {
         const int64_t n_dvt1 = d_v / kernel_dvt(d_v);
         // a piece reads at least eight times the state it writes
         const int64_t min_rows = std::max<int64_t>(512, cdiv(16 * P.dk * d_v, P.dk + d_v));
-        while ((P.G * P.C) % (2 * P.sub) == 0 && P.G * P.C / (2 * P.sub) >= min_rows &&
-               BH * n_summed * P.sub * n_dvt1 < 1024)
-            P.sub *= 2;
+        const bool stream1 = !P.i8 && !decay && (P.dk == 64 || P.dk == 128 || P.dk == 256) && d_v % 64 == 0 &&
+                             (P.G * P.C) % 64 == 0;
+        auto more = [&]() {
+            const int64_t rows = P.G * P.C / (2 * P.sub);
+            if ((P.G * P.C) % (2 * P.sub) != 0 || rows < min_rows) return false;
+            if (stream1) return rows % 64 == 0 && 2 * BH * n_summed * P.sub * n_dvt1 <= 256;
+            return BH * n_summed * P.sub * n_dvt1 < 1024;
+        };
+        while (more()) P.sub *= 2;
     }
 
     const size_t st_elem = 4;
@@ -534,10 +545,17 @@ size_t la_chunked_forward_workspace(la_dtype in_dt, int64_t BH, int64_t L, int64
     Plan P{};
     char saved[sizeof(g_last_error)];
     memcpy(saved, g_last_error, sizeof(saved));
-    const la_status s = make_plan(P, in_dt, BH, L, d_in, d_v, C, causal, normalize, f, m, in_scale, group);
+    // the decayed forward takes the same workspace: the larger of the two plans
+    la_status s = make_plan(P, in_dt, BH, L, d_in, d_v, C, causal, normalize, f, m, in_scale, group, false);
+    size_t ws = P.ws_total;
+    if (s == LA_OK) {
+        Plan Pd{};
+        if (make_plan(Pd, in_dt, BH, L, d_in, d_v, C, causal, normalize, f, m, in_scale, group, true) == LA_OK)
+            ws = std::max(ws, Pd.ws_total);
+    }
     memcpy(g_last_error, saved, sizeof(saved));
     if (s != LA_OK) return 0;
-    return P.ws_total;
+    return ws;
 }
 
 int64_t la_chunked_forward_group(la_dtype in_dt, int64_t BH, int64_t L, int64_t d_in, int64_t d_v, int64_t C,
@@ -545,7 +563,7 @@ int64_t la_chunked_forward_group(la_dtype in_dt, int64_t BH, int64_t L, int64_t 
     Plan P{};
     char saved[sizeof(g_last_error)];
     memcpy(saved, g_last_error, sizeof(saved));
-    const la_status s = make_plan(P, in_dt, BH, L, d_in, d_v, C, causal, normalize, f, m, 1.0f, group);
+    const la_status s = make_plan(P, in_dt, BH, L, d_in, d_v, C, causal, normalize, f, m, 1.0f, group, false);
     memcpy(g_last_error, saved, sizeof(saved));
     return s == LA_OK ? P.G : 0;
 }
@@ -562,9 +580,9 @@ static la_status forward_entry(const void* q, const void* k, const void* v, la_d
     if (f == LA_FMAP_FAVOR && W == nullptr) return fail(LA_ERR_INVALID_ARG, "FAVOR+ needs W");
     if (z_final != nullptr && !normalize) return fail(LA_ERR_INVALID_ARG, "z_final needs normalize");
     Plan P{};
-    st = make_plan(P, in_dt, BH, L, d_in, d_v, C, causal, normalize, f, m, in_scale, group);
-    if (st != LA_OK) return st;
     const float lg = log2_of(gamma);
+    st = make_plan(P, in_dt, BH, L, d_in, d_v, C, causal, normalize, f, m, in_scale, group, lg != 0.0f);
+    if (st != LA_OK) return st;
     if (lg != 0.0f && !(causal && P.pipe && out_dt == LA_BF16))
         return fail(LA_ERR_UNSUPPORTED,
                     "the decayed recurrence runs on the streaming kernel: causal, bf16 in and out, C in {32, 64, 128} "
@@ -676,7 +694,7 @@ static la_status chunk_output_entry(const void* q, const void* k, const void* v,
     if (z_final != nullptr && !normalize) return fail(LA_ERR_INVALID_ARG, "z_final needs normalize");
     if (group < 1) return fail(LA_ERR_INVALID_ARG, "group must be at least 1");
     Plan P{};
-    st = make_plan(P, in_dt, BH, L, d_k, d_v, C, 1, normalize, LA_FMAP_IDENTITY, 0, 1.0f, group);
+    st = make_plan(P, in_dt, BH, L, d_k, d_v, C, 1, normalize, LA_FMAP_IDENTITY, 0, 1.0f, group, gamma != 1.0f);
     if (st != LA_OK) return st;
     if (P.n_groups > 1 && (P_prefix == nullptr || (normalize && z_prefix == nullptr)))
         return fail(LA_ERR_INVALID_ARG, "more than one group needs the prefix states (and normalisers)");
