@@ -33,11 +33,13 @@ CFLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-I" + INCLUDE
 
 # Per-file flags.  The streaming kernel keeps its matrix-core accumulators in
 # ordinary VGPRs (it runs one wave per SIMD, so all 512 registers are there),
-# which saves the copies out of accumulation registers before every pack.  The
+# which saves the copies out of accumulation registers before every pack; so
+# does the FAVOR+ map, whose epilogue reads every accumulator once.  The
 # variants with the most live registers (la_pipe_wide.hip) are built without
 # it: that form fails to compile at their register pressure.
 FILE_FLAGS = {"la_pipe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-              "la_pipe_decay.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+              "la_pipe_decay.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+              "la_fmap.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _sources():

@@ -5,7 +5,8 @@
 //  * identity and elu+1 are elementwise (8 bf16 per thread, fp32 math); with a
 //    bf16 output they can also write the bf16 residual y - bf16(y).
 //  * FAVOR+ is a small GEMM x W^T (k = d_in) on bf16 matrix cores with an
-//    fp32 epilogue exp(proj - |x|^2 / 2) / sqrt(m).  W stays in LDS for the
+//    fp32 epilogue exp(proj - |x|^2 / 2) / sqrt(m) (one exp2 of a fused
+//    multiply-add per feature).  W stays in LDS for the
 //    life of the workgroup, whose waves walk slabs of 16 rows.
 #include "la_common.hpp"
 #include "la_kernels.hpp"
@@ -60,19 +61,26 @@ __global__ __launch_bounds__(256) void fmap_elementwise(FmapParams p) {
 // leave as 16-byte stores with consecutive lanes on consecutive addresses
 // (whole rows per instruction: a row's pieces spread over several instructions
 // wrote at two thirds of the rate).  No barrier after W is in.
-template <int DINP>
+// M = m features (16 MB), fixed at compile time so the feature loop has no
+// run-time bounds.
+template <int DINP, int MB>
 __global__ __launch_bounds__(256) void fmap_favor(FmapParams p) {
     constexpr int XS = DINP + 8;    // LDS row stride of W (elements)
-    constexpr int MMAX = 256;
+    constexpr int M = 16 * MB;
     constexpr int NKS = DINP / 32;
-    constexpr int YS = MMAX + 8;    // staging row stride (elements)
-    __shared__ __attribute__((aligned(16))) u16 Ws[MMAX * XS];
+    constexpr int YS = M + 8;       // staging row stride (elements)
+    __shared__ __attribute__((aligned(16))) u16 Ws[M * XS];
     __shared__ __attribute__((aligned(16))) u16 Ys[4][16 * YS];
 
     const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE, l16 = lane % 16, g = lane / 16;
-    const int m = p.m, din = p.d_in;
+    constexpr int m = M;
+    const int din = p.d_in;
     const float s = p.in_scale;
-    const float inv_sqrt_m = 1.0f / sqrtf((float)m);
+    // exp(s w.x - s^2 |x|^2 / 2) / sqrt(m) = exp2(w.x sl - (s^2 |x|^2 / 2) log2(e) - log2(m) / 2):
+    // one fused multiply-add and one exponential per feature
+    constexpr float LOG2E = 1.4426950408889634f;
+    const float sl = s * LOG2E;
+    const float half_log2_m = 0.5f * log2f((float)m);
     u16* ys = Ys[wave];
 
     // W -> LDS (zero-padded columns)
@@ -96,7 +104,7 @@ __global__ __launch_bounds__(256) void fmap_favor(FmapParams p) {
         }
     };
     // the staged 16 x m bf16 block of this slab to rows slab*16.. of dst
-    const int segs = m / 8;  // 16-byte pieces per row
+    constexpr int segs = M / 8;  // 16-byte pieces per row
     auto store_staged = [&](int64_t slab, u16* dst) {
         for (int e = lane; e < 16 * segs; e += WAVE) {
             const int r = e / segs, sg = e % segs;
@@ -129,29 +137,27 @@ __global__ __launch_bounds__(256) void fmap_favor(FmapParams p) {
         }
         sq += __shfl_xor(sq, 16);
         sq += __shfl_xor(sq, 32);
-        const float half_sq = 0.5f * s * s * sq;
+        const float off = fmaf(0.5f * s * s * sq, LOG2E, half_log2_m);
         // y for features 16 nb + 4g + i of row l16 (kept in registers: the
         // residual pass reads them again)
-        constexpr int NBM = MMAX / 16;
+        constexpr int NBM = MB;
         float y[NBM][4];
 #pragma unroll
         for (int nb = 0; nb < NBM; ++nb) {
-            if (nb < m / 16) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) {
-                    const bf16x8 wb =
-                        as_bf16x8(*reinterpret_cast<const uint4*>(Ws + (nb * 16 + l16) * XS + ks * 32 + g * 8));
-                    acc = mfma_bf16(wb, xb[ks], acc);
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) y[nb][i] = __expf(s * acc[i] - half_sq) * inv_sqrt_m;
+            for (int ks = 0; ks < NKS; ++ks) {
+                const bf16x8 wb =
+                    as_bf16x8(*reinterpret_cast<const uint4*>(Ws + (nb * 16 + l16) * XS + ks * 32 + g * 8));
+                acc = mfma_bf16(wb, xb[ks], acc);
             }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) y[nb][i] = __builtin_amdgcn_exp2f(fmaf(acc[i], sl, -off));
         }
         if (p.y_f32) {
 #pragma unroll
             for (int nb = 0; nb < NBM; ++nb)
-                if (nb < m / 16 && row < p.rows)
+                if (row < p.rows)
                     *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.y) + row * m + nb * 16 + 4 * g) =
                         make_float4(y[nb][0], y[nb][1], y[nb][2], y[nb][3]);
             continue;
@@ -159,41 +165,56 @@ __global__ __launch_bounds__(256) void fmap_favor(FmapParams p) {
         uint2 hb[NBM];
 #pragma unroll
         for (int nb = 0; nb < NBM; ++nb) {
-            if (nb < m / 16) {
-                hb[nb] = make_uint2(pack2_bf16(y[nb][0], y[nb][1]), pack2_bf16(y[nb][2], y[nb][3]));
-                *reinterpret_cast<uint2*>(ys + l16 * YS + nb * 16 + 4 * g) = hb[nb];
-            }
+            hb[nb] = make_uint2(pack2_bf16(y[nb][0], y[nb][1]), pack2_bf16(y[nb][2], y[nb][3]));
+            *reinterpret_cast<uint2*>(ys + l16 * YS + nb * 16 + 4 * g) = hb[nb];
         }
         store_staged(slab, reinterpret_cast<u16*>(p.y));
         if (p.y_lo != nullptr) {
             // residual y - bf16(y), so that hi + lo carries y to about 2^-17
 #pragma unroll
             for (int nb = 0; nb < NBM; ++nb) {
-                if (nb < m / 16) {
-                    const uint2 h = hb[nb];
-                    *reinterpret_cast<uint2*>(ys + l16 * YS + nb * 16 + 4 * g) = make_uint2(
-                        pack2_bf16(y[nb][0] - __uint_as_float(h.x << 16), y[nb][1] - __uint_as_float(h.x & 0xFFFF0000u)),
-                        pack2_bf16(y[nb][2] - __uint_as_float(h.y << 16), y[nb][3] - __uint_as_float(h.y & 0xFFFF0000u)));
-                }
+                const uint2 h = hb[nb];
+                *reinterpret_cast<uint2*>(ys + l16 * YS + nb * 16 + 4 * g) = make_uint2(
+                    pack2_bf16(y[nb][0] - __uint_as_float(h.x << 16), y[nb][1] - __uint_as_float(h.x & 0xFFFF0000u)),
+                    pack2_bf16(y[nb][2] - __uint_as_float(h.y << 16), y[nb][3] - __uint_as_float(h.y & 0xFFFF0000u)));
             }
             store_staged(slab, p.y_lo);
         }
     }
 }
 
+template <int DINP, int MB>
+static void launch_favor(const FmapParams& p, hipStream_t s) {
+    // four 16-row slabs per workgroup and round; as many workgroups as fit
+    // the CUs at once (by LDS, at most four per CU), so W is loaded once per
+    // resident workgroup
+    constexpr int64_t lds = 2 * (16 * MB * (DINP + 8) + 4 * 16 * (16 * MB + 8));
+    constexpr int64_t per_cu = 160 * 1024 / lds < 4 ? 160 * 1024 / lds : 4;
+    const int64_t n_groups = (p.rows + 63) / 64;
+    const int64_t cap = 256 * per_cu;
+    const unsigned grid = (unsigned)(n_groups < cap ? n_groups : cap);
+    hipLaunchKernelGGL((fmap_favor<DINP, MB>), dim3(grid), dim3(256), 0, s, p);
+}
+
+template <int DINP>
+static void launch_favor_m(const FmapParams& p, hipStream_t s) {
+    switch (p.m) {
+        case 16: launch_favor<DINP, 1>(p, s); break;
+        case 32: launch_favor<DINP, 2>(p, s); break;
+        case 64: launch_favor<DINP, 4>(p, s); break;
+        case 128: launch_favor<DINP, 8>(p, s); break;
+        default: launch_favor<DINP, 16>(p, s); break;
+    }
+}
+
 hipError_t run_feature_map(const FmapParams& p, hipStream_t s) {
     if (p.fmap == 2) {
-        // four 16-row slabs per workgroup and round; as many workgroups as fit
-        // the CUs at once (LDS: two per CU up to d_in = 64, one above), so W
-        // is loaded once per resident workgroup
+        // m is a power of two in 16..256 (checked by the caller)
         const int dinp = p.d_in <= 32 ? 32 : (p.d_in <= 64 ? 64 : 128);
-        const int64_t n_groups = (p.rows + 63) / 64;
-        const int64_t cap = dinp <= 64 ? 512 : 256;
-        const unsigned grid = (unsigned)(n_groups < cap ? n_groups : cap);
         switch (dinp) {
-            case 32: hipLaunchKernelGGL(fmap_favor<32>, dim3(grid), dim3(256), 0, s, p); break;
-            case 64: hipLaunchKernelGGL(fmap_favor<64>, dim3(grid), dim3(256), 0, s, p); break;
-            default: hipLaunchKernelGGL(fmap_favor<128>, dim3(grid), dim3(256), 0, s, p); break;
+            case 32: launch_favor_m<32>(p, s); break;
+            case 64: launch_favor_m<64>(p, s); break;
+            default: launch_favor_m<128>(p, s); break;
         }
     } else {
         const int64_t units = p.rows * p.d_in / 8;

@@ -76,3 +76,23 @@ def test_stream_states_favor_forward(m, C, L, group):
     assert_close(host(o), ref, what="favor o")
     assert_close(host(S), refS, what="favor S")
     assert_close(host(z), refz, what="favor z")
+
+
+@pytest.mark.parametrize("C,L,group,scale", [(64, 900, 4, -0.5), (128, 1000, 2, -0.25), (64, 700, 0, -1.0)])
+def test_elu1_negative_in_scale(C, L, group, scale):
+    """elu+1 of in_scale * x with a negative in_scale: the kernels map
+    elu+1(|s| (-x)), flipping the sign bits of the bf16 inputs first (phase 3
+    and the streaming phase 1)."""
+    q, k, v = _case(63, 2, L, 64, 64)
+    log(f"elu1 negative in_scale C={C} L={L} group={group} in_scale={scale}")
+    o, S, z = la.chunked_forward(dev_input(q), dev_input(k), dev_input(v), C, normalize=True, fmap="elu1",
+                                 in_scale=scale, return_state=True, group=group)
+    outs, Ss, zs = [], [], []
+    for h in range(2):
+        ro, rS, rz = oracle.forward(q.exact[h], k.exact[h], v.exact[h], C, True, True, "elu1", None, scale)
+        outs.append(ro)
+        Ss.append(rS)
+        zs.append(rz)
+    assert_close(host(o), np.stack(outs), what="o")
+    assert_close(host(S), np.stack(Ss), what="S")
+    assert_close(host(z), np.stack(zs), what="z")
