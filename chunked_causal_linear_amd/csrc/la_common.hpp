@@ -29,6 +29,17 @@ __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
 
 __device__ __forceinline__ u16 f2bf(float x) { return (u16)(pack2_bf16(x, 0.f) & 0xFFFFu); }
 
+// 16-byte global loads and stores with the non-temporal hint, for data a
+// kernel streams through once.
+typedef uint32_t u32x4_nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_nt(const void* p) {
+    const u32x4_nt r = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(p));
+    return make_uint4(r.x, r.y, r.z, r.w);
+}
+__device__ __forceinline__ void store_nt(void* p, const uint4& v) {
+    __builtin_nontemporal_store(u32x4_nt{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_nt*>(p));
+}
+
 // ---------------------------------------------------------------------------
 // Matrix-core wrappers.  16x16x32 bf16 -> fp32: lane l holds A[m = l%16][k = 8*(l/16) .. +7],
 // B[k = 8*(l/16) .. +7][n = l%16] and C/D[m = 4*(l/16) + i][n = l%16], i = 0..3.

@@ -17,7 +17,7 @@ __global__ __launch_bounds__(256) void fmap_elementwise(FmapParams p) {
     const int64_t units = p.rows * p.d_in / 8;
     for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < units;
          u += (int64_t)gridDim.x * blockDim.x) {
-        const uint4 raw = reinterpret_cast<const uint4*>(p.x)[u];
+        const uint4 raw = load_nt(reinterpret_cast<const uint4*>(p.x) + u);
         const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
         float f[8];
 #pragma unroll
@@ -37,7 +37,7 @@ __global__ __launch_bounds__(256) void fmap_elementwise(FmapParams p) {
             uint32_t hb[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) hb[j] = pack2_bf16(f[2 * j], f[2 * j + 1]);
-            reinterpret_cast<uint4*>(p.y)[u] = make_uint4(hb[0], hb[1], hb[2], hb[3]);
+            store_nt(reinterpret_cast<uint4*>(p.y) + u, make_uint4(hb[0], hb[1], hb[2], hb[3]));
             if (p.y_lo != nullptr) {
                 // residual y - bf16(y), so that hi + lo carries y to about 2^-17
                 uint32_t lb[4];
@@ -45,7 +45,7 @@ __global__ __launch_bounds__(256) void fmap_elementwise(FmapParams p) {
                 for (int j = 0; j < 4; ++j)
                     lb[j] = pack2_bf16(f[2 * j] - __uint_as_float(hb[j] << 16),
                                        f[2 * j + 1] - __uint_as_float(hb[j] & 0xFFFF0000u));
-                reinterpret_cast<uint4*>(p.y_lo)[u] = make_uint4(lb[0], lb[1], lb[2], lb[3]);
+                store_nt(reinterpret_cast<uint4*>(p.y_lo) + u, make_uint4(lb[0], lb[1], lb[2], lb[3]));
             }
         }
     }
@@ -110,7 +110,7 @@ __global__ __launch_bounds__(256) void fmap_favor(FmapParams p) {
             const int r = e / segs, sg = e % segs;
             const int64_t row = slab * 16 + r;
             const uint4 val = *reinterpret_cast<const uint4*>(ys + r * YS + sg * 8);
-            if (row < p.rows) *reinterpret_cast<uint4*>(dst + row * m + sg * 8) = val;
+            if (row < p.rows) store_nt(dst + row * m + sg * 8, val);
         }
     };
 
