@@ -214,16 +214,18 @@ la_status make_plan(Plan& P, la_dtype in_dt, int64_t BH, int64_t L, int64_t d_in
     // register-staged phase-1 kernel runs several workgroups per CU: pieces
     // double while fewer than 1024 run.  The streaming one (bf16 at feature
     // width 64, 128 or 256, value columns a multiple of 64, pieces of whole
-    // 64-row tiles, no decay) holds a CU alone: pieces double while the
-    // workgroups still fit the CUs in one round.
+    // 64-row tiles, no decay, K plain or pre-mapped) holds a CU alone: pieces
+    // double while the workgroups still fit the CUs in one round.  With elu+1
+    // applied in phase 1, long pieces go to the register-staged kernel (it
+    // hides the mapping better; measured), so they are planned for it.
     P.sub = 1;
     const int64_t n_summed = P.final_from_scan ? P.n_groups : P.n_groups - 1;  // groups phase 1 may sum
     if (P.causal && n_summed > 0) {
         const int64_t n_dvt1 = d_v / kernel_dvt(d_v);
         // a piece reads at least eight times the state it writes
         const int64_t min_rows = std::max<int64_t>(512, cdiv(16 * P.dk * d_v, P.dk + d_v));
-        const bool stream1 = !P.i8 && !decay && (P.dk == 64 || P.dk == 128 || P.dk == 256) && d_v % 64 == 0 &&
-                             (P.G * P.C) % 64 == 0;
+        const bool stream1 = !P.i8 && !decay && f != LA_FMAP_ELU1 && (P.dk == 64 || P.dk == 128 || P.dk == 256) &&
+                             d_v % 64 == 0 && (P.G * P.C) % 64 == 0;
         auto more = [&]() {
             const int64_t rows = P.G * P.C / (2 * P.sub);
             if ((P.G * P.C) % (2 * P.sub) != 0 || rows < min_rows) return false;
