@@ -101,6 +101,38 @@ __global__ __launch_bounds__(256) void loglinear_fwd(LogLinParams p) {
     const int valid = (int)(p.L - r0 < LL_C ? p.L - r0 : LL_C);
     const int dv = p.dv;
 
+    // Bucket states: level m (bit m - 1 of n set) holds chunks
+    // [h - 2^(m-1), h) as node (n >> (m - 1)) - 1 of its level: level 1 is the
+    // per-chunk states, levels 2.. the pyramid, level l starting after the
+    // floor(N / 2^(j-1)) nodes of every level j in 2 .. l - 1.  Each state is
+    // loaded into registers one level ahead (the first one before the chunk's
+    // tiles), so its load overlaps the products of the level before.
+    const int64_t E = (int64_t)DK * dv;
+    auto next_level = [&](int m) {  // the first level above m whose bit is set in n, or 0
+        for (int mm = m + 1; (1 << (mm - 1)) <= n; ++mm)
+            if ((n >> (mm - 1)) & 1) return mm;
+        return 0;
+    };
+    auto level_state = [&](int m) -> const float* {
+        const int node = (n >> (m - 1)) - 1;
+        if (m == 1) return p.S + (bh * p.N + node) * E;
+        int base = 0;
+        for (int l = 2; l < m; ++l) base += p.N >> (l - 1);
+        return p.T + (bh * p.n_pyr + base + node) * E;
+    };
+    constexpr int NPT = DK * (LL_DVT / 4) / 256;  // float4 pieces of a state tile per thread
+    float4 xs[NPT];
+    auto load_state = [&](const float* P) {
+#pragma unroll
+        for (int u = 0; u < NPT; ++u) {
+            const int i = tid + u * 256;
+            const int a = i / (LL_DVT / 4), j4 = (i % (LL_DVT / 4)) * 4;
+            xs[u] = *reinterpret_cast<const float4*>(P + (int64_t)a * dv + col0 + j4);
+        }
+    };
+    int m = next_level(0);
+    if (m != 0) load_state(level_state(m));
+
     // chunk tiles into LDS (rows past the end are zero)
     for (int i = tid; i < LL_C * (DK / 8); i += 256) {
         const int r = i / (DK / 8), cg = i % (DK / 8);
@@ -161,27 +193,20 @@ __global__ __launch_bounds__(256) void loglinear_fwd(LogLinParams p) {
     }
 
     // ---- inter: one bucket state per set bit of n
-    const int64_t E = (int64_t)DK * dv;
-    int pyr_base = 0;  // first node of level m in the pyramid (levels >= 2)
-    int level_nodes = p.N / 2;
-    for (int m = 1; (1 << (m - 1)) <= n; ++m) {
-        if (m >= 3) {
-            pyr_base += level_nodes;
-            level_nodes /= 2;
-        }
-        if (!((n >> (m - 1)) & 1)) continue;
-        const int node = (n >> (m - 1)) - 1;
-        const float* P = m == 1 ? p.S + (bh * p.N + node) * E : p.T + (bh * p.n_pyr + pyr_base + node) * E;
+    while (m != 0) {
+        const int mn = next_level(m);
         __syncthreads();  // Ps free
-        for (int i = tid; i < DK * (LL_DVT / 4); i += 256) {
+#pragma unroll
+        for (int u = 0; u < NPT; ++u) {
+            const int i = tid + u * 256;
             const int a = i / (LL_DVT / 4), j4 = (i % (LL_DVT / 4)) * 4;
-            const float4 x = *reinterpret_cast<const float4*>(P + (int64_t)a * dv + col0 + j4);
-            const uint32_t ab = pack2_bf16(x.x, x.y), cd = pack2_bf16(x.z, x.w);
+            const uint32_t ab = pack2_bf16(xs[u].x, xs[u].y), cd = pack2_bf16(xs[u].z, xs[u].w);
             Ps[(j4 + 0) * QS + a] = (u16)(ab & 0xFFFFu);
             Ps[(j4 + 1) * QS + a] = (u16)(ab >> 16);
             Ps[(j4 + 2) * QS + a] = (u16)(cd & 0xFFFFu);
             Ps[(j4 + 3) * QS + a] = (u16)(cd >> 16);
         }
+        if (mn != 0) load_state(level_state(mn));
         __syncthreads();
         f32x4 Om[4];
 #pragma unroll
@@ -195,6 +220,7 @@ __global__ __launch_bounds__(256) void loglinear_fwd(LogLinParams p) {
         const float lw = lam_s[qr * LL_NLMAX + LL_CB + m];
 #pragma unroll
         for (int c = 0; c < 4; ++c) O[c] += lw * Om[c];
+        m = mn;
     }
 
     // ---- output: lane holds columns 16c + 4g .. +3 of row qr
