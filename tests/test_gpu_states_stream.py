@@ -96,3 +96,21 @@ def test_elu1_negative_in_scale(C, L, group, scale):
     assert_close(host(o), np.stack(outs), what="o")
     assert_close(host(S), np.stack(Ss), what="S")
     assert_close(host(z), np.stack(zs), what="z")
+
+
+@pytest.mark.parametrize("d_in", [16, 32, 64, 128])
+@pytest.mark.parametrize("m", [16, 32, 64, 128, 256])
+def test_favor_map_every_width(m, d_in):
+    """The FAVOR+ map at every feature count (a compile-time parameter of the
+    kernel) and input width (16 is padded to 32 inside), over a ragged number
+    of rows, fp32 and bf16 outputs, against the oracle's map."""
+    torch = __import__("torch")
+    rows = 1000 if m <= 64 else 333
+    x = wl.random_case(64 + m + d_in, 1, rows, d_in, 16, "bf16", 1.0 / np.sqrt(d_in))[0]
+    Wb, W = wl.orthogonal_random_features(m, d_in, [64, m, d_in])
+    log(f"favor map m={m} d_in={d_in} rows={rows}")
+    ref = oracle.apply_phi(x.exact, "favor", W, 0.7)
+    y = la.feature_map(dev_input(x), "favor", W=dev_bf16(Wb), in_scale=0.7, out_dtype=torch.float32)
+    assert_close(host(y), ref, tol=1e-4, what="favor fp32")
+    yb = la.feature_map(dev_input(x), "favor", W=dev_bf16(Wb), in_scale=0.7)
+    assert_close(host(yb), ref, tol=8e-3, what="favor bf16")
