@@ -114,3 +114,25 @@ def test_favor_map_every_width(m, d_in):
     assert_close(host(y), ref, tol=1e-4, what="favor fp32")
     yb = la.feature_map(dev_input(x), "favor", W=dev_bf16(Wb), in_scale=0.7)
     assert_close(host(yb), ref, tol=8e-3, what="favor bf16")
+
+
+def test_scan_large_state_set():
+    """The scan of a state set larger than the last-level cache (streamed with
+    the non-temporal hint): 64 heads x 128 chunks x 128 x 128 fp32 (537 MB),
+    every head's final state and a sample of 64 elements of three heads
+    through all chunks, against the oracle's scan of the same values."""
+    torch = __import__("torch")
+    BH, N, D = 64, 128, 128
+    rng = np.random.default_rng(65)
+    S_host = rng.standard_normal((BH, N, D, D), dtype=np.float32)
+    log(f"scan of a large state set BH={BH} N={N} d={D}x{D}")
+    S = torch.from_numpy(S_host).cuda()
+    Sf, _ = la.state_scan(S, None)
+    cols = rng.choice(D * D, 64, replace=False)
+    for h in (0, 31, 63):
+        sample = S_host[h].reshape(N, D * D)[:, cols]
+        refP, reftot = oracle.exclusive_scan(sample)
+        got = host(S[h]).reshape(N, D * D)[:, cols]
+        assert_close(got, refP, tol=1e-5, what=f"prefix head {h}")
+    refall = np.stack([oracle.exclusive_scan(S_host[h])[1] for h in range(BH)])
+    assert_close(host(Sf), refall, tol=1e-5, what="totals")
