@@ -15,14 +15,16 @@
 
 namespace la {
 
-template <int DK, int DV, bool FAV>
+// WIN: the largest FAVOR+ input width the LDS copy of W holds (64 or 128;
+// the smaller copy lets four workgroups share a CU instead of two)
+template <int DK, int DV, bool FAV, int WIN>
 __global__ __launch_bounds__(256) void recurrent_step_kernel(DecodeParams p, int ns_per_block) {
     constexpr int NT = 256;
     constexpr int J4 = DV / 4;          // float4 column groups
     constexpr int AG = NT / J4;         // row groups
     constexpr int RPT = DK / AG > 0 ? DK / AG : 1;  // rows per thread
     constexpr int DINMAX = 256;
-    constexpr int WMAX = FAV ? DK * 128 : 8;  // FAVOR+ projection, d_in <= 128
+    constexpr int WMAX = FAV ? DK * WIN : 8;  // FAVOR+ projection, d_in <= WIN
     static_assert(AG * J4 == NT, "thread layout");
 
     __shared__ float fq[DK], fk[DK], vv[DV];
@@ -139,10 +141,12 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(DecodeParams p, int
 
 template <int DK, int DV>
 static void launch_decode(const DecodeParams& p, unsigned grid, int nsb, hipStream_t s) {
-    if (p.fmap == 2)
-        hipLaunchKernelGGL((recurrent_step_kernel<DK, DV, true>), dim3(grid), dim3(256), 0, s, p, nsb);
+    if (p.fmap == 2 && p.d_in <= 64)
+        hipLaunchKernelGGL((recurrent_step_kernel<DK, DV, true, 64>), dim3(grid), dim3(256), 0, s, p, nsb);
+    else if (p.fmap == 2)
+        hipLaunchKernelGGL((recurrent_step_kernel<DK, DV, true, 128>), dim3(grid), dim3(256), 0, s, p, nsb);
     else
-        hipLaunchKernelGGL((recurrent_step_kernel<DK, DV, false>), dim3(grid), dim3(256), 0, s, p, nsb);
+        hipLaunchKernelGGL((recurrent_step_kernel<DK, DV, false, 64>), dim3(grid), dim3(256), 0, s, p, nsb);
 }
 
 template <int DK>

@@ -136,3 +136,30 @@ def test_scan_large_state_set():
         assert_close(got, refP, tol=1e-5, what=f"prefix head {h}")
     refall = np.stack([oracle.exclusive_scan(S_host[h])[1] for h in range(BH)])
     assert_close(host(Sf), refall, tol=1e-5, what="totals")
+
+
+@pytest.mark.parametrize("d_in,m", [(64, 256), (128, 128), (32, 64)])
+def test_decode_favor_input_widths(d_in, m):
+    """One FAVOR+ decode step at input widths 32, 64 and 128 (the kernel keeps
+    W in LDS sized for d_in <= 64 or <= 128) against the oracle's step."""
+    torch = __import__("torch")
+    rng = np.random.default_rng([66, d_in, m])
+    n, dv = 21, 64
+    S0 = rng.standard_normal((n, m, dv)) * 0.5
+    z0 = np.abs(rng.standard_normal((n, m))) * 10 + 1
+    q, k, v = _case(66 + d_in, 1, n, d_in, dv, scale=0.3)
+    Wb, W = wl.orthogonal_random_features(m, d_in, [66, d_in, m])
+    S = torch.tensor(S0, dtype=torch.float32, device="cuda")
+    z = torch.tensor(z0, dtype=torch.float32, device="cuda")
+    s = d_in ** -0.25
+    log(f"decode FAVOR+ d_in={d_in} m={m}")
+    o = la.recurrent_step(dev_input(q)[0], dev_input(k)[0], dev_input(v)[0], S, z, fmap="favor", W=dev_bf16(Wb),
+                          in_scale=s, normalize=True)
+    S32, z32 = S0.astype(np.float32).astype(np.float64), z0.astype(np.float32).astype(np.float64)
+    for i in range(n):
+        qp = oracle.apply_phi(q.exact[0, i][None], "favor", W, s)[0]
+        kp = oracle.apply_phi(k.exact[0, i][None], "favor", W, s)[0]
+        ro, rS, rz = oracle.recurrent_step(S32[i], z32[i], qp, kp, v.exact[0, i], True)
+        assert_close(host(o)[i], ro, tol=1e-4, what="o")
+        assert_close(host(S)[i], rS, tol=1e-5, what="S")
+        assert_close(host(z)[i], rz, tol=1e-5, what="z")
