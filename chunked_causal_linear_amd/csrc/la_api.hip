@@ -216,8 +216,8 @@ la_status make_plan(Plan& P, la_dtype in_dt, int64_t BH, int64_t L, int64_t d_in
     // width 64, 128 or 256, value columns a multiple of 64, pieces of whole
     // 64-row tiles, no decay, K plain or pre-mapped) holds a CU alone: pieces
     // double while the workgroups still fit the CUs in one round.  With elu+1
-    // applied in phase 1, long pieces go to the register-staged kernel (it
-    // hides the mapping better; measured), so they are planned for it.
+    // applied in phase 1 it runs two workgroups per CU and its pieces are
+    // planned like the register-staged kernel's (measured best).
     P.sub = 1;
     const int64_t n_summed = P.final_from_scan ? P.n_groups : P.n_groups - 1;  // groups phase 1 may sum
     if (P.causal && n_summed > 0) {
@@ -417,6 +417,12 @@ static la_status chunk_states_impl(const void* k, const void* v, bool i8, int64_
     const int dvt_pipe = 64;
     bool stream_ok = (d_k == 64 || d_k == 128 || d_k == 256) && d_v % dvt_pipe == 0 && Cs % 64 == 0 &&
                            Cs >= 256 && lg == 0.0f && (fmap == 0 || fmap == 1);
+    // elu+1 mapped here at feature width 128 or 256 (one streaming workgroup
+    // per CU): only when the workgroups fit the CUs in one round; with more,
+    // the register-staged kernel at several workgroups per CU hides the
+    // mapping better.  At width 64 two streaming workgroups share a CU.
+    if (stream_ok && fmap == 1 && k_lo == nullptr && d_k != 64 && BH * (int64_t)n_items * (d_v / dvt_pipe) > 256)
+        stream_ok = false;
     la::StatesParams p{};
     p.k = static_cast<const unsigned short*>(k);
     p.v = static_cast<const unsigned short*>(v);
@@ -435,11 +441,6 @@ static la_status chunk_states_impl(const void* k, const void* v, bool i8, int64_
     p.want_z = z != nullptr;
     p.xcd_remap = xcd_ok(grid);
     p.log2_gamma = lg;
-    // elu+1 mapped here: the streaming kernel (one workgroup per CU) only when
-    // its workgroups fit the CUs in one round; with more, the register-staged
-    // kernel at several workgroups per CU hides the mapping better (measured)
-    const bool elu_in_kernel = k_lo == nullptr && fmap == 1;
-    if (stream_ok && elu_in_kernel && BH * (int64_t)n_items * (d_v / dvt_pipe) > 256) stream_ok = false;
     if (stream_ok) {
         p.n_dvt = (int)(d_v / dvt_pipe);
         const int64_t sgrid = BH * (int64_t)n_items * p.n_dvt;

@@ -58,15 +58,25 @@ __device__ __forceinline__ void wait_tiles(int after) {
 
 }  // namespace pipe
 
+// With elu+1 applied here at feature width 64, two workgroups share a CU
+// (three stages each, at most 256 VGPRs), so that the mapping of one overlaps
+// the other's waits (measured: 129 us against 157 with one workgroup of six
+// stages per CU at 32 heads x 65536 rows in 1024 pieces); otherwise one
+// workgroup per CU with as many stages as fit.
+template <int DK, int KIND>
+constexpr int states_pipe_per_cu() { return KIND == KIND_ELU && DK == 64 ? 2 : 1; }
+
 template <int DK, int DVT, int KIND, bool Z>
-__global__ __launch_bounds__(4 * WAVE) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(4 * WAVE) __attribute__((amdgpu_waves_per_eu(states_pipe_per_cu<DK, KIND>(),
+                                                                           states_pipe_per_cu<DK, KIND>())))
 void chunk_states_pipe(StatesParams p) {
     using namespace pipe;
     constexpr int TT = DK == 256 ? 32 : 64;        // rows per tile (four stages fit at every width)
     constexpr bool LO = KIND != KIND_PLAIN;        // a residual tile
     typedef StateStage<DK, DVT, TT, LO> StageT;
     constexpr int NFIT = (int)(160 * 1024 / sizeof(StageT));
-    constexpr int NSTAGE = NFIT < 8 ? NFIT : 8;    // LDS stages
+    constexpr int NMAX = states_pipe_per_cu<DK, KIND>() == 2 ? 3 : 8;
+    constexpr int NSTAGE = NFIT < NMAX ? NFIT : NMAX;  // LDS stages
     constexpr int CPW = DVT / 32;                  // 16-column blocks per compute wave
     constexpr int NCB = CPW + (Z ? 1 : 0);         // + the block of z
     constexpr int NKA = DK / 32;                   // 32-row blocks of the state
