@@ -30,7 +30,7 @@ namespace {
 constexpr int LL_C = 64;          // rows per chunk
 constexpr int LL_CB = 6;          // log2 of it
 constexpr int LL_DVT = 64;        // value columns per workgroup
-constexpr int LL_NLMAX = 40;      // levels held in LDS (bit length of L - 1 plus one)
+constexpr int LL_NLMAX = 40;      // most levels (bit length of L - 1 plus one)
 
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
@@ -80,15 +80,20 @@ __global__ __launch_bounds__(256) void loglinear_pyramid_kernel(const float4* __
     }
 }
 
+// Three workgroups share a CU (at most 168 VGPRs, 46 KB of LDS at d_k = 128):
+// the bucket state tile reuses K's LDS once the intra part is done, and only
+// the in-chunk level weights (levels 0..6) are staged; a bucket's weight is
+// read per row from global memory.
 template <int DK>
-__global__ __launch_bounds__(256) void loglinear_fwd(LogLinParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void loglinear_fwd(LogLinParams p) {
     constexpr int QS = DK + 8, VS = LL_DVT + 8;  // padded row strides (elements)
     constexpr int NKA = DK / 32;
+    constexpr int NLI = LL_CB + 2;               // in-chunk levels 0..LL_CB, padded
     __shared__ __attribute__((aligned(16))) u16 Qs[LL_C * QS];
-    __shared__ __attribute__((aligned(16))) u16 Ks[LL_C * QS];
+    __shared__ __attribute__((aligned(16))) u16 Ks[LL_C * QS];  // K, then the bucket state (transposed: [j][a])
     __shared__ __attribute__((aligned(16))) u16 Vs[LL_C * VS];
-    __shared__ __attribute__((aligned(16))) u16 Ps[LL_DVT * QS];  // bucket state, transposed: Ps[j][a]
-    __shared__ float lam_s[LL_C * LL_NLMAX];
+    __shared__ float lam_s[LL_C * NLI];
+    u16* const Ps = Ks;
 
     const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE, l16 = lane % 16, g = lane / 16;
     int w = blockIdx.x;
@@ -150,8 +155,8 @@ __global__ __launch_bounds__(256) void loglinear_fwd(LogLinParams p) {
         if (r < valid) vv = *reinterpret_cast<const uint4*>(p.v + (bh * p.L + r0 + r) * dv + col0 + cg * 8);
         *reinterpret_cast<uint4*>(Vs + r * VS + cg * 8) = vv;
     }
-    for (int i = tid; i < LL_C * LL_NLMAX; i += 256) {
-        const int r = i / LL_NLMAX, l = i % LL_NLMAX;
+    for (int i = tid; i < LL_C * NLI; i += 256) {
+        const int r = i / NLI, l = i % NLI;
         lam_s[i] = (r < valid && l < p.n_lev) ? p.lam[(bh * p.L + r0 + r) * p.n_lev + l] : 0.f;
     }
     __syncthreads();
@@ -181,7 +186,7 @@ __global__ __launch_bounds__(256) void loglinear_fwd(LogLinParams p) {
             for (int i = 0; i < 4; ++i) {
                 const int key = kb * 16 + 4 * g + i;
                 const int lev = key == qr ? 0 : bit_length((unsigned)(key ^ qr));
-                St[kb][i] = (kb <= wave && key <= qr) ? St[kb][i] * lam_s[qr * LL_NLMAX + lev] : 0.f;
+                St[kb][i] = (kb <= wave && key <= qr) ? St[kb][i] * lam_s[qr * NLI + lev] : 0.f;
             }
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
@@ -193,9 +198,11 @@ __global__ __launch_bounds__(256) void loglinear_fwd(LogLinParams p) {
     }
 
     // ---- inter: one bucket state per set bit of n
+    const float* lam_row = p.lam + (bh * p.L + r0 + (qr < valid ? qr : 0)) * p.n_lev;
     while (m != 0) {
         const int mn = next_level(m);
-        __syncthreads();  // Ps free
+        const float lw = qr < valid ? lam_row[LL_CB + m] : 0.f;
+        __syncthreads();  // Ps free (the first time: K is no longer read)
 #pragma unroll
         for (int u = 0; u < NPT; ++u) {
             const int i = tid + u * 256;
@@ -217,7 +224,6 @@ __global__ __launch_bounds__(256) void loglinear_fwd(LogLinParams p) {
 #pragma unroll
             for (int c = 0; c < 4; ++c) Om[c] = mfma_bf16(row_operand(Ps, QS, c * 16 + l16, ks * 32, g), qb, Om[c]);
         }
-        const float lw = lam_s[qr * LL_NLMAX + LL_CB + m];
 #pragma unroll
         for (int c = 0; c < 4; ++c) O[c] += lw * Om[c];
         m = mn;
