@@ -58,24 +58,53 @@ __device__ __forceinline__ bf16x8 col_operand(const u16* t, int stride, int key0
 
 __device__ __forceinline__ int bit_length(unsigned x) { return x == 0 ? 0 : 32 - __builtin_clz(x); }
 
+__device__ __forceinline__ float4 add4f(const float4& a, const float4& b) {
+    return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+}
+
+// Level m >= 2 has floor(N / 2^(m-1)) nodes; node j = nodes 2j and 2j+1 of
+// level m - 1.  Each whole group of eight chunk states is read once and its
+// level-2, -3 and -4 nodes are summed in registers (no level is read back);
+// the rest (the tail of levels 2..4 and every level from 5 on) is summed level
+// by level from the level below.
 __global__ __launch_bounds__(256) void loglinear_pyramid_kernel(const float4* __restrict__ S, float4* __restrict__ T,
                                                                 int64_t BH, int N, int n_pyr, int64_t E4) {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= BH * E4) return;
     const int64_t bh = idx / E4, e = idx % E4;
-    const float4* src = S + bh * N * E4 + e;  // level 1: the chunk states
-    int64_t src_stride = E4;
+    const float4* s1 = S + bh * N * E4 + e;  // level 1: the chunk states
     float4* out = T + bh * (int64_t)n_pyr * E4 + e;
-    int nodes = N;
-    while (nodes >= 2) {
-        const int next = nodes / 2;
-        for (int j = 0; j < next; ++j) {
-            const float4 a = src[(2 * j) * src_stride], b = src[(2 * j + 1) * src_stride];
-            out[j * E4] = make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+    const int n2 = N / 2, n3 = n2 / 2;
+    float4* l2 = out;
+    float4* l3 = l2 + (int64_t)n2 * E4;
+    float4* l4 = l3 + (int64_t)n3 * E4;
+    const int g8 = N / 8;  // whole groups of eight
+    for (int b = 0; b < g8; ++b) {
+        float4 x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = s1[(int64_t)(8 * b + u) * E4];
+        float4 y[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            y[u] = add4f(x[2 * u], x[2 * u + 1]);
+            l2[(int64_t)(4 * b + u) * E4] = y[u];
         }
-        src = out;
-        src_stride = E4;
-        out += next * E4;
+        const float4 z0 = add4f(y[0], y[1]), z1 = add4f(y[2], y[3]);
+        l3[(int64_t)(2 * b) * E4] = z0;
+        l3[(int64_t)(2 * b + 1) * E4] = z1;
+        l4[(int64_t)b * E4] = add4f(z0, z1);
+    }
+    // the rest, level by level: level m's nodes from `done` on
+    const float4* src = s1;
+    float4* dst = l2;
+    int nodes = N;
+    for (int m = 2; nodes >= 2; ++m) {
+        const int next = nodes / 2;
+        const int done = m == 2 ? 4 * g8 : (m == 3 ? 2 * g8 : (m == 4 ? g8 : 0));
+        for (int j = done; j < next; ++j)
+            dst[(int64_t)j * E4] = add4f(src[(int64_t)(2 * j) * E4], src[(int64_t)(2 * j + 1) * E4]);
+        src = dst;
+        dst += (int64_t)next * E4;
         nodes = next;
     }
 }
