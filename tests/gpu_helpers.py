@@ -57,6 +57,24 @@ def assert_close(gpu: np.ndarray, ref: np.ndarray, tol: float = TOL, what: str =
     return worst
 
 
+def assert_close_scaled(gpu: np.ndarray, ref: np.ndarray, scale: np.ndarray, tol_scale: float,
+                        tol: float = TOL, what: str = "") -> float:
+    """Per-element band |gpu - ref| <= tol (1 + |ref|) + tol_scale |scale|: the
+    usual band plus, for sums whose terms cancel, a part relative to the sum
+    of the terms' magnitudes (`scale`), to which the rounding error of bf16
+    operands is proportional."""
+    assert gpu.shape == ref.shape == scale.shape, (what, gpu.shape, ref.shape, scale.shape)
+    assert np.all(np.isfinite(gpu)), f"{what}: non-finite GPU values"
+    band = tol * (1.0 + np.abs(ref)) + tol_scale * np.abs(scale)
+    ratio = np.abs(gpu.astype(np.float64) - ref) / band
+    worst = float(ratio.max()) if ratio.size else 0.0
+    if worst > 1.0:
+        idx = np.unravel_index(int(np.argmax(ratio)), ratio.shape)
+        raise AssertionError(f"{what}: worst |err|/band = {worst:.3f} at {idx}: gpu={gpu[idx]} ref={ref[idx]} "
+                             f"scale={scale[idx]}")
+    return worst
+
+
 def assert_exact(gpu: np.ndarray, ref: np.ndarray, what: str = "") -> None:
     assert gpu.shape == ref.shape, (what, gpu.shape, ref.shape)
     ref32 = ref.astype(np.int64)
