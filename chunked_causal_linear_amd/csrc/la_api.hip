@@ -191,10 +191,13 @@ la_status make_plan(Plan& P, la_dtype in_dt, int64_t BH, int64_t L, int64_t d_in
             if (want > P.n_chunks) want = P.n_chunks;
             P.G = cdiv(P.n_chunks, want);
         }
-        // chunks of 32 are walked in tiles of two: groups start on a tile
+        // chunks of 32 are walked in tiles of two: groups start on a tile.  An
+        // odd group the caller asked for goes to the general kernel, except
+        // with the decay, which only the streaming kernel has: rounded up
+        // there (the group size changes no result beyond rounding order).
         if (P.pipe && Ce == 32 && P.G < P.n_chunks && (P.G & 1)) {
-            if (group > 0)
-                P.pipe = false;  // an odd group the caller asked for: the general kernel
+            if (group > 0 && !decay)
+                P.pipe = false;
             else
                 P.G += 1;
         }
@@ -697,8 +700,12 @@ static la_status chunk_output_entry(const void* q, const void* k, const void* v,
     if (z_final != nullptr && !normalize) return fail(LA_ERR_INVALID_ARG, "z_final needs normalize");
     if (group < 1) return fail(LA_ERR_INVALID_ARG, "group must be at least 1");
     Plan P{};
-    st = make_plan(P, in_dt, BH, L, d_k, d_v, C, 1, normalize, LA_FMAP_IDENTITY, 0, 1.0f, group, gamma != 1.0f);
+    // planned without the decay, which may round the group: the caller's
+    // prefixes are laid out at exactly this group size
+    st = make_plan(P, in_dt, BH, L, d_k, d_v, C, 1, normalize, LA_FMAP_IDENTITY, 0, 1.0f, group, false);
     if (st != LA_OK) return st;
+    if (P.G != (group < P.n_chunks ? group : P.n_chunks))
+        return fail(LA_ERR_UNSUPPORTED, "group %lld cannot be kept for these arguments", (long long)group);
     if (P.n_groups > 1 && (P_prefix == nullptr || (normalize && z_prefix == nullptr)))
         return fail(LA_ERR_INVALID_ARG, "more than one group needs the prefix states (and normalisers)");
     P.sub = 1;  // the caller's prefixes: one per group
@@ -706,7 +713,7 @@ static la_status chunk_output_entry(const void* q, const void* k, const void* v,
     if (lg != 0.0f && !(P.pipe && out_dt == LA_BF16))
         return fail(LA_ERR_UNSUPPORTED,
                     "the decayed recurrence runs on the streaming kernel: bf16 in and out, C in {32, 64, 128} with d_k "
-                    "in {64, 128} and d_v a multiple of 64, or C in {32, 64} with d_k = 256");
+                    "in {64, 128} and d_v a multiple of 64, or C in {32, 64} with d_k = 256; at C = 32 an even group");
     return launch_phase3(P, q, k, nullptr, v, o, out_dt, P_prefix, z_prefix, S_final, z_final, la::FMAP_NONE,
                          1.0f, false, (hipStream_t)stream, lg);
 }

@@ -237,8 +237,11 @@ la_status la_recurrent_step(const void* q, const void* k, const void* v, la_dtyp
  * gamma^(e-1-r) phi(k_r)^T v_r.  The forward and the chunk output run on the
  * streaming kernel only: causal, LA_BF16 in and out, C in {32, 64, 128} with
  * d_k in {64, 128} and d_v a multiple of 64, or C in {32, 64} with d_k = 256;
- * any other combination is LA_ERR_UNSUPPORTED.  The forward needs the
- * workspace la_chunked_forward_workspace gives for the same arguments.
+ * any other combination is LA_ERR_UNSUPPORTED.  At C = 32 the streaming kernel
+ * walks chunks in pairs: the forward rounds an odd group up to the next even
+ * one, and la_chunk_output_decay needs an even group (or one that covers every
+ * chunk).  The forward needs the workspace la_chunked_forward_workspace gives
+ * for the same arguments.
  */
 la_status la_chunked_forward_decay(const void* q, const void* k, const void* v, la_dtype in_dt,
                                    int64_t BH, int64_t L, int64_t d_in, int64_t d_v, int64_t C,

@@ -64,3 +64,40 @@ def test_random_shape(i):
         assert_close(host(S)[h], rS, what=f"S head {h}")
         if c["normalize"]:
             assert_close(host(z)[h], rz, what=f"z head {h}")
+
+
+def _draw_decay(i):
+    r = np.random.default_rng([79, i])
+    fmap = ["identity", "elu1"][int(r.integers(0, 2))]
+    d_k = int(r.choice([64, 128]))
+    C = int(r.choice([32, 64, 128]))
+    d_v = int(r.choice([64, 128]))
+    L = int(r.integers(1, 1400))
+    BH = int(r.integers(1, 3))
+    normalize = fmap == "elu1" and bool(r.integers(0, 2))
+    group = int(r.choice([0, 0, 1, 2, 5]))
+    gamma = float(r.choice([0.9, 0.99, 0.999]))
+    return dict(fmap=fmap, d_k=d_k, C=C, d_v=d_v, L=L, BH=BH, normalize=normalize, group=group, gamma=gamma)
+
+
+@pytest.mark.parametrize("i", range(20))
+def test_random_shape_decay(i):
+    """The decayed recurrence (gamma < 1) over seeded random streaming shapes."""
+    c = _draw_decay(i)
+    log(f"random decayed shape {i}: {c}")
+    q, k, v = wl.random_case(80 + i, c["BH"], c["L"], c["d_k"], c["d_v"], "bf16", 1.0 / np.sqrt(c["d_k"]))
+    o, S, z = la.chunked_forward(dev_input(q), dev_input(k), dev_input(v), c["C"], normalize=c["normalize"],
+                                 fmap=c["fmap"], return_state=True, group=c["group"], gamma=c["gamma"])
+    cancelling = c["fmap"] != "identity" and not c["normalize"]
+    for h in range(c["BH"]):
+        ro, rS, rz = oracle.forward(q.exact[h], k.exact[h], v.exact[h], c["C"], True, c["normalize"], c["fmap"],
+                                    None, 1.0, c["gamma"])
+        if cancelling:
+            mag, _, _ = oracle.forward(q.exact[h], k.exact[h], np.abs(v.exact[h]), c["C"], True, False, c["fmap"],
+                                       None, 1.0, c["gamma"])
+            assert_close_scaled(host(o)[h], ro, mag, 3 * 2.0 ** -8, what=f"o head {h}")
+        else:
+            assert_close(host(o)[h], ro, what=f"o head {h}")
+        assert_close(host(S)[h], rS, what=f"S head {h}")
+        if c["normalize"]:
+            assert_close(host(z)[h], rz, what=f"z head {h}")
