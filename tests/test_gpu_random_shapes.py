@@ -101,3 +101,44 @@ def test_random_shape_decay(i):
         assert_close(host(S)[h], rS, what=f"S head {h}")
         if c["normalize"]:
             assert_close(host(z)[h], rz, what=f"z head {h}")
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_shape_loglinear(i):
+    """Log-linear attention over seeded random lengths (odd chunk counts and
+    ragged tails exercise the pyramid's groups of eight and its tail) and
+    widths."""
+    torch = __import__("torch")
+    r = np.random.default_rng([83, i])
+    BH, L = int(r.integers(1, 3)), int(r.integers(65, 3000))
+    dk, dv = int(r.choice([64, 128])), int(r.choice([64, 128, 256]))
+    q, k, v = wl.random_case(84 + i, BH, L, dk, dv, "bf16", 1.0 / np.sqrt(dk))
+    nl = la.loglinear_levels(L)
+    lam = wl.loglinear_weights(84 + i, BH, L, nl)
+    log(f"random loglinear {i}: BH={BH} L={L} dk={dk} dv={dv} levels={nl}")
+    o = la.loglinear_forward(dev_input(q), dev_input(k), dev_input(v), torch.from_numpy(lam).cuda())
+    ref = np.stack([oracle.loglinear_chunked(q.exact[h], k.exact[h], v.exact[h], lam[h].astype(np.float64), 64)
+                    for h in range(BH)])
+    assert_close(host(o), ref, what="o")
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_three_phases(i):
+    """la_chunk_states at group granularity (runs of C * group rows: the
+    streaming or the register-staged kernel by size), la_state_scan and
+    la_chunk_output against the oracle's forward, over seeded random shapes."""
+    r = np.random.default_rng([85, i])
+    BH, L = int(r.integers(1, 3)), int(r.integers(1, 2500))
+    d_k, d_v = int(r.choice([64, 128])), int(r.choice([64, 128]))
+    C = int(r.choice([32, 64, 128]))
+    group = int(r.choice([1, 2, 4, 8]))
+    q, k, v = wl.random_case(86 + i, BH, L, d_k, d_v, "bf16", 1.0 / np.sqrt(d_k))
+    log(f"random three phases {i}: BH={BH} L={L} d_k={d_k} d_v={d_v} C={C} group={group}")
+    qd, kd, vd = dev_input(q), dev_input(k), dev_input(v)
+    S, _ = la.chunk_states(kd, vd, C * group)
+    la.state_scan(S, None, want_final=False)
+    o, Sf, _ = la.chunk_output(qd, kd, vd, C, group, P_prefix=S, return_state=True)
+    for h in range(BH):
+        ro, rS, _ = oracle.forward(q.exact[h], k.exact[h], v.exact[h], C)
+        assert_close(host(o)[h], ro, what=f"o head {h}")
+        assert_close(host(Sf)[h], rS, what=f"S head {h}")
