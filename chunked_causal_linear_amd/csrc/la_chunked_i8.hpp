@@ -154,8 +154,16 @@ using namespace detail_i8;
 // ===========================================================================
 // Phase 3, int8
 // ===========================================================================
+// With 64-row tiles at feature width up to 128, at most 256 VGPRs so that two
+// workgroups share a CU (their loads and barriers overlap; measured 0.68 ->
+// 0.63 ms at 128 heads x 8192 rows, d 128); wider cases keep their registers.
+template <int DK, int T>
+constexpr int i8_waves_per_eu() { return DK <= 128 && T == 64 ? 2 : 1; }
+
 template <int DK, int DVT, int T, int NW>
-__global__ __launch_bounds__(NW * WAVE) void chunked_fwd_i8(FwdParamsI8 p) {
+__global__ __launch_bounds__(NW * WAVE)
+__attribute__((amdgpu_waves_per_eu(i8_waves_per_eu<DK, T>(), i8_waves_per_eu<DK, T>())))
+void chunked_fwd_i8(FwdParamsI8 p) {
     using G = GeoI8<DK, DVT, T>;
     constexpr int NT = NW * WAVE;
     constexpr int NB = T / 16;
