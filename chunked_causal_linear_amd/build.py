@@ -39,6 +39,7 @@ CFLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-I" + INCLUDE
 # it: that form fails to compile at their register pressure.
 FILE_FLAGS = {"la_pipe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
               "la_pipe_decay.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+              "la_pipe_decay_fac.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
               "la_fmap.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 

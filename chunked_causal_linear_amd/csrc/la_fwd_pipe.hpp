@@ -74,6 +74,26 @@
 // stays below the operand rounding of the inter product; a returned final
 // state or normaliser, where it would not, is summed elsewhere with phi(k)'s
 // residual (phase 1 and the scan), and the kernel then writes none.
+//
+// Decayed recurrence (S_t = gamma S_{t-1} + k_t^T v_t, the Retention form): row
+// i of a chunk of n rows reads gamma^(i+1) P and gamma^(i-j) of key j's score,
+// and the chunk enters as P <- gamma^n P + sum_j gamma^(n-1-j) k_j^T v_j.  Two
+// forms compute it:
+//  * direct: every score times gamma^(i-j) (per-lane powers in registers), the
+//    inter product times gamma^(i+1), P times gamma^n at every update;
+//  * factored: P = sigma P' with a wave-uniform sigma (a power of gamma).  With
+//    c_j = gamma^(-1-j) / sigma, gamma^(i-j) = rho_i c_j for rho_i =
+//    gamma^(i+1) sigma, so row i is rho_i (q_i P' + sum_{j<=i} (q_i k_j) c_j v_j)
+//    and the update is P' += sum_j c_j k_j^T v_j, sigma *= gamma^n: one set of
+//    weighted V operands serves the intra product and the update, the scores
+//    need only the causal mask, rho_i is applied once per output (and cancels
+//    in the normalised ratio), and P' is rescaled only when sigma falls below
+//    2^-16.  Then c_j <= gamma^(-TT) 2^16: the host takes this form when
+//    TT |log2 gamma| <= 48 (c_j and P' stay below 2^64 times their scale).
+//    sigma = gamma^nr, nr the rows since the last rescale (an integer both
+//    sides of the workgroup count alike), and the copy waves weight the V rows
+//    of a tile in LDS as it lands (V is read only weighted), so the compute
+//    waves read V as without the decay.
 #pragma once
 
 #include <type_traits>
@@ -82,6 +102,11 @@
 #include "la_kernels.hpp"
 
 namespace la {
+
+enum { DECAY_NONE = 0, DECAY_DIRECT = 1, DECAY_FACTORED = 2 };
+// threshold of the factored form's rescaling, and its eligibility (see above)
+constexpr float kFacRescaleLog2 = -16.0f;
+constexpr float kFacMaxLog2Range = 48.0f;
 
 namespace pipe {
 
@@ -158,6 +183,13 @@ __device__ __forceinline__ bf16x8 scale_bf16x8(const bf16x8& v, const float (&w)
         y[j] = pack2_bf16(__uint_as_float(x[j] << 16) * w[2 * j], __uint_as_float(x[j] & 0xFFFF0000u) * w[2 * j + 1]);
     return as_bf16x8(make_uint4(y[0], y[1], y[2], y[3]));
 }
+__device__ __forceinline__ uint4 scale_bf16x8_by(const uint4& u, float w) {
+    const uint32_t x[4] = {u.x, u.y, u.z, u.w};
+    uint32_t y[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) y[j] = pack2_bf16(__uint_as_float(x[j] << 16) * w, __uint_as_float(x[j] & 0xFFFF0000u) * w);
+    return make_uint4(y[0], y[1], y[2], y[3]);
+}
 __device__ __forceinline__ bf16x8 pack_bf16x8(const float (&w)[8]) {
     return as_bf16x8(make_uint4(pack2_bf16(w[0], w[1]), pack2_bf16(w[2], w[3]), pack2_bf16(w[4], w[5]),
                                 pack2_bf16(w[6], w[7])));
@@ -189,7 +221,7 @@ using ic = std::integral_constant<int, I>;
 
 }  // namespace pipe
 
-template <int DK, int DVT, int CH, bool SCALED, bool NORM, bool PHI, bool DECAY>
+template <int DK, int DVT, int CH, bool SCALED, bool NORM, bool PHI, int DECAY>
 __global__ __launch_bounds__(4 * WAVE) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void chunked_fwd_pipe(FwdParams p) {
     using namespace pipe;
@@ -204,6 +236,7 @@ void chunked_fwd_pipe(FwdParams p) {
     constexpr int NCV = TT * VSEG / WAVE / 2;      // the same for V (and for the output stores)
     constexpr int NL = 2 * NCQ + NCV;              // copy instructions per tile and copy wave
     constexpr int RPV = WAVE / VSEG;               // output rows per store instruction
+    constexpr bool DIR = DECAY == DECAY_DIRECT, FAC = DECAY == DECAY_FACTORED;
     static_assert(DVT == 64 || (DVT == 32 && DK == 256), "tile of 64 value columns (32 at feature width 256)");
     static_assert(CH == 32 || CH == 64 || CH == 128, "chunks of 32, 64 or 128 rows");
     static_assert(DK == 64 || DK == 128 || DK == 256, "feature width 64, 128 or 256");
@@ -219,6 +252,8 @@ void chunked_fwd_pipe(FwdParams p) {
     const bool copier = wave >= 2;                               // wave-uniform
     const int h = __builtin_amdgcn_readfirstlane(wave & 1);      // pair (wave-uniform)
     const int colw = h * CPW * 16;                               // first column of the pair
+    // factored decay: rows after which the state is rescaled (sigma >= 2^-16)
+    const int nr_max = p.log2_gamma < 0.f ? (int)fminf(-kFacRescaleLog2 / -p.log2_gamma, 1e9f) : 1 << 30;
 
     const int w = work_index(p.xcd_remap);
     const int jt = w % p.n_dvt;
@@ -292,6 +327,28 @@ void chunked_fwd_pipe(FwdParams p) {
             phi_blocks(s, valid, ic<0>{}, ic<NPK>{});
         else
             phi_blocks(s, valid, ic<NPK>{}, ic<NPC>{});
+    };
+
+    // factored decay: this copy wave's own V slots of a landed tile (V
+    // instruction i, lane l: slot (h NCV + i) WAVE + l, row slot / VSEG) times
+    // c_j = gamma^(-(1 + j + nr)), j the row within its chunk and gamma^nr the
+    // state scale at the chunk's start (chunks of 32: the second chunk of the
+    // tile starts after the first one's rows)
+    auto weigh_v_tile = [&](StageT& s, int valid, int nr) __attribute__((always_inline)) {
+        const int na = valid < 32 ? valid : 32;
+#pragma unroll
+        for (int i = 0; i < NCV; ++i) {
+            const int slot = (h * NCV + i) * WAVE + lane;
+            const int r = slot / VSEG;
+            const int e = CH == 32 && r >= 32 ? r - 32 + 1 + nr + na : r + 1 + nr;
+            uint4* x = reinterpret_cast<uint4*>(s.v) + slot;
+            *x = scale_bf16x8_by(*x, __builtin_amdgcn_exp2f(-(float)e * p.log2_gamma));
+        }
+    };
+    // the copy side's count of rows since the rescale, advanced past a tile
+    auto next_nr = [&](int nr, int64_t t) __attribute__((always_inline)) {
+        const int n = nr > nr_max ? 0 : nr;
+        return n + valid_rows(t);
     };
 
     if (copier) {
@@ -378,6 +435,8 @@ void chunked_fwd_pipe(FwdParams p) {
             if (t_begin + s0 < t_end) issue(t_begin + s0, st[s0]);
         land(after_of(t_begin));
         if constexpr (PHI) phi_share(st[0], valid_rows(t_begin));
+        int nr_c = 0;  // factored decay: rows since the rescale before tile t
+        if constexpr (FAC) weigh_v_tile(st[0], valid_rows(t_begin), 0);
 
         // The copy side walks the stages with a run-time index (its accesses
         // take computed addresses anyway), so its code appears once.
@@ -403,6 +462,10 @@ void chunked_fwd_pipe(FwdParams p) {
             if (t + 1 < t_end) {
                 land(after_of(t + 1));
                 if constexpr (PHI) phi_share(st[sn], valid_rows(t + 1));
+                if constexpr (FAC) {
+                    nr_c = next_nr(nr_c, t);
+                    weigh_v_tile(st[sn], valid_rows(t + 1), nr_c > nr_max ? 0 : nr_c);
+                }
             }
             if (t > t_begin) store_out(t - 1, ob);
             si = sn;
@@ -465,12 +528,14 @@ void chunked_fwd_pipe(FwdParams p) {
         return e < 0 ? 0.f : __builtin_amdgcn_exp2f((float)e * lg);
     };
     constexpr int ND = CH == 128 ? 8 : 4;
-    float fd[DECAY ? ND : 1][4], fin[4], fin64[4];
-    if constexpr (DECAY) {
+    float fd[DIR ? ND : 1][4], fin[4], fin64[4];
+    if constexpr (DIR) {
 #pragma unroll
         for (int d = 0; d < ND; ++d)
 #pragma unroll
             for (int i = 0; i < 4; ++i) fd[d][i] = gpow(16 * d + l16 - 4 * g - i);
+    }
+    if constexpr (DECAY) {
 #pragma unroll
         for (int qb = 0; qb < 4; ++qb) {
             fin[qb] = gpow(16 * qb + l16 + 1);
@@ -481,7 +546,7 @@ void chunked_fwd_pipe(FwdParams p) {
     // of their chunk: scale them before the intra parts are added
     auto decay_inter = [&](f32x4 (&O)[NCB][4], const float (&f)[4], int b0, int b1, int shift)
         __attribute__((always_inline)) {
-        if constexpr (DECAY) {
+        if constexpr (DIR) {
 #pragma unroll
             for (int c = 0; c < NCB; ++c)
 #pragma unroll
@@ -528,7 +593,7 @@ void chunked_fwd_pipe(FwdParams p) {
                 for (int qb = 0; qb < 4; ++qb)
                     if ((INTER >> qb) & 1) O[c][qb] = mfma_bf16(pst[c][ks], qa[ks & 1][qb], O[c][qb]);
         }
-        if constexpr (DECAY) {
+        if constexpr (DIR) {
             // every score times gamma^(query - key); 0 above the diagonal
 #pragma unroll
             for (int qb = 0; qb < 4; ++qb)
@@ -548,15 +613,8 @@ void chunked_fwd_pipe(FwdParams p) {
 
     // intra product of a window: query blocks qb < 4 of O against the key steps
     // kk <= qb / 2 of its own 64 keys (V key rows 32 * (KK0 + kk))
-    auto tri_intra = [&](const StageT& s, auto kk0c, const f32x4 (&S)[10], f32x4 (&O)[NCB][4])
+    auto tri_intra_v = [&](const bf16x8 (&vb)[NCB][2], const f32x4 (&S)[10], f32x4 (&O)[NCB][4])
         __attribute__((always_inline)) {
-        constexpr int KK0 = decltype(kk0c)::value;
-        bf16x8 vb[NCB][2];
-#pragma unroll
-        for (int c = 0; c < NCB; ++c)
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-                vb[c][kk] = c < CPW ? col_op<VSEG>(s.v, (KK0 + kk) * 32, colw + c * 16 + c4, lane) : ones;
 #pragma unroll
         for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
@@ -567,49 +625,55 @@ void chunked_fwd_pipe(FwdParams p) {
                 for (int c = 0; c < NCB; ++c) O[c][qb] = mfma_bf16(vb[c][kk], sb, O[c][qb]);
             }
     };
-
-    // state update with the key steps KK0 .. KK0 + NK - 1 of the tile, K column
-    // operands one (ks, hf) step ahead
-    // With the decay, the chunk (keys from row kbase, n_rows of them) enters as
-    // P <- gamma^n P + sum_j gamma^(n-1-j) k_j^T v_j: the state is scaled and
-    // each key's V operand (the ones of the denominator block too) weighted.
-    auto update = [&](const StageT& s, auto kk0c, auto nkc, int n_rows, int kbase) __attribute__((always_inline)) {
+    // V column operands of key steps KK0 .. KK0 + NK - 1 (the ones of the
+    // denominator block last)
+    auto load_v = [&](const StageT& s, auto kk0c, auto nkc, bf16x8 (&vb)[NCB][decltype(nkc)::value])
+        __attribute__((always_inline)) {
         constexpr int KK0 = decltype(kk0c)::value, NK = decltype(nkc)::value;
-        bf16x8 vb[NCB][NK];
 #pragma unroll
         for (int c = 0; c < NCB; ++c)
 #pragma unroll
             for (int kk = 0; kk < NK; ++kk)
                 vb[c][kk] = c < CPW ? col_op<VSEG>(s.v, (KK0 + kk) * 32, colw + c * 16 + c4, lane) : ones;
-        if constexpr (DECAY) {
-            const float gn = __builtin_amdgcn_exp2f((float)n_rows * lg);
+    };
+    auto tri_intra = [&](const StageT& s, auto kk0c, const f32x4 (&S)[10], f32x4 (&O)[NCB][4])
+        __attribute__((always_inline)) {
+        bf16x8 vb[NCB][2];
+        load_v(s, kk0c, ic<2>{}, vb);
+        tri_intra_v(vb, S, O);
+    };
+    // the same operands with key j (local to a chunk of n_rows keys starting at
+    // tile row kbase) weighted by exp2((n_rows - 1 - j) lg - shift), 0 for
+    // j >= n_rows: one power per run of four keys, the earlier keys by
+    // multiplying by gamma.  Operand element e holds key 32 (KK0 + kk) + 4g + e
+    // (e < 4), + 16 (e >= 4).
+    auto load_v_weighted = [&](const StageT& s, auto kk0c, auto nkc, int n_rows, int kbase, float shift,
+                               bf16x8 (&vb)[NCB][decltype(nkc)::value]) __attribute__((always_inline)) {
+        constexpr int KK0 = decltype(kk0c)::value, NK = decltype(nkc)::value;
+        load_v(s, kk0c, nkc, vb);
+        const float gam = __builtin_amdgcn_exp2f(lg);
 #pragma unroll
-            for (int c = 0; c < NCB; ++c)
+        for (int kk = 0; kk < NK; ++kk) {
+            float w[8];
 #pragma unroll
-                for (int ks = 0; ks < NKA; ++ks) {
-                    P[c][ks][0] *= gn;
-                    P[c][ks][1] *= gn;
+            for (int hh = 0; hh < 2; ++hh) {
+                const int key3 = 32 * (KK0 + kk) + 16 * hh + 4 * g + 3 - kbase;
+                float wk = __builtin_amdgcn_exp2f((float)(n_rows - 1 - key3) * lg - shift);
+#pragma unroll
+                for (int j = 3; j >= 0; --j) {
+                    w[4 * hh + j] = key3 - 3 + j < n_rows ? wk : 0.f;
+                    wk *= gam;
                 }
-            const float gam = __builtin_amdgcn_exp2f(lg);
-#pragma unroll
-            for (int kk = 0; kk < NK; ++kk) {
-                // operand element j holds key 32 (KK0 + kk) + 4g + j (j < 4), + 16 (j >= 4);
-                // one power per run of four keys, the earlier keys by multiplying by gamma
-                float w[8];
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const int key3 = 32 * (KK0 + kk) + 16 * hh + 4 * g + 3 - kbase;
-                    float wk = __builtin_amdgcn_exp2f((float)(n_rows - 1 - key3) * lg);
-#pragma unroll
-                    for (int j = 3; j >= 0; --j) {
-                        w[4 * hh + j] = key3 - 3 + j < n_rows ? wk : 0.f;
-                        wk *= gam;
-                    }
-                }
-#pragma unroll
-                for (int c = 0; c < NCB; ++c) vb[c][kk] = c < CPW ? scale_bf16x8(vb[c][kk], w) : pack_bf16x8(w);
             }
+#pragma unroll
+            for (int c = 0; c < NCB; ++c) vb[c][kk] = c < CPW ? scale_bf16x8(vb[c][kk], w) : pack_bf16x8(w);
         }
+    };
+    // P += K^T V over key steps KK0 .. KK0 + NK - 1 with the given V operands,
+    // K column operands one (ks, hf) step ahead
+    auto update_v = [&](const StageT& s, auto kk0c, const auto& vb) __attribute__((always_inline)) {
+        constexpr int KK0 = decltype(kk0c)::value;
+        constexpr int NK = sizeof(vb[0]) / sizeof(vb[0][0]);
         bf16x8 kc[2][NK];
         auto load_kc = [&](int ks, int hf, bf16x8 (&k_)[NK]) __attribute__((always_inline)) {
 #pragma unroll
@@ -626,6 +690,29 @@ void chunked_fwd_pipe(FwdParams p) {
 #pragma unroll
                 for (int c = 0; c < NCB; ++c) P[c][ks][hf] = mfma_bf16(kc[t & 1][kk], vb[c][kk], P[c][ks][hf]);
         }
+    };
+
+    // state update with the key steps KK0 .. KK0 + NK - 1 of the tile.  With
+    // the direct decay the chunk (keys from row kbase, n_rows of them) enters as
+    // P <- gamma^n P + sum_j gamma^(n-1-j) k_j^T v_j: the state is scaled and
+    // each key's V operand (the ones of the denominator block too) weighted.
+    auto update = [&](const StageT& s, auto kk0c, auto nkc, int n_rows, int kbase) __attribute__((always_inline)) {
+        constexpr int NK = decltype(nkc)::value;
+        bf16x8 vb[NCB][NK];
+        if constexpr (DIR) {
+            load_v_weighted(s, kk0c, nkc, n_rows, kbase, 0.f, vb);
+            const float gn = __builtin_amdgcn_exp2f((float)n_rows * lg);
+#pragma unroll
+            for (int c = 0; c < NCB; ++c)
+#pragma unroll
+                for (int ks = 0; ks < NKA; ++ks) {
+                    P[c][ks][0] *= gn;
+                    P[c][ks][1] *= gn;
+                }
+        } else {
+            load_v(s, kk0c, nkc, vb);
+        }
+        update_v(s, kk0c, vb);
     };
 
     auto pack_state = [&](bf16x8 (&pst)[NCB][NKA]) __attribute__((always_inline)) {
@@ -654,7 +741,10 @@ void chunked_fwd_pipe(FwdParams p) {
 
     // output rows of query blocks Q0 + qb into this wave's V columns (after its
     // last V read of the tile, in program order)
-    auto write_out = [&](StageT& s, auto q0c, f32x4 (&O)[NCB][4]) __attribute__((always_inline)) {
+    // (factored decay without the normaliser: times the row factor rf[qb], which
+    // then holds the output scale too)
+    auto write_out = [&](StageT& s, auto q0c, f32x4 (&O)[NCB][4], const float (&rf)[4])
+        __attribute__((always_inline)) {
         constexpr int Q0 = decltype(q0c)::value;
         // the denominator block holds the row's denominator in every column:
         // one reciprocal (v_rcp_f32, about 1 ulp) per row and lane
@@ -667,7 +757,10 @@ void chunked_fwd_pipe(FwdParams p) {
             for (int qb = 0; qb < 4; ++qb) {
                 f32x4 o = O[c][qb];
                 if constexpr (NORM) o *= rden[qb];
-                if (SCALED) o *= osc;
+                if constexpr (FAC && !NORM)
+                    o *= rf[qb];
+                else if (SCALED)
+                    o *= osc;
                 *reinterpret_cast<uint2*>(reinterpret_cast<char*>(s.v) +
                                           tile_off<VSEG>((Q0 + qb) * 16 + l16, colw + c * 16 + 4 * g)) =
                     make_uint2(pack2_bf16(o[0], o[1]), pack2_bf16(o[2], o[3]));
@@ -681,8 +774,183 @@ void chunked_fwd_pipe(FwdParams p) {
             for (int qb = 0; qb < 4; ++qb) O[c][qb] = zero4;
     };
 
+    // ---- factored decay: P = gamma^nr P' (nr rows since the last rescale,
+    // wave-uniform); V arrives weighted from the copy waves
+    int nr = 0;
+    const float one4[4] = {1.f, 1.f, 1.f, 1.f};
+    // row factors rho = gamma^(row + 1 + nrc) (times the output scale) of query
+    // blocks whose chunk starts at the state gamma^nrc P'
+    auto row_factors = [&](const float (&f)[4], int nrc, float (&rf)[4]) __attribute__((always_inline)) {
+        const float sg = __builtin_amdgcn_exp2f((float)nrc * lg) * (SCALED ? osc : 1.f);
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb) rf[qb] = f[qb] * sg;
+    };
+    // V operands of key steps KK0 .. KK0 + NK - 1 (weighted in LDS); with the
+    // normaliser, the denominator block's operand holds the weights c_j =
+    // gamma^(-(1 + j + nrc)) of keys j (from tile row kbase), one power per run
+    // of four keys, the earlier keys by multiplying by gamma
+    auto load_v_fac = [&](const StageT& s, auto kk0c, auto nkc, int kbase, int nrc,
+                          bf16x8 (&vb)[NCB][decltype(nkc)::value]) __attribute__((always_inline)) {
+        constexpr int KK0 = decltype(kk0c)::value, NK = decltype(nkc)::value;
+        load_v(s, kk0c, nkc, vb);
+        if constexpr (NORM) {
+            const float gam = __builtin_amdgcn_exp2f(lg);
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk) {
+                float w[8];
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int key3 = 32 * (KK0 + kk) + 16 * hh + 4 * g + 3 - kbase;
+                    float wk = __builtin_amdgcn_exp2f(-(float)(1 + key3 + nrc) * lg);
+#pragma unroll
+                    for (int j = 3; j >= 0; --j) {
+                        w[4 * hh + j] = wk;
+                        wk *= gam;
+                    }
+                }
+                vb[CPW][kk] = pack_bf16x8(w);
+            }
+        }
+    };
+    auto compute_fac = [&](StageT& s, int valid) __attribute__((always_inline)) {
+        if (nr > nr_max) {
+            const float f = __builtin_amdgcn_exp2f((float)nr * lg);
+#pragma unroll
+            for (int c = 0; c < NCB; ++c)
+#pragma unroll
+                for (int ks = 0; ks < NKA; ++ks) {
+                    P[c][ks][0] *= f;
+                    P[c][ks][1] *= f;
+                }
+            nr = 0;
+        }
+        bf16x8 pst[NCB][NKA];
+        pack_state(pst);
+        if constexpr (CH == 64) {
+            f32x4 S[10], O[NCB][4];
+            zero_o(O);
+            tri_window(s, ic<0>{}, ic<0>{}, ic<0>{}, ic<15>{}, S, O, pst);
+            bf16x8 vb[NCB][2];
+            load_v_fac(s, ic<0>{}, ic<2>{}, 0, nr, vb);
+            tri_intra_v(vb, S, O);
+            update_v(s, ic<0>{}, vb);
+            float rf[4];
+            if constexpr (!NORM) row_factors(fin, nr, rf);
+            write_out(s, ic<0>{}, O, rf);
+            nr += valid;
+        } else if constexpr (CH == 32) {
+            // chunk A (rows 0..31), then chunk B (rows 32..63) from A's state
+            const int na = valid < 32 ? valid : 32, nb = valid > 32 ? valid - 32 : 0;
+            f32x4 S[10], O[NCB][4];
+            zero_o(O);
+            tri_window(s, ic<0>{}, ic<0>{}, ic<1>{}, ic<3>{}, S, O, pst);
+            bf16x8 va[NCB][1];
+            load_v_fac(s, ic<0>{}, ic<1>{}, 0, nr, va);
+            update_v(s, ic<0>{}, va);
+            {
+                const bf16x8 s0 = pack_acc_bf16(S[0], zero4);
+                const bf16x8 s1 = pack_acc_bf16(S[1], S[2]);
+#pragma unroll
+                for (int c = 0; c < NCB; ++c) {
+                    O[c][0] = mfma_bf16(va[c][0], s0, O[c][0]);
+                    O[c][1] = mfma_bf16(va[c][0], s1, O[c][1]);
+                }
+            }
+            pack_state(pst);
+            inter2(s, ic<0>{}, ic<2>{}, O, pst);
+            bf16x8 vb[NCB][1];
+            load_v_fac(s, ic<1>{}, ic<1>{}, 32, nr + na, vb);
+            update_v(s, ic<1>{}, vb);
+            {
+                const bf16x8 s2 = pack_acc_bf16(S[5], zero4);
+                const bf16x8 s3 = pack_acc_bf16(S[8], S[9]);
+#pragma unroll
+                for (int c = 0; c < NCB; ++c) {
+                    O[c][2] = mfma_bf16(vb[c][0], s2, O[c][2]);
+                    O[c][3] = mfma_bf16(vb[c][0], s3, O[c][3]);
+                }
+            }
+            float rf[4];
+            if constexpr (!NORM) {
+                float ra[4], rb[4];
+                row_factors(fin, nr, ra);
+                row_factors(fin, nr + na, rb);
+                rf[0] = ra[0];
+                rf[1] = ra[1];
+                rf[2] = rb[0];
+                rf[3] = rb[1];
+            }
+            write_out(s, ic<0>{}, O, rf);
+            nr += na + nb;
+        } else {
+            // query rows 0..63: own keys; rows 64..127: keys 0..63 (whole block)
+            // and own keys; the V operands of keys 0..63 serve the intra product
+            // of rows 0..63, the cross block and their update, then keys 64..127
+            f32x4 Ob[NCB][4];
+            zero_o(Ob);
+            {
+                f32x4 S[10], Oa[NCB][4];
+                zero_o(Oa);
+                tri_window(s, ic<0>{}, ic<0>{}, ic<0>{}, ic<15>{}, S, Oa, pst);
+                bf16x8 vb[NCB][2];
+                load_v_fac(s, ic<0>{}, ic<2>{}, 0, nr, vb);
+                tri_intra_v(vb, S, Oa);
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    f32x4 X[4][2];
+#pragma unroll
+                    for (int qb = 0; qb < 4; ++qb) X[qb][0] = X[qb][1] = zero4;
+                    bf16x8 qa[2][4], ka[2][2];
+                    auto load = [&](int ks, bf16x8 (&q_)[4], bf16x8 (&k_)[2]) __attribute__((always_inline)) {
+#pragma unroll
+                        for (int b = 0; b < 4; ++b) q_[b] = row_op<QSEG>(s.q, (4 + b) * 16 + l16, ks * 32, g);
+#pragma unroll
+                        for (int b = 0; b < 2; ++b) k_[b] = row_op<QSEG>(s.k, (2 * kk + b) * 16 + l16, ks * 32, g);
+                    };
+                    load(0, qa[0], ka[0]);
+#pragma unroll
+                    for (int ks = 0; ks < NKA; ++ks) {
+                        if (ks + 1 < NKA) load(ks + 1, qa[(ks + 1) & 1], ka[(ks + 1) & 1]);
+                        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                        for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+                            for (int b = 0; b < 2; ++b)
+                                X[qb][b] = mfma_bf16(ka[ks & 1][b], qa[ks & 1][qb], X[qb][b]);
+                    }
+#pragma unroll
+                    for (int qb = 0; qb < 4; ++qb) {
+                        const bf16x8 xb = pack_acc_bf16(X[qb][0], X[qb][1]);
+#pragma unroll
+                        for (int c = 0; c < NCB; ++c) Ob[c][qb] = mfma_bf16(vb[c][kk], xb, Ob[c][qb]);
+                    }
+                }
+                update_v(s, ic<0>{}, vb);
+                float rf[4];
+                if constexpr (!NORM) row_factors(fin, nr, rf);
+                write_out(s, ic<0>{}, Oa, rf);  // V rows 0..63 are no longer read
+            }
+            {
+                f32x4 S[10];
+                tri_window(s, ic<4>{}, ic<4>{}, ic<0>{}, ic<15>{}, S, Ob, pst);
+                bf16x8 vb[NCB][2];
+                load_v_fac(s, ic<2>{}, ic<2>{}, 0, nr, vb);
+                tri_intra_v(vb, S, Ob);
+                update_v(s, ic<2>{}, vb);
+                float rf[4];
+                if constexpr (!NORM) row_factors(fin64, nr, rf);
+                write_out(s, ic<4>{}, Ob, rf);
+            }
+            nr += valid;
+        }
+    };
+
     // ---- one tile's products
     auto compute = [&](StageT& s, int valid) __attribute__((always_inline)) {
+        if constexpr (FAC) {
+            compute_fac(s, valid);
+            return;
+        }
         bf16x8 pst[NCB][NKA];
         pack_state(pst);
         if constexpr (CH == 64) {
@@ -692,7 +960,7 @@ void chunked_fwd_pipe(FwdParams p) {
             decay_inter(O, fin, 0, 4, 0);
             tri_intra(s, ic<0>{}, S, O);
             update(s, ic<0>{}, ic<2>{}, valid, 0);
-            write_out(s, ic<0>{}, O);
+            write_out(s, ic<0>{}, O, one4);
         } else if constexpr (CH == 32) {
             // two chunks per tile: rows 0..31 (A) and 32..63 (B).  Scores only
             // inside each chunk; A's inter product reads the state before A,
@@ -725,7 +993,7 @@ void chunked_fwd_pipe(FwdParams p) {
                 O[c][2] = mfma_bf16(vb[c][1], s2, O[c][2]);
                 O[c][3] = mfma_bf16(vb[c][1], s3, O[c][3]);
             }
-            write_out(s, ic<0>{}, O);
+            write_out(s, ic<0>{}, O, one4);
         } else {
             // one chunk of 128 rows per tile: query rows 0..63 against their own
             // keys; query rows 64..127 against their own keys and the full block
@@ -788,8 +1056,8 @@ void chunked_fwd_pipe(FwdParams p) {
                 }
             }
             update(s, ic<0>{}, ic<4>{}, valid, 0);
-            write_out(s, ic<0>{}, Oa);
-            write_out(s, ic<4>{}, Ob);
+            write_out(s, ic<0>{}, Oa, one4);
+            write_out(s, ic<4>{}, Ob, one4);
         }
     };
 
@@ -815,9 +1083,10 @@ void chunked_fwd_pipe(FwdParams p) {
     }
     __syncthreads();  // matches the copy waves' final barrier
 
+    const float ss_fin = p.state_scale * (FAC ? __builtin_amdgcn_exp2f((float)nr * lg) : 1.f);
     if (t_end == n_tiles && p.S_final != nullptr) {
         float* Sf = p.S_final + (bh * DK) * (int64_t)dv + col0 + colw + l16;
-        const float ss = p.state_scale;
+        const float ss = ss_fin;
 #pragma unroll
         for (int c = 0; c < CPW; ++c)
 #pragma unroll
@@ -831,7 +1100,7 @@ void chunked_fwd_pipe(FwdParams p) {
     if constexpr (NORM) {
         if (t_end == n_tiles && p.z_final != nullptr && jt == 0 && h == 0 && l16 == 0) {
             float* zf = p.z_final + bh * DK;
-            const float ss = p.state_scale;
+            const float ss = ss_fin;
 #pragma unroll
             for (int ks = 0; ks < NKA; ++ks)
 #pragma unroll
@@ -844,7 +1113,7 @@ void chunked_fwd_pipe(FwdParams p) {
 
 // Output scaling exists for the scaled identity map without the normaliser
 // only (normalised outputs are scale-free; pre-mapped inputs carry the scale).
-template <int DK, int DVT, int CH, bool NORM, bool PHI, bool DECAY>
+template <int DK, int DVT, int CH, bool NORM, bool PHI, int DECAY>
 hipError_t launch_fwd_pipe(const FwdParams& p, int64_t grid, hipStream_t s) {
     const dim3 block(4 * WAVE);
     if (p.out_scale != 1.0f) {

@@ -6,6 +6,9 @@
 namespace la {
 
 hipError_t fwd_pipe_decay_bf16(const FwdParams& p, int DK, int DVT, int C, int64_t grid, hipStream_t s);
+// the decayed recurrence in its factored form (la_pipe_decay_fac.hip); false
+// when the case has no such instantiation
+bool fwd_pipe_decay_fac_bf16(const FwdParams& p, int DK, int C, int64_t grid, hipStream_t s, hipError_t* e);
 // the cases with the most live registers (la_pipe_wide.hip)
 hipError_t fwd_pipe_wide_bf16(const FwdParams& p, int DK, int C, bool decay, int64_t grid, hipStream_t s);
 
@@ -19,7 +22,7 @@ namespace pipe {
 
 // normaliser from p.normalize; elu+1 applied in the kernel from p.fmap;
 // tiles of 64 value columns, 32 at feature width 256 (LDS and registers)
-template <int DK, int C, bool DECAY>
+template <int DK, int C, int DECAY>
 hipError_t by_flags(const FwdParams& p, int64_t grid, hipStream_t s) {
     constexpr int DVT = DK == 256 ? 32 : 64;
     const bool norm = p.normalize != 0;

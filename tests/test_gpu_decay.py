@@ -36,11 +36,19 @@ def _oracle(q, k, v, C, normalize, fmap, gamma, W=None, in_scale=1.0):
     (128, 128, 128, 900, 0, False, "identity", 0.995), (128, 64, 64, 1300, 2, True, "elu1", 0.9),
     (64, 256, 64, 300, 0, False, "identity", 0.8), (64, 128, 128, 200, 0, False, "identity", 0.5),
     (64, 64, 64, 300, 0, False, "identity", 1.0), (128, 128, 64, 333, 3, True, "elu1", 0.98),
-    (32, 256, 32, 200, 2, True, "elu1", 0.93)])
+    (32, 256, 32, 200, 2, True, "elu1", 0.93),
+    # factored form, the state rescaled at almost every tile; at the edge of
+    # its range (TT |log2 gamma| close to 48) for every chunk size
+    (64, 128, 128, 700, 0, False, "identity", 0.7), (64, 64, 64, 900, 0, True, "elu1", 0.6),
+    (32, 64, 64, 600, 0, False, "identity", 0.6), (128, 64, 64, 900, 0, True, "elu1", 0.78),
+    # direct form past that range
+    (128, 64, 64, 700, 0, False, "identity", 0.7), (32, 64, 64, 500, 0, True, "elu1", 0.3)])
 def test_decay_forward(C, dk, dv, L, group, norm, fmap, gamma):
     """The forward with a decay: chunks of 32, 64 and 128, several groups (the
     prefixes from decayed phase-1 states and the decayed scan), ragged tails,
-    with and without the normaliser, identity and elu+1; gamma = 1 is plain."""
+    with and without the normaliser, identity and elu+1; gamma = 1 is plain.
+    The streaming kernel's two forms of the decay (direct, and factored where
+    rows of the tile times |log2 gamma| stay within 48) are both covered."""
     q, k, v = _case(51, 2, L, dk, dv)
     log(f"decay forward C={C} dk={dk} dv={dv} L={L} group={group} norm={norm} fmap={fmap} gamma={gamma}")
     o, S, z = la.chunked_forward(dev_input(q), dev_input(k), dev_input(v), C, normalize=norm, fmap=fmap,
