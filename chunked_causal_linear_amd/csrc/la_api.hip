@@ -220,7 +220,7 @@ la_status make_plan(Plan& P, la_dtype in_dt, int64_t BH, int64_t L, int64_t d_in
     // register-staged phase-1 kernel runs several workgroups per CU: pieces
     // double while fewer than 1024 run.  The streaming one (bf16 at feature
     // width 64, 128 or 256, value columns a multiple of 64, pieces of whole
-    // 64-row tiles, no decay, K plain or pre-mapped) holds a CU alone: pieces
+    // 64-row tiles, K plain or pre-mapped) holds a CU alone: pieces
     // double while the workgroups still fit the CUs in one round.  With elu+1
     // applied in phase 1 it runs two workgroups per CU and its pieces are
     // planned like the register-staged kernel's (measured best).
@@ -230,7 +230,7 @@ la_status make_plan(Plan& P, la_dtype in_dt, int64_t BH, int64_t L, int64_t d_in
         const int64_t n_dvt1 = d_v / kernel_dvt(d_v);
         // a piece reads at least eight times the state it writes
         const int64_t min_rows = std::max<int64_t>(512, cdiv(16 * P.dk * d_v, P.dk + d_v));
-        const bool stream1 = !P.i8 && !decay && f != LA_FMAP_ELU1 && (P.dk == 64 || P.dk == 128 || P.dk == 256) &&
+        const bool stream1 = !P.i8 && f != LA_FMAP_ELU1 && (P.dk == 64 || P.dk == 128 || P.dk == 256) &&
                              d_v % 64 == 0 && (P.G * P.C) % 64 == 0;
         auto more = [&]() {
             const int64_t rows = P.G * P.C / (2 * P.sub);
@@ -422,7 +422,7 @@ static la_status chunk_states_impl(const void* k, const void* v, bool i8, int64_
     // streaming kernel (its own value tiling)
     const int dvt_pipe = 64;
     bool stream_ok = (d_k == 64 || d_k == 128 || d_k == 256) && d_v % dvt_pipe == 0 && Cs % 64 == 0 &&
-                           Cs >= 256 && lg == 0.0f && (fmap == 0 || fmap == 1);
+                           Cs >= 256 && (fmap == 0 || fmap == 1) && !(lg != 0.0f && k_lo != nullptr);
     // elu+1 mapped here at feature width 128 or 256 (one streaming workgroup
     // per CU): only when the workgroups fit the CUs in one round; with more,
     // the register-staged kernel at several workgroups per CU hides the

@@ -130,9 +130,12 @@ __device__ __forceinline__ uint4 elu1_bf16x8(const uint4& u, float in_scale) {
 // elu+1 of in_scale * x for 8 bf16 values, as a bf16 pair (hi, lo) with
 // hi = bf16(phi) and lo = bf16(phi - hi): hi + lo carries phi to about 2^-17
 // relative, which keeps long state sums free of the bf16 rounding of phi.
-__device__ __forceinline__ void elu1_split_bf16x8(const uint4& u, float in_scale, uint4& hi, uint4& lo) {
+__device__ __forceinline__ void elu1_split_bf16x8(const uint4& u, float in_scale, uint4& hi, uint4& lo,
+                                                  float mul = 1.0f) {
     float f[8];
     elu1_f32x8(u, elu1_scale(in_scale), f);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f[j] *= mul;
     uint32_t h[4], l[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {

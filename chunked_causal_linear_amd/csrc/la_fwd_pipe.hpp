@@ -644,9 +644,10 @@ void chunked_fwd_pipe(FwdParams p) {
     };
     // the same operands with key j (local to a chunk of n_rows keys starting at
     // tile row kbase) weighted by exp2((n_rows - 1 - j) lg - shift), 0 for
-    // j >= n_rows: one power per run of four keys, the earlier keys by
-    // multiplying by gamma.  Operand element e holds key 32 (KK0 + kk) + 4g + e
-    // (e < 4), + 16 (e >= 4).
+    // j >= n_rows: one power per run of four keys, taken at the run's last key
+    // before n_rows (so that no power exceeds the first key's), the earlier
+    // keys by multiplying by gamma.  Operand element e holds key
+    // 32 (KK0 + kk) + 4g + e (e < 4), + 16 (e >= 4).
     auto load_v_weighted = [&](const StageT& s, auto kk0c, auto nkc, int n_rows, int kbase, float shift,
                                bf16x8 (&vb)[NCB][decltype(nkc)::value]) __attribute__((always_inline)) {
         constexpr int KK0 = decltype(kk0c)::value, NK = decltype(nkc)::value;
@@ -658,11 +659,13 @@ void chunked_fwd_pipe(FwdParams p) {
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
                 const int key3 = 32 * (KK0 + kk) + 16 * hh + 4 * g + 3 - kbase;
-                float wk = __builtin_amdgcn_exp2f((float)(n_rows - 1 - key3) * lg - shift);
+                const int top = key3 < n_rows - 1 ? key3 : n_rows - 1;
+                float wk = __builtin_amdgcn_exp2f((float)(n_rows - 1 - top) * lg - shift);
 #pragma unroll
                 for (int j = 3; j >= 0; --j) {
-                    w[4 * hh + j] = key3 - 3 + j < n_rows ? wk : 0.f;
-                    wk *= gam;
+                    const bool live = key3 - 3 + j < n_rows;
+                    w[4 * hh + j] = live ? wk : 0.f;
+                    wk = live ? wk * gam : wk;
                 }
             }
 #pragma unroll

@@ -23,6 +23,15 @@
 //   KIND_LO     pre-mapped phi(K) with its residual in a second input
 //               (FAVOR+), both copied and both multiplied.
 // K rows past the end of the sequence are set to zero before the products.
+//
+// Decayed recurrence (DECAY; S_t = gamma S_{t-1} + k_t^T v_t): the state a run
+// leaves at its end weighs row r by gamma^(e-1-r), e the run's end, and the
+// scan decays the prefix by each run's row count.  With elu+1 the weight
+// multiplies phi(k) in fp32 before the hi/lo split (the sum keeps its
+// precision, V stays exact); with plain K the compute waves weight each V
+// operand and the ones of z (fp32 multiply, rounded back to bf16, one rounding
+// as with the weight on K).  Pre-mapped K with its residual has no decayed
+// form here.
 #pragma once
 
 #include "la_fwd_pipe.hpp"
@@ -66,7 +75,7 @@ __device__ __forceinline__ void wait_tiles(int after) {
 template <int DK, int KIND>
 constexpr int states_pipe_per_cu() { return KIND == KIND_ELU && DK == 64 ? 2 : 1; }
 
-template <int DK, int DVT, int KIND, bool Z>
+template <int DK, int DVT, int KIND, bool Z, bool DECAY>
 __global__ __launch_bounds__(4 * WAVE) __attribute__((amdgpu_waves_per_eu(states_pipe_per_cu<DK, KIND>(),
                                                                            states_pipe_per_cu<DK, KIND>())))
 void chunk_states_pipe(StatesParams p) {
@@ -132,32 +141,38 @@ void chunk_states_pipe(StatesParams p) {
     // flight) and FB more after B'(t), while the products of tile t run;
     // compute wave h maps the last FC between B(t) and B'(t).
     constexpr int FC = NCK / 4, FA = NCK / 4, FB = NCK - FC - FA;
-    auto phi_blocks = [&](StageT& s, int valid, auto j0_, auto count) __attribute__((always_inline)) {
+    // (decay: row r of the tile weighs gamma^(n - 1 - r), n its rows before the
+    // run's end)
+    auto phi_blocks = [&](StageT& s, int valid, int n, auto j0_, auto count) __attribute__((always_inline)) {
         constexpr int J0 = decltype(j0_)::value, N = decltype(count)::value;
 #pragma unroll
         for (int i = 0; i < N; ++i) {
             const int slot = (h * NCK + J0 + i) * WAVE + lane;
             const uint4 x = *reinterpret_cast<const uint4*>(s.k + slot * 8);
             uint4 hi, lo;
-            elu1_split_bf16x8(x, p.in_scale, hi, lo);
+            const float wr = DECAY ? __builtin_amdgcn_exp2f((float)(n - 1 - slot / QSEG) * p.log2_gamma) : 1.0f;
+            elu1_split_bf16x8(x, p.in_scale, hi, lo, wr);
             const bool live = slot / QSEG < valid;  // rows past the end become zero
             *reinterpret_cast<uint4*>(s.k + slot * 8) = live ? hi : make_uint4(0, 0, 0, 0);
             *reinterpret_cast<uint4*>(s.klo + slot * 8) = live ? lo : make_uint4(0, 0, 0, 0);
         }
     };
-    auto phi_copy_a = [&](StageT& s, int valid) __attribute__((always_inline)) {
-        phi_blocks(s, valid, ic<0>{}, ic<FA>{});
+    // rows of tile t before the run's end
+    auto rows_to_end = [&](int64_t t) -> int { return (int)(r_end - t * TT); };
+    auto phi_copy_a = [&](StageT& s, int64_t t) __attribute__((always_inline)) {
+        phi_blocks(s, valid_rows(t), rows_to_end(t), ic<0>{}, ic<FA>{});
     };
-    auto phi_copy_b = [&](StageT& s, int valid) __attribute__((always_inline)) {
-        phi_blocks(s, valid, ic<FA>{}, ic<FB>{});
+    auto phi_copy_b = [&](StageT& s, int64_t t) __attribute__((always_inline)) {
+        phi_blocks(s, valid_rows(t), rows_to_end(t), ic<FA>{}, ic<FB>{});
     };
-    auto phi_compute = [&](StageT& s, int valid) __attribute__((always_inline)) {
-        phi_blocks(s, valid, ic<FA + FB>{}, ic<FC>{});
+    auto phi_compute = [&](StageT& s, int64_t t) __attribute__((always_inline)) {
+        phi_blocks(s, valid_rows(t), rows_to_end(t), ic<FA + FB>{}, ic<FC>{});
     };
-    // after B(t), the landed tile made ready for the products
-    auto prepare = [&](StageT& s, int valid) __attribute__((always_inline)) {
+    // after B(t), the landed tile t made ready for the products
+    auto prepare = [&](StageT& s, int64_t t) __attribute__((always_inline)) {
+        const int valid = valid_rows(t);
         if constexpr (KIND == KIND_ELU) {
-            phi_compute(s, valid);
+            phi_compute(s, t);
             __syncthreads();  // B'(t)
         } else if (valid < TT) {
             zero_tail(s, valid);
@@ -208,8 +223,8 @@ void chunk_states_pipe(StatesParams p) {
             if (t_begin + s0 < t_end) issue(t_begin + s0, st[s0]);
         land(after_of(t_begin));
         if constexpr (KIND == KIND_ELU) {
-            phi_copy_a(st[0], valid_rows(t_begin));
-            phi_copy_b(st[0], valid_rows(t_begin));
+            phi_copy_a(st[0], t_begin);
+            phi_copy_b(st[0], t_begin);
         }
 
         int si = 0;  // stage of tile t
@@ -221,12 +236,12 @@ void chunk_states_pipe(StatesParams p) {
             if constexpr (KIND == KIND_ELU) {
                 if (t + 1 < t_end) {
                     land(after_of(t + 1));
-                    phi_copy_a(st[sn], valid_rows(t + 1));
+                    phi_copy_a(st[sn], t + 1);
                 }
                 __syncthreads();  // B'(t): tile t is mapped
-                if (t + 1 < t_end) phi_copy_b(st[sn], valid_rows(t + 1));
+                if (t + 1 < t_end) phi_copy_b(st[sn], t + 1);
             } else {
-                prepare(st[si], valid_rows(t));
+                prepare(st[si], t);
                 if (t + 1 < t_end) land(after_of(t + 1));
             }
             si = sn;
@@ -267,7 +282,7 @@ void chunk_states_pipe(StatesParams p) {
                 for (int c = 0; c < NCB; ++c) P[c][ks][hf] = mfma_bf16(kc[t & 1][kk], vb[c][kk], P[c][ks][hf]);
         }
     };
-    auto compute = [&](const StageT& s) __attribute__((always_inline)) {
+    auto compute = [&](const StageT& s, int64_t t) __attribute__((always_inline)) {
         constexpr int NK = TT / 32;
         bf16x8 vb[NCB][NK];
 #pragma unroll
@@ -275,6 +290,32 @@ void chunk_states_pipe(StatesParams p) {
 #pragma unroll
             for (int kk = 0; kk < NK; ++kk)
                 vb[c][kk] = c < CPW ? col_op<VSEG>(s.v, kk * 32, colw + c * 16 + c4, lane) : ones;
+        if constexpr (DECAY && KIND == KIND_PLAIN) {
+            // operand element j holds row t TT + 32 kk + 4g + j (j < 4), + 16
+            // (j >= 4): one power per run of four rows, taken at the run's last
+            // row before the end e (so that it is at most 1), the earlier rows
+            // by multiplying by gamma; rows from e on weigh 0
+            const float lg = p.log2_gamma, gam = __builtin_amdgcn_exp2f(lg);
+            const int n = (int)(r_end - t * TT);  // rows of the tile before e
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk) {
+                float w[8];
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int r3 = 32 * kk + 16 * hh + 4 * g + 3;
+                    const int top = r3 < n - 1 ? r3 : n - 1;
+                    float wk = __builtin_amdgcn_exp2f((float)(n - 1 - top) * lg);
+#pragma unroll
+                    for (int j = 3; j >= 0; --j) {
+                        const bool live = r3 - 3 + j < n;
+                        w[4 * hh + j] = live ? wk : 0.f;
+                        wk = live ? wk * gam : wk;
+                    }
+                }
+#pragma unroll
+                for (int c = 0; c < NCB; ++c) vb[c][kk] = c < CPW ? scale_bf16x8(vb[c][kk], w) : pack_bf16x8(w);
+            }
+        }
         update(s.k, vb);
         if constexpr (LO) update(s.klo, vb);
     };
@@ -282,8 +323,8 @@ void chunk_states_pipe(StatesParams p) {
     auto step = [&](auto sidx, int64_t t) __attribute__((always_inline)) {
         constexpr int SI = decltype(sidx)::value;
         __syncthreads();  // B(t)
-        prepare(st[SI], valid_rows(t));
-        compute(st[SI]);
+        prepare(st[SI], t);
+        compute(st[SI], t);
     };
     for (int64_t t = t_begin; t < t_end; t += NSTAGE) {
         step(ic<0>{}, t);
@@ -324,5 +365,35 @@ void chunk_states_pipe(StatesParams p) {
         }
     }
 }
+
+// launch over the compile-time cases of one feature width (z from p.want_z)
+template <int DK, bool DECAY>
+hipError_t states_pipe_dk(const StatesParams& p, int kind, int64_t grid, hipStream_t s) {
+    constexpr int DVT = 64;
+    const dim3 g((unsigned)grid), b(4 * WAVE);
+    const bool z = p.want_z != 0;
+    switch (kind * 2 + (z ? 1 : 0)) {
+        case 0: hipLaunchKernelGGL((chunk_states_pipe<DK, DVT, KIND_PLAIN, false, DECAY>), g, b, 0, s, p); break;
+        case 1: hipLaunchKernelGGL((chunk_states_pipe<DK, DVT, KIND_PLAIN, true, DECAY>), g, b, 0, s, p); break;
+        case 2: hipLaunchKernelGGL((chunk_states_pipe<DK, DVT, KIND_ELU, false, DECAY>), g, b, 0, s, p); break;
+        case 3: hipLaunchKernelGGL((chunk_states_pipe<DK, DVT, KIND_ELU, true, DECAY>), g, b, 0, s, p); break;
+        case 4:
+        case 5:
+            if constexpr (DECAY) {
+                return hipErrorInvalidValue;  // no decayed form with a residual
+            } else {
+                if (z)
+                    hipLaunchKernelGGL((chunk_states_pipe<DK, DVT, KIND_LO, true, false>), g, b, 0, s, p);
+                else
+                    hipLaunchKernelGGL((chunk_states_pipe<DK, DVT, KIND_LO, false, false>), g, b, 0, s, p);
+            }
+            break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+// the decayed instantiations (la_states_pipe_decay.hip)
+hipError_t states_pipe_decay_bf16(const StatesParams& p, int DK, int kind, int64_t grid, hipStream_t s);
 
 }  // namespace la

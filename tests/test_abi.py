@@ -108,9 +108,11 @@ def test_workspace_sizes_and_errors():
     n = ws(b.LA_BF16, 32, 65536, 64, 64, 128, 1, 1, 1, 0, 1.0, 0)
     assert lib.la_chunked_forward_group(b.LA_BF16, 32, 65536, 64, 64, 128, 1, 1, 1, 0, 0) == 64
     assert n == 32 * 8 * 4 * 64 * 64 * 4 + 32 * 8 * 4 * 64 * 4
-    # the identity map: the last group is never summed (seven groups x 8 pieces)
+    # the identity map: the last group is never summed, and the streaming phase
+    # 1 sums each of the other seven whole (32 x 7 workgroups fill the CUs), with
+    # or without the decay: one state slot per group
     n = ws(b.LA_BF16, 32, 65536, 64, 64, 128, 1, 1, 0, 0, 1.0, 0)
-    assert n == 32 * 8 * 8 * 64 * 64 * 4 + 32 * 8 * 8 * 64 * 4
+    assert n == 32 * 8 * 64 * 64 * 4 + 32 * 8 * 64 * 4
     # elu+1 at d_k = 128: no copies either
     n = ws(b.LA_BF16, 2, 1024, 128, 64, 64, 1, 1, 1, 0, 1.0, 4)
     assert n == 2 * groups * 128 * 64 * 4 + 2 * groups * 128 * 4

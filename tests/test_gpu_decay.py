@@ -137,3 +137,56 @@ def test_decay_decode_resume():
         ref = oracle.decay_state_first(qp, kp, v.exact[h], gamma, True)[0][L1:]
         assert_close(got[h], ref, what=f"decode head {h}")
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("dk,dv,L,C,gamma,want_z", [
+    (64, 64, 1000, 256, 0.99, True), (128, 128, 1300, 320, 0.9, True), (256, 64, 900, 512, 0.999, True),
+    (128, 64, 700, 256, 1e-20, True), (64, 128, 2000, 1024, 0.97, False)])
+def test_decay_stream_states(dk, dv, L, C, gamma, want_z):
+    """Decayed per-run states over runs of 256 rows or more (the streaming
+    phase 1: V operands and the ones of z weighted by gamma^(e-1-r)), ragged
+    last run, against the oracle's decayed chunk states; gamma = 1e-20 leaves
+    each run's last row alone."""
+    q, k, v = _case(56, 2, L, dk, dv)
+    log(f"decay stream states dk={dk} dv={dv} L={L} C={C} gamma={gamma} want_z={want_z}")
+    S, z = la.chunk_states(dev_input(k), dev_input(v), C, gamma=gamma, want_z=want_z)
+    for h in range(2):
+        Sn, zn, _ = oracle.decay_chunk_states(k.exact[h], v.exact[h], C, gamma)
+        assert_close(host(S[h]), Sn, what="states")
+        if want_z:
+            assert_close(host(z[h]), zn, what="column sums")
+
+
+@pytest.mark.parametrize("C,dk,dv,L,group,norm,fmap,gamma", [
+    (64, 64, 64, 2000, 8, True, "elu1", 0.995), (64, 128, 128, 1500, 4, False, "identity", 0.99),
+    (128, 64, 64, 3000, 4, True, "elu1", 0.999), (32, 128, 64, 1200, 8, True, "elu1", 0.98),
+    (64, 64, 64, 700, 4, False, "identity", 1e-20), (128, 64, 128, 631, 5, True, "elu1", 0.999)])
+def test_decay_forward_stream_phase1(C, dk, dv, L, group, norm, fmap, gamma):
+    """Decayed forwards whose groups span 256 rows or more, so that phase 1
+    runs on the streaming kernel (elu+1 mapped in it, the weight applied to
+    phi(k) in fp32 before its hi/lo split), with every final state; gamma =
+    1e-20 runs the direct form."""
+    q, k, v = _case(57, 2, L, dk, dv)
+    log(f"decay forward stream phase 1 C={C} dk={dk} L={L} group={group} norm={norm} gamma={gamma}")
+    o, S, z = la.chunked_forward(dev_input(q), dev_input(k), dev_input(v), C, normalize=norm, fmap=fmap,
+                                 return_state=True, group=group, gamma=gamma)
+    ref, refS, refz = _oracle(q.exact, k.exact, v.exact, C, norm, fmap, gamma)
+    assert_close(host(o), ref, what="o")
+    assert_close(host(S), refS, what="S")
+    if norm:
+        assert_close(host(z), refz, what="z")
+
+
+def test_decay_favor_stream_phase1():
+    """FAVOR+ with the decay in groups of 256 rows (pre-mapped phi(k) with its
+    residual: phase 1 on the register-staged kernel, which weights phi(k)
+    before it rounds)."""
+    q, k, v = _case(58, 2, 1100, 64, 64, scale=1.0 / 8)
+    Wb, W = wl.orthogonal_random_features(128, 64, [58, 1])
+    log("decay favor stream phase 1 m=128")
+    o, S, z = la.chunked_forward(dev_input(q), dev_input(k), dev_input(v), 64, normalize=True, fmap="favor",
+                                 W=dev_bf16(Wb), return_state=True, group=4, gamma=0.98)
+    ref, refS, refz = _oracle(q.exact, k.exact, v.exact, 64, True, "favor", 0.98, W)
+    assert_close(host(o), ref, what="o")
+    assert_close(host(S), refS, what="S")
+    assert_close(host(z), refz, what="z")
