@@ -42,7 +42,8 @@ def _oracle(q, k, v, C, normalize, fmap, gamma, W=None, in_scale=1.0):
     (64, 128, 128, 700, 0, False, "identity", 0.7), (64, 64, 64, 900, 0, True, "elu1", 0.6),
     (32, 64, 64, 600, 0, False, "identity", 0.6), (128, 64, 64, 900, 0, True, "elu1", 0.78),
     # direct form past that range
-    (128, 64, 64, 700, 0, False, "identity", 0.7), (32, 64, 64, 500, 0, True, "elu1", 0.3)])
+    (128, 64, 64, 700, 0, False, "identity", 0.7), (32, 64, 64, 500, 0, True, "elu1", 0.3),
+    (64, 256, 64, 300, 0, False, "identity", 0.3), (128, 128, 64, 500, 2, True, "elu1", 0.7)])
 def test_decay_forward(C, dk, dv, L, group, norm, fmap, gamma):
     """The forward with a decay: chunks of 32, 64 and 128, several groups (the
     prefixes from decayed phase-1 states and the decayed scan), ragged tails,
