@@ -6,7 +6,7 @@ no code with the HIP path (``chunked_causal_linear_amd``) and imports nothing
 from it.
 
 Everything here is the plain definition of what the method computes, written
-from two pages:
+from three pages:
 
 * "attention と線形の間" (sharin-2a1.pages.dev/parts/chunked.html), below
   called *the chunking page*: section ① (the two association orders and the
@@ -33,7 +33,10 @@ v as [L, d_v].  ``over_heads`` maps a form over a leading head axis.
 
 Parity status.  Every function below is pinned by tests under
 ``tests/test_oracle_*.py`` (closed forms, brute force, exhaustive tiny cases,
-cross-form identities, the chunking page's printed tables).  ``phi_favor`` is
+cross-form identities, the chunking page's printed tables); ``apply_phi`` and
+``forward`` at hand-computed points of phi(s x), against brute force on both
+causal ends and with the scale, and against softmax attention for FAVOR+ with
+the d^(-1/4) scale.  ``phi_favor`` is
 pinned by its closed form at hand-computed points and by the large-m
 convergence of phi(q).phi(k) to exp(q.k); the W it consumes is an input.
 """

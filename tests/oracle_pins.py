@@ -532,3 +532,113 @@ def check_loglinear_causality(o, seed: int = 62) -> None:
         v2[t] -= 2
         out = o.loglinear_chunked(q, k2, v2, lam, 4)
         assert np.array_equal(out[:t], base[:t]) and not np.array_equal(out[t:], base[t:]), t
+
+
+# ---------------------------------------------------------------------------
+# The forward's reference: phi of the scaled inputs, and its non-causal branch
+# ---------------------------------------------------------------------------
+def check_apply_phi_in_scale(o) -> None:
+    """apply_phi(x, f, W, s) is phi(s x): the scale multiplies the input before the
+    map (linear-attention page: the Performer implementation scales Q and K by
+    d^(-1/4) before FAVOR+).  Hand-computed points: elu+1 at s = -0.5 and s = 1/4
+    (s x = -1 -> e^-1, s x = 0.5 -> 1.5, ...), the identity at s = 3, FAVOR+ at
+    s = 1/2 with a hand-written W."""
+    x = np.array([2.0, -1.0, 0.5, 0.0, -4.0])
+    cases = {
+        -0.5: [math.exp(-1.0), 1.5, math.exp(-0.25), 1.0, 3.0],   # s x = -1, 0.5, -0.25, 0, 2
+        0.25: [1.5, math.exp(-0.25), 1.125, 1.0, math.exp(-1.0)],  # s x = 0.5, -0.25, 0.125, 0, -1
+    }
+    for s, want in cases.items():
+        assert np.allclose(o.apply_phi(x, "elu1", None, s), want, rtol=1e-15, atol=0), s
+    assert np.array_equal(o.apply_phi(x, "identity", None, 3.0), 3.0 * x)
+    W = np.array([[1.0, 0, 0], [0, 1.0, 0], [0, 0, 1.0], [1.0, -1.0, 2.0]])
+    xf = np.array([1.0, 2.0, -1.0])
+    # s x = [0.5, 1, -0.5]: |s x|^2 / 2 = 0.75; projections 0.5, 1, -0.5, -1.5; m = 4
+    want = np.array([math.exp(-0.25), math.exp(0.25), math.exp(-1.25), math.exp(-2.25)]) / 2.0
+    assert np.allclose(o.apply_phi(xf, "favor", W, 0.5), want, rtol=1e-15, atol=0)
+    assert np.allclose(o.apply_phi(xf[None, :], "favor", W, 0.5)[0], want, rtol=1e-15, atol=0)
+
+
+def check_forward_scaled_favor_is_softmax(o, seed: int = 46) -> None:
+    """forward(..., fmap="favor", in_scale=d^(-1/4)) with many orthogonal features
+    approaches softmax(q k^T / sqrt(d)) v, causal and not (the linear-attention
+    page's Performer: FAVOR+ of the pre-scaled inputs estimates exp(q.k/sqrt(d)),
+    so the normalised ratio estimates softmax attention).  Without the scale it
+    estimates softmax at scale 1 instead, which the same check tells apart."""
+    from workloads import orthogonal_random_features
+    rng = np.random.default_rng([seed, 47])
+    L, d = 8, 4
+    q, k = rng.standard_normal((L, d)) * 0.9, rng.standard_normal((L, d)) * 0.9
+    v = rng.standard_normal((L, 3))
+    _, W = orthogonal_random_features(65536, d, [seed, 48])
+    s4 = d ** -0.25
+    for causal in (False, True):
+        out = o.forward(q, k, v, 3, causal, True, "favor", W, s4)[0]
+        ref = o.softmax_attention(q, k, v, causal)
+        assert np.allclose(out, ref, rtol=0, atol=2e-2), (causal, np.abs(out - ref).max())
+        other = o.softmax_attention(q, k, v, causal, scale=1.0)
+        assert np.abs(other - ref).max() > 0.1  # the scale is visible at this tolerance
+
+
+def check_forward_noncausal(o, seed: int = 49) -> None:
+    """forward(causal=False) against exact brute force over all keys, with and
+    without the normaliser, for the identity (integers, exact) and elu+1 (bf16
+    values), and its final state = sum_t phi(k_t)^T v_t, z = sum_t phi(k_t)
+    (chunking page, section ①; linear-attention page, normalised output).  The
+    chunk size is ignored."""
+    rng = np.random.default_rng([seed, 50])
+    L, dk, dv = 7, 3, 2
+    q, k, v = _ints(rng, (L, dk)), _ints(rng, (L, dk)), _ints(rng, (L, dv))
+    for C in (1, 3, 7):
+        out, S, z = o.forward(q, k, v, C, False, False)
+        bf = np.array([[int(x) for x in row] for row in o.brute_force(q, k, v, causal=False)], dtype=np.int64)
+        assert np.array_equal(np.asarray(out), bf), C
+        S_def = sum(np.outer(k[t], v[t]) for t in range(L))
+        assert np.array_equal(S, S_def) and np.array_equal(z, k.sum(axis=0))
+    qf, kf, vf = _bf16(rng, (L, dk)), _bf16(rng, (L, dk)), _bf16(rng, (L, dv))
+    qp, kp = o.phi_elu1(qf), o.phi_elu1(kf)
+    for normalize in (False, True):
+        out, S, z = o.forward(qf, kf, vf, 2, False, normalize, "elu1")
+        exact = _frac_matrix(o.brute_force(qp, kp, vf, causal=False, normalize=normalize))
+        assert np.allclose(out, exact, rtol=1e-12, atol=1e-13), normalize
+        assert np.allclose(S, sum(np.outer(kp[t], vf[t]) for t in range(L)), rtol=1e-13, atol=1e-14)
+        assert np.allclose(z, kp.sum(axis=0), rtol=1e-13, atol=1e-14)
+    # the identity with a scale s: s q, s k, so the unnormalised output is s^2 times
+    out = o.forward(q, k, v, 3, False, False, "identity", None, 2.0)[0]
+    assert np.array_equal(out, 4.0 * np.asarray(o.forward(q, k, v, 3, False, False)[0], dtype=np.float64))
+    # with a scale: phi(s q), phi(s k) (s < 0 flips which branch of elu+1 applies)
+    out = o.forward(qf, kf, vf, 2, False, True, "elu1", None, -0.5)[0]
+    qs, ks = o.phi_elu1(-0.5 * qf), o.phi_elu1(-0.5 * kf)
+    exact = _frac_matrix(o.brute_force(qs, ks, vf, causal=False, normalize=True))
+    assert np.allclose(out, exact, rtol=1e-12, atol=1e-13)
+
+
+def check_forward_causal_scaled(o, seed: int = 51) -> None:
+    """forward(causal=True) with a map and a scale against exact brute force on
+    phi(s q), phi(s k), for every chunk size (chunking page, section ②)."""
+    rng = np.random.default_rng([seed, 52])
+    L, dk, dv = 9, 3, 2
+    qf, kf, vf = _bf16(rng, (L, dk)), _bf16(rng, (L, dk)), _bf16(rng, (L, dv))
+    for s in (0.5, -2.0):
+        qs, ks = o.phi_elu1(s * qf), o.phi_elu1(s * kf)
+        for normalize in (False, True):
+            exact = _frac_matrix(o.brute_force(qs, ks, vf, causal=True, normalize=normalize))
+            for C in (1, 4, 9):
+                out, S, z = o.forward(qf, kf, vf, C, True, normalize, "elu1", None, s)
+                assert np.allclose(out, exact, rtol=1e-12, atol=1e-13), (s, normalize, C)
+                assert np.allclose(S, ks.T @ vf, rtol=1e-13, atol=1e-14)
+
+
+def check_over_heads(o, seed: int = 53) -> None:
+    """over_heads maps a single-head form over a leading head axis: head h of the
+    result is the form on head h alone, for forms returning one array or a tuple."""
+    rng = np.random.default_rng([seed, 54])
+    H, L, dk, dv = 3, 6, 2, 3
+    q, k, v = _ints(rng, (H, L, dk)), _ints(rng, (H, L, dk)), _ints(rng, (H, L, dv))
+    one = o.over_heads(o.causal_scores_first, q, k, v)
+    tup = o.over_heads(o.chunked, q, k, v, 4)
+    assert one.shape == (H, L, dv) and len(tup) == 3 and tup[1].shape == (H, dk, dv)
+    for h in range(H):
+        assert np.array_equal(one[h], o.causal_scores_first(q[h], k[h], v[h]))
+        out, S, z = o.chunked(q[h], k[h], v[h], 4)
+        assert np.array_equal(tup[0][h], out) and np.array_equal(tup[1][h], S) and np.array_equal(tup[2][h], z)

@@ -92,6 +92,22 @@ MUTANTS = {
                                     "acc = acc + lam[s:e, cb + m - 1][:, None] * (q[s:e] @ Sb)"),
     "loglinear_masked_wrong_level": ("            M[t, s_] = lam[t, loglinear_level(t, s_)]",
                                      "            M[t, s_] = lam[s_, loglinear_level(t, s_)]"),
+    "apply_phi_drops_in_scale": ("        x = np.asarray(x, dtype=np.float64) * in_scale\n",
+                                 "        x = np.asarray(x, dtype=np.float64)\n"),
+    "apply_phi_scale_after_map": ("    if in_scale != 1.0:\n        x = np.asarray(x, dtype=np.float64) * in_scale\n"
+                                  "    if fmap == \"identity\":\n        return phi_identity(x)\n"
+                                  "    if fmap == \"elu1\":\n        return phi_elu1(x)\n",
+                                  "    if fmap == \"identity\":\n        return phi_identity(x) * in_scale\n"
+                                  "    if fmap == \"elu1\":\n        return phi_elu1(x) * in_scale\n"),
+    "apply_phi_favor_scale_after_map": ("        return phi_favor(x, W)\n",
+                                        "        return phi_favor(x / in_scale, W) * in_scale\n"),
+    "forward_skips_scaled_identity": ("if (fmap != \"identity\" or in_scale != 1.0) else q_raw",
+                                      "if fmap != \"identity\" else q_raw"),
+    "forward_noncausal_ignores_normalize": ("    out = noncausal_state_first(qp, kp, v, normalize)\n",
+                                            "    out = noncausal_state_first(qp, kp, v, False)\n"),
+    "forward_noncausal_is_causal": ("    out = noncausal_state_first(qp, kp, v, normalize)\n",
+                                    "    out = chunked(qp, kp, v, C, normalize)[0]\n"),
+    "forward_noncausal_state_transposed": ("    S, z = final_state(kp, v)\n", "    S, z = final_state(v, kp)\n"),
     "forward_ignores_gamma": ("        return decay_chunked(qp, kp, v, C, gamma, normalize)",
                               "        return chunked(qp, kp, v, C, normalize)"),
 }

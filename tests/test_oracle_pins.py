@@ -101,3 +101,23 @@ def test_loglinear_forms():
 
 def test_loglinear_causality():
     pins.check_loglinear_causality(oracle)
+
+
+def test_apply_phi_in_scale():
+    pins.check_apply_phi_in_scale(oracle)
+
+
+def test_forward_scaled_favor_is_softmax():
+    pins.check_forward_scaled_favor_is_softmax(oracle)
+
+
+def test_forward_noncausal():
+    pins.check_forward_noncausal(oracle)
+
+
+def test_forward_causal_scaled():
+    pins.check_forward_causal_scaled(oracle)
+
+
+def test_over_heads():
+    pins.check_over_heads(oracle)
