@@ -6,7 +6,7 @@ no code with the HIP path (``chunked_causal_linear_amd``) and imports nothing
 from it.
 
 Everything here is the plain definition of what the method computes, written
-from three pages:
+from four pages:
 
 * "attention と線形の間" (sharin-2a1.pages.dev/parts/chunked.html), below
   called *the chunking page*: section ① (the two association orders and the
@@ -20,6 +20,9 @@ from three pages:
   normaliser z_t, and the decayed recurrence it gives for Retention), the
   elu+1 and FAVOR+ feature maps, and the recurrent and materialised-prefix
   causal forms.
+* "Kimi K3 と Qwen 3.8 の Attention 機構比較分析" (news.ainew.jp), below called
+  *the Kimi/Qwen page*: the delta rule's erase-then-write update (section 3.1),
+  its gated form (section 2.4) and its two-key example (section 3.3.5).
 
 Precision.  Floating-point inputs arrive as float64 arrays holding bf16 values
 (exact), and every form computes in float64 with no intermediate rounding.
@@ -670,6 +673,141 @@ def softmax_attention_loops(q, k, v, causal: bool = False, scale: Optional[float
         den = sum(e)
         out.append([sum(e[j] * float(v[j][c]) for j in range(last + 1)) / den for c in range(len(v[0]))])
     return out
+
+
+# ---------------------------------------------------------------------------
+# The delta rule and its gated form (page "Kimi K3 と Qwen 3.8 の Attention 機構
+# 比較分析", below called the Kimi/Qwen page: section 3.1, its equation (14):
+# before writing, look up what the current key already maps to in the state,
+# erase that old prediction along the key, then write the new value; section
+# 2.4: the gated form is a global decay of the whole state, the directed erase
+# and the residual write; section 3.3.5 works the erase through on two keys;
+# the chunking page's closing notes name DeltaNet and Gated DeltaNet as the
+# successors of the additive state).  With the state S (d_k x d_v) read as
+# o = q S, the write strength beta_t and the gate alpha_t per token:
+#     S_t = alpha_t (S_{t-1} - beta_t k_t (k_t^T S_{t-1})) + beta_t k_t v_t^T
+#         = alpha_t S_{t-1} + k_t u_t^T,   u_t = beta_t (v_t - alpha_t S_{t-1}^T k_t)
+#     o_t = q_t^T S_t                      (read after the update)
+# beta = 1, alpha = 1 is the page's worked case (old prediction fully erased);
+# alpha = 1 is the delta rule without the gate.  No feature map, no
+# normaliser (the page gives neither); keys are used as given (the page's
+# example takes unit keys).  All forms compute in float64.
+# ---------------------------------------------------------------------------
+def _gates(alpha, L: int) -> np.ndarray:
+    return np.ones(L) if alpha is None else np.asarray(alpha, dtype=np.float64)
+
+
+def delta_recurrent(q, k, v, beta, alpha=None, S0=None):
+    """The recurrence itself, token by token: u_t = beta_t (v_t - alpha_t S_{t-1}^T
+    k_t), S_t = alpha_t S_{t-1} + k_t u_t^T, o_t = q_t^T S_t.  Returns (out, S_L);
+    S0 continues from a given state (zero when omitted)."""
+    q, k, v = _f64(q, k, v)
+    L, dk = q.shape
+    dv = v.shape[1]
+    b = np.asarray(beta, dtype=np.float64)
+    a = _gates(alpha, L)
+    S = np.zeros((dk, dv)) if S0 is None else np.array(S0, dtype=np.float64)
+    out = np.zeros((L, dv))
+    for t in range(L):
+        old = a[t] * S                       # the decayed state
+        u = b[t] * (v[t] - k[t] @ old)       # the new value minus the old prediction at k_t
+        S = old + np.outer(k[t], u)          # erase along k_t and write
+        out[t] = q[t] @ S
+    return out, S
+
+
+def delta_step(S, q_t, k_t, v_t, beta_t: float, alpha_t: float = 1.0):
+    """One decode step of the (gated) delta rule on one state.  Returns (o, S')."""
+    old = float(alpha_t) * np.asarray(S, dtype=np.float64)
+    u = float(beta_t) * (np.asarray(v_t, dtype=np.float64) - np.asarray(k_t, dtype=np.float64) @ old)
+    S = old + np.outer(k_t, u)
+    return np.asarray(q_t, dtype=np.float64) @ S, S
+
+
+def unit_lower_solve(A: np.ndarray, R: np.ndarray) -> np.ndarray:
+    """X with (I + A) X = R for a strictly lower-triangular A, by forward
+    substitution row by row (exact on integers)."""
+    X = np.zeros_like(R, dtype=np.float64)
+    for i in range(R.shape[0]):
+        X[i] = R[i] - A[i, :i] @ X[:i]
+    return X
+
+
+def delta_chunked(q, k, v, beta, alpha=None, C: int = 64, S0=None):
+    """Chunkwise form of the (gated) delta rule, derived from the recurrence
+    (C <= 0 is treated as 1).  Inside a chunk [s, e) with P the state before it
+    and g_i the product of the gates of its rows 0..i (local indices):
+        alpha_i S_{i-1} = g_i P + sum_{j<i} (g_i / g_j) k_j u_j^T,  so
+        u_i = beta_i (v_i - g_i P^T k_i - sum_{j<i} (g_i / g_j)(k_i . k_j) u_j),
+    i.e. the unit lower-triangular system (I + A) U = diag(beta)(V - diag(g) K P)
+    with A[i, j] = beta_i (k_i . k_j) g_i / g_j for j < i.  Then
+        O   = diag(g) Q P + (tril(Q K^T) * G) U,     G[i, j] = g_i / g_j
+        P  <- g_n P + K^T diag(g_n / g) U            (n rows in the chunk).
+    Returns (out, S_L)."""
+    if C <= 0:
+        C = 1
+    q, k, v = _f64(q, k, v)
+    L, dk = q.shape
+    dv = v.shape[1]
+    b = np.asarray(beta, dtype=np.float64)
+    a = _gates(alpha, L)
+    P = np.zeros((dk, dv)) if S0 is None else np.array(S0, dtype=np.float64)
+    out = np.zeros((L, dv))
+    for s in range(0, L, C):
+        e = min(s + C, L)
+        qc, kc, vc, bc = q[s:e], k[s:e], v[s:e], b[s:e]
+        g = np.cumprod(a[s:e])
+        G = g[:, None] / g[None, :]
+        A = np.tril(bc[:, None] * (kc @ kc.T) * G, -1)
+        U = unit_lower_solve(A, bc[:, None] * (vc - g[:, None] * (kc @ P)))
+        out[s:e] = g[:, None] * (qc @ P) + (tril(qc @ kc.T) * G) @ U
+        P = g[-1] * P + kc.T @ ((g[-1] / g)[:, None] * U)
+    return out, P
+
+
+def delta_chunk_transform(k, beta, alpha=None, C: int = 64):
+    """Per chunk n the matrix T_n = (I + A_n)^(-1) diag(beta) of delta_chunked
+    (rows and columns the chunk's rows; a short last chunk gives a smaller block),
+    as the columns of the forward substitution applied to diag(beta).  Returns a
+    list of N arrays."""
+    if C <= 0:
+        C = 1
+    k = np.asarray(k, dtype=np.float64)
+    L = k.shape[0]
+    b = np.asarray(beta, dtype=np.float64)
+    a = _gates(alpha, L)
+    out = []
+    for s in range(0, L, C):
+        e = min(s + C, L)
+        g = np.cumprod(a[s:e])
+        A = np.tril(b[s:e, None] * (k[s:e] @ k[s:e].T) * (g[:, None] / g[None, :]), -1)
+        out.append(unit_lower_solve(A, np.diag(b[s:e])))
+    return out
+
+
+def brute_force_delta(q, k, v, beta, alpha=None):
+    """The recurrence in exact rational arithmetic (Fractions of the exact binary
+    values, or of given Fractions): nested loops over every state element."""
+    def exact(x):
+        if isinstance(x, Fraction):
+            return x
+        if isinstance(x, (int, np.integer)):
+            return Fraction(int(x))
+        return Fraction(float(x))
+
+    L, dk, dv = len(q), len(q[0]), len(v[0])
+    S = [[Fraction(0)] * dv for _ in range(dk)]
+    out = []
+    for t in range(L):
+        at = Fraction(1) if alpha is None else exact(alpha[t])
+        bt = exact(beta[t])
+        kt = [exact(x) for x in k[t]]
+        S = [[at * S[i][c] for c in range(dv)] for i in range(dk)]
+        pred = [sum((kt[i] * S[i][c] for i in range(dk)), Fraction(0)) for c in range(dv)]
+        u = [bt * (exact(v[t][c]) - pred[c]) for c in range(dv)]
+        S = [[S[i][c] + kt[i] * u[c] for c in range(dv)] for i in range(dk)]
+        out.append([sum((exact(q[t][i]) * S[i][c] for i in range(dk)), Fraction(0)) for c in range(dv)])
+    return out, S
 
 
 # ---------------------------------------------------------------------------

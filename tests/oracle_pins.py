@@ -642,3 +642,188 @@ def check_over_heads(o, seed: int = 53) -> None:
         assert np.array_equal(one[h], o.causal_scores_first(q[h], k[h], v[h]))
         out, S, z = o.chunked(q[h], k[h], v[h], 4)
         assert np.array_equal(tup[0][h], out) and np.array_equal(tup[1][h], S) and np.array_equal(tup[2][h], z)
+
+
+# ---------------------------------------------------------------------------
+# The delta rule (Kimi/Qwen page "Kimi K3 と Qwen 3.8 の Attention 機構比較分析":
+# section 3.1, the erase-then-write update of its equation (14); section 2.4,
+# the gated form; section 3.3.5, the two-key example).  The recurrence is the
+# definition; every other form is pinned to it, to exact brute force, to the
+# page's worked example and to cases that reduce to forms pinned above.
+# ---------------------------------------------------------------------------
+def _frac_rows(rows):
+    return np.array([[float(x) for x in r] for r in rows])
+
+
+def check_delta_page_example(o) -> None:
+    """Section 3.3.5: unit keys k1 = [1, 0], k2 = [cos t, sin t]; write v1 under k1,
+    then v2 under k2 (full strength); reading with k1 gives sin^2 t v1 + cos t v2.
+    Exact with cos t = 3/5, sin t = 4/5; the page's cos t = 0.98 leaves 0.98 of v2
+    and 1 - 0.98^2 = 0.0396 of v1."""
+    F = Fraction
+    v1, v2 = [F(2), F(-1), F(5)], [F(1), F(3), F(-2)]
+    k = [[F(1), F(0)], [F(3, 5), F(4, 5)]]
+    q = [[F(0), F(0)], [F(1), F(0)]]  # the second read is with k1
+    out, S = o.brute_force_delta(q, k, [v1, v2], [F(1), F(1)])
+    want = [F(16, 25) * a + F(3, 5) * b for a, b in zip(v1, v2)]
+    assert out[1] == want, (out[1], want)
+    c = 0.98
+    s_ = math.sqrt(1 - c * c)
+    kf = np.array([[1.0, 0.0], [c, s_]])
+    vf = np.array([[2.0, -1.0, 5.0], [1.0, 3.0, -2.0]])
+    qf = np.array([[0.0, 0.0], [1.0, 0.0]])
+    for form in (lambda: o.delta_recurrent(qf, kf, vf, [1.0, 1.0])[0],
+                 lambda: o.delta_chunked(qf, kf, vf, [1.0, 1.0], None, 2)[0]):
+        got = form()[1]
+        assert np.allclose(got, (1 - c * c) * vf[0] + c * vf[1], rtol=1e-13, atol=1e-14), got
+    assert abs((1 - c * c) - 0.0396) < 1e-15
+
+
+def check_delta_readback(o, seed: int = 70) -> None:
+    """Equation (14) of section 3.1: the old prediction at the key is erased and
+    the new value written, so right after a full-strength write under a unit key
+    the state maps that key exactly to the new value, whatever it held before;
+    and a key written twice returns the second value (section 3.3.6: the last
+    write wins).  Exact on Fractions with unit keys e_i and (3/5, 4/5)."""
+    rng = np.random.default_rng([seed, 71])
+    F = Fraction
+    dk, dv = 3, 2
+    units = [[F(1), F(0), F(0)], [F(0), F(3, 5), F(4, 5)], [F(4, 5), F(0), F(-3, 5)], [F(0), F(1), F(0)]]
+    L = 7
+    ks = [units[i % 4] for i in rng.permutation(L)]
+    ks[5] = ks[2]  # the same key twice
+    vs = [[F(int(x)) for x in rng.integers(-4, 5, dv)] for _ in range(L)]
+    # queries equal to the keys: each read-back must return the value just written
+    out, S = o.brute_force_delta(ks, ks, vs, [F(1)] * L)
+    for t in range(L):
+        assert out[t] == vs[t], t
+    # from a nonzero state, through the float forms (keys exact in binary: e_i only)
+    S0 = rng.integers(-3, 4, (dk, dv)).astype(np.float64)
+    kf = np.eye(dk)[rng.integers(0, dk, L)]
+    vf = rng.integers(-4, 5, (L, dv)).astype(np.float64)
+    for form in (o.delta_recurrent(kf, kf, vf, np.ones(L), None, S0)[0],
+                 o.delta_chunked(kf, kf, vf, np.ones(L), None, 3, S0)[0]):
+        assert np.array_equal(form, vf)
+
+
+def check_delta_orthogonal_keys(o, seed: int = 72) -> None:
+    """With keys orthogonal to every earlier key the erase finds nothing: u_t =
+    beta_t v_t, so the delta rule is causal linear attention on values beta_t v_t,
+    and with a constant gate gamma the decayed (Retention) recurrence; both pinned
+    above.  Exact on integers and dyadic beta, gamma."""
+    rng = np.random.default_rng([seed, 73])
+    L = dk = 6
+    dv = 3
+    k = np.eye(dk)[rng.permutation(dk)] * rng.choice([-1.0, 1.0], (L, 1))
+    q = rng.integers(-3, 4, (L, dk)).astype(np.float64)
+    v = rng.integers(-3, 4, (L, dv)).astype(np.float64)
+    b = rng.choice([0.25, 0.5, 1.0], L)
+    ref = o.causal_scores_first(q, k, b[:, None] * v)
+    for C in (1, 2, 4, 6):
+        assert np.array_equal(o.delta_chunked(q, k, v, b, None, C)[0], ref), C
+    assert np.array_equal(o.delta_recurrent(q, k, v, b)[0], ref)
+    gam = 0.75
+    refd, Sd, _ = o.decay_state_first(q, k, b[:, None] * v, gam)
+    for C in (1, 3, 6):
+        out, S = o.delta_chunked(q, k, v, b, np.full(L, gam), C)
+        assert np.array_equal(out, refd) and np.array_equal(S, Sd), C
+
+
+def check_delta_scalar_closed_form(o) -> None:
+    """d_k = 1 with the key 1: S_t = alpha_t (1 - beta) S_{t-1} + beta v_t, an
+    exponential moving average; with alpha = 1 and S_0 = 0,
+    S_t = sum_{j<=t} beta (1 - beta)^(t-j) v_j, so the two write orders of two
+    values differ by beta^2 (v_2 - v_1) (section 3.3.6: the update does not
+    commute), and beta = 1 keeps only the last value.  beta = 0 leaves the
+    state to the gates: S_t = (prod of alpha) S_0."""
+    v = np.array([[3.0], [-5.0], [7.0], [1.0]])
+    one = np.ones((4, 1))
+    for beta in (0.5, 0.25, 1.0):
+        out = o.delta_recurrent(one, one, v, np.full(4, beta))[0]
+        for t in range(4):
+            want = sum(beta * (1 - beta) ** (t - j) * v[j, 0] for j in range(t + 1))
+            assert out[t, 0] == want, (beta, t)
+        a = o.delta_chunked(one[:2], one[:2], v[:2], [beta, beta], None, 2)[0][1, 0]
+        b_ = o.delta_chunked(one[:2], one[:2], v[1::-1], [beta, beta], None, 2)[0][1, 0]
+        assert a - b_ == beta * beta * (v[1, 0] - v[0, 0])
+    alpha = np.array([0.5, 0.75, 1.0, 0.5])
+    S0 = np.array([[8.0, -4.0]])
+    for form in (o.delta_recurrent(one, one, np.zeros((4, 2)), np.zeros(4), alpha, S0),
+                 o.delta_chunked(one, one, np.zeros((4, 2)), np.zeros(4), alpha, 3, S0)):
+        out, S = form
+        assert np.array_equal(out[:, 0], 8.0 * np.cumprod(alpha)) and np.array_equal(S, S0 * np.prod(alpha))
+
+
+def check_delta_forms(o, seed: int = 74) -> None:
+    """The chunked form equals the recurrence for every chunk size: exactly on
+    integers at full strength without gates (the triangular system is integer);
+    with fractional beta and gates against exact brute force to float64
+    rounding; and the recurrence against brute force."""
+    rng = np.random.default_rng([seed, 75])
+    L, dk, dv = 9, 3, 2
+    q, k, v = (rng.integers(-1, 2, (L, d)).astype(np.float64) for d in (dk, dk, dv))
+    ref, S = o.delta_recurrent(q, k, v, np.ones(L))
+    bf, Sb = o.brute_force_delta(q, k, v, np.ones(L))
+    assert np.array_equal(ref, _frac_rows(bf)) and np.array_equal(S, _frac_rows(Sb))
+    for C in range(0, L + 2):
+        out, Sc = o.delta_chunked(q, k, v, np.ones(L), None, C)
+        assert np.array_equal(out, ref) and np.array_equal(Sc, S), C
+    qf, kf, vf = _bf16(rng, (L, dk)), _bf16(rng, (L, dk), 0.6), _bf16(rng, (L, dv))
+    b = rng.choice([0.25, 0.5, 0.75, 1.0], L)
+    a = rng.choice([0.5, 0.75, 1.0], L)
+    bf, Sb = o.brute_force_delta(qf, kf, vf, b, a)
+    exact, Sx = _frac_rows(bf), _frac_rows(Sb)
+    r, Sr = o.delta_recurrent(qf, kf, vf, b, a)
+    assert np.allclose(r, exact, rtol=1e-12, atol=1e-13) and np.allclose(Sr, Sx, rtol=1e-12, atol=1e-13)
+    for C in (1, 2, 4, 5, 9, 12):
+        out, Sc = o.delta_chunked(qf, kf, vf, b, a, C)
+        assert np.allclose(out, exact, rtol=1e-12, atol=1e-13), C
+        assert np.allclose(Sc, Sx, rtol=1e-12, atol=1e-13), C
+
+
+def check_delta_transform(o, seed: int = 76) -> None:
+    """The chunk transform T = (I + A)^(-1) diag(beta), A[i, j] = beta_i (k_i.k_j)
+    g_i / g_j (j < i): lower triangular with diagonal beta, (I + A) T = diag(beta)
+    exactly on integer keys, and for the first chunk (zero state) the outputs
+    are (tril(Q K^T) * G) T V, the recurrence's first rows."""
+    rng = np.random.default_rng([seed, 77])
+    L, dk, dv, C = 11, 3, 2, 5
+    k = rng.integers(-1, 2, (L, dk)).astype(np.float64)
+    Ts = o.delta_chunk_transform(k, np.ones(L), None, C)
+    assert [t.shape for t in Ts] == [(5, 5), (5, 5), (1, 1)]
+    for n, T in enumerate(Ts):
+        kc = k[n * C:(n + 1) * C]
+        A = np.tril(kc @ kc.T, -1)
+        assert np.array_equal((np.eye(len(kc)) + A) @ T, np.eye(len(kc)))
+        assert np.array_equal(np.triu(T, 1), np.zeros_like(T))
+    qf, kf, vf = _bf16(rng, (C, dk)), _bf16(rng, (C, dk), 0.6), _bf16(rng, (C, dv))
+    b = rng.choice([0.25, 0.5, 1.0], C)
+    a = rng.choice([0.5, 0.75, 1.0], C)
+    T = o.delta_chunk_transform(kf, b, a, C)[0]
+    assert np.allclose(np.diag(T), b, rtol=1e-15)
+    g = np.cumprod(a)
+    out0 = (np.tril(qf @ kf.T) * (g[:, None] / g[None, :])) @ T @ vf
+    assert np.allclose(out0, o.delta_recurrent(qf, kf, vf, b, a)[0], rtol=1e-12, atol=1e-13)
+
+
+def check_delta_causality_resume(o, seed: int = 78) -> None:
+    """Changing token t changes no earlier output; the chunked form over the
+    first L1 tokens followed by decode steps from its final state equals the
+    form over all L tokens."""
+    rng = np.random.default_rng([seed, 79])
+    L, L1, dk, dv = 14, 9, 4, 3
+    q, k, v = _bf16(rng, (L, dk)), _bf16(rng, (L, dk), 0.5), _bf16(rng, (L, dv))
+    b, a = rng.uniform(0.1, 1.0, L), rng.uniform(0.6, 1.0, L)
+    base, Sfull = o.delta_chunked(q, k, v, b, a, 4)
+    for t in (0, 5, 8, 13):
+        for which in range(3):
+            arrs = [q.copy(), k.copy(), v.copy()]
+            arrs[which][t] += 0.5
+            pert = o.delta_chunked(*arrs, b, a, 4)[0]
+            assert np.array_equal(pert[:t], base[:t]), (t, which)
+            assert not np.allclose(pert[t:], base[t:]), (t, which)
+    _, S = o.delta_chunked(q[:L1], k[:L1], v[:L1], b[:L1], a[:L1], 4)
+    for t in range(L1, L):
+        ot, S = o.delta_step(S, q[t], k[t], v[t], b[t], a[t])
+        assert np.allclose(ot, base[t], rtol=1e-12, atol=1e-13), t
+    assert np.allclose(S, Sfull, rtol=1e-12, atol=1e-13)

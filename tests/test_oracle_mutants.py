@@ -108,6 +108,45 @@ MUTANTS = {
     "forward_noncausal_is_causal": ("    out = noncausal_state_first(qp, kp, v, normalize)\n",
                                     "    out = chunked(qp, kp, v, C, normalize)[0]\n"),
     "forward_noncausal_state_transposed": ("    S, z = final_state(kp, v)\n", "    S, z = final_state(v, kp)\n"),
+    # the delta rule
+    "delta_read_before_update": ("        S = old + np.outer(k[t], u)          # erase along k_t and write\n        out[t] = q[t] @ S\n",
+                                 "        out[t] = q[t] @ old\n        S = old + np.outer(k[t], u)\n"),
+    "delta_no_erase": ("        u = b[t] * (v[t] - k[t] @ old)       # the new value minus the old prediction at k_t\n",
+                       "        u = b[t] * v[t]\n"),
+    "delta_erase_undecayed_state": ("        u = b[t] * (v[t] - k[t] @ old)       # the new value minus the old prediction at k_t\n",
+                                    "        u = b[t] * (v[t] - k[t] @ S)\n"),
+    "delta_beta_on_write_only": ("        u = b[t] * (v[t] - k[t] @ old)       # the new value minus the old prediction at k_t\n",
+                                 "        u = b[t] * v[t] - k[t] @ old\n"),
+    "delta_gate_on_write": ("        S = old + np.outer(k[t], u)          # erase along k_t and write\n",
+                            "        S = a[t] * (S + np.outer(k[t], u))\n"),
+    "delta_step_no_gate": ("    old = float(alpha_t) * np.asarray(S, dtype=np.float64)\n",
+                           "    old = np.asarray(S, dtype=np.float64)\n"),
+    "delta_step_read_before": ("    return np.asarray(q_t, dtype=np.float64) @ S, S\n",
+                               "    return np.asarray(q_t, dtype=np.float64) @ old, S\n"),
+    "delta_solve_sign": ("        X[i] = R[i] - A[i, :i] @ X[:i]\n", "        X[i] = R[i] + A[i, :i] @ X[:i]\n"),
+    "delta_chunked_A_upper": ("        A = np.tril(bc[:, None] * (kc @ kc.T) * G, -1)\n",
+                              "        A = np.triu(bc[:, None] * (kc @ kc.T) * G, 1).T\n"),
+    "delta_chunked_A_beta_on_columns": ("        A = np.tril(bc[:, None] * (kc @ kc.T) * G, -1)\n",
+                                        "        A = np.tril(bc[None, :] * (kc @ kc.T) * G, -1)\n"),
+    "delta_chunked_G_transposed": ("        G = g[:, None] / g[None, :]\n", "        G = g[None, :] / g[:, None]\n"),
+    "delta_chunked_no_gate_on_inter": ("        out[s:e] = g[:, None] * (qc @ P) + (tril(qc @ kc.T) * G) @ U\n",
+                                       "        out[s:e] = (qc @ P) + (tril(qc @ kc.T) * G) @ U\n"),
+    "delta_chunked_intra_exclusive": ("        out[s:e] = g[:, None] * (qc @ P) + (tril(qc @ kc.T) * G) @ U\n",
+                                      "        out[s:e] = g[:, None] * (qc @ P) + (np.tril(qc @ kc.T, -1) * G) @ U\n"),
+    "delta_chunked_carry_undecayed": ("        P = g[-1] * P + kc.T @ ((g[-1] / g)[:, None] * U)\n",
+                                      "        P = P + kc.T @ ((g[-1] / g)[:, None] * U)\n"),
+    "delta_chunked_carry_weights": ("        P = g[-1] * P + kc.T @ ((g[-1] / g)[:, None] * U)\n",
+                                    "        P = g[-1] * P + kc.T @ U\n"),
+    "delta_chunked_rhs_ungated": ("        U = unit_lower_solve(A, bc[:, None] * (vc - g[:, None] * (kc @ P)))\n",
+                                  "        U = unit_lower_solve(A, bc[:, None] * (vc - (kc @ P)))\n"),
+    "delta_transform_no_beta": ("        out.append(unit_lower_solve(A, np.diag(b[s:e])))\n",
+                                "        out.append(unit_lower_solve(A, np.eye(e - s)))\n"),
+    "delta_transform_ungated": ("        A = np.tril(b[s:e, None] * (k[s:e] @ k[s:e].T) * (g[:, None] / g[None, :]), -1)\n",
+                                "        A = np.tril(b[s:e, None] * (k[s:e] @ k[s:e].T), -1)\n"),
+    "brute_force_delta_ungated": ("        S = [[at * S[i][c] for c in range(dv)] for i in range(dk)]\n",
+                                  "        S = [[S[i][c] for c in range(dv)] for i in range(dk)]\n"),
+    "brute_force_delta_no_erase": ("        u = [bt * (exact(v[t][c]) - pred[c]) for c in range(dv)]\n",
+                                   "        u = [bt * exact(v[t][c]) for c in range(dv)]\n"),
     "forward_ignores_gamma": ("        return decay_chunked(qp, kp, v, C, gamma, normalize)",
                               "        return chunked(qp, kp, v, C, normalize)"),
 }

@@ -121,3 +121,31 @@ def test_forward_causal_scaled():
 
 def test_over_heads():
     pins.check_over_heads(oracle)
+
+
+def test_delta_page_example():
+    pins.check_delta_page_example(oracle)
+
+
+def test_delta_readback():
+    pins.check_delta_readback(oracle)
+
+
+def test_delta_orthogonal_keys():
+    pins.check_delta_orthogonal_keys(oracle)
+
+
+def test_delta_scalar_closed_form():
+    pins.check_delta_scalar_closed_form(oracle)
+
+
+def test_delta_forms():
+    pins.check_delta_forms(oracle)
+
+
+def test_delta_transform():
+    pins.check_delta_transform(oracle)
+
+
+def test_delta_causality_resume():
+    pins.check_delta_causality_resume(oracle)
