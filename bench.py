@@ -44,6 +44,8 @@ def lib_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "chunked_causal_linear_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
+        if not os.path.isfile(os.path.join(csrc, f)):
+            continue  # the measurement probe's sources are not the library's
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -74,6 +76,54 @@ def copy_calibration():
     torch.cuda.synchronize()
     del a, b
     torch.cuda.empty_cache()
+
+
+def mfma_peak(kind: int, grid: int = 2048, iters: int = 1024):
+    """Measured matrix-core rate (TFLOP/s for bf16, TOP/s for int8) of the probe
+    loop in libla_probe.so (include/la_probe.h): median of five launches, each
+    timed with an event pair on the current stream, after two untimed ones."""
+    import ctypes
+
+    import numpy as np
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "chunked_causal_linear_amd", "libla_probe.so"))
+    lib.la_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    lib.la_probe_mfma.restype = ctypes.c_int
+    out = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+
+    def run():
+        rc = lib.la_probe_mfma(kind, iters, grid, out.data_ptr(), torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"la_probe_mfma returned {rc}")
+    for _ in range(2):
+        run()
+    torch.cuda.synchronize()
+    ms = float(np.median(per_launch_ms(run, 5)))
+    per_inst = 16384 if kind == 0 else 32768
+    return grid * 4 * iters * 8 * per_inst / (ms * 1e-3) / 1e12, ms
+
+
+def cpu_info():
+    """CPU model (from /proc/cpuinfo) and numpy's BLAS build and thread count."""
+    model = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = []
+    try:
+        import threadpoolctl
+        for d in threadpoolctl.threadpool_info():
+            if d.get("user_api") == "blas":
+                blas.append({k: d.get(k) for k in ("internal_api", "version", "num_threads", "architecture",
+                                                    "threading_layer")})
+    except Exception as e:  # noqa: BLE001 - the record is informative only
+        blas.append({"error": str(e)})
+    return model, blas
 
 
 def dev_bf16(bits):
@@ -142,22 +192,27 @@ def cpu_baseline(w, C: int, budget_s: float = 10.0):
     """The CPU oracle's chunked form, as it stands, on whole heads of the
     workload at full L, head after head until about `budget_s` seconds of CPU
     work; tokens/s extrapolated linearly over the heads."""
+    import threadpoolctl
+
     import oracle
     import workloads as wl
     cores = len(os.sched_getaffinity(0))
     elapsed, heads = 0.0, 0
-    while elapsed < budget_s and heads < w.BH:
-        q, k, v = wl.head_inputs(w, heads)  # input generation is not timed
-        t1 = time.perf_counter()
-        oracle.chunked(q.exact, k.exact, v.exact, C, w.normalize)
-        elapsed += time.perf_counter() - t1
-        heads += 1
+    # BLAS threads = the cores this process may run on, set explicitly
+    with threadpoolctl.threadpool_limits(limits=cores, user_api="blas"):
+        model, blas = cpu_info()
+        while elapsed < budget_s and heads < w.BH:
+            q, k, v = wl.head_inputs(w, heads)  # input generation is not timed
+            t1 = time.perf_counter()
+            oracle.chunked(q.exact, k.exact, v.exact, C, w.normalize)
+            elapsed += time.perf_counter() - t1
+            heads += 1
     per_head = elapsed / heads
     tokens_per_s = w.L / (w.H * per_head)  # B*L tokens take B*H head passes
     return {"value": tokens_per_s, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"oracle.chunked (numpy float64, C={C}) on {heads} of {w.BH} heads at full L={w.L} "
                       f"({elapsed:.1f} s); {per_head:.3f} s per head, extrapolated over all heads",
-            "cpu": platform.processor() or platform.machine()}
+            "cpu": model, "blas": blas, "blas_threads_set": cores}
 
 
 def run_headline(args):
@@ -220,6 +275,9 @@ def run_headline(args):
     ref_gbs = 4 * qd.numel() * 2 / (ref_ms * 1e-3) / 1e9
     del scratch
 
+    # the matrix cores' attainable rate, measured in the same run
+    peak_bf16, _ = mfma_peak(0)
+
     work = Work(w.BH, w.L, w.d_in, w.d_k, w.d_v, C)
     tokens = w.B * w.L
     flops = work.page_flops()
@@ -251,6 +309,8 @@ def run_headline(args):
                    "parallelism": "single-gpu"},
         "tflops_page_count": flops / sec / 1e12,
         "mfma_frac_page_count": flops / sec / 1e12 / PEAK_BF16_TFLOPS,
+        "mfma_peak_measured_tflops": peak_bf16,
+        "mfma_frac_page_count_of_measured_peak": flops / sec / 1e12 / peak_bf16,
         "tflops_causal_useful": useful / sec / 1e12,
         "head_tokens_per_s": w.BH * w.L / sec,
         "phases_ms": {"chunk_states": k1, "state_scan": k2, "chunk_output": k3},
@@ -489,6 +549,127 @@ def run_extras(args, out):
     out["rows"] = rows
 
 
+ROWS = ("fwd_w3_C32", "fwd_w3_C64", "fwd_w3_C128", "fwd_w3_int8_C64", "states_w3_C64", "states_w3_C1024",
+        "scan_w3_C64", "fmap_favor_w5", "fwd_w2", "fwd_w4", "fwd_w5", "decode_w5", "mfma_peak_bf16", "mfma_peak_i8",
+        "copy_512MiB")
+
+
+def run_row(name: str, reps: int):
+    """Run one hot-path row `reps` times after one untimed call, and nothing else
+    (for rocprofv3 counter passes over a short program)."""
+    import numpy as np
+    import torch
+
+    import chunked_causal_linear_amd as la
+    import workloads as wl
+
+    if name not in ROWS:
+        raise SystemExit(f"unknown row {name}; one of {', '.join(ROWS)}")
+    fn = None
+    if name.startswith("mfma_peak"):
+        for _ in range(reps):
+            tf, ms = mfma_peak(0 if name.endswith("bf16") else 1)
+        log(f"{name}: {tf:.1f} T(FL)OP/s, {ms:.3f} ms per probe launch")
+        return
+    if name == "copy_512MiB":
+        copy_calibration()
+        log(f"{name}: two 512 MiB device copies")
+        return
+    w3 = wl.WORKLOADS[3]
+    if name.startswith(("fwd_w3_C", "states_w3", "scan_w3")):
+        q, k, v, _ = wl.workload_inputs(w3, want_exact=False)
+        qd, kd, vd = dev_bf16(q.bits), dev_bf16(k.bits), dev_bf16(v.bits)
+        del q, k, v
+        if name.startswith("fwd_w3_C"):
+            fn = la.Forward(qd, kd, vd, int(name.split("C")[-1])).run
+        elif name.startswith("states_w3"):
+            C = int(name.split("C")[-1])
+            S, _ = la.chunk_states(kd, vd, C)
+            fn = lambda: la.chunk_states(kd, vd, C, out=S)  # noqa: E731
+        else:
+            S, _ = la.chunk_states(kd, vd, 64)
+            fn = lambda: la.state_scan(S, None, want_final=False)  # noqa: E731
+    elif name == "fwd_w3_int8_C64":
+        qi, ki, vi = wl.random_case(33, w3.BH, w3.L, 128, 128, "i8")
+        tq, tk, tv = (torch.from_numpy(t.bits).cuda() for t in (qi, ki, vi))
+        fn = la.Forward(tq, tk, tv, 64).run
+    elif name == "fmap_favor_w5":
+        w5 = wl.WORKLOADS[5]
+        q5, _, _, W5 = wl.workload_inputs(w5, want_exact=False)
+        qd, Wd = dev_bf16(q5.bits), dev_bf16(W5[0])
+        yf = torch.empty(w5.BH, w5.L, w5.m, dtype=torch.bfloat16, device="cuda")
+        fn = lambda: la.feature_map(qd, "favor", W=Wd, out=yf)  # noqa: E731
+    elif name in ("fwd_w2", "fwd_w4", "fwd_w5", "decode_w5"):
+        w = wl.WORKLOADS[int(name[-1])]
+        q, k, v, W = wl.workload_inputs(w, want_exact=False)
+        qd, kd, vd = dev_bf16(q.bits), dev_bf16(k.bits), dev_bf16(v.bits)
+        del q, k, v
+        Wd = dev_bf16(W[0]) if W is not None else None
+        f = la.Forward(qd, kd, vd, w.chunks[0], normalize=w.normalize, fmap=w.fmap, W=Wd,
+                       return_state=w.return_state)
+        fn = f.run
+        if name == "decode_w5":
+            f.run()
+            n = wl.DECODE_STREAMS * w.H
+            idx = torch.tensor([(s_ % w.B) * w.H + h for s_ in range(wl.DECODE_STREAMS) for h in range(w.H)],
+                               device="cuda")
+            S = f.S_final[idx].contiguous()
+            z = f.z_final[idx].contiguous()
+            pq, pk, pv = wl.decode_pool(w, n, pool=wl.DECODE_POOL)
+            dq, dk_, dv_ = dev_bf16(pq.bits), dev_bf16(pk.bits), dev_bf16(pv.bits)
+            o = torch.empty(n, w.d_v, dtype=torch.float32, device="cuda")
+            state = {"t": 0}
+
+            def fn():
+                t = state["t"] % wl.DECODE_POOL
+                la.recurrent_step(dq[t], dk_[t], dv_[t], S, z, fmap="favor", W=Wd, normalize=True, out=o)
+                state["t"] += 1
+    fn()
+    torch.cuda.synchronize()
+    ms = per_launch_ms(fn, reps)
+    log(f"{name}: {reps} calls, median {float(np.median(ms)):.4f} ms per call")
+
+
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_I8",
+                 "SQ_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", "GRBM_GUI_ACTIVE", "GRBM_COUNT")
+N_XCD, N_SIMD = 8, 1024  # MI355X: GRBM_GUI_ACTIVE is summed over the 8 XCDs; 256 CUs x 4 SIMDs
+
+
+def pmc_summary(dirs):
+    """Per-kernel table from rocprofv3 --pmc counter_collection.csv files (one
+    directory per --row run): mean over dispatches of the kernel duration, the
+    matrix-core busy fraction SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x
+    1024 SIMDs) and the executed matrix-core work (SQ_INSTS_VALU_MFMA_MOPS_* x 512)."""
+    import csv
+    import glob
+    from collections import defaultdict
+    lines = [f"{'row':18s} {'kernel':62s} {'disp':>4s} {'avg_us':>8s} {'clk_GHz':>7s} {'mfma_busy':>9s} "
+             f"{'bf16_GFLOP':>10s} {'i8_GOP':>8s} {'exec_TFLOP/s':>12s}"]
+    for d in dirs:
+        row = os.path.basename(os.path.normpath(d))
+        row = row[4:] if row.startswith("pmc_") else row
+        files = glob.glob(os.path.join(d, "*counter_collection.csv"))
+        if not files:
+            continue
+        vals = defaultdict(lambda: defaultdict(list))
+        dur = defaultdict(dict)
+        for r in csv.DictReader(open(files[0])):
+            name = r["Kernel_Name"].replace("void ", "")
+            k = name[:name.rfind("(")] if name.endswith(")") else name
+            vals[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
+            dur[k][r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        for k, c in vals.items():
+            mean = lambda n: sum(c[n]) / len(c[n]) if c[n] else 0.0  # noqa: E731
+            t_ns = sum(dur[k].values()) / len(dur[k])
+            gui = mean("GRBM_GUI_ACTIVE") / N_XCD
+            busy = mean("SQ_VALU_MFMA_BUSY_CYCLES") / (gui * N_SIMD) if gui else 0.0
+            bf = mean("SQ_INSTS_VALU_MFMA_MOPS_BF16") * 512
+            i8 = mean("SQ_INSTS_VALU_MFMA_MOPS_I8") * 512
+            lines.append(f"{row:18s} {k[:62]:62s} {len(dur[k]):4d} {t_ns / 1e3:8.1f} {gui / t_ns:7.2f} "
+                         f"{busy:9.3f} {bf / 1e9:10.2f} {i8 / 1e9:8.2f} {(bf + i8) / t_ns / 1e3:12.1f}")
+    return "\n".join(lines)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -503,7 +684,15 @@ def main():
                     help="seconds of untimed forward calls before the warmup steps (GPU clock ramp)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="end with a plain 512 MiB device copy (counter calibration under rocprofv3)")
+    ap.add_argument("--row", default=None,
+                    help="run only this row REPS times (for counter passes): " + ", ".join(ROWS))
+    ap.add_argument("--reps", type=int, default=10)
+    ap.add_argument("--pmc-summary", nargs="+", default=None, metavar="DIR",
+                    help="print the matrix-core counter table of rocprofv3 --pmc runs of --row (no GPU needed)")
     args = ap.parse_args()
+    if args.pmc_summary:
+        print(pmc_summary(args.pmc_summary))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); this build has no multi-GPU path",
               file=sys.stderr)
@@ -512,6 +701,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.row is not None:
+        run_row(args.row, args.reps)
+        return
     res, fwd = run_headline(args)
     del fwd
     torch.cuda.empty_cache()

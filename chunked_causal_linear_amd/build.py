@@ -1,8 +1,10 @@
 """Build liblinattn.so (HIP, gfx950) in-tree.
 
 Compiles every ``csrc/*.hip`` translation unit with hipcc in parallel into
-``_build/`` and links ``chunked_causal_linear_amd/liblinattn.so``.  The build
-runs on a machine without a GPU (hipcc cross-compiles for gfx950).
+``_build/`` and links ``chunked_causal_linear_amd/liblinattn.so``; the
+measurement probe (``csrc/probe/*.hip``, a matrix-core rate loop) goes into
+``libla_probe.so`` beside it.  The build runs on a machine without a GPU
+(hipcc cross-compiles for gfx950).
 
     python -m chunked_causal_linear_amd.build            # rebuild everything
     python -m chunked_causal_linear_amd.build --changed  # only stale objects
@@ -21,6 +23,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liblinattn.so")
+PROBE_LIB = os.path.join(PKG, "libla_probe.so")
 ROOT = os.path.dirname(PKG)
 INCLUDE = os.path.join(ROOT, "include")
 
@@ -40,21 +43,26 @@ CFLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-I" + INCLUDE
 FILE_FLAGS = {"la_pipe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
               "la_pipe_decay.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
               "la_pipe_decay_fac.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-              "la_fmap.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+              "la_fmap.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+              "probe/la_probe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _sources():
     return sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
+def _probe_sources():
+    return sorted("probe/" + f for f in os.listdir(os.path.join(CSRC, "probe")) if f.endswith(".hip"))
+
+
 def _headers_mtime() -> float:
     hs = [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hpp")]
-    hs.append(os.path.join(INCLUDE, "la.h"))
+    hs += [os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE) if f.endswith(".h")]
     return max(os.path.getmtime(h) for h in hs)
 
 
 def _compile(src: str) -> tuple:
-    obj = os.path.join(BUILD, src[:-4] + ".o")
+    obj = os.path.join(BUILD, src[:-4].replace("/", "_") + ".o")
     cmd = [HIPCC] + CFLAGS + FILE_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     t0 = time.time()
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -68,10 +76,11 @@ def build(changed_only: bool = False, jobs: int = None, verbose: bool = True) ->
         raise RuntimeError(f"hipcc not found at {HIPCC}")
     os.makedirs(BUILD, exist_ok=True)
     srcs = _sources()
+    probe_srcs = _probe_sources()
     todo = []
     hdr_t = _headers_mtime()
-    for s in srcs:
-        obj = os.path.join(BUILD, s[:-4] + ".o")
+    for s in srcs + probe_srcs:
+        obj = os.path.join(BUILD, s[:-4].replace("/", "_") + ".o")
         if changed_only and os.path.exists(obj):
             ot = os.path.getmtime(obj)
             if ot >= os.path.getmtime(os.path.join(CSRC, s)) and ot >= hdr_t:
@@ -90,15 +99,16 @@ def build(changed_only: bool = False, jobs: int = None, verbose: bool = True) ->
     if failed:
         msg = "\n".join(f"--- {s}\n{e}" for s, e in failed)
         raise RuntimeError("HIP build failed:\n" + msg)
-    objs = [os.path.join(BUILD, s[:-4] + ".o") for s in srcs]
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError("link failed:\n" + r.stderr)
-    os.replace(tmp, LIB)
-    if verbose:
-        print(f"[build] linked {LIB}", flush=True)
+    for lib, group in ((LIB, srcs), (PROBE_LIB, probe_srcs)):
+        objs = [os.path.join(BUILD, s[:-4].replace("/", "_") + ".o") for s in group]
+        tmp = lib + ".tmp"
+        cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("link failed:\n" + r.stderr)
+        os.replace(tmp, lib)
+        if verbose:
+            print(f"[build] linked {lib}", flush=True)
     return LIB
 
 

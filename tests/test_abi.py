@@ -16,8 +16,8 @@ HEADER = os.path.join(ROOT, "include", "la.h")
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
 
 
-def declared_functions():
-    src = open(HEADER, encoding="utf-8").read()
+def declared_functions(header=HEADER):
+    src = open(header, encoding="utf-8").read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(la_[a-z_0-9]+)\s*\(", src)))
 
@@ -32,6 +32,21 @@ def test_library_loads_and_exports_header_symbols():
     exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
     assert set(names) <= exported
     assert set(b.EXPORTS) == set(names)
+
+
+def test_probe_library_exports_and_rejects_bad_arguments():
+    """libla_probe.so (include/la_probe.h, the matrix-core rate probe) loads and
+    exports what its header declares; invalid arguments return -1 unlaunched."""
+    path = os.path.join(ROOT, "chunked_causal_linear_amd", "libla_probe.so")
+    names = declared_functions(os.path.join(ROOT, "include", "la_probe.h"))
+    assert names == ["la_probe_mfma"]
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert set(names) <= exported
+    lib = ctypes.CDLL(path)
+    lib.la_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    for kind, iters, grid, out_ in ((0, 0, 8, FAKE), (0, 8, 0, FAKE), (2, 8, 8, FAKE), (1, 8, 8, None)):
+        assert lib.la_probe_mfma(kind, iters, grid, out_, None) == -1
 
 
 def test_version_and_status_strings():
