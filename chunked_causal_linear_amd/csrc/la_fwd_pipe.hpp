@@ -219,6 +219,42 @@ __device__ __forceinline__ int work_index(int remap) {
 template <int I>
 using ic = std::integral_constant<int, I>;
 
+// The elu+1 pass over a landed tile of the streaming kernels.  A tile's Q (or
+// K) is 2 NC blocks of 64 16-byte pieces; copy wave h copies blocks
+// h NC .. h NC + NC - 1 of each tensor it moves.  The pieces of pair h are a
+// list: entry j is block h NC + (j mod NC) of the first tensor (j < NC) or of
+// the second.  A wave waits only for its own copies, so the entries a copy
+// wave maps before the barrier that follows every copy wave's wait must be
+// its own; the compute waves map after that barrier.  Both kernels take the
+// block of an entry from here, and the checks below run at compile time for
+// every instantiation.
+template <int NC>
+struct PieceList {
+    static constexpr bool first(int j) { return j < NC; }
+    static constexpr int block(int h, int j) { return h * NC + (j < NC ? j : j - NC); }
+    static constexpr bool copied_by(int h, int j) { return block(h, j) >= h * NC && block(h, j) < h * NC + NC; }
+};
+
+// Shares of a list of NE entries per pair (NE = 2 NC with two tensors, NC with
+// one): entries [0, EARLY) are mapped by the copy wave before the barrier,
+// the rest after it (by the copy wave or the compute wave).  True when the two
+// pairs' lists together name every block of every tensor exactly once and the
+// early entries are the copy wave's own.
+template <int NC, int NE, int EARLY>
+constexpr bool piece_shares_ok() {
+    if (EARLY < 0 || EARLY > NE || (NE != NC && NE != 2 * NC)) return false;
+    int seen[2][2 * NC] = {};
+    for (int h = 0; h < 2; ++h)
+        for (int j = 0; j < NE; ++j) {
+            seen[PieceList<NC>::first(j) ? 0 : 1][PieceList<NC>::block(h, j)] += 1;
+            if (j < EARLY && !PieceList<NC>::copied_by(h, j)) return false;
+        }
+    for (int t = 0; t < NE / NC; ++t)
+        for (int b = 0; b < 2 * NC; ++b)
+            if (seen[t][b] != 1) return false;
+    return true;
+}
+
 }  // namespace pipe
 
 template <int DK, int DVT, int CH, bool SCALED, bool NORM, bool PHI, int DECAY>
@@ -297,6 +333,8 @@ void chunked_fwd_pipe(FwdParams p) {
     constexpr int NP = 2 * NCQ;
     constexpr int NPC = DECAY ? NP / 8 : (TT > 64 ? NP / 4 : NP / 2), NPK = NP - NPC;
     constexpr bool MAP2 = PHI && NPC > 0;  // the compute waves map too
+    static_assert(!PHI || piece_shares_ok<NCQ, NP, NPK>(),
+                  "elu+1 shares: a copy wave maps only pieces it copied before the barrier; every piece once");
     auto phi_blocks = [&](StageT& s, int valid, auto j0_, auto count) __attribute__((always_inline)) {
         constexpr int J0 = decltype(j0_)::value, N = decltype(count)::value;
         // four pieces in flight at a time (bounded registers)
@@ -306,13 +344,13 @@ void chunked_fwd_pipe(FwdParams p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int j = J0 + i0 + i;
-                const int slot = (h * NCQ + (j < NCQ ? j : j - NCQ)) * WAVE + lane;
+                const int slot = PieceList<NCQ>::block(h, j) * WAVE + lane;
                 if (i0 + i < N) x[i] = *reinterpret_cast<const uint4*>((j < NCQ ? s.q : s.k) + slot * 8);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int j = J0 + i0 + i;
-                const int slot = (h * NCQ + (j < NCQ ? j : j - NCQ)) * WAVE + lane;
+                const int slot = PieceList<NCQ>::block(h, j) * WAVE + lane;
                 if (i0 + i < N) {
                     const bool live = j < NCQ || slot / QSEG < valid;  // K rows past the end become zero
                     *reinterpret_cast<uint4*>((j < NCQ ? s.q : s.k) + slot * 8) =

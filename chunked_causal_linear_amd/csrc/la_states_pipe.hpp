@@ -141,13 +141,19 @@ void chunk_states_pipe(StatesParams p) {
     // flight) and FB more after B'(t), while the products of tile t run;
     // compute wave h maps the last FC between B(t) and B'(t).
     constexpr int FC = NCK / 4, FA = NCK / 4, FB = NCK - FC - FA;
+    // FA entries before B'(t - 1) (own copies only); FB after it, when both
+    // copy waves have waited for the tile; FC by the compute wave after B(t).
+    // A stage is refilled only after B(t) of the tile it held, and with two
+    // stages the tile mapped is the one just issued into it.
+    static_assert(KIND != KIND_ELU || (piece_shares_ok<NCK, NCK, FA>() && FB >= 0 && FC >= 0),
+                  "elu+1 shares: a copy wave maps only pieces it copied before the barrier; every piece once");
     // (decay: row r of the tile weighs gamma^(n - 1 - r), n its rows before the
     // run's end)
     auto phi_blocks = [&](StageT& s, int valid, int n, auto j0_, auto count) __attribute__((always_inline)) {
         constexpr int J0 = decltype(j0_)::value, N = decltype(count)::value;
 #pragma unroll
         for (int i = 0; i < N; ++i) {
-            const int slot = (h * NCK + J0 + i) * WAVE + lane;
+            const int slot = PieceList<NCK>::block(h, J0 + i) * WAVE + lane;
             const uint4 x = *reinterpret_cast<const uint4*>(s.k + slot * 8);
             uint4 hi, lo;
             const float wr = DECAY ? __builtin_amdgcn_exp2f((float)(n - 1 - slot / QSEG) * p.log2_gamma) : 1.0f;

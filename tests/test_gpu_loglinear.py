@@ -8,7 +8,7 @@ import pytest
 import chunked_causal_linear_amd as la
 import oracle
 import workloads as wl
-from tests.gpu_helpers import assert_close, dev_input, host, log, torch_cuda
+from tests.gpu_helpers import assert_close, dev_bf16, dev_input, host, log, torch_cuda
 
 pytestmark = pytest.mark.gpu
 
@@ -39,3 +39,24 @@ def test_loglinear_unit_weights_is_linear_attention():
     o = la.loglinear_forward(dev_input(q), dev_input(k), dev_input(v), torch.from_numpy(lam).cuda())
     ref = np.stack([oracle.chunked(q.exact[h], k.exact[h], v.exact[h], 64)[0] for h in range(2)])
     assert_close(host(o), ref, what="o")
+
+
+def test_loglinear_benchmarked_shape():
+    """The shape the benchmark times: 128 heads x 8192 rows, d = 128, 14 levels
+    (128 chunks: bucket sums of 1..64 chunks, the top pyramid level), checked on
+    three sampled heads."""
+    torch = torch_cuda()
+    w = wl.WORKLOADS[3]
+    q, k, v, _ = wl.workload_inputs(w, want_exact=False)
+    nl = la.loglinear_levels(w.L)
+    assert nl == 14
+    lam = wl.loglinear_weights(3, w.BH, w.L, nl)
+    log(f"loglinear benchmarked shape BH={w.BH} L={w.L} levels={nl}")
+    o = host(la.loglinear_forward(dev_bf16(q.bits), dev_bf16(k.bits), dev_bf16(v.bits),
+                                  torch.from_numpy(lam).cuda()))
+    del q, k, v
+    for bh in (0, 77, w.BH - 1):
+        qh, kh, vh = wl.head_inputs(w, bh)
+        ref = oracle.loglinear_chunked(qh.exact, kh.exact, vh.exact, lam[bh].astype(np.float64), 64)
+        worst = assert_close(o[bh], ref, what=f"head {bh}")
+        log(f"head {bh} worst ratio {worst:.3f}")
