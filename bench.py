@@ -551,7 +551,7 @@ def run_extras(args, out):
 
 ROWS = ("fwd_w3_C32", "fwd_w3_C64", "fwd_w3_C128", "fwd_w3_int8_C64", "states_w3_C64", "states_w3_C1024",
         "scan_w3_C64", "fmap_favor_w5", "fwd_w2", "fwd_w4", "fwd_w5", "decode_w5", "mfma_peak_bf16", "mfma_peak_i8",
-        "copy_512MiB")
+        "copy_512MiB", "delta_w3", "delta_w3_gated", "delta_decode_w3")
 
 
 def run_row(name: str, reps: int):
@@ -589,6 +589,24 @@ def run_row(name: str, reps: int):
         else:
             S, _ = la.chunk_states(kd, vd, 64)
             fn = lambda: la.state_scan(S, None, want_final=False)  # noqa: E731
+    elif name.startswith("delta"):
+        gated = name != "delta_w3"
+        q, k, v, beta, alpha = wl.delta_inputs(3, w3.BH, w3.L, w3.d_k, w3.d_v, gated, want_exact=False)
+        bd = torch.from_numpy(beta).cuda()
+        ad = torch.from_numpy(alpha).cuda() if gated else None
+        qd, kd, vd = dev_bf16(q.bits), dev_bf16(k.bits), dev_bf16(v.bits)
+        del q, k, v
+        if name == "delta_decode_w3":
+            # one decode step on every head's final state of the forward (128 states of 128 x 128)
+            f = la.DeltaForward(qd, kd, vd, bd, ad, return_state=True)
+            f.run()
+            S, t0 = f.S_final, w3.L - 1
+            o = torch.empty(w3.BH, w3.d_v, dtype=torch.float32, device="cuda")
+            qs, ks, vs = (x[:, t0].contiguous() for x in (qd, kd, vd))
+            bs, as_ = bd[:, t0].contiguous(), ad[:, t0].contiguous()
+            fn = lambda: la.recurrent_step_delta(qs, ks, vs, S, bs, as_, out=o)  # noqa: E731
+        else:
+            fn = la.DeltaForward(qd, kd, vd, bd, ad).run
     elif name == "fwd_w3_int8_C64":
         qi, ki, vi = wl.random_case(33, w3.BH, w3.L, 128, 128, "i8")
         tq, tk, tv = (torch.from_numpy(t.bits).cuda() for t in (qi, ki, vi))

@@ -28,6 +28,8 @@ EXPORTS = (
     "la_chunked_forward_workspace", "la_chunked_forward_group", "la_recurrent_step", "la_status_string", "la_last_error",
     "la_version", "la_chunk_states_decay", "la_state_scan_decay", "la_chunk_output_decay", "la_chunked_forward_decay",
     "la_recurrent_step_decay", "la_loglinear_forward", "la_loglinear_forward_workspace", "la_loglinear_levels",
+    "la_chunked_forward_delta", "la_chunked_forward_delta_workspace", "la_delta_chunk_transform",
+    "la_recurrent_step_delta",
 )
 
 
@@ -71,7 +73,14 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.la_loglinear_forward_workspace.restype = sz
     lib.la_loglinear_levels.argtypes = [i64]
     lib.la_loglinear_levels.restype = i64
-    for name in ("la_loglinear_forward", "la_feature_map", "la_chunk_states", "la_state_scan", "la_chunk_output",
+    lib.la_chunked_forward_delta.argtypes = [vp, vp, vp, i32, i64, i64, i64, i64, i64, vp, vp, vp, i32, vp, vp, sz,
+                                             vp]
+    lib.la_chunked_forward_delta_workspace.argtypes = [i32, i64, i64, i64, i64, i64]
+    lib.la_chunked_forward_delta_workspace.restype = sz
+    lib.la_delta_chunk_transform.argtypes = [vp, vp, vp, i32, i64, i64, i64, i64, vp, vp, vp]
+    lib.la_recurrent_step_delta.argtypes = [vp, vp, vp, i32, i64, i64, i64, vp, vp, vp, vp, i32, vp]
+    for name in ("la_chunked_forward_delta", "la_delta_chunk_transform", "la_recurrent_step_delta",
+                 "la_loglinear_forward", "la_feature_map", "la_chunk_states", "la_state_scan", "la_chunk_output",
                  "la_chunked_forward",
                  "la_recurrent_step", "la_chunk_states_decay", "la_state_scan_decay", "la_chunk_output_decay",
                  "la_chunked_forward_decay", "la_recurrent_step_decay"):
@@ -368,4 +377,80 @@ def recurrent_step(q, k, v, S, z=None, fmap: str = "identity", W=None, in_scale:
         _check(lib().la_recurrent_step(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dtype_code(q), n, d_in, d_v,
                                        _fmap_code(fmap), _dev(W, "W"), m, float(in_scale), int(normalize),
                                        _dev(S, "S"), _dev(z, "z"), _dev(out, "o"), _dtype_code(out), _stream_ptr()))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# the delta rule (include/la.h: la_chunked_forward_delta and its companions)
+# ---------------------------------------------------------------------------
+def _gates(beta, alpha, shape, device):
+    torch = _torch()
+    for name, t in (("beta", beta), ("alpha", alpha)):
+        if t is None:
+            continue
+        if t.dtype != torch.float32 or tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} must be float32 {tuple(shape)}")
+        _dev(t, name)
+
+
+class DeltaForward:
+    """A planned delta-rule forward (chunks of 64) with its output, final-state
+    and workspace buffers; ``run()`` enqueues only the library's kernels."""
+
+    def __init__(self, q, k, v, beta, alpha=None, C: int = 64, return_state: bool = False):
+        torch = _torch()
+        BH, L, d_k = q.shape
+        d_v = v.shape[-1]
+        _gates(beta, alpha, (BH, L), q.device)
+        self.q, self.k, self.v, self.beta, self.alpha, self.C = q, k, v, beta, alpha, C
+        self.shape = (BH, L, d_k, d_v)
+        self.o = torch.empty(BH, L, d_v, dtype=torch.bfloat16, device=q.device)
+        self.S_final = torch.empty(BH, d_k, d_v, dtype=torch.float32, device=q.device) if return_state else None
+        ws = int(lib().la_chunked_forward_delta_workspace(_dtype_code(q), BH, L, d_k, d_v, C))
+        self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=q.device)
+        self.ws_bytes = ws
+        for name, t in (("q", q), ("k", k), ("v", v)):
+            _dev(t, name)
+
+    def run(self):
+        BH, L, d_k, d_v = self.shape
+        _check(lib().la_chunked_forward_delta(
+            self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), _dtype_code(self.q), BH, L, d_k, d_v, self.C,
+            self.beta.data_ptr(), self.alpha.data_ptr() if self.alpha is not None else None, self.o.data_ptr(),
+            _dtype_code(self.o), self.S_final.data_ptr() if self.S_final is not None else None,
+            self.workspace.data_ptr(), self.ws_bytes, _stream_ptr()))
+        return self.o
+
+
+def delta_forward(q, k, v, beta, alpha=None, C: int = 64, return_state: bool = False):
+    """O (and, with return_state, the final state) of the (gated) delta rule; beta, alpha [BH, L] float32."""
+    f = DeltaForward(q, k, v, beta, alpha, C, return_state)
+    o = f.run()
+    return (o, f.S_final) if return_state else o
+
+
+def delta_chunk_transform(k, beta, alpha=None, C: int = 64):
+    """Per-chunk T [BH, N, 64, 64] (bf16, columns in operand order) and gate log products lg [BH, N, 64]."""
+    torch = _torch()
+    BH, L, d_k = k.shape
+    _gates(beta, alpha, (BH, L), k.device)
+    N = (L + 63) // 64
+    T = torch.empty(BH, N, 64, 64, dtype=torch.bfloat16, device=k.device)
+    lg = torch.empty(BH, N, 64, dtype=torch.float32, device=k.device)
+    _check(lib().la_delta_chunk_transform(_dev(k, "k"), _dev(beta, "beta"), _dev(alpha, "alpha"), _dtype_code(k), BH,
+                                          L, d_k, C, _dev(T, "T"), _dev(lg, "lg"), _stream_ptr()))
+    return T, lg
+
+
+def recurrent_step_delta(q, k, v, S, beta, alpha=None, out=None):
+    """One (gated) delta-rule decode step over n states; S [n, d_k, d_v] fp32 updates in place."""
+    torch = _torch()
+    n, d_k = q.shape
+    d_v = v.shape[-1]
+    _gates(beta, alpha, (n,), q.device)
+    if out is None:
+        out = torch.empty(n, d_v, dtype=torch.float32, device=q.device)
+    _check(lib().la_recurrent_step_delta(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dtype_code(q), n, d_k, d_v,
+                                         _dev(beta, "beta"), _dev(alpha, "alpha"), _dev(S, "S"), _dev(out, "o"),
+                                         _dtype_code(out), _stream_ptr()))
     return out

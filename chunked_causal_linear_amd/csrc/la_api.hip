@@ -899,4 +899,119 @@ la_status la_recurrent_step_decay(const void* q, const void* k, const void* v, l
                       stream);
 }
 
+// ---------------------------------------------------------------------------
+// the delta rule
+// ---------------------------------------------------------------------------
+static constexpr int64_t kDeltaChunk = 64;
+
+static la_status delta_sizes(la_dtype in_dt, int64_t BH, int64_t L, int64_t d_k, int64_t d_v, int64_t C) {
+    if (BH < 1 || L < 1 || d_k < 1 || d_v < 1) return fail(LA_ERR_INVALID_ARG, "sizes must be positive");
+    if (in_dt != LA_BF16) return fail(LA_ERR_UNSUPPORTED, "the delta rule takes LA_BF16 inputs");
+    if (C != kDeltaChunk) return fail(LA_ERR_UNSUPPORTED, "the delta-rule forward runs chunks of 64 rows (C = 64)");
+    if (d_k != 64 && d_k != 128) return fail(LA_ERR_UNSUPPORTED, "the delta-rule forward needs d_k in {64, 128}");
+    if (d_v % 64 != 0 || !pow2_in(d_v, 64, 256)) return fail(LA_ERR_UNSUPPORTED, "the delta-rule forward needs d_v in {64, 128, 256}");
+    if (BH * L > ((int64_t)1 << 40) || BH * (d_v / 64) > 0x7FFFFFFFLL || BH * cdiv(L, kDeltaChunk) > 0x7FFFFFFFLL)
+        return fail(LA_ERR_UNSUPPORTED, "problem too large");
+    return LA_OK;
+}
+
+static size_t delta_ws_T(int64_t BH, int64_t N) { return align256((size_t)BH * N * kDeltaChunk * kDeltaChunk * 2); }
+static size_t delta_ws_lg(int64_t BH, int64_t N) { return align256((size_t)BH * N * kDeltaChunk * 4); }
+
+size_t la_chunked_forward_delta_workspace(la_dtype in_dt, int64_t BH, int64_t L, int64_t d_k, int64_t d_v,
+                                          int64_t C) {
+    char saved[sizeof(g_last_error)];
+    memcpy(saved, g_last_error, sizeof(saved));
+    const la_status st = delta_sizes(in_dt, BH, L, d_k, d_v, C);
+    memcpy(g_last_error, saved, sizeof(saved));
+    if (st != LA_OK) return 0;
+    const int64_t N = cdiv(L, kDeltaChunk);
+    return delta_ws_T(BH, N) + delta_ws_lg(BH, N);
+}
+
+la_status la_delta_chunk_transform(const void* k, const float* beta, const float* alpha, la_dtype in_dt,
+                                   int64_t BH, int64_t L, int64_t d_k, int64_t C, void* T, float* lg,
+                                   la_stream_t stream) {
+    g_last_error[0] = 0;
+    if (k == nullptr || beta == nullptr || T == nullptr || lg == nullptr)
+        return fail(LA_ERR_INVALID_ARG, "k, beta, T and lg must not be NULL");
+    la_status st = delta_sizes(in_dt, BH, L, d_k, 64, C);
+    if (st != LA_OK) return st;
+    la::DeltaPrepParams p{};
+    p.k = static_cast<const unsigned short*>(k);
+    p.beta = beta;
+    p.alpha = alpha;
+    p.T = static_cast<unsigned short*>(T);
+    p.lg = lg;
+    p.BH = BH;
+    p.L = L;
+    p.N = cdiv(L, kDeltaChunk);
+    p.dk = (int)d_k;
+    return hip_status(la::run_delta_transform(p, (hipStream_t)stream), "delta transform launch");
+}
+
+la_status la_chunked_forward_delta(const void* q, const void* k, const void* v, la_dtype in_dt, int64_t BH,
+                                   int64_t L, int64_t d_k, int64_t d_v, int64_t C, const float* beta,
+                                   const float* alpha, void* o, la_dtype out_dt, float* S_final, void* workspace,
+                                   size_t ws_bytes, la_stream_t stream) {
+    g_last_error[0] = 0;
+    if (q == nullptr || k == nullptr || v == nullptr || beta == nullptr || o == nullptr)
+        return fail(LA_ERR_INVALID_ARG, "q, k, v, beta and o must not be NULL");
+    la_status st = delta_sizes(in_dt, BH, L, d_k, d_v, C);
+    if (st != LA_OK) return st;
+    if (out_dt != LA_BF16) return fail(LA_ERR_UNSUPPORTED, "the delta-rule forward writes LA_BF16 outputs");
+    const int64_t N = cdiv(L, kDeltaChunk);
+    const size_t need = delta_ws_T(BH, N) + delta_ws_lg(BH, N);
+    if (workspace == nullptr || ws_bytes < need)
+        return fail(LA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : (size_t)0);
+    char* ws = static_cast<char*>(workspace);
+    unsigned short* T = reinterpret_cast<unsigned short*>(ws);
+    float* lg = reinterpret_cast<float*>(ws + delta_ws_T(BH, N));
+    st = la_delta_chunk_transform(k, beta, alpha, in_dt, BH, L, d_k, C, T, lg, stream);
+    if (st != LA_OK) return st;
+    la::DeltaFwdParams p{};
+    p.q = static_cast<const unsigned short*>(q);
+    p.k = static_cast<const unsigned short*>(k);
+    p.v = static_cast<const unsigned short*>(v);
+    p.T = T;
+    p.lg = lg;
+    p.o = static_cast<unsigned short*>(o);
+    p.S_final = S_final;
+    p.BH = BH;
+    p.L = L;
+    p.N = N;
+    p.dk = (int)d_k;
+    p.dv = (int)d_v;
+    p.n_dvt = (int)(d_v / 64);
+    p.xcd_remap = xcd_ok(BH * p.n_dvt);
+    return hip_status(la::run_delta_fwd(p, (hipStream_t)stream), "delta forward launch");
+}
+
+la_status la_recurrent_step_delta(const void* q, const void* k, const void* v, la_dtype in_dt, int64_t n_states,
+                                  int64_t d_k, int64_t d_v, const float* beta, const float* alpha, float* S,
+                                  void* o, la_dtype out_dt, la_stream_t stream) {
+    g_last_error[0] = 0;
+    if (q == nullptr || k == nullptr || v == nullptr || beta == nullptr || S == nullptr || o == nullptr)
+        return fail(LA_ERR_INVALID_ARG, "q, k, v, beta, S and o must not be NULL");
+    if (n_states < 1) return fail(LA_ERR_INVALID_ARG, "n_states must be positive");
+    if (n_states > 0x7FFFFFFFLL) return fail(LA_ERR_UNSUPPORTED, "too many states");
+    if (in_dt != LA_BF16) return fail(LA_ERR_UNSUPPORTED, "the delta rule takes LA_BF16 inputs");
+    if (out_dt != LA_BF16 && out_dt != LA_F32) return fail(LA_ERR_UNSUPPORTED, "o must be LA_BF16 or LA_F32");
+    if (!pow2_in(d_k, 16, 256) || !pow2_in(d_v, 16, 256))
+        return fail(LA_ERR_UNSUPPORTED, "d_k and d_v must be 16..256, powers of two");
+    la::DeltaStepParams p{};
+    p.q = static_cast<const unsigned short*>(q);
+    p.k = static_cast<const unsigned short*>(k);
+    p.v = static_cast<const unsigned short*>(v);
+    p.beta = beta;
+    p.alpha = alpha;
+    p.S = S;
+    p.o = o;
+    p.n = n_states;
+    p.dk = (int)d_k;
+    p.dv = (int)d_v;
+    p.out_f32 = out_dt == LA_F32;
+    return hip_status(la::run_delta_step(p, (hipStream_t)stream), "delta step launch");
+}
+
 }  // extern "C"

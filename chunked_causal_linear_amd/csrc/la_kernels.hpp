@@ -140,6 +140,54 @@ struct DecodeParams {
     float gamma;    // decayed recurrence: S = gamma S + k^T v, z = gamma z + k (1: none)
 };
 
+// The delta rule (la_delta.hip).
+struct DeltaStepParams {
+    const unsigned short* q;  // [n, dk]
+    const unsigned short* k;  // [n, dk]
+    const unsigned short* v;  // [n, dv]
+    const float* beta;        // [n] write strengths
+    const float* alpha;       // [n] gates, or null (1)
+    float* S;                 // [n, dk, dv], read and updated
+    void* o;                  // [n, dv] bf16 or f32
+    int64_t n;
+    int dk;
+    int dv;
+    int out_f32;
+};
+
+struct DeltaPrepParams {
+    const unsigned short* k;  // [BH, L, dk]
+    const float* beta;        // [BH, L]
+    const float* alpha;       // [BH, L] or null
+    unsigned short* T;        // [BH, N, 64, 64] per-chunk transforms (columns in operand order)
+    float* lg;                // [BH, N, 64] log2 of the gates' product up to each row of the chunk
+    int64_t BH;
+    int64_t L;
+    int64_t N;                // chunks of 64 rows
+    int dk;
+};
+
+struct DeltaFwdParams {
+    const unsigned short* q;  // [BH, L, dk]
+    const unsigned short* k;
+    const unsigned short* v;  // [BH, L, dv]
+    const unsigned short* T;  // from the transform
+    const float* lg;
+    unsigned short* o;        // [BH, L, dv] bf16
+    float* S_final;           // [BH, dk, dv] or null
+    int64_t BH;
+    int64_t L;
+    int64_t N;
+    int dk;
+    int dv;
+    int n_dvt;                // value tiles of 64 columns
+    int xcd_remap;
+};
+
+hipError_t run_delta_step(const DeltaStepParams& p, hipStream_t s);
+hipError_t run_delta_transform(const DeltaPrepParams& p, hipStream_t s);
+hipError_t run_delta_fwd(const DeltaFwdParams& p, hipStream_t s);
+
 // Log-linear attention: bucket pyramid and the output kernel.
 struct LogLinParams {
     const unsigned short* q;  // [BH, L, dk]

@@ -305,6 +305,77 @@ size_t la_loglinear_forward_workspace(la_dtype in_dt, int64_t BH, int64_t L, int
 /* Levels a sequence of L tokens uses: 1 + the bit length of L - 1 (0 for L < 1). */
 int64_t la_loglinear_levels(int64_t L);
 
+/*
+ * The delta rule and its gated form (page "Kimi K3 と Qwen 3.8 の Attention 機構
+ * 比較分析" (news.ainew.jp): section 3.1, equation (14): before writing, look up
+ * what the current key maps to in the state, erase that old prediction along
+ * the key, write the new value; section 2.4: the gated form adds a global
+ * decay of the whole state).  With the state S (d_k x d_v, read as o = q S),
+ * a write strength beta_t and a gate alpha_t per token:
+ *     u_t = beta_t (v_t - alpha_t S_{t-1}^T k_t)
+ *     S_t = alpha_t S_{t-1} + k_t u_t^T  = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = q_t^T S_t                     (read after the update)
+ * alpha = 1 (alpha == NULL) is the delta rule without the gate; beta = 1 the
+ * page's full-strength erase.  No feature map and no normaliser; keys are used
+ * as given (the recurrence is stable for beta |k|^2 <= 2, e.g. unit keys).
+ * Gates must lie in (0, 1]; a gate at or below 2^-100 acts as 2^-100.
+ *
+ * la_chunked_forward_delta - the causal forward, chunk by chunk.  Inside a
+ * chunk of n rows starting from the state P, with g_i the product of the
+ * chunk's gates up to row i, the recurrence unrolls to the unit
+ * lower-triangular system (I + A) U = diag(beta) (V - diag(g) K P),
+ * A[i][j] = beta_i (k_i . k_j) g_i / g_j (j < i), and
+ *     O = diag(g) Q P + (tril(Q K^T) * G) U,   G[i][j] = g_i / g_j,
+ *     P <- g_n P + K^T diag(g_n / g) U.
+ *   q, k [BH, L, d_k], v [BH, L, d_v]: LA_BF16, d_k in {64, 128}, d_v in
+ *        {64, 128, 256}; C must be 64.
+ *   beta [BH, L] float32 (device); alpha [BH, L] float32 (device) or NULL.
+ *   o    [BH, L, d_v] LA_BF16.  S_final [BH, d_k, d_v] float32 or NULL: the
+ *        state after the last token.  The initial state is zero.
+ *   workspace  la_chunked_forward_delta_workspace(...) bytes: the per-chunk
+ *        transforms T = (I + A)^-1 diag(beta) and the gates' log products.
+ * Errors: LA_ERR_INVALID_ARG (NULL pointer, non-positive size),
+ * LA_ERR_UNSUPPORTED (other types, widths or chunk sizes), LA_ERR_WORKSPACE;
+ * nothing is launched on an error.
+ */
+la_status la_chunked_forward_delta(const void* q, const void* k, const void* v, la_dtype in_dt, int64_t BH,
+                                   int64_t L, int64_t d_k, int64_t d_v, int64_t C, const float* beta,
+                                   const float* alpha, void* o, la_dtype out_dt, float* S_final, void* workspace,
+                                   size_t ws_bytes, la_stream_t stream);
+size_t la_chunked_forward_delta_workspace(la_dtype in_dt, int64_t BH, int64_t L, int64_t d_k, int64_t d_v,
+                                          int64_t C);
+
+/*
+ * la_delta_chunk_transform - the forward's first kernel alone: for every chunk
+ * n of 64 rows (N = ceil(L / 64), the last one padded with zero keys and zero
+ * strengths),
+ *   T[bh, n] = (I + A)^-1 diag(beta)   (64 x 64, lower triangular, bf16) and
+ *   lg[bh, n, i] = log2 of the product of the chunk's gates over rows 0..i
+ *   (float32; rows past the end repeat the last).
+ * T's row i holds column j at position p(j): inside each 32-column half, j with
+ * j mod 32 = 4a + b < 16 at 8a + b, and j mod 32 = 16 + 4a + b at 8a + 4 + b
+ * (the key order of the forward's matrix-core operands).
+ *   k [BH, L, d_k] LA_BF16 (d_k in {64, 128}); beta, alpha as above; C = 64.
+ *   T  [BH, N, 64, 64] LA_BF16 (device); lg [BH, N, 64] float32 (device).
+ */
+la_status la_delta_chunk_transform(const void* k, const float* beta, const float* alpha, la_dtype in_dt,
+                                   int64_t BH, int64_t L, int64_t d_k, int64_t C, void* T, float* lg,
+                                   la_stream_t stream);
+
+/*
+ * la_recurrent_step_delta - one decode step of the (gated) delta rule for
+ * n_states independent states, in place:
+ *   u = beta (v - alpha S^T k);  S = alpha S + k u^T;  o = q^T S.
+ *   q, k [n_states, d_k], v [n_states, d_v]: LA_BF16, d_k, d_v in {16..256}
+ *        powers of two.  beta [n_states] float32 (device); alpha [n_states]
+ *        float32 (device) or NULL.
+ *   S    [n_states, d_k, d_v] float32, read and updated.
+ *   o    [n_states, d_v] LA_F32 or LA_BF16.
+ */
+la_status la_recurrent_step_delta(const void* q, const void* k, const void* v, la_dtype in_dt, int64_t n_states,
+                                  int64_t d_k, int64_t d_v, const float* beta, const float* alpha, float* S,
+                                  void* o, la_dtype out_dt, la_stream_t stream);
+
 /* Static description of a status code. */
 const char* la_status_string(la_status s);
 /* Thread-local description of the last failure on this thread ("" if none). */

@@ -264,3 +264,49 @@ def test_loglinear_entry_point_errors():
     assert call(in_dt=b.LA_I8) == b.LA_ERR_UNSUPPORTED
     assert call(out_dt=b.LA_F32) == b.LA_ERR_UNSUPPORTED
     assert call() == b.LA_ERR_WORKSPACE
+
+
+def test_delta_entry_point_errors():
+    """The delta rule: workspace size (per-chunk 64 x 64 bf16 transforms and the
+    gates' log products) and argument checks, all before any launch."""
+    lib = la.lib()
+    ws = lib.la_chunked_forward_delta_workspace(b.LA_BF16, 128, 8192, 128, 128, 64)
+    assert ws == 128 * 128 * 64 * 64 * 2 + 128 * 128 * 64 * 4
+    assert lib.la_chunked_forward_delta_workspace(b.LA_BF16, 2, 100, 64, 64, 64) == 2 * 2 * 8192 + 2 * 2 * 256
+    assert lib.la_chunked_forward_delta_workspace(b.LA_BF16, 2, 100, 64, 64, 32) == 0  # chunks of 64 only
+    assert lib.la_chunked_forward_delta_workspace(b.LA_BF16, 2, 100, 256, 64, 64) == 0
+    assert lib.la_chunked_forward_delta_workspace(b.LA_I8, 2, 100, 64, 64, 64) == 0
+
+    def fwd(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, in_dt=b.LA_BF16, BH=2, L=100, d_k=64, d_v=64, C=64, beta=FAKE, alpha=None,
+                 o=FAKE, out_dt=b.LA_BF16, S=None, ws=FAKE, ws_bytes=0)
+        a.update(kw)
+        return lib.la_chunked_forward_delta(a["q"], a["k"], a["v"], a["in_dt"], a["BH"], a["L"], a["d_k"], a["d_v"],
+                                            a["C"], a["beta"], a["alpha"], a["o"], a["out_dt"], a["S"], a["ws"],
+                                            a["ws_bytes"], None)
+    assert fwd(beta=None) == b.LA_ERR_INVALID_ARG
+    assert fwd(L=0) == b.LA_ERR_INVALID_ARG
+    assert fwd(C=128) == b.LA_ERR_UNSUPPORTED
+    assert fwd(d_k=32) == b.LA_ERR_UNSUPPORTED
+    assert fwd(d_v=32) == b.LA_ERR_UNSUPPORTED
+    assert fwd(in_dt=b.LA_I8) == b.LA_ERR_UNSUPPORTED
+    assert fwd(out_dt=b.LA_F32) == b.LA_ERR_UNSUPPORTED
+    assert fwd(ws_bytes=100) == b.LA_ERR_WORKSPACE
+    assert b"workspace" in lib.la_last_error()
+    assert lib.la_delta_chunk_transform(FAKE, None, None, b.LA_BF16, 2, 100, 64, 64, FAKE, FAKE, None) == \
+        b.LA_ERR_INVALID_ARG
+    assert lib.la_delta_chunk_transform(FAKE, FAKE, None, b.LA_BF16, 2, 100, 64, 16, FAKE, FAKE, None) == \
+        b.LA_ERR_UNSUPPORTED
+
+    def step(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, in_dt=b.LA_BF16, n=4, d_k=64, d_v=64, beta=FAKE, alpha=None, S=FAKE, o=FAKE,
+                 out_dt=b.LA_F32)
+        a.update(kw)
+        return lib.la_recurrent_step_delta(a["q"], a["k"], a["v"], a["in_dt"], a["n"], a["d_k"], a["d_v"], a["beta"],
+                                           a["alpha"], a["S"], a["o"], a["out_dt"], None)
+    assert step(S=None) == b.LA_ERR_INVALID_ARG
+    assert step(n=0) == b.LA_ERR_INVALID_ARG
+    assert step(d_k=48) == b.LA_ERR_UNSUPPORTED
+    assert step(d_v=512) == b.LA_ERR_UNSUPPORTED
+    assert step(out_dt=b.LA_I32) == b.LA_ERR_UNSUPPORTED
+    assert step(in_dt=b.LA_F32) == b.LA_ERR_UNSUPPORTED

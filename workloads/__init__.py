@@ -236,3 +236,52 @@ def random_case(seed: int, BH: int, L: int, d_in: int, d_v: int, dtype: str,
     k = full_tensor(1000 + seed, TENSOR_K, BH, L, d_in, dtype, scale)
     v = full_tensor(1000 + seed, TENSOR_V, BH, L, d_v, dtype, scale)
     return q, k, v
+
+
+# ---------------------------------------------------------------------------
+# Inputs of the delta rule (the Kimi/Qwen page's erase-then-write update):
+# unit keys as in its two-key example, write strengths and gates per token.
+# ---------------------------------------------------------------------------
+TENSOR_BETA, TENSOR_ALPHA = 7, 8
+
+
+def unit_rows_bf16(rng: np.random.Generator, shape) -> np.ndarray:
+    """Standard normal rows divided by their Euclidean norm (float64), rounded to
+    bf16: unit vectors up to the bf16 rounding of each entry."""
+    x = rng.standard_normal(size=shape)
+    x = x / np.linalg.norm(x, axis=-1, keepdims=True)
+    return f32_to_bf16_bits(x.astype(np.float32))
+
+
+def delta_inputs(seed: int, BH: int, L: int, d_k: int, d_v: int, gated: bool,
+                 beta_lo: float = 0.25, alpha_lo: float = 0.9, want_exact: bool = True):
+    """Seeded delta-rule inputs, per (batch*head) slice: q ~ N(0,1)/sqrt(d_k) and
+    v ~ N(0,1)/sqrt(d_k) in bf16; unit keys (unit_rows_bf16); write strengths
+    beta ~ U(beta_lo, 1) and, when gated, gates alpha ~ U(alpha_lo, 1), float32
+    [BH, L].  Returns (q, k, v Tensors, beta, alpha or None)."""
+    scale = 1.0 / math.sqrt(d_k)
+    q = full_tensor(2000 + seed, TENSOR_Q, BH, L, d_k, "bf16", scale, want_exact)
+    v = full_tensor(2000 + seed, TENSOR_V, BH, L, d_v, "bf16", scale, want_exact)
+    kb = np.empty((BH, L, d_k), dtype=np.uint16)
+    beta = np.empty((BH, L), dtype=np.float32)
+    alpha = np.empty((BH, L), dtype=np.float32) if gated else None
+    for bh in range(BH):
+        kb[bh] = unit_rows_bf16(np.random.default_rng([2000 + seed, TENSOR_K, bh]), (L, d_k))
+        beta[bh] = np.random.default_rng([2000 + seed, TENSOR_BETA, bh]).uniform(beta_lo, 1.0, L)
+        if gated:
+            alpha[bh] = np.random.default_rng([2000 + seed, TENSOR_ALPHA, bh]).uniform(alpha_lo, 1.0, L)
+    k = Tensor(kb, bf16_bits_to_f64(kb) if want_exact else None, "bf16")
+    return q, k, v, beta, alpha
+
+
+def delta_head_inputs(seed: int, bh: int, L: int, d_k: int, d_v: int, gated: bool,
+                      beta_lo: float = 0.25, alpha_lo: float = 0.9):
+    """Head bh of delta_inputs alone: (q, k, v float64 [L, d], beta, alpha or None)."""
+    scale = 1.0 / math.sqrt(d_k)
+    q = head_tensor(2000 + seed, TENSOR_Q, bh, L, d_k, "bf16", scale).exact
+    v = head_tensor(2000 + seed, TENSOR_V, bh, L, d_v, "bf16", scale).exact
+    k = bf16_bits_to_f64(unit_rows_bf16(np.random.default_rng([2000 + seed, TENSOR_K, bh]), (L, d_k)))
+    beta = np.random.default_rng([2000 + seed, TENSOR_BETA, bh]).uniform(beta_lo, 1.0, L).astype(np.float32)
+    alpha = (np.random.default_rng([2000 + seed, TENSOR_ALPHA, bh]).uniform(alpha_lo, 1.0, L).astype(np.float32)
+             if gated else None)
+    return q, k, v, beta, alpha
