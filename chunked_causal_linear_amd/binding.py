@@ -29,7 +29,7 @@ EXPORTS = (
     "la_version", "la_chunk_states_decay", "la_state_scan_decay", "la_chunk_output_decay", "la_chunked_forward_decay",
     "la_recurrent_step_decay", "la_loglinear_forward", "la_loglinear_forward_workspace", "la_loglinear_levels",
     "la_chunked_forward_delta", "la_chunked_forward_delta_workspace", "la_delta_chunk_transform",
-    "la_recurrent_step_delta",
+    "la_recurrent_step_delta", "la_chunked_forward_noalloc",
 )
 
 
@@ -79,7 +79,9 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.la_chunked_forward_delta_workspace.restype = sz
     lib.la_delta_chunk_transform.argtypes = [vp, vp, vp, i32, i64, i64, i64, i64, vp, vp, vp]
     lib.la_recurrent_step_delta.argtypes = [vp, vp, vp, i32, i64, i64, i64, vp, vp, vp, vp, i32, vp]
-    for name in ("la_chunked_forward_delta", "la_delta_chunk_transform", "la_recurrent_step_delta",
+    lib.la_chunked_forward_noalloc.argtypes = [vp, vp, vp, i32, i64, i64, i64, i64, i64, i32, i32, i32, vp, i64, f32,
+                                               vp, i32, vp, vp, i64, vp]
+    for name in ("la_chunked_forward_noalloc", "la_chunked_forward_delta", "la_delta_chunk_transform", "la_recurrent_step_delta",
                  "la_loglinear_forward", "la_feature_map", "la_chunk_states", "la_state_scan", "la_chunk_output",
                  "la_chunked_forward",
                  "la_recurrent_step", "la_chunk_states_decay", "la_state_scan_decay", "la_chunk_output_decay",
@@ -453,4 +455,23 @@ def recurrent_step_delta(q, k, v, S, beta, alpha=None, out=None):
     _check(lib().la_recurrent_step_delta(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dtype_code(q), n, d_k, d_v,
                                          _dev(beta, "beta"), _dev(alpha, "alpha"), _dev(S, "S"), _dev(out, "o"),
                                          _dtype_code(out), _stream_ptr()))
+    return out
+
+
+def chunked_forward_noalloc(q, k, v, C: int, causal: bool = True, normalize: bool = False, fmap: str = "identity",
+                            W=None, in_scale: float = 1.0, out=None, S_final=None, z_final=None, group: int = 0):
+    """la_chunked_forward_noalloc: the forward with the library's own static scratch
+    (no workspace).  Writes into `out` (and `S_final`, `z_final` when given) and
+    returns out."""
+    torch = _torch()
+    BH, L, d_in = q.shape
+    d_v = v.shape[-1]
+    m = W.shape[0] if (fmap == "favor" and W is not None) else 0
+    if out is None:
+        out = torch.empty(BH, L, d_v, dtype=torch.bfloat16, device=q.device)
+    _check(lib().la_chunked_forward_noalloc(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dtype_code(q), BH, L, d_in, d_v,
+                                            C, int(causal), int(normalize), _fmap_code(fmap), _dev(W, "W"), m,
+                                            float(in_scale), _dev(out, "o"), _dtype_code(out),
+                                            _dev(S_final, "S_final"), _dev(z_final, "z_final"), group,
+                                            _stream_ptr()))
     return out

@@ -3,6 +3,7 @@
 // anything, never allocates, never synchronises, and never throws.
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -344,6 +345,40 @@ static la_status launch_phase3(const Plan& P, const void* qm, const void* km, co
 }
 
 
+// ---------------------------------------------------------------------------
+// The forward without a workspace argument.  Its scratch is a file-scope device
+// array; each device the library runs on holds its own copy until the process
+// ends.  In host code the array's name is only a stand-in: the device address
+// comes from hipGetSymbolAddress, once per device with that device current, and
+// only that address is ever passed to a kernel.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) char scratch[LA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+}  // namespace
+
+static la_status scratch_of_current_device(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(LA_ERR_UNSUPPORTED, "device %d is beyond the %d devices the scratch table holds", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_dev[dev] == nullptr) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress of the scratch array");
+        if (ptr == nullptr) return fail(LA_ERR_HIP, "hipGetSymbolAddress gave no address for the scratch array");
+        g_scratch_dev[dev] = ptr;
+    }
+    *out = g_scratch_dev[dev];
+    return LA_OK;
+}
+
+
 extern "C" {
 
 const char* la_status_string(la_status s) {
@@ -677,6 +712,28 @@ la_status la_chunked_forward(const void* q, const void* k, const void* v, la_dty
     g_last_error[0] = 0;
     return forward_entry(q, k, v, in_dt, BH, L, d_in, d_v, C, causal, normalize, f, W, m, in_scale, 1.0f, o, out_dt,
                          S_final, z_final, group, workspace, ws_bytes, stream);
+}
+
+la_status la_chunked_forward_noalloc(const void* q, const void* k, const void* v, la_dtype in_dt, int64_t BH,
+                                     int64_t L, int64_t d_in, int64_t d_v, int64_t C, int causal, int normalize,
+                                     la_fmap f, const void* W, int64_t m, float in_scale, void* o, la_dtype out_dt,
+                                     void* S_final, void* z_final, int64_t group, la_stream_t stream) {
+    g_last_error[0] = 0;
+    Plan P{};
+    la_status st = make_plan(P, in_dt, BH, L, d_in, d_v, C, causal, normalize, f, m, in_scale, group, false);
+    if (st != LA_OK) return st;
+    if (P.ws_total > (size_t)LA_NOALLOC_SCRATCH_BYTES)
+        return fail(LA_ERR_UNSUPPORTED,
+                    "this forward needs %zu bytes of scratch; the allocation-free forward holds at most %zu "
+                    "(la_chunked_forward takes a workspace of any size)",
+                    P.ws_total, (size_t)LA_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    if (P.ws_total > 0) {
+        st = scratch_of_current_device(&ws);
+        if (st != LA_OK) return st;
+    }
+    return forward_entry(q, k, v, in_dt, BH, L, d_in, d_v, C, causal, normalize, f, W, m, in_scale, 1.0f, o, out_dt,
+                         S_final, z_final, group, ws, ws ? (size_t)LA_NOALLOC_SCRATCH_BYTES : 0, stream);
 }
 
 la_status la_chunked_forward_decay(const void* q, const void* k, const void* v, la_dtype in_dt, int64_t BH,

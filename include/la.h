@@ -191,6 +191,27 @@ la_status la_chunked_forward(const void* q, const void* k, const void* v, la_dty
                              void* z_final, int64_t group, void* workspace, size_t ws_bytes,
                              la_stream_t stream);
 
+/*
+ * la_chunked_forward_noalloc - la_chunked_forward for callers that cannot
+ * allocate device memory or pass a workspace (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  Same arguments,
+ * results and errors as la_chunked_forward, without workspace / ws_bytes: the
+ * scratch it needs (la_chunked_forward_workspace bytes for the same arguments)
+ * comes from a static device array of LA_NOALLOC_SCRATCH_BYTES inside the
+ * library, one per device, held until the process ends; its address is looked
+ * up on the first call on each device (with that device current).  It calls no
+ * allocator.  A call needing more scratch returns LA_ERR_UNSUPPORTED and
+ * launches nothing.  Every call on a device shares that device's array, which
+ * keeps the last call's contents (nothing in it needs to start at zero): calls
+ * that overlap on one device (concurrent streams or threads) race on it.
+ */
+#define LA_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+la_status la_chunked_forward_noalloc(const void* q, const void* k, const void* v, la_dtype in_dt,
+                                     int64_t BH, int64_t L, int64_t d_in, int64_t d_v, int64_t C,
+                                     int causal, int normalize, la_fmap f, const void* W, int64_t m,
+                                     float in_scale, void* o, la_dtype out_dt, void* S_final,
+                                     void* z_final, int64_t group, la_stream_t stream);
+
 /* Bytes of workspace la_chunked_forward needs for these arguments (0 when it
  * needs none, and also on an invalid combination, which la_chunked_forward
  * then reports).  FAVOR+ stores phi(q), phi(k) and phi(k)'s bf16 residual
