@@ -171,16 +171,30 @@ hipError_t run_delta_step(const DeltaStepParams& p, hipStream_t s) {
 // ---------------------------------------------------------------------------
 // chunk transform: one wave per chunk of 64 rows
 // ---------------------------------------------------------------------------
+// A's strictly lower rows packed in LDS, each padded to whole float4s: row i
+// (i entries) starts at float4 a_row(i) = sum over r < i of ceil(r / 4); with
+// i = 4q + t that is 2q^2 + q, plus q + (t - 1)(q + 1) when t > 0 (528 float4s
+// in all).  Closed form, so a lane-dependent row costs no loop.
+__host__ __device__ constexpr int a_row(int i) {
+    const int q = i / 4, t = i % 4;
+    return 2 * q * q + q + (t > 0 ? q + (t - 1) * (q + 1) : 0);
+}
+constexpr int a_row_sum(int i) {
+    int n = 0;
+    for (int r = 0; r < i; ++r) n += (r + 3) / 4;
+    return n;
+}
+constexpr bool a_row_ok() {
+    for (int i = 0; i <= 64; ++i)
+        if (a_row(i) != a_row_sum(i)) return false;
+    return true;
+}
+static_assert(a_row_ok() && a_row(64) == 528, "packed rows");
+
 template <int DK>
-__global__ __launch_bounds__(64) void delta_transform_kernel(DeltaPrepParams p) {
-    using namespace pipe;
-    constexpr int QSEG = DK / 8, NKA = DK / 32;
-    constexpr int KBYTES = 64 * DK * 2, ABYTES = 64 * 64 * 4;
-    // K rows of the chunk (row-major, 16-byte segments XOR-swizzled by row),
-    // then, once K K^T is in registers, A (fp32, 64 x 64) in the same place
-    __shared__ __attribute__((aligned(16))) char lds[KBYTES > ABYTES ? KBYTES : ABYTES];
-    const u16* kt = reinterpret_cast<const u16*>(lds);
-    float* A = reinterpret_cast<float*>(lds);
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void delta_transform_kernel(DeltaPrepParams p) {
+    constexpr int NKA = DK / 32;
+    __shared__ float4 A4[a_row(64)];
 
     const int lane = threadIdx.x, l16 = lane % 16, g = lane / 16;
     const int64_t chunk = blockIdx.x;  // bh * N + n
@@ -188,6 +202,29 @@ __global__ __launch_bounds__(64) void delta_transform_kernel(DeltaPrepParams p) 
     const int64_t L = p.L;
     const int64_t r0 = n * 64;
     const int valid = (int)(L - r0 < 64 ? L - r0 : 64);
+
+    // K K^T on the matrix cores with the operands straight from memory: lane
+    // (l16, g) of block b takes row 16 b + l16, elements 32 ks + 8 g .. + 7
+    // (rows past the end: zero).  Blocks (ib, jb), jb <= ib: lane holds row
+    // 16 ib + 4 g + e, column 16 jb + l16.
+    const u16* kg = p.k + (bh * L + r0) * DK;
+    f32x4 acc[10];
+#pragma unroll
+    for (int b = 0; b < 10; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NKA; ++ks) {
+        bf16x8 kr[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int r = 16 * b + l16;
+            kr[b] = as_bf16x8(r < valid ? *reinterpret_cast<const uint4*>(kg + (int64_t)r * DK + 32 * ks + 8 * g)
+                                        : make_uint4(0, 0, 0, 0));
+        }
+#pragma unroll
+        for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+            for (int jb = 0; jb <= ib; ++jb) acc[ib * (ib + 1) / 2 + jb] = mfma_bf16(kr[ib], kr[jb], acc[ib * (ib + 1) / 2 + jb]);
+    }
 
     // log2 of the gates' product over rows 0..lane (rows past the end: gate 1)
     float lg = 0.f;
@@ -200,34 +237,9 @@ __global__ __launch_bounds__(64) void delta_transform_kernel(DeltaPrepParams p) 
     p.lg[chunk * 64 + lane] = lg;
     const float beta = lane < valid ? p.beta[bh * L + r0 + lane] : 0.f;
 
-    // K rows into LDS (rows past the end: zero)
-    const u16* kg = p.k + (bh * L + r0) * DK;
-    for (int i = lane; i < 64 * QSEG; i += 64) {
-        const int r = i / QSEG, seg = i % QSEG;
-        const uint4 x = r < valid ? *reinterpret_cast<const uint4*>(kg + (int64_t)r * DK + seg * 8)
-                                  : make_uint4(0, 0, 0, 0);
-        *reinterpret_cast<uint4*>(lds + tile_off<QSEG>(r, seg * 8)) = x;
-    }
-    __syncthreads();
-
-    // K K^T, blocks (ib, jb) with jb <= ib: lane holds row 16 ib + 4g + e, column 16 jb + l16
-    f32x4 acc[10];
-#pragma unroll
-    for (int b = 0; b < 10; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < NKA; ++ks) {
-        bf16x8 kr[4];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) kr[b] = row_op<QSEG>(kt, 16 * b + l16, 32 * ks, g);
-#pragma unroll
-        for (int ib = 0; ib < 4; ++ib)
-#pragma unroll
-            for (int jb = 0; jb <= ib; ++jb) acc[ib * (ib + 1) / 2 + jb] = mfma_bf16(kr[ib], kr[jb], acc[ib * (ib + 1) / 2 + jb]);
-    }
-    __syncthreads();  // every K read is done before A overwrites it
-
-    // A[i][j] = beta_i g_i / g_j (k_i . k_j) for j < i, else 0 (blocks above the
-    // diagonal are never read)
+    // A[i][j] = beta_i g_i / g_j (k_i . k_j) for j < i into the packed rows; the
+    // padding of each row (i <= j < 4 ceil(i / 4)) is written as zero
+    float* A = reinterpret_cast<float*>(A4);
 #pragma unroll
     for (int ib = 0; ib < 4; ++ib)
 #pragma unroll
@@ -238,30 +250,49 @@ __global__ __launch_bounds__(64) void delta_transform_kernel(DeltaPrepParams p) 
             for (int e = 0; e < 4; ++e) {
                 const int i = 16 * ib + 4 * g + e;
                 const float bi = __shfl(beta, i), lgi = __shfl(lg, i);
-                const float val = j < i ? bi * __builtin_amdgcn_exp2f(lgi - lgj) * acc[ib * (ib + 1) / 2 + jb][e] : 0.f;
-                A[i * 64 + j] = val;
+                if (j < (i + 3) / 4 * 4)
+                    A[a_row(i) * 4 + j] =
+                        j < i ? bi * __builtin_amdgcn_exp2f(lgi - lgj) * acc[ib * (ib + 1) / 2 + jb][e] : 0.f;
             }
         }
     __syncthreads();
 
-    // forward substitution: column c = lane of X = (I + A)^-1,
-    // x_i = [i == c] - sum_{j < i} A[i][j] x_j (four partial sums per row)
+    // forward substitution, column c = lane of X = (I + A)^-1:
+    // x_i = [i == c] - sum_{j < i} A[i][j] x_j, four rows at a time (sixteen
+    // independent sums against the columns already solved, then the 4 x 4
+    // triangle of the four rows)
     float x[64];
 #pragma unroll
-    for (int i = 0; i < 64; ++i) {
-        float s0 = i == lane ? 1.f : 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-        const float* Ai = A + i * 64;
+    for (int i = 0; i < 64; ++i) x[i] = 0.f;
 #pragma unroll
-        for (int j = 0; j + 4 <= i; j += 4) {
-            const float4 a4 = *reinterpret_cast<const float4*>(Ai + j);
-            s0 = fmaf(-a4.x, x[j], s0);
-            s1 = fmaf(-a4.y, x[j + 1], s1);
-            s2 = fmaf(-a4.z, x[j + 2], s2);
-            s3 = fmaf(-a4.w, x[j + 3], s3);
+    for (int i0 = 0; i0 < 64; i0 += 4) {
+        float sacc[4][4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) sacc[r][c] = 0.f;
+#pragma unroll
+        for (int j4 = 0; j4 < i0 / 4; ++j4)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float4 a = A4[a_row(i0 + r) + j4];
+                sacc[r][0] = fmaf(a.x, x[4 * j4], sacc[r][0]);
+                sacc[r][1] = fmaf(a.y, x[4 * j4 + 1], sacc[r][1]);
+                sacc[r][2] = fmaf(a.z, x[4 * j4 + 2], sacc[r][2]);
+                sacc[r][3] = fmaf(a.w, x[4 * j4 + 3], sacc[r][3]);
+            }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = i0 + r;
+            float xi = (i == lane ? 1.f : 0.f) - ((sacc[r][0] + sacc[r][1]) + (sacc[r][2] + sacc[r][3]));
+            if (r > 0) {
+                const float4 a = A4[a_row(i) + i0 / 4];  // A[i][i0 .. i0 + 3]; entries from i on are zero
+                const float at[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+                for (int t = 0; t < r; ++t) xi = fmaf(-at[t], x[i0 + t], xi);
+            }
+            x[i] = xi;
         }
-#pragma unroll
-        for (int j = i & ~3; j < i; ++j) s0 = fmaf(-Ai[j], x[j], s0);
-        x[i] = (s0 + s1) + (s2 + s3);
     }
     // T = X diag(beta): lane c writes column c of every row, at its permuted
     // position (each store covers one whole 128-byte row)
@@ -399,35 +430,44 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
     auto compute = [&](StageT& s, int valid) __attribute__((always_inline)) {
         const char* vbytes = reinterpret_cast<const char*>(s.v);
-        // (tril(Q K^T) * G) blocks (ib, jb), jb <= ib, shared out: block b = wave, wave + 4, wave + 8.
-        // The intra product reads 32 keys at a time, so query blocks 0 and 2 also
-        // read the blocks above the diagonal (0, 1) and (2, 3): b = 10, 11 write
-        // them as zeros.
+        // (tril(Q K^T) * G) blocks (ib, jb), jb <= ib, shared out: blocks b = wave,
+        // wave + 4, wave + 8 of the ten, three independent chains per wave.  The
+        // intra product reads 32 keys at a time, so query blocks 0 and 2 also read
+        // the blocks above the diagonal (0, 1) and (2, 3): waves 2 and 3, which
+        // have only two blocks, write those as zeros (their third chain repeats a
+        // block of their own and is not stored).
+        {
+            int ib3[3], jb3[3];
 #pragma unroll
-        for (int b0 = 0; b0 < 12; b0 += 4) {
-            const int b = b0 + wave;
-            if (b >= 10) {
-                const int ib = b == 10 ? 0 : 2;
+            for (int t = 0; t < 3; ++t) {
+                const int b = t < 2 || wave < 2 ? wave + 4 * t : wave;
+                ib3[t] = b < 1 ? 0 : (b < 3 ? 1 : (b < 6 ? 2 : 3));
+                jb3[t] = b - ib3[t] * (ib3[t] + 1) / 2;
+            }
+            f32x4 acc[3] = {zero4, zero4, zero4};
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    *reinterpret_cast<u16*>(reinterpret_cast<char*>(stile) +
-                                            tile_off<8>(16 * ib + 4 * g + e, perm_pos(16 * (ib + 1) + l16))) = 0;
-            } else {
-                const int ib = b < 1 ? 0 : (b < 3 ? 1 : (b < 6 ? 2 : 3));
-                const int jb = b - ib * (ib + 1) / 2;
-                f32x4 acc = zero4;
+            for (int ks = 0; ks < NKA; ++ks) {
+                bf16x8 qa[3], kb[3];
 #pragma unroll
-                for (int ks = 0; ks < NKA; ++ks)
-                    acc = mfma_bf16(row_op<QSEG>(s.q, 16 * ib + l16, 32 * ks, g), row_op<QSEG>(s.k, 16 * jb + l16, 32 * ks, g),
-                                    acc);
-                const int j = 16 * jb + l16;
+                for (int t = 0; t < 3; ++t) {
+                    qa[t] = row_op<QSEG>(s.q, 16 * ib3[t] + l16, 32 * ks, g);
+                    kb[t] = row_op<QSEG>(s.k, 16 * jb3[t] + l16, 32 * ks, g);
+                }
+#pragma unroll
+                for (int t = 0; t < 3; ++t) acc[t] = mfma_bf16(qa[t], kb[t], acc[t]);
+            }
+#pragma unroll
+            for (int t = 0; t < 3; ++t) {
+                const bool zero_block = t == 2 && wave >= 2;
+                const int ib = zero_block ? (wave == 2 ? 0 : 2) : ib3[t];
+                const int j = zero_block ? 16 * (ib + 1) + l16 : 16 * jb3[t] + l16;
                 const float lgj = s.lg[j];
                 const float4 lgi = *reinterpret_cast<const float4*>(s.lg + 16 * ib + 4 * g);
                 const float li[4] = {lgi.x, lgi.y, lgi.z, lgi.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int i = 16 * ib + 4 * g + e;
-                    const float val = j <= i ? acc[e] * __builtin_amdgcn_exp2f(li[e] - lgj) : 0.f;
+                    const float val = !zero_block && j <= i ? acc[t][e] * __builtin_amdgcn_exp2f(li[e] - lgj) : 0.f;
                     *reinterpret_cast<u16*>(reinterpret_cast<char*>(stile) + tile_off<8>(i, perm_pos(j))) = f2bf(val);
                 }
             }
