@@ -15,7 +15,8 @@
 //    lower-triangular inverse by forward substitution in fp32 (lane c owns
 //    column c), stored as bf16 with its columns in the matrix-core operand
 //    order of delta_fwd_kernel; also log2 g per row;
-//  * delta_fwd_kernel: the chunks of one head in order, carrying the state.
+//  * delta_fwd_kernel: the chunks of one head in order, carrying the state
+//    (state waves) beside waves that move the data and form the score tile.
 //    Per chunk (P the state before it, n = 64 rows):
 //        R = V - diag(g) K P,  U = T R,
 //        O = diag(g) Q P + (tril(Q K^T) * G) U,     G[i][j] = g_i / g_j,
@@ -327,15 +328,29 @@ struct alignas(16) DeltaStage {
     float lg[64];    // log2 of the gates' product up to each row
 };
 
+// Eight waves, two per SIMD.  Waves 0-3 (state waves) own 16 value columns of
+// the state each and run the chain that depends on it; waves 4-7 (prep waves)
+// do everything that does not: every copy and output store, and the shared
+// score tile (tril(Q K^T) * G) of the chunk, on the same SIMDs, so each
+// SIMD has a second wave to issue while the other waits.  Two barriers per
+// chunk n:
+//   B1(n): chunk n has landed; the state waves are done with chunk n - 1 (its
+//          output rows are in its stage, the score tile is free);
+//   B2(n): the score tile of chunk n is complete.
+// Between B1(n) and B2(n) the state waves compute K P, Q P, R and U = T R
+// while the prep waves compute the score tile; between B2(n) and B1(n + 1)
+// the state waves finish the chunk (intra product, outputs, state update)
+// while the prep waves store the outputs of chunk n - 1, refill its stage with
+// chunk n + NSTAGE - 1 and wait for chunk n + 1.
 template <int DK>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void delta_fwd_kernel(DeltaFwdParams p) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void delta_fwd_kernel(DeltaFwdParams p) {
     using namespace pipe;
     constexpr int QSEG = DK / 8, NKA = DK / 32;
     typedef DeltaStage<DK> StageT;
     constexpr int SBYTES = 64 * 64 * 2;
     constexpr int NFIT = (int)((160 * 1024 - SBYTES) / sizeof(StageT));
     constexpr int NSTAGE = NFIT < 4 ? NFIT : 4;
-    constexpr int NQ = QSEG / 4;  // copy instructions per chunk and wave: Q (and K)
+    constexpr int NQ = QSEG / 4;  // copy instructions per chunk and prep wave: Q (and K)
     constexpr int NV = 2, NTR = 2;  // V, T
     constexpr int NL = 2 * NQ + NV + NTR + 1;  // + the gate logs
     static_assert(NSTAGE >= 2 && (NSTAGE - 2) * NL < 64, "stages and vmcnt range");
@@ -345,102 +360,100 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);  // wave-uniform
+    const bool prep = wave >= 4;
+    const int pw = wave & 3;  // prep waves: share of the copies and score blocks; state waves: column block
     const int lane = tid % WAVE, l16 = lane % 16, g = lane / 16;
     const int wi = work_index(p.xcd_remap);
     const int jt = wi % p.n_dvt;
     const int64_t bh = wi / p.n_dvt;
-    const int col0 = jt * 64, cw = 16 * wave;
+    const int col0 = jt * 64, cw = 16 * pw;
     const int64_t L = p.L, N = p.N;
     const int dv = p.dv;
-    const int c8 = 8 * (lane & 3);
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
     auto valid_of = [&](int64_t n) -> int { return (int)(L - n * 64 < 64 ? L - n * 64 : 64); };
 
-    // this wave's share of the copies of chunk n (rows past the end clamped to the last row)
-    auto issue = [&](int64_t n, StageT& s) __attribute__((always_inline)) {
-        const int64_t r0 = n * 64;
-        const int last = (int)(L - 1 - r0);
-        const u16* qb = p.q + (bh * L + r0) * DK;
-        const u16* kb = p.k + (bh * L + r0) * DK;
-        const u16* vb = p.v + (bh * L + r0) * dv + col0;
-        const u16* tb = p.T + (bh * N + n) * 64 * 64;
+    if (prep) {
+        // ================= prep wave pw =================
+        // this wave's share of the copies of chunk n (rows past the end clamped to the last row)
+        auto issue = [&](int64_t n, StageT& s) __attribute__((always_inline)) {
+            const int64_t r0 = n * 64;
+            const int last = (int)(L - 1 - r0);
+            const u16* qb = p.q + (bh * L + r0) * DK;
+            const u16* kb = p.k + (bh * L + r0) * DK;
+            const u16* vb = p.v + (bh * L + r0) * dv + col0;
+            const u16* tb = p.T + (bh * N + n) * 64 * 64;
 #pragma unroll
-        for (int i = 0; i < NQ; ++i) {
-            const int b = wave * NQ + i, slot = b * WAVE + lane;
-            const int r = slot / QSEG, seg = (slot % QSEG) ^ (r & (QSEG - 1));
-            const uint32_t off = (uint32_t)(((r < last ? r : last) * DK + seg * 8) * 2);
-            dma16(qb, off, lds_addr(s.q) + b * WAVE * 16);
-            dma16(kb, off, lds_addr(s.k) + b * WAVE * 16);
-        }
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int b = wave * NV + i, slot = b * WAVE + lane;
-            const int r = slot / 8, seg = (slot % 8) ^ (r & 7);
-            dma16(vb, (uint32_t)(((r < last ? r : last) * dv + seg * 8) * 2), lds_addr(s.v) + b * WAVE * 16);
-        }
-#pragma unroll
-        for (int i = 0; i < NTR; ++i) {
-            const int b = wave * NTR + i, slot = b * WAVE + lane;
-            const int r = slot / 8, seg = (slot % 8) ^ (r & 7);
-            dma16(tb, (uint32_t)((r * 64 + seg * 8) * 2), lds_addr(s.t) + b * WAVE * 16);
-        }
-        // 256 bytes of gate logs: four 16-byte pieces per wave
-        if (lane < 4) dma16(p.lg + (bh * N + n) * 64, (uint32_t)((wave * 4 + lane) * 16), lds_addr(s.lg) + wave * 64);
-    };
-    // wait until this wave's copies of a chunk have landed, with those of
-    // `after` later chunks issued after them (loads complete in order)
-    auto land = [&](int after) __attribute__((always_inline)) {
-        if constexpr (NSTAGE >= 4)
-            if (after >= 2) {
-                wait_vm<2 * NL>();
-                return;
+            for (int i = 0; i < NQ; ++i) {
+                const int b = pw * NQ + i, slot = b * WAVE + lane;
+                const int r = slot / QSEG, seg = (slot % QSEG) ^ (r & (QSEG - 1));
+                const uint32_t off = (uint32_t)(((r < last ? r : last) * DK + seg * 8) * 2);
+                dma16(qb, off, lds_addr(s.q) + b * WAVE * 16);
+                dma16(kb, off, lds_addr(s.k) + b * WAVE * 16);
             }
-        if constexpr (NSTAGE >= 3)
-            if (after >= 1) {
-                wait_vm<NL>();
-                return;
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                const int b = pw * NV + i, slot = b * WAVE + lane;
+                const int r = slot / 8, seg = (slot % 8) ^ (r & 7);
+                dma16(vb, (uint32_t)(((r < last ? r : last) * dv + seg * 8) * 2), lds_addr(s.v) + b * WAVE * 16);
             }
-        wait_vm<0>();
-    };
-    // output rows of a chunk from the V tile of its stage: piece (wave * 2 + i) * 64 + lane
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    auto read_out = [&](const StageT& s, u32x4 (&ob)[2]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int piece = (wave * 2 + i) * WAVE + lane, r = piece / 8, seg = piece % 8;
-            ob[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(s.v) + tile_off<8>(r, seg * 8));
-        }
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the stage may be refilled
-    };
-    auto store_out = [&](int64_t n, const u32x4 (&ob)[2]) __attribute__((always_inline)) {
-        const int valid = valid_of(n);
-        u16* o = p.o + (bh * L + n * 64) * dv + col0;
+            for (int i = 0; i < NTR; ++i) {
+                const int b = pw * NTR + i, slot = b * WAVE + lane;
+                const int r = slot / 8, seg = (slot % 8) ^ (r & 7);
+                dma16(tb, (uint32_t)((r * 64 + seg * 8) * 2), lds_addr(s.t) + b * WAVE * 16);
+            }
+            // 256 bytes of gate logs: four 16-byte pieces per prep wave
+            if (lane < 4) dma16(p.lg + (bh * N + n) * 64, (uint32_t)((pw * 4 + lane) * 16), lds_addr(s.lg) + pw * 64);
+        };
+        // wait until this wave's copies of chunk n have landed (loads complete in
+        // order; later chunks' copies and the output stores may be in flight)
+        auto land = [&](int64_t n) __attribute__((always_inline)) {
+            const int64_t issued = n + NSTAGE - 2 < N - 1 ? n + NSTAGE - 2 : N - 1;  // newest chunk issued
+            const int after = (int)(issued - n);
+            if constexpr (NSTAGE >= 4)
+                if (after >= 2) {
+                    wait_vm<2 * NL>();
+                    return;
+                }
+            if constexpr (NSTAGE >= 3)
+                if (after >= 1) {
+                    wait_vm<NL>();
+                    return;
+                }
+            wait_vm<0>();
+        };
+        // output rows of a chunk from the V tile of its stage: piece (pw * 2 + i) * 64 + lane
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        auto read_out = [&](const StageT& s, u32x4 (&ob)[2]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int piece = (wave * 2 + i) * WAVE + lane, r = piece / 8, seg = piece % 8;
-            if (r < valid) __builtin_nontemporal_store(ob[i], reinterpret_cast<u32x4*>(o + (int64_t)r * dv + seg * 8));
-        }
-    };
-
-    // state: P[ks][hf] lane (l16, g) element e = P[a = 32 ks + 8 g + 4 hf + e][c = col0 + cw + l16]
-    f32x4 P[NKA][2];
+            for (int i = 0; i < 2; ++i) {
+                const int piece = (pw * 2 + i) * WAVE + lane, r = piece / 8, seg = piece % 8;
+                ob[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(s.v) + tile_off<8>(r, seg * 8));
+            }
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the stage may be refilled
+        };
+        auto store_out = [&](int64_t n, const u32x4 (&ob)[2]) __attribute__((always_inline)) {
+            const int valid = valid_of(n);
+            u16* o = p.o + (bh * L + n * 64) * dv + col0;
 #pragma unroll
-    for (int ks = 0; ks < NKA; ++ks) P[ks][0] = P[ks][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-
-    auto compute = [&](StageT& s, int valid) __attribute__((always_inline)) {
-        const char* vbytes = reinterpret_cast<const char*>(s.v);
-        // (tril(Q K^T) * G) blocks (ib, jb), jb <= ib, shared out: blocks b = wave,
-        // wave + 4, wave + 8 of the ten, three independent chains per wave.  The
-        // intra product reads 32 keys at a time, so query blocks 0 and 2 also read
-        // the blocks above the diagonal (0, 1) and (2, 3): waves 2 and 3, which
-        // have only two blocks, write those as zeros (their third chain repeats a
-        // block of their own and is not stored).
-        {
+            for (int i = 0; i < 2; ++i) {
+                const int piece = (pw * 2 + i) * WAVE + lane, r = piece / 8, seg = piece % 8;
+                if (r < valid)
+                    __builtin_nontemporal_store(ob[i], reinterpret_cast<u32x4*>(o + (int64_t)r * dv + seg * 8));
+            }
+        };
+        // (tril(Q K^T) * G) blocks (ib, jb), jb <= ib: blocks b = pw, pw + 4,
+        // pw + 8 of the ten, three independent chains.  The intra product reads
+        // 32 keys at a time, so query blocks 0 and 2 also read the blocks above
+        // the diagonal (0, 1) and (2, 3): prep waves 2 and 3, which have only two
+        // blocks, write those as zeros (their third chain repeats a block of
+        // their own and is not stored).
+        auto score_tile = [&](const StageT& s) __attribute__((always_inline)) {
             int ib3[3], jb3[3];
 #pragma unroll
             for (int t = 0; t < 3; ++t) {
-                const int b = t < 2 || wave < 2 ? wave + 4 * t : wave;
+                const int b = t < 2 || pw < 2 ? pw + 4 * t : pw;
                 ib3[t] = b < 1 ? 0 : (b < 3 ? 1 : (b < 6 ? 2 : 3));
                 jb3[t] = b - ib3[t] * (ib3[t] + 1) / 2;
             }
@@ -458,8 +471,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             }
 #pragma unroll
             for (int t = 0; t < 3; ++t) {
-                const bool zero_block = t == 2 && wave >= 2;
-                const int ib = zero_block ? (wave == 2 ? 0 : 2) : ib3[t];
+                const bool zero_block = t == 2 && pw >= 2;
+                const int ib = zero_block ? (pw == 2 ? 0 : 2) : ib3[t];
                 const int j = zero_block ? 16 * (ib + 1) + l16 : 16 * jb3[t] + l16;
                 const float lgj = s.lg[j];
                 const float4 lgi = *reinterpret_cast<const float4*>(s.lg + 16 * ib + 4 * g);
@@ -471,9 +484,46 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                     *reinterpret_cast<u16*>(reinterpret_cast<char*>(stile) + tile_off<8>(i, perm_pos(j))) = f2bf(val);
                 }
             }
-        }
-        __syncthreads();  // the score tile is complete
+        };
 
+#pragma unroll
+        for (int s0 = 0; s0 < NSTAGE - 1; ++s0)
+            if (s0 < N) issue(s0, st[s0]);
+        land(0);
+        int si = 0;  // stage of chunk n
+        for (int64_t n = 0; n < N; ++n) {
+            const int sp = si == 0 ? NSTAGE - 1 : si - 1;  // stage of chunk n - 1 (and of chunk n + NSTAGE - 1)
+            __syncthreads();  // B1(n)
+            score_tile(st[si]);
+            __syncthreads();  // B2(n)
+            u32x4 ob[2];
+            if (n > 0) read_out(st[sp], ob);
+            if (n + NSTAGE - 1 < N) issue(n + NSTAGE - 1, st[sp]);
+            if (n > 0) store_out(n - 1, ob);
+            if (n + 1 < N) land(n + 1);
+            si = si == NSTAGE - 1 ? 0 : si + 1;
+        }
+        __syncthreads();  // B1(N): the last chunk's output is in its stage
+        const int sl = si == 0 ? NSTAGE - 1 : si - 1;
+        u32x4 ob[2];
+        read_out(st[sl], ob);
+        store_out(N - 1, ob);
+        return;
+    }
+
+    // ================= state wave pw: value columns cw .. cw + 15 =================
+    const int c8 = 8 * (lane & 3);
+    // P[ks][hf] lane (l16, g) element e = P[a = 32 ks + 8 g + 4 hf + e][c = col0 + cw + l16]
+    f32x4 P[NKA][2];
+#pragma unroll
+    for (int ks = 0; ks < NKA; ++ks) P[ks][0] = P[ks][1] = zero4;
+
+    int si = 0;
+    for (int64_t n = 0; n < N; ++n) {
+        StageT& s = st[si];
+        const int valid = valid_of(n);
+        const char* vbytes = reinterpret_cast<const char*>(s.v);
+        __syncthreads();  // B1(n)
         bf16x8 pst[NKA];
 #pragma unroll
         for (int ks = 0; ks < NKA; ++ks) pst[ks] = pack_acc_bf16(P[ks][0], P[ks][1]);
@@ -516,6 +566,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
             for (int ks = 0; ks <= ib / 2; ++ks) U[ib] = mfma_bf16(row_op<8>(s.t, 16 * ib + l16, 32 * ks, g), Rp[ks], U[ib]);
         }
+        __syncthreads();  // B2(n): the score tile is complete
         // O += (tril(Q K^T) * G) U
         const bf16x8 Up[2] = {pack_acc_bf16(U[0], U[1]), pack_acc_bf16(U[2], U[3])};
 #pragma unroll
@@ -552,31 +603,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
                 for (int hf = 0; hf < 2; ++hf)
                     P[ks][hf] = mfma_bf16(col_op<QSEG>(s.k, 32 * kk, 32 * ks + c8 + 4 * hf, lane), Uw[kk], P[ks][hf]);
-    };
-
-#pragma unroll
-    for (int s0 = 0; s0 < NSTAGE - 1; ++s0)
-        if (s0 < N) issue(s0, st[s0]);
-    int si = 0;  // stage of chunk n
-    for (int64_t n = 0; n < N; ++n) {
-        const int sp = si == 0 ? NSTAGE - 1 : si - 1;  // stage of chunk n - 1 (and of chunk n + NSTAGE - 1)
-        const int64_t newest = n + NSTAGE - 2 < N - 1 ? n + NSTAGE - 2 : N - 1;
-        land((int)(newest - n));
-        __syncthreads();  // chunk n is in; every wave is done with chunk n - 1
-        u32x4 ob[2];
-        if (n > 0) read_out(st[sp], ob);
-        if (n + NSTAGE - 1 < N) issue(n + NSTAGE - 1, st[sp]);
-        if (n > 0) store_out(n - 1, ob);
-        compute(st[si], valid_of(n));
         si = si == NSTAGE - 1 ? 0 : si + 1;
     }
-    __syncthreads();  // the last chunk's output is in its stage
-    {
-        const int sl = si == 0 ? NSTAGE - 1 : si - 1;
-        u32x4 ob[2];
-        read_out(st[sl], ob);
-        store_out(N - 1, ob);
-    }
+    __syncthreads();  // B1(N)
     if (p.S_final != nullptr) {
         float* Sf = p.S_final + (bh * DK) * (int64_t)dv + col0 + cw + l16;
 #pragma unroll
@@ -592,10 +621,10 @@ hipError_t run_delta_fwd(const DeltaFwdParams& p, hipStream_t s) {
     const int64_t grid = p.BH * p.n_dvt;
     switch (p.dk) {
         case 64:
-            hipLaunchKernelGGL((delta_fwd_kernel<64>), dim3((unsigned)grid), dim3(256), 0, s, p);
+            hipLaunchKernelGGL((delta_fwd_kernel<64>), dim3((unsigned)grid), dim3(512), 0, s, p);
             break;
         case 128:
-            hipLaunchKernelGGL((delta_fwd_kernel<128>), dim3((unsigned)grid), dim3(256), 0, s, p);
+            hipLaunchKernelGGL((delta_fwd_kernel<128>), dim3((unsigned)grid), dim3(512), 0, s, p);
             break;
         default: return hipErrorInvalidValue;
     }
