@@ -45,6 +45,7 @@ FILE_FLAGS = {"la_pipe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
               "la_pipe_decay_fac.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
               "la_fmap.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
               "la_delta.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+              "la_favor.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
               "probe/la_probe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 

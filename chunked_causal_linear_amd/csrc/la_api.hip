@@ -81,6 +81,7 @@ struct Plan {
     int64_t n_chunks, G, n_groups;
     int DK, DVT, T, n_dvt;
     bool premap;  // phi computed by a separate pass into the workspace
+    bool favor;   // FAVOR+ mapped inside the streaming kernels (no mapped copies)
     bool pipe;    // streaming phase-3 kernel (chunks of 32, 64 or 128 rows)
     bool causal, normalize;
     int64_t sub;       // phase-1 states per group (finer grain than the groups when they are few and long)
@@ -109,7 +110,7 @@ la_status check_dtypes_forward(la_dtype in_dt, la_dtype out_dt, int normalize, l
 
 la_status make_plan(Plan& P, la_dtype in_dt, int64_t BH, int64_t L, int64_t d_in, int64_t d_v, int64_t C,
                     int causal, int normalize, la_fmap f, int64_t m, float in_scale, int64_t group,
-                    bool decay) {
+                    bool decay, bool bf16_out = false) {
     if (BH < 1 || L < 1 || d_in < 1 || d_v < 1) return fail(LA_ERR_INVALID_ARG, "sizes must be positive");
     if (f != LA_FMAP_IDENTITY && f != LA_FMAP_ELU1 && f != LA_FMAP_FAVOR)
         return fail(LA_ERR_INVALID_ARG, "unknown feature map %d", (int)f);
@@ -155,11 +156,18 @@ la_status make_plan(Plan& P, la_dtype in_dt, int64_t BH, int64_t L, int64_t d_in
     P.pipe = !P.i8 && P.causal &&
              (((Ce == 32 || Ce == 64 || Ce == 128) && d_v % 64 == 0 && (P.dk == 64 || P.dk == 128)) ||
               ((Ce == 32 || Ce == 64) && d_v % 32 == 0 && P.dk == 256));
+    // FAVOR+ with 64 input features, 64, 128 or 256 random features, chunks
+    // of 64 rows, value columns a multiple of 64 and a bf16 output: the
+    // streaming kernels map q and k themselves from W held in LDS
+    // (la_favor.hip), so the mapped copies never go through memory.
+    P.favor = !P.i8 && P.causal && f == LA_FMAP_FAVOR && bf16_out && !decay && d_in == 64 &&
+              (m == 64 || m == 128 || m == 256) && Ce == 64 && d_v % 64 == 0;
+    if (P.favor) P.pipe = true;
     P.final_from_scan = P.pipe && f != LA_FMAP_IDENTITY;
-    P.premap = f == LA_FMAP_FAVOR;
+    P.premap = f == LA_FMAP_FAVOR && !P.favor;
     if (P.pipe) {
         P.DK = (int)P.dk;
-        P.DVT = P.dk == 256 ? 32 : 64;
+        P.DVT = (P.dk == 256 && !P.favor) ? 32 : 64;
         P.n_dvt = (int)(d_v / P.DVT);
     }
 
@@ -596,6 +604,10 @@ size_t la_chunked_forward_workspace(la_dtype in_dt, int64_t BH, int64_t L, int64
         Plan Pd{};
         if (make_plan(Pd, in_dt, BH, L, d_in, d_v, C, causal, normalize, f, m, in_scale, group, true) == LA_OK)
             ws = std::max(ws, Pd.ws_total);
+        // and the plan of a bf16 output (FAVOR+ mapped in the kernels)
+        Plan Pb{};
+        if (make_plan(Pb, in_dt, BH, L, d_in, d_v, C, causal, normalize, f, m, in_scale, group, false, true) == LA_OK)
+            ws = std::max(ws, Pb.ws_total);
     }
     memcpy(g_last_error, saved, sizeof(saved));
     if (s != LA_OK) return 0;
@@ -607,9 +619,73 @@ int64_t la_chunked_forward_group(la_dtype in_dt, int64_t BH, int64_t L, int64_t 
     Plan P{};
     char saved[sizeof(g_last_error)];
     memcpy(saved, g_last_error, sizeof(saved));
-    const la_status s = make_plan(P, in_dt, BH, L, d_in, d_v, C, causal, normalize, f, m, 1.0f, group, false);
+    const la_status s = make_plan(P, in_dt, BH, L, d_in, d_v, C, causal, normalize, f, m, 1.0f, group, false,
+                                  in_dt == LA_BF16);
     memcpy(g_last_error, saved, sizeof(saved));
     return s == LA_OK ? P.G : 0;
+}
+
+// FAVOR+ mapped inside the kernels: phase 1 sums each run's phi(k)^T v (and
+// phi(k)) from the raw keys, the scan forms the groups' prefixes and the total,
+// and phase 3 maps q and k of each chunk as it streams the group.
+static la_status favor_forward(const Plan& P, const void* q, const void* k, const void* v, const void* W,
+                               float in_scale, void* o, void* S_final, void* z_final, char* ws, hipStream_t s) {
+    const int64_t BH = P.BH;
+    float* states = P.ws_states ? reinterpret_cast<float*>(ws) : nullptr;
+    float* zst = P.ws_z ? reinterpret_cast<float*>(ws + P.ws_states) : nullptr;
+    la::FavorParams fp{};
+    fp.q = static_cast<const unsigned short*>(q);
+    fp.k = static_cast<const unsigned short*>(k);
+    fp.v = static_cast<const unsigned short*>(v);
+    fp.W = static_cast<const unsigned short*>(W);
+    fp.L = P.L;
+    fp.dv = (int)P.dv;
+    fp.n_dvt = P.n_dvt;
+    fp.in_scale = in_scale;
+    const bool want_final = S_final != nullptr || z_final != nullptr;
+    if (P.n_groups > 1 || want_final) {
+        const int64_t n_slots = P.n_groups * P.sub;
+        const int64_t n_items = want_final ? n_slots : n_slots - P.sub;
+        const int64_t rows = P.G * P.C / P.sub;  // a multiple of 64 (planned so)
+        if (rows % 64 != 0 || states == nullptr || (P.normalize && zst == nullptr))
+            return fail(LA_ERR_UNSUPPORTED, "FAVOR+ phase-1 plan: rows %lld", (long long)rows);
+        fp.S = states;
+        fp.z = zst;
+        fp.rows = rows;
+        fp.n_groups = (int)n_items;
+        fp.n_out = (int)n_slots;
+        const int64_t grid1 = BH * n_items * P.n_dvt;
+        fp.xcd_remap = xcd_ok(grid1);
+        la_status st = hip_status(la::run_favor_states(fp, (int)P.dk, P.normalize, grid1, s), "FAVOR+ states launch");
+        if (st != LA_OK) return st;
+        la::ScanParams sp{};
+        sp.S = states;
+        sp.z = zst;
+        sp.N = n_slots;
+        sp.L = P.L;
+        sp.Cs = rows;
+        if (want_final) {
+            sp.S_final = S_final;
+            sp.z_final = z_final;
+        }
+        sp.E = P.dk * P.dv;
+        sp.Ez = P.dk;
+        st = hip_status(la::run_state_scan(sp, BH, s), "state scan launch");
+        if (st != LA_OK) return st;
+    }
+    fp.S = nullptr;
+    fp.z = nullptr;
+    fp.rows = 0;
+    fp.n_out = 0;
+    fp.o = static_cast<unsigned short*>(o);
+    fp.P0 = P.n_groups > 1 ? states : nullptr;
+    fp.z0 = P.n_groups > 1 ? zst : nullptr;
+    fp.G = (int)P.G;
+    fp.n_groups = (int)P.n_groups;
+    fp.p0_sub = (int)P.sub;
+    const int64_t grid = BH * P.n_groups * P.n_dvt;
+    fp.xcd_remap = xcd_ok(grid);
+    return hip_status(la::run_favor_fwd(fp, (int)P.dk, P.normalize, grid, s), "FAVOR+ forward launch");
 }
 
 static la_status forward_entry(const void* q, const void* k, const void* v, la_dtype in_dt, int64_t BH, int64_t L,
@@ -625,7 +701,8 @@ static la_status forward_entry(const void* q, const void* k, const void* v, la_d
     if (z_final != nullptr && !normalize) return fail(LA_ERR_INVALID_ARG, "z_final needs normalize");
     Plan P{};
     const float lg = log2_of(gamma);
-    st = make_plan(P, in_dt, BH, L, d_in, d_v, C, causal, normalize, f, m, in_scale, group, lg != 0.0f);
+    st = make_plan(P, in_dt, BH, L, d_in, d_v, C, causal, normalize, f, m, in_scale, group, lg != 0.0f,
+                   out_dt == LA_BF16);
     if (st != LA_OK) return st;
     if (lg != 0.0f && !(causal && P.pipe && out_dt == LA_BF16))
         return fail(LA_ERR_UNSUPPORTED,
@@ -636,6 +713,7 @@ static la_status forward_entry(const void* q, const void* k, const void* v, la_d
                     workspace ? ws_bytes : (size_t)0);
     hipStream_t s = (hipStream_t)stream;
     char* ws = static_cast<char*>(workspace);
+    if (P.favor) return favor_forward(P, q, k, v, W, in_scale, o, S_final, z_final, ws, s);
     const void* qm = q;
     const void* km = k;
     const void* klo = nullptr;

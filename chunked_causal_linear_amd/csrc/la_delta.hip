@@ -30,14 +30,6 @@ namespace {
 
 constexpr float kMinGateLog2 = -100.0f;  // a zero gate acts as 2^-100
 
-// position of key j (0..63) in a row of an operand whose k index runs in the
-// permuted order of packed accumulator pairs: inside each 32-key step, lane
-// group g' holds keys 4g'..4g'+3 (elements 0..3) and 16+4g'..16+4g'+3 (4..7)
-__device__ __forceinline__ int perm_pos(int j) {
-    const int jj = j & 31;
-    return (j & 32) + (jj < 16 ? 8 * (jj >> 2) + (jj & 3) : 8 * ((jj - 16) >> 2) + 4 + (jj & 3));
-}
-
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -297,7 +289,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void de
     }
     // T = X diag(beta): lane c writes column c of every row, at its permuted
     // position (each store covers one whole 128-byte row)
-    u16* T = p.T + chunk * 64 * 64 + perm_pos(lane);
+    u16* T = p.T + chunk * 64 * 64 + pipe::perm_pos(lane);
 #pragma unroll
     for (int i = 0; i < 64; ++i) T[i * 64] = f2bf(x[i] * beta);
 }

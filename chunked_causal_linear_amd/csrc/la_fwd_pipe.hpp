@@ -219,6 +219,15 @@ __device__ __forceinline__ int work_index(int remap) {
 template <int I>
 using ic = std::integral_constant<int, I>;
 
+// Position of key j (0..63) in a row of an operand whose k index runs in the
+// permuted order of packed accumulator pairs and of column operands: inside
+// each 32-key step, lane group g' holds keys 4g'..4g'+3 (elements 0..3) and
+// 16+4g'..16+4g'+3 (elements 4..7).
+__device__ __forceinline__ int perm_pos(int j) {
+    const int jj = j & 31;
+    return (j & 32) + (jj < 16 ? 8 * (jj >> 2) + (jj & 3) : 8 * ((jj - 16) >> 2) + 4 + (jj & 3));
+}
+
 // The elu+1 pass over a landed tile of the streaming kernels.  A tile's Q (or
 // K) is 2 NC blocks of 64 16-byte pieces; copy wave h copies blocks
 // h NC .. h NC + NC - 1 of each tensor it moves.  The pieces of pair h are a

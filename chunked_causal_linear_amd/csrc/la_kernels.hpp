@@ -184,6 +184,34 @@ struct DeltaFwdParams {
     int xcd_remap;
 };
 
+// FAVOR+ mapped inside the streaming kernels (la_favor.hip): 64 input
+// features, m in {64, 128, 256} random features, chunks of 64 rows, value
+// tiles of 64 columns.
+struct FavorParams {
+    const unsigned short* q;  // [BH, L, 64] (phase 3)
+    const unsigned short* k;  // [BH, L, 64]
+    const unsigned short* v;  // [BH, L, dv]
+    const unsigned short* W;  // [m, 64]
+    unsigned short* o;        // [BH, L, dv] bf16 (phase 3)
+    const float* P0;          // phase 3: [BH, n_groups * p0_sub, m, dv] exclusive prefixes, or null
+    const float* z0;          // phase 3: [BH, n_groups * p0_sub, m], or null
+    float* S;                 // phase 1: [BH, n_out, m, dv]
+    float* z;                 // phase 1: [BH, n_out, m] (when the normaliser is wanted)
+    int64_t L;
+    int64_t rows;             // phase 1: rows per run, a multiple of 64
+    int G;                    // phase 3: chunks per group
+    int n_groups;             // phase 3: groups per head; phase 1: runs computed per head
+    int n_out;                // phase 1: run stride of S and z per head
+    int n_dvt;                // value tiles per head
+    int dv;
+    int p0_sub;               // phase 3: prefix slots per group (group g starts at slot g p0_sub); 0 means 1
+    float in_scale;
+    int xcd_remap;
+};
+
+hipError_t run_favor_states(const FavorParams& p, int m, int norm, int64_t grid, hipStream_t s);
+hipError_t run_favor_fwd(const FavorParams& p, int m, int norm, int64_t grid, hipStream_t s);
+
 hipError_t run_delta_step(const DeltaStepParams& p, hipStream_t s);
 hipError_t run_delta_transform(const DeltaPrepParams& p, hipStream_t s);
 hipError_t run_delta_fwd(const DeltaFwdParams& p, hipStream_t s);
