@@ -2,32 +2,35 @@
 // 実装", the positive random features: phi(x)_a = exp(w_a . x - |x|^2 / 2) /
 // sqrt(m) for the m rows w_a of W, applied to queries and keys; the normalised
 // causal output and the RNN view's state and normaliser).  Raw 64-wide q and k
-// tiles are mapped on the matrix cores as they arrive, with W resident in LDS,
-// so the m-wide phi(q) and phi(k) never go through memory.
+// tiles are mapped on the matrix cores as they arrive; the m-wide phi(q) and
+// phi(k) never go through memory.
 //
-// Mapping (both kernels): for a tile of 64 rows, wave w takes one block of 16
-// rows and a range of feature blocks; W rows are the A operand and x rows the
-// B operand of 16x16x32 bf16 products over the 64 input features, so a lane
-// ends with four consecutive features a = 16 fb + 4 g + e of its row
-// r = 16 rb + l16, and phi = exp2(log2(e) s proj - log2(e) s^2 |x_r|^2 / 2 -
-// log2(m) / 2) (s = in_scale) is one fused multiply-add and one exp2 per
-// feature, packed to bf16 and written as 8 bytes.  Key rows past the end of the
-// sequence are mapped to zero.
+// Mapping: W stays in registers.  A wave maps a fixed range of feature blocks
+// (16 features each) for the rows it takes; for a 16-row block the product of
+// its x rows with W rows over the 64 input features is two 16x16x32 bf16
+// matrix-core steps, and each result element becomes
+// phi = exp2(log2(e) s proj - log2(e) s^2 |x|^2 / 2 - log2(m) / 2) (s =
+// in_scale): one fused multiply-add and one exp2.  The row norms come from the
+// x fragments the products use (two lane exchanges).  Key rows past the end of
+// the sequence map to zero.
 //
 //  * favor_states_kernel: phase 1, the state of a run of rows,
-//    S = phi(K)^T V and z = sum of phi(K) rows, with phi(k) carried as a bf16
-//    pair hi = bf16(phi), lo = bf16(phi - hi) (about 2^-17 relative), both
-//    multiplied: the long sums do not collect the bf16 rounding of phi.
+//    S = phi(K)^T V and z = the sum of the rows of phi(K).  Each wave owns
+//    a range of features of S for all value columns of its tile: it maps
+//    phi(k) with the features along the product's columns, so the results pack
+//    straight into the update's operand (features by keys) in registers, and
+//    sums z from the fp32 values.  phi(k) enters the update as a bf16 pair
+//    hi = bf16(phi), lo = bf16(phi - hi) (about 2^-17 relative): the long sums
+//    do not collect the bf16 rounding of phi.
 //  * favor_fwd_kernel: phase 3, the chunks (of 64 rows) of a group from its
 //    prefix state: O = phi(Q) P + tril(phi(Q) phi(K)^T) V, normalised by
 //    phi(Q) z + the row sums of tril(phi(Q) phi(K)^T), then P += phi(K)^T V,
-//    z += the column sums of phi(K).
-//
-// Eight waves, two per SIMD: state waves 0-3 own 16 value columns of the
-// m x 64 state each (fp32 accumulators, the layout of the other streaming
-// kernels: a packed pair is an operand in feature order); prep waves 4-7 issue
-// the direct-to-LDS copies of the raw tiles and the output stores and keep the
-// normaliser.  All eight waves map.
+//    z += the column sums of phi(K).  Eight waves, two per SIMD: state waves
+//    0-3 own 16 value columns of the m x 64 state each (fp32 accumulators; a
+//    packed pair of them is an operand in feature order) and map phi(q) for
+//    a quarter of the features; prep waves 4-7 issue the direct-to-LDS copies
+//    of the raw tiles and the output stores, map phi(k) for a quarter of the
+//    features and keep that quarter of z in registers.
 #include "la_fwd_pipe.hpp"
 
 namespace la {
@@ -48,74 +51,148 @@ struct alignas(16) RawStageKV {
     u16 v[64 * 64];
 };
 
-// phi of one 16-row block of a raw 64-wide tile for feature blocks FB0 .. FB0 + NFB - 1
-// into a [64 x M] bf16 tile (hi, and the residual lo when lo != nullptr);
-// rows at or past `valid` map to zero when zero_tail
-template <int M, int NFB>
-__device__ __forceinline__ void map_rows(const u16* W, const u16* x, int rb, int fb0, float s, bool zero_tail,
-                                         int valid, u16* hi, u16* lo, int lane) {
-    using namespace pipe;
-    constexpr int FSEG = M / 8;
+// W fragment of feature block fb: lane (g, l16) holds W[16 fb + l16][32 h + 8 g .. + 7]
+// in wf[h] (the A operand with features as rows, the B operand with features as columns)
+__device__ __forceinline__ void load_w_frag(const u16* W, int fb, int lane, bf16x8 (&wf)[2]) {
     const int l16 = lane % 16, g = lane / 16;
-    const int r = 16 * rb + l16;
-    // |x_r|^2 (the four lane groups compute the same row)
-    float xx = 0.f;
-#pragma unroll
-    for (int seg = 0; seg < 8; ++seg) {
-        const uint4 u = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(x) + tile_off<8>(r, seg * 8));
-        const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float a = __uint_as_float(w4[j] << 16), b = __uint_as_float(w4[j] & 0xFFFF0000u);
-            xx = fmaf(a, a, fmaf(b, b, xx));
-        }
-    }
-    const float c1 = kLog2e * s;
-    const float c0 = -0.5f * kLog2e * s * s * xx - 0.5f * __builtin_amdgcn_logf((float)M);
-    const bool dead = zero_tail && r >= valid;
-    const bf16x8 xb0 = row_op<8>(x, r, 0, g), xb1 = row_op<8>(x, r, 32, g);
-#pragma unroll 4
-    for (int f = 0; f < NFB; ++f) {
-        const int fb = fb0 + f;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = mfma_bf16(row_op<8>(W, 16 * fb + l16, 0, g), xb0, acc);
-        acc = mfma_bf16(row_op<8>(W, 16 * fb + l16, 32, g), xb1, acc);
-        float ph[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ph[e] = dead ? 0.f : __builtin_amdgcn_exp2f(fmaf(c1, acc[e], c0));
-        const uint32_t h0 = pack2_bf16(ph[0], ph[1]), h1 = pack2_bf16(ph[2], ph[3]);
-        const int off = tile_off<FSEG>(r, 16 * fb + 4 * g);
-        *reinterpret_cast<uint2*>(reinterpret_cast<char*>(hi) + off) = make_uint2(h0, h1);
-        if (lo != nullptr) {
-            const uint32_t l0 = pack2_bf16(ph[0] - __uint_as_float(h0 << 16), ph[1] - __uint_as_float(h0 & 0xFFFF0000u));
-            const uint32_t l1 = pack2_bf16(ph[2] - __uint_as_float(h1 << 16), ph[3] - __uint_as_float(h1 & 0xFFFF0000u));
-            *reinterpret_cast<uint2*>(reinterpret_cast<char*>(lo) + off) = make_uint2(l0, l1);
-        }
-    }
+    const u16* row = W + (16 * fb + l16) * 64 + 8 * g;
+    wf[0] = as_bf16x8(*reinterpret_cast<const uint4*>(row));
+    wf[1] = as_bf16x8(*reinterpret_cast<const uint4*>(row + 32));
 }
 
-// W [M x 64] bf16 into LDS (row-major, swizzled), by all threads of the workgroup
-template <int M>
-__device__ __forceinline__ void load_W(const u16* Wg, u16* Wl, int tid, int nthreads) {
-    using namespace pipe;
-    for (int i = tid; i < M * 8; i += nthreads) {
-        const int r = i / 8, seg = i % 8;
-        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(Wl) + tile_off<8>(r, seg * 8)) =
-            *reinterpret_cast<const uint4*>(Wg + r * 64 + seg * 8);
+// sum of squares of the 16 bf16 values of two fragments
+__device__ __forceinline__ float sumsq(const bf16x8& a, const bf16x8& b) {
+    const uint4 u = __builtin_bit_cast(uint4, a), v = __builtin_bit_cast(uint4, b);
+    const uint32_t w[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const float lo = __uint_as_float(w[j] << 16), hi = __uint_as_float(w[j] & 0xFFFF0000u);
+        s = fmaf(lo, lo, fmaf(hi, hi, s));
     }
+    return s;
 }
 
-// direct-to-LDS copy of this prep wave's share (two instructions) of one
-// 64 x 64 bf16 tile of rows r0 .. r0 + 63 (clamped to `last`) with row stride
-// `stride` (elements)
-__device__ __forceinline__ void copy_tile(const u16* base, int stride, int last, u16* dst, int pw, int lane) {
-    using namespace pipe;
+// |x_r|^2 for the row r = 16 rb + l16 whose fragments (x[r][8g .. 8g+7] and
+// x[r][32 + 8g ..]) this lane holds: the four lane groups' partial sums added
+__device__ __forceinline__ float row_norm(const bf16x8& a, const bf16x8& b) {
+    float s = sumsq(a, b);
+    s += __shfl_xor(s, 16);
+    s += __shfl_xor(s, 32);
+    return s;
+}
+
+__device__ __forceinline__ uint4 pack8(const float (&a)[4], const float (&b)[4]) {
+    return make_uint4(pack2_bf16(a[0], a[1]), pack2_bf16(a[2], a[3]), pack2_bf16(b[0], b[1]), pack2_bf16(b[2], b[3]));
+}
+// the residuals x - bf16(x) of eight values packed by pack8
+__device__ __forceinline__ uint4 pack8_lo(const float (&a)[4], const float (&b)[4], const uint4& h) {
+    auto r2 = [](float x0, float x1, uint32_t hw) {
+        return pack2_bf16(x0 - __uint_as_float(hw << 16), x1 - __uint_as_float(hw & 0xFFFF0000u));
+    };
+    return make_uint4(r2(a[0], a[1], h.x), r2(a[2], a[3], h.y), r2(b[0], b[1], h.z), r2(b[2], b[3], h.w));
+}
+
+// wait until at most `after` copy groups of N instructions each are in flight
+template <int N, int MAXAFTER>
+__device__ __forceinline__ void wait_groups(int after) {
+    using pipe::wait_vm;
+    if constexpr (MAXAFTER >= 4)
+        if (after >= 4) {
+            wait_vm<4 * N>();
+            return;
+        }
+    if constexpr (MAXAFTER >= 3)
+        if (after >= 3) {
+            wait_vm<3 * N>();
+            return;
+        }
+    if constexpr (MAXAFTER >= 2)
+        if (after >= 2) {
+            wait_vm<2 * N>();
+            return;
+        }
+    if constexpr (MAXAFTER >= 1)
+        if (after >= 1) {
+            wait_vm<N>();
+            return;
+        }
+    wait_vm<0>();
+}
+
+// Lane base addresses for the swizzled tiles (tile_off: segment index XOR
+// row).  For a 16-byte row read of row R0 + l16 at elements K0 + 8g .. (R0 a
+// multiple of 16, K0 of 32) the segment index is ((4 ks + g) ^ (R0 + l16)) mod
+// NSEG with ks = K0 / 32: its low four bits depend on the lane and on ks mod 4
+// only, its higher bits on R0 and ks only.  So four lane registers (one per
+// ks mod 4) and a compile-time immediate give every such address, with no
+// per-access arithmetic.
+template <int NSEG>
+struct RowAddr {
+    int b[4];
+    __device__ __forceinline__ explicit RowAddr(int lane) {
+        const int l16 = lane & 15, g = lane >> 4, B = g ^ l16;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int b = pw * 2 + i, slot = b * WAVE + lane;
-        const int r = slot / 8, seg = (slot % 8) ^ (r & 7);
-        dma16(base, (uint32_t)(((r < last ? r : last) * stride + seg * 8) * 2), lds_addr(dst) + b * WAVE * 16);
+        for (int c = 0; c < 4; ++c) b[c] = l16 * NSEG * 16 + (((4 * c) ^ B) & (NSEG - 1)) * 16;
     }
+    // byte offset of pipe::tile_off<NSEG>(R0 + l16, K0 + 8g)
+    __device__ __forceinline__ int off(int R0, int K0) const {
+        const int ks = K0 / 32;
+        return b[ks & 3] + R0 * NSEG * 16 + ((((4 * ks) ^ R0) & ~15) & (NSEG - 1)) * 16;
+    }
+};
+
+// The same for the transposed 8-byte reads of a column operand: rows K0 + H +
+// 4g + rr (K0 a multiple of 32, H 0 or 16, rr = (l % 16) / 4) at columns CB +
+// 8c + 4hf (CB a multiple of 32, c = l % 4).
+template <int NSEG>
+struct ColAddr {
+    int b[4];
+    __device__ __forceinline__ explicit ColAddr(int lane) {
+        const int g = lane >> 4, rr = (lane & 15) >> 2, c = lane & 3, rl = 4 * g + rr, B = c ^ rl;
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) b[cc] = rl * NSEG * 16 + (((4 * cc) ^ B) & (NSEG - 1)) * 16;
+    }
+    // byte offset of pipe::tile_off<NSEG>(K0 + H + 4g + rr, CB + 8c + 4hf)
+    __device__ __forceinline__ int off(int K0, int H, int CB, int hf) const {
+        const int ks = CB / 32;
+        return b[ks & 3] + (K0 + H) * NSEG * 16 + ((((4 * ks) ^ (K0 + H)) & ~15) & (NSEG - 1)) * 16 + 8 * hf;
+    }
+};
+
+__device__ __forceinline__ bf16x8 row_at(const u16* tile, int off) {
+    return as_bf16x8(*reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(tile) + off));
+}
+// the column operand (keys K0 .. K0 + 31 in operand order) from its two transposed reads
+template <int NSEG>
+__device__ __forceinline__ bf16x8 col_at(const u16* tile, const ColAddr<NSEG>& ca, int K0, int CB, int hf) {
+    const char* t = reinterpret_cast<const char*>(tile);
+    const uint2 lo = pipe::tr_read(t + ca.off(K0, 0, CB, hf));
+    const uint2 hi = pipe::tr_read(t + ca.off(K0, 16, CB, hf));
+    return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
+// Hands a value loaded before a loop to an empty asm statement: the compiler
+// then waits for the load there, not at the first use inside the loop, where
+// its memory-counter wait would also hold back the copies in flight.
+template <typename T>
+__device__ __forceinline__ void settle(T& v) {
+    asm volatile("" : "+v"(v));
+}
+
+// one direct-to-LDS copy of 1 KiB (rows 8b .. 8b + 7 of a 64 x 64 bf16 tile,
+// rows clamped to `last`, row stride `stride` elements) into piece b of dst
+__device__ __forceinline__ void copy_piece(const u16* base, int stride, int last, u16* dst, int b, int lane) {
+    using namespace pipe;
+    const int slot = b * WAVE + lane;
+    const int r = slot / 8, seg = (slot % 8) ^ (r & 7);
+    // the copy takes its base and LDS address from scalar registers: both are
+    // wave-uniform, made explicit for the compiler
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t alo = __builtin_amdgcn_readfirstlane((uint32_t)a), ahi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const u16* ub = reinterpret_cast<const u16*>(((uint64_t)ahi << 32) | alo);
+    dma16(ub, (uint32_t)(((r < last ? r : last) * stride + seg * 8) * 2),
+          __builtin_amdgcn_readfirstlane(lds_addr(dst) + b * WAVE * 16));
 }
 
 }  // namespace
@@ -123,121 +200,229 @@ __device__ __forceinline__ void copy_tile(const u16* base, int stride, int last,
 // ---------------------------------------------------------------------------
 // phase 1: one workgroup per (head, run of rows, 64 value columns)
 // ---------------------------------------------------------------------------
+// Wave w owns FPW feature blocks from fb0 for the 32-key halves kh0 .. kh0 +
+// NKH - 1 of every tile (all four row blocks when there are at least eight
+// feature blocks; at m = 64 two waves share a feature block, one per half, and
+// add their sums at the end).  Per tile: the x fragments of its row blocks,
+// the mapping (row blocks as rows, features as columns: lane (g, l16) gets
+// rows 16 rb + 4g + i of feature 16 fb + l16), the operand pair of each
+// 32-key half from the results of its two row blocks (key order 4g + i, then
+// 16 + 4g + i: the order of the value tile's column operand), then the
+// update S[f][16 cb + ..] += phi(K)^T V.  Every wave copies one eighth of each
+// tile and waits for its own copies; one barrier per tile.
 template <int M, bool Z>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void favor_states_kernel(FavorParams p) {
     using namespace pipe;
-    constexpr int FSEG = M / 8, NKS = M / 32;
-    constexpr int FIXED = M * 64 * 2 + 2 * 64 * M * 2;  // W, hi, lo
-    constexpr int NFIT = (int)((160 * 1024 - FIXED) / sizeof(RawStageKV));
-    constexpr int NSTAGE = NFIT < 4 ? NFIT : 4;
-    constexpr int NL = 4;  // copy instructions per tile and prep wave
-    static_assert(NSTAGE >= 2, "stages");
+    constexpr int NFB = M / 16;
+    constexpr int KSPLIT = NFB >= 8 ? 1 : 8 / NFB;
+    constexpr int FPW = NFB >= 8 ? NFB / 8 : 1;
+    constexpr int NRB = 4 / KSPLIT;
+    constexpr int NKH = NRB / 2;
+    constexpr int NSTAGE = 6;
+    static_assert(FPW * 8 / KSPLIT == NFB && NKH >= 1, "feature split");
 
-    __shared__ __attribute__((aligned(16))) u16 Wl[M * 64];
     __shared__ RawStageKV st[NSTAGE];
-    __shared__ __attribute__((aligned(16))) u16 hi[64 * M];
-    __shared__ __attribute__((aligned(16))) u16 lo[64 * M];
+    __shared__ __attribute__((aligned(16))) float crl[NSTAGE][64];  // row constants of each stage's keys
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);
-    const bool prep = wave >= 4;
-    const int pw = wave & 3;
     const int lane = tid % WAVE, l16 = lane % 16, g = lane / 16;
+    const int fb0 = (wave % (8 / KSPLIT)) * FPW;
+    const int kh0 = (wave / (8 / KSPLIT)) * NKH;
     const int wi = work_index(p.xcd_remap);
     const int jt = wi % p.n_dvt;
     const int64_t n = (wi / p.n_dvt) % p.n_groups;
     const int64_t bh = wi / ((int64_t)p.n_dvt * p.n_groups);
-    const int col0 = jt * 64, cw = 16 * pw;
+    const int col0 = jt * 64;
     const int64_t L = p.L;
     const int dv = p.dv;
     const int64_t r_begin = n * p.rows;
     const int64_t r_end = r_begin + p.rows < L ? r_begin + p.rows : L;
     const int64_t t_begin = r_begin / 64, t_end = (r_end + 63) / 64;
-    auto valid_of = [&](int64_t t) -> int { return (int)(L - t * 64 < 64 ? L - t * 64 : 64); };
     const u16* kh = p.k + bh * L * 64;
     const u16* vh = p.v + bh * L * dv + col0;
+    const float c1 = kLog2e * p.in_scale;
+    const float cA = -0.5f * kLog2e * p.in_scale * p.in_scale;
+    const float cB = -0.5f * __builtin_amdgcn_logf((float)M);
     auto issue = [&](int64_t t, RawStageKV& s) __attribute__((always_inline)) {
         const int last = (int)(L - 1 - t * 64);
-        copy_tile(kh + t * 64 * 64, 64, last, s.k, pw, lane);
-        copy_tile(vh + t * 64 * dv, dv, last, s.v, pw, lane);
+        copy_piece(kh + t * 64 * 64, 64, last, s.k, wave, lane);
+        copy_piece(vh + t * 64 * dv, dv, last, s.v, wave, lane);
     };
     auto land = [&](int64_t t) __attribute__((always_inline)) {
         const int64_t newest = t + NSTAGE - 2 < t_end - 1 ? t + NSTAGE - 2 : t_end - 1;
-        const int after = (int)(newest - t);
-        if constexpr (NSTAGE >= 4)
-            if (after >= 2) {
-                wait_vm<2 * NL>();
-                return;
-            }
-        if constexpr (NSTAGE >= 3)
-            if (after >= 1) {
-                wait_vm<NL>();
-                return;
-            }
-        wait_vm<0>();
+        wait_groups<2, NSTAGE - 2>((int)(newest - t));
+    };
+    // Row constants log2(e) (-s^2 |k_r|^2 / 2) - log2(m) / 2 of the eight key
+    // rows this wave copied (8w .. 8w + 7) of tile t, once its copy is in;
+    // -inf past the end of the sequence, so that those rows map to exp2(-inf) = 0.
+    auto row_consts = [&](int64_t t, const RawStageKV& s, float* out) __attribute__((always_inline)) {
+        const int r = 8 * wave + lane / 8, seg = lane % 8;
+        const uint4 u = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(s.k) + tile_off<8>(r, seg * 8));
+        const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+        float q = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float a = __uint_as_float(w4[j] << 16), b = __uint_as_float(w4[j] & 0xFFFF0000u);
+            q = fmaf(a, a, fmaf(b, b, q));
+        }
+        q += __shfl_xor(q, 1);
+        q += __shfl_xor(q, 2);
+        q += __shfl_xor(q, 4);
+        if (seg == 0) out[r] = t * 64 + r < L ? fmaf(cA, q, cB) : -__builtin_inff();
     };
 
-    if (prep)
-        for (int s0 = 0; s0 < NSTAGE - 1; ++s0)
-            if (t_begin + s0 < t_end) issue(t_begin + s0, st[s0]);
-    load_W<M>(p.W, Wl, tid, 8 * WAVE);
-    if (prep) land(t_begin);
+    for (int s0 = 0; s0 < NSTAGE - 1; ++s0)
+        if (t_begin + s0 < t_end) issue(t_begin + s0, st[s0]);
+    bf16x8 wf[FPW][2];
+#pragma unroll
+    for (int f = 0; f < FPW; ++f) {
+        load_w_frag(p.W, fb0 + f, lane, wf[f]);
+        settle(wf[f][0]);
+        settle(wf[f][1]);
+    }
+    land(t_begin);
+    if (t_begin < t_end) row_consts(t_begin, st[0], crl[0]);
 
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-    f32x4 P[NKS][2];
+    // bf16 ones: the operand that turns an update step into a column sum (z)
+    const bf16x8 ones = as_bf16x8(make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
+    f32x4 P[FPW][4], Zs[FPW];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) P[ks][0] = P[ks][1] = zero4;
-    float zacc = 0.f;  // prep waves: z of feature 64 pw + lane
-    const int c4 = 4 * (lane & 3), c8 = 8 * (lane & 3);
+    for (int f = 0; f < FPW; ++f) {
+        Zs[f] = zero4;
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) P[f][cb] = zero4;
+    }
 
     int si = 0;
     for (int64_t t = t_begin; t < t_end; ++t) {
         RawStageKV& s = st[si];
         const int sp = si == 0 ? NSTAGE - 1 : si - 1;
-        __syncthreads();  // B1(t): tile t is in; the products of tile t - 1 are done
-        if (prep && t + NSTAGE - 1 < t_end) issue(t + NSTAGE - 1, st[sp]);
-        // every wave maps one 16-row block, half of the feature blocks
-        map_rows<M, M / 32>(Wl, s.k, wave & 3, (wave >> 2) * (M / 32), p.in_scale, true, valid_of(t), hi, lo, lane);
-        __syncthreads();  // B2(t): hi and lo of tile t are complete
-        if (!prep) {
-            bf16x8 vb[2];
+        const int sn = si == NSTAGE - 1 ? 0 : si + 1;
+        // the lane's values formed again each tile (opaque to the compiler), so
+        // that the LDS addresses derived from them are not all held in registers
+        int lane_o = lane;
+        asm volatile("" : "+v"(lane_o));
+        const int l16o = lane_o % 16, go = lane_o / 16, c4 = 4 * (lane_o & 3);
+        __syncthreads();  // B(t): tile t and its row constants are in; every wave is done with tile t - 1
+        if (t + NSTAGE - 1 < t_end) issue(t + NSTAGE - 1, st[sp]);
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) vb[kk] = col_op<8>(s.v, 32 * kk, cw + c4, lane);
+        for (int kq = 0; kq < NKH; ++kq) {
+            const int khh = kh0 + kq;
+            // the two row blocks of this 32-key half and the constants of rows 16 rb + 4g + i
+            bf16x8 xa[2][2];
+            float4 cr[2];
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
+            for (int hb = 0; hb < 2; ++hb) {
+                const int rb = 2 * khh + hb;
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-                    for (int hf = 0; hf < 2; ++hf) {
-                        P[ks][hf] = mfma_bf16(col_op<FSEG>(hi, 32 * kk, 32 * ks + c8 + 4 * hf, lane), vb[kk], P[ks][hf]);
-                        P[ks][hf] = mfma_bf16(col_op<FSEG>(lo, 32 * kk, 32 * ks + c8 + 4 * hf, lane), vb[kk], P[ks][hf]);
-                    }
-        } else {
-            if (Z && 64 * pw < M) {
-                const int a = 64 * pw + lane;
-                float acc = 0.f;
-#pragma unroll 8
-                for (int r = 0; r < 64; ++r) {
-                    const int off = tile_off<FSEG>(r, a);
-                    acc += bf2f(*reinterpret_cast<const u16*>(reinterpret_cast<const char*>(hi) + off)) +
-                           bf2f(*reinterpret_cast<const u16*>(reinterpret_cast<const char*>(lo) + off));
-                }
-                zacc += acc;
+                for (int h = 0; h < 2; ++h) xa[hb][h] = row_op<8>(s.k, 16 * rb + l16o, 32 * h, go);
+                cr[hb] = *reinterpret_cast<const float4*>(&crl[si][16 * rb + 4 * go]);
             }
-            if (t + 1 < t_end) land(t + 1);
+            bf16x8 vb[4];
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) vb[cb] = col_op<8>(s.v, 32 * khh, 16 * cb + c4, lane_o);
+#pragma unroll
+            for (int f = 0; f < FPW; ++f) {
+                float ph[2][4];
+#pragma unroll
+                for (int hb = 0; hb < 2; ++hb) {
+                    f32x4 acc = mfma_bf16(xa[hb][0], wf[f][0], zero4);
+                    acc = mfma_bf16(xa[hb][1], wf[f][1], acc);
+                    ph[hb][0] = __builtin_amdgcn_exp2f(fmaf(c1, acc[0], cr[hb].x));
+                    ph[hb][1] = __builtin_amdgcn_exp2f(fmaf(c1, acc[1], cr[hb].y));
+                    ph[hb][2] = __builtin_amdgcn_exp2f(fmaf(c1, acc[2], cr[hb].z));
+                    ph[hb][3] = __builtin_amdgcn_exp2f(fmaf(c1, acc[3], cr[hb].w));
+                }
+                const uint4 hi = pack8(ph[0], ph[1]);
+                const uint4 lo = pack8_lo(ph[0], ph[1], hi);
+#pragma unroll
+                for (int cb = 0; cb < 4; ++cb) {
+                    P[f][cb] = mfma_bf16(as_bf16x8(hi), vb[cb], P[f][cb]);
+                    P[f][cb] = mfma_bf16(as_bf16x8(lo), vb[cb], P[f][cb]);
+                }
+                if constexpr (Z) {
+                    Zs[f] = mfma_bf16(as_bf16x8(hi), ones, Zs[f]);
+                    Zs[f] = mfma_bf16(as_bf16x8(lo), ones, Zs[f]);
+                }
+            }
         }
-        si = si == NSTAGE - 1 ? 0 : si + 1;
+        if (t + 1 < t_end) {
+            land(t + 1);
+            row_consts(t + 1, st[sn], crl[sn]);
+        }
+        si = sn;
     }
-    if (!prep) {
-        float* S = p.S + ((bh * p.n_out + n) * M) * (int64_t)dv + col0 + cw + l16;
+    float* S = p.S + ((bh * p.n_out + n) * M) * (int64_t)dv + col0 + l16;
+    float* zo = (Z && jt == 0) ? p.z + (bh * p.n_out + n) * M : nullptr;
+    if constexpr (KSPLIT > 1) {
+        // the second key half's sums to the first through the (idle) stages
+        __syncthreads();
+        float* red = reinterpret_cast<float*>(&st[0]);
+        const int pw = wave % (8 / KSPLIT);
+        if (wave >= 8 / KSPLIT) {
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
+            for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf)
+                for (int e = 0; e < 4; ++e) red[((pw * 4 + cb) * 4 + e) * WAVE + lane] = P[0][cb][e];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) S[(int64_t)(32 * ks + 8 * g + 4 * hf + e) * dv] = P[ks][hf][e];
-    } else if (Z && jt == 0 && 64 * pw < M) {
-        p.z[(bh * p.n_out + n) * M + 64 * pw + lane] = zacc;
+            for (int e = 0; e < 4; ++e) red[((8 / KSPLIT) * 16 + pw * 4 + e) * WAVE + lane] = Zs[0][e];
+        }
+        __syncthreads();
+        if (wave < 8 / KSPLIT) {
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) P[0][cb][e] += red[((pw * 4 + cb) * 4 + e) * WAVE + lane];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Zs[0][e] += red[((8 / KSPLIT) * 16 + pw * 4 + e) * WAVE + lane];
+        } else {
+            return;
+        }
+    }
+    // S[f][feature 16 fb + 4g + e][column 16 cb + l16]; z of feature 16 fb + 4g + e
+    // is in every column of Zs
+#pragma unroll
+    for (int f = 0; f < FPW; ++f) {
+        const int a0 = 16 * (fb0 + f);
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) S[(int64_t)(a0 + 4 * g + e) * dv + 16 * cb] = P[f][cb][e];
+        if (Z && zo != nullptr && l16 == 0)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) zo[a0 + 4 * g + e] = Zs[f][e];
+    }
+}
+
+// Phase-3 mapping of one tile (q or k): the wave's FPW feature blocks from
+// fb0 for all four row blocks (features as rows, rows as columns: lane (g, l16)
+// gets features 16 fb + 4g + i of row 16 rb + l16), with the row constants cr
+// (-inf for key rows past the end, which then map to 0), stored into the phi tile.
+template <int M>
+__device__ __forceinline__ void map_tile(const bf16x8 (&wf)[M / 64][2], const u16* x, const RowAddr<8>& ra8, u16* phi,
+                                         int fb0, float c1, const float* cr, int lane) {
+    using namespace pipe;
+    constexpr int FSEG = M / 8, FPW = M / 64;
+    const int l16 = lane % 16, g = lane / 16;
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+        const int r = 16 * rb + l16;
+        const bf16x8 x0 = row_at(x, ra8.off(16 * rb, 0)), x1 = row_at(x, ra8.off(16 * rb, 32));
+        const float c = cr[r];
+#pragma unroll
+        for (int f = 0; f < FPW; ++f) {
+            f32x4 acc = mfma_bf16(wf[f][0], x0, zero4);
+            acc = mfma_bf16(wf[f][1], x1, acc);
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(c1, acc[0], c));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(c1, acc[1], c));
+            const float p2 = __builtin_amdgcn_exp2f(fmaf(c1, acc[2], c));
+            const float p3 = __builtin_amdgcn_exp2f(fmaf(c1, acc[3], c));
+            *reinterpret_cast<uint2*>(reinterpret_cast<char*>(phi) + tile_off<FSEG>(r, 16 * (fb0 + f) + 4 * g)) =
+                make_uint2(pack2_bf16(p0, p1), pack2_bf16(p2, p3));
+        }
     }
 }
 
@@ -245,30 +430,34 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // phase 3: one workgroup per (head, group of chunks of 64, 64 value columns)
 // ---------------------------------------------------------------------------
 // Three barriers per chunk t:
-//   B1(t): tile t is in; the state waves are done with chunk t - 1 (its output
-//          rows are in its stage's V columns; phi(q), phi(k) and the score tile
-//          are free); the prep waves have added chunk t - 1 to z;
+//   B1(t): tile t and its row constants are in; the state waves are done with
+//          chunk t - 1 (its output rows are in its stage's V columns; phi(q),
+//          phi(k) and the score tile are free; z after chunk t - 1 is in zhl);
 //   B2(t): phi(q) and phi(k) of tile t are complete (all eight waves map);
 //   B3(t): the score tile (tril(phi(Q) phi(K)^T), columns in operand key
-//          order) is complete and, with the normaliser, both parts of each
-//          row's denominator: phi(q_i) . z and sum_{j <= i} S_ij.
-// Right after B1(t) the prep waves store chunk t - 1's outputs and issue tile
-// t + 1 into the stage they leave.  After B3 the state waves form the outputs
-// and update their state while the prep waves add the chunk's keys to z and
-// wait for tile t + 1.
+//          order) and, with the normaliser, phi(q_i) . z for every row.
+// The score blocks are computed transposed (keys as rows): a lane then holds
+// four consecutive keys of one query row, one 8-byte store.  The state waves
+// likewise form O^T (value columns as rows: four consecutive columns of one
+// output row per lane), and the row sums of the score tile come from the
+// matrix cores with a ones operand, in the same layout.  Right after B1(t) the
+// prep waves store chunk t - 1's outputs and issue tile t + 1 into the stage
+// they leave; after B3 they wait for it and form its row constants.
 template <int M, bool NORM>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void favor_fwd_kernel(FavorParams p) {
     using namespace pipe;
-    constexpr int FSEG = M / 8, NKS = M / 32;
+    constexpr int FSEG = M / 8, NKS = M / 32, FPW = M / 64;
+    // z is kept by the state waves, KPW 32-feature steps each (waves pw < NKS / KPW)
+    constexpr int KPW = NKS >= 4 ? NKS / 4 : 1;
 
-    __shared__ __attribute__((aligned(16))) u16 Wl[M * 64];
     __shared__ RawStage st[2];
     __shared__ __attribute__((aligned(16))) u16 fq[64 * M];
     __shared__ __attribute__((aligned(16))) u16 fk[64 * M];
     __shared__ __attribute__((aligned(16))) u16 stile[64 * 64];
-    __shared__ __attribute__((aligned(16))) float zl[NORM ? M : 4];
-    __shared__ __attribute__((aligned(16))) float rowsum[64];
-    __shared__ __attribute__((aligned(16))) float qz[64];
+    __shared__ __attribute__((aligned(16))) float crl[2][2][64];  // row constants [stage][q, k][row]
+    // z before the chunk as operand pieces: [hi, lo][32-feature step ks][lane group g]
+    __shared__ __attribute__((aligned(16))) uint4 zhl[NORM ? 2 * NKS * 4 : 1];
+    __shared__ __attribute__((aligned(16))) float qzl[64];  // phi(q_i) . z
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);
@@ -280,6 +469,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int grp = (wi / p.n_dvt) % p.n_groups;
     const int64_t bh = wi / ((int64_t)p.n_dvt * p.n_groups);
     const int col0 = jt * 64, cw = 16 * pw;
+    const int fb0 = pw * FPW;  // first feature block this wave maps (of q or of k)
     const int64_t L = p.L;
     const int dv = p.dv;
     const int64_t n_tiles = (L + 63) / 64;
@@ -291,13 +481,36 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const u16* vh = p.v + bh * L * dv + col0;
     const int64_t slot = (bh * p.n_groups + grp) * (int64_t)(p.p0_sub > 1 ? p.p0_sub : 1);
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    const bf16x8 ones = as_bf16x8(make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
+    const float c1 = kLog2e * p.in_scale;
+    const float cA = -0.5f * kLog2e * p.in_scale * p.in_scale;
+    const float cB = -0.5f * __builtin_amdgcn_logf((float)M);
 
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     auto issue = [&](int64_t t, RawStage& s) __attribute__((always_inline)) {
         const int last = (int)(L - 1 - t * 64);
-        copy_tile(qh + t * 64 * 64, 64, last, s.q, pw, lane);
-        copy_tile(kh + t * 64 * 64, 64, last, s.k, pw, lane);
-        copy_tile(vh + t * 64 * dv, dv, last, s.v, pw, lane);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            copy_piece(qh + t * 64 * 64, 64, last, s.q, pw * 2 + i, lane);
+            copy_piece(kh + t * 64 * 64, 64, last, s.k, pw * 2 + i, lane);
+            copy_piece(vh + t * 64 * dv, dv, last, s.v, pw * 2 + i, lane);
+        }
+    };
+    // Row constants log2(e) (-s^2 |x_r|^2 / 2) - log2(m) / 2 of the 16 q and k
+    // rows this prep wave copied (16 pw .. 16 pw + 15); -inf for key rows past
+    // the end of the sequence.
+    auto row_consts = [&](int64_t t, const RawStage& s, float (*out)[64]) __attribute__((always_inline)) {
+        const int r = 16 * pw + lane / 4, qd = lane % 4;
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+            const char* tile = reinterpret_cast<const char*>(x == 0 ? s.q : s.k);
+            const uint4 u0 = *reinterpret_cast<const uint4*>(tile + tile_off<8>(r, 16 * qd));
+            const uint4 u1 = *reinterpret_cast<const uint4*>(tile + tile_off<8>(r, 16 * qd + 8));
+            float q = sumsq(as_bf16x8(u0), as_bf16x8(u1));
+            q += __shfl_xor(q, 1);
+            q += __shfl_xor(q, 2);
+            if (qd == 0) out[x][r] = (x == 1 && t * 64 + r >= L) ? -__builtin_inff() : fmaf(cA, q, cB);
+        }
     };
     // output rows from the V tile of a stage: piece (pw * 2 + i) * 64 + lane
     auto read_out = [&](const RawStage& s, u32x4 (&ob)[2]) __attribute__((always_inline)) {
@@ -317,15 +530,35 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             if (r < valid) __builtin_nontemporal_store(ob[i], reinterpret_cast<u32x4*>(o + (int64_t)r * dv + seg * 8));
         }
     };
+    const bool has_z = pw < NKS / KPW;  // this state wave keeps steps KPW pw .. KPW pw + KPW - 1 of z
+    // z after this state wave's update, as bf16 hi / lo operand pieces
+    auto put_z = [&](const f32x4 (&Zs)[KPW][2]) __attribute__((always_inline)) {
+        if (l16 == 0)
+#pragma unroll
+            for (int k2 = 0; k2 < KPW; ++k2) {
+                const float a[4] = {Zs[k2][0][0], Zs[k2][0][1], Zs[k2][0][2], Zs[k2][0][3]};
+                const float b[4] = {Zs[k2][1][0], Zs[k2][1][1], Zs[k2][1][2], Zs[k2][1][3]};
+                const uint4 hi = pack8(a, b);
+                zhl[(KPW * pw + k2) * 4 + g] = hi;
+                zhl[(NKS + KPW * pw + k2) * 4 + g] = pack8_lo(a, b, hi);
+            }
+    };
 
-    // prologue: the first tile, W, the group's prefix state and normaliser
+    // prologue: the first tile and its row constants, W, the group's prefix state and normaliser
     if (prep) issue(t_begin, st[0]);
-    load_W<M>(p.W, Wl, tid, 8 * WAVE);
+    bf16x8 wf[FPW][2];
+#pragma unroll
+    for (int f = 0; f < FPW; ++f) load_w_frag(p.W, fb0 + f, lane, wf[f]);
     f32x4 P[NKS][2];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) P[ks][0] = P[ks][1] = zero4;
+    // state waves: z of features 32 (KPW pw + k2) + 8g + 4hf + i (every l16)
+    f32x4 Zs[KPW][2];
+#pragma unroll
+    for (int k2 = 0; k2 < KPW; ++k2) Zs[k2][0] = Zs[k2][1] = zero4;
+    const bool has_prefix = grp > 0;
     if (!prep) {
-        if (p.P0 != nullptr && grp > 0) {
+        if (p.P0 != nullptr && has_prefix) {
             const float* P0 = p.P0 + (slot * M) * (int64_t)dv + col0 + cw + l16;
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks)
@@ -334,16 +567,47 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
                     for (int e = 0; e < 4; ++e) P[ks][hf][e] = P0[(int64_t)(32 * ks + 8 * g + 4 * hf + e) * dv];
         }
-    } else if (NORM && 64 * pw < M) {
-        zl[64 * pw + lane] = (p.z0 != nullptr && grp > 0) ? p.z0[slot * M + 64 * pw + lane] : 0.f;
+        if constexpr (NORM) {
+            if (has_z) {
+                if (p.z0 != nullptr && has_prefix)
+#pragma unroll
+                    for (int k2 = 0; k2 < KPW; ++k2)
+#pragma unroll
+                        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                Zs[k2][hf][e] = p.z0[slot * M + 32 * (KPW * pw + k2) + 8 * g + 4 * hf + e];
+                put_z(Zs);
+            }
+        }
     }
-    if (prep) wait_vm<0>();
+#pragma unroll
+    for (int f = 0; f < FPW; ++f) {
+        settle(wf[f][0]);
+        settle(wf[f][1]);
+    }
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        settle(P[ks][0]);
+        settle(P[ks][1]);
+    }
+#pragma unroll
+    for (int k2 = 0; k2 < KPW; ++k2) {
+        settle(Zs[k2][0]);
+        settle(Zs[k2][1]);
+    }
+    if (prep) {
+        wait_vm<0>();
+        row_consts(t_begin, st[0], crl[0]);
+    }
+    const RowAddr<FSEG> raf(lane);
+    const RowAddr<8> ra8(lane);
+    const ColAddr<FSEG> caf(lane);
 
     int si = 0;
     for (int64_t t = t_begin; t < t_end; ++t) {
         RawStage& s = st[si];
         RawStage& sn = st[si ^ 1];
-        const int valid = valid_of(t);
         // the lane's values formed again each chunk (opaque to the compiler), so
         // that the LDS addresses derived from them are not all held in registers
         // across the chunk loop
@@ -360,85 +624,58 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 store_out(t - 1, ob);
             }
             if (t + 1 < t_end) issue(t + 1, sn);
-            if (NORM && pw == 0) rowsum[lane] = 0.f;
         }
-        // phi(q) (waves 0-3) and phi(k) (waves 4-7), one 16-row block each
-        map_rows<M, M / 16>(Wl, prep ? s.k : s.q, pw, 0, p.in_scale, prep, valid, prep ? fk : fq, nullptr, lane_o);
+        // phi(q) (waves 0-3) and phi(k) (waves 4-7) of feature blocks fb0 .. fb0 + FPW - 1
+        map_tile<M>(wf, prep ? s.k : s.q, ra8, prep ? fk : fq, fb0, c1, crl[si][prep ? 1 : 0], lane_o);
         __syncthreads();  // B2(t)
-        // score blocks (ib, jb), jb <= ib (b = 0..9), and the two blocks above the
-        // diagonal the 32-key operand reads also cover, (0, 1) and (2, 3)
-        // (b = 10, 11), as zeros: wave w takes b = w and, for w < 4, b = w + 8
+        // score blocks (ib, jb), jb <= ib (b = 0..9), as S^T (lane (g, l16): keys
+        // 16 jb + 4g + e of query row 16 ib + l16), and the two blocks above the
+        // diagonal the 32-key operand reads also cover, (0, 1) and (2, 3) (b = 10,
+        // 11), as zeros: wave w takes b = w and, for w < 4, b = w + 8
 #pragma unroll
         for (int pass = 0; pass < 2; ++pass) {
             const int b = wave + 8 * pass;
             if (b < 12) {
-                if (b >= 10) {
-                    const int ib = b == 10 ? 0 : 2;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        *reinterpret_cast<u16*>(reinterpret_cast<char*>(stile) +
-                                                tile_off<8>(16 * ib + 4 * g + e, perm_pos(16 * (ib + 1) + l16))) = 0;
-                } else {
-                    const int ib = b < 1 ? 0 : (b < 3 ? 1 : (b < 6 ? 2 : 3));
-                    const int jb = b - ib * (ib + 1) / 2;
+                const int ib = b < 1 ? 0 : (b < 3 ? 1 : (b < 6 ? 2 : (b < 10 ? 3 : (b == 10 ? 0 : 2))));
+                const int jb = b < 10 ? b - ib * (ib + 1) / 2 : ib + 1;
+                const int i = 16 * ib + l16;
+                uint2 w2 = make_uint2(0u, 0u);
+                if (b < 10) {
                     f32x4 acc = zero4;
 #pragma unroll
                     for (int ks = 0; ks < NKS; ++ks)
-                        acc = mfma_bf16(row_op<FSEG>(fq, 16 * ib + l16, 32 * ks, g),
-                                        row_op<FSEG>(fk, 16 * jb + l16, 32 * ks, g), acc);
-                    const int j = 16 * jb + l16;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int i = 16 * ib + 4 * g + e;
-                        const float sv = j <= i ? acc[e] : 0.f;
-                        *reinterpret_cast<u16*>(reinterpret_cast<char*>(stile) + tile_off<8>(i, perm_pos(j))) = f2bf(sv);
-                        if constexpr (NORM) {
-                            // the row's partial sum over this block's 16 keys
-                            float rs = sv;
-                            rs += __shfl_xor(rs, 1);
-                            rs += __shfl_xor(rs, 2);
-                            rs += __shfl_xor(rs, 4);
-                            rs += __shfl_xor(rs, 8);
-                            if (l16 == 0) atomicAdd(&rowsum[i], rs);
-                        }
-                    }
+                        acc = mfma_bf16(row_at(fk, raf.off(16 * jb, 32 * ks)), row_at(fq, raf.off(16 * ib, 32 * ks)), acc);
+                    const int j0 = 16 * jb + 4 * g;
+                    w2 = make_uint2(pack2_bf16(j0 <= i ? acc[0] : 0.f, j0 + 1 <= i ? acc[1] : 0.f),
+                                    pack2_bf16(j0 + 2 <= i ? acc[2] : 0.f, j0 + 3 <= i ? acc[3] : 0.f));
                 }
+                *reinterpret_cast<uint2*>(reinterpret_cast<char*>(stile) + tile_off<8>(i, perm_pos(16 * jb + 4 * g))) = w2;
             }
         }
-        if (NORM && prep) {
-            // phi(q_i) . z for row i = 16 pw + l16, the four lane groups a quarter of the features each
-            const int i = 16 * pw + l16;
-            float acc = 0.f;
+        if constexpr (NORM) {
+            if (prep) {
+                // phi(q_r) . z for rows 16 ib + 4g + e (ib = pw): z as bf16 hi + lo
+                f32x4 acc = zero4;
 #pragma unroll
-            for (int c = 0; c < M / 32; ++c) {
-                const int a0 = g * (M / 4) + 8 * c;
-                const uint4 u = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(fq) + tile_off<FSEG>(i, a0));
-                const float4 z0 = *reinterpret_cast<const float4*>(zl + a0);
-                const float4 z1 = *reinterpret_cast<const float4*>(zl + a0 + 4);
-                acc = fmaf(__uint_as_float(u.x << 16), z0.x, acc);
-                acc = fmaf(__uint_as_float(u.x & 0xFFFF0000u), z0.y, acc);
-                acc = fmaf(__uint_as_float(u.y << 16), z0.z, acc);
-                acc = fmaf(__uint_as_float(u.y & 0xFFFF0000u), z0.w, acc);
-                acc = fmaf(__uint_as_float(u.z << 16), z1.x, acc);
-                acc = fmaf(__uint_as_float(u.z & 0xFFFF0000u), z1.y, acc);
-                acc = fmaf(__uint_as_float(u.w << 16), z1.z, acc);
-                acc = fmaf(__uint_as_float(u.w & 0xFFFF0000u), z1.w, acc);
+                for (int ks = 0; ks < NKS; ++ks) {
+                    const bf16x8 a = row_at(fq, raf.off(16 * pw, 32 * ks));
+                    acc = mfma_bf16(a, as_bf16x8(zhl[ks * 4 + g]), acc);
+                    acc = mfma_bf16(a, as_bf16x8(zhl[(NKS + ks) * 4 + g]), acc);
+                }
+                if (l16 == 0) *reinterpret_cast<float4*>(qzl + 16 * pw + 4 * g) = make_float4(acc[0], acc[1], acc[2], acc[3]);
             }
-            acc += __shfl_xor(acc, 16);
-            acc += __shfl_xor(acc, 32);
-            if (g == 0) qz[i] = acc;
         }
         __syncthreads();  // B3(t)
         if (!prep) {
-            // inter phi(Q) P and intra tril(S) V: lane holds row 16 ib + 4g + e, column cw + l16
-            f32x4 O[4];
+            // O^T: lane (g, l16) holds output row 16 ib + l16, columns cw + 4g + e
+            f32x4 O[4], R[4];
 #pragma unroll
-            for (int ib = 0; ib < 4; ++ib) O[ib] = zero4;
+            for (int ib = 0; ib < 4; ++ib) O[ib] = R[ib] = zero4;
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
                 const bf16x8 pk = pack_acc_bf16(P[ks][0], P[ks][1]);
 #pragma unroll
-                for (int ib = 0; ib < 4; ++ib) O[ib] = mfma_bf16(row_op<FSEG>(fq, 16 * ib + l16, 32 * ks, g), pk, O[ib]);
+                for (int ib = 0; ib < 4; ++ib) O[ib] = mfma_bf16(pk, row_at(fq, raf.off(16 * ib, 32 * ks)), O[ib]);
                 __builtin_amdgcn_sched_barrier(0);
             }
             bf16x8 vb[2];
@@ -447,23 +684,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
             for (int ib = 0; ib < 4; ++ib)
 #pragma unroll
-                for (int kk = 0; kk <= ib / 2; ++kk) O[ib] = mfma_bf16(row_op<8>(stile, 16 * ib + l16, 32 * kk, g), vb[kk], O[ib]);
-            // the output rows (normalised) into this wave's own V columns
+                for (int kk = 0; kk <= ib / 2; ++kk) {
+                    const bf16x8 sb = row_at(stile, ra8.off(16 * ib, 32 * kk));
+                    O[ib] = mfma_bf16(vb[kk], sb, O[ib]);
+                    if constexpr (NORM) R[ib] = mfma_bf16(ones, sb, R[ib]);
+                }
+            // the output rows (normalised by phi(q_r) . z + the row's score sum)
+            // into this wave's own V columns
 #pragma unroll
             for (int ib = 0; ib < 4; ++ib) {
-                float rden[4] = {1.f, 1.f, 1.f, 1.f};
-                if constexpr (NORM) {
-                    const float4 q4 = *reinterpret_cast<const float4*>(qz + 16 * ib + 4 * g);
-                    const float4 r4 = *reinterpret_cast<const float4*>(rowsum + 16 * ib + 4 * g);
-                    rden[0] = __builtin_amdgcn_rcpf(q4.x + r4.x);
-                    rden[1] = __builtin_amdgcn_rcpf(q4.y + r4.y);
-                    rden[2] = __builtin_amdgcn_rcpf(q4.z + r4.z);
-                    rden[3] = __builtin_amdgcn_rcpf(q4.w + r4.w);
-                }
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    *reinterpret_cast<u16*>(reinterpret_cast<char*>(s.v) + tile_off<8>(16 * ib + 4 * g + e, cw + l16)) =
-                        f2bf(O[ib][e] * rden[e]);
+                const int r = 16 * ib + l16;
+                const float rd = NORM ? __builtin_amdgcn_rcpf(qzl[r] + R[ib][0]) : 1.f;
+                *reinterpret_cast<uint2*>(reinterpret_cast<char*>(s.v) + tile_off<8>(r, cw + 4 * g)) =
+                    make_uint2(pack2_bf16(O[ib][0] * rd, O[ib][1] * rd), pack2_bf16(O[ib][2] * rd, O[ib][3] * rd));
             }
             // P += phi(K)^T V
 #pragma unroll
@@ -472,20 +705,26 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
                     for (int hf = 0; hf < 2; ++hf)
-                        P[ks][hf] = mfma_bf16(col_op<FSEG>(fk, 32 * kk, 32 * ks + c8 + 4 * hf, lane_o), vb[kk], P[ks][hf]);
+                        P[ks][hf] = mfma_bf16(col_at(fk, caf, 32 * kk, 32 * ks, hf), vb[kk], P[ks][hf]);
                 __builtin_amdgcn_sched_barrier(0);
             }
-        } else {
-            if (NORM && 64 * pw < M) {
-                // z += the column sums of phi(K) (rows past the end are zero)
-                const int a = 64 * pw + lane;
-                float acc = 0.f;
-#pragma unroll 8
-                for (int r = 0; r < 64; ++r)
-                    acc += bf2f(*reinterpret_cast<const u16*>(reinterpret_cast<const char*>(fk) + tile_off<FSEG>(r, a)));
-                zl[a] += acc;
+            if constexpr (NORM) {
+                if (has_z) {
+                    // z += the column sums of phi(K) at this wave's features
+#pragma unroll
+                    for (int k2 = 0; k2 < KPW; ++k2)
+#pragma unroll
+                        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                            for (int hf = 0; hf < 2; ++hf)
+                                Zs[k2][hf] = mfma_bf16(col_op<FSEG>(fk, 32 * kk, 32 * (KPW * pw + k2) + c8 + 4 * hf, lane_o),
+                                                       ones, Zs[k2][hf]);
+                    put_z(Zs);
+                }
             }
-            if (t + 1 < t_end) wait_vm<0>();  // tile t + 1 (and chunk t - 1's stores) are done
+        } else if (t + 1 < t_end) {
+            wait_vm<0>();  // tile t + 1 (and chunk t - 1's stores) are done
+            row_consts(t + 1, sn, crl[si ^ 1]);
         }
         si ^= 1;
     }
