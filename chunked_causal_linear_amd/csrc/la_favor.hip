@@ -25,12 +25,14 @@
 //  * favor_fwd_kernel: phase 3, the chunks (of 64 rows) of a group from its
 //    prefix state: O = phi(Q) P + tril(phi(Q) phi(K)^T) V, normalised by
 //    phi(Q) z + the row sums of tril(phi(Q) phi(K)^T), then P += phi(K)^T V,
-//    z += the column sums of phi(K).  Eight waves, two per SIMD: state waves
-//    0-3 own 16 value columns of the m x 64 state each (fp32 accumulators; a
-//    packed pair of them is an operand in feature order) and map phi(q) for
-//    a quarter of the features; prep waves 4-7 issue the direct-to-LDS copies
-//    of the raw tiles and the output stores, map phi(k) for a quarter of the
-//    features and keep that quarter of z in registers.
+//    z += the column sums of phi(K).  Eight waves, two per SIMD.  Waves 0-3
+//    map phi(q), waves 4-7 (the prep waves, which also issue the
+//    direct-to-LDS copies of the raw tiles) phi(k), each for a quarter of the
+//    features.  Wave w keeps the state of value columns 16 (w mod 4) .. + 15
+//    over one half of the features (fp32 accumulators; a packed pair of them
+//    is an operand in feature order); waves 0-3 add the other half's partial
+//    outputs and put the output rows into the stage's V tile, which the prep
+//    waves store as whole rows.
 #include "la_fwd_pipe.hpp"
 
 namespace la {
@@ -160,10 +162,51 @@ struct ColAddr {
     }
 };
 
+// The same two with the feature steps ks = ks0 + c (c = 0..3) of a run that
+// starts at a wave-uniform ks0, a multiple of 4 when NSEG = 32 (bit 4 of the
+// segment index then depends on ks0 and the row's 16-block parity only).
+template <int NSEG>
+struct RowAddrK {
+    int b[4];
+    int h[2];
+    __device__ __forceinline__ RowAddrK(int lane, int ks0) {
+        const int l16 = lane & 15, g = lane >> 4, B = g ^ l16;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) b[c] = l16 * NSEG * 16 + (((4 * ((ks0 + c) & 3)) ^ B) & (NSEG - 1)) * 16;
+#pragma unroll
+        for (int par = 0; par < 2; ++par) h[par] = NSEG == 32 ? 256 * (((ks0 >> 2) & 1) ^ par) : 0;
+    }
+    // byte offset of pipe::tile_off<NSEG>(R0 + l16, 32 (ks0 + c) + 8g), R0 a multiple of 16
+    __device__ __forceinline__ int off(int R0, int c) const { return b[c] + R0 * NSEG * 16 + h[(R0 >> 4) & 1]; }
+};
+template <int NSEG>
+struct ColAddrK {
+    int b[4];
+    int h[2];
+    __device__ __forceinline__ ColAddrK(int lane, int ks0) {
+        const int g = lane >> 4, rr = (lane & 15) >> 2, cl = lane & 3, rl = 4 * g + rr, B = cl ^ rl;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) b[c] = rl * NSEG * 16 + (((4 * ((ks0 + c) & 3)) ^ B) & (NSEG - 1)) * 16;
+#pragma unroll
+        for (int par = 0; par < 2; ++par) h[par] = NSEG == 32 ? 256 * (((ks0 >> 2) & 1) ^ par) : 0;
+    }
+    // byte offset of pipe::tile_off<NSEG>(K0 + H + 4g + rr, 32 (ks0 + c) + 8 cl + 4hf), K0 a multiple of 32, H 0 or 16
+    __device__ __forceinline__ int off(int K0, int H, int c, int hf) const {
+        return b[c] + (K0 + H) * NSEG * 16 + h[H >> 4] + 8 * hf;
+    }
+};
+
 __device__ __forceinline__ bf16x8 row_at(const u16* tile, int off) {
     return as_bf16x8(*reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(tile) + off));
 }
 // the column operand (keys K0 .. K0 + 31 in operand order) from its two transposed reads
+template <int NSEG>
+__device__ __forceinline__ bf16x8 col_at_k(const u16* tile, const ColAddrK<NSEG>& ca, int K0, int c, int hf) {
+    const char* t = reinterpret_cast<const char*>(tile);
+    const uint2 lo = pipe::tr_read(t + ca.off(K0, 0, c, hf));
+    const uint2 hi = pipe::tr_read(t + ca.off(K0, 16, c, hf));
+    return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
 template <int NSEG>
 __device__ __forceinline__ bf16x8 col_at(const u16* tile, const ColAddr<NSEG>& ca, int K0, int CB, int hf) {
     const char* t = reinterpret_cast<const char*>(tile);
@@ -272,8 +315,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         if (seg == 0) out[r] = t * 64 + r < L ? fmaf(cA, q, cB) : -__builtin_inff();
     };
 
-    for (int s0 = 0; s0 < NSTAGE - 1; ++s0)
-        if (t_begin + s0 < t_end) issue(t_begin + s0, st[s0]);
+    // W first: its loads are then waited for before the copies go out
     bf16x8 wf[FPW][2];
 #pragma unroll
     for (int f = 0; f < FPW; ++f) {
@@ -281,6 +323,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         settle(wf[f][0]);
         settle(wf[f][1]);
     }
+    for (int s0 = 0; s0 < NSTAGE - 1; ++s0)
+        if (t_begin + s0 < t_end) issue(t_begin + s0, st[s0]);
     land(t_begin);
     if (t_begin < t_end) row_consts(t_begin, st[0], crl[0]);
 
@@ -429,32 +473,42 @@ __device__ __forceinline__ void map_tile(const bf16x8 (&wf)[M / 64][2], const u1
 // ---------------------------------------------------------------------------
 // phase 3: one workgroup per (head, group of chunks of 64, 64 value columns)
 // ---------------------------------------------------------------------------
-// Three barriers per chunk t:
-//   B1(t): tile t and its row constants are in; the state waves are done with
-//          chunk t - 1 (its output rows are in its stage's V columns; phi(q),
-//          phi(k) and the score tile are free; z after chunk t - 1 is in zhl);
+// Four barriers per chunk t:
+//   B1(t): tile t and its row constants are in; every wave is done with chunk
+//          t - 1 (its output rows are in its stage's V tile; phi(q), phi(k)
+//          and the score tile are free; z after chunk t - 1 is in zhl);
 //   B2(t): phi(q) and phi(k) of tile t are complete (all eight waves map);
 //   B3(t): the score tile (tril(phi(Q) phi(K)^T), columns in operand key
-//          order) and, with the normaliser, phi(q_i) . z for every row.
+//          order) and, with the normaliser, phi(q_i) . z for every row;
+//   B4(t): the upper feature half's partial outputs are in LDS (in the raw q
+//          and k tiles of the chunk's stage, free since B2).
 // The score blocks are computed transposed (keys as rows): a lane then holds
-// four consecutive keys of one query row, one 8-byte store.  The state waves
+// four consecutive keys of one query row, one 8-byte store.  The products
 // likewise form O^T (value columns as rows: four consecutive columns of one
 // output row per lane), and the row sums of the score tile come from the
 // matrix cores with a ones operand, in the same layout.  Right after B1(t) the
-// prep waves store chunk t - 1's outputs and issue tile t + 1 into the stage
-// they leave; after B3 they wait for it and form its row constants.
+// prep waves store chunk t - 1's output rows and issue tile t + NSTAGE - 1
+// into the stage chunk t - 1 used; after B4 they wait for tile t + 1 and form
+// its row constants.
 template <int M, bool NORM>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void favor_fwd_kernel(FavorParams p) {
     using namespace pipe;
     constexpr int FSEG = M / 8, NKS = M / 32, FPW = M / 64;
-    // z is kept by the state waves, KPW 32-feature steps each (waves pw < NKS / KPW)
-    constexpr int KPW = NKS >= 4 ? NKS / 4 : 1;
+    // Wave w keeps the state of value columns 16 (w mod 4) .. + 15 over the
+    // half fh = w / 4 of the 32-feature steps (NKH steps from fh NKH; at m = 64
+    // there are two steps, one per half).
+    constexpr int NKH = NKS / 2;
+    // as many raw stages as the LDS holds beside the fixed tiles, at most four
+    constexpr int FIXED = 2 * 64 * M * 2 + 64 * 64 * 2 + 2 * 2 * 64 * 4 + 2 * NKS * 4 * 16 + 64 * 4;
+    constexpr int NFIT = (int)((160 * 1024 - FIXED) / sizeof(RawStage));
+    constexpr int NSTAGE = NFIT < 4 ? NFIT : 4;
+    static_assert(NSTAGE >= 2, "stages");
 
-    __shared__ RawStage st[2];
+    __shared__ RawStage st[NSTAGE];
     __shared__ __attribute__((aligned(16))) u16 fq[64 * M];
     __shared__ __attribute__((aligned(16))) u16 fk[64 * M];
     __shared__ __attribute__((aligned(16))) u16 stile[64 * 64];
-    __shared__ __attribute__((aligned(16))) float crl[2][2][64];  // row constants [stage][q, k][row]
+    __shared__ __attribute__((aligned(16))) float crl[2][2][64];  // row constants [chunk parity][q, k][row]
     // z before the chunk as operand pieces: [hi, lo][32-feature step ks][lane group g]
     __shared__ __attribute__((aligned(16))) uint4 zhl[NORM ? 2 * NKS * 4 : 1];
     __shared__ __attribute__((aligned(16))) float qzl[64];  // phi(q_i) . z
@@ -469,6 +523,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int grp = (wi / p.n_dvt) % p.n_groups;
     const int64_t bh = wi / ((int64_t)p.n_dvt * p.n_groups);
     const int col0 = jt * 64, cw = 16 * pw;
+    const int fh = wave >> 2, ks0 = fh * NKH;  // this wave's half of the feature steps
     const int fb0 = pw * FPW;  // first feature block this wave maps (of q or of k)
     const int64_t L = p.L;
     const int dv = p.dv;
@@ -486,7 +541,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const float cA = -0.5f * kLog2e * p.in_scale * p.in_scale;
     const float cB = -0.5f * __builtin_amdgcn_logf((float)M);
 
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     auto issue = [&](int64_t t, RawStage& s) __attribute__((always_inline)) {
         const int last = (int)(L - 1 - t * 64);
 #pragma unroll
@@ -512,6 +566,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             if (qd == 0) out[x][r] = (x == 1 && t * 64 + r >= L) ? -__builtin_inff() : fmaf(cA, q, cB);
         }
     };
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     // output rows from the V tile of a stage: piece (pw * 2 + i) * 64 + lane
     auto read_out = [&](const RawStage& s, u32x4 (&ob)[2]) __attribute__((always_inline)) {
 #pragma unroll
@@ -530,55 +585,54 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             if (r < valid) __builtin_nontemporal_store(ob[i], reinterpret_cast<u32x4*>(o + (int64_t)r * dv + seg * 8));
         }
     };
-    const bool has_z = pw < NKS / KPW;  // this state wave keeps steps KPW pw .. KPW pw + KPW - 1 of z
-    // z after this state wave's update, as bf16 hi / lo operand pieces
-    auto put_z = [&](const f32x4 (&Zs)[KPW][2]) __attribute__((always_inline)) {
-        if (l16 == 0)
-#pragma unroll
-            for (int k2 = 0; k2 < KPW; ++k2) {
-                const float a[4] = {Zs[k2][0][0], Zs[k2][0][1], Zs[k2][0][2], Zs[k2][0][3]};
-                const float b[4] = {Zs[k2][1][0], Zs[k2][1][1], Zs[k2][1][2], Zs[k2][1][3]};
-                const uint4 hi = pack8(a, b);
-                zhl[(KPW * pw + k2) * 4 + g] = hi;
-                zhl[(NKS + KPW * pw + k2) * 4 + g] = pack8_lo(a, b, hi);
-            }
+    // z: wave (fh, pw) with pw < NKH keeps feature step kz = fh NKH + pw
+    const bool has_z = pw < NKH;
+    const int kz = ks0 + pw;
+    // z after the update, as bf16 hi / lo operand pieces
+    auto put_z = [&](const f32x4 (&Zs)[2]) __attribute__((always_inline)) {
+        if (l16 == 0) {
+            const float a[4] = {Zs[0][0], Zs[0][1], Zs[0][2], Zs[0][3]};
+            const float b[4] = {Zs[1][0], Zs[1][1], Zs[1][2], Zs[1][3]};
+            const uint4 hi = pack8(a, b);
+            zhl[kz * 4 + g] = hi;
+            zhl[(NKS + kz) * 4 + g] = pack8_lo(a, b, hi);
+        }
     };
 
-    // prologue: the first tile and its row constants, W, the group's prefix state and normaliser
-    if (prep) issue(t_begin, st[0]);
+    // prologue: W, the group's prefix state and normaliser, then the first
+    // tiles and the row constants of the first
+    // land(t): this prep wave's copies of tile t are in (six copy instructions per tile)
+    auto land = [&](int64_t t) __attribute__((always_inline)) {
+        const int64_t newest = t + NSTAGE - 2 < t_end - 1 ? t + NSTAGE - 2 : t_end - 1;
+        wait_groups<6, NSTAGE - 2>((int)(newest - t));
+    };
     bf16x8 wf[FPW][2];
 #pragma unroll
     for (int f = 0; f < FPW; ++f) load_w_frag(p.W, fb0 + f, lane, wf[f]);
-    f32x4 P[NKS][2];
+    // P[c][hf]: state rows 32 (ks0 + c) + 8g + 4hf + i, column cw + l16
+    f32x4 P[NKH][2];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) P[ks][0] = P[ks][1] = zero4;
-    // state waves: z of features 32 (KPW pw + k2) + 8g + 4hf + i (every l16)
-    f32x4 Zs[KPW][2];
-#pragma unroll
-    for (int k2 = 0; k2 < KPW; ++k2) Zs[k2][0] = Zs[k2][1] = zero4;
+    for (int c = 0; c < NKH; ++c) P[c][0] = P[c][1] = zero4;
+    // z of features 32 kz + 8g + 4hf + i (every l16)
+    f32x4 Zs[2] = {zero4, zero4};
     const bool has_prefix = grp > 0;
-    if (!prep) {
-        if (p.P0 != nullptr && has_prefix) {
-            const float* P0 = p.P0 + (slot * M) * (int64_t)dv + col0 + cw + l16;
+    if (p.P0 != nullptr && has_prefix) {
+        const float* P0 = p.P0 + (slot * M) * (int64_t)dv + col0 + cw + l16;
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks)
+        for (int c = 0; c < NKH; ++c)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) P[c][hf][e] = P0[(int64_t)(32 * (ks0 + c) + 8 * g + 4 * hf + e) * dv];
+    }
+    if constexpr (NORM) {
+        if (has_z) {
+            if (p.z0 != nullptr && has_prefix)
 #pragma unroll
                 for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) P[ks][hf][e] = P0[(int64_t)(32 * ks + 8 * g + 4 * hf + e) * dv];
-        }
-        if constexpr (NORM) {
-            if (has_z) {
-                if (p.z0 != nullptr && has_prefix)
-#pragma unroll
-                    for (int k2 = 0; k2 < KPW; ++k2)
-#pragma unroll
-                        for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                Zs[k2][hf][e] = p.z0[slot * M + 32 * (KPW * pw + k2) + 8 * g + 4 * hf + e];
-                put_z(Zs);
-            }
+                    for (int e = 0; e < 4; ++e) Zs[hf][e] = p.z0[slot * M + 32 * kz + 8 * g + 4 * hf + e];
+            put_z(Zs);
         }
     }
 #pragma unroll
@@ -587,27 +641,30 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         settle(wf[f][1]);
     }
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-        settle(P[ks][0]);
-        settle(P[ks][1]);
+    for (int c = 0; c < NKH; ++c) {
+        settle(P[c][0]);
+        settle(P[c][1]);
     }
-#pragma unroll
-    for (int k2 = 0; k2 < KPW; ++k2) {
-        settle(Zs[k2][0]);
-        settle(Zs[k2][1]);
-    }
+    settle(Zs[0]);
+    settle(Zs[1]);
+    // the copies go out after the loads above have been waited for
     if (prep) {
-        wait_vm<0>();
+        for (int s0 = 0; s0 < NSTAGE - 1; ++s0)
+            if (t_begin + s0 < t_end) issue(t_begin + s0, st[s0]);
+        land(t_begin);
         row_consts(t_begin, st[0], crl[0]);
     }
     const RowAddr<FSEG> raf(lane);
     const RowAddr<8> ra8(lane);
-    const ColAddr<FSEG> caf(lane);
+    const RowAddrK<FSEG> rak(lane, ks0);
+    const ColAddrK<FSEG> cak(lane, ks0);
 
     int si = 0;
     for (int64_t t = t_begin; t < t_end; ++t) {
         RawStage& s = st[si];
-        RawStage& sn = st[si ^ 1];
+        const int sp = si == 0 ? NSTAGE - 1 : si - 1;  // stage of chunk t - 1
+        const int sn = si == NSTAGE - 1 ? 0 : si + 1;  // stage of tile t + 1
+        const int cp = (int)((t - t_begin) & 1);       // chunk parity (row constants)
         // the lane's values formed again each chunk (opaque to the compiler), so
         // that the LDS addresses derived from them are not all held in registers
         // across the chunk loop
@@ -618,15 +675,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         if (prep) {
             // chunk t - 1's outputs leave the other stage (stored first, so that
             // the stores drain during the chunk), which then takes tile t + 1
+            // chunk t - 1's outputs leave its stage (stored first, so that the
+            // stores drain during the chunk), which then takes tile t + NSTAGE - 1
             if (t > t_begin) {
                 u32x4 ob[2];
-                read_out(sn, ob);
+                read_out(st[sp], ob);
                 store_out(t - 1, ob);
             }
-            if (t + 1 < t_end) issue(t + 1, sn);
+            if (t + NSTAGE - 1 < t_end) issue(t + NSTAGE - 1, st[sp]);
         }
         // phi(q) (waves 0-3) and phi(k) (waves 4-7) of feature blocks fb0 .. fb0 + FPW - 1
-        map_tile<M>(wf, prep ? s.k : s.q, ra8, prep ? fk : fq, fb0, c1, crl[si][prep ? 1 : 0], lane_o);
+        map_tile<M>(wf, prep ? s.k : s.q, ra8, prep ? fk : fq, fb0, c1, crl[cp][prep ? 1 : 0], lane_o);
         __syncthreads();  // B2(t)
         // score blocks (ib, jb), jb <= ib (b = 0..9), as S^T (lane (g, l16): keys
         // 16 jb + 4g + e of query row 16 ib + l16), and the two blocks above the
@@ -641,10 +700,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 const int i = 16 * ib + l16;
                 uint2 w2 = make_uint2(0u, 0u);
                 if (b < 10) {
-                    f32x4 acc = zero4;
+                    f32x4 acc = zero4, acc2 = zero4;  // two chains (even and odd steps)
 #pragma unroll
-                    for (int ks = 0; ks < NKS; ++ks)
+                    for (int ks = 0; ks < NKS; ks += 2) {
                         acc = mfma_bf16(row_at(fk, raf.off(16 * jb, 32 * ks)), row_at(fq, raf.off(16 * ib, 32 * ks)), acc);
+                        acc2 = mfma_bf16(row_at(fk, raf.off(16 * jb, 32 * ks + 32)), row_at(fq, raf.off(16 * ib, 32 * ks + 32)),
+                                         acc2);
+                    }
+                    acc += acc2;
                     const int j0 = 16 * jb + 4 * g;
                     w2 = make_uint2(pack2_bf16(j0 <= i ? acc[0] : 0.f, j0 + 1 <= i ? acc[1] : 0.f),
                                     pack2_bf16(j0 + 2 <= i ? acc[2] : 0.f, j0 + 3 <= i ? acc[3] : 0.f));
@@ -655,83 +718,100 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         if constexpr (NORM) {
             if (prep) {
                 // phi(q_r) . z for rows 16 ib + 4g + e (ib = pw): z as bf16 hi + lo
-                f32x4 acc = zero4;
+                f32x4 acc = zero4, acc2 = zero4;  // hi and lo chains
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks) {
                     const bf16x8 a = row_at(fq, raf.off(16 * pw, 32 * ks));
                     acc = mfma_bf16(a, as_bf16x8(zhl[ks * 4 + g]), acc);
-                    acc = mfma_bf16(a, as_bf16x8(zhl[(NKS + ks) * 4 + g]), acc);
+                    acc2 = mfma_bf16(a, as_bf16x8(zhl[(NKS + ks) * 4 + g]), acc2);
                 }
+                acc += acc2;
                 if (l16 == 0) *reinterpret_cast<float4*>(qzl + 16 * pw + 4 * g) = make_float4(acc[0], acc[1], acc[2], acc[3]);
             }
         }
         __syncthreads();  // B3(t)
-        if (!prep) {
-            // O^T: lane (g, l16) holds output row 16 ib + l16, columns cw + 4g + e
-            f32x4 O[4], R[4];
+        {
+            // this wave's half of the feature steps: the inter product O^T (lane
+            // (g, l16): output row 16 ib + l16, columns cw + 4g + e), partial
+            f32x4 O[4];
 #pragma unroll
-            for (int ib = 0; ib < 4; ++ib) O[ib] = R[ib] = zero4;
+            for (int ib = 0; ib < 4; ++ib) O[ib] = zero4;
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                const bf16x8 pk = pack_acc_bf16(P[ks][0], P[ks][1]);
+            for (int c = 0; c < NKH; ++c) {
+                const bf16x8 pk = pack_acc_bf16(P[c][0], P[c][1]);
 #pragma unroll
-                for (int ib = 0; ib < 4; ++ib) O[ib] = mfma_bf16(pk, row_at(fq, raf.off(16 * ib, 32 * ks)), O[ib]);
+                for (int ib = 0; ib < 4; ++ib) O[ib] = mfma_bf16(pk, row_at(fq, rak.off(16 * ib, c)), O[ib]);
                 __builtin_amdgcn_sched_barrier(0);
             }
+            // the upper half's partial goes through the raw q and k tiles of this
+            // stage (free since B2)
+            f32x4* obuf = reinterpret_cast<f32x4*>(s.q);
+            if (fh == 1)
+#pragma unroll
+                for (int ib = 0; ib < 4; ++ib) obuf[(pw * 4 + ib) * WAVE + lane_o] = O[ib];
             bf16x8 vb[2];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) vb[kk] = col_op<8>(s.v, 32 * kk, cw + c4, lane_o);
+            // P += phi(K)^T V over this wave's feature steps
 #pragma unroll
-            for (int ib = 0; ib < 4; ++ib)
-#pragma unroll
-                for (int kk = 0; kk <= ib / 2; ++kk) {
-                    const bf16x8 sb = row_at(stile, ra8.off(16 * ib, 32 * kk));
-                    O[ib] = mfma_bf16(vb[kk], sb, O[ib]);
-                    if constexpr (NORM) R[ib] = mfma_bf16(ones, sb, R[ib]);
-                }
-            // the output rows (normalised by phi(q_r) . z + the row's score sum)
-            // into this wave's own V columns
-#pragma unroll
-            for (int ib = 0; ib < 4; ++ib) {
-                const int r = 16 * ib + l16;
-                const float rd = NORM ? __builtin_amdgcn_rcpf(qzl[r] + R[ib][0]) : 1.f;
-                *reinterpret_cast<uint2*>(reinterpret_cast<char*>(s.v) + tile_off<8>(r, cw + 4 * g)) =
-                    make_uint2(pack2_bf16(O[ib][0] * rd, O[ib][1] * rd), pack2_bf16(O[ib][2] * rd, O[ib][3] * rd));
-            }
-            // P += phi(K)^T V
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
+            for (int c = 0; c < NKH; ++c) {
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
                     for (int hf = 0; hf < 2; ++hf)
-                        P[ks][hf] = mfma_bf16(col_at(fk, caf, 32 * kk, 32 * ks, hf), vb[kk], P[ks][hf]);
+                        P[c][hf] = mfma_bf16(col_at_k(fk, cak, 32 * kk, c, hf), vb[kk], P[c][hf]);
                 __builtin_amdgcn_sched_barrier(0);
             }
             if constexpr (NORM) {
                 if (has_z) {
-                    // z += the column sums of phi(K) at this wave's features
+                    // z += the column sums of phi(K) at feature step kz
 #pragma unroll
-                    for (int k2 = 0; k2 < KPW; ++k2)
+                    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-                        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-                            for (int hf = 0; hf < 2; ++hf)
-                                Zs[k2][hf] = mfma_bf16(col_op<FSEG>(fk, 32 * kk, 32 * (KPW * pw + k2) + c8 + 4 * hf, lane_o),
-                                                       ones, Zs[k2][hf]);
+                        for (int hf = 0; hf < 2; ++hf)
+                            Zs[hf] = mfma_bf16(col_op<FSEG>(fk, 32 * kk, 32 * kz + c8 + 4 * hf, lane_o), ones, Zs[hf]);
                     put_z(Zs);
                 }
             }
-        } else if (t + 1 < t_end) {
-            wait_vm<0>();  // tile t + 1 (and chunk t - 1's stores) are done
-            row_consts(t + 1, sn, crl[si ^ 1]);
+            __syncthreads();  // B4(t): the upper halves' partial outputs are in
+            if (fh == 0) {
+                // the lower half adds the upper half's partial and the intra product
+                // tril(S) V, and with the normaliser divides by phi(q_r) . z + the
+                // row's score sum (from the matrix cores with a ones operand)
+                f32x4 R[4];
+#pragma unroll
+                for (int ib = 0; ib < 4; ++ib) {
+                    O[ib] += obuf[(pw * 4 + ib) * WAVE + lane_o];
+                    R[ib] = zero4;
+                }
+#pragma unroll
+                for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+                    for (int kk = 0; kk <= ib / 2; ++kk) {
+                        const bf16x8 sb = row_at(stile, ra8.off(16 * ib, 32 * kk));
+                        O[ib] = mfma_bf16(vb[kk], sb, O[ib]);
+                        if constexpr (NORM) R[ib] = mfma_bf16(ones, sb, R[ib]);
+                    }
+                // four consecutive columns of row 16 ib + l16 per lane into this
+                // wave's V columns of the stage (the prep waves store whole rows)
+#pragma unroll
+                for (int ib = 0; ib < 4; ++ib) {
+                    const int r = 16 * ib + l16;
+                    const float rd = NORM ? __builtin_amdgcn_rcpf(qzl[r] + R[ib][0]) : 1.f;
+                    *reinterpret_cast<uint2*>(reinterpret_cast<char*>(s.v) + tile_off<8>(r, cw + 4 * g)) =
+                        make_uint2(pack2_bf16(O[ib][0] * rd, O[ib][1] * rd), pack2_bf16(O[ib][2] * rd, O[ib][3] * rd));
+                }
+            } else if (t + 1 < t_end) {
+                land(t + 1);
+                row_consts(t + 1, st[sn], crl[cp ^ 1]);
+            }
         }
-        si ^= 1;
+        si = sn;
     }
     __syncthreads();  // B1(t_end): the last chunk's outputs are in its stage
     if (prep) {
         u32x4 ob[2];
-        read_out(st[si ^ 1], ob);
+        read_out(st[si == 0 ? NSTAGE - 1 : si - 1], ob);
         store_out(t_end - 1, ob);
     }
 }
