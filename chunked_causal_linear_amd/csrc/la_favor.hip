@@ -440,82 +440,55 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
 }
 
-// Phase-3 mapping of one tile (q or k): the wave's FPW feature blocks from
-// fb0 for all four row blocks (features as rows, rows as columns: lane (g, l16)
-// gets features 16 fb + 4g + i of row 16 rb + l16), with the row constants cr
-// (-inf for key rows past the end, which then map to 0), stored into the phi tile.
-template <int M>
-__device__ __forceinline__ void map_tile(const bf16x8 (&wf)[M / 64][2], const u16* x, const RowAddr<8>& ra8, u16* phi,
-                                         int fb0, float c1, const float* cr, int lane) {
-    using namespace pipe;
-    constexpr int FSEG = M / 8, FPW = M / 64;
-    const int l16 = lane % 16, g = lane / 16;
-    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-        const int r = 16 * rb + l16;
-        const bf16x8 x0 = row_at(x, ra8.off(16 * rb, 0)), x1 = row_at(x, ra8.off(16 * rb, 32));
-        const float c = cr[r];
-#pragma unroll
-        for (int f = 0; f < FPW; ++f) {
-            f32x4 acc = mfma_bf16(wf[f][0], x0, zero4);
-            acc = mfma_bf16(wf[f][1], x1, acc);
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(c1, acc[0], c));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(c1, acc[1], c));
-            const float p2 = __builtin_amdgcn_exp2f(fmaf(c1, acc[2], c));
-            const float p3 = __builtin_amdgcn_exp2f(fmaf(c1, acc[3], c));
-            *reinterpret_cast<uint2*>(reinterpret_cast<char*>(phi) + tile_off<FSEG>(r, 16 * (fb0 + f) + 4 * g)) =
-                make_uint2(pack2_bf16(p0, p1), pack2_bf16(p2, p3));
-        }
-    }
-}
-
 // ---------------------------------------------------------------------------
 // phase 3: one workgroup per (head, group of chunks of 64, 64 value columns)
 // ---------------------------------------------------------------------------
-// Four barriers per chunk t:
-//   B1(t): tile t and its row constants are in; every wave is done with chunk
-//          t - 1 (its output rows are in its stage's V tile; phi(q), phi(k)
-//          and the score tile are free; z after chunk t - 1 is in zhl);
-//   B2(t): phi(q) and phi(k) of tile t are complete (all eight waves map);
-//   B3(t): the score tile (tril(phi(Q) phi(K)^T), columns in operand key
-//          order) and, with the normaliser, phi(q_i) . z for every row;
-//   B4(t): the upper feature half's partial outputs are in LDS (in the raw q
-//          and k tiles of the chunk's stage, free since B2).
-// The score blocks are computed transposed (keys as rows): a lane then holds
-// four consecutive keys of one query row, one 8-byte store.  The products
-// likewise form O^T (value columns as rows: four consecutive columns of one
-// output row per lane), and the row sums of the score tile come from the
-// matrix cores with a ones operand, in the same layout.  Right after B1(t) the
-// prep waves store chunk t - 1's output rows and issue tile t + NSTAGE - 1
-// into the stage chunk t - 1 used; after B4 they wait for tile t + 1 and form
-// its row constants.
+// Two groups of four waves, one of each on every SIMD, a chunk apart:
+//  * product waves 0-3 run chunk t: the score tile, phi(q_i) . z, the inter
+//    and intra products, the outputs and the state update, with the state of
+//    value columns 16 w .. 16 w + 15 over all features in fp32 accumulators (a
+//    packed pair is an operand in feature order); they also move the value
+//    tiles (direct-to-LDS copies) and store the output rows;
+//  * mapper waves 4-7 map chunk t + 1 meanwhile: each keeps W for a quarter of
+//    the features in registers and reads the raw q and k rows it needs straight
+//    into registers (one chunk ahead), so the raw q and k never occupy LDS.
+// phi(q) and phi(k) are double-buffered by chunk parity.  Two barriers per
+// chunk t:
+//   B(t):  phi of chunk t is complete (mapped during chunk t - 1), its value
+//          tile has landed, and chunk t - 1's products are done (the other
+//          phi buffer, the score tile and chunk t - 1's stage are free);
+//   BS(t): the score tile (tril(phi(Q) phi(K)^T), columns in operand key
+//          order) and, with the normaliser, phi(q_i) . z are complete.
+// The mapper waves map phi(q) of chunk t + 1 before BS(t) and phi(k) after.
+// Scores and outputs are computed transposed (keys, resp. value columns, as
+// rows), so a lane holds four consecutive keys or columns of one row (one
+// 8-byte store); the row sums of the score tile come from the matrix cores with
+// a ones operand, in the outputs' layout.  Row norms come from the matrix
+// cores too: the diagonal of x x^T for each 16-row block.
 template <int M, bool NORM>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void favor_fwd_kernel(FavorParams p) {
     using namespace pipe;
     constexpr int FSEG = M / 8, NKS = M / 32, FPW = M / 64;
-    // Wave w keeps the state of value columns 16 (w mod 4) .. + 15 over the
-    // half fh = w / 4 of the 32-feature steps (NKH steps from fh NKH; at m = 64
-    // there are two steps, one per half).
-    constexpr int NKH = NKS / 2;
-    // as many raw stages as the LDS holds beside the fixed tiles, at most four
-    constexpr int FIXED = 2 * 64 * M * 2 + 64 * 64 * 2 + 2 * 2 * 64 * 4 + 2 * NKS * 4 * 16 + 64 * 4;
-    constexpr int NFIT = (int)((160 * 1024 - FIXED) / sizeof(RawStage));
-    constexpr int NSTAGE = NFIT < 4 ? NFIT : 4;
-    static_assert(NSTAGE >= 2, "stages");
+    constexpr int PHI_E = 64 * M;  // elements of one phi tile
+    // z is kept by the product waves, KPW feature steps each (waves w < NKS / KPW)
+    constexpr int KPW = NKS >= 4 ? NKS / 4 : 1;
+    // as many value stages as the LDS holds beside the rest, at most four
+    constexpr int FIXED = 2 * 2 * PHI_E * 2 + 64 * 64 * 2 + 64 * 4 + 2 * NKS * 4 * 16;
+    constexpr int NVFIT = (160 * 1024 - FIXED) / (64 * 64 * 2);
+    constexpr int NV = NVFIT < 4 ? NVFIT : 4;
+    static_assert(NV >= 2, "value stages");
 
-    __shared__ RawStage st[NSTAGE];
-    __shared__ __attribute__((aligned(16))) u16 fq[64 * M];
-    __shared__ __attribute__((aligned(16))) u16 fk[64 * M];
+    __shared__ __attribute__((aligned(16))) u16 fq[2][PHI_E];
+    __shared__ __attribute__((aligned(16))) u16 fk[2][PHI_E];
+    __shared__ __attribute__((aligned(16))) u16 vst[NV][64 * 64];
     __shared__ __attribute__((aligned(16))) u16 stile[64 * 64];
-    __shared__ __attribute__((aligned(16))) float crl[2][2][64];  // row constants [chunk parity][q, k][row]
+    __shared__ __attribute__((aligned(16))) float qzl[64];  // phi(q_i) . z
     // z before the chunk as operand pieces: [hi, lo][32-feature step ks][lane group g]
     __shared__ __attribute__((aligned(16))) uint4 zhl[NORM ? 2 * NKS * 4 : 1];
-    __shared__ __attribute__((aligned(16))) float qzl[64];  // phi(q_i) . z
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);
-    const bool prep = wave >= 4;
+    const bool mapper = wave >= 4;
     const int pw = wave & 3;
     const int lane = tid % WAVE, l16 = lane % 16, g = lane / 16;
     const int wi = work_index(p.xcd_remap);
@@ -523,8 +496,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int grp = (wi / p.n_dvt) % p.n_groups;
     const int64_t bh = wi / ((int64_t)p.n_dvt * p.n_groups);
     const int col0 = jt * 64, cw = 16 * pw;
-    const int fh = wave >> 2, ks0 = fh * NKH;  // this wave's half of the feature steps
-    const int fb0 = pw * FPW;  // first feature block this wave maps (of q or of k)
+    const int fb0 = pw * FPW;  // mapper: first feature block
     const int64_t L = p.L;
     const int dv = p.dv;
     const int64_t n_tiles = (L + 63) / 64;
@@ -540,39 +512,100 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const float c1 = kLog2e * p.in_scale;
     const float cA = -0.5f * kLog2e * p.in_scale * p.in_scale;
     const float cB = -0.5f * __builtin_amdgcn_logf((float)M);
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-    auto issue = [&](int64_t t, RawStage& s) __attribute__((always_inline)) {
+    if (mapper) {
+        // ================= mapper waves =================
+        bf16x8 wf[FPW][2];
+#pragma unroll
+        for (int f = 0; f < FPW; ++f) load_w_frag(p.W, fb0 + f, lane, wf[f]);
+        // x fragments of tile t: rows 16 rb + l16 (clamped to the last row),
+        // inputs 32 h + 8g .. + 7
+        auto load_x = [&](const u16* base, int64_t t, bf16x8 (&x)[4][2]) __attribute__((always_inline)) {
+            const int last = (int)(L - 1 - t * 64);
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                const int r = 16 * rb + l16;
+                const u16* row = base + (t * 64 + (r < last ? r : last)) * 64 + 8 * g;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) x[rb][h] = as_bf16x8(*reinterpret_cast<const uint4*>(row + 32 * h));
+            }
+        };
+        // phi of a tile into a phi tile: row norms from the diagonal of x x^T
+        // (lane (g, l16) holds rows 16 rb + 4g + i against row 16 rb + l16; the
+        // diagonal of row r sits in lane (r / 4, r), element r mod 4), then the
+        // features fb0 .. fb0 + FPW - 1 of every row (lane (g, l16): features
+        // 16 fb + 4g + i of row 16 rb + l16); key rows at or past `valid` map to 0
+        auto map = [&](const bf16x8 (&x)[4][2], u16* phi, int valid) __attribute__((always_inline)) {
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                f32x4 d = mfma_bf16(x[rb][0], x[rb][0], zero4);
+                d = mfma_bf16(x[rb][1], x[rb][1], d);
+                const int e = l16 & 3;
+                const float dd = e == 0 ? d[0] : (e == 1 ? d[1] : (e == 2 ? d[2] : d[3]));
+                const float nrm = __shfl(dd, (l16 >> 2) * 16 + l16);
+                const int r = 16 * rb + l16;
+                const float cr = r < valid ? fmaf(cA, nrm, cB) : -__builtin_inff();
+#pragma unroll
+                for (int f = 0; f < FPW; ++f) {
+                    f32x4 acc = mfma_bf16(wf[f][0], x[rb][0], zero4);
+                    acc = mfma_bf16(wf[f][1], x[rb][1], acc);
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(c1, acc[0], cr));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(c1, acc[1], cr));
+                    const float p2 = __builtin_amdgcn_exp2f(fmaf(c1, acc[2], cr));
+                    const float p3 = __builtin_amdgcn_exp2f(fmaf(c1, acc[3], cr));
+                    *reinterpret_cast<uint2*>(reinterpret_cast<char*>(phi) + tile_off<FSEG>(r, 16 * (fb0 + f) + 4 * g)) =
+                        make_uint2(pack2_bf16(p0, p1), pack2_bf16(p2, p3));
+                }
+            }
+        };
+        bf16x8 xq[4][2], xk[4][2];
+        // prologue: chunk t_begin mapped into buffer 0 (queries need no zeroing:
+        // their rows past the end give outputs that are not stored)
+        load_x(qh, t_begin, xq);
+        load_x(kh, t_begin, xk);
+        map(xq, fq[0], 64);
+        map(xk, fk[0], valid_of(t_begin));
+        if (t_begin + 1 < t_end) {
+            load_x(qh, t_begin + 1, xq);
+            load_x(kh, t_begin + 1, xk);
+        }
+        for (int64_t t = t_begin; t < t_end; ++t) {
+            const int b = (int)((t - t_begin) & 1);
+            __syncthreads();  // B(t)
+            if (t + 1 < t_end) {
+                map(xq, fq[b ^ 1], 64);
+                if (t + 2 < t_end) load_x(qh, t + 2, xq);
+            }
+            __syncthreads();  // BS(t)
+            if (t + 1 < t_end) {
+                map(xk, fk[b ^ 1], valid_of(t + 1));
+                if (t + 2 < t_end) load_x(kh, t + 2, xk);
+            }
+        }
+        __syncthreads();  // B(t_end)
+        return;
+    }
+
+    // ================= product waves =================
+    // value tile t: this wave's two 1 KiB pieces (rows 16 pw .. 16 pw + 15)
+    auto issue = [&](int64_t t, u16* dst) __attribute__((always_inline)) {
         const int last = (int)(L - 1 - t * 64);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            copy_piece(qh + t * 64 * 64, 64, last, s.q, pw * 2 + i, lane);
-            copy_piece(kh + t * 64 * 64, 64, last, s.k, pw * 2 + i, lane);
-            copy_piece(vh + t * 64 * dv, dv, last, s.v, pw * 2 + i, lane);
-        }
+        for (int i = 0; i < 2; ++i) copy_piece(vh + t * 64 * dv, dv, last, dst, pw * 2 + i, lane);
     };
-    // Row constants log2(e) (-s^2 |x_r|^2 / 2) - log2(m) / 2 of the 16 q and k
-    // rows this prep wave copied (16 pw .. 16 pw + 15); -inf for key rows past
-    // the end of the sequence.
-    auto row_consts = [&](int64_t t, const RawStage& s, float (*out)[64]) __attribute__((always_inline)) {
-        const int r = 16 * pw + lane / 4, qd = lane % 4;
-#pragma unroll
-        for (int x = 0; x < 2; ++x) {
-            const char* tile = reinterpret_cast<const char*>(x == 0 ? s.q : s.k);
-            const uint4 u0 = *reinterpret_cast<const uint4*>(tile + tile_off<8>(r, 16 * qd));
-            const uint4 u1 = *reinterpret_cast<const uint4*>(tile + tile_off<8>(r, 16 * qd + 8));
-            float q = sumsq(as_bf16x8(u0), as_bf16x8(u1));
-            q += __shfl_xor(q, 1);
-            q += __shfl_xor(q, 2);
-            if (qd == 0) out[x][r] = (x == 1 && t * 64 + r >= L) ? -__builtin_inff() : fmaf(cA, q, cB);
-        }
+    // this wave's copies of value tile t are in (two copy instructions per tile)
+    auto land = [&](int64_t t) __attribute__((always_inline)) {
+        const int64_t newest = t + NV - 2 < t_end - 1 ? t + NV - 2 : t_end - 1;
+        wait_groups<2, NV - 2>((int)(newest - t));
     };
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    // output rows from the V tile of a stage: piece (pw * 2 + i) * 64 + lane
-    auto read_out = [&](const RawStage& s, u32x4 (&ob)[2]) __attribute__((always_inline)) {
+    // output rows of a stage (the same rows as this wave's copies): piece
+    // (pw * 2 + i) * 64 + lane
+    auto read_out = [&](const u16* from, u32x4 (&ob)[2]) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int piece = (pw * 2 + i) * WAVE + lane, r = piece / 8, seg = piece % 8;
-            ob[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(s.v) + tile_off<8>(r, seg * 8));
+            ob[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(from) + tile_off<8>(r, seg * 8));
         }
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the stage may be refilled
     };
@@ -585,235 +618,190 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             if (r < valid) __builtin_nontemporal_store(ob[i], reinterpret_cast<u32x4*>(o + (int64_t)r * dv + seg * 8));
         }
     };
-    // z: wave (fh, pw) with pw < NKH keeps feature step kz = fh NKH + pw
-    const bool has_z = pw < NKH;
-    const int kz = ks0 + pw;
-    // z after the update, as bf16 hi / lo operand pieces
-    auto put_z = [&](const f32x4 (&Zs)[2]) __attribute__((always_inline)) {
-        if (l16 == 0) {
-            const float a[4] = {Zs[0][0], Zs[0][1], Zs[0][2], Zs[0][3]};
-            const float b[4] = {Zs[1][0], Zs[1][1], Zs[1][2], Zs[1][3]};
-            const uint4 hi = pack8(a, b);
-            zhl[kz * 4 + g] = hi;
-            zhl[(NKS + kz) * 4 + g] = pack8_lo(a, b, hi);
-        }
+    const bool has_z = pw < NKS / KPW;  // keeps feature steps KPW pw .. KPW pw + KPW - 1 of z
+    auto put_z = [&](const f32x4 (&Zs)[KPW][2]) __attribute__((always_inline)) {
+        if (l16 == 0)
+#pragma unroll
+            for (int k2 = 0; k2 < KPW; ++k2) {
+                const float a[4] = {Zs[k2][0][0], Zs[k2][0][1], Zs[k2][0][2], Zs[k2][0][3]};
+                const float c[4] = {Zs[k2][1][0], Zs[k2][1][1], Zs[k2][1][2], Zs[k2][1][3]};
+                const uint4 hi = pack8(a, c);
+                zhl[(KPW * pw + k2) * 4 + g] = hi;
+                zhl[(NKS + KPW * pw + k2) * 4 + g] = pack8_lo(a, c, hi);
+            }
     };
 
-    // prologue: W, the group's prefix state and normaliser, then the first
-    // tiles and the row constants of the first
-    // land(t): this prep wave's copies of tile t are in (six copy instructions per tile)
-    auto land = [&](int64_t t) __attribute__((always_inline)) {
-        const int64_t newest = t + NSTAGE - 2 < t_end - 1 ? t + NSTAGE - 2 : t_end - 1;
-        wait_groups<6, NSTAGE - 2>((int)(newest - t));
-    };
-    bf16x8 wf[FPW][2];
+    // state: P[ks][hf] lane (g, l16) element i = P[32 ks + 8g + 4hf + i][cw + l16]
+    f32x4 P[NKS][2];
 #pragma unroll
-    for (int f = 0; f < FPW; ++f) load_w_frag(p.W, fb0 + f, lane, wf[f]);
-    // P[c][hf]: state rows 32 (ks0 + c) + 8g + 4hf + i, column cw + l16
-    f32x4 P[NKH][2];
+    for (int ks = 0; ks < NKS; ++ks) P[ks][0] = P[ks][1] = zero4;
+    f32x4 Zs[KPW][2];
 #pragma unroll
-    for (int c = 0; c < NKH; ++c) P[c][0] = P[c][1] = zero4;
-    // z of features 32 kz + 8g + 4hf + i (every l16)
-    f32x4 Zs[2] = {zero4, zero4};
+    for (int k2 = 0; k2 < KPW; ++k2) Zs[k2][0] = Zs[k2][1] = zero4;
     const bool has_prefix = grp > 0;
     if (p.P0 != nullptr && has_prefix) {
         const float* P0 = p.P0 + (slot * M) * (int64_t)dv + col0 + cw + l16;
 #pragma unroll
-        for (int c = 0; c < NKH; ++c)
+        for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) P[c][hf][e] = P0[(int64_t)(32 * (ks0 + c) + 8 * g + 4 * hf + e) * dv];
+                for (int e = 0; e < 4; ++e) P[ks][hf][e] = P0[(int64_t)(32 * ks + 8 * g + 4 * hf + e) * dv];
     }
     if constexpr (NORM) {
         if (has_z) {
             if (p.z0 != nullptr && has_prefix)
 #pragma unroll
-                for (int hf = 0; hf < 2; ++hf)
+                for (int k2 = 0; k2 < KPW; ++k2)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) Zs[hf][e] = p.z0[slot * M + 32 * kz + 8 * g + 4 * hf + e];
+                    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            Zs[k2][hf][e] = p.z0[slot * M + 32 * (KPW * pw + k2) + 8 * g + 4 * hf + e];
             put_z(Zs);
         }
     }
 #pragma unroll
-    for (int f = 0; f < FPW; ++f) {
-        settle(wf[f][0]);
-        settle(wf[f][1]);
+    for (int ks = 0; ks < NKS; ++ks) {
+        settle(P[ks][0]);
+        settle(P[ks][1]);
     }
 #pragma unroll
-    for (int c = 0; c < NKH; ++c) {
-        settle(P[c][0]);
-        settle(P[c][1]);
+    for (int k2 = 0; k2 < KPW; ++k2) {
+        settle(Zs[k2][0]);
+        settle(Zs[k2][1]);
     }
-    settle(Zs[0]);
-    settle(Zs[1]);
     // the copies go out after the loads above have been waited for
-    if (prep) {
-        for (int s0 = 0; s0 < NSTAGE - 1; ++s0)
-            if (t_begin + s0 < t_end) issue(t_begin + s0, st[s0]);
-        land(t_begin);
-        row_consts(t_begin, st[0], crl[0]);
-    }
+    for (int s0 = 0; s0 < NV - 1; ++s0)
+        if (t_begin + s0 < t_end) issue(t_begin + s0, vst[s0]);
+    land(t_begin);
     const RowAddr<FSEG> raf(lane);
     const RowAddr<8> ra8(lane);
-    const RowAddrK<FSEG> rak(lane, ks0);
-    const ColAddrK<FSEG> cak(lane, ks0);
+    const ColAddr<FSEG> caf(lane);
 
-    int si = 0;
+    u32x4 ob[2];  // chunk t - 1's output rows, stored once tile t + 1 has landed
+    int si = 0;   // value stage of chunk t
     for (int64_t t = t_begin; t < t_end; ++t) {
-        RawStage& s = st[si];
-        const int sp = si == 0 ? NSTAGE - 1 : si - 1;  // stage of chunk t - 1
-        const int sn = si == NSTAGE - 1 ? 0 : si + 1;  // stage of tile t + 1
-        const int cp = (int)((t - t_begin) & 1);       // chunk parity (row constants)
+        const int b = (int)((t - t_begin) & 1);
+        const int sp = si == 0 ? NV - 1 : si - 1;  // stage of chunk t - 1
+        const int sn = si == NV - 1 ? 0 : si + 1;  // stage of tile t + 1
+        const u16* q_ = fq[b];
+        const u16* k_ = fk[b];
+        u16* v_ = vst[si];
         // the lane's values formed again each chunk (opaque to the compiler), so
         // that the LDS addresses derived from them are not all held in registers
         // across the chunk loop
         int lane_o = lane;
         asm volatile("" : "+v"(lane_o));
         const int l16 = lane_o % 16, g = lane_o / 16, c4 = 4 * (lane_o & 3), c8 = 8 * (lane_o & 3);
-        __syncthreads();  // B1(t)
-        if (prep) {
-            // chunk t - 1's outputs leave the other stage (stored first, so that
-            // the stores drain during the chunk), which then takes tile t + 1
-            // chunk t - 1's outputs leave its stage (stored first, so that the
-            // stores drain during the chunk), which then takes tile t + NSTAGE - 1
-            if (t > t_begin) {
-                u32x4 ob[2];
-                read_out(st[sp], ob);
-                store_out(t - 1, ob);
-            }
-            if (t + NSTAGE - 1 < t_end) issue(t + NSTAGE - 1, st[sp]);
-        }
-        // phi(q) (waves 0-3) and phi(k) (waves 4-7) of feature blocks fb0 .. fb0 + FPW - 1
-        map_tile<M>(wf, prep ? s.k : s.q, ra8, prep ? fk : fq, fb0, c1, crl[cp][prep ? 1 : 0], lane_o);
-        __syncthreads();  // B2(t)
+        __syncthreads();  // B(t)
+        // chunk t - 1's output rows leave its stage, which takes value tile t + NV - 1
+        if (t > t_begin) read_out(vst[sp], ob);
+        if (t + NV - 1 < t_end) issue(t + NV - 1, vst[sp]);
         // score blocks (ib, jb), jb <= ib (b = 0..9), as S^T (lane (g, l16): keys
         // 16 jb + 4g + e of query row 16 ib + l16), and the two blocks above the
         // diagonal the 32-key operand reads also cover, (0, 1) and (2, 3) (b = 10,
-        // 11), as zeros: wave w takes b = w and, for w < 4, b = w + 8
+        // 11), as zeros: wave w takes b = w, w + 4, w + 8
 #pragma unroll
-        for (int pass = 0; pass < 2; ++pass) {
-            const int b = wave + 8 * pass;
-            if (b < 12) {
-                const int ib = b < 1 ? 0 : (b < 3 ? 1 : (b < 6 ? 2 : (b < 10 ? 3 : (b == 10 ? 0 : 2))));
-                const int jb = b < 10 ? b - ib * (ib + 1) / 2 : ib + 1;
-                const int i = 16 * ib + l16;
-                uint2 w2 = make_uint2(0u, 0u);
-                if (b < 10) {
-                    f32x4 acc = zero4, acc2 = zero4;  // two chains (even and odd steps)
+        for (int pass = 0; pass < 3; ++pass) {
+            const int bb = pw + 4 * pass;
+            const int ib = bb < 1 ? 0 : (bb < 3 ? 1 : (bb < 6 ? 2 : (bb < 10 ? 3 : (bb == 10 ? 0 : 2))));
+            const int jb = bb < 10 ? bb - ib * (ib + 1) / 2 : ib + 1;
+            const int i = 16 * ib + l16;
+            uint2 w2 = make_uint2(0u, 0u);
+            if (bb < 10) {
+                f32x4 acc = zero4, acc2 = zero4;  // two chains (even and odd steps)
 #pragma unroll
-                    for (int ks = 0; ks < NKS; ks += 2) {
-                        acc = mfma_bf16(row_at(fk, raf.off(16 * jb, 32 * ks)), row_at(fq, raf.off(16 * ib, 32 * ks)), acc);
-                        acc2 = mfma_bf16(row_at(fk, raf.off(16 * jb, 32 * ks + 32)), row_at(fq, raf.off(16 * ib, 32 * ks + 32)),
-                                         acc2);
-                    }
-                    acc += acc2;
-                    const int j0 = 16 * jb + 4 * g;
-                    w2 = make_uint2(pack2_bf16(j0 <= i ? acc[0] : 0.f, j0 + 1 <= i ? acc[1] : 0.f),
-                                    pack2_bf16(j0 + 2 <= i ? acc[2] : 0.f, j0 + 3 <= i ? acc[3] : 0.f));
-                }
-                *reinterpret_cast<uint2*>(reinterpret_cast<char*>(stile) + tile_off<8>(i, perm_pos(16 * jb + 4 * g))) = w2;
-            }
-        }
-        if constexpr (NORM) {
-            if (prep) {
-                // phi(q_r) . z for rows 16 ib + 4g + e (ib = pw): z as bf16 hi + lo
-                f32x4 acc = zero4, acc2 = zero4;  // hi and lo chains
-#pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) {
-                    const bf16x8 a = row_at(fq, raf.off(16 * pw, 32 * ks));
-                    acc = mfma_bf16(a, as_bf16x8(zhl[ks * 4 + g]), acc);
-                    acc2 = mfma_bf16(a, as_bf16x8(zhl[(NKS + ks) * 4 + g]), acc2);
+                for (int ks = 0; ks < NKS; ks += 2) {
+                    acc = mfma_bf16(row_at(k_, raf.off(16 * jb, 32 * ks)), row_at(q_, raf.off(16 * ib, 32 * ks)), acc);
+                    acc2 = mfma_bf16(row_at(k_, raf.off(16 * jb, 32 * ks + 32)), row_at(q_, raf.off(16 * ib, 32 * ks + 32)),
+                                     acc2);
                 }
                 acc += acc2;
-                if (l16 == 0) *reinterpret_cast<float4*>(qzl + 16 * pw + 4 * g) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+                const int j0 = 16 * jb + 4 * g;
+                w2 = make_uint2(pack2_bf16(j0 <= i ? acc[0] : 0.f, j0 + 1 <= i ? acc[1] : 0.f),
+                                pack2_bf16(j0 + 2 <= i ? acc[2] : 0.f, j0 + 3 <= i ? acc[3] : 0.f));
             }
+            *reinterpret_cast<uint2*>(reinterpret_cast<char*>(stile) + tile_off<8>(i, perm_pos(16 * jb + 4 * g))) = w2;
         }
-        __syncthreads();  // B3(t)
+        if constexpr (NORM) {
+            // phi(q_r) . z for rows 16 pw + 4g + e: z as bf16 hi + lo
+            f32x4 acc = zero4, acc2 = zero4;
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const bf16x8 a = row_at(q_, raf.off(16 * pw, 32 * ks));
+                acc = mfma_bf16(a, as_bf16x8(zhl[ks * 4 + g]), acc);
+                acc2 = mfma_bf16(a, as_bf16x8(zhl[(NKS + ks) * 4 + g]), acc2);
+            }
+            acc += acc2;
+            if (l16 == 0) *reinterpret_cast<float4*>(qzl + 16 * pw + 4 * g) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        }
+        __syncthreads();  // BS(t)
         {
-            // this wave's half of the feature steps: the inter product O^T (lane
-            // (g, l16): output row 16 ib + l16, columns cw + 4g + e), partial
-            f32x4 O[4];
+            // O^T: lane (g, l16) holds output row 16 ib + l16, columns cw + 4g + e
+            f32x4 O[4], R[4];
 #pragma unroll
-            for (int ib = 0; ib < 4; ++ib) O[ib] = zero4;
+            for (int ib = 0; ib < 4; ++ib) O[ib] = R[ib] = zero4;
 #pragma unroll
-            for (int c = 0; c < NKH; ++c) {
-                const bf16x8 pk = pack_acc_bf16(P[c][0], P[c][1]);
+            for (int ks = 0; ks < NKS; ++ks) {
+                const bf16x8 pk = pack_acc_bf16(P[ks][0], P[ks][1]);
 #pragma unroll
-                for (int ib = 0; ib < 4; ++ib) O[ib] = mfma_bf16(pk, row_at(fq, rak.off(16 * ib, c)), O[ib]);
+                for (int ib = 0; ib < 4; ++ib) O[ib] = mfma_bf16(pk, row_at(q_, raf.off(16 * ib, 32 * ks)), O[ib]);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            // the upper half's partial goes through the raw q and k tiles of this
-            // stage (free since B2)
-            f32x4* obuf = reinterpret_cast<f32x4*>(s.q);
-            if (fh == 1)
-#pragma unroll
-                for (int ib = 0; ib < 4; ++ib) obuf[(pw * 4 + ib) * WAVE + lane_o] = O[ib];
             bf16x8 vb[2];
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) vb[kk] = col_op<8>(s.v, 32 * kk, cw + c4, lane_o);
-            // P += phi(K)^T V over this wave's feature steps
+            for (int kk = 0; kk < 2; ++kk) vb[kk] = col_op<8>(v_, 32 * kk, cw + c4, lane_o);
 #pragma unroll
-            for (int c = 0; c < NKH; ++c) {
+            for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+                for (int kk = 0; kk <= ib / 2; ++kk) {
+                    const bf16x8 sb = row_at(stile, ra8.off(16 * ib, 32 * kk));
+                    O[ib] = mfma_bf16(vb[kk], sb, O[ib]);
+                    if constexpr (NORM) R[ib] = mfma_bf16(ones, sb, R[ib]);
+                }
+            // the output rows (normalised by phi(q_r) . z + the row's score sum)
+            // into this wave's own V columns
+#pragma unroll
+            for (int ib = 0; ib < 4; ++ib) {
+                const int r = 16 * ib + l16;
+                const float rd = NORM ? __builtin_amdgcn_rcpf(qzl[r] + R[ib][0]) : 1.f;
+                *reinterpret_cast<uint2*>(reinterpret_cast<char*>(v_) + tile_off<8>(r, cw + 4 * g)) =
+                    make_uint2(pack2_bf16(O[ib][0] * rd, O[ib][1] * rd), pack2_bf16(O[ib][2] * rd, O[ib][3] * rd));
+            }
+            // P += phi(K)^T V
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
                     for (int hf = 0; hf < 2; ++hf)
-                        P[c][hf] = mfma_bf16(col_at_k(fk, cak, 32 * kk, c, hf), vb[kk], P[c][hf]);
+                        P[ks][hf] = mfma_bf16(col_at(k_, caf, 32 * kk, 32 * ks, hf), vb[kk], P[ks][hf]);
                 __builtin_amdgcn_sched_barrier(0);
             }
             if constexpr (NORM) {
                 if (has_z) {
-                    // z += the column sums of phi(K) at feature step kz
+                    // z += the column sums of phi(K) at this wave's feature steps
 #pragma unroll
-                    for (int kk = 0; kk < 2; ++kk)
+                    for (int k2 = 0; k2 < KPW; ++k2)
 #pragma unroll
-                        for (int hf = 0; hf < 2; ++hf)
-                            Zs[hf] = mfma_bf16(col_op<FSEG>(fk, 32 * kk, 32 * kz + c8 + 4 * hf, lane_o), ones, Zs[hf]);
+                        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                            for (int hf = 0; hf < 2; ++hf)
+                                Zs[k2][hf] = mfma_bf16(col_op<FSEG>(k_, 32 * kk, 32 * (KPW * pw + k2) + c8 + 4 * hf, lane_o),
+                                                       ones, Zs[k2][hf]);
                     put_z(Zs);
                 }
             }
-            __syncthreads();  // B4(t): the upper halves' partial outputs are in
-            if (fh == 0) {
-                // the lower half adds the upper half's partial and the intra product
-                // tril(S) V, and with the normaliser divides by phi(q_r) . z + the
-                // row's score sum (from the matrix cores with a ones operand)
-                f32x4 R[4];
-#pragma unroll
-                for (int ib = 0; ib < 4; ++ib) {
-                    O[ib] += obuf[(pw * 4 + ib) * WAVE + lane_o];
-                    R[ib] = zero4;
-                }
-#pragma unroll
-                for (int ib = 0; ib < 4; ++ib)
-#pragma unroll
-                    for (int kk = 0; kk <= ib / 2; ++kk) {
-                        const bf16x8 sb = row_at(stile, ra8.off(16 * ib, 32 * kk));
-                        O[ib] = mfma_bf16(vb[kk], sb, O[ib]);
-                        if constexpr (NORM) R[ib] = mfma_bf16(ones, sb, R[ib]);
-                    }
-                // four consecutive columns of row 16 ib + l16 per lane into this
-                // wave's V columns of the stage (the prep waves store whole rows)
-#pragma unroll
-                for (int ib = 0; ib < 4; ++ib) {
-                    const int r = 16 * ib + l16;
-                    const float rd = NORM ? __builtin_amdgcn_rcpf(qzl[r] + R[ib][0]) : 1.f;
-                    *reinterpret_cast<uint2*>(reinterpret_cast<char*>(s.v) + tile_off<8>(r, cw + 4 * g)) =
-                        make_uint2(pack2_bf16(O[ib][0] * rd, O[ib][1] * rd), pack2_bf16(O[ib][2] * rd, O[ib][3] * rd));
-                }
-            } else if (t + 1 < t_end) {
-                land(t + 1);
-                row_consts(t + 1, st[sn], crl[cp ^ 1]);
-            }
         }
+        // tile t + 1 must be in before B(t + 1); then chunk t - 1's rows go out
+        if (t + 1 < t_end) land(t + 1);
+        if (t > t_begin) store_out(t - 1, ob);
         si = sn;
     }
-    __syncthreads();  // B1(t_end): the last chunk's outputs are in its stage
-    if (prep) {
-        u32x4 ob[2];
-        read_out(st[si == 0 ? NSTAGE - 1 : si - 1], ob);
-        store_out(t_end - 1, ob);
-    }
+    __syncthreads();  // B(t_end): the last chunk's outputs are in its stage
+    read_out(vst[si == 0 ? NV - 1 : si - 1], ob);
+    store_out(t_end - 1, ob);
 }
 
 // ---------------------------------------------------------------------------
