@@ -51,6 +51,22 @@ def lib_hash() -> str:
     return h.hexdigest()[:16]
 
 
+# the sources the dominant kernel (chunked_fwd_pipe at d_k = 64 and 128) is
+# compiled from: its translation unit and the headers it includes
+KERNEL_SOURCES = ("la_pipe.hip", "la_pipe.hpp", "la_fwd_pipe.hpp", "la_common.hpp", "la_kernels.hpp")
+
+
+def kernel_hash() -> str:
+    """Hash of the dominant kernel's sources (ties its traffic counters to the
+    code they were taken on; other kernels' changes leave it alone)."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "chunked_causal_linear_amd", "csrc")
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
 def read_traffic():
     """The `key: value` lines of the committed counter summary (or {})."""
     out = {}
@@ -288,7 +304,7 @@ def run_headline(args):
     achieved_gbs = alg_bytes3 / (k3 * 1e-3) / 1e9
     traffic = None
     tr = read_traffic()
-    if tr.get("lib_hash") == lib_hash() and tr.get("chunk") == str(C) and tr.get("group") == str(G):
+    if tr.get("kernel_hash") == kernel_hash() and tr.get("chunk") == str(C) and tr.get("group") == str(G):
         traffic = float(tr["bytes_per_launch"])
     res = {
         "metric": METRIC,
@@ -526,6 +542,46 @@ def run_extras(args, out):
         "oracle_sample": "oracle.loglinear_chunked on 1024 rows of one head, scaled to L"}
     del f, qd, kd, vd, lamd
     torch.cuda.empty_cache()
+    # ---- next: the delta rule and its gated form at the headline shape (chunks of 64)
+    delta = {}
+    C = 64
+    n_ch = (w3.L + C - 1) // C
+    # matrix-core work per chunk and head: K K^T, Q K^T, T R, the intra product
+    # (4 C^2 d), K P, Q P, K^T U (3 C d^2) and the substitution (C^3 / 2)
+    d_flops = 2 * (4 * C * C * w3.d_k + 3 * C * w3.d_k * w3.d_v + C ** 3 // 2) * n_ch * w3.BH
+    # bytes: q, k, v, o; k again for the transform; T written once and read by each value
+    # tile; the gate logs written and read by each value tile; beta (and alpha) read once
+    n_vt = w3.d_v // 64
+    d_bytes = w3.BH * (w3.L * (3 * w3.d_k + 2 * w3.d_v) * 2 + n_ch * C * C * 2 * (1 + n_vt)
+                       + n_ch * C * 4 * (1 + n_vt))
+    for gated in (False, True):
+        q, k, v, beta, alpha = wl.delta_inputs(3, w3.BH, w3.L, w3.d_k, w3.d_v, gated, want_exact=False)
+        bd = torch.from_numpy(beta).cuda()
+        ad = torch.from_numpy(alpha).cuda() if gated else None
+        qd, kd, vd = dev_bf16(q.bits), dev_bf16(k.bits), dev_bf16(v.bits)
+        del q, k, v
+        f = la.DeltaForward(qd, kd, vd, bd, ad, return_state=True)
+        ms = row_time(f.run)
+        nb = d_bytes + w3.BH * w3.L * 4 * (2 if gated else 1)
+        ent = {"ms": ms, "tokens_per_s": w3.B * w3.L / (ms * 1e-3), **hbm(nb, ms),
+               "TFLOP/s": d_flops / (ms * 1e-3) / 1e12, "vs_linear_forward": fwd["w3_C64"]["ms"] / ms}
+        if gated:
+            # one decode step on the 128 final states (128 x 128 fp32), from the forward's last token
+            S, t0 = f.S_final, w3.L - 1
+            o = torch.empty(w3.BH, w3.d_v, dtype=torch.float32, device="cuda")
+            qs, ks, vs = (x[:, t0].contiguous() for x in (qd, kd, vd))
+            bs, as_ = bd[:, t0].contiguous(), ad[:, t0].contiguous()
+            ms_d = row_time(lambda: la.recurrent_step_delta(qs, ks, vs, S, bs, as_, out=o))
+            delta["decode_128_states"] = {"ms": ms_d, **hbm(w3.BH * w3.d_k * w3.d_v * 4 * 2, ms_d)}
+            qh_, kh_, vh_, bh_, ah_ = wl.delta_head_inputs(3, 0, 1024, w3.d_k, w3.d_v, True)
+            ent["oracle_s_per_head"] = _oracle_time(
+                lambda: oracle.delta_chunked(qh_, kh_, vh_, bh_.astype(np.float64), ah_.astype(np.float64), C)) \
+                * w3.L / 1024
+            ent["oracle_sample"] = "oracle.delta_chunked on 1024 rows of one head, scaled to L"
+        delta["w3_gated" if gated else "w3"] = ent
+        del f, qd, kd, vd, bd, ad
+        torch.cuda.empty_cache()
+    rows["next_delta"] = delta
     # ---- next: FAVOR+ against exact softmax (the linear-attention page's error study)
     qf, kf, vf = wl.favor_study_inputs()
     dd = qf.exact.shape[2]
