@@ -798,7 +798,8 @@ la_status la_chunked_forward_noalloc(const void* q, const void* k, const void* v
                                      void* S_final, void* z_final, int64_t group, la_stream_t stream) {
     g_last_error[0] = 0;
     Plan P{};
-    la_status st = make_plan(P, in_dt, BH, L, d_in, d_v, C, causal, normalize, f, m, in_scale, group, false);
+    la_status st = make_plan(P, in_dt, BH, L, d_in, d_v, C, causal, normalize, f, m, in_scale, group, false,
+                             out_dt == LA_BF16);
     if (st != LA_OK) return st;
     if (P.ws_total > (size_t)LA_NOALLOC_SCRATCH_BYTES)
         return fail(LA_ERR_UNSUPPORTED,

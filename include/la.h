@@ -196,8 +196,10 @@ la_status la_chunked_forward(const void* q, const void* k, const void* v, la_dty
  * allocate device memory or pass a workspace (code under HIP graph capture,
  * tight serving loops, harnesses that forbid allocation).  Same arguments,
  * results and errors as la_chunked_forward, without workspace / ws_bytes: the
- * scratch it needs (la_chunked_forward_workspace bytes for the same arguments)
- * comes from a static device array of LA_NOALLOC_SCRATCH_BYTES inside the
+ * scratch it needs (at most la_chunked_forward_workspace bytes for the same
+ * arguments; FAVOR+ with a bf16 output, mapped inside the kernels, needs only
+ * the phase-1 states) comes from a static device array of
+ * LA_NOALLOC_SCRATCH_BYTES inside the
  * library, one per device, held until the process ends; its address is looked
  * up on the first call on each device (with that device current).  It calls no
  * allocator.  A call needing more scratch returns LA_ERR_UNSUPPORTED and

@@ -1,9 +1,9 @@
 """The allocation-free forward (la_chunked_forward_noalloc) through the C ABI,
 against la_chunked_forward with a workspace of its own: two calls in a row, the
 second smaller than the first, each needing scratch (phase-1 states of several
-groups, their scan, and for FAVOR+ the mapped q and k).  The two entry points
-run the same kernels on the same plan, so their outputs agree bit for bit; one
-head of each is also checked against the oracle at the bf16 band."""
+groups and their scan).  The two entry points run the same kernels on the same
+plan, so their outputs agree bit for bit; one head of each is also checked
+against the oracle at the bf16 band."""
 import numpy as np
 import pytest
 
@@ -56,14 +56,35 @@ def test_noalloc_two_calls_second_smaller():
         _check_case(c)
 
 
+def test_noalloc_full_favor_workload():
+    """Workload 5 at full size with a bf16 output: FAVOR+ mapped inside the kernels
+    needs only the phase-1 states (about 16 MB), so the allocation-free forward
+    takes it, and agrees bit for bit with the forward given a workspace."""
+    torch = torch_cuda()
+    w = wl.WORKLOADS[5]
+    q, k, v, W = wl.workload_inputs(w, want_exact=False)
+    qd, kd, vd, Wd = dev_bf16(q.bits), dev_bf16(k.bits), dev_bf16(v.bits), dev_bf16(W[0])
+    del q, k, v
+    log(f"noalloc forward at workload 5's full size BH={w.BH} L={w.L}")
+    ref_o, ref_S, ref_z = la.chunked_forward(qd, kd, vd, 64, normalize=True, fmap="favor", W=Wd, return_state=True)
+    o = torch.empty_like(ref_o)
+    S = torch.empty_like(ref_S)
+    z = torch.empty_like(ref_z)
+    la.chunked_forward_noalloc(qd, kd, vd, 64, normalize=True, fmap="favor", W=Wd, out=o, S_final=S, z_final=z)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref_o) and torch.equal(S, ref_S) and torch.equal(z, ref_z)
+
+
 def test_noalloc_rejects_more_than_its_scratch():
-    """A forward whose scratch exceeds the static array is refused before any launch."""
+    """A forward whose scratch exceeds the static array is refused before any
+    launch: workload 5 with an fp32 output maps q and k beforehand, three
+    [24, 16384, 256] bf16 copies."""
     w = wl.WORKLOADS[5]
     ws = la.forward_workspace_bytes(b.LA_BF16, w.BH, w.L, w.d_in, w.d_v, 64, True, True, "favor", w.m)
     assert ws > SCRATCH
     lib = la.lib()
     fake = 0x1000  # never dereferenced: the call fails its size check first
     st = lib.la_chunked_forward_noalloc(fake, fake, fake, b.LA_BF16, w.BH, w.L, w.d_in, w.d_v, 64, 1, 1, 2, fake,
-                                        w.m, 1.0, fake, b.LA_BF16, None, None, 0, None)
+                                        w.m, 1.0, fake, b.LA_F32, None, None, 0, None)
     assert st == b.LA_ERR_UNSUPPORTED
     assert b"scratch" in lib.la_last_error()
