@@ -25,14 +25,10 @@
 //  * favor_fwd_kernel: phase 3, the chunks (of 64 rows) of a group from its
 //    prefix state: O = phi(Q) P + tril(phi(Q) phi(K)^T) V, normalised by
 //    phi(Q) z + the row sums of tril(phi(Q) phi(K)^T), then P += phi(K)^T V,
-//    z += the column sums of phi(K).  Eight waves, two per SIMD.  Waves 0-3
-//    map phi(q), waves 4-7 (the prep waves, which also issue the
-//    direct-to-LDS copies of the raw tiles) phi(k), each for a quarter of the
-//    features.  Wave w keeps the state of value columns 16 (w mod 4) .. + 15
-//    over one half of the features (fp32 accumulators; a packed pair of them
-//    is an operand in feature order); waves 0-3 add the other half's partial
-//    outputs and put the output rows into the stage's V tile, which the prep
-//    waves store as whole rows.
+//    z += the column sums of phi(K).  Eight waves, two per SIMD: mapper
+//    waves map phi(k) and phi(q) of the next chunk (a quarter of the features
+//    each) and keep z, while product waves run the current chunk, each with
+//    the state of 16 value columns over all features in fp32 accumulators.
 #include "la_fwd_pipe.hpp"
 
 namespace la {
@@ -221,6 +217,61 @@ __device__ __forceinline__ bf16x8 col_at(const u16* tile, const ColAddr<NSEG>& c
 template <typename T>
 __device__ __forceinline__ void settle(T& v) {
     asm volatile("" : "+v"(v));
+}
+
+// the sum over the 16 lanes of a row of lanes: swaps within quads of lanes,
+// then rotations of the row by 4 and by 8 (DPP)
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float sum16(float v) {
+    v += dpp_f<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+    v += dpp_f<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+    v += dpp_f<0x124>(v);  // row_ror 4
+    v += dpp_f<0x128>(v);  // row_ror 8
+    return v;
+}
+
+// Blocks (I0, J0), (I1, J1) and, when I2 >= 0, (I2, J2) of the score tile
+// tril(phi(Q) phi(K)^T), computed transposed (lane (g, l16): keys 16 J + 4g + e
+// of query row 16 I + l16) over all feature steps and stored, masked, in bf16
+// into the score tile (columns in operand key order).  Blocks that share a
+// query or key block read its fragments once.
+template <int FSEG, int NKS, int I0, int J0, int I1, int J1, int I2, int J2>
+__device__ __forceinline__ void score_blocks(const u16* q_, const u16* k_, u16* stile, const RowAddr<FSEG>& raf,
+                                             int l16, int g) {
+    using namespace pipe;
+    constexpr int NB = I2 >= 0 ? 3 : 2;
+    constexpr int I[3] = {I0, I1, I2 >= 0 ? I2 : 0}, J[3] = {J0, J1, I2 >= 0 ? J2 : 0};
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc[NB][2];  // two chains per block (even and odd feature steps)
+#pragma unroll
+    for (int n = 0; n < NB; ++n) acc[n][0] = acc[n][1] = zero4;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ks += 2)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int n = 0; n < NB; ++n)
+                acc[n][h] = mfma_bf16(row_at(k_, raf.off(16 * J[n], 32 * (ks + h))),
+                                      row_at(q_, raf.off(16 * I[n], 32 * (ks + h))), acc[n][h]);
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+        const f32x4 s = acc[n][0] + acc[n][1];
+        const int i = 16 * I[n] + l16, j0 = 16 * J[n] + 4 * g;
+        const uint2 w2 = make_uint2(pack2_bf16(j0 <= i ? s[0] : 0.f, j0 + 1 <= i ? s[1] : 0.f),
+                                    pack2_bf16(j0 + 2 <= i ? s[2] : 0.f, j0 + 3 <= i ? s[3] : 0.f));
+        *reinterpret_cast<uint2*>(reinterpret_cast<char*>(stile) + tile_off<8>(i, perm_pos(j0))) = w2;
+    }
+}
+// zeros into block (I, J) of the score tile (a block above the diagonal that
+// the 32-key operands of the intra product also read)
+template <int I, int J>
+__device__ __forceinline__ void zero_block(u16* stile, int l16, int g) {
+    using namespace pipe;
+    *reinterpret_cast<uint2*>(reinterpret_cast<char*>(stile) + tile_off<8>(16 * I + l16, perm_pos(16 * J + 4 * g))) =
+        make_uint2(0u, 0u);
 }
 
 // one direct-to-LDS copy of 1 KiB (rows 8b .. 8b + 7 of a 64 x 64 bf16 tile,
@@ -451,40 +502,46 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 //    tiles (direct-to-LDS copies) and store the output rows;
 //  * mapper waves 4-7 map chunk t + 1 meanwhile: each keeps W for a quarter of
 //    the features in registers and reads the raw q and k rows it needs straight
-//    into registers (one chunk ahead), so the raw q and k never occupy LDS.
-// phi(q) and phi(k) are double-buffered by chunk parity.  Two barriers per
-// chunk t:
+//    into registers (one chunk ahead), so the raw q and k never occupy LDS;
+//    phi(k) of chunk t + 1 before BS(t), phi(q) after it.
+// With the normaliser the mapper waves also keep z (the key sums before the
+// chunk they map next) for their features in fp32 registers: they add the
+// column sums of each phi(k) tile they map once the phi(q) tile of the same
+// chunk is mapped, and for each phi(q) tile they put the rows' partial
+// products phi(q_r) . z over their features into LDS; the product waves add
+// the four partials.  phi(k) and these partials are double-buffered by chunk
+// parity; phi(q) is read before BS only, so it has one buffer.  Two barriers
+// per chunk t:
 //   B(t):  phi of chunk t is complete (mapped during chunk t - 1), its value
 //          tile has landed, and chunk t - 1's products are done (the other
-//          phi buffer, the score tile and chunk t - 1's stage are free);
+//          phi(k) buffer, the score tile and chunk t - 1's stage are free);
 //   BS(t): the score tile (tril(phi(Q) phi(K)^T), columns in operand key
-//          order) and, with the normaliser, phi(q_i) . z are complete.
-// The mapper waves map phi(q) of chunk t + 1 before BS(t) and phi(k) after.
+//          order) is complete, and so are the inter products phi(Q) P (the
+//          phi(q) buffer is free).
 // Scores and outputs are computed transposed (keys, resp. value columns, as
 // rows), so a lane holds four consecutive keys or columns of one row (one
 // 8-byte store); the row sums of the score tile come from the matrix cores with
 // a ones operand, in the outputs' layout.  Row norms come from the matrix
-// cores too: the diagonal of x x^T for each 16-row block.
+// cores too: the diagonal of x x^T for each 16-row block.  The ten score blocks
+// on and below the diagonal go to the product waves in groups that share query
+// or key blocks: (0,0) (1,0) (1,1) | (2,0) (2,1) (3,0) | (2,2) (3,2) | (3,1) (3,3).
 template <int M, bool NORM>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void favor_fwd_kernel(FavorParams p) {
     using namespace pipe;
     constexpr int FSEG = M / 8, NKS = M / 32, FPW = M / 64;
     constexpr int PHI_E = 64 * M;  // elements of one phi tile
-    // z is kept by the product waves, KPW feature steps each (waves w < NKS / KPW)
-    constexpr int KPW = NKS >= 4 ? NKS / 4 : 1;
     // as many value stages as the LDS holds beside the rest, at most four
-    constexpr int FIXED = 2 * 2 * PHI_E * 2 + 64 * 64 * 2 + 64 * 4 + 2 * NKS * 4 * 16;
+    constexpr int FIXED = 3 * PHI_E * 2 + 64 * 64 * 2 + 2 * 64 * 4 * 4;
     constexpr int NVFIT = (160 * 1024 - FIXED) / (64 * 64 * 2);
     constexpr int NV = NVFIT < 4 ? NVFIT : 4;
     static_assert(NV >= 2, "value stages");
 
-    __shared__ __attribute__((aligned(16))) u16 fq[2][PHI_E];
+    __shared__ __attribute__((aligned(16))) u16 fq[PHI_E];
     __shared__ __attribute__((aligned(16))) u16 fk[2][PHI_E];
     __shared__ __attribute__((aligned(16))) u16 vst[NV][64 * 64];
     __shared__ __attribute__((aligned(16))) u16 stile[64 * 64];
-    __shared__ __attribute__((aligned(16))) float qzl[64];  // phi(q_i) . z
-    // z before the chunk as operand pieces: [hi, lo][32-feature step ks][lane group g]
-    __shared__ __attribute__((aligned(16))) uint4 zhl[NORM ? 2 * NKS * 4 : 1];
+    // phi(q_r) . z partials: [chunk parity][row r][mapper wave]
+    __shared__ __attribute__((aligned(16))) float qzp[NORM ? 2 * 64 * 4 : 4];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);
@@ -496,7 +553,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int grp = (wi / p.n_dvt) % p.n_groups;
     const int64_t bh = wi / ((int64_t)p.n_dvt * p.n_groups);
     const int col0 = jt * 64, cw = 16 * pw;
-    const int fb0 = pw * FPW;  // mapper: first feature block
+    const int fb0 = pw * FPW;  // mapper: first feature block (FPW blocks of 16 features)
     const int64_t L = p.L;
     const int dv = p.dv;
     const int64_t n_tiles = (L + 63) / 64;
@@ -519,6 +576,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         bf16x8 wf[FPW][2];
 #pragma unroll
         for (int f = 0; f < FPW; ++f) load_w_frag(p.W, fb0 + f, lane, wf[f]);
+        // with the normaliser: z before the chunk whose phi(q) is mapped next,
+        // lane (g, l16) keeping features 16 (fb0 + f) + 4g + i, and the column
+        // sums of the phi(k) tile mapped last (added once its chunk's phi(q) is)
+        float zr[FPW][4], zp[FPW][4];
+#pragma unroll
+        for (int f = 0; f < FPW; ++f)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) zr[f][i] = zp[f][i] = 0.f;
+        if constexpr (NORM)
+            if (p.z0 != nullptr && grp > 0)
+#pragma unroll
+                for (int f = 0; f < FPW; ++f)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) zr[f][i] = p.z0[slot * M + 16 * (fb0 + f) + 4 * g + i];
         // x fragments of tile t: rows 16 rb + l16 (clamped to the last row),
         // inputs 32 h + 8g .. + 7
         auto load_x = [&](const u16* base, int64_t t, bf16x8 (&x)[4][2]) __attribute__((always_inline)) {
@@ -535,37 +606,88 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // (lane (g, l16) holds rows 16 rb + 4g + i against row 16 rb + l16; the
         // diagonal of row r sits in lane (r / 4, r), element r mod 4), then the
         // features fb0 .. fb0 + FPW - 1 of every row (lane (g, l16): features
-        // 16 fb + 4g + i of row 16 rb + l16); key rows at or past `valid` map to 0
-        auto map = [&](const bf16x8 (&x)[4][2], u16* phi, int valid) __attribute__((always_inline)) {
+        // 16 fb + 4g + i of row 16 rb + l16); key rows at or past `valid` map to
+        // 0.  With the normaliser: for queries the rows' partials phi(q_r) . z
+        // into qz, for keys the column sums into zp.
+        auto map = [&](const bf16x8 (&x)[4][2], u16* phi, int valid, bool is_q, float* qz) __attribute__((always_inline)) {
+            float zs[FPW][4];  // this key tile's column sums, before the sum over the lanes of a row
+            float part[4];     // phi(q_r) . z for r = 16 rb + l16, before the sum over the lane groups
+#pragma unroll
+            for (int f = 0; f < FPW; ++f)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) zs[f][i] = 0.f;
+            // the row norms of all four row blocks first (their lane exchanges overlap)
+            float nrm[4];
+            const int e = l16 & 3;
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb) {
                 f32x4 d = mfma_bf16(x[rb][0], x[rb][0], zero4);
                 d = mfma_bf16(x[rb][1], x[rb][1], d);
-                const int e = l16 & 3;
-                const float dd = e == 0 ? d[0] : (e == 1 ? d[1] : (e == 2 ? d[2] : d[3]));
-                const float nrm = __shfl(dd, (l16 >> 2) * 16 + l16);
+                const float d01 = (e & 1) ? d[1] : d[0], d23 = (e & 1) ? d[3] : d[2];
+                nrm[rb] = __shfl((e & 2) ? d23 : d01, (l16 >> 2) * 16 + l16);
+            }
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
                 const int r = 16 * rb + l16;
-                const float cr = r < valid ? fmaf(cA, nrm, cB) : -__builtin_inff();
+                const float cr = r < valid ? fmaf(cA, nrm[rb], cB) : -__builtin_inff();
+                part[rb] = 0.f;
+                // the feature blocks' products as independent chains, then their exponentials
+                f32x4 acc[FPW];
+#pragma unroll
+                for (int f = 0; f < FPW; ++f) acc[f] = mfma_bf16(wf[f][0], x[rb][0], zero4);
+#pragma unroll
+                for (int f = 0; f < FPW; ++f) acc[f] = mfma_bf16(wf[f][1], x[rb][1], acc[f]);
 #pragma unroll
                 for (int f = 0; f < FPW; ++f) {
-                    f32x4 acc = mfma_bf16(wf[f][0], x[rb][0], zero4);
-                    acc = mfma_bf16(wf[f][1], x[rb][1], acc);
-                    const float p0 = __builtin_amdgcn_exp2f(fmaf(c1, acc[0], cr));
-                    const float p1 = __builtin_amdgcn_exp2f(fmaf(c1, acc[1], cr));
-                    const float p2 = __builtin_amdgcn_exp2f(fmaf(c1, acc[2], cr));
-                    const float p3 = __builtin_amdgcn_exp2f(fmaf(c1, acc[3], cr));
-                    *reinterpret_cast<uint2*>(reinterpret_cast<char*>(phi) + tile_off<FSEG>(r, 16 * (fb0 + f) + 4 * g)) =
-                        make_uint2(pack2_bf16(p0, p1), pack2_bf16(p2, p3));
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(c1, acc[f][0], cr));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(c1, acc[f][1], cr));
+                    const float p2 = __builtin_amdgcn_exp2f(fmaf(c1, acc[f][2], cr));
+                    const float p3 = __builtin_amdgcn_exp2f(fmaf(c1, acc[f][3], cr));
+                    const uint2 w2 = make_uint2(pack2_bf16(p0, p1), pack2_bf16(p2, p3));
+                    *reinterpret_cast<uint2*>(reinterpret_cast<char*>(phi) + tile_off<FSEG>(r, 16 * (fb0 + f) + 4 * g)) = w2;
+                    if constexpr (NORM) {
+                        const float ev[4] = {p0, p1, p2, p3};
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            if (is_q)
+                                part[rb] = fmaf(ev[i], zr[f][i], part[rb]);
+                            else
+                                zs[f][i] += ev[i];
+                        }
+                    }
                 }
             }
+            if constexpr (NORM) {
+                if (is_q) {
+#pragma unroll
+                    for (int rb = 0; rb < 4; ++rb) part[rb] += __shfl_xor(part[rb], 16);
+#pragma unroll
+                    for (int rb = 0; rb < 4; ++rb) part[rb] += __shfl_xor(part[rb], 32);
+                    if (g == 0)
+#pragma unroll
+                        for (int rb = 0; rb < 4; ++rb) qz[(16 * rb + l16) * 4 + pw] = part[rb];
+                } else {
+#pragma unroll
+                    for (int f = 0; f < FPW; ++f)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) zp[f][i] = sum16(zs[f][i]);
+                }
+            }
+        };
+        auto add_zp = [&]() __attribute__((always_inline)) {
+#pragma unroll
+            for (int f = 0; f < FPW; ++f)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) zr[f][i] += zp[f][i];
         };
         bf16x8 xq[4][2], xk[4][2];
         // prologue: chunk t_begin mapped into buffer 0 (queries need no zeroing:
         // their rows past the end give outputs that are not stored)
         load_x(qh, t_begin, xq);
         load_x(kh, t_begin, xk);
-        map(xq, fq[0], 64);
-        map(xk, fk[0], valid_of(t_begin));
+        map(xq, fq, 64, true, qzp);
+        map(xk, fk[0], valid_of(t_begin), false, nullptr);
+        add_zp();
         if (t_begin + 1 < t_end) {
             load_x(qh, t_begin + 1, xq);
             load_x(kh, t_begin + 1, xk);
@@ -574,13 +696,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const int b = (int)((t - t_begin) & 1);
             __syncthreads();  // B(t)
             if (t + 1 < t_end) {
-                map(xq, fq[b ^ 1], 64);
-                if (t + 2 < t_end) load_x(qh, t + 2, xq);
+                map(xk, fk[b ^ 1], valid_of(t + 1), false, nullptr);
+                if (t + 2 < t_end) load_x(kh, t + 2, xk);
             }
             __syncthreads();  // BS(t)
             if (t + 1 < t_end) {
-                map(xk, fk[b ^ 1], valid_of(t + 1));
-                if (t + 2 < t_end) load_x(kh, t + 2, xk);
+                map(xq, fq, 64, true, qzp + (b ^ 1) * 256);
+                add_zp();
+                if (t + 2 < t_end) load_x(qh, t + 2, xq);
             }
         }
         __syncthreads();  // B(t_end)
@@ -618,26 +741,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             if (r < valid) __builtin_nontemporal_store(ob[i], reinterpret_cast<u32x4*>(o + (int64_t)r * dv + seg * 8));
         }
     };
-    const bool has_z = pw < NKS / KPW;  // keeps feature steps KPW pw .. KPW pw + KPW - 1 of z
-    auto put_z = [&](const f32x4 (&Zs)[KPW][2]) __attribute__((always_inline)) {
-        if (l16 == 0)
-#pragma unroll
-            for (int k2 = 0; k2 < KPW; ++k2) {
-                const float a[4] = {Zs[k2][0][0], Zs[k2][0][1], Zs[k2][0][2], Zs[k2][0][3]};
-                const float c[4] = {Zs[k2][1][0], Zs[k2][1][1], Zs[k2][1][2], Zs[k2][1][3]};
-                const uint4 hi = pack8(a, c);
-                zhl[(KPW * pw + k2) * 4 + g] = hi;
-                zhl[(NKS + KPW * pw + k2) * 4 + g] = pack8_lo(a, c, hi);
-            }
-    };
-
     // state: P[ks][hf] lane (g, l16) element i = P[32 ks + 8g + 4hf + i][cw + l16]
     f32x4 P[NKS][2];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) P[ks][0] = P[ks][1] = zero4;
-    f32x4 Zs[KPW][2];
-#pragma unroll
-    for (int k2 = 0; k2 < KPW; ++k2) Zs[k2][0] = Zs[k2][1] = zero4;
     const bool has_prefix = grp > 0;
     if (p.P0 != nullptr && has_prefix) {
         const float* P0 = p.P0 + (slot * M) * (int64_t)dv + col0 + cw + l16;
@@ -648,28 +755,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
                 for (int e = 0; e < 4; ++e) P[ks][hf][e] = P0[(int64_t)(32 * ks + 8 * g + 4 * hf + e) * dv];
     }
-    if constexpr (NORM) {
-        if (has_z) {
-            if (p.z0 != nullptr && has_prefix)
-#pragma unroll
-                for (int k2 = 0; k2 < KPW; ++k2)
-#pragma unroll
-                    for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            Zs[k2][hf][e] = p.z0[slot * M + 32 * (KPW * pw + k2) + 8 * g + 4 * hf + e];
-            put_z(Zs);
-        }
-    }
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
         settle(P[ks][0]);
         settle(P[ks][1]);
-    }
-#pragma unroll
-    for (int k2 = 0; k2 < KPW; ++k2) {
-        settle(Zs[k2][0]);
-        settle(Zs[k2][1]);
     }
     // the copies go out after the loads above have been waited for
     for (int s0 = 0; s0 < NV - 1; ++s0)
@@ -685,7 +774,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int b = (int)((t - t_begin) & 1);
         const int sp = si == 0 ? NV - 1 : si - 1;  // stage of chunk t - 1
         const int sn = si == NV - 1 ? 0 : si + 1;  // stage of tile t + 1
-        const u16* q_ = fq[b];
+        const u16* q_ = fq;
         const u16* k_ = fk[b];
         u16* v_ = vst[si];
         // the lane's values formed again each chunk (opaque to the compiler), so
@@ -693,62 +782,39 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // across the chunk loop
         int lane_o = lane;
         asm volatile("" : "+v"(lane_o));
-        const int l16 = lane_o % 16, g = lane_o / 16, c4 = 4 * (lane_o & 3), c8 = 8 * (lane_o & 3);
+        const int l16 = lane_o % 16, g = lane_o / 16, c4 = 4 * (lane_o & 3);
         __syncthreads();  // B(t)
         // chunk t - 1's output rows leave its stage, which takes value tile t + NV - 1
         if (t > t_begin) read_out(vst[sp], ob);
         if (t + NV - 1 < t_end) issue(t + NV - 1, vst[sp]);
-        // score blocks (ib, jb), jb <= ib (b = 0..9), as S^T (lane (g, l16): keys
-        // 16 jb + 4g + e of query row 16 ib + l16), and the two blocks above the
-        // diagonal the 32-key operand reads also cover, (0, 1) and (2, 3) (b = 10,
-        // 11), as zeros: wave w takes b = w, w + 4, w + 8
-#pragma unroll
-        for (int pass = 0; pass < 3; ++pass) {
-            const int bb = pw + 4 * pass;
-            const int ib = bb < 1 ? 0 : (bb < 3 ? 1 : (bb < 6 ? 2 : (bb < 10 ? 3 : (bb == 10 ? 0 : 2))));
-            const int jb = bb < 10 ? bb - ib * (ib + 1) / 2 : ib + 1;
-            const int i = 16 * ib + l16;
-            uint2 w2 = make_uint2(0u, 0u);
-            if (bb < 10) {
-                f32x4 acc = zero4, acc2 = zero4;  // two chains (even and odd steps)
-#pragma unroll
-                for (int ks = 0; ks < NKS; ks += 2) {
-                    acc = mfma_bf16(row_at(k_, raf.off(16 * jb, 32 * ks)), row_at(q_, raf.off(16 * ib, 32 * ks)), acc);
-                    acc2 = mfma_bf16(row_at(k_, raf.off(16 * jb, 32 * ks + 32)), row_at(q_, raf.off(16 * ib, 32 * ks + 32)),
-                                     acc2);
-                }
-                acc += acc2;
-                const int j0 = 16 * jb + 4 * g;
-                w2 = make_uint2(pack2_bf16(j0 <= i ? acc[0] : 0.f, j0 + 1 <= i ? acc[1] : 0.f),
-                                pack2_bf16(j0 + 2 <= i ? acc[2] : 0.f, j0 + 3 <= i ? acc[3] : 0.f));
-            }
-            *reinterpret_cast<uint2*>(reinterpret_cast<char*>(stile) + tile_off<8>(i, perm_pos(16 * jb + 4 * g))) = w2;
+        // the score tile: this wave's group of blocks (the product waves'
+        // groups share query or key blocks), and zeros in blocks (0, 1) and
+        // (2, 3), which the 32-key operands of the intra product also read
+        if (pw == 0) {
+            score_blocks<FSEG, NKS, 0, 0, 1, 0, 1, 1>(q_, k_, stile, raf, l16, g);
+            zero_block<0, 1>(stile, l16, g);
+        } else if (pw == 1) {
+            score_blocks<FSEG, NKS, 2, 0, 2, 1, 3, 0>(q_, k_, stile, raf, l16, g);
+        } else if (pw == 2) {
+            score_blocks<FSEG, NKS, 2, 2, 3, 2, -1, -1>(q_, k_, stile, raf, l16, g);
+        } else {
+            score_blocks<FSEG, NKS, 3, 1, 3, 3, -1, -1>(q_, k_, stile, raf, l16, g);
+            zero_block<2, 3>(stile, l16, g);
         }
-        if constexpr (NORM) {
-            // phi(q_r) . z for rows 16 pw + 4g + e: z as bf16 hi + lo
-            f32x4 acc = zero4, acc2 = zero4;
+        // the inter product O^T = P^T phi(Q)^T: lane (g, l16) holds output row
+        // 16 ib + l16, columns cw + 4g + e
+        f32x4 O[4], R[4];
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                const bf16x8 a = row_at(q_, raf.off(16 * pw, 32 * ks));
-                acc = mfma_bf16(a, as_bf16x8(zhl[ks * 4 + g]), acc);
-                acc2 = mfma_bf16(a, as_bf16x8(zhl[(NKS + ks) * 4 + g]), acc2);
-            }
-            acc += acc2;
-            if (l16 == 0) *reinterpret_cast<float4*>(qzl + 16 * pw + 4 * g) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        for (int ib = 0; ib < 4; ++ib) O[ib] = R[ib] = zero4;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            const bf16x8 pk = pack_acc_bf16(P[ks][0], P[ks][1]);
+#pragma unroll
+            for (int ib = 0; ib < 4; ++ib) O[ib] = mfma_bf16(pk, row_at(q_, raf.off(16 * ib, 32 * ks)), O[ib]);
+            __builtin_amdgcn_sched_barrier(0);
         }
         __syncthreads();  // BS(t)
         {
-            // O^T: lane (g, l16) holds output row 16 ib + l16, columns cw + 4g + e
-            f32x4 O[4], R[4];
-#pragma unroll
-            for (int ib = 0; ib < 4; ++ib) O[ib] = R[ib] = zero4;
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                const bf16x8 pk = pack_acc_bf16(P[ks][0], P[ks][1]);
-#pragma unroll
-                for (int ib = 0; ib < 4; ++ib) O[ib] = mfma_bf16(pk, row_at(q_, raf.off(16 * ib, 32 * ks)), O[ib]);
-                __builtin_amdgcn_sched_barrier(0);
-            }
             bf16x8 vb[2];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) vb[kk] = col_op<8>(v_, 32 * kk, cw + c4, lane_o);
@@ -760,12 +826,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     O[ib] = mfma_bf16(vb[kk], sb, O[ib]);
                     if constexpr (NORM) R[ib] = mfma_bf16(ones, sb, R[ib]);
                 }
-            // the output rows (normalised by phi(q_r) . z + the row's score sum)
-            // into this wave's own V columns
+            // the output rows (normalised by phi(q_r) . z, the mapper waves'
+            // four partials, + the row's score sum) into this wave's own V columns
 #pragma unroll
             for (int ib = 0; ib < 4; ++ib) {
                 const int r = 16 * ib + l16;
-                const float rd = NORM ? __builtin_amdgcn_rcpf(qzl[r] + R[ib][0]) : 1.f;
+                float rd = 1.f;
+                if constexpr (NORM) {
+                    const float4 qq = *reinterpret_cast<const float4*>(qzp + (b * 64 + r) * 4);
+                    rd = __builtin_amdgcn_rcpf((qq.x + qq.y) + (qq.z + qq.w) + R[ib][0]);
+                }
                 *reinterpret_cast<uint2*>(reinterpret_cast<char*>(v_) + tile_off<8>(r, cw + 4 * g)) =
                     make_uint2(pack2_bf16(O[ib][0] * rd, O[ib][1] * rd), pack2_bf16(O[ib][2] * rd, O[ib][3] * rd));
             }
@@ -778,20 +848,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     for (int hf = 0; hf < 2; ++hf)
                         P[ks][hf] = mfma_bf16(col_at(k_, caf, 32 * kk, 32 * ks, hf), vb[kk], P[ks][hf]);
                 __builtin_amdgcn_sched_barrier(0);
-            }
-            if constexpr (NORM) {
-                if (has_z) {
-                    // z += the column sums of phi(K) at this wave's feature steps
-#pragma unroll
-                    for (int k2 = 0; k2 < KPW; ++k2)
-#pragma unroll
-                        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-                            for (int hf = 0; hf < 2; ++hf)
-                                Zs[k2][hf] = mfma_bf16(col_op<FSEG>(k_, 32 * kk, 32 * (KPW * pw + k2) + c8 + 4 * hf, lane_o),
-                                                       ones, Zs[k2][hf]);
-                    put_z(Zs);
-                }
             }
         }
         // tile t + 1 must be in before B(t + 1); then chunk t - 1's rows go out
