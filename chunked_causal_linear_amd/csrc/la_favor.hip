@@ -360,9 +360,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const float a = __uint_as_float(w4[j] << 16), b = __uint_as_float(w4[j] & 0xFFFF0000u);
             q = fmaf(a, a, fmaf(b, b, q));
         }
-        q += __shfl_xor(q, 1);
-        q += __shfl_xor(q, 2);
-        q += __shfl_xor(q, 4);
+        // the sum over the row's eight lanes: swaps within quads, then the
+        // mirror within halves of a row of lanes (DPP)
+        q += dpp_f<0xB1>(q);   // quad_perm [1, 0, 3, 2]
+        q += dpp_f<0x4E>(q);   // quad_perm [2, 3, 0, 1]
+        q += dpp_f<0x141>(q);  // row_half_mirror
         if (seg == 0) out[r] = t * 64 + r < L ? fmaf(cA, q, cB) : -__builtin_inff();
     };
 
@@ -402,47 +404,63 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int l16o = lane_o % 16, go = lane_o / 16, c4 = 4 * (lane_o & 3);
         __syncthreads();  // B(t): tile t and its row constants are in; every wave is done with tile t - 1
         if (t + NSTAGE - 1 < t_end) issue(t + NSTAGE - 1, st[sp]);
+        // operands of this wave's 32-key halves: the x fragments of their row
+        // blocks, the row constants of rows 16 rb + 4g + i, the value columns
+        bf16x8 xa[NKH][2][2], vb[NKH][4];
+        float4 cr[NKH][2];
 #pragma unroll
         for (int kq = 0; kq < NKH; ++kq) {
             const int khh = kh0 + kq;
-            // the two row blocks of this 32-key half and the constants of rows 16 rb + 4g + i
-            bf16x8 xa[2][2];
-            float4 cr[2];
 #pragma unroll
             for (int hb = 0; hb < 2; ++hb) {
                 const int rb = 2 * khh + hb;
 #pragma unroll
-                for (int h = 0; h < 2; ++h) xa[hb][h] = row_op<8>(s.k, 16 * rb + l16o, 32 * h, go);
-                cr[hb] = *reinterpret_cast<const float4*>(&crl[si][16 * rb + 4 * go]);
+                for (int h = 0; h < 2; ++h) xa[kq][hb][h] = row_op<8>(s.k, 16 * rb + l16o, 32 * h, go);
+                cr[kq][hb] = *reinterpret_cast<const float4*>(&crl[si][16 * rb + 4 * go]);
             }
-            bf16x8 vb[4];
 #pragma unroll
-            for (int cb = 0; cb < 4; ++cb) vb[cb] = col_op<8>(s.v, 32 * khh, 16 * cb + c4, lane_o);
+            for (int cb = 0; cb < 4; ++cb) vb[kq][cb] = col_op<8>(s.v, 32 * khh, 16 * cb + c4, lane_o);
+        }
+        // every mapping product first (independent chains), then per feature
+        // block and key half the exponentials, the hi/lo pair and the updates
+        f32x4 acc[NKH][FPW][2];
+#pragma unroll
+        for (int kq = 0; kq < NKH; ++kq)
+#pragma unroll
+            for (int f = 0; f < FPW; ++f)
+#pragma unroll
+                for (int hb = 0; hb < 2; ++hb) acc[kq][f][hb] = mfma_bf16(xa[kq][hb][0], wf[f][0], zero4);
+#pragma unroll
+        for (int kq = 0; kq < NKH; ++kq)
+#pragma unroll
+            for (int f = 0; f < FPW; ++f)
+#pragma unroll
+                for (int hb = 0; hb < 2; ++hb) acc[kq][f][hb] = mfma_bf16(xa[kq][hb][1], wf[f][1], acc[kq][f][hb]);
+#pragma unroll
+        for (int kq = 0; kq < NKH; ++kq)
 #pragma unroll
             for (int f = 0; f < FPW; ++f) {
                 float ph[2][4];
 #pragma unroll
                 for (int hb = 0; hb < 2; ++hb) {
-                    f32x4 acc = mfma_bf16(xa[hb][0], wf[f][0], zero4);
-                    acc = mfma_bf16(xa[hb][1], wf[f][1], acc);
-                    ph[hb][0] = __builtin_amdgcn_exp2f(fmaf(c1, acc[0], cr[hb].x));
-                    ph[hb][1] = __builtin_amdgcn_exp2f(fmaf(c1, acc[1], cr[hb].y));
-                    ph[hb][2] = __builtin_amdgcn_exp2f(fmaf(c1, acc[2], cr[hb].z));
-                    ph[hb][3] = __builtin_amdgcn_exp2f(fmaf(c1, acc[3], cr[hb].w));
+                    const f32x4 a = acc[kq][f][hb];
+                    ph[hb][0] = __builtin_amdgcn_exp2f(fmaf(c1, a[0], cr[kq][hb].x));
+                    ph[hb][1] = __builtin_amdgcn_exp2f(fmaf(c1, a[1], cr[kq][hb].y));
+                    ph[hb][2] = __builtin_amdgcn_exp2f(fmaf(c1, a[2], cr[kq][hb].z));
+                    ph[hb][3] = __builtin_amdgcn_exp2f(fmaf(c1, a[3], cr[kq][hb].w));
                 }
                 const uint4 hi = pack8(ph[0], ph[1]);
                 const uint4 lo = pack8_lo(ph[0], ph[1], hi);
 #pragma unroll
                 for (int cb = 0; cb < 4; ++cb) {
-                    P[f][cb] = mfma_bf16(as_bf16x8(hi), vb[cb], P[f][cb]);
-                    P[f][cb] = mfma_bf16(as_bf16x8(lo), vb[cb], P[f][cb]);
+                    P[f][cb] = mfma_bf16(as_bf16x8(hi), vb[kq][cb], P[f][cb]);
+                    P[f][cb] = mfma_bf16(as_bf16x8(lo), vb[kq][cb], P[f][cb]);
                 }
                 if constexpr (Z) {
                     Zs[f] = mfma_bf16(as_bf16x8(hi), ones, Zs[f]);
                     Zs[f] = mfma_bf16(as_bf16x8(lo), ones, Zs[f]);
                 }
             }
-        }
         if (t + 1 < t_end) {
             land(t + 1);
             row_consts(t + 1, st[sn], crl[sn]);
