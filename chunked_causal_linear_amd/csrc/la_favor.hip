@@ -27,8 +27,9 @@
 //    phi(Q) z + the row sums of tril(phi(Q) phi(K)^T), then P += phi(K)^T V,
 //    z += the column sums of phi(K).  Eight waves, two per SIMD: mapper
 //    waves map phi(k) and phi(q) of the next chunk (a quarter of the features
-//    each) and keep z, while product waves run the current chunk, each with
-//    the state of 16 value columns over all features in fp32 accumulators.
+//    each), while product waves run the current chunk, each with the state of
+//    16 value columns over all features and z over a quarter of the features
+//    in fp32 accumulators.
 #include "la_fwd_pipe.hpp"
 
 namespace la {
@@ -522,14 +523,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 //    the features in registers and reads the raw q and k rows it needs straight
 //    into registers (one chunk ahead), so the raw q and k never occupy LDS;
 //    phi(k) of chunk t + 1 before BS(t), phi(q) after it.
-// With the normaliser the mapper waves also keep z (the key sums before the
-// chunk they map next) for their features in fp32 registers: they add the
-// column sums of each phi(k) tile they map once the phi(q) tile of the same
-// chunk is mapped, and for each phi(q) tile they put the rows' partial
-// products phi(q_r) . z over their features into LDS; the product waves add
-// the four partials.  phi(k) and these partials are double-buffered by chunk
-// parity; phi(q) is read before BS only, so it has one buffer.  Two barriers
-// per chunk t:
+// With the normaliser each product wave also keeps z for a quarter of the
+// feature steps in fp32 accumulators: z += the column sums of phi(K) comes
+// from the matrix cores with a ones operand on the state update's phi(K)
+// operands, and the rows' partial products phi(q_r) . z over those steps from
+// z as a bf16 hi/lo operand against the inter product's phi(q) operands; the
+// four partials meet in LDS.  phi(k) is double-buffered by chunk parity;
+// phi(q) is read before BS only, so it has one buffer.  Two barriers per chunk t:
 //   B(t):  phi of chunk t is complete (mapped during chunk t - 1), its value
 //          tile has landed, and chunk t - 1's products are done (the other
 //          phi(k) buffer, the score tile and chunk t - 1's stage are free);
@@ -549,7 +549,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     constexpr int FSEG = M / 8, NKS = M / 32, FPW = M / 64;
     constexpr int PHI_E = 64 * M;  // elements of one phi tile
     // as many value stages as the LDS holds beside the rest, at most four
-    constexpr int FIXED = 3 * PHI_E * 2 + 64 * 64 * 2 + 2 * 64 * 4 * 4;
+    // z is kept by the product waves, KPW feature steps each (waves w < NKS / KPW)
+    constexpr int KPW = NKS >= 4 ? NKS / 4 : 1;
+    constexpr int FIXED = 3 * PHI_E * 2 + 64 * 64 * 2 + 64 * 4 * 4;
     constexpr int NVFIT = (160 * 1024 - FIXED) / (64 * 64 * 2);
     constexpr int NV = NVFIT < 4 ? NVFIT : 4;
     static_assert(NV >= 2, "value stages");
@@ -558,8 +560,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __shared__ __attribute__((aligned(16))) u16 fk[2][PHI_E];
     __shared__ __attribute__((aligned(16))) u16 vst[NV][64 * 64];
     __shared__ __attribute__((aligned(16))) u16 stile[64 * 64];
-    // phi(q_r) . z partials: [chunk parity][row r][mapper wave]
-    __shared__ __attribute__((aligned(16))) float qzp[NORM ? 2 * 64 * 4 : 4];
+    // phi(q_r) . z partials: [row r][product wave]
+    __shared__ __attribute__((aligned(16))) float qzp[NORM ? 64 * 4 : 4];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);
@@ -594,20 +596,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         bf16x8 wf[FPW][2];
 #pragma unroll
         for (int f = 0; f < FPW; ++f) load_w_frag(p.W, fb0 + f, lane, wf[f]);
-        // with the normaliser: z before the chunk whose phi(q) is mapped next,
-        // lane (g, l16) keeping features 16 (fb0 + f) + 4g + i, and the column
-        // sums of the phi(k) tile mapped last (added once its chunk's phi(q) is)
-        float zr[FPW][4], zp[FPW][4];
-#pragma unroll
-        for (int f = 0; f < FPW; ++f)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) zr[f][i] = zp[f][i] = 0.f;
-        if constexpr (NORM)
-            if (p.z0 != nullptr && grp > 0)
-#pragma unroll
-                for (int f = 0; f < FPW; ++f)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) zr[f][i] = p.z0[slot * M + 16 * (fb0 + f) + 4 * g + i];
         // x fragments of tile t: rows 16 rb + l16 (clamped to the last row),
         // inputs 32 h + 8g .. + 7
         auto load_x = [&](const u16* base, int64_t t, bf16x8 (&x)[4][2]) __attribute__((always_inline)) {
@@ -624,16 +612,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // (lane (g, l16) holds rows 16 rb + 4g + i against row 16 rb + l16; the
         // diagonal of row r sits in lane (r / 4, r), element r mod 4), then the
         // features fb0 .. fb0 + FPW - 1 of every row (lane (g, l16): features
-        // 16 fb + 4g + i of row 16 rb + l16); key rows at or past `valid` map to
-        // 0.  With the normaliser: for queries the rows' partials phi(q_r) . z
-        // into qz, for keys the column sums into zp.
-        auto map = [&](const bf16x8 (&x)[4][2], u16* phi, int valid, bool is_q, float* qz) __attribute__((always_inline)) {
-            float zs[FPW][4];  // this key tile's column sums, before the sum over the lanes of a row
-            float part[4];     // phi(q_r) . z for r = 16 rb + l16, before the sum over the lane groups
-#pragma unroll
-            for (int f = 0; f < FPW; ++f)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) zs[f][i] = 0.f;
+        // 16 fb + 4g + i of row 16 rb + l16); key rows at or past `valid` map to 0
+        auto map = [&](const bf16x8 (&x)[4][2], u16* phi, int valid) __attribute__((always_inline)) {
             // the row norms of all four row blocks first (their lane exchanges overlap)
             float nrm[4];
             const int e = l16 & 3;
@@ -648,7 +628,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             for (int rb = 0; rb < 4; ++rb) {
                 const int r = 16 * rb + l16;
                 const float cr = r < valid ? fmaf(cA, nrm[rb], cB) : -__builtin_inff();
-                part[rb] = 0.f;
                 // the feature blocks' products as independent chains, then their exponentials
                 f32x4 acc[FPW];
 #pragma unroll
@@ -663,49 +642,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     const float p3 = __builtin_amdgcn_exp2f(fmaf(c1, acc[f][3], cr));
                     const uint2 w2 = make_uint2(pack2_bf16(p0, p1), pack2_bf16(p2, p3));
                     *reinterpret_cast<uint2*>(reinterpret_cast<char*>(phi) + tile_off<FSEG>(r, 16 * (fb0 + f) + 4 * g)) = w2;
-                    if constexpr (NORM) {
-                        const float ev[4] = {p0, p1, p2, p3};
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            if (is_q)
-                                part[rb] = fmaf(ev[i], zr[f][i], part[rb]);
-                            else
-                                zs[f][i] += ev[i];
-                        }
-                    }
                 }
             }
-            if constexpr (NORM) {
-                if (is_q) {
-#pragma unroll
-                    for (int rb = 0; rb < 4; ++rb) part[rb] += __shfl_xor(part[rb], 16);
-#pragma unroll
-                    for (int rb = 0; rb < 4; ++rb) part[rb] += __shfl_xor(part[rb], 32);
-                    if (g == 0)
-#pragma unroll
-                        for (int rb = 0; rb < 4; ++rb) qz[(16 * rb + l16) * 4 + pw] = part[rb];
-                } else {
-#pragma unroll
-                    for (int f = 0; f < FPW; ++f)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) zp[f][i] = sum16(zs[f][i]);
-                }
-            }
-        };
-        auto add_zp = [&]() __attribute__((always_inline)) {
-#pragma unroll
-            for (int f = 0; f < FPW; ++f)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) zr[f][i] += zp[f][i];
         };
         bf16x8 xq[4][2], xk[4][2];
         // prologue: chunk t_begin mapped into buffer 0 (queries need no zeroing:
         // their rows past the end give outputs that are not stored)
         load_x(qh, t_begin, xq);
         load_x(kh, t_begin, xk);
-        map(xq, fq, 64, true, qzp);
-        map(xk, fk[0], valid_of(t_begin), false, nullptr);
-        add_zp();
+        map(xq, fq, 64);
+        map(xk, fk[0], valid_of(t_begin));
         if (t_begin + 1 < t_end) {
             load_x(qh, t_begin + 1, xq);
             load_x(kh, t_begin + 1, xk);
@@ -714,13 +660,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const int b = (int)((t - t_begin) & 1);
             __syncthreads();  // B(t)
             if (t + 1 < t_end) {
-                map(xk, fk[b ^ 1], valid_of(t + 1), false, nullptr);
+                map(xk, fk[b ^ 1], valid_of(t + 1));
                 if (t + 2 < t_end) load_x(kh, t + 2, xk);
             }
             __syncthreads();  // BS(t)
             if (t + 1 < t_end) {
-                map(xq, fq, 64, true, qzp + (b ^ 1) * 256);
-                add_zp();
+                map(xq, fq, 64);
                 if (t + 2 < t_end) load_x(qh, t + 2, xq);
             }
         }
@@ -763,6 +708,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     f32x4 P[NKS][2];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) P[ks][0] = P[ks][1] = zero4;
+    // z at feature steps KPW pw + k2: Zs[k2][hf] lane (g, l16) element i =
+    // z[32 (KPW pw + k2) + 8g + 4hf + i] (every column the same)
+    const bool has_z = NORM && pw < NKS / KPW;
+    f32x4 Zs[KPW][2];
+#pragma unroll
+    for (int k2 = 0; k2 < KPW; ++k2) Zs[k2][0] = Zs[k2][1] = zero4;
     const bool has_prefix = grp > 0;
     if (p.P0 != nullptr && has_prefix) {
         const float* P0 = p.P0 + (slot * M) * (int64_t)dv + col0 + cw + l16;
@@ -773,10 +724,22 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
                 for (int e = 0; e < 4; ++e) P[ks][hf][e] = P0[(int64_t)(32 * ks + 8 * g + 4 * hf + e) * dv];
     }
+    if (has_z && p.z0 != nullptr && has_prefix)
+#pragma unroll
+        for (int k2 = 0; k2 < KPW; ++k2)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) Zs[k2][hf][e] = p.z0[slot * M + 32 * (KPW * pw + k2) + 8 * g + 4 * hf + e];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
         settle(P[ks][0]);
         settle(P[ks][1]);
+    }
+#pragma unroll
+    for (int k2 = 0; k2 < KPW; ++k2) {
+        settle(Zs[k2][0]);
+        settle(Zs[k2][1]);
     }
     // the copies go out after the loads above have been waited for
     for (int s0 = 0; s0 < NV - 1; ++s0)
@@ -820,17 +783,37 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             zero_block<2, 3>(stile, l16, g);
         }
         // the inter product O^T = P^T phi(Q)^T: lane (g, l16) holds output row
-        // 16 ib + l16, columns cw + 4g + e
-        f32x4 O[4], R[4];
+        // 16 ib + l16, columns cw + 4g + e; with the normaliser, at this wave's
+        // feature steps, phi(q_r) . z from the same phi(q) operands (z as a
+        // bf16 hi/lo pair broadcast over the rows of the A operand)
+        f32x4 O[4], R[4], QZ[4];
 #pragma unroll
-        for (int ib = 0; ib < 4; ++ib) O[ib] = R[ib] = zero4;
+        for (int ib = 0; ib < 4; ++ib) O[ib] = R[ib] = QZ[ib] = zero4;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
             const bf16x8 pk = pack_acc_bf16(P[ks][0], P[ks][1]);
+            if (has_z && ks / KPW == pw) {
+                const f32x4& za = Zs[ks % KPW][0];
+                const f32x4& zb = Zs[ks % KPW][1];
+                const float a4[4] = {za[0], za[1], za[2], za[3]}, b4[4] = {zb[0], zb[1], zb[2], zb[3]};
+                const uint4 zh = pack8(a4, b4), zl = pack8_lo(a4, b4, zh);
 #pragma unroll
-            for (int ib = 0; ib < 4; ++ib) O[ib] = mfma_bf16(pk, row_at(q_, raf.off(16 * ib, 32 * ks)), O[ib]);
+                for (int ib = 0; ib < 4; ++ib) {
+                    const bf16x8 qf = row_at(q_, raf.off(16 * ib, 32 * ks));
+                    O[ib] = mfma_bf16(pk, qf, O[ib]);
+                    QZ[ib] = mfma_bf16(as_bf16x8(zh), qf, QZ[ib]);
+                    QZ[ib] = mfma_bf16(as_bf16x8(zl), qf, QZ[ib]);
+                }
+            } else {
+#pragma unroll
+                for (int ib = 0; ib < 4; ++ib) O[ib] = mfma_bf16(pk, row_at(q_, raf.off(16 * ib, 32 * ks)), O[ib]);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
+        if constexpr (NORM)
+            if (g == 0)
+#pragma unroll
+                for (int ib = 0; ib < 4; ++ib) qzp[(16 * ib + l16) * 4 + pw] = QZ[ib][0];
         __syncthreads();  // BS(t)
         {
             bf16x8 vb[2];
@@ -844,27 +827,39 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     O[ib] = mfma_bf16(vb[kk], sb, O[ib]);
                     if constexpr (NORM) R[ib] = mfma_bf16(ones, sb, R[ib]);
                 }
-            // the output rows (normalised by phi(q_r) . z, the mapper waves'
+            // the output rows (normalised by phi(q_r) . z, the product waves'
             // four partials, + the row's score sum) into this wave's own V columns
 #pragma unroll
             for (int ib = 0; ib < 4; ++ib) {
                 const int r = 16 * ib + l16;
                 float rd = 1.f;
                 if constexpr (NORM) {
-                    const float4 qq = *reinterpret_cast<const float4*>(qzp + (b * 64 + r) * 4);
+                    const float4 qq = *reinterpret_cast<const float4*>(qzp + r * 4);
                     rd = __builtin_amdgcn_rcpf((qq.x + qq.y) + (qq.z + qq.w) + R[ib][0]);
                 }
                 *reinterpret_cast<uint2*>(reinterpret_cast<char*>(v_) + tile_off<8>(r, cw + 4 * g)) =
                     make_uint2(pack2_bf16(O[ib][0] * rd, O[ib][1] * rd), pack2_bf16(O[ib][2] * rd, O[ib][3] * rd));
             }
-            // P += phi(K)^T V
+            // P += phi(K)^T V, and at this wave's feature steps z += the column
+            // sums of phi(K) from the same operands
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
+                if (has_z && ks / KPW == pw) {
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk)
+                    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-                    for (int hf = 0; hf < 2; ++hf)
-                        P[ks][hf] = mfma_bf16(col_at(k_, caf, 32 * kk, 32 * ks, hf), vb[kk], P[ks][hf]);
+                        for (int hf = 0; hf < 2; ++hf) {
+                            const bf16x8 a = col_at(k_, caf, 32 * kk, 32 * ks, hf);
+                            P[ks][hf] = mfma_bf16(a, vb[kk], P[ks][hf]);
+                            Zs[ks % KPW][hf] = mfma_bf16(a, ones, Zs[ks % KPW][hf]);
+                        }
+                } else {
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                        for (int hf = 0; hf < 2; ++hf)
+                            P[ks][hf] = mfma_bf16(col_at(k_, caf, 32 * kk, 32 * ks, hf), vb[kk], P[ks][hf]);
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
