@@ -119,22 +119,38 @@ __device__ __forceinline__ void wait_groups(int after) {
     wait_vm<0>();
 }
 
-// Lane base addresses for the swizzled tiles (tile_off: segment index XOR
-// row).  For a 16-byte row read of row R0 + l16 at elements K0 + 8g .. (R0 a
-// multiple of 16, K0 of 32) the segment index is ((4 ks + g) ^ (R0 + l16)) mod
-// NSEG with ks = K0 / 32: its low four bits depend on the lane and on ks mod 4
-// only, its higher bits on R0 and ks only.  So four lane registers (one per
-// ks mod 4) and a compile-time immediate give every such address, with no
-// per-access arithmetic.
-template <int NSEG>
+// The phi tiles' swizzle: the 16-byte segment index XOR a row key, the row
+// itself (pipe::tile_off), or with SWAP the row with its two low bit pairs
+// exchanged.  Measured on the LDS conflict counters at 16 and 32 segments per
+// row: with the plain key the 16-byte row reads run conflict-free (4 LDS
+// cycles each) and the transposed 8-byte column reads take 8; with the
+// exchanged key the column reads take 4 and the row reads 8.  phi(k), read
+// mostly by columns (the state update), takes the exchanged key there; phi(q)
+// and every tile of 8 segments the plain one (both reads conflict-free).
+template <bool SWAP>
+__device__ __forceinline__ int row_key(int r) {
+    return SWAP ? (((r & 3) << 2) | ((r >> 2) & 3) | (r & ~15)) : r;
+}
+template <int NSEG, bool SWAP>
+__device__ __forceinline__ int phi_off(int r, int e) {
+    return r * NSEG * 16 + ((((e >> 3) ^ row_key<SWAP>(r)) & (NSEG - 1)) << 4) + ((e & 7) << 1);
+}
+
+// Lane base addresses for the swizzled tiles.  For a 16-byte row read of row
+// R0 + l16 at elements K0 + 8g .. (R0 a multiple of 16, K0 of 32) the segment
+// index is ((4 ks + g) ^ key(R0 + l16)) mod NSEG with ks = K0 / 32: its low
+// four bits depend on the lane and on ks mod 4 only, its higher bits on R0
+// and ks only.  So four lane registers (one per ks mod 4) and a compile-time
+// immediate give every such address, with no per-access arithmetic.
+template <int NSEG, bool SWAP = false>
 struct RowAddr {
     int b[4];
     __device__ __forceinline__ explicit RowAddr(int lane) {
-        const int l16 = lane & 15, g = lane >> 4, B = g ^ l16;
+        const int l16 = lane & 15, g = lane >> 4, B = g ^ row_key<SWAP>(l16);
 #pragma unroll
         for (int c = 0; c < 4; ++c) b[c] = l16 * NSEG * 16 + (((4 * c) ^ B) & (NSEG - 1)) * 16;
     }
-    // byte offset of pipe::tile_off<NSEG>(R0 + l16, K0 + 8g)
+    // byte offset of phi_off<NSEG, SWAP>(R0 + l16, K0 + 8g)
     __device__ __forceinline__ int off(int R0, int K0) const {
         const int ks = K0 / 32;
         return b[ks & 3] + R0 * NSEG * 16 + ((((4 * ks) ^ R0) & ~15) & (NSEG - 1)) * 16;
@@ -144,52 +160,18 @@ struct RowAddr {
 // The same for the transposed 8-byte reads of a column operand: rows K0 + H +
 // 4g + rr (K0 a multiple of 32, H 0 or 16, rr = (l % 16) / 4) at columns CB +
 // 8c + 4hf (CB a multiple of 32, c = l % 4).
-template <int NSEG>
+template <int NSEG, bool SWAP = false>
 struct ColAddr {
     int b[4];
     __device__ __forceinline__ explicit ColAddr(int lane) {
-        const int g = lane >> 4, rr = (lane & 15) >> 2, c = lane & 3, rl = 4 * g + rr, B = c ^ rl;
+        const int g = lane >> 4, rr = (lane & 15) >> 2, c = lane & 3, rl = 4 * g + rr, B = c ^ row_key<SWAP>(rl);
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) b[cc] = rl * NSEG * 16 + (((4 * cc) ^ B) & (NSEG - 1)) * 16;
     }
-    // byte offset of pipe::tile_off<NSEG>(K0 + H + 4g + rr, CB + 8c + 4hf)
+    // byte offset of phi_off<NSEG, SWAP>(K0 + H + 4g + rr, CB + 8c + 4hf)
     __device__ __forceinline__ int off(int K0, int H, int CB, int hf) const {
         const int ks = CB / 32;
         return b[ks & 3] + (K0 + H) * NSEG * 16 + ((((4 * ks) ^ (K0 + H)) & ~15) & (NSEG - 1)) * 16 + 8 * hf;
-    }
-};
-
-// The same two with the feature steps ks = ks0 + c (c = 0..3) of a run that
-// starts at a wave-uniform ks0, a multiple of 4 when NSEG = 32 (bit 4 of the
-// segment index then depends on ks0 and the row's 16-block parity only).
-template <int NSEG>
-struct RowAddrK {
-    int b[4];
-    int h[2];
-    __device__ __forceinline__ RowAddrK(int lane, int ks0) {
-        const int l16 = lane & 15, g = lane >> 4, B = g ^ l16;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) b[c] = l16 * NSEG * 16 + (((4 * ((ks0 + c) & 3)) ^ B) & (NSEG - 1)) * 16;
-#pragma unroll
-        for (int par = 0; par < 2; ++par) h[par] = NSEG == 32 ? 256 * (((ks0 >> 2) & 1) ^ par) : 0;
-    }
-    // byte offset of pipe::tile_off<NSEG>(R0 + l16, 32 (ks0 + c) + 8g), R0 a multiple of 16
-    __device__ __forceinline__ int off(int R0, int c) const { return b[c] + R0 * NSEG * 16 + h[(R0 >> 4) & 1]; }
-};
-template <int NSEG>
-struct ColAddrK {
-    int b[4];
-    int h[2];
-    __device__ __forceinline__ ColAddrK(int lane, int ks0) {
-        const int g = lane >> 4, rr = (lane & 15) >> 2, cl = lane & 3, rl = 4 * g + rr, B = cl ^ rl;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) b[c] = rl * NSEG * 16 + (((4 * ((ks0 + c) & 3)) ^ B) & (NSEG - 1)) * 16;
-#pragma unroll
-        for (int par = 0; par < 2; ++par) h[par] = NSEG == 32 ? 256 * (((ks0 >> 2) & 1) ^ par) : 0;
-    }
-    // byte offset of pipe::tile_off<NSEG>(K0 + H + 4g + rr, 32 (ks0 + c) + 8 cl + 4hf), K0 a multiple of 32, H 0 or 16
-    __device__ __forceinline__ int off(int K0, int H, int c, int hf) const {
-        return b[c] + (K0 + H) * NSEG * 16 + h[H >> 4] + 8 * hf;
     }
 };
 
@@ -197,15 +179,8 @@ __device__ __forceinline__ bf16x8 row_at(const u16* tile, int off) {
     return as_bf16x8(*reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(tile) + off));
 }
 // the column operand (keys K0 .. K0 + 31 in operand order) from its two transposed reads
-template <int NSEG>
-__device__ __forceinline__ bf16x8 col_at_k(const u16* tile, const ColAddrK<NSEG>& ca, int K0, int c, int hf) {
-    const char* t = reinterpret_cast<const char*>(tile);
-    const uint2 lo = pipe::tr_read(t + ca.off(K0, 0, c, hf));
-    const uint2 hi = pipe::tr_read(t + ca.off(K0, 16, c, hf));
-    return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-}
-template <int NSEG>
-__device__ __forceinline__ bf16x8 col_at(const u16* tile, const ColAddr<NSEG>& ca, int K0, int CB, int hf) {
+template <int NSEG, bool SWAP>
+__device__ __forceinline__ bf16x8 col_at(const u16* tile, const ColAddr<NSEG, SWAP>& ca, int K0, int CB, int hf) {
     const char* t = reinterpret_cast<const char*>(tile);
     const uint2 lo = pipe::tr_read(t + ca.off(K0, 0, CB, hf));
     const uint2 hi = pipe::tr_read(t + ca.off(K0, 16, CB, hf));
@@ -239,9 +214,9 @@ __device__ __forceinline__ float sum16(float v) {
 // of query row 16 I + l16) over all feature steps and stored, masked, in bf16
 // into the score tile (columns in operand key order).  Blocks that share a
 // query or key block read its fragments once.
-template <int FSEG, int NKS, int I0, int J0, int I1, int J1, int I2, int J2>
-__device__ __forceinline__ void score_blocks(const u16* q_, const u16* k_, u16* stile, const RowAddr<FSEG>& raf,
-                                             int l16, int g) {
+template <int FSEG, int NKS, bool SWK, int I0, int J0, int I1, int J1, int I2, int J2>
+__device__ __forceinline__ void score_blocks(const u16* q_, const u16* k_, u16* stile, const RowAddr<FSEG>& raq,
+                                             const RowAddr<FSEG, SWK>& rak, int l16, int g) {
     using namespace pipe;
     constexpr int NB = I2 >= 0 ? 3 : 2;
     constexpr int I[3] = {I0, I1, I2 >= 0 ? I2 : 0}, J[3] = {J0, J1, I2 >= 0 ? J2 : 0};
@@ -255,8 +230,8 @@ __device__ __forceinline__ void score_blocks(const u16* q_, const u16* k_, u16* 
         for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int n = 0; n < NB; ++n)
-                acc[n][h] = mfma_bf16(row_at(k_, raf.off(16 * J[n], 32 * (ks + h))),
-                                      row_at(q_, raf.off(16 * I[n], 32 * (ks + h))), acc[n][h]);
+                acc[n][h] = mfma_bf16(row_at(k_, rak.off(16 * J[n], 32 * (ks + h))),
+                                      row_at(q_, raq.off(16 * I[n], 32 * (ks + h))), acc[n][h]);
 #pragma unroll
     for (int n = 0; n < NB; ++n) {
         const f32x4 s = acc[n][0] + acc[n][1];
@@ -547,6 +522,7 @@ template <int M, bool NORM>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void favor_fwd_kernel(FavorParams p) {
     using namespace pipe;
     constexpr int FSEG = M / 8, NKS = M / 32, FPW = M / 64;
+    constexpr bool SWK = FSEG >= 16;  // phi(k)'s swizzle key (phi_off)
     constexpr int PHI_E = 64 * M;  // elements of one phi tile
     // as many value stages as the LDS holds beside the rest, at most four
     // z is kept by the product waves, KPW feature steps each (waves w < NKS / KPW)
@@ -613,7 +589,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // diagonal of row r sits in lane (r / 4, r), element r mod 4), then the
         // features fb0 .. fb0 + FPW - 1 of every row (lane (g, l16): features
         // 16 fb + 4g + i of row 16 rb + l16); key rows at or past `valid` map to 0
-        auto map = [&](const bf16x8 (&x)[4][2], u16* phi, int valid) __attribute__((always_inline)) {
+        auto map = [&](const bf16x8 (&x)[4][2], u16* phi, int valid, auto swap) __attribute__((always_inline)) {
+            constexpr bool SW = decltype(swap)::value;
             // the row norms of all four row blocks first (their lane exchanges overlap)
             float nrm[4];
             const int e = l16 & 3;
@@ -641,7 +618,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     const float p2 = __builtin_amdgcn_exp2f(fmaf(c1, acc[f][2], cr));
                     const float p3 = __builtin_amdgcn_exp2f(fmaf(c1, acc[f][3], cr));
                     const uint2 w2 = make_uint2(pack2_bf16(p0, p1), pack2_bf16(p2, p3));
-                    *reinterpret_cast<uint2*>(reinterpret_cast<char*>(phi) + tile_off<FSEG>(r, 16 * (fb0 + f) + 4 * g)) = w2;
+                    *reinterpret_cast<uint2*>(reinterpret_cast<char*>(phi) + phi_off<FSEG, SW>(r, 16 * (fb0 + f) + 4 * g)) = w2;
                 }
             }
         };
@@ -650,8 +627,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // their rows past the end give outputs that are not stored)
         load_x(qh, t_begin, xq);
         load_x(kh, t_begin, xk);
-        map(xq, fq, 64);
-        map(xk, fk[0], valid_of(t_begin));
+        map(xq, fq, 64, std::false_type{});
+        map(xk, fk[0], valid_of(t_begin), std::integral_constant<bool, SWK>{});
         if (t_begin + 1 < t_end) {
             load_x(qh, t_begin + 1, xq);
             load_x(kh, t_begin + 1, xk);
@@ -660,12 +637,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const int b = (int)((t - t_begin) & 1);
             __syncthreads();  // B(t)
             if (t + 1 < t_end) {
-                map(xk, fk[b ^ 1], valid_of(t + 1));
+                map(xk, fk[b ^ 1], valid_of(t + 1), std::integral_constant<bool, SWK>{});
                 if (t + 2 < t_end) load_x(kh, t + 2, xk);
             }
             __syncthreads();  // BS(t)
             if (t + 1 < t_end) {
-                map(xq, fq, 64);
+                map(xq, fq, 64, std::false_type{});
                 if (t + 2 < t_end) load_x(qh, t + 2, xq);
             }
         }
@@ -746,8 +723,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         if (t_begin + s0 < t_end) issue(t_begin + s0, vst[s0]);
     land(t_begin);
     const RowAddr<FSEG> raf(lane);
+    const RowAddr<FSEG, SWK> rak(lane);
     const RowAddr<8> ra8(lane);
-    const ColAddr<FSEG> caf(lane);
+    const ColAddr<FSEG, SWK> caf(lane);
 
     u32x4 ob[2];  // chunk t - 1's output rows, stored once tile t + 1 has landed
     int si = 0;   // value stage of chunk t
@@ -772,14 +750,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // groups share query or key blocks), and zeros in blocks (0, 1) and
         // (2, 3), which the 32-key operands of the intra product also read
         if (pw == 0) {
-            score_blocks<FSEG, NKS, 0, 0, 1, 0, 1, 1>(q_, k_, stile, raf, l16, g);
+            score_blocks<FSEG, NKS, SWK, 0, 0, 1, 0, 1, 1>(q_, k_, stile, raf, rak, l16, g);
             zero_block<0, 1>(stile, l16, g);
         } else if (pw == 1) {
-            score_blocks<FSEG, NKS, 2, 0, 2, 1, 3, 0>(q_, k_, stile, raf, l16, g);
+            score_blocks<FSEG, NKS, SWK, 2, 0, 2, 1, 3, 0>(q_, k_, stile, raf, rak, l16, g);
         } else if (pw == 2) {
-            score_blocks<FSEG, NKS, 2, 2, 3, 2, -1, -1>(q_, k_, stile, raf, l16, g);
+            score_blocks<FSEG, NKS, SWK, 2, 2, 3, 2, -1, -1>(q_, k_, stile, raf, rak, l16, g);
         } else {
-            score_blocks<FSEG, NKS, 3, 1, 3, 3, -1, -1>(q_, k_, stile, raf, l16, g);
+            score_blocks<FSEG, NKS, SWK, 3, 1, 3, 3, -1, -1>(q_, k_, stile, raf, rak, l16, g);
             zero_block<2, 3>(stile, l16, g);
         }
         // the inter product O^T = P^T phi(Q)^T: lane (g, l16) holds output row
