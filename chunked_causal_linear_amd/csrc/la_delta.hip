@@ -12,9 +12,10 @@
 //  * delta_transform_kernel: per chunk of 64 rows, T = (I + A)^-1 diag(beta)
 //    with A[i][j] = beta_i (k_i . k_j) g_i / g_j for j < i (g_i the product of
 //    the chunk's gates up to row i): K K^T on the matrix cores, the unit
-//    lower-triangular inverse by forward substitution in fp32 (lane c owns
-//    column c), stored as bf16 with its columns in the matrix-core operand
-//    order of delta_fwd_kernel; also log2 g per row;
+//    lower-triangular inverse blockwise in fp32 (the four 16 x 16 diagonal
+//    blocks by forward substitution, the blocks below them on the fp32 matrix
+//    cores), stored as bf16 with its columns in the matrix-core operand order
+//    of delta_fwd_kernel; also log2 g per row;
 //  * delta_fwd_kernel: the chunks of one head in order, carrying the state
 //    (state waves) beside waves that move the data and form the score tile.
 //    Per chunk (P the state before it, n = 64 rows):
@@ -164,30 +165,29 @@ hipError_t run_delta_step(const DeltaStepParams& p, hipStream_t s) {
 // ---------------------------------------------------------------------------
 // chunk transform: one wave per chunk of 64 rows
 // ---------------------------------------------------------------------------
-// A's strictly lower rows packed in LDS, each padded to whole float4s: row i
-// (i entries) starts at float4 a_row(i) = sum over r < i of ceil(r / 4); with
-// i = 4q + t that is 2q^2 + q, plus q + (t - 1)(q + 1) when t > 0 (528 float4s
-// in all).  Closed form, so a lane-dependent row costs no loop.
-__host__ __device__ constexpr int a_row(int i) {
-    const int q = i / 4, t = i % 4;
-    return 2 * q * q + q + (t > 0 ? q + (t - 1) * (q + 1) : 0);
+// A in 16 x 16 blocks (ib, jb), jb <= ib (index ib (ib + 1) / 2 + jb), rows
+// of 20 floats: a lane's 16-byte slice of row l16 at columns 4g .. 4g + 3 and
+// the element writes of a column both meet distinct banks.
+constexpr int TB_ROW = 20, TB_BLK = 16 * TB_ROW;
+__device__ __forceinline__ constexpr int tblk(int ib, int jb) { return (ib * (ib + 1) / 2 + jb) * TB_BLK; }
+
+// acc += X Y for 16 x 16 blocks on the fp32 matrix cores (four 16x16x4 steps):
+// `a` is the lane's slice X[l16][4g .. 4g + 3], `b` Y in the accumulator
+// layout (lane (g, l16) element i = Y[4g + i][l16]); step i multiplies column
+// 4g + i of X by row 4g + i of Y, each lane group g supplying its k index.
+__device__ __forceinline__ f32x4 mm16(const float4& a, const f32x4& b, f32x4 acc) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, b[0], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, b[1], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, b[2], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, b[3], acc, 0, 0, 0);
+    return acc;
 }
-constexpr int a_row_sum(int i) {
-    int n = 0;
-    for (int r = 0; r < i; ++r) n += (r + 3) / 4;
-    return n;
-}
-constexpr bool a_row_ok() {
-    for (int i = 0; i <= 64; ++i)
-        if (a_row(i) != a_row_sum(i)) return false;
-    return true;
-}
-static_assert(a_row_ok() && a_row(64) == 528, "packed rows");
 
 template <int DK>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void delta_transform_kernel(DeltaPrepParams p) {
     constexpr int NKA = DK / 32;
-    __shared__ float4 A4[a_row(64)];
+    __shared__ __attribute__((aligned(16))) float Ab[10 * TB_BLK];
+    __shared__ __attribute__((aligned(16))) float lgs[64], bes[64];
 
     const int lane = threadIdx.x, l16 = lane % 16, g = lane / 16;
     const int64_t chunk = blockIdx.x;  // bh * N + n
@@ -230,68 +230,119 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void de
     p.lg[chunk * 64 + lane] = lg;
     const float beta = lane < valid ? p.beta[bh * L + r0 + lane] : 0.f;
 
-    // A[i][j] = beta_i g_i / g_j (k_i . k_j) for j < i into the packed rows; the
-    // padding of each row (i <= j < 4 ceil(i / 4)) is written as zero
-    float* A = reinterpret_cast<float*>(A4);
+    lgs[lane] = lg;
+    bes[lane] = beta;
+    __syncthreads();
+
+    // A[i][j] = beta_i g_i / g_j (k_i . k_j) for j < i, 0 on and above the
+    // diagonal, into its blocks (lane (g, l16): rows 16 ib + 4g + e, column 16 jb + l16)
 #pragma unroll
-    for (int ib = 0; ib < 4; ++ib)
+    for (int ib = 0; ib < 4; ++ib) {
+        const float4 lgi = *reinterpret_cast<const float4*>(&lgs[16 * ib + 4 * g]);
+        const float4 bi = *reinterpret_cast<const float4*>(&bes[16 * ib + 4 * g]);
+        const float lgi4[4] = {lgi.x, lgi.y, lgi.z, lgi.w}, bi4[4] = {bi.x, bi.y, bi.z, bi.w};
 #pragma unroll
         for (int jb = 0; jb <= ib; ++jb) {
             const int j = 16 * jb + l16;
-            const float lgj = __shfl(lg, j);
+            const float lgj = lgs[j];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = 16 * ib + 4 * g + e;
-                const float bi = __shfl(beta, i), lgi = __shfl(lg, i);
-                if (j < (i + 3) / 4 * 4)
-                    A[a_row(i) * 4 + j] =
-                        j < i ? bi * __builtin_amdgcn_exp2f(lgi - lgj) * acc[ib * (ib + 1) / 2 + jb][e] : 0.f;
+                Ab[tblk(ib, jb) + (4 * g + e) * TB_ROW + l16] =
+                    j < i ? bi4[e] * __builtin_amdgcn_exp2f(lgi4[e] - lgj) * acc[ib * (ib + 1) / 2 + jb][e] : 0.f;
             }
-        }
-    __syncthreads();
-
-    // forward substitution, column c = lane of X = (I + A)^-1:
-    // x_i = [i == c] - sum_{j < i} A[i][j] x_j, four rows at a time (sixteen
-    // independent sums against the columns already solved, then the 4 x 4
-    // triangle of the four rows)
-    float x[64];
-#pragma unroll
-    for (int i = 0; i < 64; ++i) x[i] = 0.f;
-#pragma unroll
-    for (int i0 = 0; i0 < 64; i0 += 4) {
-        float sacc[4][4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int c = 0; c < 4; ++c) sacc[r][c] = 0.f;
-#pragma unroll
-        for (int j4 = 0; j4 < i0 / 4; ++j4)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float4 a = A4[a_row(i0 + r) + j4];
-                sacc[r][0] = fmaf(a.x, x[4 * j4], sacc[r][0]);
-                sacc[r][1] = fmaf(a.y, x[4 * j4 + 1], sacc[r][1]);
-                sacc[r][2] = fmaf(a.z, x[4 * j4 + 2], sacc[r][2]);
-                sacc[r][3] = fmaf(a.w, x[4 * j4 + 3], sacc[r][3]);
-            }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int i = i0 + r;
-            float xi = (i == lane ? 1.f : 0.f) - ((sacc[r][0] + sacc[r][1]) + (sacc[r][2] + sacc[r][3]));
-            if (r > 0) {
-                const float4 a = A4[a_row(i) + i0 / 4];  // A[i][i0 .. i0 + 3]; entries from i on are zero
-                const float at[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-                for (int t = 0; t < r; ++t) xi = fmaf(-at[t], x[i0 + t], xi);
-            }
-            x[i] = xi;
         }
     }
-    // T = X diag(beta): lane c writes column c of every row, at its permuted
-    // position (each store covers one whole 128-byte row)
-    u16* T = p.T + chunk * 64 * 64 + pipe::perm_pos(lane);
+    __syncthreads();
+
+    // The diagonal blocks' inverses X_bb = (I + A_bb)^-1 by forward
+    // substitution, lane (b = g, c = l16) solving for column c of block b:
+    // x_i = [i == c] - sum_{j < i} A_bb[i][j] x_j (A_bb's entries from i on are zero).
+    float x[16];
 #pragma unroll
-    for (int i = 0; i < 64; ++i) T[i * 64] = f2bf(x[i] * beta);
+    for (int i = 0; i < 16; ++i) x[i] = 0.f;
+    {
+        const float* Abb = Ab + tblk(g, g);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float sacc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j4 = 0; j4 < (i + 3) / 4; ++j4) {
+                const float4 a = *reinterpret_cast<const float4*>(Abb + i * TB_ROW + 4 * j4);
+                sacc[0] = fmaf(a.x, x[4 * j4], sacc[0]);
+                sacc[1] = fmaf(a.y, x[4 * j4 + 1], sacc[1]);
+                sacc[2] = fmaf(a.z, x[4 * j4 + 2], sacc[2]);
+                sacc[3] = fmaf(a.w, x[4 * j4 + 3], sacc[3]);
+            }
+            x[i] = (i == l16 ? 1.f : 0.f) - ((sacc[0] + sacc[1]) + (sacc[2] + sacc[3]));
+        }
+    }
+    __syncthreads();  // every lane has read its A_bb
+    // X_bb in place of A_bb
+#pragma unroll
+    for (int i = 0; i < 16; ++i) Ab[tblk(g, g) + i * TB_ROW + l16] = x[i];
+    __syncthreads();
+
+    // The blocks below the diagonal, by distance from it:
+    //   X_ij = -X_ii Y_ij,  Y_ij = sum_{k = j .. i - 1} A_ik X_kj.
+    auto slice = [&](int blk) __attribute__((always_inline)) {  // X[l16][4g .. 4g + 3] of a block
+        return *reinterpret_cast<const float4*>(Ab + blk + l16 * TB_ROW + 4 * g);
+    };
+    auto dlay = [&](int blk) __attribute__((always_inline)) {  // a block in the accumulator layout
+        f32x4 r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = Ab[blk + (4 * g + e) * TB_ROW + l16];
+        return r;
+    };
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+    // one distance at a time, each stage's operands loaded where it starts
+    const f32x4 X00 = dlay(tblk(0, 0));
+    f32x4 X10, X21, X32, X20, X31, X30;
+    {
+        const f32x4 X11 = dlay(tblk(1, 1)), X22 = dlay(tblk(2, 2));
+        X10 = -mm16(slice(tblk(1, 1)), mm16(slice(tblk(1, 0)), X00, z4), z4);
+        X21 = -mm16(slice(tblk(2, 2)), mm16(slice(tblk(2, 1)), X11, z4), z4);
+        X32 = -mm16(slice(tblk(3, 3)), mm16(slice(tblk(3, 2)), X22, z4), z4);
+        __builtin_amdgcn_sched_barrier(0);
+        X20 = -mm16(slice(tblk(2, 2)), mm16(slice(tblk(2, 1)), X10, mm16(slice(tblk(2, 0)), X00, z4)), z4);
+        X31 = -mm16(slice(tblk(3, 3)), mm16(slice(tblk(3, 2)), X21, mm16(slice(tblk(3, 1)), X11, z4)), z4);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    X30 = -mm16(slice(tblk(3, 3)),
+                mm16(slice(tblk(3, 2)), X20, mm16(slice(tblk(3, 1)), X10, mm16(slice(tblk(3, 0)), X00, z4))), z4);
+    // this lane's column of its diagonal block, for T
+    float xd[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) xd[i] = Ab[tblk(g, g) + i * TB_ROW + l16];
+    __syncthreads();  // A and X_bb are read: the blocks' area takes T
+
+    // T = X diag(beta) in bf16 into LDS (row i, column j at its permuted
+    // position), then out in whole rows of 16-byte pieces
+    u16* Ts = reinterpret_cast<u16*>(Ab);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) reinterpret_cast<uint4*>(Ts)[k * 64 + lane] = make_uint4(0, 0, 0, 0);
+    __syncthreads();
+    {
+        const float bc = bes[16 * g + l16];  // diagonal block g, column 16 g + l16
+#pragma unroll
+        for (int i = 0; i < 16; ++i) Ts[(16 * g + i) * 64 + pipe::perm_pos(16 * g + l16)] = f2bf(xd[i] * bc);
+    }
+    auto put = [&](int ib, int jb, const f32x4& X) __attribute__((always_inline)) {
+        const int j = 16 * jb + l16;
+        const float bj = bes[j];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Ts[(16 * ib + 4 * g + e) * 64 + pipe::perm_pos(j)] = f2bf(X[e] * bj);
+    };
+    put(1, 0, X10);
+    put(2, 1, X21);
+    put(3, 2, X32);
+    put(2, 0, X20);
+    put(3, 1, X31);
+    put(3, 0, X30);
+    __syncthreads();
+    uint4* T = reinterpret_cast<uint4*>(p.T + chunk * 64 * 64);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) T[k * 64 + lane] = reinterpret_cast<const uint4*>(Ts)[k * 64 + lane];
 }
 
 template <int DK>
