@@ -271,7 +271,14 @@ __global__ __launch_bounds__(4 * WAVE) __attribute__((amdgpu_waves_per_eu(1, 1))
 void chunked_fwd_pipe(FwdParams p) {
     using namespace pipe;
     constexpr int TT = CH > 64 ? CH : 64;          // rows per tile
-    constexpr int NFIT = (int)(160 * 1024 / sizeof(Stage<DK, DVT, TT>));
+    // chunks of 128 rows without the decay: the two compute waves split the
+    // tile's score blocks and exchange them (20 operand fragments of 1 KB)
+    // through its Q slot, the fragments past the slot's end through XF more
+    // KB of their own (two more barriers per tile, SYNC1 and SYNC2)
+    constexpr bool SHARE = CH == 128 && DECAY == DECAY_NONE;
+    constexpr int QF = SHARE ? (TT * DK * 2 / 1024 < 20 ? TT * DK * 2 / 1024 : 20) : 0;  // fragments in the Q slot
+    constexpr int XF = SHARE ? 20 - QF : 0;
+    constexpr int NFIT = (int)((160 * 1024 - XF * 1024) / sizeof(Stage<DK, DVT, TT>));
     constexpr int NSTAGE = NFIT < 4 ? NFIT : 4;    // LDS stages
     constexpr int CPW = DVT / 32;                  // 16-column blocks per pair
     constexpr int NCB = CPW + (NORM ? 1 : 0);      // + the denominator block
@@ -287,10 +294,11 @@ void chunked_fwd_pipe(FwdParams p) {
     static_assert(DK == 64 || DK == 128 || DK == 256, "feature width 64, 128 or 256");
     static_assert(NSTAGE >= 2, "two stages at least");
     static_assert((NSTAGE - 2) * NL + NCQ + NCV < 64, "vmcnt range");
-    static_assert(NSTAGE * (int)sizeof(Stage<DK, DVT, TT>) <= 160 * 1024, "LDS");
+    static_assert(NSTAGE * (int)sizeof(Stage<DK, DVT, TT>) + XF * 1024 <= 160 * 1024, "LDS");
     typedef Stage<DK, DVT, TT> StageT;
 
     __shared__ StageT st[NSTAGE];
+    __shared__ __attribute__((aligned(16))) char xfrag[XF > 0 ? XF * 1024 : 16];
 
     const int tid = threadIdx.x;
     const int wave = tid / WAVE, lane = tid % WAVE, l16 = lane % 16, g = lane / 16;
@@ -340,7 +348,7 @@ void chunked_fwd_pipe(FwdParams p) {
     // leave them less time, and an eighth with the decay, whose products leave
     // them the least (the shares that measured fastest).
     constexpr int NP = 2 * NCQ;
-    constexpr int NPC = DECAY ? NP / 8 : (TT > 64 ? NP / 4 : NP / 2), NPK = NP - NPC;
+    constexpr int NPC = DECAY ? NP / 8 : (TT > 64 && !SHARE ? NP / 4 : NP / 2), NPK = NP - NPC;
     constexpr bool MAP2 = PHI && NPC > 0;  // the compute waves map too
     static_assert(!PHI || piece_shares_ok<NCQ, NP, NPK>(),
                   "elu+1 shares: a copy wave maps only pieces it copied before the barrier; every piece once");
@@ -503,6 +511,10 @@ void chunked_fwd_pipe(FwdParams p) {
             if (t > t_begin) read_out(st[sp], ob);
             if (t + NSTAGE - 1 < t_end) issue(t + NSTAGE - 1, st[sp]);
             if constexpr (MAP2) __syncthreads();  // B'(t): the compute waves have mapped their share of tile t
+            if constexpr (SHARE) {
+                __syncthreads();  // SYNC1(t): the compute waves have read Q
+                __syncthreads();  // SYNC2(t): the score operands are in the Q slot
+            }
             // tile t + 1 must have landed (and this wave's share of it been
             // mapped) before B(t + 1); the newest tile issued is now
             // t + NSTAGE - 1 (or the last one)
@@ -1044,6 +1056,149 @@ void chunked_fwd_pipe(FwdParams p) {
                 O[c][3] = mfma_bf16(vb[c][1], s3, O[c][3]);
             }
             write_out(s, ic<0>{}, O, one4);
+        } else if constexpr (SHARE) {
+            // one chunk of 128 rows per tile (windows A = rows 0..63 and B =
+            // rows 64..127, B also against the full block of A's keys), the 36
+            // score blocks split between the two compute waves: wave 0 takes
+            // window A and the cross block's keys 0..31, wave 1 window B and
+            // the cross keys 32..63 (18 blocks each).  Each packs its blocks
+            // into the intra product's operands (ten per wave, 1 KB each,
+            // lane-major) and, once both waves are done with Q, puts them into
+            // the Q slot (and xfrag) for the other wave: fragment f at byte
+            // 1024 f + 16 lane,
+            // f = 0..5 window A (query block qb, key step kk <= qb / 2 in order),
+            // 6..11 window B, 12..15 cross keys 0..31 (query block 4 + qb),
+            // 16..19 cross keys 32..63.
+            f32x4 Oa[NCB][4], Ob[NCB][4];
+            zero_o(Oa);
+            zero_o(Ob);
+            bf16x8 fr[10];
+            auto pack_window = [&](const f32x4 (&S)[10]) __attribute__((always_inline)) {
+                int f = 0;
+#pragma unroll
+                for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+                    for (int kk = 0; kk <= qb / 2; ++kk) {
+                        const f32x4 s1 = 2 * kk + 1 <= qb ? S[qb * (qb + 1) / 2 + 2 * kk + 1] : zero4;
+                        fr[f++] = pack_acc_bf16(S[qb * (qb + 1) / 2 + 2 * kk], s1);
+                    }
+            };
+            // the cross scores of query rows 64 .. 127 against keys 32 KK ..
+            // 32 KK + 31 (fragments 6 .. 9 of this wave), and with WITH_B the
+            // inter product of window B from the same query operands
+            auto cross = [&](auto kkc, auto with_bc) __attribute__((always_inline)) {
+                constexpr int KK = decltype(kkc)::value;
+                constexpr bool WITH_B = decltype(with_bc)::value != 0;
+                f32x4 X[4][2];
+#pragma unroll
+                for (int qb = 0; qb < 4; ++qb) X[qb][0] = X[qb][1] = zero4;
+                bf16x8 qa[2][4], ka[2][2];
+                auto load = [&](int ks, bf16x8 (&q_)[4], bf16x8 (&k_)[2]) __attribute__((always_inline)) {
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) q_[b] = row_op<QSEG>(s.q, (4 + b) * 16 + l16, ks * 32, g);
+#pragma unroll
+                    for (int b = 0; b < 2; ++b) k_[b] = row_op<QSEG>(s.k, (2 * KK + b) * 16 + l16, ks * 32, g);
+                };
+                load(0, qa[0], ka[0]);
+#pragma unroll
+                for (int ks = 0; ks < NKA; ++ks) {
+                    if (ks + 1 < NKA) load(ks + 1, qa[(ks + 1) & 1], ka[(ks + 1) & 1]);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+                        for (int b = 0; b < 2; ++b) X[qb][b] = mfma_bf16(ka[ks & 1][b], qa[ks & 1][qb], X[qb][b]);
+                    if constexpr (WITH_B)
+#pragma unroll
+                        for (int c = 0; c < NCB; ++c)
+#pragma unroll
+                            for (int qb = 0; qb < 4; ++qb) Ob[c][qb] = mfma_bf16(pst[c][ks], qa[ks & 1][qb], Ob[c][qb]);
+                }
+#pragma unroll
+                for (int qb = 0; qb < 4; ++qb) fr[6 + qb] = pack_acc_bf16(X[qb][0], X[qb][1]);
+            };
+            if (h == 0) {
+                f32x4 S[10];
+                tri_window(s, ic<0>{}, ic<0>{}, ic<0>{}, ic<15>{}, S, Oa, pst);
+                pack_window(S);
+                cross(ic<0>{}, ic<1>{});
+            } else {
+                f32x4 S[10];
+                tri_window(s, ic<4>{}, ic<4>{}, ic<0>{}, ic<15>{}, S, Ob, pst);
+                pack_window(S);
+                cross(ic<1>{}, ic<0>{});
+                // window A's inter product
+#pragma unroll
+                for (int ks = 0; ks < NKA; ++ks)
+#pragma unroll
+                    for (int qb = 0; qb < 4; ++qb) {
+                        const bf16x8 qa = row_op<QSEG>(s.q, qb * 16 + l16, ks * 32, g);
+#pragma unroll
+                        for (int c = 0; c < NCB; ++c) Oa[c][qb] = mfma_bf16(pst[c][ks], qa, Oa[c][qb]);
+                    }
+            }
+            __syncthreads();  // SYNC1(t): both compute waves are done reading Q
+            // fragment f: in the Q slot while f < QF, then in xfrag
+            auto fa = [&](int f) __attribute__((always_inline)) {
+                return (f < QF ? reinterpret_cast<char*>(s.q) + 1024 * f : xfrag + 1024 * (f - QF)) + 16 * lane;
+            };
+            const int own_w = h == 0 ? 0 : 6, own_x = h == 0 ? 12 : 16;
+            const int oth_w = h == 0 ? 6 : 0, oth_x = h == 0 ? 16 : 12;
+#pragma unroll
+            for (int i = 0; i < 6; ++i) *reinterpret_cast<bf16x8*>(fa(own_w + i)) = fr[i];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) *reinterpret_cast<bf16x8*>(fa(own_x + i)) = fr[6 + i];
+            __syncthreads();  // SYNC2(t): every score operand is in place
+            bf16x8 ot[10];
+#pragma unroll
+            for (int i = 0; i < 6; ++i) ot[i] = *reinterpret_cast<const bf16x8*>(fa(oth_w + i));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ot[6 + i] = *reinterpret_cast<const bf16x8*>(fa(oth_x + i));
+            // window A's operands and the cross keys 0..31 are wave 0's, window B's and
+            // the cross keys 32..63 wave 1's
+            bf16x8 wa[6], wb[6], x0[4], x1[4];
+#pragma unroll
+            for (int i = 0; i < 6; ++i) {
+                wa[i] = h == 0 ? fr[i] : ot[i];
+                wb[i] = h == 0 ? ot[i] : fr[i];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x0[i] = h == 0 ? fr[6 + i] : ot[6 + i];
+                x1[i] = h == 0 ? ot[6 + i] : fr[6 + i];
+            }
+            {
+                bf16x8 vb[NCB][2];
+                load_v(s, ic<0>{}, ic<2>{}, vb);  // keys 0..63
+                int f = 0;
+#pragma unroll
+                for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+                    for (int kk = 0; kk <= qb / 2; ++kk, ++f)
+#pragma unroll
+                        for (int c = 0; c < NCB; ++c) Oa[c][qb] = mfma_bf16(vb[c][kk], wa[f], Oa[c][qb]);
+#pragma unroll
+                for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+                    for (int c = 0; c < NCB; ++c) {
+                        Ob[c][qb] = mfma_bf16(vb[c][0], x0[qb], Ob[c][qb]);
+                        Ob[c][qb] = mfma_bf16(vb[c][1], x1[qb], Ob[c][qb]);
+                    }
+            }
+            {
+                bf16x8 vb[NCB][2];
+                load_v(s, ic<2>{}, ic<2>{}, vb);  // keys 64..127
+                int f = 0;
+#pragma unroll
+                for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+                    for (int kk = 0; kk <= qb / 2; ++kk, ++f)
+#pragma unroll
+                        for (int c = 0; c < NCB; ++c) Ob[c][qb] = mfma_bf16(vb[c][kk], wb[f], Ob[c][qb]);
+            }
+            update(s, ic<0>{}, ic<4>{}, valid, 0);
+            write_out(s, ic<0>{}, Oa, one4);
+            write_out(s, ic<4>{}, Ob, one4);
         } else {
             // one chunk of 128 rows per tile: query rows 0..63 against their own
             // keys; query rows 64..127 against their own keys and the full block
