@@ -1139,6 +1139,43 @@ void chunked_fwd_pipe(FwdParams p) {
                         for (int c = 0; c < NCB; ++c) Oa[c][qb] = mfma_bf16(pst[c][ks], qa, Oa[c][qb]);
                     }
             }
+            // intra products of ten fragments: window A's (with V keys 0..63,
+            // into Oa) or window B's (keys 64..127, into Ob), and the cross
+            // block's keys 32 CK .. 32 CK + 31 (into Ob).  Each wave applies its
+            // own fragments before SYNC1 and the other wave's after SYNC2, so
+            // that its own are dead by the time the other's are read.
+            auto apply = [&](const bf16x8 (&f)[10], auto wac, auto ckc) __attribute__((always_inline)) {
+                constexpr bool WA = decltype(wac)::value != 0;
+                constexpr int CK = decltype(ckc)::value;
+                bf16x8 vw[NCB][2], vx[NCB][1];
+                load_v(s, ic<WA ? 0 : 2>{}, ic<2>{}, vw);
+                if constexpr (WA && CK == 0) {
+#pragma unroll
+                    for (int c = 0; c < NCB; ++c) vx[c][0] = vw[c][0];
+                } else {
+                    load_v(s, ic<CK>{}, ic<1>{}, vx);
+                }
+                int i = 0;
+#pragma unroll
+                for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+                    for (int kk = 0; kk <= qb / 2; ++kk, ++i)
+#pragma unroll
+                        for (int c = 0; c < NCB; ++c) {
+                            if constexpr (WA)
+                                Oa[c][qb] = mfma_bf16(vw[c][kk], f[i], Oa[c][qb]);
+                            else
+                                Ob[c][qb] = mfma_bf16(vw[c][kk], f[i], Ob[c][qb]);
+                        }
+#pragma unroll
+                for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+                    for (int c = 0; c < NCB; ++c) Ob[c][qb] = mfma_bf16(vx[c][0], f[6 + qb], Ob[c][qb]);
+            };
+            if (h == 0)
+                apply(fr, ic<1>{}, ic<0>{});
+            else
+                apply(fr, ic<0>{}, ic<1>{});
             __syncthreads();  // SYNC1(t): both compute waves are done reading Q
             // fragment f: in the Q slot while f < QF, then in xfrag
             auto fa = [&](int f) __attribute__((always_inline)) {
@@ -1156,48 +1193,10 @@ void chunked_fwd_pipe(FwdParams p) {
             for (int i = 0; i < 6; ++i) ot[i] = *reinterpret_cast<const bf16x8*>(fa(oth_w + i));
 #pragma unroll
             for (int i = 0; i < 4; ++i) ot[6 + i] = *reinterpret_cast<const bf16x8*>(fa(oth_x + i));
-            // window A's operands and the cross keys 0..31 are wave 0's, window B's and
-            // the cross keys 32..63 wave 1's
-            bf16x8 wa[6], wb[6], x0[4], x1[4];
-#pragma unroll
-            for (int i = 0; i < 6; ++i) {
-                wa[i] = h == 0 ? fr[i] : ot[i];
-                wb[i] = h == 0 ? ot[i] : fr[i];
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                x0[i] = h == 0 ? fr[6 + i] : ot[6 + i];
-                x1[i] = h == 0 ? ot[6 + i] : fr[6 + i];
-            }
-            {
-                bf16x8 vb[NCB][2];
-                load_v(s, ic<0>{}, ic<2>{}, vb);  // keys 0..63
-                int f = 0;
-#pragma unroll
-                for (int qb = 0; qb < 4; ++qb)
-#pragma unroll
-                    for (int kk = 0; kk <= qb / 2; ++kk, ++f)
-#pragma unroll
-                        for (int c = 0; c < NCB; ++c) Oa[c][qb] = mfma_bf16(vb[c][kk], wa[f], Oa[c][qb]);
-#pragma unroll
-                for (int qb = 0; qb < 4; ++qb)
-#pragma unroll
-                    for (int c = 0; c < NCB; ++c) {
-                        Ob[c][qb] = mfma_bf16(vb[c][0], x0[qb], Ob[c][qb]);
-                        Ob[c][qb] = mfma_bf16(vb[c][1], x1[qb], Ob[c][qb]);
-                    }
-            }
-            {
-                bf16x8 vb[NCB][2];
-                load_v(s, ic<2>{}, ic<2>{}, vb);  // keys 64..127
-                int f = 0;
-#pragma unroll
-                for (int qb = 0; qb < 4; ++qb)
-#pragma unroll
-                    for (int kk = 0; kk <= qb / 2; ++kk, ++f)
-#pragma unroll
-                        for (int c = 0; c < NCB; ++c) Ob[c][qb] = mfma_bf16(vb[c][kk], wb[f], Ob[c][qb]);
-            }
+            if (h == 0)
+                apply(ot, ic<0>{}, ic<1>{});
+            else
+                apply(ot, ic<1>{}, ic<0>{});
             update(s, ic<0>{}, ic<4>{}, valid, 0);
             write_out(s, ic<0>{}, Oa, one4);
             write_out(s, ic<4>{}, Ob, one4);
