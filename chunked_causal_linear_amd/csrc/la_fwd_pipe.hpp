@@ -378,12 +378,20 @@ void chunked_fwd_pipe(FwdParams p) {
             }
         }
     };
-    // this wave's share of the mapping of a landed tile
+    // this wave's share of the mapping of a landed tile (a whole tile without
+    // the per-piece row test, so that the reads are not each sunk into a branch)
     auto phi_share = [&](StageT& s, int valid) __attribute__((always_inline)) {
-        if (copier)
-            phi_blocks(s, valid, ic<0>{}, ic<NPK>{});
-        else
-            phi_blocks(s, valid, ic<NPK>{}, ic<NPC>{});
+        if (copier) {
+            if (valid == TT)
+                phi_blocks(s, TT, ic<0>{}, ic<NPK>{});
+            else
+                phi_blocks(s, valid, ic<0>{}, ic<NPK>{});
+        } else {
+            if (valid == TT)
+                phi_blocks(s, TT, ic<NPK>{}, ic<NPC>{});
+            else
+                phi_blocks(s, valid, ic<NPK>{}, ic<NPC>{});
+        }
     };
 
     // factored decay: this copy wave's own V slots of a landed tile (V
