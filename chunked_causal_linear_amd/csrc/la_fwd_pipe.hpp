@@ -1137,15 +1137,22 @@ void chunked_fwd_pipe(FwdParams p) {
                 tri_window(s, ic<4>{}, ic<4>{}, ic<0>{}, ic<15>{}, S, Ob, pst);
                 pack_window(S);
                 cross(ic<1>{}, ic<0>{});
-                // window A's inter product
+                // window A's inter product, the next feature step's query
+                // operands read during this one's products
+                bf16x8 qa[2][4];
 #pragma unroll
-                for (int ks = 0; ks < NKA; ++ks)
+                for (int qb = 0; qb < 4; ++qb) qa[0][qb] = row_op<QSEG>(s.q, qb * 16 + l16, 0, g);
 #pragma unroll
-                    for (int qb = 0; qb < 4; ++qb) {
-                        const bf16x8 qa = row_op<QSEG>(s.q, qb * 16 + l16, ks * 32, g);
+                for (int ks = 0; ks < NKA; ++ks) {
+                    if (ks + 1 < NKA)
 #pragma unroll
-                        for (int c = 0; c < NCB; ++c) Oa[c][qb] = mfma_bf16(pst[c][ks], qa, Oa[c][qb]);
-                    }
+                        for (int qb = 0; qb < 4; ++qb) qa[(ks + 1) & 1][qb] = row_op<QSEG>(s.q, qb * 16 + l16, (ks + 1) * 32, g);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+                        for (int c = 0; c < NCB; ++c) Oa[c][qb] = mfma_bf16(pst[c][ks], qa[ks & 1][qb], Oa[c][qb]);
+                }
             }
             // intra products of ten fragments: window A's (with V keys 0..63,
             // into Oa) or window B's (keys 64..127, into Ob), and the cross
