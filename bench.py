@@ -750,6 +750,56 @@ def pmc_summary(dirs):
     return "\n".join(lines)
 
 
+def traffic_summary(fetch_dir: str, write_dir: str, chunk: int, group: int, commands: list) -> str:
+    """The HBM traffic file of the dominant kernel from two rocprofv3 --pmc runs
+    of `bench.py --copy-calibration` (FETCH_SIZE, then WRITE_SIZE; KiB per
+    dispatch).  Each counter is scaled by what it reads for the run's last two
+    dispatches of the runtime's copy kernel: the two plain 512 MiB copies that
+    end the program, factor = 524288 KiB / their mean reading."""
+    import csv
+    import glob
+
+    def read(d, counter):
+        f = glob.glob(os.path.join(d, "*counter_collection.csv"))[0]
+        kern, copies, name = [], [], None
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != counter:
+                continue
+            if "chunked_fwd_pipe" in r["Kernel_Name"]:
+                kern.append(float(r["Counter_Value"]))
+                name = r["Kernel_Name"].replace("void ", "").split("(")[0]
+            elif "copyBuffer" in r["Kernel_Name"]:
+                copies.append((int(r["Dispatch_Id"]), float(r["Counter_Value"])))
+        copies.sort()
+        cal = [v for _, v in copies[-2:]]
+        return name, kern, sum(cal) / len(cal)
+
+    name, kf, cf = read(fetch_dir, "FETCH_SIZE")
+    _, kw, cw = read(write_dir, "WRITE_SIZE")
+    ff, wf = 524288.0 / cf, 524288.0 / cw
+    fetch, write = sum(kf) / len(kf), sum(kw) / len(kw)
+    per_launch = (fetch * ff + write * wf) * 1024
+    alg = 1073741824  # q, k, v read and o written once: 4 x 8 x 16 x 8192 x 128 x 2 B
+    lines = ["# HBM traffic of chunked_fwd_pipe (phase 3), bench.py headline: identity map, "
+             "B=8 H=16 L=8192 d=128, bf16",
+             "# commands (repo root; each pass its own run):"]
+    lines += [f"#   {c}" for c in commands]
+    lines += ["# calibration: the same runs end with a plain device copy of 512 MiB (bench.py --copy-calibration);",
+              "# factor = 524288 KiB / what the counter reads for that copy.",
+              "# bytes_per_launch = (FETCH_SIZE * fetch_factor + WRITE_SIZE * write_factor) * 1024, "
+              "mean over dispatches.",
+              "# written by: python3 bench.py --traffic-summary <fetch dir> <write dir>",
+              f"kernel: {name}", f"kernel_hash: {kernel_hash()}", f"lib_hash: {lib_hash()}",
+              f"chunk: {chunk}", f"group: {group}",
+              f"dispatches_fetch: {len(kf)}", f"dispatches_write: {len(kw)}",
+              f"fetch_kib_per_dispatch: {fetch:.1f}", f"write_kib_per_dispatch: {write:.1f}",
+              f"copy_fetch_kib: {cf:.1f}", f"copy_write_kib: {cw:.1f}",
+              f"fetch_factor: {ff:.4f}", f"write_factor: {wf:.4f}",
+              f"bytes_per_launch: {per_launch:.0f}", f"algorithmic_bytes_per_launch: {alg}",
+              f"traffic_over_algorithmic: {per_launch / alg:.4f}"]
+    return "\n".join(lines) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -769,9 +819,21 @@ def main():
     ap.add_argument("--reps", type=int, default=10)
     ap.add_argument("--pmc-summary", nargs="+", default=None, metavar="DIR",
                     help="print the matrix-core counter table of rocprofv3 --pmc runs of --row (no GPU needed)")
+    ap.add_argument("--traffic-summary", nargs=2, default=None, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the headline kernel's HBM traffic file from rocprofv3 --pmc FETCH_SIZE and "
+                         "WRITE_SIZE runs of bench.py --copy-calibration (no GPU needed)")
     args = ap.parse_args()
     if args.pmc_summary:
         print(pmc_summary(args.pmc_summary))
+        return
+    if args.traffic_summary:
+        cmd = ("rocprofv3 --pmc {c} --output-format csv -d gpurun_out/ph/pmc_{d} -o run -- python3 bench.py "
+               "--steps 3 --warmup 1 --no-cpu-baseline --copy-calibration")
+        text = traffic_summary(*args.traffic_summary, args.chunk, 8192 // args.chunk,
+                               [cmd.format(c="FETCH_SIZE", d="fetch"), cmd.format(c="WRITE_SIZE", d="write")])
+        with open(TRAFFIC_FILE, "w") as fh:
+            fh.write(text)
+        print(text, end="")
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); this build has no multi-GPU path",
