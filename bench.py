@@ -336,6 +336,9 @@ def run_headline(args):
         "tflops_causal_useful": useful / sec / 1e12,
         "head_tokens_per_s": w.BH * w.L / sec,
         "phases_ms": {"chunk_states": k1, "state_scan": k2, "chunk_output": k3},
+        "step_ms_spread": {"from": "event pair around each of the K steps of the second pass",
+                           "median": float(np.median(per_step)), "min": float(np.min(per_step)),
+                           "max": float(np.max(per_step))},
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved_gbs / PEAK_HBM_GBS, "traffic": traffic,
                      "kernel": "chunked_fwd_pipe" if C in (32, 64, 128) else "chunked_fwd_bf16",

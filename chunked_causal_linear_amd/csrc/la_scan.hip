@@ -46,11 +46,21 @@ __device__ __forceinline__ void st4(V4* p, const V4& v) {
         *p = v;
 }
 
+// One launch scans two state sets of the same heads and chunk count: threads
+// [0, BH E4) walk S (E4 vectors per chunk), the next BH Ez4 walk z (Ez4 per
+// chunk; Ez4 = 0 when there is none).
 template <typename V4, typename E, bool NT>
-__global__ __launch_bounds__(256) void state_scan_kernel(V4* __restrict__ S, V4* __restrict__ total, int64_t N,
-                                                          int64_t E4, int64_t BH) {
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= BH * E4) return;
+__global__ __launch_bounds__(256) void state_scan_kernel(V4* __restrict__ S, V4* __restrict__ total, int64_t E4,
+                                                          V4* __restrict__ Z, V4* __restrict__ ztotal, int64_t Ez4,
+                                                          int64_t N, int64_t BH) {
+    int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= BH * E4) {
+        idx -= BH * E4;
+        if (idx >= BH * Ez4) return;
+        S = Z;
+        total = ztotal;
+        E4 = Ez4;
+    }
     const int64_t bh = idx / E4, e = idx % E4;
     V4* base = S + bh * N * E4 + e;
     V4 run;
@@ -79,11 +89,19 @@ __global__ __launch_bounds__(256) void state_scan_kernel(V4* __restrict__ S, V4*
 // decayed recurrence): chunk n's state as it stands at the chunk's end enters
 // after the carried state has decayed over the chunk's rows,
 // P_n = gamma^len(n-1) P_{n-1} + S_{n-1}, len(n) = clamp(L - n Cs, 0, Cs).
+// (S and z in one launch, split over the threads as above)
 __global__ __launch_bounds__(256) void state_scan_decay_kernel(float4* __restrict__ S, float4* __restrict__ total,
-                                                               int64_t N, int64_t E4, int64_t BH, float lg,
-                                                               int64_t L, int64_t Cs) {
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= BH * E4) return;
+                                                               int64_t E4, float4* __restrict__ Z,
+                                                               float4* __restrict__ ztotal, int64_t Ez4, int64_t N,
+                                                               int64_t BH, float lg, int64_t L, int64_t Cs) {
+    int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= BH * E4) {
+        idx -= BH * E4;
+        if (idx >= BH * Ez4) return;
+        S = Z;
+        total = ztotal;
+        E4 = Ez4;
+    }
     const int64_t bh = idx / E4, e = idx % E4;
     float4* base = S + bh * N * E4 + e;
     float4 run = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -120,31 +138,28 @@ struct WrapInt4 {
     unsigned x, y, z, w;
 };
 
-static hipError_t scan_one(void* S, void* total, int64_t N, int64_t E, int64_t BH, int is_int, hipStream_t s,
-                           float lg, int64_t L, int64_t Cs) {
-    const int64_t E4 = E / 4;
-    const int64_t threads = BH * E4;
+hipError_t run_state_scan(const ScanParams& p, int64_t BH, hipStream_t s) {
+    const int64_t E4 = p.E / 4, Ez4 = p.z != nullptr ? p.Ez / 4 : 0;
+    const int64_t threads = BH * (E4 + Ez4);
     const int64_t blocks = (threads + 255) / 256;
-    if (lg != 0.0f && !is_int)
+    if (p.log2_gamma != 0.0f && !p.is_int)
         hipLaunchKernelGGL(state_scan_decay_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
-                           reinterpret_cast<float4*>(S), reinterpret_cast<float4*>(total), N, E4, BH, lg, L, Cs);
-    else if (is_int)
+                           reinterpret_cast<float4*>(p.S), reinterpret_cast<float4*>(p.S_final), E4,
+                           reinterpret_cast<float4*>(p.z), reinterpret_cast<float4*>(p.z_final), Ez4, p.N, BH,
+                           p.log2_gamma, p.L, p.Cs);
+    else if (p.is_int)
         hipLaunchKernelGGL((state_scan_kernel<WrapInt4, unsigned, false>), dim3((unsigned)blocks), dim3(256), 0, s,
-                           reinterpret_cast<WrapInt4*>(S), reinterpret_cast<WrapInt4*>(total), N, E4, BH);
-    else if (BH * N * E * 4 > (int64_t)512 << 20)  // larger than the last-level cache
+                           reinterpret_cast<WrapInt4*>(p.S), reinterpret_cast<WrapInt4*>(p.S_final), E4,
+                           reinterpret_cast<WrapInt4*>(p.z), reinterpret_cast<WrapInt4*>(p.z_final), Ez4, p.N, BH);
+    else if (BH * p.N * (p.E + (Ez4 ? p.Ez : 0)) * 4 > (int64_t)512 << 20)  // larger than the last-level cache
         hipLaunchKernelGGL((state_scan_kernel<float4, float, true>), dim3((unsigned)blocks), dim3(256), 0, s,
-                           reinterpret_cast<float4*>(S), reinterpret_cast<float4*>(total), N, E4, BH);
+                           reinterpret_cast<float4*>(p.S), reinterpret_cast<float4*>(p.S_final), E4,
+                           reinterpret_cast<float4*>(p.z), reinterpret_cast<float4*>(p.z_final), Ez4, p.N, BH);
     else
         hipLaunchKernelGGL((state_scan_kernel<float4, float, false>), dim3((unsigned)blocks), dim3(256), 0, s,
-                           reinterpret_cast<float4*>(S), reinterpret_cast<float4*>(total), N, E4, BH);
+                           reinterpret_cast<float4*>(p.S), reinterpret_cast<float4*>(p.S_final), E4,
+                           reinterpret_cast<float4*>(p.z), reinterpret_cast<float4*>(p.z_final), Ez4, p.N, BH);
     return hipGetLastError();
-}
-
-hipError_t run_state_scan(const ScanParams& p, int64_t BH, hipStream_t s) {
-    hipError_t e = scan_one(p.S, p.S_final, p.N, p.E, BH, p.is_int, s, p.log2_gamma, p.L, p.Cs);
-    if (e != hipSuccess) return e;
-    if (p.z != nullptr) e = scan_one(p.z, p.z_final, p.N, p.Ez, BH, p.is_int, s, p.log2_gamma, p.L, p.Cs);
-    return e;
 }
 
 }  // namespace la
