@@ -119,6 +119,53 @@ def mfma_peak(kind: int, grid: int = 2048, iters: int = 1024):
     return grid * 4 * iters * 8 * per_inst / (ms * 1e-3) / 1e12, ms
 
 
+def memory_ceilings():
+    """What plain streams get from this memory system, by access mix (GB/s,
+    median of five launches each, after one untimed): reads only over 1 GiB
+    and 2 GiB sets (libla_probe.so's la_probe_read, include/la_probe.h), the
+    same probe re-reading a 128 MiB set four times per launch (the Infinity
+    Cache), three reads and one write (torch.addcmul over 256 MiB operands) and
+    one read and one write (a 512 MiB device copy)."""
+    import ctypes
+
+    import numpy as np
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "chunked_causal_linear_amd", "libla_probe.so"))
+    lib.la_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                  ctypes.c_void_p]
+    lib.la_probe_read.restype = ctypes.c_int
+    grid = 2048
+    out = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+    buf = torch.ones(1 << 29, dtype=torch.float32, device="cuda")  # 2 GiB
+    res = {}
+
+    def rate(fn, nbytes):
+        fn()
+        torch.cuda.synchronize()
+        return nbytes / (float(np.median(per_launch_ms(fn, 5))) * 1e-3) / 1e9
+
+    def read(nbytes, reps):
+        def run():
+            rc = lib.la_probe_read(buf.data_ptr(), nbytes // 16, reps, grid, out.data_ptr(),
+                                   torch.cuda.current_stream().cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"la_probe_read returned {rc}")
+        return rate(run, nbytes * reps)
+    res["reads_1GiB"] = read(1 << 30, 1)
+    res["reads_2GiB"] = read(1 << 31, 1)
+    res["rereads_128MiB_x4"] = read(1 << 27, 4)
+    del buf
+    a, b, c, d = (torch.ones(1 << 27, dtype=torch.bfloat16, device="cuda") for _ in range(4))
+    res["three_reads_one_write_1GiB"] = rate(lambda: torch.addcmul(a, b, c, out=d), 4 << 28)
+    del a, b, c, d
+    x = torch.ones(1 << 28, dtype=torch.bfloat16, device="cuda")
+    y = torch.empty_like(x)
+    res["one_read_one_write_1GiB"] = rate(lambda: y.copy_(x), 2 << 29)
+    del x, y
+    torch.cuda.empty_cache()
+    return {k: {"GB/s": v, "frac_of_8TBs": v / PEAK_HBM_GBS} for k, v in res.items()}
+
+
 def cpu_info():
     """CPU model (from /proc/cpuinfo) and numpy's BLAS build and thread count."""
     model = platform.processor() or platform.machine()
@@ -376,7 +423,7 @@ def run_extras(args, out):
     import workloads as wl
     from chunked_causal_linear_amd.accounting import Work, decode_bytes, phase1_bytes, scan_bytes
 
-    rows = {}
+    rows = {"memory_ceilings": memory_ceilings()}
     hbm = lambda b, ms: {"GB/s": b / (ms * 1e-3) / 1e9, "frac_of_8TBs": b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}  # noqa
 
     def med_ms(fn, n=10):
@@ -616,7 +663,7 @@ def run_extras(args, out):
 
 ROWS = ("fwd_w3_C32", "fwd_w3_C64", "fwd_w3_C128", "fwd_w3_int8_C64", "states_w3_C64", "states_w3_C1024",
         "scan_w3_C64", "fmap_favor_w5", "fwd_w2", "fwd_w4", "fwd_w5", "decode_w5", "mfma_peak_bf16", "mfma_peak_i8",
-        "copy_512MiB", "delta_w3", "delta_w3_gated", "delta_decode_w3")
+        "copy_512MiB", "memory_ceilings", "delta_w3", "delta_w3_gated", "delta_decode_w3")
 
 
 def run_row(name: str, reps: int):
@@ -639,6 +686,10 @@ def run_row(name: str, reps: int):
     if name == "copy_512MiB":
         copy_calibration()
         log(f"{name}: two 512 MiB device copies")
+        return
+    if name == "memory_ceilings":
+        for _ in range(reps):
+            log(json.dumps(memory_ceilings()))
         return
     w3 = wl.WORKLOADS[3]
     if name.startswith(("fwd_w3_C", "states_w3", "scan_w3")):

@@ -1,4 +1,6 @@
-// Matrix-core rate probe (see include/la_probe.h): eight independent
+// Matrix-core rate and read bandwidth probes (see include/la_probe.h).
+//
+// Matrix cores: eight independent
 // accumulators per wave, each updated once per round, so consecutive
 // instructions never depend on each other and the matrix core never waits
 // for a result.  The operands come from the thread index, so nothing folds.
@@ -58,6 +60,20 @@ __global__ __launch_bounds__(256) void probe_i8(int64_t iters, float* out) {
     out[(int64_t)blockIdx.x * 256 + tid] = (float)s;
 }
 
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// grid-stride 16-byte reads of x, reps passes, folded per thread
+__global__ __launch_bounds__(256) void probe_read(const u32x4* __restrict__ x, int64_t n16, int64_t reps, float* out) {
+    const int64_t i0 = (int64_t)blockIdx.x * 256 + threadIdx.x, stride = (int64_t)gridDim.x * 256;
+    unsigned acc = 0;
+    for (int64_t r = 0; r < reps; ++r)
+        for (int64_t i = i0; i < n16; i += stride) {
+            const u32x4 v = x[i];
+            acc ^= v.x ^ v.y ^ v.z ^ v.w;
+        }
+    out[i0] = (float)acc;
+}
+
 }  // namespace
 
 extern "C" int la_probe_mfma(int kind, int64_t iters, int64_t grid, float* out, struct ihipStream_t* stream) {
@@ -67,6 +83,17 @@ extern "C" int la_probe_mfma(int kind, int64_t iters, int64_t grid, float* out, 
         hipLaunchKernelGGL(probe_bf16, dim3((unsigned)grid), dim3(256), 0, s, iters, out);
     else
         hipLaunchKernelGGL(probe_i8, dim3((unsigned)grid), dim3(256), 0, s, iters, out);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? 0 : (int)e;
+}
+
+extern "C" int la_probe_read(const void* x, int64_t n16, int64_t reps, int64_t grid, float* out,
+                             struct ihipStream_t* stream) {
+    if (x == nullptr || out == nullptr || n16 < 1 || reps < 1 || grid < 1 || grid > 0x7FFFFFFFLL / 256 ||
+        (reinterpret_cast<uintptr_t>(x) & 15) != 0)
+        return -1;
+    hipLaunchKernelGGL(probe_read, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream,
+                       reinterpret_cast<const u32x4*>(x), n16, reps, out);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? 0 : (int)e;
 }

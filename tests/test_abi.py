@@ -35,11 +35,12 @@ def test_library_loads_and_exports_header_symbols():
 
 
 def test_probe_library_exports_and_rejects_bad_arguments():
-    """libla_probe.so (include/la_probe.h, the matrix-core rate probe) loads and
-    exports what its header declares; invalid arguments return -1 unlaunched."""
+    """libla_probe.so (include/la_probe.h, the matrix-core rate and read
+    bandwidth probes) loads and exports what its header declares; invalid
+    arguments return -1 unlaunched."""
     path = os.path.join(ROOT, "chunked_causal_linear_amd", "libla_probe.so")
     names = declared_functions(os.path.join(ROOT, "include", "la_probe.h"))
-    assert names == ["la_probe_mfma"]
+    assert names == ["la_probe_mfma", "la_probe_read"]
     out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True).stdout
     exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
     assert set(names) <= exported
@@ -47,6 +48,11 @@ def test_probe_library_exports_and_rejects_bad_arguments():
     lib.la_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
     for kind, iters, grid, out_ in ((0, 0, 8, FAKE), (0, 8, 0, FAKE), (2, 8, 8, FAKE), (1, 8, 8, None)):
         assert lib.la_probe_mfma(kind, iters, grid, out_, None) == -1
+    lib.la_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                  ctypes.c_void_p]
+    for x, n16, reps, grid, out_ in ((None, 8, 1, 8, FAKE), (FAKE, 0, 1, 8, FAKE), (FAKE, 8, 0, 8, FAKE),
+                                     (FAKE, 8, 1, 0, FAKE), (FAKE, 8, 1, 8, None), (0x1008, 8, 1, 8, FAKE)):
+        assert lib.la_probe_read(x, n16, reps, grid, out_, None) == -1
 
 
 def test_version_and_status_strings():
