@@ -881,16 +881,17 @@ def main():
         print(pmc_summary(args.pmc_summary))
         return
     if args.traffic_summary:
-        cmd = ("rocprofv3 --pmc {c} --output-format csv -d gpurun_out/ph/pmc_{d} -o run -- python3 bench.py "
+        fetch_dir, write_dir = (os.path.relpath(d, ROOT) for d in args.traffic_summary)
+        cmd = ("rocprofv3 --pmc {c} --output-format csv -d {d} -o run -- python3 bench.py "
                "--steps 3 --warmup 1 --no-cpu-baseline --copy-calibration")
         text = traffic_summary(*args.traffic_summary, args.chunk, 8192 // args.chunk,
-                               [cmd.format(c="FETCH_SIZE", d="fetch"), cmd.format(c="WRITE_SIZE", d="write")])
+                               [cmd.format(c="FETCH_SIZE", d=fetch_dir), cmd.format(c="WRITE_SIZE", d=write_dir)])
         with open(TRAFFIC_FILE, "w") as fh:
             fh.write(text)
         print(text, end="")
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for {args.gpus}); this build has no multi-GPU path",
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the library has no multi-GPU path",
               file=sys.stderr)
         sys.exit(2)
     import torch
