@@ -843,7 +843,7 @@ def traffic_summary(fetch_dir: str, write_dir: str, chunk: int, group: int, comm
               "# bytes_per_launch = (FETCH_SIZE * fetch_factor + WRITE_SIZE * write_factor) * 1024, "
               "mean over dispatches.",
               "# written by: python3 bench.py --traffic-summary <fetch dir> <write dir>",
-              f"kernel: {name}", f"kernel_hash: {kernel_hash()}", f"lib_hash: {lib_hash()}",
+              f"kernel: {name}", f"kernel_hash: {kernel_hash()}",
               f"chunk: {chunk}", f"group: {group}",
               f"dispatches_fetch: {len(kf)}", f"dispatches_write: {len(kw)}",
               f"fetch_kib_per_dispatch: {fetch:.1f}", f"write_kib_per_dispatch: {write:.1f}",
