@@ -552,28 +552,33 @@ def loglinear_scores_first(q, k, v, lam) -> np.ndarray:
     return ((q @ k.T) * M) @ v
 
 
-def loglinear_recurrent(q, k, v, lam) -> np.ndarray:
+def loglinear_recurrent(q, k, v, lam, S0=None, t0: int = 0, return_state: bool = False):
     """The Fenwick tree recurrence over level states S^l (sum of k_s^T v_s over
     level l's bucket): at token t, with b = the position of t's lowest set bit,
     the buckets of levels 0..b at t-1 merge into level b+1, levels 1..b empty,
     level 0 takes k_t^T v_t, higher levels stay; then y_t = sum_l lam[t, l] q_t S^l
-    (t = 0: only level 0)."""
+    (t = 0: only level 0).
+
+    Row i of q, k, v, lam is token t0 + i; S0 (levels x d_k x d_v) is the state
+    after token t0 - 1 (zeros when None).  With return_state, also the level
+    states after the last token."""
     q, k, v = _f64(q, k, v)
     lam = np.asarray(lam, dtype=np.float64)
     L, dk = q.shape
     dv = v.shape[1]
     n_lev = lam.shape[1]
-    S = np.zeros((n_lev, dk, dv))
+    S = np.zeros((n_lev, dk, dv)) if S0 is None else np.array(S0, dtype=np.float64)
     out = np.zeros((L, dv))
-    for t in range(L):
+    for i in range(L):
+        t = t0 + i
         if t > 0:
             b = (t & -t).bit_length() - 1
             merged = S[:b + 1].sum(axis=0)
             S[1:b + 1] = 0.0
             S[b + 1] = merged
-        S[0] = np.outer(k[t], v[t])
-        out[t] = sum(lam[t, l] * (q[t] @ S[l]) for l in range(n_lev))
-    return out
+        S[0] = np.outer(k[i], v[i])
+        out[i] = sum(lam[i, l] * (q[i] @ S[l]) for l in range(n_lev))
+    return (out, S) if return_state else out
 
 
 def loglinear_chunked(q, k, v, lam, C: int) -> np.ndarray:

@@ -534,6 +534,43 @@ def check_loglinear_causality(o, seed: int = 62) -> None:
         assert np.array_equal(out[:t], base[:t]) and not np.array_equal(out[t:], base[t:]), t
 
 
+def check_loglinear_state(o, seed: int = 64) -> None:
+    """The level states the Fenwick tree recurrence leaves after token T - 1 are
+    the bucket sums by definition: level l holds the sum of k_s^T v_s over the
+    keys s <= T - 1 at level(T - 1, s) = l, and a level without keys is zero
+    (integers: exact), for every T up to L."""
+    rng = np.random.default_rng([seed, 65])
+    L, dk, dv = 37, 3, 2
+    q, k, v = _ints(rng, (L, dk)), _ints(rng, (L, dk)), _ints(rng, (L, dv))
+    nl = o.loglinear_levels(L)
+    lam = _ints(rng, (L, nl), -2, 3)
+    for T in range(1, L + 1):
+        _, S = o.loglinear_recurrent(q[:T], k[:T], v[:T], lam[:T], return_state=True)
+        assert S.shape == (nl, dk, dv)
+        for l in range(nl):
+            want = np.zeros((dk, dv))
+            for s_ in range(T):
+                if o.loglinear_level(T - 1, s_) == l:
+                    want += np.outer(k[s_], v[s_]).astype(np.float64)
+            assert np.array_equal(S[l], want), (T, l)
+
+
+def check_loglinear_resume(o, seed: int = 66) -> None:
+    """Running the recurrence to token T0 - 1, then on from its state at token
+    T0, gives the uninterrupted run's outputs and final state (integers:
+    exact), for split points on and between powers of two."""
+    rng = np.random.default_rng([seed, 67])
+    L, dk, dv = 70, 3, 2
+    q, k, v = _ints(rng, (L, dk)), _ints(rng, (L, dk)), _ints(rng, (L, dv))
+    lam = _ints(rng, (L, o.loglinear_levels(L)), -2, 3)
+    full, S_full = o.loglinear_recurrent(q, k, v, lam, return_state=True)
+    for T0 in (1, 2, 7, 8, 31, 32, 33, 64, 69):
+        a, S_a = o.loglinear_recurrent(q[:T0], k[:T0], v[:T0], lam[:T0], return_state=True)
+        b, S_b = o.loglinear_recurrent(q[T0:], k[T0:], v[T0:], lam[T0:], S0=S_a, t0=T0, return_state=True)
+        assert np.array_equal(np.concatenate([a, b]), full), T0
+        assert np.array_equal(S_b, S_full), T0
+
+
 # ---------------------------------------------------------------------------
 # The forward's reference: phi of the scaled inputs, and its non-causal branch
 # ---------------------------------------------------------------------------

@@ -86,6 +86,8 @@ MUTANTS = {
     "loglinear_merge_skips_level0": ("            merged = S[:b + 1].sum(axis=0)\n",
                                      "            merged = S[1:b + 1].sum(axis=0)\n"),
     "loglinear_merge_one_level_low": ("            S[b + 1] = merged\n", "            S[b] = merged\n"),
+    "loglinear_resume_ignores_start": ("        t = t0 + i\n", "        t = i\n"),
+    "loglinear_state_keeps_merged_levels": ("            S[1:b + 1] = 0.0\n", "\n"),
     "loglinear_bucket_shifted": ("Sb = sum(states[c_] for c_ in range(h - (1 << (m - 1)), h))",
                                  "Sb = sum(states[c_] for c_ in range(h - (1 << (m - 1)), h + 1) if c_ < n)"),
     "loglinear_chunk_level_index": ("acc = acc + lam[s:e, cb + m][:, None] * (q[s:e] @ Sb)",

@@ -103,6 +103,14 @@ def test_loglinear_causality():
     pins.check_loglinear_causality(oracle)
 
 
+def test_loglinear_state():
+    pins.check_loglinear_state(oracle)
+
+
+def test_loglinear_resume():
+    pins.check_loglinear_resume(oracle)
+
+
 def test_apply_phi_in_scale():
     pins.check_apply_phi_in_scale(oracle)
 
