@@ -596,7 +596,25 @@ def run_extras(args, out):
         **hbm(ll_bytes, ms), "bytes": ll_bytes,
         "oracle_s_per_head": _oracle_time(lambda: oracle.loglinear_chunked(lq, lk, lv, lam_h, 64)) * w3.L / 1024,
         "oracle_sample": "oracle.loglinear_chunked on 1024 rows of one head, scaled to L"}
-    del f, qd, kd, vd, lamd
+    # one decode step per head at position L - 1 = 8191 (twelve levels above
+    # level 0 hold keys: the step reads thirteen level states and writes two)
+    t_step = w3.L - 1
+    qs_, ks_, vs_ = (x[:, t_step].contiguous() for x in (qd, kd, vd))
+    lam_s = lamd[:, t_step].contiguous()
+    S_ll = torch.randn(w3.BH, nl, w3.d_k, w3.d_v, device="cuda")
+    o_ll = torch.empty(w3.BH, w3.d_v, device="cuda")
+    step = lambda: la.recurrent_step_loglinear(qs_, ks_, vs_, lam_s, S_ll, t_step, out=o_ll)  # noqa: E731
+    ms_step = med_ms(step, 20)
+    n_read = 1 + bin(t_step >> 1).count("1")  # level 0 (merged into level 1) and the set bits above
+    step_bytes = w3.BH * (n_read + 2) * w3.d_k * w3.d_v * 4
+    lq1, lk1, lv1 = (x.exact[0][:64] for x in wl.head_inputs(w3, 0, 64))
+    lam1 = wl.loglinear_weights(3, 1, 64, oracle.loglinear_levels(64))[0].astype(np.float64)
+    rows["next_loglinear"]["decode_step"] = {
+        "states": w3.BH, "position": t_step, "levels_read": n_read, "ms": ms_step, **hbm(step_bytes, ms_step),
+        "bytes": step_bytes,
+        "oracle_s_per_state_step": _oracle_time(lambda: oracle.loglinear_recurrent(lq1, lk1, lv1, lam1)) / 64,
+        "oracle_sample": "oracle.loglinear_recurrent over 64 positions of one head (d = 128)"}
+    del f, qd, kd, vd, lamd, S_ll
     torch.cuda.empty_cache()
     # ---- next: the delta rule and its gated form at the headline shape (chunks of 64)
     delta = {}

@@ -29,7 +29,7 @@ EXPORTS = (
     "la_version", "la_chunk_states_decay", "la_state_scan_decay", "la_chunk_output_decay", "la_chunked_forward_decay",
     "la_recurrent_step_decay", "la_loglinear_forward", "la_loglinear_forward_workspace", "la_loglinear_levels",
     "la_chunked_forward_delta", "la_chunked_forward_delta_workspace", "la_delta_chunk_transform",
-    "la_recurrent_step_delta", "la_chunked_forward_noalloc",
+    "la_recurrent_step_delta", "la_chunked_forward_noalloc", "la_recurrent_step_loglinear",
 )
 
 
@@ -73,6 +73,7 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.la_loglinear_forward_workspace.restype = sz
     lib.la_loglinear_levels.argtypes = [i64]
     lib.la_loglinear_levels.restype = i64
+    lib.la_recurrent_step_loglinear.argtypes = [vp, vp, vp, i32, i64, i64, i64, vp, i64, i64, vp, vp, i32, vp]
     lib.la_chunked_forward_delta.argtypes = [vp, vp, vp, i32, i64, i64, i64, i64, i64, vp, vp, vp, i32, vp, vp, sz,
                                              vp]
     lib.la_chunked_forward_delta_workspace.argtypes = [i32, i64, i64, i64, i64, i64]
@@ -358,6 +359,26 @@ class LogLinearForward:
 def loglinear_forward(q, k, v, lam, C: int = 64):
     """Log-linear attention output (see la_loglinear_forward); lam [BH, L, levels] float32."""
     return LogLinearForward(q, k, v, lam, C).run()
+
+
+def recurrent_step_loglinear(q, k, v, lam, S, t: int, out=None):
+    """One log-linear decode step (la_recurrent_step_loglinear) at position t over
+    n streams: q, k [n, d_k], v [n, d_v] bf16; lam [n, levels] float32 (this
+    token's level weights); S [n, levels, d_k, d_v] float32 updates in place."""
+    torch = _torch()
+    n, d_k = q.shape
+    d_v = v.shape[-1]
+    if lam.dtype != torch.float32 or lam.dim() != 2 or lam.shape[0] != n:
+        raise ValueError(f"lam must be float32 [{n}, levels]")
+    n_lev = lam.shape[1]
+    if S.dtype != torch.float32 or tuple(S.shape) != (n, n_lev, d_k, d_v):
+        raise ValueError(f"S must be float32 {(n, n_lev, d_k, d_v)}")
+    if out is None:
+        out = torch.empty(n, d_v, dtype=torch.float32, device=q.device)
+    _check(lib().la_recurrent_step_loglinear(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dtype_code(q), n, d_k, d_v,
+                                             _dev(lam, "lam"), n_lev, int(t), _dev(S, "S"), _dev(out, "o"),
+                                             _dtype_code(out), _stream_ptr()))
+    return out
 
 
 def recurrent_step(q, k, v, S, z=None, fmap: str = "identity", W=None, in_scale: float = 1.0,

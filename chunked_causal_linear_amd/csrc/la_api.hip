@@ -912,6 +912,41 @@ static la_status loglinear_check(la_dtype in_dt, int64_t BH, int64_t L, int64_t 
 
 int64_t la_loglinear_levels(int64_t L) { return L < 1 ? 0 : loglinear_levels_of(L); }
 
+la_status la_recurrent_step_loglinear(const void* q, const void* k, const void* v, la_dtype in_dt, int64_t n_states,
+                                      int64_t d_k, int64_t d_v, const float* lam, int64_t n_levels, int64_t t,
+                                      float* S, void* o, la_dtype out_dt, la_stream_t stream) {
+    g_last_error[0] = 0;
+    if (q == nullptr || k == nullptr || v == nullptr || lam == nullptr || S == nullptr || o == nullptr)
+        return fail(LA_ERR_INVALID_ARG, "q, k, v, lam, S and o must not be NULL");
+    if (n_states < 1 || d_k < 1 || d_v < 1) return fail(LA_ERR_INVALID_ARG, "sizes must be positive");
+    if (t < 0) return fail(LA_ERR_INVALID_ARG, "position t=%lld is negative", (long long)t);
+    int64_t need = 1;  // 1 + the bit length of t
+    for (int64_t x = t; x > 0; x >>= 1) ++need;
+    if (n_levels < need || n_levels > 40)
+        return fail(LA_ERR_INVALID_ARG, "n_levels=%lld: position %lld needs %lld..40", (long long)n_levels,
+                    (long long)t, (long long)need);
+    if (in_dt != LA_BF16) return fail(LA_ERR_UNSUPPORTED, "the log-linear step takes LA_BF16 inputs");
+    if (out_dt != LA_F32 && out_dt != LA_BF16) return fail(LA_ERR_UNSUPPORTED, "output must be LA_F32 or LA_BF16");
+    if (!pow2_in(d_k, 16, 256) || !pow2_in(d_v, 16, 256))
+        return fail(LA_ERR_UNSUPPORTED, "d_k=%lld, d_v=%lld: powers of two in 16..256", (long long)d_k,
+                    (long long)d_v);
+    if (n_states > 0x7FFFFFFFLL) return fail(LA_ERR_UNSUPPORTED, "too many states");
+    la::LogLinStepParams p{};
+    p.q = static_cast<const unsigned short*>(q);
+    p.k = static_cast<const unsigned short*>(k);
+    p.v = static_cast<const unsigned short*>(v);
+    p.lam = lam;
+    p.S = S;
+    p.o = o;
+    p.n = n_states;
+    p.t = t;
+    p.dk = (int)d_k;
+    p.dv = (int)d_v;
+    p.n_lev = (int)n_levels;
+    p.out_f32 = out_dt == LA_F32;
+    return hip_status(la::run_loglinear_step(p, (hipStream_t)stream), "log-linear step launch");
+}
+
 size_t la_loglinear_forward_workspace(la_dtype in_dt, int64_t BH, int64_t L, int64_t d_k, int64_t d_v, int64_t C) {
     char saved[sizeof(g_last_error)];
     memcpy(saved, g_last_error, sizeof(saved));

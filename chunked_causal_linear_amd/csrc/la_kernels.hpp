@@ -239,6 +239,22 @@ hipError_t run_loglinear_pyramid(const float* S, float* T, int64_t BH, int N, in
                                  hipStream_t s);
 hipError_t run_loglinear_fwd(const LogLinParams& p, int64_t grid, hipStream_t s);
 
+// One decode step of log-linear attention over n streams (the Fenwick tree
+// recurrence; see loglinear_step_kernel).
+struct LogLinStepParams {
+    const unsigned short* q;  // [n, dk] bf16
+    const unsigned short* k;  // [n, dk] bf16
+    const unsigned short* v;  // [n, dv] bf16
+    const float* lam;         // [n, n_lev] this token's level weights
+    float* S;                 // [n, n_lev, dk, dv] level states, in place
+    void* o;                  // [n, dv] f32 or bf16
+    int64_t n;
+    int64_t t;                // the token's position (>= 0)
+    int dk, dv, n_lev;
+    int out_f32;
+};
+hipError_t run_loglinear_step(const LogLinStepParams& p, hipStream_t s);
+
 hipError_t run_chunked_fwd_i8(const FwdParamsI8& p, int DK, int DVT, int T, int64_t grid, hipStream_t s);
 hipError_t run_chunk_states_i8(const StatesParamsI8& p, int DK, int DVT, int64_t grid, hipStream_t s);
 // Streaming phase 1 (la_states_pipe.hip): d_k = DK in {64, 128, 256}, value

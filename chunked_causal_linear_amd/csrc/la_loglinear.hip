@@ -20,6 +20,8 @@
 //     bf16 (P^T, rows = value columns), O_m^T = P^T Q^T, and O += lam[t, c + m]
 //     O_m.  Outputs come out transposed (a lane holds four consecutive columns
 //     of one row) and are stored as 8-byte pieces.
+//   * loglinear_step_kernel: one decode step, the Fenwick tree recurrence over
+//     each stream's level states (below).
 #include "la_common.hpp"
 #include "la_kernels.hpp"
 
@@ -268,6 +270,84 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     }
 }
 
+// One decode step (the slides' Fenwick tree recurrence): the level states
+// S[l] of a stream (the sum of k_s^T v_s over level l's bucket) advance to the
+// token at position t.  With b the position of t's lowest set bit (t > 0),
+// the buckets of levels 0..b merge into level b + 1 and levels 1..b empty;
+// level 0 takes k_t^T v_t; then o = sum_l lam[l] q_t S[l].  After the step,
+// level l >= 1 is non-empty only when bit l - 1 of t is set, so the output
+// reads just those (besides level 0 and the merged level, which it forms
+// itself).  One workgroup per stream; thread t owns four value columns
+// (j4 = t % (DV / 4)) of the rows a = t / (DV / 4) + AG i through every
+// level, so every state access is a coalesced 16-byte vector and each
+// element's merge, update and output share is formed in one pass; the row
+// partial sums of o reduce through LDS.
+template <int DV>
+__global__ __launch_bounds__(256) void loglinear_step_kernel(LogLinStepParams p) {
+    constexpr int NT = 256, J4 = DV / 4, AG = NT / J4;
+    static_assert(J4 * AG == NT, "thread layout");
+    __shared__ float qs[256], ks[256], vs[DV], lw[LL_NLMAX];
+    __shared__ float red[AG][DV + 4];
+    const int tid = threadIdx.x;
+    const int j4 = tid % J4, ag = tid / J4;
+    const int64_t st = blockIdx.x;
+    const int dk = p.dk, nl = p.n_lev;
+    const int64_t t = p.t;
+    for (int i = tid; i < dk; i += NT) {
+        qs[i] = bf2f(p.q[st * dk + i]);
+        ks[i] = bf2f(p.k[st * dk + i]);
+    }
+    for (int i = tid; i < DV; i += NT) vs[i] = bf2f(p.v[st * DV + i]);
+    for (int i = tid; i < nl; i += NT) lw[i] = p.lam[st * nl + i];
+    __syncthreads();
+    // b = the lowest set bit of t (-1 at t = 0: nothing merges)
+    const int b = t > 0 ? __builtin_ctzll((unsigned long long)t) : -1;
+    const int64_t lev = (int64_t)dk * DV / 4;  // float4s per level
+    float4* S = reinterpret_cast<float4*>(p.S) + st * nl * lev;
+    const float4 v4 = make_float4(vs[4 * j4], vs[4 * j4 + 1], vs[4 * j4 + 2], vs[4 * j4 + 3]);
+    const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 part = zero;
+    for (int a = ag; a < dk; a += AG) {
+        const int64_t e = (int64_t)a * J4 + j4;
+        const float ka = ks[a];
+        const float4 s0 = make_float4(ka * v4.x, ka * v4.y, ka * v4.z, ka * v4.w);
+        float4 acc = make_float4(lw[0] * s0.x, lw[0] * s0.y, lw[0] * s0.z, lw[0] * s0.w);
+        if (b >= 0) {
+            float4 merged = S[e];
+            for (int l = 1; l <= b; ++l) merged = add4f(merged, S[l * lev + e]);
+            const float w = lw[b + 1];
+            acc = make_float4(fmaf(w, merged.x, acc.x), fmaf(w, merged.y, acc.y), fmaf(w, merged.z, acc.z),
+                              fmaf(w, merged.w, acc.w));
+            S[(b + 1) * lev + e] = merged;
+            for (int l = 1; l <= b; ++l) S[l * lev + e] = zero;
+        }
+        // the untouched levels that hold keys: bit l - 1 of t set, l > b + 1
+        for (int l = b + 2; l < nl; ++l) {
+            if (((t >> (l - 1)) & 1) == 0) continue;
+            const float4 x = S[l * lev + e];
+            const float w = lw[l];
+            acc = make_float4(fmaf(w, x.x, acc.x), fmaf(w, x.y, acc.y), fmaf(w, x.z, acc.z), fmaf(w, x.w, acc.w));
+        }
+        S[e] = s0;
+        const float qa = qs[a];
+        part = make_float4(fmaf(qa, acc.x, part.x), fmaf(qa, acc.y, part.y), fmaf(qa, acc.z, part.z),
+                           fmaf(qa, acc.w, part.w));
+    }
+    red[ag][4 * j4] = part.x;
+    red[ag][4 * j4 + 1] = part.y;
+    red[ag][4 * j4 + 2] = part.z;
+    red[ag][4 * j4 + 3] = part.w;
+    __syncthreads();
+    for (int c = tid; c < DV; c += NT) {
+        float sum = 0.f;
+        for (int r = 0; r < AG; ++r) sum += red[r][c];
+        if (p.out_f32)
+            reinterpret_cast<float*>(p.o)[st * DV + c] = sum;
+        else
+            reinterpret_cast<u16*>(p.o)[st * DV + c] = f2bf(sum);
+    }
+}
+
 }  // namespace
 
 hipError_t run_loglinear_pyramid(const float* S, float* T, int64_t BH, int N, int n_pyr, int64_t E, hipStream_t s) {
@@ -284,6 +364,29 @@ hipError_t run_loglinear_fwd(const LogLinParams& p, int64_t grid, hipStream_t s)
     switch (p.dk) {
         case 64: hipLaunchKernelGGL(loglinear_fwd<64>, dim3((unsigned)grid), dim3(256), 0, s, p); break;
         case 128: hipLaunchKernelGGL(loglinear_fwd<128>, dim3((unsigned)grid), dim3(256), 0, s, p); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace la
+
+namespace la {
+
+hipError_t run_loglinear_step(const LogLinStepParams& p, hipStream_t s) {
+    if (p.n < 1 || p.n > 0x7FFFFFFFLL || p.dk < 1 || p.dk > 256 || p.n_lev < 1 || p.n_lev > LL_NLMAX || p.t < 0)
+        return hipErrorInvalidValue;
+    // the merged level (lowest set bit of t, plus one) and every level that
+    // holds keys after the step (up to the bit length of t) must exist
+    const int bits = p.t > 0 ? 64 - __builtin_clzll((unsigned long long)p.t) : 0;
+    if (p.n_lev < bits + 1) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)p.n);
+    switch (p.dv) {
+        case 16: hipLaunchKernelGGL(loglinear_step_kernel<16>, grid, dim3(256), 0, s, p); break;
+        case 32: hipLaunchKernelGGL(loglinear_step_kernel<32>, grid, dim3(256), 0, s, p); break;
+        case 64: hipLaunchKernelGGL(loglinear_step_kernel<64>, grid, dim3(256), 0, s, p); break;
+        case 128: hipLaunchKernelGGL(loglinear_step_kernel<128>, grid, dim3(256), 0, s, p); break;
+        case 256: hipLaunchKernelGGL(loglinear_step_kernel<256>, grid, dim3(256), 0, s, p); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -329,6 +329,37 @@ size_t la_loglinear_forward_workspace(la_dtype in_dt, int64_t BH, int64_t L, int
 int64_t la_loglinear_levels(int64_t L);
 
 /*
+ * One decode step of log-linear attention (slide deck "Log-Linear Attention",
+ * the Fenwick tree recurrence and its per-level update): each stream keeps
+ * level states S[l], the sum of k_s^T v_s over level l's bucket of the past.
+ * The token at position t (t >= 0, the same for every stream) advances them:
+ * with b the position of t's lowest set bit (t > 0), the buckets of levels
+ * 0..b merge into level b + 1 and levels 1..b empty; level 0 takes k_t^T v_t;
+ * the other levels stay.  Then o = sum_l lam[l] q_t S[l] (update, then read).
+ * Steps t = 0, 1, 2, ... from zero states give, token by token,
+ * la_loglinear_forward's outputs for the same inputs and weights.
+ *
+ *   q, k [n_states, d_k], v [n_states, d_v]: LA_BF16; d_k and d_v powers of
+ *        two in 16..256.
+ *   lam  [n_states, n_levels] float32 (device): this token's level weights
+ *        (row t of the forward's lam).
+ *   n_levels  levels each stream keeps: at least la_loglinear_levels(t + 1)
+ *        (1 + the bit length of t), at most 40; la_loglinear_levels(T) covers
+ *        every position below T.
+ *   S    [n_states, n_levels, d_k, d_v] float32 (device), read and updated in
+ *        place; all zero before position 0.  After the step, level l >= 1
+ *        holds keys (and is otherwise zero) exactly when bit l - 1 of t is set.
+ *   o    [n_states, d_v] of type out_dt (LA_F32 or LA_BF16).
+ * Errors: LA_ERR_INVALID_ARG (NULL pointer, non-positive n_states, t < 0,
+ * n_levels outside [la_loglinear_levels(t + 1), 40]), LA_ERR_UNSUPPORTED
+ * (other types or widths); nothing is launched on an error.
+ */
+la_status la_recurrent_step_loglinear(const void* q, const void* k, const void* v, la_dtype in_dt,
+                                      int64_t n_states, int64_t d_k, int64_t d_v, const float* lam,
+                                      int64_t n_levels, int64_t t, float* S, void* o, la_dtype out_dt,
+                                      la_stream_t stream);
+
+/*
  * The delta rule and its gated form (page "Kimi K3 と Qwen 3.8 の Attention 機構
  * 比較分析" (news.ainew.jp): section 3.1, equation (14): before writing, look up
  * what the current key maps to in the state, erase that old prediction along

@@ -272,6 +272,31 @@ def test_loglinear_entry_point_errors():
     assert call() == b.LA_ERR_WORKSPACE
 
 
+def test_loglinear_step_entry_point_errors():
+    """The log-linear decode step: NULL pointers, sizes, a negative position,
+    too few (or more than 40) levels for the position, types and widths are
+    rejected before any launch."""
+    lib = la.lib()
+
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, in_dt=b.LA_BF16, n=3, d_k=64, d_v=64, lam=FAKE, n_lev=4, t=7, S=FAKE,
+                 o=FAKE, out_dt=b.LA_F32)
+        a.update(kw)
+        return lib.la_recurrent_step_loglinear(a["q"], a["k"], a["v"], a["in_dt"], a["n"], a["d_k"], a["d_v"],
+                                               a["lam"], a["n_lev"], a["t"], a["S"], a["o"], a["out_dt"], None)
+    for name in ("q", "k", "v", "lam", "S", "o"):
+        assert call(**{name: None}) == b.LA_ERR_INVALID_ARG, name
+    assert call(n=0) == b.LA_ERR_INVALID_ARG
+    assert call(t=-1) == b.LA_ERR_INVALID_ARG
+    assert call(t=8, n_lev=4) == b.LA_ERR_INVALID_ARG  # position 8 needs 5 levels
+    assert call(t=0, n_lev=0) == b.LA_ERR_INVALID_ARG
+    assert call(t=0, n_lev=41) == b.LA_ERR_INVALID_ARG
+    assert call(in_dt=b.LA_I8) == b.LA_ERR_UNSUPPORTED
+    assert call(out_dt=b.LA_I32) == b.LA_ERR_UNSUPPORTED
+    assert call(d_k=48) == b.LA_ERR_UNSUPPORTED
+    assert call(d_v=512) == b.LA_ERR_UNSUPPORTED
+
+
 def test_delta_entry_point_errors():
     """The delta rule: workspace size (per-chunk 64 x 64 bf16 transforms and the
     gates' log products) and argument checks, all before any launch."""

@@ -60,3 +60,87 @@ def test_loglinear_benchmarked_shape():
         ref = oracle.loglinear_chunked(qh.exact, kh.exact, vh.exact, lam[bh].astype(np.float64), 64)
         worst = assert_close(o[bh], ref, what=f"head {bh}")
         log(f"head {bh} worst ratio {worst:.3f}")
+
+
+def _step_inputs(seed, n, T, dk, dv, nl):
+    q, k, v = wl.random_case(seed, n, T, dk, dv, "bf16", 1.0 / np.sqrt(dk))
+    lam = wl.loglinear_weights(seed, n, T, nl)
+    return q, k, v, lam
+
+
+def _run_steps(q, k, v, lam, S, t0, t1, out_dtype):
+    """GPU steps at positions t0 .. t1 - 1; row i of q, k, v, lam is position i."""
+    torch = torch_cuda()
+    outs = []
+    for t in range(t0, t1):
+        qt, kt, vt = (dev_bf16(np.ascontiguousarray(x.bits[:, t])) for x in (q, k, v))
+        lt = torch.from_numpy(np.ascontiguousarray(lam[:, t])).cuda()
+        out = torch.empty(qt.shape[0], vt.shape[1], dtype=out_dtype, device="cuda")
+        la.recurrent_step_loglinear(qt, kt, vt, lt, S, t, out=out)
+        outs.append(host(out))
+    return np.stack(outs, axis=1)
+
+
+@pytest.mark.parametrize("n,T,dk,dv,out", [(3, 300, 64, 64, "f32"), (2, 70, 16, 256, "bf16"),
+                                           (2, 130, 128, 32, "f32")])
+def test_loglinear_step_from_zero(n, T, dk, dv, out):
+    """Steps at positions 0 .. T - 1 from zero level states give the oracle's
+    Fenwick tree recurrence, output by output, and its level states at the end
+    (merges of up to 9 levels at T = 300)."""
+    torch = torch_cuda()
+    nl = oracle.loglinear_levels(T)
+    q, k, v, lam = _step_inputs(83, n, T, dk, dv, nl)
+    log(f"loglinear step from zero n={n} T={T} dk={dk} dv={dv} out={out}")
+    S = torch.zeros(n, nl, dk, dv, dtype=torch.float32, device="cuda")
+    got = _run_steps(q, k, v, lam, S, 0, T, torch.float32 if out == "f32" else torch.bfloat16)
+    Sg = host(S)
+    for h in range(n):
+        ref, rS = oracle.loglinear_recurrent(q.exact[h], k.exact[h], v.exact[h], lam[h].astype(np.float64),
+                                             return_state=True)
+        assert_close(got[h], ref, what=f"o stream {h}")
+        assert_close(Sg[h], rS, what=f"S stream {h}")
+
+
+def test_loglinear_step_resume_deep_merge():
+    """Steps at positions 1024 .. 1063 from the oracle's level states after
+    token 1023 (position 1024 merges eleven levels into level 11), d_k = 128,
+    bf16 output, twelve levels kept."""
+    torch = torch_cuda()
+    n, T0, T1, dk, dv = 2, 1024, 1064, 128, 64
+    nl = oracle.loglinear_levels(1100)
+    q, k, v, lam = _step_inputs(84, n, T1, dk, dv, nl)
+    log(f"loglinear step resume at {T0}, levels={nl}")
+    S0, refs, rSs = [], [], []
+    for h in range(n):
+        lam_h = lam[h].astype(np.float64)
+        _, Sa = oracle.loglinear_recurrent(q.exact[h][:T0], k.exact[h][:T0], v.exact[h][:T0], lam_h[:T0],
+                                           return_state=True)
+        ref, rS = oracle.loglinear_recurrent(q.exact[h][T0:], k.exact[h][T0:], v.exact[h][T0:], lam_h[T0:],
+                                             S0=Sa, t0=T0, return_state=True)
+        S0.append(Sa)
+        refs.append(ref)
+        rSs.append(rS)
+    S = torch.from_numpy(np.stack(S0).astype(np.float32)).cuda()
+    got = _run_steps(q, k, v, lam, S, T0, T1, torch.bfloat16)
+    Sg = host(S)
+    for h in range(n):
+        assert_close(got[h], refs[h], what=f"o stream {h}")
+        assert_close(Sg[h], rSs[h], what=f"S stream {h}")
+
+
+def test_loglinear_steps_match_forward():
+    """Decode steps from zero and the chunked forward on the same inputs and
+    weights: both against the oracle's masked form, position by position
+    (the decode path and the forward path reach the same outputs)."""
+    torch = torch_cuda()
+    n, T, dk, dv = 2, 200, 64, 128
+    nl = la.loglinear_levels(T)
+    q, k, v, lam = _step_inputs(85, n, T, dk, dv, nl)
+    log("loglinear steps vs forward")
+    S = torch.zeros(n, nl, dk, dv, dtype=torch.float32, device="cuda")
+    got = _run_steps(q, k, v, lam, S, 0, T, torch.float32)
+    fwd = host(la.loglinear_forward(dev_input(q), dev_input(k), dev_input(v), torch.from_numpy(lam).cuda()))
+    for h in range(n):
+        ref = oracle.loglinear_scores_first(q.exact[h], k.exact[h], v.exact[h], lam[h].astype(np.float64))
+        assert_close(got[h], ref, what=f"steps stream {h}")
+        assert_close(fwd[h], ref, what=f"forward stream {h}")
