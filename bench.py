@@ -607,7 +607,7 @@ def run_extras(args, out):
     ms_step = med_ms(step, 20)
     n_read = 1 + bin(t_step >> 1).count("1")  # level 0 (merged into level 1) and the set bits above
     step_bytes = w3.BH * (n_read + 2) * w3.d_k * w3.d_v * 4
-    lq1, lk1, lv1 = (x.exact[0][:64] for x in wl.head_inputs(w3, 0, 64))
+    lq1, lk1, lv1 = (x.exact for x in wl.head_inputs(w3, 0, 64))
     lam1 = wl.loglinear_weights(3, 1, 64, oracle.loglinear_levels(64))[0].astype(np.float64)
     rows["next_loglinear"]["decode_step"] = {
         "states": w3.BH, "position": t_step, "levels_read": n_read, "ms": ms_step, **hbm(step_bytes, ms_step),

@@ -277,74 +277,105 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 // level 0 takes k_t^T v_t; then o = sum_l lam[l] q_t S[l].  After the step,
 // level l >= 1 is non-empty only when bit l - 1 of t is set, so the output
 // reads just those (besides level 0 and the merged level, which it forms
-// itself).  One workgroup per stream; thread t owns four value columns
-// (j4 = t % (DV / 4)) of the rows a = t / (DV / 4) + AG i through every
-// level, so every state access is a coalesced 16-byte vector and each
-// element's merge, update and output share is formed in one pass; the row
-// partial sums of o reduce through LDS.
-template <int DV>
+// itself).  One workgroup per (stream, DVS value columns): the columns of o
+// are independent, so the slices need no reduction between workgroups.
+// Thread t owns four columns (j4 = t % (DVS / 4)) of the rows
+// a = t / (DVS / 4) + AG r, r < RPT, through every level; each level's RPT
+// 16-byte loads go out together, and each element's merge, update and output
+// share are formed in one pass.  The row partial sums of o reduce through LDS.
+template <int DK, int DVS>
 __global__ __launch_bounds__(256) void loglinear_step_kernel(LogLinStepParams p) {
-    constexpr int NT = 256, J4 = DV / 4, AG = NT / J4;
+    constexpr int NT = 256, J4 = DVS / 4, AG = NT / J4;
+    constexpr int RPT = DK > AG ? DK / AG : 1;  // rows per thread (threads past DK idle)
     static_assert(J4 * AG == NT, "thread layout");
-    __shared__ float qs[256], ks[256], vs[DV], lw[LL_NLMAX];
-    __shared__ float red[AG][DV + 4];
+    __shared__ float qs[DK], ks[DK], vs[DVS], lw[LL_NLMAX];
+    __shared__ float red[AG][DVS + 4];
     const int tid = threadIdx.x;
     const int j4 = tid % J4, ag = tid / J4;
-    const int64_t st = blockIdx.x;
-    const int dk = p.dk, nl = p.n_lev;
+    const int n_sl = p.dv / DVS;
+    const int64_t st = blockIdx.x / n_sl;
+    const int col0 = (blockIdx.x % n_sl) * DVS;
+    const int dv = p.dv, nl = p.n_lev;
     const int64_t t = p.t;
-    for (int i = tid; i < dk; i += NT) {
-        qs[i] = bf2f(p.q[st * dk + i]);
-        ks[i] = bf2f(p.k[st * dk + i]);
+    for (int i = tid; i < DK; i += NT) {
+        qs[i] = bf2f(p.q[st * DK + i]);
+        ks[i] = bf2f(p.k[st * DK + i]);
     }
-    for (int i = tid; i < DV; i += NT) vs[i] = bf2f(p.v[st * DV + i]);
+    for (int i = tid; i < DVS; i += NT) vs[i] = bf2f(p.v[st * dv + col0 + i]);
     for (int i = tid; i < nl; i += NT) lw[i] = p.lam[st * nl + i];
     __syncthreads();
     // b = the lowest set bit of t (-1 at t = 0: nothing merges)
     const int b = t > 0 ? __builtin_ctzll((unsigned long long)t) : -1;
-    const int64_t lev = (int64_t)dk * DV / 4;  // float4s per level
+    const int64_t lev = (int64_t)DK * dv / 4;  // float4s per level
     float4* S = reinterpret_cast<float4*>(p.S) + st * nl * lev;
+    const bool live = ag < DK;
+    // element r of this thread: row ag + AG r, columns col0 + 4 j4 ..
+    int64_t e[RPT];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) e[r] = (int64_t)(live ? ag + AG * r : 0) * (dv / 4) + col0 / 4 + j4;
     const float4 v4 = make_float4(vs[4 * j4], vs[4 * j4 + 1], vs[4 * j4 + 2], vs[4 * j4 + 3]);
     const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
-    float4 part = zero;
-    for (int a = ag; a < dk; a += AG) {
-        const int64_t e = (int64_t)a * J4 + j4;
-        const float ka = ks[a];
-        const float4 s0 = make_float4(ka * v4.x, ka * v4.y, ka * v4.z, ka * v4.w);
-        float4 acc = make_float4(lw[0] * s0.x, lw[0] * s0.y, lw[0] * s0.z, lw[0] * s0.w);
+    auto fma4 = [](float w, const float4& x, const float4& y) {
+        return make_float4(fmaf(w, x.x, y.x), fmaf(w, x.y, y.y), fmaf(w, x.z, y.z), fmaf(w, x.w, y.w));
+    };
+    float4 s0[RPT], acc[RPT];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+        const float ka = live ? ks[ag + AG * r] : 0.f;
+        s0[r] = make_float4(ka * v4.x, ka * v4.y, ka * v4.z, ka * v4.w);
+        acc[r] = fma4(lw[0], s0[r], zero);
+    }
+    if (live) {
         if (b >= 0) {
-            float4 merged = S[e];
-            for (int l = 1; l <= b; ++l) merged = add4f(merged, S[l * lev + e]);
+            float4 merged[RPT];
+#pragma unroll
+            for (int r = 0; r < RPT; ++r) merged[r] = S[e[r]];
+            for (int l = 1; l <= b; ++l) {
+                float4 x[RPT];
+#pragma unroll
+                for (int r = 0; r < RPT; ++r) x[r] = S[l * lev + e[r]];
+#pragma unroll
+                for (int r = 0; r < RPT; ++r) merged[r] = add4f(merged[r], x[r]);
+            }
             const float w = lw[b + 1];
-            acc = make_float4(fmaf(w, merged.x, acc.x), fmaf(w, merged.y, acc.y), fmaf(w, merged.z, acc.z),
-                              fmaf(w, merged.w, acc.w));
-            S[(b + 1) * lev + e] = merged;
-            for (int l = 1; l <= b; ++l) S[l * lev + e] = zero;
+#pragma unroll
+            for (int r = 0; r < RPT; ++r) {
+                acc[r] = fma4(w, merged[r], acc[r]);
+                S[(b + 1) * lev + e[r]] = merged[r];
+            }
+            for (int l = 1; l <= b; ++l)
+#pragma unroll
+                for (int r = 0; r < RPT; ++r) S[l * lev + e[r]] = zero;
         }
         // the untouched levels that hold keys: bit l - 1 of t set, l > b + 1
         for (int l = b + 2; l < nl; ++l) {
             if (((t >> (l - 1)) & 1) == 0) continue;
-            const float4 x = S[l * lev + e];
+            float4 x[RPT];
+#pragma unroll
+            for (int r = 0; r < RPT; ++r) x[r] = S[l * lev + e[r]];
             const float w = lw[l];
-            acc = make_float4(fmaf(w, x.x, acc.x), fmaf(w, x.y, acc.y), fmaf(w, x.z, acc.z), fmaf(w, x.w, acc.w));
+#pragma unroll
+            for (int r = 0; r < RPT; ++r) acc[r] = fma4(w, x[r], acc[r]);
         }
-        S[e] = s0;
-        const float qa = qs[a];
-        part = make_float4(fmaf(qa, acc.x, part.x), fmaf(qa, acc.y, part.y), fmaf(qa, acc.z, part.z),
-                           fmaf(qa, acc.w, part.w));
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) S[e[r]] = s0[r];
     }
+    float4 part = zero;
+    if (live)
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) part = fma4(qs[ag + AG * r], acc[r], part);
     red[ag][4 * j4] = part.x;
     red[ag][4 * j4 + 1] = part.y;
     red[ag][4 * j4 + 2] = part.z;
     red[ag][4 * j4 + 3] = part.w;
     __syncthreads();
-    for (int c = tid; c < DV; c += NT) {
+    for (int c = tid; c < DVS; c += NT) {
         float sum = 0.f;
         for (int r = 0; r < AG; ++r) sum += red[r][c];
         if (p.out_f32)
-            reinterpret_cast<float*>(p.o)[st * DV + c] = sum;
+            reinterpret_cast<float*>(p.o)[st * dv + col0 + c] = sum;
         else
-            reinterpret_cast<u16*>(p.o)[st * DV + c] = f2bf(sum);
+            reinterpret_cast<u16*>(p.o)[st * dv + col0 + c] = f2bf(sum);
     }
 }
 
@@ -380,13 +411,21 @@ hipError_t run_loglinear_step(const LogLinStepParams& p, hipStream_t s) {
     // holds keys after the step (up to the bit length of t) must exist
     const int bits = p.t > 0 ? 64 - __builtin_clzll((unsigned long long)p.t) : 0;
     if (p.n_lev < bits + 1) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)p.n);
-    switch (p.dv) {
-        case 16: hipLaunchKernelGGL(loglinear_step_kernel<16>, grid, dim3(256), 0, s, p); break;
-        case 32: hipLaunchKernelGGL(loglinear_step_kernel<32>, grid, dim3(256), 0, s, p); break;
-        case 64: hipLaunchKernelGGL(loglinear_step_kernel<64>, grid, dim3(256), 0, s, p); break;
-        case 128: hipLaunchKernelGGL(loglinear_step_kernel<128>, grid, dim3(256), 0, s, p); break;
-        case 256: hipLaunchKernelGGL(loglinear_step_kernel<256>, grid, dim3(256), 0, s, p); break;
+    // value columns per workgroup: 32 (16 when there are only 16)
+    const int dvs = p.dv < 32 ? p.dv : 32;
+    if (p.dv % dvs != 0 || p.n * (p.dv / dvs) > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)(p.n * (p.dv / dvs)));
+    switch (p.dk * 1000 + dvs) {
+        case 16016: hipLaunchKernelGGL((loglinear_step_kernel<16, 16>), grid, dim3(256), 0, s, p); break;
+        case 32016: hipLaunchKernelGGL((loglinear_step_kernel<32, 16>), grid, dim3(256), 0, s, p); break;
+        case 64016: hipLaunchKernelGGL((loglinear_step_kernel<64, 16>), grid, dim3(256), 0, s, p); break;
+        case 128016: hipLaunchKernelGGL((loglinear_step_kernel<128, 16>), grid, dim3(256), 0, s, p); break;
+        case 256016: hipLaunchKernelGGL((loglinear_step_kernel<256, 16>), grid, dim3(256), 0, s, p); break;
+        case 16032: hipLaunchKernelGGL((loglinear_step_kernel<16, 32>), grid, dim3(256), 0, s, p); break;
+        case 32032: hipLaunchKernelGGL((loglinear_step_kernel<32, 32>), grid, dim3(256), 0, s, p); break;
+        case 64032: hipLaunchKernelGGL((loglinear_step_kernel<64, 32>), grid, dim3(256), 0, s, p); break;
+        case 128032: hipLaunchKernelGGL((loglinear_step_kernel<128, 32>), grid, dim3(256), 0, s, p); break;
+        case 256032: hipLaunchKernelGGL((loglinear_step_kernel<256, 32>), grid, dim3(256), 0, s, p); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

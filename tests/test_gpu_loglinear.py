@@ -144,3 +144,32 @@ def test_loglinear_steps_match_forward():
         ref = oracle.loglinear_scores_first(q.exact[h], k.exact[h], v.exact[h], lam[h].astype(np.float64))
         assert_close(got[h], ref, what=f"steps stream {h}")
         assert_close(fwd[h], ref, what=f"forward stream {h}")
+
+
+def test_loglinear_step_benchmarked_positions():
+    """The positions the benchmark's step row and the deepest merge use, at its
+    width (d_k = d_v = 128): from the oracle's level states after token 8190,
+    steps at 8191 (twelve levels above level 0 hold keys) and 8192 (levels
+    0..13 merge into level 14), fifteen levels kept."""
+    torch = torch_cuda()
+    n, T0, T1, dk, dv = 2, 8191, 8193, 128, 128
+    nl = oracle.loglinear_levels(T1)
+    assert nl == 15
+    q, k, v, lam = _step_inputs(86, n, T1, dk, dv, nl)
+    log(f"loglinear step at positions {T0}, {T0 + 1}, levels={nl}")
+    S0, refs, rSs = [], [], []
+    for h in range(n):
+        lam_h = lam[h].astype(np.float64)
+        _, Sa = oracle.loglinear_recurrent(q.exact[h][:T0], k.exact[h][:T0], v.exact[h][:T0], lam_h[:T0],
+                                           return_state=True)
+        ref, rS = oracle.loglinear_recurrent(q.exact[h][T0:], k.exact[h][T0:], v.exact[h][T0:], lam_h[T0:],
+                                             S0=Sa, t0=T0, return_state=True)
+        S0.append(Sa)
+        refs.append(ref)
+        rSs.append(rS)
+    S = torch.from_numpy(np.stack(S0).astype(np.float32)).cuda()
+    got = _run_steps(q, k, v, lam, S, T0, T1, torch.float32)
+    Sg = host(S)
+    for h in range(n):
+        assert_close(got[h], refs[h], what=f"o stream {h}")
+        assert_close(Sg[h], rSs[h], what=f"S stream {h}")
