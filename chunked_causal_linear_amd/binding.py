@@ -30,6 +30,7 @@ EXPORTS = (
     "la_recurrent_step_decay", "la_loglinear_forward", "la_loglinear_forward_workspace", "la_loglinear_levels",
     "la_chunked_forward_delta", "la_chunked_forward_delta_workspace", "la_delta_chunk_transform",
     "la_recurrent_step_delta", "la_chunked_forward_noalloc", "la_recurrent_step_loglinear",
+    "la_loglinear_prefix_levels", "la_loglinear_prefix_levels_workspace",
 )
 
 
@@ -74,6 +75,9 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.la_loglinear_levels.argtypes = [i64]
     lib.la_loglinear_levels.restype = i64
     lib.la_recurrent_step_loglinear.argtypes = [vp, vp, vp, i32, i64, i64, i64, vp, i64, i64, vp, vp, i32, vp]
+    lib.la_loglinear_prefix_levels.argtypes = [vp, vp, i32, i64, i64, i64, i64, i64, vp, vp, sz, vp]
+    lib.la_loglinear_prefix_levels_workspace.argtypes = [i32, i64, i64, i64, i64]
+    lib.la_loglinear_prefix_levels_workspace.restype = sz
     lib.la_chunked_forward_delta.argtypes = [vp, vp, vp, i32, i64, i64, i64, i64, i64, vp, vp, vp, i32, vp, vp, sz,
                                              vp]
     lib.la_chunked_forward_delta_workspace.argtypes = [i32, i64, i64, i64, i64, i64]
@@ -359,6 +363,23 @@ class LogLinearForward:
 def loglinear_forward(q, k, v, lam, C: int = 64):
     """Log-linear attention output (see la_loglinear_forward); lam [BH, L, levels] float32."""
     return LogLinearForward(q, k, v, lam, C).run()
+
+
+def loglinear_prefix_levels(k, v, n_levels: Optional[int] = None):
+    """The level states after the L tokens of k, v [BH, L, d] (bf16): what decode
+    steps at positions 0 .. L - 1 from zero states leave (la_loglinear_prefix_levels).
+    Returns S [BH, n_levels, d_k, d_v] float32; n_levels defaults to
+    loglinear_levels(L) (pass more to continue decoding past a power of two)."""
+    torch = _torch()
+    BH, L, d_k = k.shape
+    d_v = v.shape[-1]
+    n_lev = loglinear_levels(L) if n_levels is None else int(n_levels)
+    S = torch.empty(BH, n_lev, d_k, d_v, dtype=torch.float32, device=k.device)
+    ws = int(lib().la_loglinear_prefix_levels_workspace(_dtype_code(k), BH, L, d_k, d_v))
+    work = torch.empty(max(ws, 1), dtype=torch.uint8, device=k.device)
+    _check(lib().la_loglinear_prefix_levels(_dev(k, "k"), _dev(v, "v"), _dtype_code(k), BH, L, d_k, d_v, n_lev,
+                                            _dev(S, "S"), work.data_ptr(), ws, _stream_ptr()))
+    return S
 
 
 def recurrent_step_loglinear(q, k, v, lam, S, t: int, out=None):

@@ -912,6 +912,60 @@ static la_status loglinear_check(la_dtype in_dt, int64_t BH, int64_t L, int64_t 
 
 int64_t la_loglinear_levels(int64_t L) { return L < 1 ? 0 : loglinear_levels_of(L); }
 
+static la_status loglinear_prefix_check(la_dtype in_dt, int64_t BH, int64_t L, int64_t d_k, int64_t d_v,
+                                        size_t* ws) {
+    if (BH < 1 || L < 1 || d_k < 1 || d_v < 1) return fail(LA_ERR_INVALID_ARG, "sizes must be positive");
+    if (in_dt != LA_BF16) return fail(LA_ERR_UNSUPPORTED, "the log-linear prefix levels take LA_BF16 inputs");
+    if (!pow2_in(d_k, 16, 256) || !pow2_in(d_v, 16, 256))
+        return fail(LA_ERR_UNSUPPORTED, "d_k=%lld, d_v=%lld: powers of two in 16..256", (long long)d_k,
+                    (long long)d_v);
+    if (loglinear_levels_of(L) > 40) return fail(LA_ERR_UNSUPPORTED, "sequence too long");
+    // the states of the whole chunks of 64 rows before the last row's chunk
+    *ws = align256((size_t)BH * (size_t)((L - 1) >> 6) * (size_t)(d_k * d_v) * 4);
+    return LA_OK;
+}
+
+size_t la_loglinear_prefix_levels_workspace(la_dtype in_dt, int64_t BH, int64_t L, int64_t d_k, int64_t d_v) {
+    size_t ws = 0;
+    if (loglinear_prefix_check(in_dt, BH, L, d_k, d_v, &ws) != LA_OK) return 0;
+    return ws;
+}
+
+la_status la_loglinear_prefix_levels(const void* k, const void* v, la_dtype in_dt, int64_t BH, int64_t L,
+                                     int64_t d_k, int64_t d_v, int64_t n_levels, float* S, void* workspace,
+                                     size_t ws_bytes, la_stream_t stream) {
+    g_last_error[0] = 0;
+    if (k == nullptr || v == nullptr || S == nullptr) return fail(LA_ERR_INVALID_ARG, "k, v and S must not be NULL");
+    size_t ws = 0;
+    la_status st = loglinear_prefix_check(in_dt, BH, L, d_k, d_v, &ws);
+    if (st != LA_OK) return st;
+    if (n_levels < loglinear_levels_of(L) || n_levels > 40)
+        return fail(LA_ERR_INVALID_ARG, "n_levels=%lld: %lld tokens need %lld..40", (long long)n_levels,
+                    (long long)L, (long long)loglinear_levels_of(L));
+    if (ws > 0 && (workspace == nullptr || ws_bytes < ws))
+        return fail(LA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", ws, workspace ? ws_bytes : (size_t)0);
+    hipStream_t s = (hipStream_t)stream;
+    const int64_t n_chunks = (L - 1) >> 6;
+    if (n_chunks > 0x7FFFFFFFLL) return fail(LA_ERR_UNSUPPORTED, "too many chunks");
+    if (n_chunks > 0) {
+        st = chunk_states_impl(k, v, false, BH, L, d_k, d_v, 64, (int)n_chunks, (int)n_chunks, workspace, nullptr,
+                               0, 1.0f, s);
+        if (st != LA_OK) return st;
+    }
+    la::LogLinPrefixParams p{};
+    p.k = static_cast<const unsigned short*>(k);
+    p.v = static_cast<const unsigned short*>(v);
+    p.chunks = n_chunks > 0 ? static_cast<const float*>(workspace) : nullptr;
+    p.S = S;
+    p.BH = BH;
+    p.L = L;
+    p.dk = (int)d_k;
+    p.dv = (int)d_v;
+    p.n_lev = (int)n_levels;
+    p.n_chunks = (int)n_chunks;
+    return hip_status(la::run_loglinear_prefix_levels(p, s), "log-linear prefix levels launch");
+}
+
 la_status la_recurrent_step_loglinear(const void* q, const void* k, const void* v, la_dtype in_dt, int64_t n_states,
                                       int64_t d_k, int64_t d_v, const float* lam, int64_t n_levels, int64_t t,
                                       float* S, void* o, la_dtype out_dt, la_stream_t stream) {

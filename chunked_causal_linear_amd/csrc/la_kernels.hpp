@@ -255,6 +255,18 @@ struct LogLinStepParams {
 };
 hipError_t run_loglinear_step(const LogLinStepParams& p, hipStream_t s);
 
+// The level states a stream holds after its token L - 1 (what L decode steps
+// from zero leave), from k, v and the states of its whole 64-row chunks.
+struct LogLinPrefixParams {
+    const unsigned short* k;  // [BH, L, dk] bf16
+    const unsigned short* v;  // [BH, L, dv] bf16
+    const float* chunks;      // [BH, n_chunks, dk, dv] states of the chunks before the last one (or null)
+    float* S;                 // [BH, n_lev, dk, dv]
+    int64_t BH, L;
+    int dk, dv, n_lev, n_chunks;
+};
+hipError_t run_loglinear_prefix_levels(const LogLinPrefixParams& p, hipStream_t s);
+
 hipError_t run_chunked_fwd_i8(const FwdParamsI8& p, int DK, int DVT, int T, int64_t grid, hipStream_t s);
 hipError_t run_chunk_states_i8(const StatesParamsI8& p, int DK, int DVT, int64_t grid, hipStream_t s);
 // Streaming phase 1 (la_states_pipe.hip): d_k = DK in {64, 128, 256}, value

@@ -21,7 +21,9 @@
 //     O_m.  Outputs come out transposed (a lane holds four consecutive columns
 //     of one row) and are stored as 8-byte pieces.
 //   * loglinear_step_kernel: one decode step, the Fenwick tree recurrence over
-//     each stream's level states (below).
+//     each stream's level states (below);
+//   * loglinear_prefix_levels_kernel: the level states after a prefix, for a
+//     decode that follows a forward.
 #include "la_common.hpp"
 #include "la_kernels.hpp"
 
@@ -379,6 +381,57 @@ __global__ __launch_bounds__(256) void loglinear_step_kernel(LogLinStepParams p)
     }
 }
 
+// The level states after token T = L - 1: level 0 = k_T^T v_T; level l >= 1
+// = the sum of k_s^T v_s over its bucket [h - 2^(l-1), h), h = T with its bits
+// below l - 1 cleared, when bit l - 1 of T is set, else zero.  A bucket of
+// 64 rows or more (l >= 7) is a run of whole chunks before T's chunk: the sum
+// of their states, in chunk order; the smaller ones lie in T's chunk and are
+// summed from the rows.  One workgroup per (head, level, 1024 float4s of the
+// state); a thread owns four float4s.
+__global__ __launch_bounds__(256) void loglinear_prefix_levels_kernel(LogLinPrefixParams p) {
+    const int64_t E4 = (int64_t)p.dk * p.dv / 4;
+    const int64_t nblk = (E4 + 1023) / 1024;
+    const int64_t blk = blockIdx.x % nblk;
+    const int l = (int)((blockIdx.x / nblk) % p.n_lev);
+    const int64_t bh = blockIdx.x / (nblk * p.n_lev);
+    const int64_t T = p.L - 1;
+    const int dv4 = p.dv / 4;
+    const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
+    float4* out = reinterpret_cast<float4*>(p.S) + (bh * p.n_lev + l) * E4;
+    const bool present = l == 0 || ((T >> (l - 1)) & 1);
+    int64_t r0 = T, r1 = T + 1;  // level 0: row T
+    if (l > 0) {
+        const int64_t h = (T >> (l - 1)) << (l - 1);
+        r0 = h - ((int64_t)1 << (l - 1));
+        r1 = h;
+    }
+    const u16* kh = p.k + bh * p.L * p.dk;
+    const u16* vh = p.v + bh * p.L * p.dv;
+    for (int i = 0; i < 4; ++i) {
+        const int64_t e = blk * 1024 + i * 256 + threadIdx.x;
+        if (e >= E4) break;
+        float4 sum = zero;
+        if (present) {
+            if (r1 - r0 >= 64) {
+                const float4* ch = reinterpret_cast<const float4*>(p.chunks) + bh * p.n_chunks * E4 + e;
+#pragma unroll 8
+                for (int64_t c = r0 / 64; c < r1 / 64; ++c) sum = add4f(sum, ch[c * E4]);
+            } else {
+                const int a = (int)(e / dv4), c4 = (int)(e % dv4) * 4;
+                for (int64_t r = r0; r < r1; ++r) {
+                    const float ka = bf2f(kh[r * p.dk + a]);
+                    const u16* vr = vh + r * p.dv + c4;
+                    sum.x = fmaf(ka, bf2f(vr[0]), sum.x);
+                    sum.y = fmaf(ka, bf2f(vr[1]), sum.y);
+                    sum.z = fmaf(ka, bf2f(vr[2]), sum.z);
+                    sum.w = fmaf(ka, bf2f(vr[3]), sum.w);
+                }
+            }
+        }
+        out[e] = sum;
+    }
+}
+
 }  // namespace
 
 hipError_t run_loglinear_pyramid(const float* S, float* T, int64_t BH, int N, int n_pyr, int64_t E, hipStream_t s) {
@@ -428,6 +481,22 @@ hipError_t run_loglinear_step(const LogLinStepParams& p, hipStream_t s) {
         case 256032: hipLaunchKernelGGL((loglinear_step_kernel<256, 32>), grid, dim3(256), 0, s, p); break;
         default: return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+}  // namespace la
+
+namespace la {
+
+hipError_t run_loglinear_prefix_levels(const LogLinPrefixParams& p, hipStream_t s) {
+    if (p.BH < 1 || p.L < 1 || p.dk < 1 || p.dv < 4 || p.dv % 4 != 0 || p.n_lev < 1 || p.n_lev > LL_NLMAX)
+        return hipErrorInvalidValue;
+    const int64_t T = p.L - 1;
+    if ((T >> 6) > p.n_chunks || ((T >> 6) > 0 && p.chunks == nullptr)) return hipErrorInvalidValue;
+    const int64_t E4 = (int64_t)p.dk * p.dv / 4;
+    const int64_t grid = p.BH * p.n_lev * ((E4 + 1023) / 1024);
+    if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(loglinear_prefix_levels_kernel, dim3((unsigned)grid), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 

@@ -360,6 +360,30 @@ la_status la_recurrent_step_loglinear(const void* q, const void* k, const void* 
                                       la_stream_t stream);
 
 /*
+ * The level states of log-linear attention after a prefix (for a decode that
+ * follows la_loglinear_forward): for each head, the states S[l] that decode
+ * steps at positions 0 .. L - 1 from zero states would leave, computed
+ * directly from k and v: level 0 = k_T^T v_T (T = L - 1); level l >= 1 = the
+ * sum of k_s^T v_s over its Fenwick bucket [h - 2^(l-1), h), h = T with its
+ * bits below l - 1 cleared, when bit l - 1 of T is set, else zero (slide deck
+ * "Log-Linear Attention": the partition of the past and the per-level state).
+ *
+ *   k [BH, L, d_k], v [BH, L, d_v]: LA_BF16; d_k and d_v powers of two in 16..256.
+ *   n_levels  levels per head in S: at least la_loglinear_levels(L), at most 40
+ *        (la_loglinear_levels(T1) lets decode steps continue up to position T1 - 1).
+ *   S    [BH, n_levels, d_k, d_v] float32 (device): written (every level).
+ *   workspace  la_loglinear_prefix_levels_workspace(...) bytes: the states of the
+ *        whole 64-row chunks before the last row's chunk (0 when L <= 64).
+ * Errors: LA_ERR_INVALID_ARG (NULL pointer, non-positive size, n_levels out of
+ * range), LA_ERR_UNSUPPORTED (other types or widths), LA_ERR_WORKSPACE; nothing
+ * is launched on an error.
+ */
+la_status la_loglinear_prefix_levels(const void* k, const void* v, la_dtype in_dt, int64_t BH, int64_t L,
+                                     int64_t d_k, int64_t d_v, int64_t n_levels, float* S, void* workspace,
+                                     size_t ws_bytes, la_stream_t stream);
+size_t la_loglinear_prefix_levels_workspace(la_dtype in_dt, int64_t BH, int64_t L, int64_t d_k, int64_t d_v);
+
+/*
  * The delta rule and its gated form (page "Kimi K3 と Qwen 3.8 の Attention 機構
  * 比較分析" (news.ainew.jp): section 3.1, equation (14): before writing, look up
  * what the current key maps to in the state, erase that old prediction along

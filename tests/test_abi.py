@@ -341,3 +341,28 @@ def test_delta_entry_point_errors():
     assert step(d_v=512) == b.LA_ERR_UNSUPPORTED
     assert step(out_dt=b.LA_I32) == b.LA_ERR_UNSUPPORTED
     assert step(in_dt=b.LA_F32) == b.LA_ERR_UNSUPPORTED
+
+
+def test_loglinear_prefix_levels_entry_point_errors():
+    """The log-linear prefix levels: workspace (the states of the whole 64-row
+    chunks before the last row's chunk) and argument checks before any launch."""
+    lib = la.lib()
+    assert lib.la_loglinear_prefix_levels_workspace(b.LA_BF16, 2, 64, 64, 64) == 0  # one chunk
+    assert lib.la_loglinear_prefix_levels_workspace(b.LA_BF16, 2, 65, 64, 64) == 2 * 1 * 64 * 64 * 4
+    assert lib.la_loglinear_prefix_levels_workspace(b.LA_BF16, 128, 8192, 128, 128) == 128 * 127 * 128 * 128 * 4
+    assert lib.la_loglinear_prefix_levels_workspace(b.LA_I8, 2, 100, 64, 64) == 0  # unsupported
+
+    def call(**kw):
+        a = dict(k=FAKE, v=FAKE, in_dt=b.LA_BF16, BH=2, L=1000, d_k=64, d_v=64, n_lev=lib.la_loglinear_levels(1000),
+                 S=FAKE, ws=None, ws_bytes=0)
+        a.update(kw)
+        return lib.la_loglinear_prefix_levels(a["k"], a["v"], a["in_dt"], a["BH"], a["L"], a["d_k"], a["d_v"],
+                                              a["n_lev"], a["S"], a["ws"], a["ws_bytes"], None)
+    for name in ("k", "v", "S"):
+        assert call(**{name: None}) == b.LA_ERR_INVALID_ARG, name
+    assert call(L=0) == b.LA_ERR_INVALID_ARG
+    assert call(n_lev=lib.la_loglinear_levels(1000) - 1) == b.LA_ERR_INVALID_ARG
+    assert call(n_lev=41) == b.LA_ERR_INVALID_ARG
+    assert call(in_dt=b.LA_I8) == b.LA_ERR_UNSUPPORTED
+    assert call(d_k=48) == b.LA_ERR_UNSUPPORTED
+    assert call() == b.LA_ERR_WORKSPACE

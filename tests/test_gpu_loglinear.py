@@ -173,3 +173,42 @@ def test_loglinear_step_benchmarked_positions():
     for h in range(n):
         assert_close(got[h], refs[h], what=f"o stream {h}")
         assert_close(Sg[h], rSs[h], what=f"S stream {h}")
+
+
+
+@pytest.mark.parametrize("BH,L,dk,dv", [(2, 1, 64, 64), (2, 63, 64, 64), (2, 64, 64, 64), (2, 65, 64, 64),
+                                        (2, 1000, 64, 128), (1, 4133, 128, 128), (2, 300, 16, 256)])
+def test_loglinear_prefix_levels(BH, L, dk, dv):
+    """The level states after a prefix of L tokens (la_loglinear_prefix_levels)
+    against the oracle's Fenwick recurrence run over the prefix: one token,
+    a chunk and one row either side, buckets of whole chunks (up to 2048 rows at
+    L = 4133), one level more than the prefix needs."""
+    torch = torch_cuda()
+    q, k, v = wl.random_case(87, BH, L, dk, dv, "bf16", 1.0 / np.sqrt(dk))
+    nl = oracle.loglinear_levels(L) + 1
+    lam = np.ones((L, nl))
+    log(f"loglinear prefix levels BH={BH} L={L} dk={dk} dv={dv} levels={nl}")
+    S = host(la.loglinear_prefix_levels(dev_input(k), dev_input(v), nl))
+    for h in range(BH):
+        _, rS = oracle.loglinear_recurrent(q.exact[h], k.exact[h], v.exact[h], lam, return_state=True)
+        assert_close(S[h], rS, what=f"levels head {h}")
+
+
+def test_loglinear_prefill_then_decode():
+    """A forward over the first 1500 tokens, the level states at its end, then
+    decode steps at positions 1500 .. 1539: every output against the oracle's
+    masked form over the whole sequence."""
+    torch = torch_cuda()
+    n, T0, T1, dk, dv = 2, 1500, 1540, 128, 64
+    nl = oracle.loglinear_levels(T1)
+    q, k, v, lam = _step_inputs(88, n, T1, dk, dv, nl)
+    log(f"loglinear prefill {T0} then decode to {T1}")
+    qp, kp, vp = (dev_bf16(np.ascontiguousarray(x.bits[:, :T0])) for x in (q, k, v))
+    lam_p = torch.from_numpy(np.ascontiguousarray(lam[:, :T0, :oracle.loglinear_levels(T0)])).cuda()
+    o_pre = host(la.loglinear_forward(qp, kp, vp, lam_p))
+    S = la.loglinear_prefix_levels(kp, vp, nl)
+    got = _run_steps(q, k, v, lam, S, T0, T1, torch.float32)
+    for h in range(n):
+        ref = oracle.loglinear_scores_first(q.exact[h], k.exact[h], v.exact[h], lam[h].astype(np.float64))
+        assert_close(o_pre[h], ref[:T0], what=f"prefill head {h}")
+        assert_close(got[h], ref[T0:], what=f"decode head {h}")
