@@ -614,6 +614,14 @@ def run_extras(args, out):
         "bytes": step_bytes,
         "oracle_s_per_state_step": _oracle_time(lambda: oracle.loglinear_recurrent(lq1, lk1, lv1, lam1)) / 64,
         "oracle_sample": "oracle.loglinear_recurrent over 64 positions of one head (d = 128)"}
+    # the level states after the whole sequence (a prefill for the decode)
+    ms_pre = med_ms(lambda: la.loglinear_prefix_levels(kd, vd, nl), 10)
+    n_ch = (w3.L - 1) // 64
+    pre_bytes = (w3.BH * w3.L * (w3.d_k + w3.d_v) * 2 + 2 * w3.BH * n_ch * w3.d_k * w3.d_v * 4
+                 + w3.BH * nl * w3.d_k * w3.d_v * 4)
+    rows["next_loglinear"]["prefix_levels"] = {
+        "heads": w3.BH, "L": w3.L, "levels": nl, "ms": ms_pre, **hbm(pre_bytes, ms_pre), "bytes": pre_bytes,
+        "note": "k, v read by phase 1 (chunks of 64), chunk states written and read once, the levels written"}
     del f, qd, kd, vd, lamd, S_ll
     torch.cuda.empty_cache()
     # ---- next: the delta rule and its gated form at the headline shape (chunks of 64)
