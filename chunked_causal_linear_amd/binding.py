@@ -30,7 +30,7 @@ EXPORTS = (
     "la_recurrent_step_decay", "la_loglinear_forward", "la_loglinear_forward_workspace", "la_loglinear_levels",
     "la_chunked_forward_delta", "la_chunked_forward_delta_workspace", "la_delta_chunk_transform",
     "la_recurrent_step_delta", "la_chunked_forward_noalloc", "la_recurrent_step_loglinear",
-    "la_loglinear_prefix_levels", "la_loglinear_prefix_levels_workspace",
+    "la_loglinear_prefix_levels", "la_loglinear_prefix_levels_workspace", "la_recurrent_step_i8",
 )
 
 
@@ -76,6 +76,7 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.la_loglinear_levels.restype = i64
     lib.la_recurrent_step_loglinear.argtypes = [vp, vp, vp, i32, i64, i64, i64, vp, i64, i64, vp, vp, i32, vp]
     lib.la_loglinear_prefix_levels.argtypes = [vp, vp, i32, i64, i64, i64, i64, i64, vp, vp, sz, vp]
+    lib.la_recurrent_step_i8.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, vp]
     lib.la_loglinear_prefix_levels_workspace.argtypes = [i32, i64, i64, i64, i64]
     lib.la_loglinear_prefix_levels_workspace.restype = sz
     lib.la_chunked_forward_delta.argtypes = [vp, vp, vp, i32, i64, i64, i64, i64, i64, vp, vp, vp, i32, vp, vp, sz,
@@ -363,6 +364,24 @@ class LogLinearForward:
 def loglinear_forward(q, k, v, lam, C: int = 64):
     """Log-linear attention output (see la_loglinear_forward); lam [BH, L, levels] float32."""
     return LogLinearForward(q, k, v, lam, C).run()
+
+
+def recurrent_step_i8(q, k, v, S, out=None):
+    """One exact int8 decode step (la_recurrent_step_i8) over n states: q, k [n, d_k],
+    v [n, d_v] int8; S [n, d_k, d_v] int32 updates in place; returns o [n, d_v] int32."""
+    torch = _torch()
+    n, d_k = q.shape
+    d_v = v.shape[-1]
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.int8:
+            raise ValueError(f"{name} must be int8")
+    if S.dtype != torch.int32 or tuple(S.shape) != (n, d_k, d_v):
+        raise ValueError(f"S must be int32 {(n, d_k, d_v)}")
+    if out is None:
+        out = torch.empty(n, d_v, dtype=torch.int32, device=q.device)
+    _check(lib().la_recurrent_step_i8(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), n, d_k, d_v, _dev(S, "S"),
+                                      _dev(out, "o"), _stream_ptr()))
+    return out
 
 
 def loglinear_prefix_levels(k, v, n_levels: Optional[int] = None):

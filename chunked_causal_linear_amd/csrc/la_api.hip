@@ -1113,6 +1113,29 @@ la_status la_recurrent_step(const void* q, const void* k, const void* v, la_dtyp
                       stream);
 }
 
+la_status la_recurrent_step_i8(const void* q, const void* k, const void* v, int64_t n_states, int64_t d_k,
+                               int64_t d_v, int32_t* S, int32_t* o, la_stream_t stream) {
+    g_last_error[0] = 0;
+    if (q == nullptr || k == nullptr || v == nullptr || S == nullptr || o == nullptr)
+        return fail(LA_ERR_INVALID_ARG, "q, k, v, S and o must not be NULL");
+    if (n_states < 1 || d_k < 1 || d_v < 1) return fail(LA_ERR_INVALID_ARG, "sizes must be positive");
+    if (!pow2_in(d_k, 16, 256) || !pow2_in(d_v, 16, 256))
+        return fail(LA_ERR_UNSUPPORTED, "d_k=%lld, d_v=%lld: powers of two in 16..256", (long long)d_k,
+                    (long long)d_v);
+    if (n_states > 0x7FFFFFFFLL) return fail(LA_ERR_UNSUPPORTED, "too many states");
+    if ((reinterpret_cast<uintptr_t>(S) & 15) != 0) return fail(LA_ERR_INVALID_ARG, "S must be 16-byte aligned");
+    la::DecodeParamsI8 p{};
+    p.q = static_cast<const signed char*>(q);
+    p.k = static_cast<const signed char*>(k);
+    p.v = static_cast<const signed char*>(v);
+    p.S = S;
+    p.o = o;
+    p.n = n_states;
+    p.dk = (int)d_k;
+    p.dv = (int)d_v;
+    return hip_status(la::run_recurrent_step_i8(p, (hipStream_t)stream), "int8 step launch");
+}
+
 la_status la_recurrent_step_decay(const void* q, const void* k, const void* v, la_dtype in_dt, int64_t n_states,
                                   int64_t d_in, int64_t d_v, la_fmap f, const void* W, int64_t m, float in_scale,
                                   int normalize, float gamma, float* S, float* z, void* o, la_dtype out_dt,

@@ -177,3 +177,73 @@ hipError_t run_recurrent_step(const DecodeParams& p, hipStream_t s) {
 }
 
 }  // namespace la
+
+namespace la {
+
+// Exact int8 decode step (the int8 path of the forward, one token): S += k^T v
+// and o = q S, every product and sum in wrapping 32-bit arithmetic, so the
+// results are exact modulo 2^32 and therefore exact whenever they fit int32 -
+// the int8 forward's convention.  One workgroup per state; thread t owns four
+// value columns (j4 = t % (DV / 4)) of the rows t / (DV / 4) + AG i, so every
+// state access is a 16-byte vector; the row partial sums of o reduce through
+// LDS.
+template <int DV>
+__global__ __launch_bounds__(256) void recurrent_step_i8_kernel(DecodeParamsI8 p) {
+    constexpr int NT = 256, J4 = DV / 4, AG = NT / J4;
+    static_assert(J4 * AG == NT, "thread layout");
+    __shared__ int qs[256], ks[256], vs[DV];
+    __shared__ unsigned red[AG][DV + 4];
+    const int tid = threadIdx.x;
+    const int j4 = tid % J4, ag = tid / J4;
+    const int64_t st = blockIdx.x;
+    const int dk = p.dk;
+    for (int i = tid; i < dk; i += NT) {
+        qs[i] = p.q[st * dk + i];
+        ks[i] = p.k[st * dk + i];
+    }
+    for (int i = tid; i < DV; i += NT) vs[i] = p.v[st * DV + i];
+    __syncthreads();
+    const unsigned v0 = (unsigned)vs[4 * j4], v1 = (unsigned)vs[4 * j4 + 1], v2 = (unsigned)vs[4 * j4 + 2],
+                   v3 = (unsigned)vs[4 * j4 + 3];
+    uint4* S = reinterpret_cast<uint4*>(p.S) + st * (int64_t)dk * J4;
+    uint4 part = make_uint4(0u, 0u, 0u, 0u);
+    for (int a = ag; a < dk; a += AG) {
+        uint4 x = S[(int64_t)a * J4 + j4];
+        const unsigned ka = (unsigned)ks[a], qa = (unsigned)qs[a];
+        x.x += ka * v0;
+        x.y += ka * v1;
+        x.z += ka * v2;
+        x.w += ka * v3;
+        S[(int64_t)a * J4 + j4] = x;
+        part.x += qa * x.x;
+        part.y += qa * x.y;
+        part.z += qa * x.z;
+        part.w += qa * x.w;
+    }
+    red[ag][4 * j4] = part.x;
+    red[ag][4 * j4 + 1] = part.y;
+    red[ag][4 * j4 + 2] = part.z;
+    red[ag][4 * j4 + 3] = part.w;
+    __syncthreads();
+    for (int c = tid; c < DV; c += NT) {
+        unsigned sum = 0u;
+        for (int r = 0; r < AG; ++r) sum += red[r][c];
+        p.o[st * DV + c] = (int)sum;
+    }
+}
+
+hipError_t run_recurrent_step_i8(const DecodeParamsI8& p, hipStream_t s) {
+    if (p.n < 1 || p.n > 0x7FFFFFFFLL || p.dk < 1 || p.dk > 256) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)p.n);
+    switch (p.dv) {
+        case 16: hipLaunchKernelGGL(recurrent_step_i8_kernel<16>, grid, dim3(256), 0, s, p); break;
+        case 32: hipLaunchKernelGGL(recurrent_step_i8_kernel<32>, grid, dim3(256), 0, s, p); break;
+        case 64: hipLaunchKernelGGL(recurrent_step_i8_kernel<64>, grid, dim3(256), 0, s, p); break;
+        case 128: hipLaunchKernelGGL(recurrent_step_i8_kernel<128>, grid, dim3(256), 0, s, p); break;
+        case 256: hipLaunchKernelGGL(recurrent_step_i8_kernel<256>, grid, dim3(256), 0, s, p); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace la

@@ -277,4 +277,16 @@ hipError_t run_state_scan(const ScanParams& p, int64_t BH, hipStream_t s);
 hipError_t run_feature_map(const FmapParams& p, hipStream_t s);
 hipError_t run_recurrent_step(const DecodeParams& p, hipStream_t s);
 
+// One exact int8 decode step: S += k^T v, o = q S in wrapping int32.
+struct DecodeParamsI8 {
+    const signed char* q;  // [n, dk]
+    const signed char* k;  // [n, dk]
+    const signed char* v;  // [n, dv]
+    int* S;                // [n, dk, dv]
+    int* o;                // [n, dv]
+    int64_t n;
+    int dk, dv;
+};
+hipError_t run_recurrent_step_i8(const DecodeParamsI8& p, hipStream_t s);
+
 }  // namespace la

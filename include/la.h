@@ -248,6 +248,23 @@ la_status la_recurrent_step(const void* q, const void* k, const void* v, la_dtyp
                             float* z, void* o, la_dtype out_dt, la_stream_t stream);
 
 /*
+ * The decode step on the exact int8 path (the int8 forward's arithmetic, one
+ * token; the RNN view of the linear-attention page and the token-by-token form
+ * of the chunking page, section ②): S += k^T v, then o = q S.  Identity map,
+ * no normaliser.  Every product and sum is taken in wrapping 32-bit
+ * arithmetic: exact modulo 2^32, hence exact whenever the true values fit
+ * int32; steps after an int8 forward's final state continue it exactly.
+ *
+ *   q, k [n_states, d_k], v [n_states, d_v]: int8; d_k, d_v powers of two in 16..256.
+ *   S    [n_states, d_k, d_v] int32, 16-byte aligned, read and updated in place.
+ *   o    [n_states, d_v] int32.
+ * Errors: LA_ERR_INVALID_ARG (NULL pointer, non-positive size, S not 16-byte aligned),
+ * LA_ERR_UNSUPPORTED (other widths); nothing is launched on an error.
+ */
+la_status la_recurrent_step_i8(const void* q, const void* k, const void* v, int64_t n_states, int64_t d_k,
+                               int64_t d_v, int32_t* S, int32_t* o, la_stream_t stream);
+
+/*
  * The decayed recurrence (Retention): S_t = gamma S_{t-1} + phi(k_t) v_t^T and,
  * as read here, z_t = gamma z_{t-1} + phi(k_t), with 0 < gamma <= 1 shared by
  * every head; the output still reads y_t = phi(q_t)^T S_t [/ phi(q_t)^T z_t]

@@ -366,3 +366,20 @@ def test_loglinear_prefix_levels_entry_point_errors():
     assert call(in_dt=b.LA_I8) == b.LA_ERR_UNSUPPORTED
     assert call(d_k=48) == b.LA_ERR_UNSUPPORTED
     assert call() == b.LA_ERR_WORKSPACE
+
+
+def test_int8_step_entry_point_errors():
+    """The exact int8 decode step: NULL pointers, sizes, widths and a misaligned
+    state are rejected before any launch."""
+    lib = la.lib()
+
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, n=3, d_k=16, d_v=16, S=FAKE, o=FAKE)
+        a.update(kw)
+        return lib.la_recurrent_step_i8(a["q"], a["k"], a["v"], a["n"], a["d_k"], a["d_v"], a["S"], a["o"], None)
+    for name in ("q", "k", "v", "S", "o"):
+        assert call(**{name: None}) == b.LA_ERR_INVALID_ARG, name
+    assert call(n=0) == b.LA_ERR_INVALID_ARG
+    assert call(S=0x1004) == b.LA_ERR_INVALID_ARG
+    assert call(d_k=24) == b.LA_ERR_UNSUPPORTED
+    assert call(d_v=512) == b.LA_ERR_UNSUPPORTED

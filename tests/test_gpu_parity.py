@@ -11,7 +11,7 @@ import pytest
 import chunked_causal_linear_amd as la
 import oracle
 import workloads as wl
-from tests.gpu_helpers import assert_close, assert_exact, dev_input, host, log, torch_cuda
+from tests.gpu_helpers import assert_close, assert_exact, dev_i8, dev_input, host, log, torch_cuda
 
 pytestmark = pytest.mark.gpu
 
@@ -91,6 +91,28 @@ def test_int8_phases():
         assert_exact(host(Sf), np.stack([r[1] for r in refP]), "scan total")
         assert_exact(host(z), np.stack([r[0] for r in refz]), "scan z")
         assert_exact(host(zf), np.stack([r[1] for r in refz]), "scan z total")
+
+
+@pytest.mark.parametrize("dk,dv,L1", [(16, 16, 1), (64, 32, 137), (128, 128, 64), (256, 64, 199)])
+def test_int8_forward_then_steps_exact(dk, dv, L1):
+    """Resume on the exact int8 path: the int8 forward over the first L1 tokens,
+    then int8 decode steps (la_recurrent_step_i8) from its final state, give the
+    causal form's outputs for all 200 tokens and its final state, bit for bit."""
+    torch = torch_cuda()
+    BH, L = 3, 200
+    q, k, v = _case(5, BH, L, dk, dv, "i8")
+    log(f"int8 forward {L1} then steps to {L}, dk={dk} dv={dv}")
+    first = [dev_i8(np.ascontiguousarray(x.bits[:, :L1])) for x in (q, k, v)]
+    o1, S, _ = la.chunked_forward(*first, 64, return_state=True)
+    outs = []
+    for t in range(L1, L):
+        qt, kt, vt = (dev_i8(np.ascontiguousarray(x.bits[:, t])) for x in (q, k, v))
+        outs.append(host(la.recurrent_step_i8(qt, kt, vt, S)))
+    for h in range(BH):
+        ref = oracle.causal_scores_first(q.exact[h], k.exact[h], v.exact[h])
+        assert_exact(host(o1)[h], ref[:L1], f"forward head {h}")
+        assert_exact(np.stack([o[h] for o in outs]), ref[L1:], f"steps head {h}")
+        assert_exact(host(S)[h], oracle.final_state(k.exact[h], v.exact[h])[0], f"final state head {h}")
 
 
 # ---------------------------------------------------------------------------
