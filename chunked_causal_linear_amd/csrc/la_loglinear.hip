@@ -386,11 +386,11 @@ __global__ __launch_bounds__(256) void loglinear_step_kernel(LogLinStepParams p)
 // below l - 1 cleared, when bit l - 1 of T is set, else zero.  A bucket of
 // 64 rows or more (l >= 7) is a run of whole chunks before T's chunk: the sum
 // of their states, in chunk order; the smaller ones lie in T's chunk and are
-// summed from the rows.  One workgroup per (head, level, 1024 float4s of the
-// state); a thread owns four float4s.
+// summed from the rows.  One workgroup per (head, level, 256 float4s of the
+// state); a thread owns one float4 and keeps sixteen chunk loads in flight.
 __global__ __launch_bounds__(256) void loglinear_prefix_levels_kernel(LogLinPrefixParams p) {
     const int64_t E4 = (int64_t)p.dk * p.dv / 4;
-    const int64_t nblk = (E4 + 1023) / 1024;
+    const int64_t nblk = (E4 + 255) / 256;
     const int64_t blk = blockIdx.x % nblk;
     const int l = (int)((blockIdx.x / nblk) % p.n_lev);
     const int64_t bh = blockIdx.x / (nblk * p.n_lev);
@@ -407,29 +407,27 @@ __global__ __launch_bounds__(256) void loglinear_prefix_levels_kernel(LogLinPref
     }
     const u16* kh = p.k + bh * p.L * p.dk;
     const u16* vh = p.v + bh * p.L * p.dv;
-    for (int i = 0; i < 4; ++i) {
-        const int64_t e = blk * 1024 + i * 256 + threadIdx.x;
-        if (e >= E4) break;
-        float4 sum = zero;
-        if (present) {
-            if (r1 - r0 >= 64) {
-                const float4* ch = reinterpret_cast<const float4*>(p.chunks) + bh * p.n_chunks * E4 + e;
-#pragma unroll 8
-                for (int64_t c = r0 / 64; c < r1 / 64; ++c) sum = add4f(sum, ch[c * E4]);
-            } else {
-                const int a = (int)(e / dv4), c4 = (int)(e % dv4) * 4;
-                for (int64_t r = r0; r < r1; ++r) {
-                    const float ka = bf2f(kh[r * p.dk + a]);
-                    const u16* vr = vh + r * p.dv + c4;
-                    sum.x = fmaf(ka, bf2f(vr[0]), sum.x);
-                    sum.y = fmaf(ka, bf2f(vr[1]), sum.y);
-                    sum.z = fmaf(ka, bf2f(vr[2]), sum.z);
-                    sum.w = fmaf(ka, bf2f(vr[3]), sum.w);
-                }
+    const int64_t e = blk * 256 + threadIdx.x;
+    if (e >= E4) return;
+    float4 sum = zero;
+    if (present) {
+        if (r1 - r0 >= 64) {
+            const float4* ch = reinterpret_cast<const float4*>(p.chunks) + bh * p.n_chunks * E4 + e;
+#pragma unroll 16
+            for (int64_t c = r0 / 64; c < r1 / 64; ++c) sum = add4f(sum, ch[c * E4]);
+        } else {
+            const int a = (int)(e / dv4), c4 = (int)(e % dv4) * 4;
+            for (int64_t r = r0; r < r1; ++r) {
+                const float ka = bf2f(kh[r * p.dk + a]);
+                const u16* vr = vh + r * p.dv + c4;
+                sum.x = fmaf(ka, bf2f(vr[0]), sum.x);
+                sum.y = fmaf(ka, bf2f(vr[1]), sum.y);
+                sum.z = fmaf(ka, bf2f(vr[2]), sum.z);
+                sum.w = fmaf(ka, bf2f(vr[3]), sum.w);
             }
         }
-        out[e] = sum;
     }
+    out[e] = sum;
 }
 
 }  // namespace
@@ -494,7 +492,7 @@ hipError_t run_loglinear_prefix_levels(const LogLinPrefixParams& p, hipStream_t 
     const int64_t T = p.L - 1;
     if ((T >> 6) > p.n_chunks || ((T >> 6) > 0 && p.chunks == nullptr)) return hipErrorInvalidValue;
     const int64_t E4 = (int64_t)p.dk * p.dv / 4;
-    const int64_t grid = p.BH * p.n_lev * ((E4 + 1023) / 1024);
+    const int64_t grid = p.BH * p.n_lev * ((E4 + 255) / 256);
     if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
     hipLaunchKernelGGL(loglinear_prefix_levels_kernel, dim3((unsigned)grid), dim3(256), 0, s, p);
     return hipGetLastError();
