@@ -622,7 +622,14 @@ def run_extras(args, out):
     rows["next_loglinear"]["prefix_levels"] = {
         "heads": w3.BH, "L": w3.L, "levels": nl, "ms": ms_pre, **hbm(pre_bytes, ms_pre), "bytes": pre_bytes,
         "note": "k, v read by phase 1 (chunks of 64), chunk states written and read once, the levels written"}
-    del f, qd, kd, vd, lamd, S_ll
+    # the forward that also leaves the level states (one pyramid node per level of 2 chunks or more)
+    fl = la.LogLinearForward(qd, kd, vd, lamd, state_levels=nl)
+    ms_fl = row_time(fl.run)
+    rows["next_loglinear"]["forward_with_levels"] = {
+        "ms": ms_fl, "extra_ms_over_forward": ms_fl - ms,
+        "saved_ms_vs_forward_then_prefix_levels": ms + ms_pre - ms_fl,
+        "note": "the levels gathered from the forward's own chunk states and pyramid (no second pass over k, v)"}
+    del f, fl, qd, kd, vd, lamd, S_ll
     torch.cuda.empty_cache()
     # ---- next: the delta rule and its gated form at the headline shape (chunks of 64)
     delta = {}

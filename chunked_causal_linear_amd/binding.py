@@ -69,7 +69,7 @@ def _declare(lib: ctypes.CDLL) -> None:
                                              vp, i32, vp, vp, i64, vp, sz, vp]
     lib.la_recurrent_step_decay.argtypes = [vp, vp, vp, i32, i64, i64, i64, i32, vp, i64, f32, i32, f32, vp, vp, vp,
                                             i32, vp]
-    lib.la_loglinear_forward.argtypes = [vp, vp, vp, i32, i64, i64, i64, i64, i64, vp, i64, vp, i32, vp, sz, vp]
+    lib.la_loglinear_forward.argtypes = [vp, vp, vp, i32, i64, i64, i64, i64, i64, vp, i64, vp, i32, vp, i64, vp, sz, vp]
     lib.la_loglinear_forward_workspace.argtypes = [i32, i64, i64, i64, i64, i64]
     lib.la_loglinear_forward_workspace.restype = sz
     lib.la_loglinear_levels.argtypes = [i64]
@@ -337,7 +337,9 @@ def loglinear_levels(L: int) -> int:
 class LogLinearForward:
     """A planned log-linear forward (chunks of 64) with its output and workspace."""
 
-    def __init__(self, q, k, v, lam, C: int = 64):
+    def __init__(self, q, k, v, lam, C: int = 64, state_levels: Optional[int] = None):
+        """state_levels: also write the level states after the last token (see
+        la_loglinear_forward's S_levels) with that many levels, into self.S_levels."""
         torch = _torch()
         BH, L, d_k = q.shape
         d_v = v.shape[-1]
@@ -346,6 +348,10 @@ class LogLinearForward:
         if lam.dtype != torch.float32 or tuple(lam.shape) != (BH, L, loglinear_levels(L)):
             raise ValueError(f"lam must be float32 {(BH, L, loglinear_levels(L))}")
         self.o = torch.empty(BH, L, d_v, dtype=torch.bfloat16, device=q.device)
+        self.n_state_levels = 0 if state_levels is None else int(state_levels)
+        self.S_levels = None
+        if state_levels is not None:
+            self.S_levels = torch.empty(BH, self.n_state_levels, d_k, d_v, dtype=torch.float32, device=q.device)
         ws = int(lib().la_loglinear_forward_workspace(_dtype_code(q), BH, L, d_k, d_v, C))
         self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=q.device)
         self.ws_bytes = ws
@@ -357,13 +363,22 @@ class LogLinearForward:
         _check(lib().la_loglinear_forward(self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(),
                                           _dtype_code(self.q), BH, L, d_k, d_v, self.C, self.lam.data_ptr(),
                                           self.lam.shape[-1], self.o.data_ptr(), _dtype_code(self.o),
-                                          self.workspace.data_ptr(), self.ws_bytes, _stream_ptr()))
+                                          self.S_levels.data_ptr() if self.S_levels is not None else None,
+                                          self.n_state_levels, self.workspace.data_ptr(), self.ws_bytes,
+                                          _stream_ptr()))
         return self.o
 
 
-def loglinear_forward(q, k, v, lam, C: int = 64):
-    """Log-linear attention output (see la_loglinear_forward); lam [BH, L, levels] float32."""
-    return LogLinearForward(q, k, v, lam, C).run()
+def loglinear_forward(q, k, v, lam, C: int = 64, return_levels: bool = False, n_state_levels: Optional[int] = None):
+    """Log-linear attention output (see la_loglinear_forward); lam [BH, L, levels] float32.
+    With return_levels, returns (o, S_levels): also the level states after the last
+    token [BH, n_state_levels, d_k, d_v] float32 (n_state_levels defaults to
+    loglinear_levels(L); pass more to decode past a power of two)."""
+    if not return_levels:
+        return LogLinearForward(q, k, v, lam, C).run()
+    n = loglinear_levels(q.shape[1]) if n_state_levels is None else n_state_levels
+    f = LogLinearForward(q, k, v, lam, C, state_levels=n)
+    return f.run(), f.S_levels
 
 
 def recurrent_step_i8(q, k, v, S, out=None):

@@ -1012,7 +1012,8 @@ size_t la_loglinear_forward_workspace(la_dtype in_dt, int64_t BH, int64_t L, int
 
 la_status la_loglinear_forward(const void* q, const void* k, const void* v, la_dtype in_dt, int64_t BH, int64_t L,
                                int64_t d_k, int64_t d_v, int64_t C, const float* lam, int64_t n_levels, void* o,
-                               la_dtype out_dt, void* workspace, size_t ws_bytes, la_stream_t stream) {
+                               la_dtype out_dt, float* S_levels, int64_t n_state_levels, void* workspace,
+                               size_t ws_bytes, la_stream_t stream) {
     g_last_error[0] = 0;
     if (q == nullptr || k == nullptr || v == nullptr || lam == nullptr || o == nullptr)
         return fail(LA_ERR_INVALID_ARG, "q, k, v, lam and o must not be NULL");
@@ -1023,6 +1024,9 @@ la_status la_loglinear_forward(const void* q, const void* k, const void* v, la_d
     if (n_levels != loglinear_levels_of(L))
         return fail(LA_ERR_INVALID_ARG, "lam must hold %lld levels per token for L = %lld, got %lld",
                     (long long)loglinear_levels_of(L), (long long)L, (long long)n_levels);
+    if (S_levels != nullptr && (n_state_levels < n_levels || n_state_levels > 40))
+        return fail(LA_ERR_INVALID_ARG, "n_state_levels=%lld: %lld tokens need %lld..40", (long long)n_state_levels,
+                    (long long)L, (long long)n_levels);
     if (ws_S + ws_T > 0 && (workspace == nullptr || ws_bytes < ws_S + ws_T))
         return fail(LA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", ws_S + ws_T,
                     workspace ? ws_bytes : (size_t)0);
@@ -1055,7 +1059,23 @@ la_status la_loglinear_forward(const void* q, const void* k, const void* v, la_d
     p.dv = (int)d_v;
     const int64_t grid = BH * N * p.n_dvt;
     p.xcd_remap = xcd_ok(grid);
-    return hip_status(la::run_loglinear_fwd(p, grid, s), "log-linear forward launch");
+    st = hip_status(la::run_loglinear_fwd(p, grid, s), "log-linear forward launch");
+    if (st != LA_OK || S_levels == nullptr) return st;
+    // the level states after the last token, from the chunk states and the pyramid above
+    la::LogLinPrefixParams lp{};
+    lp.k = p.k;
+    lp.v = p.v;
+    lp.chunks = S;
+    lp.pyr = T;
+    lp.S = S_levels;
+    lp.BH = BH;
+    lp.L = L;
+    lp.dk = (int)d_k;
+    lp.dv = (int)d_v;
+    lp.n_lev = (int)n_state_levels;
+    lp.n_chunks = N > 1 ? (int)N : 0;
+    lp.n_pyr = p.n_pyr;
+    return hip_status(la::run_loglinear_prefix_levels(lp, s), "log-linear level states launch");
 }
 
 // ---------------------------------------------------------------------------

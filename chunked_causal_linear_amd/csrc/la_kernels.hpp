@@ -260,10 +260,11 @@ hipError_t run_loglinear_step(const LogLinStepParams& p, hipStream_t s);
 struct LogLinPrefixParams {
     const unsigned short* k;  // [BH, L, dk] bf16
     const unsigned short* v;  // [BH, L, dv] bf16
-    const float* chunks;      // [BH, n_chunks, dk, dv] states of the chunks before the last one (or null)
+    const float* chunks;      // [BH, n_chunks, dk, dv] per-chunk states (at least the chunks before the last one; or null)
+    const float* pyr;         // null, or the bucket sums of the chunk states (levels 2, 3, ... of the forward's pyramid)
     float* S;                 // [BH, n_lev, dk, dv]
     int64_t BH, L;
-    int dk, dv, n_lev, n_chunks;
+    int dk, dv, n_lev, n_chunks, n_pyr;
 };
 hipError_t run_loglinear_prefix_levels(const LogLinPrefixParams& p, hipStream_t s);
 

@@ -23,7 +23,8 @@
 //   * loglinear_step_kernel: one decode step, the Fenwick tree recurrence over
 //     each stream's level states (below);
 //   * loglinear_prefix_levels_kernel: the level states after a prefix, for a
-//     decode that follows a forward.
+//     decode that follows a forward (from the forward's own chunk states and
+//     pyramid when it is asked for them).
 #include "la_common.hpp"
 #include "la_kernels.hpp"
 
@@ -385,9 +386,11 @@ __global__ __launch_bounds__(256) void loglinear_step_kernel(LogLinStepParams p)
 // = the sum of k_s^T v_s over its bucket [h - 2^(l-1), h), h = T with its bits
 // below l - 1 cleared, when bit l - 1 of T is set, else zero.  A bucket of
 // 64 rows or more (l >= 7) is a run of whole chunks before T's chunk: the sum
-// of their states, in chunk order; the smaller ones lie in T's chunk and are
-// summed from the rows.  One workgroup per (head, level, 256 float4s of the
-// state); a thread owns one float4 and keeps sixteen chunk loads in flight.
+// of their states, in chunk order, or, after a forward, the one node of its
+// bucket pyramid that covers exactly that run (l >= 8); the smaller buckets
+// lie in T's chunk and are summed from the rows.  One workgroup per (head,
+// level, 256 float4s of the state); a thread owns one float4 and keeps sixteen
+// chunk loads in flight.
 __global__ __launch_bounds__(256) void loglinear_prefix_levels_kernel(LogLinPrefixParams p) {
     const int64_t E4 = (int64_t)p.dk * p.dv / 4;
     const int64_t nblk = (E4 + 255) / 256;
@@ -411,7 +414,15 @@ __global__ __launch_bounds__(256) void loglinear_prefix_levels_kernel(LogLinPref
     if (e >= E4) return;
     float4 sum = zero;
     if (present) {
-        if (r1 - r0 >= 64) {
+        if (r1 - r0 >= 128 && p.pyr != nullptr) {
+            // one node of the pyramid: level m = l - 6 >= 2 has floor(n_chunks / 2^(m-1))
+            // nodes, node j covering chunks j 2^(m-1) .. (j + 1) 2^(m-1) - 1
+            const int m = l - 6;
+            int64_t base = 0;
+            for (int u = 2; u < m; ++u) base += p.n_chunks >> (u - 1);
+            const int64_t node = (r0 >> 6) >> (m - 1);
+            sum = reinterpret_cast<const float4*>(p.pyr)[(bh * p.n_pyr + base + node) * E4 + e];
+        } else if (r1 - r0 >= 64) {
             const float4* ch = reinterpret_cast<const float4*>(p.chunks) + bh * p.n_chunks * E4 + e;
 #pragma unroll 16
             for (int64_t c = r0 / 64; c < r1 / 64; ++c) sum = add4f(sum, ch[c * E4]);
@@ -491,6 +502,7 @@ hipError_t run_loglinear_prefix_levels(const LogLinPrefixParams& p, hipStream_t 
         return hipErrorInvalidValue;
     const int64_t T = p.L - 1;
     if ((T >> 6) > p.n_chunks || ((T >> 6) > 0 && p.chunks == nullptr)) return hipErrorInvalidValue;
+    if (p.pyr != nullptr && p.n_pyr < (p.n_chunks >> 1)) return hipErrorInvalidValue;
     const int64_t E4 = (int64_t)p.dk * p.dv / 4;
     const int64_t grid = p.BH * p.n_lev * ((E4 + 255) / 256);
     if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;

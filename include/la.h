@@ -330,16 +330,23 @@ la_status la_recurrent_step_decay(const void* q, const void* k, const void* v, l
  *        {64, 128, 256}; C must be 64 (chunks of 64 rows).
  *   lam  [BH, L, n_levels] float32 (device), n_levels = la_loglinear_levels(L).
  *   o    [BH, L, d_v] LA_BF16.
+ *   S_levels  NULL, or [BH, n_state_levels, d_k, d_v] float32 (device): written
+ *        with the level states after the last token, those that
+ *        la_loglinear_prefix_levels gives for the same k, v (summed from this
+ *        call's own chunk states and bucket sums), for decode steps that go on
+ *        from position L.  n_state_levels (read only with S_levels) lies in
+ *        [n_levels, 40]; levels above n_levels are written as zero.
  *   workspace  la_loglinear_forward_workspace(...) bytes (per-chunk states and
  *        their bucket sums; 0 for a single chunk).
  * Errors: LA_ERR_INVALID_ARG (NULL pointer, non-positive size, wrong
- * n_levels), LA_ERR_UNSUPPORTED (other types, widths or chunk sizes),
- * LA_ERR_WORKSPACE; nothing is launched on an error.
+ * n_levels or n_state_levels), LA_ERR_UNSUPPORTED (other types, widths or
+ * chunk sizes), LA_ERR_WORKSPACE; nothing is launched on an error.
  */
 la_status la_loglinear_forward(const void* q, const void* k, const void* v, la_dtype in_dt,
                                int64_t BH, int64_t L, int64_t d_k, int64_t d_v, int64_t C,
                                const float* lam, int64_t n_levels, void* o, la_dtype out_dt,
-                               void* workspace, size_t ws_bytes, la_stream_t stream);
+                               float* S_levels, int64_t n_state_levels, void* workspace,
+                               size_t ws_bytes, la_stream_t stream);
 size_t la_loglinear_forward_workspace(la_dtype in_dt, int64_t BH, int64_t L, int64_t d_k,
                                       int64_t d_v, int64_t C);
 /* Levels a sequence of L tokens uses: 1 + the bit length of L - 1 (0 for L < 1). */

@@ -257,13 +257,19 @@ def test_loglinear_entry_point_errors():
 
     def call(**kw):
         a = dict(q=FAKE, k=FAKE, v=FAKE, in_dt=b.LA_BF16, BH=2, L=1000, d_k=64, d_v=64, C=64, lam=FAKE,
-                 n_lev=lib.la_loglinear_levels(1000), o=FAKE, out_dt=b.LA_BF16, ws=None, ws_bytes=0)
+                 n_lev=lib.la_loglinear_levels(1000), o=FAKE, out_dt=b.LA_BF16, S_lev=None, n_slev=0, ws=None,
+                 ws_bytes=0)
         a.update(kw)
         return lib.la_loglinear_forward(a["q"], a["k"], a["v"], a["in_dt"], a["BH"], a["L"], a["d_k"], a["d_v"],
-                                        a["C"], a["lam"], a["n_lev"], a["o"], a["out_dt"], a["ws"], a["ws_bytes"],
-                                        None)
+                                        a["C"], a["lam"], a["n_lev"], a["o"], a["out_dt"], a["S_lev"], a["n_slev"],
+                                        a["ws"], a["ws_bytes"], None)
     assert call(lam=None) == b.LA_ERR_INVALID_ARG
     assert call(n_lev=5) == b.LA_ERR_INVALID_ARG
+    # the level states: n_state_levels from la_loglinear_levels(L) (11 here) to 40, read only with S_levels
+    assert call(S_lev=FAKE, n_slev=10) == b.LA_ERR_INVALID_ARG
+    assert call(S_lev=FAKE, n_slev=41) == b.LA_ERR_INVALID_ARG
+    assert call(S_lev=FAKE, n_slev=11) == b.LA_ERR_WORKSPACE
+    assert call(S_lev=None, n_slev=-3) == b.LA_ERR_WORKSPACE
     assert call(C=32) == b.LA_ERR_UNSUPPORTED
     assert call(d_k=32) == b.LA_ERR_UNSUPPORTED
     assert call(d_v=32) == b.LA_ERR_UNSUPPORTED

@@ -194,19 +194,71 @@ def test_loglinear_prefix_levels(BH, L, dk, dv):
         assert_close(S[h], rS, what=f"levels head {h}")
 
 
-def test_loglinear_prefill_then_decode():
-    """A forward over the first 1500 tokens, the level states at its end, then
-    decode steps at positions 1500 .. 1539: every output against the oracle's
-    masked form over the whole sequence."""
+@pytest.mark.parametrize("BH,L,dk,dv", [(2, 1, 64, 64), (2, 64, 64, 64), (2, 65, 64, 64), (2, 200, 64, 128),
+                                        (2, 1000, 128, 256), (1, 4133, 128, 128)])
+def test_loglinear_forward_levels(BH, L, dk, dv):
+    """The forward's level states after its last token (from its own chunk
+    states and bucket pyramid: single nodes of 2 .. 32 chunks at L = 4133)
+    against the oracle's Fenwick recurrence over the same tokens, output and
+    states, with one level more than the tokens need (written as zero)."""
+    torch = torch_cuda()
+    q, k, v = wl.random_case(89, BH, L, dk, dv, "bf16", 1.0 / np.sqrt(dk))
+    nl = la.loglinear_levels(L)
+    lam = wl.loglinear_weights(89, BH, L, nl)
+    log(f"loglinear forward levels BH={BH} L={L} dk={dk} dv={dv} levels={nl}+1")
+    o, S = la.loglinear_forward(dev_input(q), dev_input(k), dev_input(v), torch.from_numpy(lam).cuda(),
+                                return_levels=True, n_state_levels=nl + 1)
+    o, S = host(o), host(S)
+    assert S.shape == (BH, nl + 1, dk, dv)
+    assert not np.any(S[:, nl])
+    for h in range(BH):
+        lam_h = np.pad(lam[h].astype(np.float64), ((0, 0), (0, 1)))  # the extra level stays empty
+        ref, rS = oracle.loglinear_recurrent(q.exact[h], k.exact[h], v.exact[h], lam_h, return_state=True)
+        assert_close(o[h], ref, what=f"o head {h}")
+        assert_close(S[h], rS, what=f"levels head {h}")
+
+
+def test_loglinear_forward_levels_benchmarked_shape():
+    """The level states the forward leaves at the benchmarked shape (128 heads x
+    8192 rows, d = 128: all fourteen levels hold keys, the top one the
+    64-chunk pyramid node), on two sampled heads, against the oracle's
+    recurrence."""
+    torch = torch_cuda()
+    w = wl.WORKLOADS[3]
+    q, k, v, _ = wl.workload_inputs(w, want_exact=False)
+    nl = la.loglinear_levels(w.L)
+    lam = wl.loglinear_weights(3, w.BH, w.L, nl)
+    log(f"loglinear forward levels at the benchmarked shape BH={w.BH} L={w.L} levels={nl}")
+    _, S = la.loglinear_forward(dev_bf16(q.bits), dev_bf16(k.bits), dev_bf16(v.bits), torch.from_numpy(lam).cuda(),
+                                return_levels=True)
+    del q, k, v
+    for bh in (5, w.BH - 1):
+        qh, kh, vh = wl.head_inputs(w, bh)
+        _, rS = oracle.loglinear_recurrent(qh.exact, kh.exact, vh.exact, lam[bh].astype(np.float64),
+                                           return_state=True)
+        worst = assert_close(host(S[bh]), rS, what=f"levels head {bh}")
+        log(f"head {bh} worst ratio {worst:.3f}")
+
+
+@pytest.mark.parametrize("source", ["prefix_levels", "forward"])
+def test_loglinear_prefill_then_decode(source):
+    """A forward over the first 1500 tokens, the level states at its end (from
+    la_loglinear_prefix_levels, or from the forward itself), then decode steps
+    at positions 1500 .. 1539: every output against the oracle's masked form
+    over the whole sequence."""
     torch = torch_cuda()
     n, T0, T1, dk, dv = 2, 1500, 1540, 128, 64
     nl = oracle.loglinear_levels(T1)
     q, k, v, lam = _step_inputs(88, n, T1, dk, dv, nl)
-    log(f"loglinear prefill {T0} then decode to {T1}")
+    log(f"loglinear prefill {T0} ({source}) then decode to {T1}")
     qp, kp, vp = (dev_bf16(np.ascontiguousarray(x.bits[:, :T0])) for x in (q, k, v))
     lam_p = torch.from_numpy(np.ascontiguousarray(lam[:, :T0, :oracle.loglinear_levels(T0)])).cuda()
-    o_pre = host(la.loglinear_forward(qp, kp, vp, lam_p))
-    S = la.loglinear_prefix_levels(kp, vp, nl)
+    if source == "forward":
+        o_pre, S = la.loglinear_forward(qp, kp, vp, lam_p, return_levels=True, n_state_levels=nl)
+        o_pre = host(o_pre)
+    else:
+        o_pre = host(la.loglinear_forward(qp, kp, vp, lam_p))
+        S = la.loglinear_prefix_levels(kp, vp, nl)
     got = _run_steps(q, k, v, lam, S, T0, T1, torch.float32)
     for h in range(n):
         ref = oracle.loglinear_scores_first(q.exact[h], k.exact[h], v.exact[h], lam[h].astype(np.float64))
