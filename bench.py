@@ -584,9 +584,11 @@ def run_extras(args, out):
     state = w3.d_k * w3.d_v * 4
     wk3 = Work(w3.BH, w3.L, w3.d_in, w3.d_k, w3.d_v, 64)
     ll_bytes = (wk3.fused_bytes() + w3.BH * w3.L * nl * 4           # q, k, v, o and the level weights
-                + w3.BH * N * state * 2                              # phase 1 reads k, v (in fused) and writes N states
-                + w3.BH * (N - 1) * state * 2                        # the pyramid reads and writes ~N states
-                + w3.BH * pops * state)                              # each chunk reads one bucket per set bit
+                + w3.BH * w3.L * (w3.d_k + w3.d_v) * 2                # phase 1 reads k, v
+                + w3.BH * N * state * 2                              # it writes N fp32 states, the pyramid reads them
+                + w3.BH * (N - 1) * state // 2                       # and writes N - 1 bf16 nodes
+                + w3.BH * (N // 2) * state                           # odd chunks read a level-1 bucket (fp32)
+                + w3.BH * (pops - N // 2) * state // 2)              # and every chunk one bf16 node per higher set bit
     lq, lk, lv = (wl.head_tensor(3, t, 0, 1024, w3.d_in, "bf16", 1.0 / np.sqrt(w3.d_in)).exact for t in
                   (wl.TENSOR_Q, wl.TENSOR_K, wl.TENSOR_V))
     lam_h = wl.loglinear_weights(3, 1, 1024, oracle.loglinear_levels(1024))[0].astype(np.float64)
@@ -696,7 +698,8 @@ def run_extras(args, out):
 
 ROWS = ("fwd_w3_C32", "fwd_w3_C64", "fwd_w3_C128", "fwd_w3_int8_C64", "states_w3_C64", "states_w3_C1024",
         "scan_w3_C64", "fmap_favor_w5", "fwd_w2", "fwd_w4", "fwd_w5", "decode_w5", "mfma_peak_bf16", "mfma_peak_i8",
-        "copy_512MiB", "memory_ceilings", "delta_w3", "delta_w3_gated", "delta_decode_w3")
+        "copy_512MiB", "memory_ceilings", "delta_w3", "delta_w3_gated", "delta_decode_w3", "loglinear_w3",
+        "loglinear_w3_levels")
 
 
 def run_row(name: str, reps: int):
@@ -756,6 +759,15 @@ def run_row(name: str, reps: int):
             fn = lambda: la.recurrent_step_delta(qs, ks, vs, S, bs, as_, out=o)  # noqa: E731
         else:
             fn = la.DeltaForward(qd, kd, vd, bd, ad).run
+    elif name.startswith("loglinear_w3"):
+        # log-linear attention at the headline shape (chunks of 64, seeded level weights),
+        # optionally also writing the level states after the last token
+        q, k, v, _ = wl.workload_inputs(w3, want_exact=False)
+        qd, kd, vd = dev_bf16(q.bits), dev_bf16(k.bits), dev_bf16(v.bits)
+        del q, k, v
+        nl = la.loglinear_levels(w3.L)
+        lamd = torch.from_numpy(wl.loglinear_weights(3, w3.BH, w3.L, nl)).cuda()
+        fn = la.LogLinearForward(qd, kd, vd, lamd, state_levels=nl if name.endswith("levels") else None).run
     elif name == "fwd_w3_int8_C64":
         qi, ki, vi = wl.random_case(33, w3.BH, w3.L, 128, 128, "i8")
         tq, tk, tv = (torch.from_numpy(t.bits).cuda() for t in (qi, ki, vi))

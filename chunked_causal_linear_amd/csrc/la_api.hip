@@ -906,7 +906,7 @@ static la_status loglinear_check(la_dtype in_dt, int64_t BH, int64_t L, int64_t 
     const int64_t N = cdiv(L, C);
     if (BH * N * (d_v / 64) > 0x7FFFFFFFLL) return fail(LA_ERR_UNSUPPORTED, "grid too large");
     *ws_S = N > 1 ? align256((size_t)(BH * N * d_k * d_v * 4)) : 0;
-    *ws_T = align256((size_t)(BH * loglinear_pyramid_nodes(N) * d_k * d_v * 4));
+    *ws_T = align256((size_t)(BH * loglinear_pyramid_nodes(N) * d_k * d_v * 2));  // bf16 nodes
     return LA_OK;
 }
 
@@ -1034,11 +1034,12 @@ la_status la_loglinear_forward(const void* q, const void* k, const void* v, la_d
     const int64_t N = cdiv(L, C);
     char* ws = static_cast<char*>(workspace);
     float* S = N > 1 ? reinterpret_cast<float*>(ws) : nullptr;
-    float* T = ws_T > 0 ? reinterpret_cast<float*>(ws + ws_S) : nullptr;
+    unsigned short* T = ws_T > 0 ? reinterpret_cast<unsigned short*>(ws + ws_S) : nullptr;
     if (N > 1) {
         st = chunk_states_impl(k, v, false, BH, L, d_k, d_v, C, (int)N, (int)N, S, nullptr, la::FMAP_NONE, 1.0f, s);
         if (st != LA_OK) return st;
-        st = hip_status(la::run_loglinear_pyramid(S, T, BH, (int)N, (int)loglinear_pyramid_nodes(N), d_k * d_v, s),
+        st = hip_status(la::run_loglinear_pyramid(S, T, BH, (int)N, (int)loglinear_pyramid_nodes(N), d_k * d_v,
+                                                  S_levels, L - 1, (int)n_state_levels, s),
                         "log-linear pyramid launch");
         if (st != LA_OK) return st;
     }
@@ -1061,12 +1062,12 @@ la_status la_loglinear_forward(const void* q, const void* k, const void* v, la_d
     p.xcd_remap = xcd_ok(grid);
     st = hip_status(la::run_loglinear_fwd(p, grid, s), "log-linear forward launch");
     if (st != LA_OK || S_levels == nullptr) return st;
-    // the level states after the last token, from the chunk states and the pyramid above
+    // the level states after the last token: levels of two chunks or more were
+    // written by the pyramid above; level 7 is one chunk state, the rest rows
     la::LogLinPrefixParams lp{};
     lp.k = p.k;
     lp.v = p.v;
     lp.chunks = S;
-    lp.pyr = T;
     lp.S = S_levels;
     lp.BH = BH;
     lp.L = L;
@@ -1074,7 +1075,7 @@ la_status la_loglinear_forward(const void* q, const void* k, const void* v, la_d
     lp.dv = (int)d_v;
     lp.n_lev = (int)n_state_levels;
     lp.n_chunks = N > 1 ? (int)N : 0;
-    lp.n_pyr = p.n_pyr;
+    lp.pyr_written = N > 1 ? 1 : 0;
     return hip_status(la::run_loglinear_prefix_levels(lp, s), "log-linear level states launch");
 }
 

@@ -223,7 +223,7 @@ struct LogLinParams {
     const unsigned short* v;  // [BH, L, dv]
     const float* lam;         // [BH, L, n_lev] level weights
     const float* S;           // [BH, N, dk, dv] per-chunk states (level-1 buckets)
-    const float* T;           // [BH, n_pyr, dk, dv] whole-chunk buckets of levels 2.. (or null)
+    const unsigned short* T;  // [BH, n_pyr, dk, dv] bf16 whole-chunk buckets of levels 2.. (or null)
     unsigned short* o;        // [BH, L, dv]
     int64_t L;
     int N;          // chunks
@@ -235,8 +235,10 @@ struct LogLinParams {
     int xcd_remap;
 };
 
-hipError_t run_loglinear_pyramid(const float* S, float* T, int64_t BH, int N, int n_pyr, int64_t E,
-                                 hipStream_t s);
+// With lev (the level states after token Tl, n_lev levels), the pyramid nodes
+// that are buckets of that state are also written there (fp32).
+hipError_t run_loglinear_pyramid(const float* S, unsigned short* T, int64_t BH, int N, int n_pyr, int64_t E,
+                                 float* lev, int64_t Tl, int n_lev, hipStream_t s);
 hipError_t run_loglinear_fwd(const LogLinParams& p, int64_t grid, hipStream_t s);
 
 // One decode step of log-linear attention over n streams (the Fenwick tree
@@ -261,10 +263,10 @@ struct LogLinPrefixParams {
     const unsigned short* k;  // [BH, L, dk] bf16
     const unsigned short* v;  // [BH, L, dv] bf16
     const float* chunks;      // [BH, n_chunks, dk, dv] per-chunk states (at least the chunks before the last one; or null)
-    const float* pyr;         // null, or the bucket sums of the chunk states (levels 2, 3, ... of the forward's pyramid)
     float* S;                 // [BH, n_lev, dk, dv]
     int64_t BH, L;
-    int dk, dv, n_lev, n_chunks, n_pyr;
+    int dk, dv, n_lev, n_chunks;
+    int pyr_written;          // levels >= 8 that hold keys were written by the forward's pyramid: left alone
 };
 hipError_t run_loglinear_prefix_levels(const LogLinPrefixParams& p, hipStream_t s);
 

@@ -50,6 +50,14 @@ __device__ __forceinline__ bf16x8 row_operand(const u16* t, int stride, int r, i
     return as_bf16x8(*reinterpret_cast<const uint4*>(t + r * stride + k0 + 8 * g));
 }
 
+// Row r's elements k0 + 4g .. k0 + 4g + 3 and k0 + 16 + 4g .. k0 + 16 + 4g + 3:
+// the order of the column operand below.
+__device__ __forceinline__ bf16x8 row_operand_split(const u16* t, int stride, int r, int k0, int g) {
+    const uint2 lo = *reinterpret_cast<const uint2*>(t + r * stride + k0 + 4 * g);
+    const uint2 hi = *reinterpret_cast<const uint2*>(t + r * stride + k0 + 16 + 4 * g);
+    return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
 // Column operand over keys key0 .. key0 + 31 in the order the S^T accumulators
 // come out in (lane group g: keys 4g..4g+3 and 16+4g..16+4g+3), column base + n
 // for lane n of the group (transpose reads of four rows at a time).
@@ -63,27 +71,45 @@ __device__ __forceinline__ bf16x8 col_operand(const u16* t, int stride, int key0
 
 __device__ __forceinline__ int bit_length(unsigned x) { return x == 0 ? 0 : 32 - __builtin_clz(x); }
 
+int bit_length_host(int64_t x) {
+    int b = 0;
+    for (; x > 0; x >>= 1) ++b;
+    return b;
+}
+
 __device__ __forceinline__ float4 add4f(const float4& a, const float4& b) {
     return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
 }
 
-// Level m >= 2 has floor(N / 2^(m-1)) nodes; node j = nodes 2j and 2j+1 of
-// level m - 1.  Each whole group of eight chunk states is read once and its
-// level-2, -3 and -4 nodes are summed in registers (no level is read back);
-// the rest (the tail of levels 2..4 and every level from 5 on) is summed level
-// by level from the level below.
-__global__ __launch_bounds__(256) void loglinear_pyramid_kernel(const float4* __restrict__ S, float4* __restrict__ T,
-                                                                int64_t BH, int N, int n_pyr, int64_t E4) {
+// Level m >= 2 has floor(N / 2^(m-1)) nodes; node j is the sum of chunk
+// states j 2^(m-1) .. (j + 1) 2^(m-1) - 1, stored in bf16 (the forward's
+// products take bucket states in bf16, so it reads half the bytes).  Every
+// node is summed in fp32 and rounded once.  A thread owns four state elements:
+// it reads each whole group of eight chunk states once and sums its level-2,
+// -3 and -4 nodes in registers; the level-4 nodes feed a binary carry (cy[i]:
+// the waiting left node of level 4 + i) that completes the nodes of levels 5
+// and up in the same pass; the chunks past the last whole group give the tail
+// of levels 2 and 3.  With `lev`, a node that is a bucket of the state after
+// token Tl (level m + 6 of that state when bit m + 5 of Tl is set: node
+// (Tl >> (m + 5)) - 1) is also written there, in fp32.  NC >= floor(log2 N) - 3.
+template <int NC>
+__global__ __launch_bounds__(256) void loglinear_pyramid_kernel(const float4* __restrict__ S, uint2* __restrict__ T,
+                                                                int64_t BH, int N, int n_pyr, int64_t E4,
+                                                                float4* __restrict__ lev, int64_t Tl, int n_lev) {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= BH * E4) return;
     const int64_t bh = idx / E4, e = idx % E4;
     const float4* s1 = S + bh * N * E4 + e;  // level 1: the chunk states
-    float4* out = T + bh * (int64_t)n_pyr * E4 + e;
-    const int n2 = N / 2, n3 = n2 / 2;
-    float4* l2 = out;
-    float4* l3 = l2 + (int64_t)n2 * E4;
-    float4* l4 = l3 + (int64_t)n3 * E4;
+    uint2* out = T + bh * (int64_t)n_pyr * E4 + e;
+    // node j of level m at out[(off + j) E4], off = the nodes of levels 2 .. m - 1
+    auto put = [&](int m, int64_t off, int64_t j, const float4& x) {
+        out[(off + j) * E4] = make_uint2(pack2_bf16(x.x, x.y), pack2_bf16(x.z, x.w));
+        if (lev != nullptr && ((Tl >> (m + 5)) & 1) && j == (Tl >> (m + 5)) - 1)
+            lev[(bh * n_lev + m + 6) * E4 + e] = x;
+    };
+    const int64_t off3 = N >> 1, off4 = off3 + (N >> 2), off5 = off4 + (N >> 3);
     const int g8 = N / 8;  // whole groups of eight
+    float4 cy[NC];
     for (int b = 0; b < g8; ++b) {
         float4 x[8];
 #pragma unroll
@@ -92,42 +118,66 @@ __global__ __launch_bounds__(256) void loglinear_pyramid_kernel(const float4* __
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             y[u] = add4f(x[2 * u], x[2 * u + 1]);
-            l2[(int64_t)(4 * b + u) * E4] = y[u];
+            put(2, 0, 4 * b + u, y[u]);
         }
         const float4 z0 = add4f(y[0], y[1]), z1 = add4f(y[2], y[3]);
-        l3[(int64_t)(2 * b) * E4] = z0;
-        l3[(int64_t)(2 * b + 1) * E4] = z1;
-        l4[(int64_t)b * E4] = add4f(z0, z1);
+        put(3, off3, 2 * b, z0);
+        put(3, off3, 2 * b + 1, z1);
+        float4 cur = add4f(z0, z1);
+        put(4, off4, b, cur);
+        // carry: a level-(4 + i) node with an even index waits; an odd one
+        // completes node j / 2 of level 5 + i with the one waiting
+        int64_t j = b, off = off5;
+        bool go = true;
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+            if (go) {
+                if ((j & 1) == 0) {
+                    cy[i] = cur;
+                    go = false;
+                } else {
+                    cur = add4f(cy[i], cur);
+                    j >>= 1;
+                    put(5 + i, off, j, cur);
+                    off += N >> (4 + i);  // the nodes of level 5 + i
+                }
+            }
+        }
     }
-    // the rest, level by level: level m's nodes from `done` on
-    const float4* src = s1;
-    float4* dst = l2;
-    int nodes = N;
-    for (int m = 2; nodes >= 2; ++m) {
-        const int next = nodes / 2;
-        const int done = m == 2 ? 4 * g8 : (m == 3 ? 2 * g8 : (m == 4 ? g8 : 0));
-        for (int j = done; j < next; ++j)
-            dst[(int64_t)j * E4] = add4f(src[(int64_t)(2 * j) * E4], src[(int64_t)(2 * j + 1) * E4]);
-        src = dst;
-        dst += (int64_t)next * E4;
-        nodes = next;
+    const int rem = N - 8 * g8;  // chunks past the last whole group (0..7)
+    if (rem >= 2) {
+        float4 y[2];
+#pragma unroll
+        for (int u = 0; u < 3; ++u) {
+            if (2 * u + 1 < rem) {
+                const int64_t c = 8 * g8 + 2 * u;
+                const float4 yu = add4f(s1[c * E4], s1[(c + 1) * E4]);
+                put(2, 0, 4 * g8 + u, yu);
+                if (u < 2) y[u] = yu;
+            }
+        }
+        if (rem >= 4) put(3, off3, 2 * g8, add4f(y[0], y[1]));
     }
 }
 
 // Three workgroups share a CU (at most 168 VGPRs, 46 KB of LDS at d_k = 128):
-// the bucket state tile reuses K's LDS once the intra part is done, and only
-// the in-chunk level weights (levels 0..6) are staged; a bucket's weight is
+// the bucket state tile reuses K's and V's LDS once the intra part is done (stored
+// [a][j] by 8-byte writes, read back by transpose reads), and only the in-chunk level
+// weights (levels 0..6) are staged; a bucket's weight is
 // read per row from global memory.
 template <int DK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void loglinear_fwd(LogLinParams p) {
     constexpr int QS = DK + 8, VS = LL_DVT + 8;  // padded row strides (elements)
     constexpr int NKA = DK / 32;
     constexpr int NLI = LL_CB + 2;               // in-chunk levels 0..LL_CB, padded
+    constexpr int PS = LL_DVT + 8;               // the bucket state's row stride ([a][j], d_k rows)
+    static_assert(DK * PS <= LL_C * (QS + VS), "the bucket state fits where K and V were");
     __shared__ __attribute__((aligned(16))) u16 Qs[LL_C * QS];
-    __shared__ __attribute__((aligned(16))) u16 Ks[LL_C * QS];  // K, then the bucket state (transposed: [j][a])
-    __shared__ __attribute__((aligned(16))) u16 Vs[LL_C * VS];
+    __shared__ __attribute__((aligned(16))) u16 KV[LL_C * (QS + VS)];  // K and V, then the bucket state
     __shared__ float lam_s[LL_C * NLI];
-    u16* const Ps = Ks;
+    u16* const Ks = KV;
+    u16* const Vs = KV + LL_C * QS;
+    u16* const Ps = KV;
 
     const int tid = threadIdx.x, wave = tid / WAVE, lane = tid % WAVE, l16 = lane % 16, g = lane / 16;
     int w = blockIdx.x;
@@ -152,25 +202,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
             if ((n >> (mm - 1)) & 1) return mm;
         return 0;
     };
-    auto level_state = [&](int m) -> const float* {
+    // A level-1 bucket is a chunk state (fp32); the pyramid's nodes are bf16.
+    constexpr int NPT = DK * (LL_DVT / 4) / 256;  // four-element pieces of a state tile per thread
+    float4 xf[NPT];                               // a level-1 bucket
+    uint2 xb[NPT];                                // a node of level 2 or more, four bf16 packed
+    auto load_state = [&](int m) {
         const int node = (n >> (m - 1)) - 1;
-        if (m == 1) return p.S + (bh * p.N + node) * E;
-        int base = 0;
-        for (int l = 2; l < m; ++l) base += p.N >> (l - 1);
-        return p.T + (bh * p.n_pyr + base + node) * E;
-    };
-    constexpr int NPT = DK * (LL_DVT / 4) / 256;  // float4 pieces of a state tile per thread
-    float4 xs[NPT];
-    auto load_state = [&](const float* P) {
+        if (m == 1) {
+            const float* P = p.S + (bh * p.N + node) * E;
 #pragma unroll
-        for (int u = 0; u < NPT; ++u) {
-            const int i = tid + u * 256;
-            const int a = i / (LL_DVT / 4), j4 = (i % (LL_DVT / 4)) * 4;
-            xs[u] = *reinterpret_cast<const float4*>(P + (int64_t)a * dv + col0 + j4);
+            for (int u = 0; u < NPT; ++u) {
+                const int i = tid + u * 256;
+                const int a = i / (LL_DVT / 4), j4 = (i % (LL_DVT / 4)) * 4;
+                xf[u] = *reinterpret_cast<const float4*>(P + (int64_t)a * dv + col0 + j4);
+            }
+        } else {
+            int base = 0;
+            for (int l = 2; l < m; ++l) base += p.N >> (l - 1);
+            const u16* P = p.T + (bh * p.n_pyr + base + node) * E;
+#pragma unroll
+            for (int u = 0; u < NPT; ++u) {
+                const int i = tid + u * 256;
+                const int a = i / (LL_DVT / 4), j4 = (i % (LL_DVT / 4)) * 4;
+                xb[u] = *reinterpret_cast<const uint2*>(P + (int64_t)a * dv + col0 + j4);
+            }
         }
     };
     int m = next_level(0);
-    if (m != 0) load_state(level_state(m));
+    if (m != 0) load_state(m);
 
     // chunk tiles into LDS (rows past the end are zero)
     for (int i = tid; i < LL_C * (DK / 8); i += 256) {
@@ -236,27 +295,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     while (m != 0) {
         const int mn = next_level(m);
         const float lw = qr < valid ? lam_row[LL_CB + m] : 0.f;
-        __syncthreads();  // Ps free (the first time: K is no longer read)
+        __syncthreads();  // Ps free (the first time: K and V are no longer read)
 #pragma unroll
         for (int u = 0; u < NPT; ++u) {
             const int i = tid + u * 256;
             const int a = i / (LL_DVT / 4), j4 = (i % (LL_DVT / 4)) * 4;
-            const uint32_t ab = pack2_bf16(xs[u].x, xs[u].y), cd = pack2_bf16(xs[u].z, xs[u].w);
-            Ps[(j4 + 0) * QS + a] = (u16)(ab & 0xFFFFu);
-            Ps[(j4 + 1) * QS + a] = (u16)(ab >> 16);
-            Ps[(j4 + 2) * QS + a] = (u16)(cd & 0xFFFFu);
-            Ps[(j4 + 3) * QS + a] = (u16)(cd >> 16);
+            const uint32_t ab = m == 1 ? pack2_bf16(xf[u].x, xf[u].y) : xb[u].x;
+            const uint32_t cd = m == 1 ? pack2_bf16(xf[u].z, xf[u].w) : xb[u].y;
+            *reinterpret_cast<uint2*>(Ps + a * PS + j4) = make_uint2(ab, cd);
         }
-        if (mn != 0) load_state(level_state(mn));
+        if (mn != 0) load_state(mn);
         __syncthreads();
         f32x4 Om[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) Om[c] = zero4;
 #pragma unroll
         for (int ks = 0; ks < NKA; ++ks) {
-            const bf16x8 qb = row_operand(Qs, QS, qr, ks * 32, g);
+            // P^T's rows by transpose reads over a = 32 ks .. 32 ks + 31 in the column
+            // operand's order; the query operand takes the same order of a
+            const bf16x8 qb = row_operand_split(Qs, QS, qr, ks * 32, g);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) Om[c] = mfma_bf16(row_operand(Ps, QS, c * 16 + l16, ks * 32, g), qb, Om[c]);
+            for (int c = 0; c < 4; ++c) Om[c] = mfma_bf16(col_operand(Ps, PS, ks * 32, c * 16, lane), qb, Om[c]);
         }
 #pragma unroll
         for (int c = 0; c < 4; ++c) O[c] += lw * Om[c];
@@ -386,9 +445,9 @@ __global__ __launch_bounds__(256) void loglinear_step_kernel(LogLinStepParams p)
 // = the sum of k_s^T v_s over its bucket [h - 2^(l-1), h), h = T with its bits
 // below l - 1 cleared, when bit l - 1 of T is set, else zero.  A bucket of
 // 64 rows or more (l >= 7) is a run of whole chunks before T's chunk: the sum
-// of their states, in chunk order, or, after a forward, the one node of its
-// bucket pyramid that covers exactly that run (l >= 8); the smaller buckets
-// lie in T's chunk and are summed from the rows.  One workgroup per (head,
+// of their states, in chunk order (after a forward, the levels of two chunks
+// or more are written by its pyramid and left alone here); the smaller
+// buckets lie in T's chunk and are summed from the rows.  One workgroup per (head,
 // level, 256 float4s of the state); a thread owns one float4 and keeps sixteen
 // chunk loads in flight.
 __global__ __launch_bounds__(256) void loglinear_prefix_levels_kernel(LogLinPrefixParams p) {
@@ -411,18 +470,10 @@ __global__ __launch_bounds__(256) void loglinear_prefix_levels_kernel(LogLinPref
     const u16* kh = p.k + bh * p.L * p.dk;
     const u16* vh = p.v + bh * p.L * p.dv;
     const int64_t e = blk * 256 + threadIdx.x;
-    if (e >= E4) return;
+    if (e >= E4 || (present && l >= 8 && p.pyr_written)) return;
     float4 sum = zero;
     if (present) {
-        if (r1 - r0 >= 128 && p.pyr != nullptr) {
-            // one node of the pyramid: level m = l - 6 >= 2 has floor(n_chunks / 2^(m-1))
-            // nodes, node j covering chunks j 2^(m-1) .. (j + 1) 2^(m-1) - 1
-            const int m = l - 6;
-            int64_t base = 0;
-            for (int u = 2; u < m; ++u) base += p.n_chunks >> (u - 1);
-            const int64_t node = (r0 >> 6) >> (m - 1);
-            sum = reinterpret_cast<const float4*>(p.pyr)[(bh * p.n_pyr + base + node) * E4 + e];
-        } else if (r1 - r0 >= 64) {
+        if (r1 - r0 >= 64) {
             const float4* ch = reinterpret_cast<const float4*>(p.chunks) + bh * p.n_chunks * E4 + e;
 #pragma unroll 16
             for (int64_t c = r0 / 64; c < r1 / 64; ++c) sum = add4f(sum, ch[c * E4]);
@@ -443,12 +494,29 @@ __global__ __launch_bounds__(256) void loglinear_prefix_levels_kernel(LogLinPref
 
 }  // namespace
 
-hipError_t run_loglinear_pyramid(const float* S, float* T, int64_t BH, int N, int n_pyr, int64_t E, hipStream_t s) {
+hipError_t run_loglinear_pyramid(const float* S, unsigned short* T, int64_t BH, int N, int n_pyr, int64_t E,
+                                 float* lev, int64_t Tl, int n_lev, hipStream_t s) {
     if (N < 2 || T == nullptr) return hipSuccess;
+    if (E % 4 != 0 || (lev != nullptr && (Tl < 0 || n_lev < bit_length_host(Tl) + 1))) return hipErrorInvalidValue;
     const int64_t E4 = E / 4;
     const int64_t blocks = (BH * E4 + 255) / 256;
-    hipLaunchKernelGGL(loglinear_pyramid_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
-                       reinterpret_cast<const float4*>(S), reinterpret_cast<float4*>(T), BH, N, n_pyr, E4);
+    if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+    const int lg = bit_length_host(N) - 1;  // floor(log2 N)
+    const float4* S4 = reinterpret_cast<const float4*>(S);
+    uint2* T2 = reinterpret_cast<uint2*>(T);
+    float4* L4 = reinterpret_cast<float4*>(lev);
+    if (lg - 3 <= 4)
+        hipLaunchKernelGGL(loglinear_pyramid_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, s, S4, T2, BH, N, n_pyr,
+                           E4, L4, Tl, n_lev);
+    else if (lg - 3 <= 8)
+        hipLaunchKernelGGL(loglinear_pyramid_kernel<8>, dim3((unsigned)blocks), dim3(256), 0, s, S4, T2, BH, N, n_pyr,
+                           E4, L4, Tl, n_lev);
+    else if (lg - 3 <= 16)
+        hipLaunchKernelGGL(loglinear_pyramid_kernel<16>, dim3((unsigned)blocks), dim3(256), 0, s, S4, T2, BH, N,
+                           n_pyr, E4, L4, Tl, n_lev);
+    else
+        hipLaunchKernelGGL(loglinear_pyramid_kernel<32>, dim3((unsigned)blocks), dim3(256), 0, s, S4, T2, BH, N,
+                           n_pyr, E4, L4, Tl, n_lev);
     return hipGetLastError();
 }
 
@@ -502,7 +570,6 @@ hipError_t run_loglinear_prefix_levels(const LogLinPrefixParams& p, hipStream_t 
         return hipErrorInvalidValue;
     const int64_t T = p.L - 1;
     if ((T >> 6) > p.n_chunks || ((T >> 6) > 0 && p.chunks == nullptr)) return hipErrorInvalidValue;
-    if (p.pyr != nullptr && p.n_pyr < (p.n_chunks >> 1)) return hipErrorInvalidValue;
     const int64_t E4 = (int64_t)p.dk * p.dv / 4;
     const int64_t grid = p.BH * p.n_lev * ((E4 + 255) / 256);
     if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;

@@ -251,7 +251,7 @@ def test_loglinear_entry_point_errors():
     assert [lib.la_loglinear_levels(L) for L in (0, 1, 2, 3, 8, 9, 8192)] == [0, 1, 2, 3, 4, 5, 14]
     # 128 heads x 8192 rows, d = 128: 128 chunk states + 64 + 32 + ... + 1 = 127 bucket sums per head
     ws = lib.la_loglinear_forward_workspace(b.LA_BF16, 128, 8192, 128, 128, 64)
-    assert ws == 128 * 128 * 128 * 128 * 4 + 128 * 127 * 128 * 128 * 4
+    assert ws == 128 * 128 * 128 * 128 * 4 + 128 * 127 * 128 * 128 * 2  # fp32 chunk states, bf16 bucket sums
     assert lib.la_loglinear_forward_workspace(b.LA_BF16, 2, 64, 64, 64, 64) == 0  # one chunk
     assert lib.la_loglinear_forward_workspace(b.LA_BF16, 2, 1000, 64, 64, 32) == 0  # unsupported chunk size
 
