@@ -218,6 +218,44 @@ def test_loglinear_forward_levels(BH, L, dk, dv):
         assert_close(S[h], rS, what=f"levels head {h}")
 
 
+@pytest.mark.parametrize("L,v_shift,oracle_levels", [(16500, 2, True), (262200, 4, False)])
+def test_loglinear_long_sequences(L, v_shift, oracle_levels):
+    """Sequences long enough for the pyramid's deeper carries (258 chunks: nine
+    pyramid levels; 4097 chunks: thirteen): the output against the oracle's
+    chunked form, the level states the forward leaves against the oracle's
+    recurrence (16,500 tokens) or against la_loglinear_prefix_levels, which sums
+    the chunk states in order without the pyramid (262,200 tokens; it is itself
+    pinned to the oracle's recurrence).
+
+    Bucket states are sums of up to L/2 outer products and grow as the square
+    root of their rows; the products take them as bf16 operands, whose rounding
+    grows with them (at unit scale and 16,500 tokens, that rounding alone
+    reaches 1.45 of the band at one element: the same figure a CPU model of
+    bf16 bucket operands gives).  v is scaled by 2^-v_shift (exact in bf16) so
+    that the largest bucket (128 and 2048 chunks) stays below the size of the
+    benchmarked shape's (64 chunks at unit scale), where the per-element band
+    holds (the model: 0.36 and 0.43 of it); a wrong node would still miss it
+    many times over."""
+    torch = torch_cuda()
+    dk = dv = 64
+    q, k, v = wl.random_case(91, 1, L, dk, dv, "bf16", 1.0 / np.sqrt(dk))
+    nl = la.loglinear_levels(L)
+    lam = wl.loglinear_weights(91, 1, L, nl)
+    log(f"loglinear long sequence L={L} levels={nl} v scaled by 2^-{v_shift}")
+    scale = 2.0 ** -v_shift
+    v_exact = v.exact * scale
+    kd, vd = dev_input(k), dev_input(v) * scale
+    o, S = la.loglinear_forward(dev_input(q), kd, vd, torch.from_numpy(lam).cuda(), return_levels=True)
+    ref = oracle.loglinear_chunked(q.exact[0], k.exact[0], v_exact[0], lam[0].astype(np.float64), 64)
+    assert_close(host(o)[0], ref, what="o")
+    if oracle_levels:
+        _, rS = oracle.loglinear_recurrent(q.exact[0], k.exact[0], v_exact[0], lam[0].astype(np.float64),
+                                           return_state=True)
+    else:
+        rS = host(la.loglinear_prefix_levels(kd, vd))[0].astype(np.float64)
+    assert_close(host(S)[0], rS, what="levels")
+
+
 def test_loglinear_forward_levels_benchmarked_shape():
     """The level states the forward leaves at the benchmarked shape (128 heads x
     8192 rows, d = 128: all fourteen levels hold keys, the top one the
