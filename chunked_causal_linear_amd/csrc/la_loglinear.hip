@@ -479,6 +479,7 @@ __global__ __launch_bounds__(256) void loglinear_prefix_levels_kernel(LogLinPref
             for (int64_t c = r0 / 64; c < r1 / 64; ++c) sum = add4f(sum, ch[c * E4]);
         } else {
             const int a = (int)(e / dv4), c4 = (int)(e % dv4) * 4;
+#pragma unroll 8
             for (int64_t r = r0; r < r1; ++r) {
                 const float ka = bf2f(kh[r * p.dk + a]);
                 const u16* vr = vh + r * p.dv + c4;
